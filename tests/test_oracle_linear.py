@@ -1,0 +1,297 @@
+"""Pins of the fp64 oracle (TTT-Linear) against what the pages and the
+mathematics fix, independently of the oracle's own code.
+
+Sources: dmarx.github.io record LIT-801 (arXiv 2407.04620), "Key
+takeaways": item 1 (state = weights W, update W_t = W_{t-1} - eta grad l,
+output z_t = f(q_t; W_t)), item 2 (loss || f(k; W) - v ||^2), item 3
+(Theorem 1), item 5 (mini-batch b = 16; LayerNorm and residual in f).
+
+Independent references used here: brute-force double loops (Theorem 1),
+torch autograd with torch.nn.functional.layer_norm in fp64 (gradients,
+online and batch GD), central finite differences, closed forms (eta = 0,
+gamma = 0) and structural invariants (segment split, unit permutation,
+thread count, zero-eta padding).
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_problem(rng, B=1, H=2, T=40, d=8, w_scale=0.3, qkv_scale=1.0):
+    q, k, v = (qkv_scale * rng.standard_normal((B, H, T, d))).astype(np.float32), \
+        (qkv_scale * rng.standard_normal((B, H, T, d))).astype(np.float32), \
+        (qkv_scale * rng.standard_normal((B, H, T, d))).astype(np.float32)
+    eta = (0.05 + 0.1 * rng.random((B, H, T))).astype(np.float32)
+    w0 = (w_scale * rng.standard_normal((H, d, d))).astype(np.float32)
+    gamma = (1.0 + 0.2 * rng.standard_normal((H, d))).astype(np.float32)
+    beta = (0.2 * rng.standard_normal((H, d))).astype(np.float32)
+    return q, k, v, eta, w0, gamma, beta
+
+
+# --- independent torch reference pieces (fp64, autograd) -------------------
+
+def _f_torch(x, W, gamma, beta, ln, res, eps):
+    h = x @ W
+    y = F.layer_norm(h, (h.shape[-1],), gamma, beta, eps) if ln else h
+    return (x if res else 0) + y
+
+
+def _grad_torch(W, k, v, gamma, beta, ln, res, eps):
+    W = W.detach().clone().requires_grad_(True)
+    loss = ((_f_torch(k, W, gamma, beta, ln, res, eps) - v) ** 2).sum()
+    (g,) = torch.autograd.grad(loss, W)
+    return g
+
+
+def _scan_torch(q, k, v, eta, W0, gamma, beta, b, ln=True, res=True, eps=1e-6):
+    """Mini-batch inner GD for one unit, gradients from autograd."""
+    T = q.shape[0]
+    W = W0.clone()
+    z = torch.empty_like(q)
+    for t0 in range(0, T, b):
+        Wb = W.clone()
+        for t in range(t0, min(t0 + b, T)):
+            W = W - eta[t] * _grad_torch(Wb, k[t], v[t], gamma, beta, ln, res, eps)
+            z[t] = _f_torch(q[t], W, gamma, beta, ln, res, eps)
+    return z, W
+
+
+def _t(a):
+    return torch.from_numpy(np.asarray(a, dtype=np.float64))
+
+
+# --- Theorem 1 ---------------------------------------------------------------
+
+def test_theorem1_golden_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "theorem1_d2_t3.json")))
+    q = np.array(g["q"], np.float32)[None, None]
+    k = np.array(g["k"], np.float32)[None, None]
+    v = np.array(g["v"], np.float32)[None, None]
+    T, d = g["T"], g["d"]
+    eta = np.full((1, 1, T), 0.5, np.float32)
+    w0 = np.zeros((1, d, d), np.float32)
+    z, w = oracle.linear(q, k, v, eta, w0, mini_batch=T, layer_norm=False, residual=False)
+    np.testing.assert_array_equal(z[0, 0], np.array(g["z"], np.float64))
+    np.testing.assert_array_equal(w[0, 0], np.array(g["w_final"], np.float64))
+
+
+@pytest.mark.parametrize("T,d", [(40, 8), (64, 16)])
+def test_theorem1_brute_force(T, d):
+    rng = np.random.default_rng(11)
+    q, k, v = (rng.standard_normal((1, 3, T, d)).astype(np.float32) for _ in range(3))
+    eta = np.full((1, 3, T), 0.5, np.float32)
+    w0 = np.zeros((3, d, d), np.float32)
+    z, w = oracle.linear(q, k, v, eta, w0, mini_batch=T, layer_norm=False, residual=False)
+    Q, K, V = (x.astype(np.float64) for x in (q, k, v))
+    for h in range(3):
+        zb = np.zeros((T, d))
+        for t in range(T):
+            for s in range(t + 1):
+                zb[t] += (Q[0, h, t] @ K[0, h, s]) * V[0, h, s]
+        scale = np.abs(zb).max()
+        assert np.abs(z[0, h] - zb).max() <= 1e-13 * scale
+        wb = K[0, h].T @ V[0, h]
+        assert np.abs(w[0, h] - wb).max() <= 1e-13 * np.abs(wb).max()
+
+
+def test_theorem1_fails_for_minibatch_16():
+    """Mini-batch GD (b < T) is not batch GD: the closed form must NOT hold
+    (guards against a scan that ignores the mini-batch boundary)."""
+    rng = np.random.default_rng(12)
+    T, d = 48, 8
+    q, k, v = (rng.standard_normal((1, 1, T, d)).astype(np.float32) for _ in range(3))
+    eta = np.full((1, 1, T), 0.5, np.float32)
+    z, _ = oracle.linear(q, k, v, eta, np.zeros((1, d, d), np.float32), mini_batch=16,
+                         layer_norm=False, residual=False)
+    Q, K, V = (x[0, 0].astype(np.float64) for x in (q, k, v))
+    zb = np.stack([sum((Q[t] @ K[s]) * V[s] for s in range(t + 1)) for t in range(T)])
+    assert np.abs(z[0, 0, :16] - zb[:16]).max() < 1e-12 * np.abs(zb).max()
+    assert np.abs(z[0, 0, 16:] - zb[16:]).max() > 1e-3 * np.abs(zb).max()
+
+
+# --- reductions of the mini-batch rule ---------------------------------------
+
+@pytest.mark.parametrize("ln,res", [(True, True), (False, True), (True, False), (False, False)])
+def test_b1_is_online_gd_autograd(ln, res):
+    rng = np.random.default_rng(21)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, H=1, T=24, d=8)
+    z, w = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=1, layer_norm=ln,
+                         residual=res)
+    zt, wt = _scan_torch(_t(q[0, 0]), _t(k[0, 0]), _t(v[0, 0]), _t(eta[0, 0]), _t(w0[0]),
+                         _t(gamma[0]), _t(beta[0]), 1, ln, res)
+    assert np.abs(z[0, 0] - zt.numpy()).max() <= 1e-12 * max(1.0, np.abs(zt.numpy()).max())
+    assert np.abs(w[0, 0] - wt.numpy()).max() <= 1e-12 * max(1.0, np.abs(wt.numpy()).max())
+
+
+def test_bT_is_batch_gd_autograd():
+    """b = T: every gradient at W0, causal prefix sums (Theorem 1's batch GD)."""
+    rng = np.random.default_rng(22)
+    T, d = 20, 8
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, H=1, T=T, d=d)
+    z, w = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=T)
+    Q, K, V, E, W0, G, Bt = (_t(x) for x in (q[0, 0], k[0, 0], v[0, 0], eta[0, 0], w0[0],
+                                             gamma[0], beta[0]))
+    grads = [_grad_torch(W0, K[s], V[s], G, Bt, True, True, 1e-6) for s in range(T)]
+    for t in range(T):
+        Wt = W0 - sum(E[s] * grads[s] for s in range(t + 1))
+        zt = _f_torch(Q[t], Wt, G, Bt, True, True, 1e-6)
+        assert np.abs(z[0, 0, t] - zt.numpy()).max() <= 1e-12 * np.abs(zt.numpy()).max()
+    assert np.abs(w[0, 0] - Wt.numpy()).max() <= 1e-12 * np.abs(Wt.numpy()).max()
+
+
+@pytest.mark.parametrize("b", [4, 16])
+def test_minibatch_matches_autograd_scan(b):
+    rng = np.random.default_rng(23)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, H=1, T=37, d=8)
+    z, w = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=b)
+    zt, wt = _scan_torch(*(_t(x) for x in (q[0, 0], k[0, 0], v[0, 0], eta[0, 0], w0[0],
+                                           gamma[0], beta[0])), b)
+    assert np.abs(z[0, 0] - zt.numpy()).max() <= 1e-12 * np.abs(zt.numpy()).max()
+    assert np.abs(w[0, 0] - wt.numpy()).max() <= 1e-12 * np.abs(wt.numpy()).max()
+
+
+# --- the inner gradient --------------------------------------------------------
+
+@pytest.mark.parametrize("ln,res", [(True, True), (False, False), (True, False)])
+def test_linear_grad_finite_differences(ln, res):
+    rng = np.random.default_rng(31)
+    d = 8
+    W = 0.3 * rng.standard_normal((d, d))
+    k, v = rng.standard_normal(d), rng.standard_normal(d)
+    gamma, beta = 1 + 0.2 * rng.standard_normal(d), 0.2 * rng.standard_normal(d)
+    _, g = oracle.linear_loss_grad(W, k, v, gamma, beta, layer_norm=ln, residual=res)
+    h = 1e-6
+    fd = np.zeros_like(W)
+    for i in range(d):
+        for j in range(d):
+            Wp, Wm = W.copy(), W.copy()
+            Wp[i, j] += h
+            Wm[i, j] -= h
+            lp, _ = oracle.linear_loss_grad(Wp, k, v, gamma, beta, layer_norm=ln,
+                                            residual=res, grad=False)
+            lm, _ = oracle.linear_loss_grad(Wm, k, v, gamma, beta, layer_norm=ln,
+                                            residual=res, grad=False)
+            fd[i, j] = (lp - lm) / (2 * h)
+    assert np.abs(g - fd).max() <= 1e-7 * np.abs(g).max()
+
+
+def test_linear_loss_matches_torch_layer_norm():
+    rng = np.random.default_rng(32)
+    d = 16
+    W = 0.3 * rng.standard_normal((d, d))
+    k, v = rng.standard_normal(d), rng.standard_normal(d)
+    gamma, beta = 1 + 0.2 * rng.standard_normal(d), 0.2 * rng.standard_normal(d)
+    loss, g = oracle.linear_loss_grad(W, k, v, gamma, beta, eps=1e-6)
+    Wt = _t(W).requires_grad_(True)
+    lt = ((_f_torch(_t(k), Wt, _t(gamma), _t(beta), True, True, 1e-6) - _t(v)) ** 2).sum()
+    lt.backward()
+    assert abs(loss - lt.item()) <= 1e-13 * abs(lt.item())
+    assert np.abs(g - Wt.grad.numpy()).max() <= 1e-12 * np.abs(g).max()
+
+
+def test_ln_gradient_rows_sum_to_zero():
+    """LN makes f invariant to a shift of x W along the all-ones direction,
+    so every row of dl/dW sums to zero (W 1 is conserved by the scan)."""
+    rng = np.random.default_rng(33)
+    d = 16
+    W = 0.3 * rng.standard_normal((d, d))
+    k, v = rng.standard_normal(d), rng.standard_normal(d)
+    gamma, beta = 1 + 0.2 * rng.standard_normal(d), 0.2 * rng.standard_normal(d)
+    _, g = oracle.linear_loss_grad(W, k, v, gamma, beta)
+    assert np.abs(g.sum(axis=1)).max() <= 1e-12 * np.abs(g).max()
+
+
+# --- closed-form special cases -------------------------------------------------
+
+def test_eta_zero_is_plain_layer_norm_output():
+    rng = np.random.default_rng(41)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, B=2, H=2, T=20, d=8)
+    eta[:] = 0
+    z, w = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=4, eps=1e-5)
+    for b in range(2):
+        for h in range(2):
+            zt = _f_torch(_t(q[b, h]), _t(w0[h]), _t(gamma[h]), _t(beta[h]), True, True, 1e-5)
+            assert np.abs(z[b, h] - zt.numpy()).max() <= 1e-13 * np.abs(zt.numpy()).max()
+            np.testing.assert_array_equal(w[b, h], w0[h].astype(np.float64))
+
+
+def test_gamma_zero_freezes_state():
+    rng = np.random.default_rng(42)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, H=2, T=20, d=8)
+    gamma[:] = 0
+    z, w = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=4)
+    for h in range(2):
+        np.testing.assert_array_equal(w[0, h], w0[h].astype(np.float64))
+        np.testing.assert_allclose(z[0, h], q[0, h].astype(np.float64) + beta[h][None].astype(np.float64),
+                                   rtol=0, atol=1e-15)
+
+
+# --- structural invariants -------------------------------------------------------
+
+def test_segment_split_resume():
+    """forward(0:T) == forward(T1:T; W0 = W_final(0:T1)) when T1 is a
+    multiple of b: the state W is the whole carried state."""
+    rng = np.random.default_rng(51)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, B=2, H=2, T=48, d=8)
+    z, w = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=8)
+    T1 = 24
+    z1, w1 = oracle.linear(q[:, :, :T1], k[:, :, :T1], v[:, :, :T1], eta[:, :, :T1], w0,
+                           gamma, beta, mini_batch=8)
+    # the resumed call needs its initial state as fp32; carry it exactly by
+    # comparing against a second full run started from the same fp32 state
+    w1f = w1.astype(np.float32)
+    z2, w2 = oracle.linear(q[:, :, T1:], k[:, :, T1:], v[:, :, T1:], eta[:, :, T1:], w1f,
+                           gamma, beta, mini_batch=8, state0_per_batch=True)
+    np.testing.assert_array_equal(z1, z[:, :, :T1])
+    # rounding the carried state to fp32 perturbs the continuation slightly
+    assert np.abs(z2 - z[:, :, T1:]).max() <= 1e-5 * np.abs(z).max()
+    assert np.abs(w2 - w).max() <= 1e-5 * np.abs(w).max()
+
+
+def test_ragged_tail_equals_zero_eta_padding():
+    """T mod b != 0: the last partial mini-batch is one step on its tokens,
+    i.e. the same as padding it with eta = 0 tokens and dropping their z."""
+    rng = np.random.default_rng(52)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, H=2, T=42, d=8)
+    z, w = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=16)
+    pad = lambda x, val: np.concatenate(
+        [x, np.full(x.shape[:2] + (6,) + x.shape[3:], val, x.dtype)], axis=2)
+    rz, rw = oracle.linear(pad(q, 0.7), pad(k, -0.3), pad(v, 1.1), pad(eta, 0.0), w0,
+                           gamma, beta, mini_batch=16)
+    np.testing.assert_array_equal(z, rz[:, :, :42])
+    np.testing.assert_array_equal(w, rw)
+
+
+def test_unit_permutation_and_thread_count():
+    rng = np.random.default_rng(53)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, B=2, H=3, T=20, d=8)
+    z, w = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=4, n_threads=1)
+    z4, w4 = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=4, n_threads=4)
+    np.testing.assert_array_equal(z, z4)
+    np.testing.assert_array_equal(w, w4)
+    p = [2, 0, 1]
+    zp, wp = oracle.linear(q[:, p], k[:, p], v[:, p], eta[:, p], w0[p], gamma[p], beta[p],
+                           mini_batch=4)
+    np.testing.assert_array_equal(zp, z[:, p])
+    np.testing.assert_array_equal(wp, w[:, p])
+    bp = [1, 0]
+    zb, wb = oracle.linear(q[bp], k[bp], v[bp], eta[bp], w0, gamma, beta, mini_batch=4)
+    np.testing.assert_array_equal(zb, z[bp])
+
+
+def test_nan_propagates():
+    rng = np.random.default_rng(54)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, H=1, T=20, d=8)
+    k[0, 0, 9, 3] = np.nan
+    z, w = oracle.linear(q, k, v, eta, w0, gamma, beta, mini_batch=4)
+    assert np.isfinite(z[0, 0, :8]).all()
+    assert np.isnan(z[0, 0, 9:]).all()
+    assert np.isnan(w).all()
