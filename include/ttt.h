@@ -1,0 +1,132 @@
+/*
+ * ttt.h -- C ABI of the MI355X (gfx950) TTT-layer forward scan.
+ *
+ * The method (arXiv 2407.04620, "Learning to (Learn at Test Time): RNNs with
+ * Expressive Hidden States"; summarised in the dmarx.github.io record
+ * LIT-801, "Key takeaways" items 1, 2 and 5, and in the codewithpapers.app
+ * record's "abstract"): a sequence layer whose hidden state is the weights S
+ * of an inner model f.  For each (batch, head) unit and each token t,
+ *     loss    l(S; k, v) = || f(k; S) - v ||^2                 (item 2)
+ *     update  S_t = S_{t-1} - eta_t * grad l(S_{t-1}; k_t, v_t)  (item 1)
+ *     output  z_t = f(q_t; S_t)                                (item 1)
+ * with mini-batch inner gradient descent (item 5): the gradients of the
+ * tokens of one mini-batch of b tokens are all taken at the state held when
+ * the mini-batch began, and the state absorbs them token by token, so z_t
+ * sees the updates of tokens s <= t.  A last partial mini-batch (T mod b
+ * != 0) is one step on its tokens.  Inner models (abstract; item 5):
+ *     TTT-Linear  f(x) = x + LN(x W)                        state W  [d,d]
+ *     TTT-MLP     f(x) = x + LN(GELU(x W1 + b1) W2 + b2)    state W1 [d,m],
+ *                                                  b1 [m], W2 [m,d], b2 [d]
+ * LN normalises the d features of one token (biased variance, epsilon
+ * ln_eps) and applies the per-head gamma/beta, which are parameters, not
+ * state.  GELU is the exact erf form.  The loss is the squared Euclidean
+ * norm summed over the d outputs; eta_t is used exactly as given.
+ * TTT_NO_LN and TTT_NO_RESIDUAL drop the LN or the residual (both: the
+ * linear model of Theorem 1, item 3).
+ *
+ * Conventions shared by every entry point
+ *  - Pointers q, k, v, eta, states, gamma, beta, z and the *_out buffers are
+ *    DEVICE pointers (HIP global memory of the current device), owned by
+ *    the caller.  The library allocates no memory and keeps no global
+ *    mutable state; calls are thread-safe and reentrant.
+ *  - Layout: contiguous, row-major, feature dimension fastest.
+ *      q, k, v, z  [B,H,T,d] of io_dtype     eta  [B,H,T] fp32
+ *      gamma, beta [H,d] fp32 (not read with TTT_NO_LN; may be NULL then)
+ *      initial state: [H,...] fp32 shared across the batch, or [B,H,...]
+ *      when state0_per_batch = 1.  Final state: [B,H,...] fp32.
+ *  - Execution is asynchronous on hip_stream (NULL = the default stream).
+ *    Outputs are valid once the caller synchronises that stream.
+ *  - Errors: argument errors are detected before anything is launched and
+ *    nothing is written.  A launch failure returns TTT_ERR_DEVICE.  Faults
+ *    during execution surface at the caller's next synchronisation.  No C++
+ *    exception crosses this boundary.
+ *  - Aliasing: z must not overlap q, k, v or eta (TTT_ERR_ALIAS).  A final
+ *    state buffer may equal the matching initial-state buffer only when
+ *    state0_per_batch = 1 (in-place resume; each unit reads its whole state
+ *    before it writes any of it); any other overlap between outputs and
+ *    inputs is TTT_ERR_ALIAS.
+ *  - Resume: the final state of a call started with the last tokens of a
+ *    sequence is the initial state (state0_per_batch = 1) of a call on the
+ *    continuation; this is exact when the first call's T is a multiple of
+ *    the mini-batch size.
+ */
+#ifndef TTT_H
+#define TTT_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TTT_ABI_VERSION 1
+
+typedef enum {
+  TTT_OK = 0,
+  TTT_ERR_NULL = 1,         /* a required pointer is NULL */
+  TTT_ERR_SHAPE = 2,        /* B, H, T, d, mini_batch or hidden out of range */
+  TTT_ERR_UNSUPPORTED = 3,  /* valid for the method, not built for gfx950 */
+  TTT_ERR_ALIAS = 4,        /* forbidden overlap between buffers */
+  TTT_ERR_DEVICE = 5,       /* HIP reported an error at launch */
+  TTT_ERR_ARG = 6           /* bad dtype, flag or epsilon */
+} ttt_status;
+
+typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
+
+enum {
+  TTT_NO_LN = 1u << 0,        /* f(x) = [x +] g(x) */
+  TTT_NO_RESIDUAL = 1u << 1   /* f(x) = [LN](g(x)) */
+};
+
+typedef struct {
+  int32_t B, H, T, d;        /* B, H >= 1; T >= 1; d == 64 on gfx950 */
+  int32_t mini_batch;        /* b: Linear 16*n (n >= 1; b >= T allowed); MLP 16 */
+  int32_t io_dtype;          /* ttt_dtype of q, k, v and z */
+  uint32_t flags;            /* TTT_NO_LN | TTT_NO_RESIDUAL */
+  float ln_eps;              /* LN epsilon, >= 0 (the workloads use 1e-6) */
+  int32_t state0_per_batch;  /* 0: initial state [H,...]; 1: [B,H,...] */
+} ttt_params;
+
+/*
+ * TTT-Linear forward scan.
+ *   w0     [H,d,d] (or [B,H,d,d]) fp32, input row index first: h = x W.
+ *   z      [B,H,T,d] io_dtype, written for every token.
+ *   w_out  [B,H,d,d] fp32 final state, or NULL to skip it.
+ * Supported: d = 64, mini_batch a positive multiple of 16 (values >= T
+ * give batch GD over the causal prefix), both io dtypes, any flags.
+ * gfx950 kernel: one 256-thread workgroup per (batch, head) unit; the state
+ * stays in registers across the whole sequence.
+ */
+ttt_status ttt_linear_forward(const ttt_params* p,
+                              const void* q, const void* k, const void* v,
+                              const float* eta, const float* w0,
+                              const float* ln_gamma, const float* ln_beta,
+                              void* z, float* w_out, void* hip_stream);
+
+/*
+ * TTT-MLP forward scan, hidden width `hidden` (m).
+ *   w1_0 [H,d,m], b1_0 [H,m], w2_0 [H,m,d], b2_0 [H,d] fp32
+ *   (leading B with state0_per_batch).  The biases are state.
+ *   w1_out, b1_out, w2_out, b2_out: [B,H,...] fp32, all NULL or all set.
+ * Supported: d = 64, hidden = 256, mini_batch = 16, both io dtypes, any
+ * flags.
+ */
+ttt_status ttt_mlp_forward(const ttt_params* p, int32_t hidden,
+                           const void* q, const void* k, const void* v,
+                           const float* eta,
+                           const float* w1_0, const float* b1_0,
+                           const float* w2_0, const float* b2_0,
+                           const float* ln_gamma, const float* ln_beta,
+                           void* z, float* w1_out, float* b1_out,
+                           float* w2_out, float* b2_out, void* hip_stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* ttt_status_string(ttt_status s);
+
+/* TTT_ABI_VERSION of the built library. */
+int32_t ttt_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

@@ -1,0 +1,201 @@
+// ttt_api.cpp -- C ABI entry points (include/ttt.h): argument validation,
+// alias checks and dispatch to the gfx950 kernels.  Everything here runs on
+// the host; validation makes no HIP call, so argument errors are reported
+// the same way with or without a GPU.
+#include "ttt.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdint>
+
+#include "ttt_kernels.hpp"
+
+namespace {
+
+constexpr int32_t kHeadDim = 64;
+constexpr int32_t kMlpHidden = 256;
+
+struct Range {
+  uintptr_t lo, hi;  // [lo, hi)
+};
+
+Range span(const void* p, uint64_t bytes) {
+  const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+  return Range{a, a + static_cast<uintptr_t>(bytes)};
+}
+
+bool overlap(Range a, Range b) {
+  if (a.lo == a.hi || b.lo == b.hi || a.lo == 0 || b.lo == 0) return false;
+  return a.lo < b.hi && b.lo < a.hi;
+}
+
+// Shared shape / flag checks.  *elems receives B*H*T*d.
+ttt_status check_common(const ttt_params* p, uint64_t* elems) {
+  if (!p) return TTT_ERR_NULL;
+  if (p->io_dtype != TTT_F32 && p->io_dtype != TTT_BF16) return TTT_ERR_ARG;
+  if (p->flags & ~static_cast<uint32_t>(TTT_NO_LN | TTT_NO_RESIDUAL)) return TTT_ERR_ARG;
+  if (!(p->ln_eps >= 0.0f) || !std::isfinite(p->ln_eps)) return TTT_ERR_ARG;
+  if (p->state0_per_batch != 0 && p->state0_per_batch != 1) return TTT_ERR_ARG;
+  if (p->B < 1 || p->H < 1 || p->T < 1 || p->d < 1 || p->mini_batch < 1) return TTT_ERR_SHAPE;
+  if (p->d != kHeadDim) return TTT_ERR_UNSUPPORTED;
+  const uint64_t units = static_cast<uint64_t>(p->B) * static_cast<uint64_t>(p->H);
+  if (units > 0x7fffffffull) return TTT_ERR_SHAPE;  // one workgroup per unit
+  const uint64_t tokens = units * static_cast<uint64_t>(p->T);
+  if (tokens > (1ull << 40)) return TTT_ERR_SHAPE;
+  *elems = tokens * static_cast<uint64_t>(p->d);
+  return TTT_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttt_status_string(ttt_status s) {
+  switch (s) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_NULL: return "a required pointer is NULL";
+    case TTT_ERR_SHAPE: return "B, H, T, d, mini_batch or hidden out of range";
+    case TTT_ERR_UNSUPPORTED:
+      return "configuration not built for gfx950 (needs d = 64; Linear: mini_batch a multiple "
+             "of 16; MLP: hidden = 256, mini_batch = 16)";
+    case TTT_ERR_ALIAS: return "an output buffer overlaps an input or another output";
+    case TTT_ERR_DEVICE: return "HIP reported an error at kernel launch";
+    case TTT_ERR_ARG: return "bad io_dtype, flags, ln_eps or state0_per_batch";
+  }
+  return "unknown ttt_status";
+}
+
+int32_t ttt_abi_version(void) { return TTT_ABI_VERSION; }
+
+ttt_status ttt_linear_forward(const ttt_params* p, const void* q, const void* k, const void* v,
+                              const float* eta, const float* w0, const float* ln_gamma,
+                              const float* ln_beta, void* z, float* w_out, void* hip_stream) {
+  uint64_t elems = 0;
+  ttt_status st = check_common(p, &elems);
+  if (st != TTT_OK) return st;
+  const bool ln = !(p->flags & TTT_NO_LN);
+  if (!q || !k || !v || !eta || !w0 || !z) return TTT_ERR_NULL;
+  if (ln && (!ln_gamma || !ln_beta)) return TTT_ERR_NULL;
+  if (p->mini_batch % 16 != 0) return TTT_ERR_UNSUPPORTED;
+
+  const uint64_t es = p->io_dtype == TTT_BF16 ? 2 : 4;
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t dd = static_cast<uint64_t>(kHeadDim) * kHeadDim;
+  const Range rq = span(q, elems * es), rk = span(k, elems * es), rv = span(v, elems * es);
+  const Range re = span(eta, units * p->T * 4), rz = span(z, elems * es);
+  const Range rw0 = span(w0, (p->state0_per_batch ? units : p->H) * dd * 4);
+  const Range rg = span(ln ? ln_gamma : nullptr, p->H * 256ull);
+  const Range rb = span(ln ? ln_beta : nullptr, p->H * 256ull);
+  if (overlap(rz, rq) || overlap(rz, rk) || overlap(rz, rv) || overlap(rz, re) ||
+      overlap(rz, rw0) || overlap(rz, rg) || overlap(rz, rb))
+    return TTT_ERR_ALIAS;
+  if (w_out) {
+    const Range rwo = span(w_out, units * dd * 4);
+    const bool in_place = p->state0_per_batch == 1 && static_cast<const void*>(w_out) == w0;
+    if (overlap(rwo, rq) || overlap(rwo, rk) || overlap(rwo, rv) || overlap(rwo, re) ||
+        overlap(rwo, rz) || overlap(rwo, rg) || overlap(rwo, rb) ||
+        (!in_place && overlap(rwo, rw0)))
+      return TTT_ERR_ALIAS;
+  }
+
+  tttk::LinearArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.eta = eta;
+  a.w0 = w0;
+  a.gamma = ln_gamma;
+  a.beta = ln_beta;
+  a.z = z;
+  a.w_out = w_out;
+  a.B = p->B;
+  a.H = p->H;
+  a.T = p->T;
+  a.tiles_per_mb = p->mini_batch / 16;
+  a.eps = p->ln_eps;
+  a.state0_per_batch = p->state0_per_batch;
+  const hipError_t e = tttk::launch_linear(a, p->io_dtype == TTT_BF16, ln,
+                                           !(p->flags & TTT_NO_RESIDUAL),
+                                           static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
+}
+
+ttt_status ttt_mlp_forward(const ttt_params* p, int32_t hidden, const void* q, const void* k,
+                           const void* v, const float* eta, const float* w1_0, const float* b1_0,
+                           const float* w2_0, const float* b2_0, const float* ln_gamma,
+                           const float* ln_beta, void* z, float* w1_out, float* b1_out,
+                           float* w2_out, float* b2_out, void* hip_stream) {
+  uint64_t elems = 0;
+  ttt_status st = check_common(p, &elems);
+  if (st != TTT_OK) return st;
+  if (hidden < 1) return TTT_ERR_SHAPE;
+  const bool ln = !(p->flags & TTT_NO_LN);
+  if (!q || !k || !v || !eta || !w1_0 || !b1_0 || !w2_0 || !b2_0 || !z) return TTT_ERR_NULL;
+  if (ln && (!ln_gamma || !ln_beta)) return TTT_ERR_NULL;
+  const int n_out = (w1_out != nullptr) + (b1_out != nullptr) + (w2_out != nullptr) +
+                    (b2_out != nullptr);
+  if (n_out != 0 && n_out != 4) return TTT_ERR_NULL;
+  if (hidden != kMlpHidden || p->mini_batch != 16) return TTT_ERR_UNSUPPORTED;
+
+  const uint64_t es = p->io_dtype == TTT_BF16 ? 2 : 4;
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t s0 = p->state0_per_batch ? units : static_cast<uint64_t>(p->H);
+  const uint64_t dm = static_cast<uint64_t>(kHeadDim) * hidden;
+  const Range rq = span(q, elems * es), rk = span(k, elems * es), rv = span(v, elems * es);
+  const Range re = span(eta, units * p->T * 4), rz = span(z, elems * es);
+  const Range rin[4] = {span(w1_0, s0 * dm * 4), span(b1_0, s0 * hidden * 4),
+                        span(w2_0, s0 * dm * 4), span(b2_0, s0 * kHeadDim * 4)};
+  const Range rg = span(ln ? ln_gamma : nullptr, p->H * 256ull);
+  const Range rb = span(ln ? ln_beta : nullptr, p->H * 256ull);
+  const Range inputs[] = {rq, rk, rv, re, rg, rb, rin[0], rin[1], rin[2], rin[3]};
+  for (const Range& r : inputs)
+    if (overlap(rz, r)) return TTT_ERR_ALIAS;
+  if (n_out == 4) {
+    float* outs[4] = {w1_out, b1_out, w2_out, b2_out};
+    const void* ins[4] = {w1_0, b1_0, w2_0, b2_0};
+    const uint64_t sizes[4] = {units * dm * 4, units * hidden * 4ull, units * dm * 4,
+                               units * kHeadDim * 4ull};
+    Range ro[4];
+    for (int i = 0; i < 4; ++i) ro[i] = span(outs[i], sizes[i]);
+    for (int i = 0; i < 4; ++i) {
+      if (overlap(ro[i], rq) || overlap(ro[i], rk) || overlap(ro[i], rv) ||
+          overlap(ro[i], re) || overlap(ro[i], rz) || overlap(ro[i], rg) || overlap(ro[i], rb))
+        return TTT_ERR_ALIAS;
+      for (int j = 0; j < 4; ++j) {
+        if (j != i && overlap(ro[i], ro[j])) return TTT_ERR_ALIAS;
+        const bool in_place = i == j && p->state0_per_batch == 1 &&
+                              static_cast<const void*>(outs[i]) == ins[i];
+        if (!in_place && overlap(ro[i], rin[j])) return TTT_ERR_ALIAS;
+      }
+    }
+  }
+
+  tttk::MlpArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.eta = eta;
+  a.w1 = w1_0;
+  a.b1 = b1_0;
+  a.w2 = w2_0;
+  a.b2 = b2_0;
+  a.gamma = ln_gamma;
+  a.beta = ln_beta;
+  a.z = z;
+  a.w1_out = w1_out;
+  a.b1_out = b1_out;
+  a.w2_out = w2_out;
+  a.b2_out = b2_out;
+  a.B = p->B;
+  a.H = p->H;
+  a.T = p->T;
+  a.eps = p->ln_eps;
+  a.state0_per_batch = p->state0_per_batch;
+  const hipError_t e = tttk::launch_mlp(a, p->io_dtype == TTT_BF16, ln,
+                                        !(p->flags & TTT_NO_RESIDUAL),
+                                        static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
+}
+
+}  // extern "C"

@@ -1,0 +1,87 @@
+// ttt_device.hpp -- gfx950 (CDNA4) building blocks shared by the TTT scan
+// kernels: MFMA wrappers, bf16 hi/lo splitting, cross-lane sums.
+//
+// MFMA fragment conventions used throughout (64-lane wave, lane l,
+// group g = l / 16, column c = l % 16):
+//   16x16 accumulator D (f32x4):     lane holds D[4g + i][c],       i = 0..3
+//   16x16x16 bf16 A operand (4 bf16): lane holds A[c][4g + i]
+//   16x16x16 bf16 B operand (4 bf16): lane holds B[4g + i][c]
+//   16x16x32 bf16 A / B operand (8 bf16): lane holds A[c][k(g, j)] /
+//       B[k(g, j)][c], j = 0..7, where k(g, j) is the same function for A
+//       and B.  The kernels only rely on that: they assign their own meaning
+//       ("slot j of group g") to the contraction index, identically in both
+//       operands, so the hardware's exact k-order is irrelevant.
+// Consequences the kernels use:
+//   * an accumulator X is directly the B operand of X and the A operand of
+//     X^T for a 16-deep contraction over its row index;
+//   * X (16x16, A-operand layout) times the identity gives X in accumulator
+//     layout, i.e. a register-level 16x16 transpose on the matrix unit.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tttk {
+
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+
+// D = A * B + C, 16x16x32, bf16 operands (8 per lane), fp32 accumulate.
+__device__ __forceinline__ f32x4 mfma32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// D = A * B + C, 16x16x16, bf16 operands (4 per lane), fp32 accumulate.
+__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4, a),
+                                                   __builtin_bit_cast(s16x4, b), c, 0, 0, 0);
+}
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) {
+  return __builtin_bit_cast(float, w << 16);
+}
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) {
+  return __builtin_bit_cast(float, w & 0xffff0000u);
+}
+
+// x = hi + lo with hi = bf16(x) and lo = bf16(x - hi): about 16 significant
+// bits in two bf16 operands.  Returns {hi(x0,x1), hi(x2,x3)} and the same
+// for lo.
+struct Split4 {
+  u32x2 hi, lo;
+};
+__device__ __forceinline__ Split4 split4(f32x4 x) {
+  Split4 s;
+  s.hi.x = pack_bf16(x[0], x[1]);
+  s.hi.y = pack_bf16(x[2], x[3]);
+  float r0 = x[0] - bf16_lo_to_f32(s.hi.x);
+  float r1 = x[1] - bf16_hi_to_f32(s.hi.x);
+  float r2 = x[2] - bf16_lo_to_f32(s.hi.y);
+  float r3 = x[3] - bf16_hi_to_f32(s.hi.y);
+  s.lo.x = pack_bf16(r0, r1);
+  s.lo.y = pack_bf16(r2, r3);
+  return s;
+}
+
+__device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
+
+// Sum over the four 16-lane groups (lanes c, c+16, c+32, c+48).
+__device__ __forceinline__ float group_sum(float x) {
+  x += __shfl_xor(x, 16);
+  x += __shfl_xor(x, 32);
+  return x;
+}
+
+}  // namespace tttk

@@ -1,0 +1,54 @@
+// ttt_kernels.hpp -- launch interface between the host API (ttt_api.cpp) and
+// the gfx950 kernels.  Plain structs of device pointers and sizes; the host
+// API has validated every field before a launcher is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tttk {
+
+struct LinearArgs {
+  const void* q;          // [B,H,T,64] bf16 or fp32
+  const void* k;
+  const void* v;
+  const float* eta;       // [B,H,T]
+  const float* w0;        // [H,64,64] or [B,H,64,64]
+  const float* gamma;     // [H,64] (unused without LN)
+  const float* beta;
+  void* z;                // [B,H,T,64]
+  float* w_out;           // [B,H,64,64] or nullptr
+  int32_t B, H, T;
+  int32_t tiles_per_mb;   // mini-batch size / 16
+  float eps;
+  int32_t state0_per_batch;
+};
+
+struct MlpArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* eta;
+  const float* w1;        // [H,64,256] or [B,H,64,256]
+  const float* b1;        // [H,256]
+  const float* w2;        // [H,256,64]
+  const float* b2;        // [H,64]
+  const float* gamma;
+  const float* beta;
+  void* z;
+  float* w1_out;          // all four nullptr or all set
+  float* b1_out;
+  float* w2_out;
+  float* b2_out;
+  int32_t B, H, T;
+  float eps;
+  int32_t state0_per_batch;
+};
+
+// Each returns the hipError_t of the launch.
+hipError_t launch_linear(const LinearArgs& a, bool bf16, bool ln, bool residual,
+                         hipStream_t stream);
+hipError_t launch_mlp(const MlpArgs& a, bool bf16, bool ln, bool residual,
+                      hipStream_t stream);
+
+}  // namespace tttk

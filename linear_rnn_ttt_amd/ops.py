@@ -1,0 +1,137 @@
+"""Python entry points with the names of the C ABI (include/ttt.h).
+
+PyTorch provides device memory and the stream; these functions check and
+marshal arguments, allocate the outputs with torch, and call the library,
+which launches the gfx950 kernels asynchronously on the current stream.
+"""
+from __future__ import annotations
+
+import ctypes
+from typing import Optional, Tuple
+
+import torch
+
+from . import _lib
+
+__all__ = ["ttt_linear_forward", "ttt_mlp_forward"]
+
+HEAD_DIM = 64
+
+
+def _dev_tensor(name, t, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device.type != "cuda":
+        raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s (got %s)" % (name, tuple(shape), tuple(t.shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch):
+    if q.dtype == torch.bfloat16:
+        io = _lib.TTT_BF16
+    elif q.dtype == torch.float32:
+        io = _lib.TTT_F32
+    else:
+        raise ValueError("q, k, v must be bfloat16 or float32 (got %s)" % q.dtype)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    flags = (0 if layer_norm else _lib.TTT_NO_LN) | (0 if residual else _lib.TTT_NO_RESIDUAL)
+    return _lib.TTTParams(B, H, T, d, int(mini_batch), io, flags, float(eps),
+                          int(bool(state0_per_batch)))
+
+
+def _stream(q, stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream(q.device) if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,
+                       w0: torch.Tensor, ln_gamma: Optional[torch.Tensor] = None,
+                       ln_beta: Optional[torch.Tensor] = None, *, mini_batch: int = 16,
+                       eps: float = 1e-6, layer_norm: bool = True, residual: bool = True,
+                       state0_per_batch: bool = False, z: Optional[torch.Tensor] = None,
+                       w_out: Optional[torch.Tensor] = None, return_state: bool = True,
+                       stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """TTT-Linear forward scan on the GPU; returns (z [B,H,T,d], W_final
+    [B,H,d,d] fp32 or None).  See include/ttt.h for the semantics."""
+    _dev_tensor("q", q)
+    B, H, T, d = q.shape
+    _dev_tensor("k", k, q.dtype, q.shape)
+    _dev_tensor("v", v, q.dtype, q.shape)
+    _dev_tensor("eta", eta, torch.float32, (B, H, T))
+    _dev_tensor("w0", w0, torch.float32, (B, H, d, d) if state0_per_batch else (H, d, d))
+    if layer_norm:
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d))
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d))
+    else:
+        ln_gamma = ln_beta = None
+    if z is None:
+        z = torch.empty_like(q)
+    _dev_tensor("z", z, q.dtype, q.shape)
+    if w_out is None and return_state:
+        w_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
+    if w_out is not None:
+        _dev_tensor("w_out", w_out, torch.float32, (B, H, d, d))
+    p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
+    rc = _lib.lib().ttt_linear_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+                                       _ptr(w0), _ptr(ln_gamma), _ptr(ln_beta), _ptr(z),
+                                       _ptr(w_out), _stream(q, stream))
+    _lib.check("ttt_linear_forward", rc)
+    return z, w_out
+
+
+def ttt_mlp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,
+                    w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: torch.Tensor,
+                    ln_gamma: Optional[torch.Tensor] = None,
+                    ln_beta: Optional[torch.Tensor] = None, *, mini_batch: int = 16,
+                    eps: float = 1e-6, layer_norm: bool = True, residual: bool = True,
+                    state0_per_batch: bool = False, z: Optional[torch.Tensor] = None,
+                    state_out=None, return_state: bool = True, stream=None):
+    """TTT-MLP forward scan on the GPU; returns (z, (W1, b1, W2, b2) final
+    or None).  See include/ttt.h for the semantics."""
+    _dev_tensor("q", q)
+    B, H, T, d = q.shape
+    m = w1.shape[-1]
+    _dev_tensor("k", k, q.dtype, q.shape)
+    _dev_tensor("v", v, q.dtype, q.shape)
+    _dev_tensor("eta", eta, torch.float32, (B, H, T))
+    lead = (B, H) if state0_per_batch else (H,)
+    _dev_tensor("w1", w1, torch.float32, lead + (d, m))
+    _dev_tensor("b1", b1, torch.float32, lead + (m,))
+    _dev_tensor("w2", w2, torch.float32, lead + (m, d))
+    _dev_tensor("b2", b2, torch.float32, lead + (d,))
+    if layer_norm:
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d))
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d))
+    else:
+        ln_gamma = ln_beta = None
+    if z is None:
+        z = torch.empty_like(q)
+    _dev_tensor("z", z, q.dtype, q.shape)
+    if state_out is None and return_state:
+        f = dict(dtype=torch.float32, device=q.device)
+        state_out = (torch.empty((B, H, d, m), **f), torch.empty((B, H, m), **f),
+                     torch.empty((B, H, m, d), **f), torch.empty((B, H, d), **f))
+    if state_out is not None:
+        for name, t, shp in zip(("w1_out", "b1_out", "w2_out", "b2_out"), state_out,
+                                ((B, H, d, m), (B, H, m), (B, H, m, d), (B, H, d))):
+            _dev_tensor(name, t, torch.float32, shp)
+    outs = state_out if state_out is not None else (None,) * 4
+    p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
+    rc = _lib.lib().ttt_mlp_forward(ctypes.byref(p), int(m), _ptr(q), _ptr(k), _ptr(v),
+                                    _ptr(eta), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                    _ptr(ln_gamma), _ptr(ln_beta), _ptr(z),
+                                    *[_ptr(t) for t in outs], _stream(q, stream))
+    _lib.check("ttt_mlp_forward", rc)
+    return z, state_out

@@ -1,0 +1,125 @@
+"""C ABI checks that need no GPU: the library loads, exports every function
+include/ttt.h declares, and rejects bad arguments with the documented status
+before anything is launched (the pointers below are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from linear_rnn_ttt_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    src = open(os.path.join(ROOT, "include", "ttt.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(ttt_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declares_the_boundary():
+    assert _declared_functions() == sorted(_lib.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    L = _lib.lib()
+    for name in _declared_functions():
+        assert hasattr(L, name), name
+    assert _lib.abi_version() == 1
+    for code in range(7):
+        assert _lib.status_string(code)
+    assert "unknown" in _lib.status_string(99)
+
+
+# fake, distinct, non-overlapping device addresses (never dereferenced)
+BASE = 1 << 40
+GAP = 1 << 36
+
+
+def _addr(i):
+    return ctypes.c_void_p(BASE + i * GAP)
+
+
+def _params(**kw):
+    d = dict(B=2, H=3, T=100, d=64, mini_batch=16, io_dtype=_lib.TTT_BF16, flags=0,
+             ln_eps=1e-6, state0_per_batch=0)
+    d.update(kw)
+    return _lib.TTTParams(**d)
+
+
+def _linear(p, **ptrs):
+    names = ["q", "k", "v", "eta", "w0", "g", "b", "z", "w_out"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    return _lib.lib().ttt_linear_forward(ctypes.byref(p) if p is not None else None, *args, None)
+
+
+def _mlp(p, hidden=256, **ptrs):
+    names = ["q", "k", "v", "eta", "w1", "b1", "w2", "b2", "g", "b", "z", "w1o", "b1o",
+             "w2o", "b2o"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    return _lib.lib().ttt_mlp_forward(ctypes.byref(p) if p is not None else None, hidden,
+                                      *args, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(d=32), _lib.TTT_ERR_UNSUPPORTED),
+    (dict(d=0), _lib.TTT_ERR_SHAPE),
+    (dict(T=0), _lib.TTT_ERR_SHAPE),
+    (dict(B=0), _lib.TTT_ERR_SHAPE),
+    (dict(H=-1), _lib.TTT_ERR_SHAPE),
+    (dict(mini_batch=0), _lib.TTT_ERR_SHAPE),
+    (dict(mini_batch=8), _lib.TTT_ERR_UNSUPPORTED),
+    (dict(mini_batch=24), _lib.TTT_ERR_UNSUPPORTED),
+    (dict(io_dtype=7), _lib.TTT_ERR_ARG),
+    (dict(flags=4), _lib.TTT_ERR_ARG),
+    (dict(ln_eps=-1.0), _lib.TTT_ERR_ARG),
+    (dict(ln_eps=float("nan")), _lib.TTT_ERR_ARG),
+    (dict(state0_per_batch=2), _lib.TTT_ERR_ARG),
+])
+def test_linear_rejects_bad_params(kw, code):
+    assert _linear(_params(**kw)) == code
+
+
+def test_linear_rejects_null_pointers():
+    assert _linear(None) == _lib.TTT_ERR_NULL
+    for name in ["q", "k", "v", "eta", "w0", "z", "g", "b"]:
+        assert _linear(_params(), **{name: None}) == _lib.TTT_ERR_NULL, name
+    # without LN the LN parameters may be NULL (then an unlaunchable fake
+    # pointer set would go on to the GPU, so stop at a shape error instead)
+    p = _params(flags=_lib.TTT_NO_LN, d=32)
+    assert _linear(p, g=None, b=None) == _lib.TTT_ERR_UNSUPPORTED
+
+
+def test_linear_rejects_aliasing():
+    assert _linear(_params(), z=_addr(1)) == _lib.TTT_ERR_ALIAS            # z == q
+    q = BASE + 1 * GAP
+    assert _linear(_params(), z=ctypes.c_void_p(q + 64)) == _lib.TTT_ERR_ALIAS
+    assert _linear(_params(), w_out=_addr(3)) == _lib.TTT_ERR_ALIAS        # w_out == v
+    assert _linear(_params(), w_out=_addr(5)) == _lib.TTT_ERR_ALIAS        # w_out == w0
+    assert _linear(_params(), w_out=_addr(8)) == _lib.TTT_ERR_ALIAS        # w_out == z
+    # in-place resume is allowed only with a per-batch initial state; this
+    # call passes validation, so prove it with an unsupported d instead
+    assert _linear(_params(state0_per_batch=1, d=32), w_out=_addr(5)) == \
+        _lib.TTT_ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("kw,hidden,code", [
+    (dict(), 128, _lib.TTT_ERR_UNSUPPORTED),
+    (dict(), 0, _lib.TTT_ERR_SHAPE),
+    (dict(mini_batch=32), 256, _lib.TTT_ERR_UNSUPPORTED),
+    (dict(d=16), 256, _lib.TTT_ERR_UNSUPPORTED),
+    (dict(flags=8), 256, _lib.TTT_ERR_ARG),
+])
+def test_mlp_rejects_bad_params(kw, hidden, code):
+    assert _mlp(_params(**kw), hidden) == code
+
+
+def test_mlp_rejects_null_and_partial_outputs_and_aliasing():
+    assert _mlp(None) == _lib.TTT_ERR_NULL
+    for name in ["q", "k", "v", "eta", "w1", "b1", "w2", "b2", "z", "g", "b"]:
+        assert _mlp(_params(), **{name: None}) == _lib.TTT_ERR_NULL, name
+    assert _mlp(_params(), b1o=None) == _lib.TTT_ERR_NULL
+    assert _mlp(_params(), z=_addr(2)) == _lib.TTT_ERR_ALIAS
+    assert _mlp(_params(), w2o=_addr(12)) == _lib.TTT_ERR_ALIAS            # w2_out == w1_out
+    assert _mlp(_params(), b2o=_addr(8)) == _lib.TTT_ERR_ALIAS             # b2_out == b2

@@ -1,0 +1,139 @@
+"""GPU parity of the TTT-Linear scan (gfx950 kernels through the C ABI)
+against the fp64 oracle on the same seeded inputs.
+
+Small cases compare every output; the full-size workloads (125M- and
+1.3B-shaped layers, 32k context) run in the configuration the benchmark
+times and compare sampled (batch, head) units, which the oracle computes on
+their own (units are independent).  Tolerances: 1e-4 max relative error for
+fp32 inputs, 2e-2 for bf16 inputs."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from linear_rnn_ttt_amd import ttt_linear_forward
+from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs, unit_slice
+
+from _parity import TOL, from_dev, state_err, to_dev, z_err
+
+pytestmark = pytest.mark.gpu
+
+
+def _gpu(inp, io, **kw):
+    z, w = ttt_linear_forward(to_dev(inp["q"], io), to_dev(inp["k"], io), to_dev(inp["v"], io),
+                              to_dev(inp["eta"]), to_dev(inp["w0"]), to_dev(inp["gamma"]),
+                              to_dev(inp["beta"]), **kw)
+    torch.cuda.synchronize()
+    return from_dev(z), from_dev(w)
+
+
+def _oracle(inp, **kw):
+    return oracle.linear(inp["q"], inp["k"], inp["v"], inp["eta"], inp["w0"], inp["gamma"],
+                         inp["beta"], **kw)
+
+
+def _check(name, inp, io, tol=None, **kw):
+    tol = TOL[io] if tol is None else tol
+    z, w = _gpu(inp, io, **kw)
+    okw = {k: v for k, v in kw.items() if k in ("mini_batch", "layer_norm", "residual", "eps",
+                                                 "state0_per_batch")}
+    zr, wr = _oracle(inp, **okw)
+    ez, ew = z_err(z, zr), state_err(w, wr)
+    print("%s: z err %.3e, state err %.3e (tol %.0e)" % (name, ez, ew, tol), flush=True)
+    assert ez <= tol and ew <= tol, (ez, ew)
+    return z, w
+
+
+def test_fp32_small_workload():
+    w = WORKLOADS["linear_b1h1_t256_f32"]
+    _check(w.name, make_inputs(w), "f32")
+
+
+def test_theorem1_mode_is_linear_attention():
+    w = WORKLOADS["theorem1_b1h1_t256_f32"]
+    inp = make_inputs(w)
+    z, wf = _check(w.name, inp, "f32", mini_batch=256, layer_norm=False, residual=False)
+    Q, K, V = (inp[x][0, 0].astype(np.float64) for x in "qkv")
+    zb = np.tril(Q @ K.T) @ V                    # z_t = sum_{s<=t} (q_t . k_s) v_s
+    assert z_err(z[0, 0], zb) <= 1e-4
+    assert state_err(wf, (K.T @ V)[None, None]) <= 1e-4
+
+
+@pytest.mark.parametrize("T", [1, 15, 16, 17, 47, 300])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_ragged_lengths(T, io):
+    base = WORKLOADS["linear_b1h1_t256_f32" if io == "f32" else "linear_125m_b8h12_t2k"]
+    inp = make_inputs(base, B=2, H=3, T=T)
+    _check("ragged T=%d %s" % (T, io), inp, io)
+
+
+@pytest.mark.parametrize("b", [32, 64, 256])
+def test_larger_minibatches(b):
+    inp = make_inputs(WORKLOADS["linear_b1h1_t256_f32"], B=1, H=2, T=200)
+    _check("mini_batch=%d" % b, inp, "f32", mini_batch=b)
+
+
+@pytest.mark.parametrize("ln,res", [(False, True), (True, False), (False, False)])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_flags(ln, res, io):
+    base = WORKLOADS["linear_b1h1_t256_f32" if io == "f32" else "linear_125m_b8h12_t2k"]
+    inp = make_inputs(base, B=1, H=2, T=100)
+    _check("ln=%d res=%d %s" % (ln, res, io), inp, io, layer_norm=ln, residual=res)
+
+
+def test_eps_and_per_batch_state():
+    w = WORKLOADS["linear_125m_b8h12_t2k"]
+    inp = make_inputs(w, B=2, H=2, T=64)
+    inp["w0"] = np.ascontiguousarray(
+        np.stack([inp["w0"], 1.5 * inp["w0"][::-1]])).astype(np.float32)
+    _check("eps=1e-5 per-batch W0", inp, "bf16", eps=1e-5, state0_per_batch=True)
+
+
+def test_resume_is_exact_and_in_place():
+    """forward(0:T) == forward(T1:T) started from forward(0:T1)'s state,
+    bit for bit, including the in-place form (w_out is w0)."""
+    w = WORKLOADS["linear_125m_b8h12_t2k"]
+    inp = make_inputs(w, B=2, H=3, T=256)
+    dev = {k: to_dev(v, "bf16" if k in "qkv" else None) for k, v in inp.items()}
+    z, wf = ttt_linear_forward(dev["q"], dev["k"], dev["v"], dev["eta"], dev["w0"],
+                               dev["gamma"], dev["beta"])
+    T1 = 128
+    part = lambda x, a, b: x[:, :, a:b].contiguous()
+    z1, w1 = ttt_linear_forward(*(part(dev[x], 0, T1) for x in "qkv"),
+                                part(dev["eta"], 0, T1), dev["w0"], dev["gamma"], dev["beta"])
+    z2, w2 = ttt_linear_forward(*(part(dev[x], T1, 256) for x in "qkv"),
+                                part(dev["eta"], T1, 256), w1, dev["gamma"], dev["beta"],
+                                state0_per_batch=True, w_out=w1)
+    torch.cuda.synchronize()
+    assert torch.equal(torch.cat([z1, z2], dim=2), z)
+    assert torch.equal(w2, wf) and w2.data_ptr() == w1.data_ptr()
+
+
+def test_deterministic():
+    w = WORKLOADS["linear_125m_b8h12_t2k"]
+    inp = make_inputs(w, T=512)
+    a = _gpu(inp, "bf16")
+    b = _gpu(inp, "bf16")
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+@pytest.mark.parametrize("name,units", [
+    ("linear_125m_b8h12_t2k", [(0, 0), (3, 7), (7, 11)]),
+    ("linear_1p3b_b4h32_t8k", [(0, 0), (3, 31)]),
+    ("linear_long_b1h32_t32k", [(0, 5)]),
+])
+def test_full_size_sampled_units(name, units):
+    """The full workload as the benchmark runs it; the oracle recomputes a
+    few (batch, head) units on their own."""
+    w = WORKLOADS[name]
+    inp = make_inputs(w)
+    z, wf = _gpu(inp, w.io)
+    sub = unit_slice(inp, units, w.H)
+    zr, wr = oracle.linear(sub["q"], sub["k"], sub["v"], sub["eta"], sub["w0"], sub["gamma"],
+                           sub["beta"], state0_per_batch=True)
+    bs, hs = [u[0] for u in units], [u[1] for u in units]
+    ez = z_err(z[bs, hs][None], zr)
+    ew = state_err(wf[bs, hs][None], wr)
+    print("%s units %s: z err %.3e, state err %.3e" % (name, units, ez, ew), flush=True)
+    assert ez <= TOL[w.io] and ew <= TOL[w.io]
+    assert np.isfinite(z).all()
