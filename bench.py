@@ -1,0 +1,365 @@
+#!/usr/bin/env python3
+"""Benchmark of the TTT-layer forward scan on one MI355X.
+
+A step is one forward scan over the whole workload (every (batch, head)
+unit, every token): one call of ttt_linear_forward (or ttt_mlp_forward),
+i.e. one launch of the scan kernel, on inputs already resident in HBM.
+
+Default workload: TTT-Linear at the 1.3B-model layer shape, B = 4, H = 32,
+d = 64, T = 8192, mini-batch 16, bf16 q/k/v/z, fp32 state and eta (seeded
+synthetic inputs, see linear_rnn_ttt_amd/inputs.py).
+
+Output: one JSON line with the throughput (tokens/s = B*T per second), the
+roofline of the scan kernel (algorithmic bytes or flops per launch over the
+launch time measured with HIP events on the launch stream) and the fp64 CPU
+oracle timed on the host cores.
+
+Other modes:
+  --summarize-pmc FETCH_DIR WRITE_DIR   turn two rocprofv3 --pmc runs
+      (FETCH_SIZE, then WRITE_SIZE) of `bench.py --copy-calibration` into the
+      markdown summary kept under profiles/ (HBM traffic per launch, scaled
+      by the same counters read on a plain copy of known size).
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "TTT layer forward tokens/s at 1.3B shape T=8k; % MFMA/HBM roofline"
+DEFAULT_WORKLOAD = "linear_1p3b_b4h32_t8k"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
+BF16_MFMA_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix
+COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
+KERNEL_SOURCES = {
+    "linear": ["ttt_linear.hip", "ttt_device.hpp", "ttt_kernels.hpp"],
+    "mlp": ["ttt_mlp.hip", "ttt_device.hpp", "ttt_kernels.hpp"],
+}
+KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd"}
+
+
+def kernel_hash(kind: str) -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kind]:
+        with open(os.path.join(ROOT, "linear_rnn_ttt_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def pmc_summary_path(kind: str, workload: str) -> str:
+    return os.path.join(ROOT, "profiles", "%s_%s_hbm_traffic.md" % (KERNEL_NAME[kind], workload))
+
+
+def algorithmic(w) -> dict:
+    """What the method itself must move and compute per launch.
+
+    Bytes: per token-head read q, k, v (3 d elements) and eta (4 B), write z
+    (d elements); per head read the initial state once; per unit write the
+    final state.  Flops: the three d x d (Linear) or seven d x 4d (MLP)
+    products per token-head that the method defines (x W for the gradient
+    point, its backward/update, and the output), 2 flops per multiply-add."""
+    es = 2 if w.io == "bf16" else 4
+    th = w.B * w.H * w.T
+    d = w.d
+    per_th = 4 * d * es + 4
+    if w.kind == "linear":
+        state = d * d * 4
+        flops_th = 6 * d * d
+    else:
+        m = w.hidden
+        state = (2 * d * m + m + d) * 4
+        flops_th = 14 * d * m
+    return {"bytes": th * per_th + w.H * state + w.B * w.H * state,
+            "bytes_per_token_head": per_th, "state_bytes_per_unit": state,
+            "flops": th * flops_th, "flops_per_token_head": flops_th}
+
+
+def read_traffic(kind: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None when there is none or the kernel source changed since."""
+    path = pmc_summary_path(kind, workload)
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if line.startswith("- ") and ":" in line:
+            k, v = line[2:].split(":", 1)
+            vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_source_sha256") != kernel_hash(kind):
+        return None
+    try:
+        return int(float(vals["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+def upload(inp, io):
+    import torch
+
+    dev = {}
+    for k, v in inp.items():
+        t = torch.from_numpy(v).cuda()
+        dev[k] = t.to(torch.bfloat16) if (io == "bf16" and k in ("q", "k", "v")) else t
+    return dev
+
+
+def make_step(w, dev):
+    from linear_rnn_ttt_amd import ttt_linear_forward, ttt_mlp_forward
+
+    if w.kind == "linear":
+        z, wo = ttt_linear_forward(dev["q"], dev["k"], dev["v"], dev["eta"], dev["w0"],
+                                   dev["gamma"], dev["beta"], mini_batch=w.mini_batch,
+                                   eps=w.eps)
+
+        def step():
+            ttt_linear_forward(dev["q"], dev["k"], dev["v"], dev["eta"], dev["w0"],
+                               dev["gamma"], dev["beta"], mini_batch=w.mini_batch, eps=w.eps,
+                               z=z, w_out=wo)
+        return step, z
+    z, so = ttt_mlp_forward(dev["q"], dev["k"], dev["v"], dev["eta"], dev["w1"], dev["b1"],
+                            dev["w2"], dev["b2"], dev["gamma"], dev["beta"], eps=w.eps)
+
+    def step():
+        ttt_mlp_forward(dev["q"], dev["k"], dev["v"], dev["eta"], dev["w1"], dev["b1"],
+                        dev["w2"], dev["b2"], dev["gamma"], dev["beta"], eps=w.eps, z=z,
+                        state_out=so)
+    return step, z
+
+
+def cpu_baseline(w, inp, budget_s: float):
+    """The fp64 oracle as it stands, on the host cores (at most 16 threads,
+    the host share of one GPU).  The whole workload when it fits the
+    budget, else a prefix of every unit's sequence; scaled to tokens/s."""
+    import oracle
+
+    cores = min(os.cpu_count() or 1, 16)
+    # probe: every unit over its first 256 tokens, to size the sample
+    units = w.B * w.H
+    T_probe = min(w.T, 256)
+    sub = lambda x, T: x[..., :T, :] if x.ndim == 4 else x[..., :T]
+    args = lambda T: [sub(inp[k], T) for k in ("q", "k", "v", "eta")]
+    t0 = time.perf_counter()
+    if w.kind == "linear":
+        oracle.linear(*args(T_probe), inp["w0"], inp["gamma"], inp["beta"],
+                      mini_batch=w.mini_batch, eps=w.eps, n_threads=cores)
+    else:
+        oracle.mlp(*args(T_probe), inp["w1"], inp["b1"], inp["w2"], inp["b2"], inp["gamma"],
+                   inp["beta"], mini_batch=w.mini_batch, eps=w.eps, n_threads=cores)
+    probe = time.perf_counter() - t0
+    est_full = probe * w.T / T_probe
+    T_s = w.T if est_full <= budget_s else max(16, int(w.T * budget_s / est_full) // 16 * 16)
+    t0 = time.perf_counter()
+    if w.kind == "linear":
+        oracle.linear(*args(T_s), inp["w0"], inp["gamma"], inp["beta"],
+                      mini_batch=w.mini_batch, eps=w.eps, n_threads=cores)
+    else:
+        oracle.mlp(*args(T_s), inp["w1"], inp["b1"], inp["w2"], inp["b2"], inp["gamma"],
+                   inp["beta"], mini_batch=w.mini_batch, eps=w.eps, n_threads=cores)
+    dt = time.perf_counter() - t0
+    sample = ("whole workload" if T_s == w.T else
+              "all %d units, first %d of %d tokens each" % (units, T_s, w.T))
+    return {"value": round(w.B * T_s / dt, 1), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle", "sample": sample + ", %.1f s wall, fp64" % dt}
+
+
+def run(args) -> dict:
+    import torch
+
+    from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    inp = make_inputs(w)
+    dev = upload(inp, w.io)
+    step, z = make_step(w, dev)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        # a plain copy of known size, outside the timed region, for scaling
+        # the rocprofv3 FETCH_SIZE / WRITE_SIZE counters
+        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s, e in ev:
+        s.record(stream)
+        step()
+        e.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    launch_ms = [s.elapsed_time(e) for s, e in ev]
+    avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    ok = bool(torch.isfinite(z.float()).all().item())
+
+    alg = algorithmic(w)
+    if w.kind == "linear":
+        achieved = alg["bytes"] / avg_launch_s / 1e9
+        traffic = read_traffic(w.kind, w.name)
+        roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
+                "kernel": KERNEL_NAME[w.kind], "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                "algorithmic_bytes_per_launch": alg["bytes"]}
+    else:
+        achieved = alg["flops"] / avg_launch_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": BF16_MFMA_PEAK_TFS,
+                "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFS, 5),
+                "traffic": read_traffic(w.kind, w.name), "kernel": KERNEL_NAME[w.kind],
+                "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                "algorithmic_flops_per_launch": alg["flops"]}
+
+    out = {
+        "metric": METRIC,
+        "value": round(w.B * w.T / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "inner_model": "TTT-" + ("Linear" if w.kind == "linear"
+                                                                 else "MLP"),
+                   "B": w.B, "H": w.H, "T": w.T, "d": w.d, "mini_batch": w.mini_batch,
+                   "io": w.io, "state": "fp32", "ln_eps": w.eps, "global_batch": w.B,
+                   "seq_len": w.T, "parallelism": "none (1 GPU, one workgroup per unit)"},
+        "roofline": roof,
+        "outputs_finite": ok,
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, inp, args.cpu_budget)
+    return out
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 counter summaries
+
+def _read_counter_csv(d: str):
+    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+    if not files:
+        raise SystemExit("no *counter_collection.csv under %s" % d)
+    rows = []
+    for f in files:
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _per_dispatch(rows, counter):
+    """{kernel name: [value per dispatch]} for one counter (values summed
+    over the counter's instances within a dispatch)."""
+    acc = {}
+    for r in rows:
+        if r.get("Counter_Name") != counter:
+            continue
+        key = (r.get("Kernel_Name", ""), r.get("Dispatch_Id", ""))
+        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
+    out = {}
+    for (name, _), v in acc.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write):
+    from linear_rnn_ttt_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[workload]
+    kname = KERNEL_NAME[w.kind]
+    fetch = _per_dispatch(_read_counter_csv(fetch_dir), "FETCH_SIZE")
+    write = _per_dispatch(_read_counter_csv(write_dir), "WRITE_SIZE")
+
+    def pick(d, pred):
+        vals = [v for name, vs in d.items() if pred(name) for v in vs]
+        return vals
+
+    kf = pick(fetch, lambda n: kname in n)
+    kw = pick(write, lambda n: kname in n)
+    cf = pick(fetch, lambda n: "copy" in n.lower() or "elementwise" in n.lower())
+    cw = pick(write, lambda n: "copy" in n.lower() or "elementwise" in n.lower())
+    # the largest elementwise dispatch is the 1 GiB copy (fills are smaller
+    # reads); use it for both factors
+    copy_fetch_kib = max(cf) if cf else float("nan")
+    copy_write_kib = max(cw) if cw else float("nan")
+    f_fetch = (COPY_BYTES / 1024.0) / copy_fetch_kib
+    f_write = (COPY_BYTES / 1024.0) / copy_write_kib
+    fetch_kib = sum(kf) / len(kf)
+    write_kib = sum(kw) / len(kw)
+    traffic = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
+    alg = algorithmic(w)["bytes"]
+    lines = [
+        "# HBM traffic of `%s` on %s (rocprofv3 --pmc)" % (kname, workload),
+        "",
+        "Two counter runs of the benchmark (kernel launches plus one plain 1 GiB",
+        "device-to-device copy used to scale the counters):",
+        "",
+        "    " + cmd_fetch,
+        "    " + cmd_write,
+        "",
+        "- kernel_source_sha256: `%s`" % kernel_hash(w.kind),
+        "- dispatches_measured: %d (FETCH_SIZE), %d (WRITE_SIZE)" % (len(kf), len(kw)),
+        "- fetch_kib_per_dispatch: %.1f" % fetch_kib,
+        "- write_kib_per_dispatch: %.1f" % write_kib,
+        "- copy_fetch_kib (1 GiB copy): %.1f -> factor %.4f" % (copy_fetch_kib, f_fetch),
+        "- copy_write_kib (1 GiB copy): %.1f -> factor %.4f" % (copy_write_kib, f_write),
+        "- traffic_bytes_per_launch: %d" % int(traffic),
+        "- algorithmic_bytes_per_launch: %d" % alg,
+        "- traffic / algorithmic: %.3f" % (traffic / alg),
+    ]
+    return "\n".join(lines) + "\n"
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0,
+                    help="seconds of oracle wall time for the CPU baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run one 1 GiB copy before the timed region (counter scaling)")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
+    ap.add_argument("--pmc-commands", nargs=2, default=["", ""])
+    args = ap.parse_args(argv)
+
+    if args.summarize_pmc:
+        sys.stdout.write(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
+                                       args.workload, *args.pmc_commands))
+        return 0
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU (the scan shards over "
+              "independent (batch, head) units with no exchange; multi-GPU runs are not "
+              "provided). Use --gpus 1.", file=sys.stderr)
+        return 2
+    if args.steps < 1 or args.warmup < 0:
+        print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
+        return 2
+    out = run(args)
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -77,11 +77,48 @@ __device__ __forceinline__ Split4 split4(f32x4 x) {
 
 __device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
 
-// Sum over the four 16-lane groups (lanes c, c+16, c+32, c+48).
-__device__ __forceinline__ float group_sum(float x) {
-  x += __shfl_xor(x, 16);
-  x += __shfl_xor(x, 32);
-  return x;
+// Workgroup barrier that orders LDS only (release/acquire fences on the
+// local address space around s_barrier).  Unlike __syncthreads() it does not
+// wait for outstanding global loads and stores, so prefetches and output
+// stores stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
+
+__device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// v_permlane32_swap on (a, b) leaves lanes 0-31 of a in place, moves lanes
+// 0-31 of b to lanes 32-63 of a, and returns lanes 32-63 of a and b in b's
+// place.  Summing the two results: lanes 0-31 get a[l] + a[l+32], lanes
+// 32-63 get b[l-32] + b[l].
+__device__ __forceinline__ float swap32_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane32_swap(fbits(a), fbits(b), false, false);
+  return bitsf(r[0]) + bitsf(r[1]);
+}
+// v_permlane16_swap on (a, b) exchanges the odd 16-lane rows of a with the
+// even rows of b.  Summing the two results: row 0 gets a0 + a1, row 1
+// b0 + b1, row 2 a2 + a3, row 3 b2 + b3 (rows of 16 lanes).
+__device__ __forceinline__ float swap16_sum(float a, float b) {
+  const auto r = __builtin_amdgcn_permlane16_swap(fbits(a), fbits(b), false, false);
+  return bitsf(r[0]) + bitsf(r[1]);
+}
+
+// Sum over the four 16-lane groups (lanes c, c+16, c+32, c+48), in every lane.
+__device__ __forceinline__ float group_sum(float x) {
+  const float y = swap16_sum(x, x);
+  return swap32_sum(y, y);
+}
+
+// Reduce-scatter of four per-lane partial sums over the four lane groups:
+// group 0 receives the total of q0, group 1 of q2, group 2 of q1, group 3
+// of q3 (three swaps instead of eight for four full group sums).
+__device__ __forceinline__ float group_reduce_scatter4(float q0, float q1, float q2, float q3) {
+  return swap16_sum(swap32_sum(q0, q1), swap32_sum(q2, q3));
+}
+// Which quantity group g holds after group_reduce_scatter4.
+__device__ __forceinline__ constexpr int rs4_slot(int g) { return g == 1 ? 2 : (g == 2 ? 1 : g); }
 
 }  // namespace tttk

@@ -16,19 +16,25 @@
 // for several tiles).
 //
 // Mapping onto one CU:
-//   * one 256-thread workgroup (4 waves) per (batch, head) unit; wave w
-//     owns output columns 16w..16w+15 of W and of every H, G, Z tile;
+//   * one 256-thread workgroup (4 waves, one per SIMD) per (batch, head)
+//     unit; wave w owns output columns 16w..16w+15 of W, H, G and Z;
 //   * the state never leaves the registers: W[:, 16w:16w+16] is four 16x16
-//     MFMA accumulators per wave, updated in place by the update product;
-//   * H is produced transposed (H^T = W^T K^T), so a lane holds 4 features
-//     of ONE token and the LN row sums are 3 in-lane adds plus 2 cross-group
-//     steps; the 4 waves exchange 6 (chain) or 2 (output) partial sums per
-//     token through LDS, one barrier each;
-//   * fp32 operands are fed to the bf16 matrix unit as hi + lo bf16 pairs
-//     (about 16 significant bits); bf16 inputs are exact;
-//   * q, k, v, eta stream from HBM in 16 KB-per-tensor blocks: the next
-//     block is loaded into registers while the current one is processed
-//     from LDS, then written to the other LDS buffer.
+//     fp32 MFMA accumulators per wave, updated in place by the update product;
+//   * H is produced transposed (H^T = W^T K^T): a lane holds 4 features of
+//     ONE token, so LN row sums are 3 in-lane adds plus a reduce-scatter over
+//     the 4 lane groups (v_permlane16/32_swap);
+//   * LN sums are taken around the shift k . w_bar with w_bar = W 1 / d: the
+//     LN gradient of every token sums to zero over the features, so W 1 is a
+//     constant of the scan and k . w_bar is the exact row mean up to rounding.
+//     The shift comes out of the matrix unit (w_bar as an A operand), so no
+//     serial mean pass precedes the variance;
+//   * the 4 waves exchange 8 partial sums per token per tile through LDS,
+//     behind ONE barrier: 6 for the gradient of tile t and 2 for the output
+//     LN of tile t-1 (the output path runs one tile behind the state chain);
+//   * fp32 operands enter the bf16 matrix unit as hi + lo bf16 pairs (about
+//     16 significant bits); bf16 inputs are exact;
+//   * q, k, v, eta stream from HBM in blocks of 8 tiles: the next block is
+//     loaded into registers while the current one is processed from LDS.
 #include "ttt_device.hpp"
 #include "ttt_kernels.hpp"
 
@@ -44,133 +50,198 @@ template <>
 struct Io<true> {
   using E = uint16_t;
   static constexpr int TB = 8;     // tiles per staged block (128 tokens)
-  static constexpr int ROW = 72;   // LDS row stride in elements (144 B)
   static constexpr int CPR = 8;    // 16-byte chunks per 64-element row
 };
 template <>
 struct Io<false> {
   using E = float;
   static constexpr int TB = 4;     // 64 tokens
-  static constexpr int ROW = 68;   // 272 B
   static constexpr int CPR = 16;
 };
+
+// Staged blocks hold rows of 64 elements without padding; the 16-byte chunk
+// j of row t sits in slot j ^ (t & 7) of the row, which spreads the
+// row-strided operand reads of a 16x16 tile over the LDS banks.
+template <bool BF16>
+__device__ __forceinline__ int lds_off(int t, int col) {  // element offset
+  constexpr int EPC = 16 / sizeof(typename Io<BF16>::E);  // elements per chunk
+  return t * D + (((col / EPC) ^ (t & 7)) * EPC) + (col % EPC);
+}
 
 template <bool BF16>
 struct Lds {
   using E = typename Io<BF16>::E;
   static constexpr int TOK = Io<BF16>::TB * 16;
-  static constexpr int ROW = Io<BF16>::ROW;
-  E qkv[2][3][TOK * ROW];       // staged q, k, v blocks (double buffered)
+  E qkv[2][3][TOK * D];         // staged q, k, v blocks (double buffered)
   float eta[2][TOK];
-  float stats_k[2][16][4][8];   // chain LN partial sums [parity][token][wave]
-  float stats_q[2][16][4][4];   // output LN partial sums
+  // LN partial sums [parity][wave][round][token][quantity slot]: the 16
+  // tokens of one (wave, round) are 16 consecutive 16-byte rows, so the
+  // readers (lane c reads token c) hit distinct banks.
+  f32x4 xch[2][4][2][16];
+  float wbar[D];                // W0 1 / d
 };
 
-// Per-thread registers holding the next staged block.
-template <bool BF16>
-struct Staged {
-  u32x4 r[3][4];
-  float eta;
-};
+#define TTT_LDS __attribute__((address_space(3)))
 
+// Start copying block `blk` (TB tiles) of q, k, v and eta from HBM straight
+// into LDS buffer `buf` (global_load_lds: no registers, no VALU).  Each wave
+// moves 1 KB per instruction; lane l lands at byte 16 l of it, so the lane
+// picks the source chunk that belongs in that swizzled slot.  Rows past T
+// re-read row T-1 (finite data; their eta is ignored by the scan).
 template <bool BF16>
-__device__ __forceinline__ void stage_load(Staged<BF16>& s, const LinearArgs& a,
-                                           size_t row0, int tok0, int T) {
+__device__ __forceinline__ void stage_issue(Lds<BF16>& L, const LinearArgs& a, size_t row0,
+                                            int blk, int T, int buf) {
   using E = typename Io<BF16>::E;
   constexpr int CPR = Io<BF16>::CPR;
-  const int tid = threadIdx.x;
+  constexpr int TOK = Io<BF16>::TB * 16;
+  constexpr int RB = D * sizeof(E);            // row bytes
+  constexpr int NI = TOK * RB / (4 * 1024);    // instructions per wave per tensor
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int tok0 = blk * TOK;
   const char* src[3] = {static_cast<const char*>(a.q), static_cast<const char*>(a.k),
                         static_cast<const char*>(a.v)};
 #pragma unroll
-  for (int t = 0; t < 3; ++t) {
+  for (int n = 0; n < NI; ++n) {
+    const int off = (NI * w + n) * 1024 + 16 * l;   // byte offset in the block
+    const int t = off / RB, slot = (off % RB) / 16;
+    const int j = slot ^ (t & 7);
+    const int tok = min(tok0 + t, T - 1);
+    const size_t goff = (row0 + tok) * (size_t)RB + j * 16;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int id = j * NT + tid;
-      const int row = id / CPR, cc = id % CPR;
-      const int tok = tok0 + row;
-      if (tok < T) {
-        const char* p = src[t] + (row0 + tok) * (size_t)D * sizeof(E) + cc * 16;
-        s.r[t][j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
-      } else {
-        s.r[t][j] = u32x4{0u, 0u, 0u, 0u};
-      }
+    for (int x = 0; x < 3; ++x) {
+      TTT_LDS void* dst = (TTT_LDS void*)(reinterpret_cast<char*>(L.qkv[buf][x]) +
+                                          (NI * w + n) * 1024);
+      __builtin_amdgcn_global_load_lds(src[x] + goff, dst, 16, 0, 0);
     }
   }
-  constexpr int TOK = Io<BF16>::TB * 16;
-  if (tid < TOK) {
-    const int tok = tok0 + tid;
-    s.eta = tok < T ? a.eta[row0 + tok] : 0.0f;
+  if (w * 64 < TOK) {
+    const int tok = min(tok0 + w * 64 + l, T - 1);
+    TTT_LDS void* dst = (TTT_LDS void*)(&L.eta[buf][w * 64]);
+    __builtin_amdgcn_global_load_lds(a.eta + row0 + tok, dst, 4, 0, 0);
   }
+  (void)CPR;
 }
 
-template <bool BF16>
-__device__ __forceinline__ void stage_store(const Staged<BF16>& s, Lds<BF16>& L, int buf) {
-  using E = typename Io<BF16>::E;
-  constexpr int CPR = Io<BF16>::CPR;
-  constexpr int ROW = Io<BF16>::ROW;
-  const int tid = threadIdx.x;
-#pragma unroll
-  for (int t = 0; t < 3; ++t) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int id = j * NT + tid;
-      const int row = id / CPR, cc = id % CPR;
-      char* p = reinterpret_cast<char*>(L.qkv[buf][t]) + (row * ROW) * sizeof(E) + cc * 16;
-      *reinterpret_cast<u32x4*>(p) = s.r[t][j];
-    }
-  }
-  constexpr int TOK = Io<BF16>::TB * 16;
-  if (tid < TOK) L.eta[buf][tid] = s.eta;
-}
+// Wait for this wave's outstanding global->LDS copies (and stores).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
-// Four consecutive elements of one LDS row as float, plus their bf16 hi/lo.
-struct Frag4 {
-  f32x4 f;
+// ---- LDS operand fetch ---------------------------------------------------
+// Four consecutive elements of one row as bf16 hi (and lo for fp32 data).
+struct Op4 {
   u32x2 hi, lo;
 };
+__device__ __forceinline__ Op4 op4(const uint16_t* p) {
+  return Op4{*reinterpret_cast<const u32x2*>(p), u32x2{0u, 0u}};
+}
+__device__ __forceinline__ Op4 op4(const float* p) {
+  const Split4 s = split4(*reinterpret_cast<const f32x4*>(p));
+  return Op4{s.hi, s.lo};
+}
+__device__ __forceinline__ Op4 op4_of(f32x4 v) {
+  const Split4 s = split4(v);
+  return Op4{s.hi, s.lo};
+}
+__device__ __forceinline__ Op4 op4_of(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3) {
+  return Op4{u32x2{e0 | (e1 << 16), e2 | (e3 << 16)}, u32x2{0u, 0u}};
+}
+// Four consecutive elements of one row as fp32.
+__device__ __forceinline__ f32x4 val4(const uint16_t* p) {
+  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
+  return f32x4{bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y),
+               bf16_hi_to_f32(w.y)};
+}
+__device__ __forceinline__ f32x4 val4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
 
-__device__ __forceinline__ Frag4 frag4(const uint16_t* p) {
-  Frag4 r;
-  r.hi = *reinterpret_cast<const u32x2*>(p);
-  r.lo = u32x2{0u, 0u};
-  r.f = f32x4{bf16_lo_to_f32(r.hi.x), bf16_hi_to_f32(r.hi.x), bf16_lo_to_f32(r.hi.y),
-              bf16_hi_to_f32(r.hi.y)};
-  return r;
-}
-__device__ __forceinline__ Frag4 frag4(const float* p) {
-  Frag4 r;
-  r.f = *reinterpret_cast<const f32x4*>(p);
-  Split4 s = split4(r.f);
-  r.hi = s.hi;
-  r.lo = s.lo;
-  return r;
+// The 4 accumulator registers of two 16x16 tiles of X, split into bf16 hi/lo
+// and laid out as 16x16x32 operands: slot j < 4 -> tile a element j, slot
+// j >= 4 -> tile b element j - 4.
+struct Op8 {
+  u32x4 hi, lo;
+};
+__device__ __forceinline__ Op8 split_pair(f32x4 a, f32x4 b) {
+  const Split4 sa = split4(a), sb = split4(b);
+  return Op8{cat(sa.hi, sb.hi), cat(sa.lo, sb.lo)};
 }
 
-// Four elements of one LDS column (stride `row` elements).
-__device__ __forceinline__ Frag4 frag4_col(const uint16_t* p, int row) {
-  Frag4 r;
-  uint32_t e0 = p[0], e1 = p[row], e2 = p[2 * row], e3 = p[3 * row];
-  r.hi = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-  r.lo = u32x2{0u, 0u};
-  r.f = f32x4{bf16_lo_to_f32(r.hi.x), bf16_hi_to_f32(r.hi.x), bf16_lo_to_f32(r.hi.y),
-              bf16_hi_to_f32(r.hi.y)};
+// acc + A B over hi/lo parts: hi*hi, plus lo*hi when A has a lo part, plus
+// hi*lo when B has one (the lo*lo term is below the split's precision).
+template <bool ALO, bool BLO>
+__device__ __forceinline__ f32x4 mma8(const Op8& a, const Op8& b, f32x4 acc) {
+  acc = mfma32(a.hi, b.hi, acc);
+  if (ALO) acc = mfma32(a.lo, b.hi, acc);
+  if (BLO) acc = mfma32(a.hi, b.lo, acc);
+  return acc;
+}
+
+// Rows c of a staged 16-token tile at features 32p + 4g + (0..3) and
+// 32p + 16 + 4g + (0..3): the B operand of X^T (16x16x32, slots matching
+// split_pair of two state tiles) and the A / B operand of X X'^T.
+struct Rows {
+  Op8 p[2];
+};
+template <bool BF16>
+__device__ __forceinline__ Rows load_rows(const typename Io<BF16>::E* X, int t0, int c, int g) {
+  Rows r;
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const Op4 a = op4(X + lds_off<BF16>(t0 + c, 32 * p + 4 * g));
+    const Op4 b = op4(X + lds_off<BF16>(t0 + c, 32 * p + 16 + 4 * g));
+    r.p[p] = Op8{cat(a.hi, b.hi), cat(a.lo, b.lo)};
+  }
   return r;
 }
-__device__ __forceinline__ Frag4 frag4_col(const float* p, int row) {
-  Frag4 r;
-  r.f = f32x4{p[0], p[row], p[2 * row], p[3 * row]};
-  Split4 s = split4(r.f);
-  r.hi = s.hi;
-  r.lo = s.lo;
-  return r;
+// K^T of a staged tile as 16x16x16 A operands: kt[r] lane (g,c) holds
+// K[t0 + 4g + i][16r + c].
+template <bool BF16>
+__device__ __forceinline__ void load_cols(Op4 kt[4], const typename Io<BF16>::E* X, int t0, int c,
+                                          int g) {
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const auto e0 = X[lds_off<BF16>(t0 + 4 * g + 0, 16 * r + c)];
+    const auto e1 = X[lds_off<BF16>(t0 + 4 * g + 1, 16 * r + c)];
+    const auto e2 = X[lds_off<BF16>(t0 + 4 * g + 2, 16 * r + c)];
+    const auto e3 = X[lds_off<BF16>(t0 + 4 * g + 3, 16 * r + c)];
+    if constexpr (BF16) kt[r] = op4_of(e0, e1, e2, e3);
+    else kt[r] = op4_of(f32x4{e0, e1, e2, e3});
+  }
+}
+// The state W (four accumulator tiles of one wave) as A operands of W^T.
+__device__ __forceinline__ void split_state(Op8 A[2], const f32x4 W[4]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) A[p] = split_pair(W[2 * p], W[2 * p + 1]);
+}
+// X W for the wave's 16 output columns, transposed: lane (g,c) gets
+// (X W)[row c][16w + 4g + i].
+template <bool LO>
+__device__ __forceinline__ f32x4 times_state(const Op8 A[2], const Rows& X) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < 2; ++p) acc = mma8<true, LO>(A[p], X.p[p], acc);
+  return acc;
+}
+// X Y^T in accumulator layout: lane (g,c) gets x_{4g+i} . y_c.
+template <bool LO>
+__device__ __forceinline__ f32x4 gram(const Rows& X, const Rows& Y) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < 2; ++p) acc = mma8<LO, LO>(X.p[p], Y.p[p], acc);
+  return acc;
+}
+// acc + (-eta G)^T S for a 16x16 token-by-token tile S (accumulator layout,
+// split here): the correction products of the chunked form.
+__device__ __forceinline__ f32x4 correct(const Op4& gt, f32x4 S, f32x4 acc) {
+  const Split4 sp = split4(S);
+  acc = mfma16(gt.hi, sp.hi, acc);
+  acc = mfma16(gt.lo, sp.hi, acc);
+  acc = mfma16(gt.hi, sp.lo, acc);
+  return acc;
 }
 
 template <bool BF16, bool LN, bool RES, bool MB16>
-__global__ __launch_bounds__(NT) void ttt_linear_fwd(LinearArgs a) {
+__global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
   using E = typename Io<BF16>::E;
   constexpr int TB = Io<BF16>::TB;
-  constexpr int ROW = Io<BF16>::ROW;
-  constexpr int TOK = TB * 16;
+  constexpr bool LO = !BF16;  // inputs carry a lo part (fp32 data)
   __shared__ Lds<BF16> L;
 
   const int tid = threadIdx.x;
@@ -181,25 +252,23 @@ __global__ __launch_bounds__(NT) void ttt_linear_fwd(LinearArgs a) {
   const int unit = blockIdx.x;     // (batch, head)
   const int head = unit % a.H;
   const int T = a.T;
+  const int tpm = MB16 ? 1 : a.tiles_per_mb;
   const size_t row0 = (size_t)unit * T;
+  const int fo = 16 * w + 4 * g;   // transposed tiles: lane holds token c, features fo..fo+3
 
-  // ---- prologue: state, LN parameters --------------------------------
+  // ---- prologue ---------------------------------------------------------
   // Wc[r] lane (g,c) = W[16r + 4g + i][16w + c]
-  f32x4 Wc[4], Wb[4];
-  {
-    const float* w0 = a.w0 + (size_t)(a.state0_per_batch ? unit : head) * D * D;
+  f32x4 Wc[4];
+  const float* w0 = a.w0 + (size_t)(a.state0_per_batch ? unit : head) * D * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+  for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Wc[r][i] = w0[(16 * r + 4 * g + i) * D + 16 * w + c];
-  }
-#pragma unroll
-  for (int r = 0; r < 4; ++r) Wb[r] = Wc[r];
+    for (int i = 0; i < 4; ++i) Wc[r][i] = w0[(16 * r + 4 * g + i) * D + 16 * w + c];
 
-  // lane (g,c) works on features fo..fo+3 of token c in the transposed tiles
-  const int fo = 16 * w + 4 * g;
-  f32x4 gam = {1.f, 1.f, 1.f, 1.f}, bet = {0.f, 0.f, 0.f, 0.f}, gam2 = gam;
-  float Gam[4] = {16.f, 16.f, 16.f, 16.f};  // sum of gamma^2 over each wave's columns
+  f32x4 gam = {1.f, 1.f, 1.f, 1.f}, bet = {0.f, 0.f, 0.f, 0.f};
+  f32x4 g2x2 = {2.f, 2.f, 2.f, 2.f}, twog = g2x2, twogb = bet;
+  float Gam = 64.f;  // sum of gamma^2 over the features
+  u32x4 wbar[2] = {};  // w_bar (bf16) as a 16x16x32 A operand (every row the same)
   if (LN) {
     const float* gp = a.gamma + (size_t)head * D;
     const float* bp = a.beta + (size_t)head * D;
@@ -207,16 +276,22 @@ __global__ __launch_bounds__(NT) void ttt_linear_fwd(LinearArgs a) {
     for (int i = 0; i < 4; ++i) {
       gam[i] = gp[fo + i];
       bet[i] = bp[fo + i];
-      gam2[i] = gam[i] * gam[i];
+      g2x2[i] = 2.f * gam[i] * gam[i];
+      twog[i] = 2.f * gam[i];
+      twogb[i] = 2.f * gam[i] * bet[i];
     }
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    Gam = 0.f;
+    for (int j = 0; j < D; ++j) Gam += gp[j] * gp[j];
+    if (tid < D) {
       float s = 0.f;
-      for (int j = 0; j < 16; ++j) s += gp[16 * ww + j] * gp[16 * ww + j];
-      Gam[ww] = s;
+      for (int j = 0; j < D; ++j) s += w0[tid * D + j];
+      L.wbar[tid] = s * (1.0f / D);
     }
   }
-
+  // causal mask of the 16x16 score tile: lane holds M[s = 4g+i][t = c]
+  bool causal[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) causal[i] = (4 * g + i) <= c;
   // identity as a 16x16x16 B operand: lane (g,c) holds I[4g + i][c]
   u32x2 ident;
   {
@@ -227,249 +302,271 @@ __global__ __launch_bounds__(NT) void ttt_linear_fwd(LinearArgs a) {
   }
 
   const int n_tiles = (T + 15) / 16;
-  const int n_blocks = (n_tiles + TB - 1) / TB;
+  stage_issue<BF16>(L, a, row0, 0, T, 0);
+  wait_vmem();
+  lds_barrier();
+  if (LN) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) {
+      const f32x4 m0 = *reinterpret_cast<const f32x4*>(&L.wbar[32 * p + 4 * g]);
+      const f32x4 m1 = *reinterpret_cast<const f32x4*>(&L.wbar[32 * p + 16 + 4 * g]);
+      wbar[p] = split_pair(m0, m1).hi;  // a shift need not be exact
+    }
+  }
 
-  Staged<BF16> st;
-  stage_load<BF16>(st, a, row0, 0, T);
-  stage_store<BF16>(st, L, 0);
-  __syncthreads();
-  if (n_blocks > 1) stage_load<BF16>(st, a, row0, TOK, T);
+  // Carried from tile to tile (t is the tile of the current iteration):
+  //   Wc       state before the pending update of tile t-1 (zero at t = 0)
+  //   gt, kt   the pending update of tile t-1: W -= K^T (eta G)
+  //   bk       K_t times the state before that update
+  //   pm       K_{t-1} K_t^T, to correct bk by the pending update
+  //   mu4      K_t w_bar, the LN shift of tile t
+  //   Ab       gradient point of the current mini-batch (mini-batches of
+  //            several tiles; otherwise the state itself)
+  // Everything for tile t+1 is formed before tile t's barrier from data
+  // that does not depend on tile t's gradient, so the serial chain per tile
+  // is: correction -> LN sums -> exchange -> gradient -> transpose.
+  Op8 Ab[2];
+  Op4 gt = {}, kt[4] = {};
+  Rows kb = load_rows<BF16>(L.qkv[0][1], 0, c, g);
+  f32x4 bk, pm = {0.f, 0.f, 0.f, 0.f}, mu4 = pm;
+  split_state(Ab, Wc);
+  bk = times_state<LO>(Ab, kb);
+  if (LN) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p) mu4 = mfma32(wbar[p], kb.p[p].hi, mu4);
+  }
+  // output path of the previous tile
+  f32x4 hq_prev = {0.f, 0.f, 0.f, 0.f}, qb_prev = hq_prev;
+  float muq_prev = 0.f;
+  int tok_prev = -1;
 
-  for (int blk = 0; blk < n_blocks; ++blk) {
+  for (int blk = 0; blk * TB < n_tiles; ++blk) {
     const int buf = blk & 1;
+    const bool next_block = (blk + 1) * TB < n_tiles;
     const E* Lq = L.qkv[buf][0];
     const E* Lk = L.qkv[buf][1];
     const E* Lv = L.qkv[buf][2];
+#pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int tile = blk * TB + tb;
       if (tile >= n_tiles) break;
       const int par = tile & 1;
-      if (!MB16 && (tile % a.tiles_per_mb) == 0) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Wb[r] = Wc[r];
-      }
-      const E* Kt = Lk + tb * 16 * ROW;
-      const E* Qt = Lq + tb * 16 * ROW;
-      const E* Vt = Lv + tb * 16 * ROW;
-      const int tok = tile * 16 + c;     // this lane's token (transposed layout)
-      const bool valid = tok < T;
-      const float eta = L.eta[buf][tb * 16 + c];
+      const int t0 = tb * 16;               // first row of the tile in the block
+      const int tok = tile * 16 + c;
+      const bool mb_start = MB16 || (tile % tpm) == 0;
+      const bool mb_start_next = MB16 || ((tile + 1) % tpm) == 0;
+      // the next block must be visible by the barrier of this tile, for the
+      // lookahead of the block's last tile
+      if (tb == TB - 2 && next_block) wait_vmem();
 
-      // ---- operands from LDS ------------------------------------------
-      Frag4 kc[4], qc[4], kt[4];
+      // ===== [A] gradient point of tile t: K_t W_t = K_t W_{t-1} - (K_t K_{t-1}^T)(eta G)_{t-1}
+      f32x4 hk = mb_start ? correct(gt, pm, bk) : bk;
+      const float eta = L.eta[buf][t0 + c];
+      const f32x4 kres = val4(Lk + lds_off<BF16>(t0 + c, fo));
+      const f32x4 vres = val4(Lv + lds_off<BF16>(t0 + c, fo));
+
+      // ===== [B] independent of tile t's gradient: pending update, output
+      //       products of tile t, products for tile t+1
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        kc[r] = frag4(Kt + c * ROW + 16 * r + 4 * g);          // K[c][16r+4g+i]
-        qc[r] = frag4(Qt + c * ROW + 16 * r + 4 * g);          // Q[c][16r+4g+i]
-        kt[r] = frag4_col(Kt + (4 * g) * ROW + 16 * r + c, ROW);  // K[4g+i][16r+c]
+        Wc[r] = mfma16(kt[r].hi, gt.hi, Wc[r]);
+        Wc[r] = mfma16(kt[r].hi, gt.lo, Wc[r]);
+        if (LO) Wc[r] = mfma16(kt[r].lo, gt.hi, Wc[r]);
       }
-      const f32x4 kres = frag4(Kt + c * ROW + fo).f;
-      const f32x4 qres = frag4(Qt + c * ROW + fo).f;
-      const f32x4 vres = frag4(Vt + c * ROW + fo).f;
-      // K and Q rows c, features 32p + 8g + j, as 16x16x32 operands
-      u32x4 krow_hi[2], krow_lo[2], qrow_hi[2], qrow_lo[2];
-#pragma unroll
-      for (int p = 0; p < 2; ++p) {
-        Frag4 k0 = frag4(Kt + c * ROW + 32 * p + 8 * g);
-        Frag4 k1 = frag4(Kt + c * ROW + 32 * p + 8 * g + 4);
-        Frag4 q0 = frag4(Qt + c * ROW + 32 * p + 8 * g);
-        Frag4 q1 = frag4(Qt + c * ROW + 32 * p + 8 * g + 4);
-        krow_hi[p] = cat(k0.hi, k1.hi);
-        krow_lo[p] = cat(k0.lo, k1.lo);
-        qrow_hi[p] = cat(q0.hi, q1.hi);
-        qrow_lo[p] = cat(q0.lo, q1.lo);
+      Op8 Ac[2];
+      split_state(Ac, Wc);                   // W_t
+      if (!MB16 && mb_start) {
+        Ab[0] = Ac[0];
+        Ab[1] = Ac[1];
       }
-
-      // ---- split the state into bf16 hi/lo operands ----------------------
-      // A[r] as the A operand of W^T: slot j<4 -> hi of W[16r+4g+j][16w+c],
-      // slot j>=4 -> lo of the same element.
-      u32x4 Ab[4], Ac[4];
+      const Rows qr = load_rows<BF16>(Lq, t0, c, g);
+      const f32x4 qres = val4(Lq + lds_off<BF16>(t0 + c, fo));
+      const f32x4 hqb = times_state<LO>(Ac, qr);       // (Q_t W_t)^T
+      f32x4 M = gram<LO>(kb, qr);                      // K_t Q_t^T
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        Split4 s = split4(MB16 ? Wc[r] : Wb[r]);
-        Ab[r] = cat(s.hi, s.lo);
-      }
-      if (MB16) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) Ac[r] = Ab[r];
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          Split4 s = split4(Wc[r]);
-          Ac[r] = cat(s.hi, s.lo);
-        }
-      }
-
-      // ---- H_k^T = W_base^T K^T  (lane: token c, features fo..fo+3) -----
-      f32x4 hk = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hk = mfma32(Ab[r], cat(kc[r].hi, kc[r].hi), hk);
-        if (!BF16) hk = mfma32(Ab[r], cat(kc[r].lo, kc[r].lo), hk);
-      }
-
-      // ---- gradient factor G (dl/dh of token c) ------------------------
-      f32x4 G;
+      for (int i = 0; i < 4; ++i)
+        if (!causal[i]) M[i] = 0.f;
+      float muq = 0.f;
       if (LN) {
-        const float s1 = group_sum(hk[0] + hk[1] + hk[2] + hk[3]);
-        const float mw = s1 * (1.0f / 16.0f);
-        f32x4 e, u;
+        f32x4 m4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int p = 0; p < 2; ++p) m4 = mfma32(wbar[p], qr.p[p].hi, m4);
+        muq = m4[0];
+      }
+      load_cols<BF16>(kt, Lk, t0, c, g);              // K_t^T, for the next update
+      // tile t+1 (first tile of the next buffer after the last of this block;
+      // past the end the products are formed from stale data and unused)
+      const bool wrap = tb == TB - 1;
+      const Rows kn = load_rows<BF16>(wrap ? L.qkv[buf ^ 1][1] : Lk, wrap ? 0 : t0 + 16, c, g);
+      const f32x4 bk_next = times_state<LO>(mb_start_next ? Ac : Ab, kn);
+      const f32x4 pm_next = mb_start_next ? gram<LO>(kb, kn) : pm;
+      f32x4 mu_next = {0.f, 0.f, 0.f, 0.f};
+      if (LN) {
+#pragma unroll
+        for (int p = 0; p < 2; ++p) mu_next = mfma32(wbar[p], kn.p[p].hi, mu_next);
+      }
+
+      // ===== [C] local LN sums: gradient of tile t, output of tile t-1
+      f32x4 ep = {0.f, 0.f, 0.f, 0.f}, u = ep, eq = ep;
+      float S[8];
+      if (LN) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          e[i] = hk[i] - mw;
-          u[i] = 2.0f * gam[i] * ((RES ? kres[i] : 0.0f) + bet[i] - vres[i]);
+          ep[i] = hk[i] - mu4[0];
+          u[i] = __builtin_fmaf(twog[i], (RES ? kres[i] : 0.f) - vres[i], twogb[i]);
+          eq[i] = hq_prev[i] - muq_prev;
         }
-        float P = 0.f, A = 0.f, Bq = 0.f, C = 0.f, U = 0.f;
+        f32x4 ge;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          P += e[i] * e[i];
-          A += gam2[i] * e[i];
-          Bq += u[i] * e[i];
-          C += gam2[i] * e[i] * e[i];
-          U += u[i];
+        for (int i = 0; i < 4; ++i) ge[i] = gam[i] * gam[i] * ep[i];
+        const float q0 = (ep[0] + ep[1]) + (ep[2] + ep[3]);
+        const float q2 = (ge[0] + ge[1]) + (ge[2] + ge[3]);
+        const float q5 = (u[0] + u[1]) + (u[2] + u[3]);
+        const float q6 = (eq[0] + eq[1]) + (eq[2] + eq[3]);
+        float q1 = ep[0] * ep[0], q3 = ge[0] * ep[0], q4 = u[0] * ep[0], q7 = eq[0] * eq[0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) {
+          q1 = __builtin_fmaf(ep[i], ep[i], q1);
+          q3 = __builtin_fmaf(ge[i], ep[i], q3);
+          q4 = __builtin_fmaf(u[i], ep[i], q4);
+          q7 = __builtin_fmaf(eq[i], eq[i], q7);
         }
-        P = group_sum(P);
-        A = group_sum(A);
-        Bq = group_sum(Bq);
-        C = group_sum(C);
-        U = group_sum(U);
-        if (g == 0) {
-          f32x4* dst = reinterpret_cast<f32x4*>(L.stats_k[par][c][w]);
-          dst[0] = f32x4{s1, P, A, Bq};
-          dst[1] = f32x4{C, U, 0.f, 0.f};
-        }
-        __syncthreads();
-        f32x4 s0[4], s1v[4];
+        // ===== [D] exchange across the 4 waves
+        const float r1 = group_reduce_scatter4(q0, q1, q2, q3);
+        const float r2 = group_reduce_scatter4(q4, q5, q6, q7);
+        reinterpret_cast<float*>(&L.xch[par][w][0][c])[rs4_slot(g)] = r1;
+        reinterpret_cast<float*>(&L.xch[par][w][1][c])[rs4_slot(g)] = r2;
+        lds_barrier();
+        f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = s1;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-          const f32x4* src = reinterpret_cast<const f32x4*>(L.stats_k[par][c][ww]);
-          s0[ww] = src[0];
-          s1v[ww] = src[1];
+          s1 += L.xch[par][ww][0][c];
+          s2 += L.xch[par][ww][1][c];
         }
-        const float mu = (s0[0][0] + s0[1][0] + s0[2][0] + s0[3][0]) * (1.0f / 64.0f);
-        float M2 = 0.f, SgE = 0.f, SuE = 0.f, SgE2 = 0.f, Su = 0.f, dme = 0.f;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-          const float dl = s0[ww][0] * (1.0f / 16.0f) - mu;   // local mean - mean
-          M2 += s0[ww][1] + 16.0f * dl * dl;
-          SgE += s0[ww][2] + dl * Gam[ww];
-          SuE += s0[ww][3] + dl * s1v[ww][1];
-          SgE2 += s1v[ww][0] + 2.0f * dl * s0[ww][2] + dl * dl * Gam[ww];
-          Su += s1v[ww][1];
-          if (ww == w) dme = dl;
+        for (int j = 0; j < 4; ++j) {
+          S[j] = s1[j];
+          S[4 + j] = s2[j];
         }
-        const float rs = __frsqrt_rn(M2 * (1.0f / 64.0f) + a.eps);
-        const float ma = (Su + 2.0f * rs * SgE) * (1.0f / 64.0f);
-        const float max = (rs * SuE + 2.0f * rs * rs * SgE2) * (1.0f / 64.0f);
+      } else if (tb == TB - 2 && next_block) {
+        lds_barrier();                       // publish the next block
+      }
+
+      // ===== [E] finish the previous tile's output
+      {
+        f32x4 zf;
+        if (LN) {
+          const float mr = S[6] * (1.0f / D);
+          const float var = __builtin_fmaf(-mr, mr, S[7] * (1.0f / D));
+          const float rs = __frsqrt_rn(var + a.eps);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zf[i] = __builtin_fmaf(gam[i] * rs, eq[i] - mr, qb_prev[i]);
+        } else {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) zf[i] = qb_prev[i] + hq_prev[i];
+        }
+        if (tok_prev >= 0 && tok_prev < T) {
+          if (BF16) {
+            const u32x2 o = {pack_bf16(zf[0], zf[1]), pack_bf16(zf[2], zf[3])};
+            *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.z) + (row0 + tok_prev) * D + fo) = o;
+          } else {
+            *reinterpret_cast<f32x4*>(static_cast<float*>(a.z) + (row0 + tok_prev) * D + fo) = zf;
+          }
+        }
+      }
+
+      // ===== [F] gradient of tile t, transposed on the matrix unit
+      const bool valid = tok < T;
+      f32x4 eg;
+      if (LN) {
+        const float mr = S[0] * (1.0f / D);
+        const float var = __builtin_fmaf(-mr, mr, S[1] * (1.0f / D));
+        const float rs = __frsqrt_rn(var + a.eps);
+        const float sge = __builtin_fmaf(-mr, Gam, S[2]);
+        const float sue = __builtin_fmaf(-mr, S[5], S[4]);
+        const float sge2 = __builtin_fmaf(mr * mr, Gam, __builtin_fmaf(-2.f * mr, S[2], S[3]));
+        float ma = (S[5] + 2.f * rs * sge) * (1.0f / D);
+        float mx = (rs * sue + 2.f * rs * rs * sge2) * (1.0f / D);
+        float c1 = -eta * rs, c2 = -eta * rs * rs;
+        if (!valid) ma = mx = c1 = c2 = 0.f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float xh = (e[i] + dme) * rs;
-          const float av = u[i] + 2.0f * gam2[i] * xh;
-          G[i] = rs * (av - ma - xh * max);
+          const float e = ep[i] - mr;
+          eg[i] = __builtin_fmaf(c1, u[i] - ma, c2 * (e * (g2x2[i] - mx)));
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) G[i] = 2.0f * (hk[i] + (RES ? kres[i] : 0.0f) - vres[i]);
+        for (int i = 0; i < 4; ++i)
+          eg[i] = valid ? -2.f * eta * (hk[i] + (RES ? kres[i] : 0.f) - vres[i]) : 0.f;
       }
-
-      // -eta * G, zero for padding tokens past T
-      f32x4 eg;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) eg[i] = valid ? -eta * G[i] : 0.0f;
-
-      // ---- transpose -eta*G on the matrix unit: lane gets token 4g+i,
-      //      column 16w+c; slots j<4 hi, j>=4 lo -----------------------------
-      u32x4 gop;
       {
         const Split4 s = split4(eg);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         const f32x4 th = mfma16(s.hi, ident, zero);
         const f32x4 tl = mfma16(s.lo, ident, zero);
-        gop = u32x4{pack_bf16(th[0], th[1]), pack_bf16(th[2], th[3]), pack_bf16(tl[0], tl[1]),
-                    pack_bf16(tl[2], tl[3])};
+        gt.hi = u32x2{pack_bf16(th[0], th[1]), pack_bf16(th[2], th[3])};
+        gt.lo = u32x2{pack_bf16(tl[0], tl[1]), pack_bf16(tl[2], tl[3])};
       }
 
-      // ---- output pre-activation H_q^T = W^T Q^T - (eta G)^T tril(Q K^T)^T
-      f32x4 hq = {0.f, 0.f, 0.f, 0.f};
+      // ===== [G] output pre-activation of tile t; carry to tile t+1
+      hq_prev = correct(gt, M, hqb);         // H_q^T = (Q W_t)^T + (-eta G)^T tril(K Q^T)
+      muq_prev = muq;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        hq = mfma32(Ac[r], cat(qc[r].hi, qc[r].hi), hq);
-        if (!BF16) hq = mfma32(Ac[r], cat(qc[r].lo, qc[r].lo), hq);
-      }
-      {
-        // M = K Q^T: lane (g,c) holds M[s = 4g+i][t = c] = k_s . q_t
-        f32x4 m = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int p = 0; p < 2; ++p) {
-          m = mfma32(krow_hi[p], qrow_hi[p], m);
-          if (!BF16) {
-            m = mfma32(krow_hi[p], qrow_lo[p], m);
-            m = mfma32(krow_lo[p], qrow_hi[p], m);
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (4 * g + i > c) m[i] = 0.0f;                 // causal: s <= t
-        const Split4 ms = split4(m);
-        hq = mfma32(gop, cat(ms.hi, ms.hi), hq);
-        hq = mfma32(gop, cat(ms.lo, ms.lo), hq);
-      }
+      for (int i = 0; i < 4; ++i) qb_prev[i] = (RES ? qres[i] : 0.f) + (LN ? bet[i] : 0.f);
+      tok_prev = tok;
+      bk = bk_next;
+      pm = pm_next;
+      mu4 = mu_next;
+      kb = kn;
 
-      // ---- state update W <- W - K^T (eta G) ---------------------------
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        Wc[r] = mfma32(cat(kt[r].hi, kt[r].hi), gop, Wc[r]);
-        if (!BF16) Wc[r] = mfma32(cat(kt[r].lo, kt[r].lo), gop, Wc[r]);
-      }
-
-      // ---- output: Z = Q + LN(H_q) ------------------------------------
-      f32x4 zf;
-      if (LN) {
-        const float s1 = group_sum(hq[0] + hq[1] + hq[2] + hq[3]);
-        const float mw = s1 * (1.0f / 16.0f);
-        f32x4 e;
-        float P = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          e[i] = hq[i] - mw;
-          P += e[i] * e[i];
-        }
-        P = group_sum(P);
-        if (g == 0) *reinterpret_cast<f32x4*>(L.stats_q[par][c][w]) = f32x4{s1, P, 0.f, 0.f};
-        __syncthreads();
-        f32x4 sq[4];
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) sq[ww] = *reinterpret_cast<const f32x4*>(L.stats_q[par][c][ww]);
-        const float mu = (sq[0][0] + sq[1][0] + sq[2][0] + sq[3][0]) * (1.0f / 64.0f);
-        float M2 = 0.f, dme = 0.f;
-#pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
-          const float dl = sq[ww][0] * (1.0f / 16.0f) - mu;
-          M2 += sq[ww][1] + 16.0f * dl * dl;
-          if (ww == w) dme = dl;
-        }
-        const float rs = __frsqrt_rn(M2 * (1.0f / 64.0f) + a.eps);
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          zf[i] = (RES ? qres[i] : 0.0f) + gam[i] * ((e[i] + dme) * rs) + bet[i];
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zf[i] = (RES ? qres[i] : 0.0f) + hq[i];
-      }
-      if (valid) {
-        if (BF16) {
-          u32x2 o = {pack_bf16(zf[0], zf[1]), pack_bf16(zf[2], zf[3])};
-          *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.z) + (row0 + tok) * D + fo) = o;
-        } else {
-          *reinterpret_cast<f32x4*>(static_cast<float*>(a.z) + (row0 + tok) * D + fo) = zf;
-        }
+      // refill the other buffer once every wave is past the previous block
+      if (tb == 0 && next_block) {
+        if (!LN) lds_barrier();
+        stage_issue<BF16>(L, a, row0, blk + 1, T, buf ^ 1);
       }
     }  // tiles of the block
+  }
 
-    if (blk + 1 < n_blocks) {
-      stage_store<BF16>(st, L, buf ^ 1);
-      __syncthreads();
-      if (blk + 2 < n_blocks) stage_load<BF16>(st, a, row0, (blk + 2) * TOK, T);
+  // ---- drain: last update and the last tile's output --------------------
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    Wc[r] = mfma16(kt[r].hi, gt.hi, Wc[r]);
+    Wc[r] = mfma16(kt[r].hi, gt.lo, Wc[r]);
+    if (LO) Wc[r] = mfma16(kt[r].lo, gt.hi, Wc[r]);
+  }
+  {
+    f32x4 zf;
+    if (LN) {
+      f32x4 eq;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) eq[i] = hq_prev[i] - muq_prev;
+      const float q6 = (eq[0] + eq[1]) + (eq[2] + eq[3]);
+      float q7 = eq[0] * eq[0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) q7 = __builtin_fmaf(eq[i], eq[i], q7);
+      const int par = n_tiles & 1;
+      const float r2 = group_reduce_scatter4(0.f, 0.f, q6, q7);
+      reinterpret_cast<float*>(&L.xch[par][w][1][c])[rs4_slot(g)] = r2;
+      lds_barrier();
+      f32x4 s2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ww = 0; ww < 4; ++ww) s2 += L.xch[par][ww][1][c];
+      const float mr = s2[2] * (1.0f / D);
+      const float var = __builtin_fmaf(-mr, mr, s2[3] * (1.0f / D));
+      const float rs = __frsqrt_rn(var + a.eps);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zf[i] = __builtin_fmaf(gam[i] * rs, eq[i] - mr, qb_prev[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zf[i] = qb_prev[i] + hq_prev[i];
+    }
+    if (tok_prev < T) {
+      if (BF16) {
+        const u32x2 o = {pack_bf16(zf[0], zf[1]), pack_bf16(zf[2], zf[3])};
+        *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.z) + (row0 + tok_prev) * D + fo) = o;
+      } else {
+        *reinterpret_cast<f32x4*>(static_cast<float*>(a.z) + (row0 + tok_prev) * D + fo) = zf;
+      }
     }
   }
 

@@ -144,6 +144,20 @@ def test_linear_output_split_identity():
     assert np.abs(lhs - rhs).max() <= 1e-12 * np.abs(lhs).max()
 
 
+def test_linear_lookahead_identity():
+    """K_t W_t == K_t W_{t-1} - (K_t K_{t-1}^T)(eta G)_{t-1}: the product for
+    the next tile can be formed before the current tile's gradient is known
+    and corrected afterwards with a 16x16 score tile."""
+    rng = np.random.default_rng(75)
+    Kp, Kt, G, W = (rng.standard_normal(s) for s in ((16, 8), (16, 8), (16, 8), (8, 8)))
+    E = rng.random(16)
+    EG = E[:, None] * G
+    Wn = W - Kp.T @ EG
+    lhs = Kt @ Wn
+    rhs = Kt @ W - (Kt @ Kp.T) @ EG
+    assert np.abs(lhs - rhs).max() <= 1e-12 * np.abs(lhs).max()
+
+
 @pytest.mark.parametrize("T", [48, 45])
 def test_mlp_chunk_form_matches_oracle(T):
     rng = np.random.default_rng(74)

@@ -89,9 +89,11 @@ def test_eps_and_per_batch_state():
     _check("eps=1e-5 per-batch W0", inp, "bf16", eps=1e-5, state0_per_batch=True)
 
 
-def test_resume_is_exact_and_in_place():
-    """forward(0:T) == forward(T1:T) started from forward(0:T1)'s state,
-    bit for bit, including the in-place form (w_out is w0)."""
+def test_resume_and_in_place():
+    """forward(0:T) vs forward(T1:T) started from forward(0:T1)'s final
+    state: equal up to rounding (the LN shift is recomputed from the carried
+    state's row sums), and the in-place form (w_out is w0) gives exactly the
+    out-of-place result."""
     w = WORKLOADS["linear_125m_b8h12_t2k"]
     inp = make_inputs(w, B=2, H=3, T=256)
     dev = {k: to_dev(v, "bf16" if k in "qkv" else None) for k, v in inp.items()}
@@ -101,12 +103,17 @@ def test_resume_is_exact_and_in_place():
     part = lambda x, a, b: x[:, :, a:b].contiguous()
     z1, w1 = ttt_linear_forward(*(part(dev[x], 0, T1) for x in "qkv"),
                                 part(dev["eta"], 0, T1), dev["w0"], dev["gamma"], dev["beta"])
-    z2, w2 = ttt_linear_forward(*(part(dev[x], T1, 256) for x in "qkv"),
-                                part(dev["eta"], T1, 256), w1, dev["gamma"], dev["beta"],
-                                state0_per_batch=True, w_out=w1)
+    tail = [part(dev[x], T1, 256) for x in "qkv"] + [part(dev["eta"], T1, 256)]
+    z2, w2 = ttt_linear_forward(*tail, w1, dev["gamma"], dev["beta"], state0_per_batch=True)
+    w1c = w1.clone()
+    z3, w3 = ttt_linear_forward(*tail, w1c, dev["gamma"], dev["beta"], state0_per_batch=True,
+                                w_out=w1c)
     torch.cuda.synchronize()
-    assert torch.equal(torch.cat([z1, z2], dim=2), z)
-    assert torch.equal(w2, wf) and w2.data_ptr() == w1.data_ptr()
+    assert torch.equal(z1, z[:, :, :T1])
+    assert torch.equal(z3, z2) and torch.equal(w3, w2) and w3.data_ptr() == w1c.data_ptr()
+    zc = from_dev(torch.cat([z1, z2], dim=2))
+    assert z_err(zc, from_dev(z)) <= 2 ** -7          # a bf16 rounding flip at most
+    assert state_err(from_dev(w2), from_dev(wf)) <= 1e-5
 
 
 def test_deterministic():
