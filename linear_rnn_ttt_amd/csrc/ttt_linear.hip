@@ -37,212 +37,34 @@
 //     loaded into registers while the current one is processed from LDS.
 #include "ttt_device.hpp"
 #include "ttt_kernels.hpp"
+#include "ttt_tile.hpp"
 
 namespace tttk {
 namespace {
 
-constexpr int D = 64;
 constexpr int NT = 256;  // threads per workgroup
 
 template <bool BF16>
-struct Io;
-template <>
-struct Io<true> {
-  using E = uint16_t;
-  static constexpr int TB = 8;     // tiles per staged block (128 tokens)
-  static constexpr int CPR = 8;    // 16-byte chunks per 64-element row
-};
-template <>
-struct Io<false> {
-  using E = float;
-  static constexpr int TB = 4;     // 64 tokens
-  static constexpr int CPR = 16;
+struct LinCfg {
+  static constexpr int TB = BF16 ? 8 : 4;  // tiles per staged block (16 KB per tensor)
 };
 
-// Staged blocks hold rows of 64 elements without padding; the 16-byte chunk
-// j of row t sits in slot j ^ (t & 7) of the row, which spreads the
-// row-strided operand reads of a 16x16 tile over the LDS banks.
 template <bool BF16>
-__device__ __forceinline__ int lds_off(int t, int col) {  // element offset
-  constexpr int EPC = 16 / sizeof(typename Io<BF16>::E);  // elements per chunk
-  return t * D + (((col / EPC) ^ (t & 7)) * EPC) + (col % EPC);
-}
-
-template <bool BF16>
-struct Lds {
-  using E = typename Io<BF16>::E;
-  static constexpr int TOK = Io<BF16>::TB * 16;
-  E qkv[2][3][TOK * D];         // staged q, k, v blocks (double buffered)
-  float eta[2][TOK];
+struct LinLds {
+  Stage<BF16, LinCfg<BF16>::TB> st;
   // LN partial sums [parity][wave][round][token][quantity slot]: the 16
   // tokens of one (wave, round) are 16 consecutive 16-byte rows, so the
   // readers (lane c reads token c) hit distinct banks.
   f32x4 xch[2][4][2][16];
-  float wbar[D];                // W0 1 / d
+  float wbar[D];  // W0 1 / d
 };
-
-#define TTT_LDS __attribute__((address_space(3)))
-
-// Start copying block `blk` (TB tiles) of q, k, v and eta from HBM straight
-// into LDS buffer `buf` (global_load_lds: no registers, no VALU).  Each wave
-// moves 1 KB per instruction; lane l lands at byte 16 l of it, so the lane
-// picks the source chunk that belongs in that swizzled slot.  Rows past T
-// re-read row T-1 (finite data; their eta is ignored by the scan).
-template <bool BF16>
-__device__ __forceinline__ void stage_issue(Lds<BF16>& L, const LinearArgs& a, size_t row0,
-                                            int blk, int T, int buf) {
-  using E = typename Io<BF16>::E;
-  constexpr int CPR = Io<BF16>::CPR;
-  constexpr int TOK = Io<BF16>::TB * 16;
-  constexpr int RB = D * sizeof(E);            // row bytes
-  constexpr int NI = TOK * RB / (4 * 1024);    // instructions per wave per tensor
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-  const int tok0 = blk * TOK;
-  const char* src[3] = {static_cast<const char*>(a.q), static_cast<const char*>(a.k),
-                        static_cast<const char*>(a.v)};
-#pragma unroll
-  for (int n = 0; n < NI; ++n) {
-    const int off = (NI * w + n) * 1024 + 16 * l;   // byte offset in the block
-    const int t = off / RB, slot = (off % RB) / 16;
-    const int j = slot ^ (t & 7);
-    const int tok = min(tok0 + t, T - 1);
-    const size_t goff = (row0 + tok) * (size_t)RB + j * 16;
-#pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      TTT_LDS void* dst = (TTT_LDS void*)(reinterpret_cast<char*>(L.qkv[buf][x]) +
-                                          (NI * w + n) * 1024);
-      __builtin_amdgcn_global_load_lds(src[x] + goff, dst, 16, 0, 0);
-    }
-  }
-  if (w * 64 < TOK) {
-    const int tok = min(tok0 + w * 64 + l, T - 1);
-    TTT_LDS void* dst = (TTT_LDS void*)(&L.eta[buf][w * 64]);
-    __builtin_amdgcn_global_load_lds(a.eta + row0 + tok, dst, 4, 0, 0);
-  }
-  (void)CPR;
-}
-
-// Wait for this wave's outstanding global->LDS copies (and stores).
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
-
-// ---- LDS operand fetch ---------------------------------------------------
-// Four consecutive elements of one row as bf16 hi (and lo for fp32 data).
-struct Op4 {
-  u32x2 hi, lo;
-};
-__device__ __forceinline__ Op4 op4(const uint16_t* p) {
-  return Op4{*reinterpret_cast<const u32x2*>(p), u32x2{0u, 0u}};
-}
-__device__ __forceinline__ Op4 op4(const float* p) {
-  const Split4 s = split4(*reinterpret_cast<const f32x4*>(p));
-  return Op4{s.hi, s.lo};
-}
-__device__ __forceinline__ Op4 op4_of(f32x4 v) {
-  const Split4 s = split4(v);
-  return Op4{s.hi, s.lo};
-}
-__device__ __forceinline__ Op4 op4_of(uint32_t e0, uint32_t e1, uint32_t e2, uint32_t e3) {
-  return Op4{u32x2{e0 | (e1 << 16), e2 | (e3 << 16)}, u32x2{0u, 0u}};
-}
-// Four consecutive elements of one row as fp32.
-__device__ __forceinline__ f32x4 val4(const uint16_t* p) {
-  const u32x2 w = *reinterpret_cast<const u32x2*>(p);
-  return f32x4{bf16_lo_to_f32(w.x), bf16_hi_to_f32(w.x), bf16_lo_to_f32(w.y),
-               bf16_hi_to_f32(w.y)};
-}
-__device__ __forceinline__ f32x4 val4(const float* p) { return *reinterpret_cast<const f32x4*>(p); }
-
-// The 4 accumulator registers of two 16x16 tiles of X, split into bf16 hi/lo
-// and laid out as 16x16x32 operands: slot j < 4 -> tile a element j, slot
-// j >= 4 -> tile b element j - 4.
-struct Op8 {
-  u32x4 hi, lo;
-};
-__device__ __forceinline__ Op8 split_pair(f32x4 a, f32x4 b) {
-  const Split4 sa = split4(a), sb = split4(b);
-  return Op8{cat(sa.hi, sb.hi), cat(sa.lo, sb.lo)};
-}
-
-// acc + A B over hi/lo parts: hi*hi, plus lo*hi when A has a lo part, plus
-// hi*lo when B has one (the lo*lo term is below the split's precision).
-template <bool ALO, bool BLO>
-__device__ __forceinline__ f32x4 mma8(const Op8& a, const Op8& b, f32x4 acc) {
-  acc = mfma32(a.hi, b.hi, acc);
-  if (ALO) acc = mfma32(a.lo, b.hi, acc);
-  if (BLO) acc = mfma32(a.hi, b.lo, acc);
-  return acc;
-}
-
-// Rows c of a staged 16-token tile at features 32p + 4g + (0..3) and
-// 32p + 16 + 4g + (0..3): the B operand of X^T (16x16x32, slots matching
-// split_pair of two state tiles) and the A / B operand of X X'^T.
-struct Rows {
-  Op8 p[2];
-};
-template <bool BF16>
-__device__ __forceinline__ Rows load_rows(const typename Io<BF16>::E* X, int t0, int c, int g) {
-  Rows r;
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const Op4 a = op4(X + lds_off<BF16>(t0 + c, 32 * p + 4 * g));
-    const Op4 b = op4(X + lds_off<BF16>(t0 + c, 32 * p + 16 + 4 * g));
-    r.p[p] = Op8{cat(a.hi, b.hi), cat(a.lo, b.lo)};
-  }
-  return r;
-}
-// K^T of a staged tile as 16x16x16 A operands: kt[r] lane (g,c) holds
-// K[t0 + 4g + i][16r + c].
-template <bool BF16>
-__device__ __forceinline__ void load_cols(Op4 kt[4], const typename Io<BF16>::E* X, int t0, int c,
-                                          int g) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const auto e0 = X[lds_off<BF16>(t0 + 4 * g + 0, 16 * r + c)];
-    const auto e1 = X[lds_off<BF16>(t0 + 4 * g + 1, 16 * r + c)];
-    const auto e2 = X[lds_off<BF16>(t0 + 4 * g + 2, 16 * r + c)];
-    const auto e3 = X[lds_off<BF16>(t0 + 4 * g + 3, 16 * r + c)];
-    if constexpr (BF16) kt[r] = op4_of(e0, e1, e2, e3);
-    else kt[r] = op4_of(f32x4{e0, e1, e2, e3});
-  }
-}
-// The state W (four accumulator tiles of one wave) as A operands of W^T.
-__device__ __forceinline__ void split_state(Op8 A[2], const f32x4 W[4]) {
-#pragma unroll
-  for (int p = 0; p < 2; ++p) A[p] = split_pair(W[2 * p], W[2 * p + 1]);
-}
-// X W for the wave's 16 output columns, transposed: lane (g,c) gets
-// (X W)[row c][16w + 4g + i].
-template <bool LO>
-__device__ __forceinline__ f32x4 times_state(const Op8 A[2], const Rows& X) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int p = 0; p < 2; ++p) acc = mma8<true, LO>(A[p], X.p[p], acc);
-  return acc;
-}
-// X Y^T in accumulator layout: lane (g,c) gets x_{4g+i} . y_c.
-template <bool LO>
-__device__ __forceinline__ f32x4 gram(const Rows& X, const Rows& Y) {
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int p = 0; p < 2; ++p) acc = mma8<LO, LO>(X.p[p], Y.p[p], acc);
-  return acc;
-}
-// acc + (-eta G)^T S for a 16x16 token-by-token tile S (accumulator layout,
-// split here): the correction products of the chunked form.
-__device__ __forceinline__ f32x4 correct(const Op4& gt, f32x4 S, f32x4 acc) {
-  const Split4 sp = split4(S);
-  acc = mfma16(gt.hi, sp.hi, acc);
-  acc = mfma16(gt.lo, sp.hi, acc);
-  acc = mfma16(gt.hi, sp.lo, acc);
-  return acc;
-}
 
 template <bool BF16, bool LN, bool RES, bool MB16>
 __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
   using E = typename Io<BF16>::E;
-  constexpr int TB = Io<BF16>::TB;
+  constexpr int TB = LinCfg<BF16>::TB;
   constexpr bool LO = !BF16;  // inputs carry a lo part (fp32 data)
-  __shared__ Lds<BF16> L;
+  __shared__ LinLds<BF16> L;
 
   const int tid = threadIdx.x;
   const int w = tid >> 6;          // wave: output columns 16w..16w+15
@@ -302,7 +124,7 @@ __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
   }
 
   const int n_tiles = (T + 15) / 16;
-  stage_issue<BF16>(L, a, row0, 0, T, 0);
+  stage_issue<BF16, TB>(L.st, a.q, a.k, a.v, a.eta, row0, 0, T, 0);
   wait_vmem();
   lds_barrier();
   if (LN) {
@@ -327,7 +149,7 @@ __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
   // is: correction -> LN sums -> exchange -> gradient -> transpose.
   Op8 Ab[2];
   Op4 gt = {}, kt[4] = {};
-  Rows kb = load_rows<BF16>(L.qkv[0][1], 0, c, g);
+  Rows kb = load_rows<BF16>(L.st.qkv[0][1], 0, c, g);
   f32x4 bk, pm = {0.f, 0.f, 0.f, 0.f}, mu4 = pm;
   split_state(Ab, Wc);
   bk = times_state<LO>(Ab, kb);
@@ -343,9 +165,9 @@ __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
   for (int blk = 0; blk * TB < n_tiles; ++blk) {
     const int buf = blk & 1;
     const bool next_block = (blk + 1) * TB < n_tiles;
-    const E* Lq = L.qkv[buf][0];
-    const E* Lk = L.qkv[buf][1];
-    const E* Lv = L.qkv[buf][2];
+    const E* Lq = L.st.qkv[buf][0];
+    const E* Lk = L.st.qkv[buf][1];
+    const E* Lv = L.st.qkv[buf][2];
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int tile = blk * TB + tb;
@@ -360,8 +182,8 @@ __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
       if (tb == TB - 2 && next_block) wait_vmem();
 
       // ===== [A] gradient point of tile t: K_t W_t = K_t W_{t-1} - (K_t K_{t-1}^T)(eta G)_{t-1}
-      f32x4 hk = mb_start ? correct(gt, pm, bk) : bk;
-      const float eta = L.eta[buf][t0 + c];
+      f32x4 hk = mb_start ? correct<true>(gt, pm, bk) : bk;
+      const float eta = L.st.eta[buf][t0 + c];
       const f32x4 kres = val4(Lk + lds_off<BF16>(t0 + c, fo));
       const f32x4 vres = val4(Lv + lds_off<BF16>(t0 + c, fo));
 
@@ -397,7 +219,7 @@ __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
       // tile t+1 (first tile of the next buffer after the last of this block;
       // past the end the products are formed from stale data and unused)
       const bool wrap = tb == TB - 1;
-      const Rows kn = load_rows<BF16>(wrap ? L.qkv[buf ^ 1][1] : Lk, wrap ? 0 : t0 + 16, c, g);
+      const Rows kn = load_rows<BF16>(wrap ? L.st.qkv[buf ^ 1][1] : Lk, wrap ? 0 : t0 + 16, c, g);
       const f32x4 bk_next = times_state<LO>(mb_start_next ? Ac : Ab, kn);
       const f32x4 pm_next = mb_start_next ? gram<LO>(kb, kn) : pm;
       f32x4 mu_next = {0.f, 0.f, 0.f, 0.f};
@@ -509,7 +331,7 @@ __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
       }
 
       // ===== [G] output pre-activation of tile t; carry to tile t+1
-      hq_prev = correct(gt, M, hqb);         // H_q^T = (Q W_t)^T + (-eta G)^T tril(K Q^T)
+      hq_prev = correct<true>(gt, M, hqb);         // H_q^T = (Q W_t)^T + (-eta G)^T tril(K Q^T)
       muq_prev = muq;
 #pragma unroll
       for (int i = 0; i < 4; ++i) qb_prev[i] = (RES ? qres[i] : 0.f) + (LN ? bet[i] : 0.f);
@@ -522,7 +344,7 @@ __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
       // refill the other buffer once every wave is past the previous block
       if (tb == 0 && next_block) {
         if (!LN) lds_barrier();
-        stage_issue<BF16>(L, a, row0, blk + 1, T, buf ^ 1);
+        stage_issue<BF16, TB>(L.st, a.q, a.k, a.v, a.eta, row0, blk + 1, T, buf ^ 1);
       }
     }  // tiles of the block
   }
