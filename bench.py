@@ -14,16 +14,17 @@ roofline of the scan kernel (algorithmic bytes or flops per launch over the
 launch time measured with HIP events on the launch stream) and the fp64 CPU
 oracle timed on the host cores.
 
-Other modes:
-  --summarize-pmc FETCH_DIR WRITE_DIR   turn two rocprofv3 --pmc runs
-      (FETCH_SIZE, then WRITE_SIZE) of `bench.py --copy-calibration` into the
-      markdown summary kept under profiles/ (HBM traffic per launch, scaled
-      by the same counters read on a plain copy of known size).
+Other modes (turn rocprofv3 output into the short summaries kept under
+profiles/):
+  --summarize-trace DIR                 a `rocprofv3 --kernel-trace --stats`
+      run of this benchmark: per-kernel average durations;
+  --summarize-pmc FETCH_DIR WRITE_DIR   two `rocprofv3 --pmc` runs (FETCH_SIZE,
+      then WRITE_SIZE) of `bench.py --copy-calibration`: HBM traffic per
+      launch, scaled by the same counters read on a plain 1 GiB copy.
 """
 from __future__ import annotations
 
 import argparse
-import csv
 import glob
 import hashlib
 import json
@@ -253,32 +254,53 @@ def run(args) -> dict:
 
 
 # ---------------------------------------------------------------------------
-# rocprofv3 counter summaries
+# rocprofv3 summaries (rocprofv3 writes an SQLite database, run_results.db)
 
-def _read_counter_csv(d: str):
-    files = glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True)
+def _db(d: str):
+    import sqlite3
+
+    files = glob.glob(os.path.join(d, "**", "*results.db"), recursive=True)
     if not files:
-        raise SystemExit("no *counter_collection.csv under %s" % d)
-    rows = []
-    for f in files:
-        with open(f) as fh:
-            rows.extend(csv.DictReader(fh))
-    return rows
+        raise SystemExit("no rocprofv3 results database under %s" % d)
+    return sqlite3.connect(sorted(files)[-1])
 
 
-def _per_dispatch(rows, counter):
-    """{kernel name: [value per dispatch]} for one counter (values summed
-    over the counter's instances within a dispatch)."""
-    acc = {}
-    for r in rows:
-        if r.get("Counter_Name") != counter:
-            continue
-        key = (r.get("Kernel_Name", ""), r.get("Dispatch_Id", ""))
-        acc[key] = acc.get(key, 0.0) + float(r["Counter_Value"])
-    out = {}
-    for (name, _), v in acc.items():
-        out.setdefault(name, []).append(v)
-    return out
+def _counter_per_dispatch(d, counter):
+    """[(kernel name, dispatch id, value)] for one counter (summed over the
+    counter's instances within a dispatch)."""
+    con = _db(d)
+    return con.execute(
+        "select kernel_name, dispatch_id, sum(value) from counters_collection "
+        "where counter_name = ? group by dispatch_id order by dispatch_id", (counter,)).fetchall()
+
+
+def summarize_trace(d, workload, cmd):
+    from linear_rnn_ttt_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[workload]
+    con = _db(d)
+    rows = con.execute("select name, total_calls, total_duration, average, percentage from "
+                       "top_kernels order by total_duration desc limit 8").fetchall()
+    lines = ["# Kernel trace: %s on %s (rocprofv3 --kernel-trace --stats)" % (
+        KERNEL_NAME[w.kind], workload), "", "Command:", "", "    " + cmd, "",
+        "- kernel_source_sha256: `%s`" % kernel_hash(w.kind), "",
+        "| kernel | calls | total (us) | average (us) | % of GPU time |", "|---|---|---|---|---|"]
+    for name, calls, tot, avg, pct in rows:
+        short = name if len(name) < 70 else name[:67] + "..."
+        lines.append("| `%s` | %d | %.1f | %.2f | %.1f |" % (short, calls, tot, avg, pct))
+    k = con.execute("select count(*), avg(duration), min(duration), max(duration) from kernels "
+                    "where name like ?", ("%" + KERNEL_NAME[w.kind] + "%",)).fetchone()
+    if k and k[0]:
+        avg_us = k[1] / 1e3
+        alg = algorithmic(w)
+        lines += ["", "Scan kernel: %d launches, average %.2f us (min %.2f, max %.2f)." % (
+            k[0], avg_us, k[2] / 1e3, k[3] / 1e3)]
+        lines += ["", "Average %.2f us per launch; %d algorithmic bytes per launch "
+                  "-> %.1f GB/s (%.2f%% of 8 TB/s); %.3e algorithmic flops -> %.2f TFLOP/s." % (
+                      avg_us, alg["bytes"], alg["bytes"] / avg_us / 1e3,
+                      100 * alg["bytes"] / avg_us / 1e3 / HBM_PEAK_GBS, alg["flops"],
+                      alg["flops"] / avg_us / 1e6)]
+    return "\n".join(lines) + "\n"
 
 
 def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write):
@@ -286,23 +308,15 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write):
 
     w = WORKLOADS[workload]
     kname = KERNEL_NAME[w.kind]
-    fetch = _per_dispatch(_read_counter_csv(fetch_dir), "FETCH_SIZE")
-    write = _per_dispatch(_read_counter_csv(write_dir), "WRITE_SIZE")
-
-    def pick(d, pred):
-        vals = [v for name, vs in d.items() if pred(name) for v in vs]
-        return vals
-
-    kf = pick(fetch, lambda n: kname in n)
-    kw = pick(write, lambda n: kname in n)
-    cf = pick(fetch, lambda n: "copy" in n.lower() or "elementwise" in n.lower())
-    cw = pick(write, lambda n: "copy" in n.lower() or "elementwise" in n.lower())
-    # the largest elementwise dispatch is the 1 GiB copy (fills are smaller
-    # reads); use it for both factors
-    copy_fetch_kib = max(cf) if cf else float("nan")
-    copy_write_kib = max(cw) if cw else float("nan")
-    f_fetch = (COPY_BYTES / 1024.0) / copy_fetch_kib
-    f_write = (COPY_BYTES / 1024.0) / copy_write_kib
+    fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
+    write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
+    kf = [v for n, _, v in fetch if kname in n]
+    kw = [v for n, _, v in write if kname in n]
+    # the 1 GiB device-to-device copy: the largest copyBuffer dispatch
+    cf = max(v for n, _, v in fetch if "copyBuffer" in n)
+    cw = max(v for n, _, v in write if "copyBuffer" in n)
+    f_fetch = (COPY_BYTES / 1024.0) / cf
+    f_write = (COPY_BYTES / 1024.0) / cw
     fetch_kib = sum(kf) / len(kf)
     write_kib = sum(kw) / len(kw)
     traffic = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
@@ -311,7 +325,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write):
         "# HBM traffic of `%s` on %s (rocprofv3 --pmc)" % (kname, workload),
         "",
         "Two counter runs of the benchmark (kernel launches plus one plain 1 GiB",
-        "device-to-device copy used to scale the counters):",
+        "device-to-device copy whose counters scale the kernel's):",
         "",
         "    " + cmd_fetch,
         "    " + cmd_write,
@@ -320,8 +334,8 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write):
         "- dispatches_measured: %d (FETCH_SIZE), %d (WRITE_SIZE)" % (len(kf), len(kw)),
         "- fetch_kib_per_dispatch: %.1f" % fetch_kib,
         "- write_kib_per_dispatch: %.1f" % write_kib,
-        "- copy_fetch_kib (1 GiB copy): %.1f -> factor %.4f" % (copy_fetch_kib, f_fetch),
-        "- copy_write_kib (1 GiB copy): %.1f -> factor %.4f" % (copy_write_kib, f_write),
+        "- copy_fetch_kib (1 GiB copy): %.1f -> factor %.4f" % (cf, f_fetch),
+        "- copy_write_kib (1 GiB copy): %.1f -> factor %.4f" % (cw, f_write),
         "- traffic_bytes_per_launch: %d" % int(traffic),
         "- algorithmic_bytes_per_launch: %d" % alg,
         "- traffic / algorithmic: %.3f" % (traffic / alg),
@@ -342,8 +356,13 @@ def main(argv=None):
                     help="run one 1 GiB copy before the timed region (counter scaling)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-commands", nargs=2, default=["", ""])
+    ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--trace-command", default="")
     args = ap.parse_args(argv)
 
+    if args.summarize_trace:
+        sys.stdout.write(summarize_trace(args.summarize_trace, args.workload, args.trace_command))
+        return 0
     if args.summarize_pmc:
         sys.stdout.write(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
                                        args.workload, *args.pmc_commands))
