@@ -201,7 +201,7 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
   const Op4 ones = {ones_op(), u32x2{0u, 0u}};
 
   const int n_tiles = (T + 15) / 16;
-  stage_issue<BF16, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, 0, T, 0);
+  stage_issue<BF16, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, 0, T, 0, tid >> 6);
   wait_vmem();
   lds_barrier();
 
@@ -211,7 +211,8 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
     if (tb == 0 && next_block) {
       // every wave has passed the previous tile's barriers: the other buffer
       // (previous block) is free
-      stage_issue<BF16, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, blk + 1, T, buf ^ 1);
+      stage_issue<BF16, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, blk + 1, T, buf ^ 1,
+                             tid >> 6);
     }
     const E* Lq = L.st.qkv[buf][0];
     const E* Lk = L.st.qkv[buf][1];

@@ -45,19 +45,20 @@ struct Stage {
 #define TTT_LDS __attribute__((address_space(3)))
 
 // Start copying block `blk` (TB tiles) of q, k, v and eta from HBM straight
-// into LDS buffer `buf` (global_load_lds: no registers, no VALU).  Each wave
+// into LDS buffer `buf` (global_load_lds: no registers, no VALU).  Four
+// waves share the copy; `w` (0..3) is the calling wave's share.  Each wave
 // moves 1 KB per instruction; lane l lands at byte 16 l of it, so the lane
 // picks the source chunk that belongs in that swizzled slot.  Rows past T
 // re-read row T-1 (finite data; their eta is ignored by the scan).
 template <bool BF16, int TB>
 __device__ __forceinline__ void stage_issue(Stage<BF16, TB>& L, const void* q, const void* k,
                                             const void* v, const float* eta, size_t row0,
-                                            int blk, int T, int buf) {
+                                            int blk, int T, int buf, int w) {
   using E = typename Io<BF16>::E;
   constexpr int TOK = TB * 16;
   constexpr int RB = D * sizeof(E);            // row bytes
   constexpr int NI = TOK * RB / (4 * 1024);    // instructions per wave per tensor
-  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int l = threadIdx.x & 63;
   const int tok0 = blk * TOK;
   const char* src[3] = {static_cast<const char*>(q), static_cast<const char*>(k),
                         static_cast<const char*>(v)};
