@@ -15,49 +15,56 @@
 // (W_base == W for 16-token mini-batches; larger mini-batches keep W_base
 // for several tiles).
 //
-// Mapping onto one CU: one 512-thread workgroup per (batch, head) unit.
-//   * Waves 4-7 ("state" waves) keep W[:, 16w:16w+16] as four 16x16 fp32
-//     MFMA accumulators.  In period t they apply the update of tile t-1,
-//     split W_{t-1} into bf16 hi/lo, and form Q_t W_{t-1} (output of tile
-//     t) and K_{t+2} W_{t-1} (gradient point two tiles ahead).
-//   * Waves 0-3 ("chain" waves) own the same column blocks and run the
-//     serial part: they bring K_{t+1} W_{t-2} up to date with the two
-//     updates it misses, K_{t+1} W_t = K_{t+1} W_{t-2}
-//     + (K_{t+1} K_{t-1}^T)(-eta G_{t-1}) + (K_{t+1} K_t^T)(-eta G_t), of
-//     which only the last 16x16 correction waits for tile t's gradient.  The
-//     serial path per tile is: correction -> LN sums -> one exchange among
-//     the chain waves -> gradient -> transpose.  Off that path the chain
-//     waves also finish the outputs (tril(K Q^T) correction, output LN, z).
-//   * A chain wave and a state wave share each SIMD, so one fills the issue
-//     slots while the other waits on the barrier, the LDS or the matrix
-//     unit; the chain waves run at a higher wave priority.
+// Mapping onto one CU: one 768-thread workgroup per (batch, head) unit, in
+// three kinds of waves; wave w of each kind owns output columns
+// 16(w mod 4)..+15, and one wave of each kind shares each SIMD, so the
+// others fill the issue slots while one waits on the barrier, the LDS or
+// the matrix unit (the chain waves run at a higher wave priority).
+//   * Waves 0-3 ("chain") run only the serial part of the scan.  With the
+//     gradient point K_{t+1} W_{t-2} and the score tiles K_{t-1} K_{t+1}^T,
+//     K_t K_{t+1}^T prepared for them, they form
+//     K_{t+1} W_t = K_{t+1} W_{t-2} + (K_{t+1} K_{t-1}^T)(-eta G_{t-1})
+//     + (K_{t+1} K_t^T)(-eta G_t), of which only the last 16x16 correction
+//     waits for tile t's gradient.  The serial path per tile is:
+//     correction -> LN sums -> one exchange among the chain waves ->
+//     gradient -> transpose.
+//   * Waves 4-7 ("update") keep W[:, 16w:16w+16] as four 16x16 fp32 MFMA
+//     accumulators.  In period t they apply the update of tile t-1, split
+//     W_{t-1} into bf16 hi/lo and form Q_t W_{t-1} and K_{t+2} W_{t-1}; they
+//     also issue the input copies.
+//   * Waves 8-11 ("output") finish the outputs (tril(K Q^T) correction,
+//     output LN, z) and, one wave per item, the column-independent inputs:
+//     the two score tiles and (k . w_bar, sum_f u_f) of tile t+2, and
+//     tril(K_t Q_t^T), q . w_bar of tile t.
 //   * H is produced transposed (H^T = W^T K^T): a lane holds 4 features of
 //     ONE token, so LN row sums are in-lane adds plus a reduce-scatter over
 //     the 4 lane groups (v_permlane16/32_swap).
-//   * LN sums are taken around the shift k . w_bar with w_bar = W0 1 / d: the
-//     LN gradient of every token sums to zero over the features, so W 1 is a
-//     constant of the scan and k . w_bar is the exact row mean up to
-//     rounding.  The shift comes out of the matrix unit.
+//   * LN sums are taken around the shifts k . w_bar and q . w_bar,
+//     w_bar = W0 1 / d: the LN gradient of every token sums to zero over the
+//     features, so W 1 is a constant of the scan and the shift is the row
+//     mean up to rounding (it comes out of the matrix unit).  The means
+//     themselves are still reduced from the data: centring on the shift
+//     alone would turn the rounding drift of W 1 into gradients whose rows
+//     no longer sum to zero, a feedback that grows along the sequence.
+//   * Per-feature scalings are products with diagonal tiles on the matrix
+//     unit (u = 2 gamma (k - v) + 2 gamma beta, q + beta); dot products of a
+//     row with w_bar and 2 gamma are one product with a constant A operand.
 //   * fp32 operands enter the bf16 matrix unit as hi + lo bf16 pairs (about
-//     16 significant bits); bf16 inputs are exact.  hi and lo terms share
-//     16x16x32 products where the 8 operand slots allow it.  The output
-//     correction of bf16 data uses the hi part of the score tile only: its
-//     error does not feed back into the state.
+//     16 significant bits); bf16 inputs are exact.  The output correction of
+//     bf16 data uses the hi part of the score tile only: its error does not
+//     feed back into the state.
 //   * Row m of the state's accumulator tile r holds input feature
 //     32 (r/2) + 8 (m/4) + 4 (r%2) + m%4, so the 8 contraction slots of a
 //     lane in a 16x16x32 product with W are 8 consecutive features: every
-//     row operand (K, Q, w_bar) is a single 16-byte LDS read.
+//     row operand is a single 16-byte LDS read.
 //   * Accumulate chains never mix the 16x16x32 and 16x16x16 shapes: on this
 //     toolchain a result of one shape fed back to back as the C operand of
 //     the other came out wrong in two of its four registers.
 //   * q, k, v, eta stream from HBM to LDS in blocks of TB tiles
-//     (global_load_lds, double-buffered), issued by the state waves.
-//   * One barrier per tile orders every exchange: the chain's LN sums,
-//     -eta G (chain -> state), Q_t W_{t-1} and K_{t+2} W_{t-1}
-//     (state -> chain).  Both loops are free of branches within a tile;
-//     tiles past the end compute on stale rows with their gradient forced
-//     to zero, and z stores past the end are dropped by the buffer range
-//     check.
+//     (global_load_lds, double-buffered), issued by the update waves.
+//   * One barrier per tile orders every exchange.  Both loops are free of
+//     branches within a tile (past the end: stale rows, gradient forced to
+//     zero, z stores dropped by the buffer range check).
 #include "ttt_device.hpp"
 #include "ttt_kernels.hpp"
 #include "ttt_tile.hpp"
@@ -65,7 +72,7 @@
 namespace tttk {
 namespace {
 
-constexpr int NT = 512;  // 4 chain waves + 4 state waves
+constexpr int NT = 768;  // 4 chain, 4 update and 4 output waves
 
 template <bool BF16>
 struct LinCfg {
@@ -75,14 +82,20 @@ struct LinCfg {
 template <bool BF16>
 struct LinLds {
   Stage<BF16, LinCfg<BF16>::TB> st;
-  // chain LN partial sums [parity][wave][round][token][quantity]: the 16
-  // tokens of one (wave, round) are 16 consecutive 16-byte rows, so the
-  // readers (lane c reads token c) hit distinct banks.
-  f32x4 xc[2][4][2][16];
-  u32x4 gtb[2][4][64];  // (-eta G_t)^T operand, chain wave -> state wave
-  f32x4 qwb[2][4][64];  // (Q_t W_{t-1})^T, state wave -> chain wave
-  f32x4 bkb[2][4][64];  // (K_{t+2} W_{t-1})^T, state wave -> chain wave
-  float wbar[D];        // W0 1 / d
+  // chain LN partial sums around the shift [parity][wave][token]: (sum e,
+  // sum e^2, sum gamma^2 e, sum gamma^2 e^2); lane c reads the 16-byte row
+  // of token c.  xu[parity][token][wave]: sum u e.
+  f32x4 xc[2][4][16];
+  f32x4 xu[2][16];
+  u32x4 gtb[2][4][64];  // (-eta G_t)^T as [hi, lo], chain wave -> update and output waves
+  f32x4 bkb[2][4][64];  // (K_{t+2} W_{t-1})^T, update wave -> chain wave
+  f32x4 qwb[2][4][64];  // (Q_t W_{t-1})^T, update wave -> output wave
+  u32x4 grb[2][2][64];  // K_{t+1} K_{t+2}^T, K_t K_{t+2}^T as [hi, lo]
+  f32x2 tkb[2][16];     // per token of tile t+2: (k . w_bar, sum_f u_f)
+  u32x4 mqb[2][64];     // tril(K_t Q_t^T) as [hi, lo]
+  float mqm[2][16];     // q . w_bar per token of tile t
+  f32x2 xo[2][16][4];   // output LN: (sum e, sum e^2) per token and wave
+  uint16_t cst[4][D];   // bf16 rows: w_bar hi, 2 gamma hi, w_bar lo, 2 gamma lo
 };
 
 struct Ctx {
@@ -119,7 +132,8 @@ __device__ __forceinline__ Rows rows8(const typename Io<BF16>::E* X, int c, int 
       r.p[p].hi = *reinterpret_cast<const u32x4*>(X + lds_off<true>(c, 32 * p + 8 * g));
       r.p[p].lo = u32x4{0u, 0u, 0u, 0u};
     } else {
-      const Split4 a = split4(*reinterpret_cast<const f32x4*>(X + lds_off<false>(c, 32 * p + 8 * g)));
+      const Split4 a =
+          split4(*reinterpret_cast<const f32x4*>(X + lds_off<false>(c, 32 * p + 8 * g)));
       const Split4 b =
           split4(*reinterpret_cast<const f32x4*>(X + lds_off<false>(c, 32 * p + 8 * g + 4)));
       r.p[p] = Op8{cat(a.hi, b.hi), cat(a.lo, b.lo)};
@@ -142,6 +156,11 @@ __device__ __forceinline__ void cols8(Op4 kt[4], const typename Io<BF16>::E* X, 
     else kt[r] = op4_of(f32x4{e0, e1, e2, e3});
   }
 }
+// Features fo..fo+3 of row c of a bf16 tile: the 16x16x16 B operand of X^T
+// restricted to one column block (lane (g,c) holds X[c][16w + 4g + i]).
+__device__ __forceinline__ u32x2 quad(const uint16_t* X, int c, int fo) {
+  return *reinterpret_cast<const u32x2*>(X + lds_off<true>(c, fo));
+}
 
 __device__ __forceinline__ u32x4 zero_unless(bool keep, u32x4 x) {
   const u32x4 z = {0u, 0u, 0u, 0u};
@@ -149,35 +168,40 @@ __device__ __forceinline__ u32x4 zero_unless(bool keep, u32x4 x) {
 }
 __device__ __forceinline__ u32x2 hi_of(u32x4 g) { return u32x2{g.x, g.y}; }
 __device__ __forceinline__ u32x2 lo_of(u32x4 g) { return u32x2{g.z, g.w}; }
+__device__ __forceinline__ u32x4 hilo(const Split4& s) { return cat(s.hi, s.lo); }
 
-// acc + (-eta G)^T S for a score tile S (tokens x tokens, accumulator
-// layout, split into bf16 hi/lo) and G given as [hi, lo]: the hi*hi, lo*hi
-// and hi*lo terms as a chain of 16x16x16 products on sub-operands of the
-// two tuples (no register moves; acc may be a value loaded from LDS).
-__device__ __forceinline__ f32x4 corr(u32x4 gt, const Split4& s, f32x4 acc) {
-  acc = mfma16(hi_of(gt), s.hi, acc);
-  acc = mfma16(lo_of(gt), s.hi, acc);
-  acc = mfma16(hi_of(gt), s.lo, acc);
+// acc + (-eta G)^T S for a score tile S (tokens x tokens) and G, both given
+// as [hi, lo]: the hi*hi, lo*hi and hi*lo terms as a chain of 16x16x16
+// products on sub-operands of the two tuples (acc may come from LDS).
+__device__ __forceinline__ f32x4 corr(u32x4 gt, u32x4 s, f32x4 acc) {
+  acc = mfma16(hi_of(gt), hi_of(s), acc);
+  acc = mfma16(lo_of(gt), hi_of(s), acc);
+  acc = mfma16(hi_of(gt), lo_of(s), acc);
   return acc;
 }
 
-// w_bar as 16x16x32 A operands (every row the same, slots as in rows8):
-// mfma(wbar, rows of X) gives x . w_bar for each token of X in every
-// register of its lane.
-__device__ __forceinline__ void wbar_ops(const float* wb, int g, u32x4 op[2]) {
+// Dot products of the rows of X with the constant rows (w_bar hi, 2 gamma hi,
+// w_bar lo, 2 gamma lo): lane (g,c) gets them for token c in registers 0-3.
+template <bool LO>
+__device__ __forceinline__ f32x4 stats(const u32x4 ast[2], const Rows& x) {
+  f32x4 d = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    const f32x4 m0 = *reinterpret_cast<const f32x4*>(&wb[32 * p + 8 * g]);
-    const f32x4 m1 = *reinterpret_cast<const f32x4*>(&wb[32 * p + 8 * g + 4]);
-    op[p] = split_pair(m0, m1).hi;  // a shift need not be exact
+    d = mfma32(ast[p], x.p[p].hi, d);
+    if (LO) d = mfma32(ast[p], x.p[p].lo, d);
   }
+  return d;
 }
-__device__ __forceinline__ float shift_of(const u32x4 wb[2], const Rows& x) {
-  f32x4 m = {0.f, 0.f, 0.f, 0.f};
+
+// A diagonal 16x16 tile diag(x_{16w + m}) as a 16x16x16 A operand: lane
+// (g,c) holds A[c][4g + i], nonzero only at 4g + i == c.
+__device__ __forceinline__ u32x2 diag_op(int g, int c, uint32_t bits16) {
+  uint32_t e[4];
 #pragma unroll
-  for (int p = 0; p < 2; ++p) m = mfma32(wb[p], x.p[p].hi, m);
-  return m[0];
+  for (int i = 0; i < 4; ++i) e[i] = (4 * g + i == c) ? bits16 : 0u;
+  return u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
 }
+__device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16(x, 0.f) & 0xffffu; }
 
 // Row stores of z through a buffer resource covering exactly the unit's T
 // rows: rows outside [0, T) fail the hardware range check and are dropped.
@@ -201,146 +225,164 @@ struct ZOut {
 };
 
 // ---------------------------------------------------------------------------
-// Chain waves.  The inputs of tile j's gradient that do not depend on the
-// scan are prepared two periods ahead.
-struct Prep {
-  f32x4 u;     // LN: 2 gamma (k - v) + 2 gamma beta, else k - v (no k without residual)
-  float su;    // in-lane sum of u
-  float mu;    // k . w_bar
-  Split4 p1;   // K_{j-1} K_j^T, bf16 hi/lo
-  Split4 p2;   // K_{j-2} K_j^T
-};
-
-template <bool BF16, bool LN, bool RES>
-__device__ __forceinline__ Prep prepare(const typename Io<BF16>::E* Kj,
-                                        const typename Io<BF16>::E* Vj, const Rows& km1,
-                                        const Rows& km2, const u32x4 wb[2], f32x4 twog,
-                                        f32x4 twogb, int c, int g, int fo) {
-  constexpr bool LO = !BF16;
-  Prep r;
-  const f32x4 kv = val4(Kj + lds_off<BF16>(c, fo));
-  const f32x4 vv = val4(Vj + lds_off<BF16>(c, fo));
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const float kmv = (RES ? kv[i] : 0.f) - vv[i];
-    r.u[i] = LN ? __builtin_fmaf(twog[i], kmv, twogb[i]) : kmv;
-  }
-  r.su = (r.u[0] + r.u[1]) + (r.u[2] + r.u[3]);
-  const Rows kj = rows8<BF16>(Kj, c, g);
-  r.mu = LN ? shift_of(wb, kj) : 0.f;
-  r.p1 = split4(gram<LO>(km1, kj));
-  r.p2 = split4(gram<LO>(km2, kj));
-  return r;
-}
-
 template <bool BF16, bool LN, bool RES, bool MB16>
 __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x) {
   constexpr int TB = LinCfg<BF16>::TB;
-  constexpr bool LO = !BF16;
-  using E = typename Io<BF16>::E;
   const int lane = x.lane, g = x.g, c = x.c, w = x.w, fo = x.fo, n = x.n, T = x.T;
   const int tpm = x.tpm;
   auto mbs = [&](int j) { return MB16 || (j % tpm) == 0; };
   __builtin_amdgcn_s_setprio(2);
 
-  f32x4 gam = {1.f, 1.f, 1.f, 1.f}, bet = {0.f, 0.f, 0.f, 0.f};
-  f32x4 gsq = gam, g2x2 = {2.f, 2.f, 2.f, 2.f}, twog = g2x2, twogb = bet;
+  f32x4 gsq = {1.f, 1.f, 1.f, 1.f}, g2x2 = {2.f, 2.f, 2.f, 2.f}, twog = g2x2;
+  f32x4 twogb = {0.f, 0.f, 0.f, 0.f};
   float Gam = 64.f;  // sum of gamma^2 over the features
   if (LN) {
     const float* gp = a.gamma + (size_t)x.head * D;
     const float* bp = a.beta + (size_t)x.head * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      gam[i] = gp[fo + i];
-      bet[i] = bp[fo + i];
-      gsq[i] = gam[i] * gam[i];
+      const float gm = gp[fo + i];
+      gsq[i] = gm * gm;
       g2x2[i] = 2.f * gsq[i];
-      twog[i] = 2.f * gam[i];
-      twogb[i] = 2.f * gam[i] * bet[i];
+      twog[i] = 2.f * gm;
+      twogb[i] = 2.f * gm * bp[fo + i];
     }
     Gam = 0.f;
     for (int j = 0; j < D; ++j) Gam += gp[j] * gp[j];
   }
   const u32x2 ident = ident_op(g, c);
-  bool causal[4];
+  // u^T = diag(2 gamma) (k - v)^T + 2 gamma beta on the matrix unit (bf16
+  // data): diag(2 gamma) as a bf16 hi/lo pair and its negation.
+  u32x2 dph = ident, dpl = {0u, 0u}, dnh, dnl = {0u, 0u};
+  if (LN) {
+    const float t2 = 2.f * a.gamma[(size_t)x.head * D + 16 * w + c];
+    const uint32_t h = bf16_bits(t2);
+    const uint32_t l = bf16_bits(t2 - __builtin_bit_cast(float, h << 16));
+    dph = diag_op(g, c, h);
+    dpl = diag_op(g, c, l);
+    dnh = diag_op(g, c, h ? (h ^ 0x8000u) : 0u);
+    dnl = diag_op(g, c, l ? (l ^ 0x8000u) : 0u);
+  } else {
+    dnh = diag_op(g, c, 0xBF80u);  // -1
+  }
+  // k and v of a tile at the wave's features (raw, as staged) and u from them
+  struct KV {
+    u32x4 k, v;  // bf16: 4 values in .xy; fp32: 4 values
+  };
+  auto kv_of = [&](int blk, int tb) -> KV {
+    KV r;
+    if constexpr (BF16) {
+      const u32x2 k4 = quad(tile_rows(L.st, 1, blk, tb), c, fo);
+      const u32x2 v4 = quad(tile_rows(L.st, 2, blk, tb), c, fo);
+      r.k = u32x4{k4.x, k4.y, 0u, 0u};
+      r.v = u32x4{v4.x, v4.y, 0u, 0u};
+    } else {
+      r.k = __builtin_bit_cast(u32x4, val4(tile_rows(L.st, 1, blk, tb) + lds_off<false>(c, fo)));
+      r.v = __builtin_bit_cast(u32x4, val4(tile_rows(L.st, 2, blk, tb) + lds_off<false>(c, fo)));
+    }
+    return r;
+  };
+  auto u_of = [&](const KV& kv) -> f32x4 {
+    if constexpr (BF16) {
+      const u32x2 k4 = {kv.k.x, kv.k.y}, v4 = {kv.v.x, kv.v.y};
+      f32x4 u = LN ? twogb : f32x4{0.f, 0.f, 0.f, 0.f};
+      if (RES) {
+        u = mfma16(dph, k4, u);
+        if (LN) u = mfma16(dpl, k4, u);
+      }
+      u = mfma16(dnh, v4, u);
+      if (LN) u = mfma16(dnl, v4, u);
+      return u;
+    } else {
+      const f32x4 kk = __builtin_bit_cast(f32x4, kv.k), vv = __builtin_bit_cast(f32x4, kv.v);
+      f32x4 u;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) causal[i] = (4 * g + i) <= c;
-  const ZOut<BF16> zo(a.z, x.row0, T);
+      for (int i = 0; i < 4; ++i) {
+        const float kmv = (RES ? kk[i] : 0.f) - vv[i];
+        u[i] = LN ? __builtin_fmaf(twog[i], kmv, twogb[i]) : kmv;
+      }
+      return u;
+    }
+  };
+  // LN partial sums of one tile around its shift, reduced over the 4 lane
+  // groups, into this wave's exchange slots.
+  auto publish = [&](int par, f32x4 ep, f32x4 u) {
+    if (!LN) return;
+    f32x4 ge;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ge[i] = gsq[i] * ep[i];
+    const float q0 = (ep[0] + ep[1]) + (ep[2] + ep[3]);
+    const float q2 = (ge[0] + ge[1]) + (ge[2] + ge[3]);
+    float q1 = ep[0] * ep[0], q3 = ge[0] * ep[0], q4 = u[0] * ep[0];
+#pragma unroll
+    for (int i = 1; i < 4; ++i) {
+      q1 = __builtin_fmaf(ep[i], ep[i], q1);
+      q3 = __builtin_fmaf(ge[i], ep[i], q3);
+      q4 = __builtin_fmaf(u[i], ep[i], q4);
+    }
+    reinterpret_cast<float*>(&L.xc[par][w][c])[rs4_slot(g)] =
+        group_reduce_scatter4(q0, q1, q2, q3);
+    reinterpret_cast<float*>(&L.xu[par][c])[w] = group_sum(q4);
+  };
 
-  lds_barrier();  // A: block 0 staged, w_bar published
-  u32x4 wb[2] = {};
-  if (LN) wbar_ops(L.wbar, g, wb);
-  const Rows k0 = rows8<BF16>(tile_rows(L.st, 1, 0, 0), c, g);
-  const Prep p0 = prepare<BF16, LN, RES>(tile_rows(L.st, 1, 0, 0), tile_rows(L.st, 2, 0, 0), k0,
-                                         k0, wb, twog, twogb, c, g, fo);
-  Prep nx = prepare<BF16, LN, RES>(tile_rows(L.st, 1, 0, 1), tile_rows(L.st, 2, 0, 1), k0, k0,
-                                   wb, twog, twogb, c, g, fo);
-  lds_barrier();  // B: K_0 W0 and K_1 W0 published by the state waves
-  f32x4 ep, uc = p0.u;
+  lds_barrier();  // A: block 0 staged, constants published
+  lds_barrier();  // B: inputs of tiles 0 and 1 published
+  f32x4 ep, uc = u_of(kv_of(0, 0));
+  float su;       // sum_f u_f of the current tile
   {
     const f32x4 h = L.bkb[0][w][lane];
+    const f32x2 tk = L.tkb[0][c];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ep[i] = h[i] - p0.mu;
-    if (LN) {
-      f32x4 ge;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ge[i] = gsq[i] * ep[i];
-      const float q0 = (ep[0] + ep[1]) + (ep[2] + ep[3]);
-      const float q2 = (ge[0] + ge[1]) + (ge[2] + ge[3]);
-      float q1 = ep[0] * ep[0], q3 = ge[0] * ep[0], q4 = uc[0] * ep[0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) {
-        q1 = __builtin_fmaf(ep[i], ep[i], q1);
-        q3 = __builtin_fmaf(ge[i], ep[i], q3);
-        q4 = __builtin_fmaf(uc[i], ep[i], q4);
-      }
-      reinterpret_cast<float*>(&L.xc[0][w][0][c])[rs4_slot(g)] =
-          group_reduce_scatter4(q0, q1, q2, q3);
-      reinterpret_cast<float*>(&L.xc[0][w][1][c])[rs4_slot(g)] =
-          group_reduce_scatter4(q4, p0.su, 0.f, 0.f);
-    }
+    for (int i = 0; i < 4; ++i) ep[i] = LN ? h[i] - tk.x : h[i];
+    su = tk.y;
+    publish(0, ep, uc);
   }
   lds_barrier();  // period 0 starts
-
-  // carried from period to period (p is the current period)
-  u32x4 gtm1 = {};                        // (-eta G_{p-1})^T as [hi, lo]
-  Split4 m1 = {};                         // tril(K_{p-1} Q_{p-1}^T) (hi only for bf16 data)
-  float muq1 = 0.f;                       // q . w_bar, tile p-1
-  f32x4 qb1 = {0.f, 0.f, 0.f, 0.f};       // q + beta (residual part of z), tile p-1
-  f32x4 qb2 = qb1, eq2 = qb1;             // tile p-2: q + beta, centred H_q
+  u32x4 gtm1 = {};  // (-eta G_{p-1})^T as [hi, lo]
 
   for (int blk = 0; blk * TB <= n + 1; ++blk) {
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int p = blk * TB + tb;
       if (p > n + 1) break;
-      f32x4 s1 = {0.f, 0.f, 0.f, 0.f}, s2 = s1;
+      // ---- every LDS read of the period first, so that their latencies
+      //      overlap: the exchanged sums of tile p and the inputs of tile
+      //      p+1 prepared in the last period
+      f32x4 xs[4], su4;
       if (LN) {
-        s1 = L.xc[p & 1][0][0][c];
-        s2 = L.xc[p & 1][0][1][c];
 #pragma unroll
-        for (int ww = 1; ww < 4; ++ww) {
-          s1 += L.xc[p & 1][ww][0][c];
-          s2 += L.xc[p & 1][ww][1][c];
-        }
+        for (int ww = 0; ww < 4; ++ww) xs[ww] = L.xc[p & 1][ww][c];
+        su4 = L.xu[p & 1][c];
       }
+      const float eta = tile_eta(L.st, blk, tb, c);
+      const f32x4 bk = L.bkb[(p - 1) & 1][w][lane];  // K_{p+1} W_{p-2}
+      const u32x4 s1 = L.grb[(p - 1) & 1][0][lane];  // K_p K_{p+1}^T
+      const u32x4 s2 = L.grb[(p - 1) & 1][1][lane];  // K_{p-1} K_{p+1}^T
+      const f32x2 tk = L.tkb[(p - 1) & 1][c];
+      const KV kvn = kv_of(blk, tb + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- independent of tile p's gradient: u of tile p+1, the
+      //      correction of K_{p+1} W_{p-2} by tile p-1
+      const f32x4 un = u_of(kvn);
+      f32x4 h = corr(zero_unless(MB16 || mbs(p + 1) || mbs(p), gtm1), s2, bk);
       // ---- gradient of tile p (zero for rows past T, so past the end the
-      //      state waves' update is a no-op)
+      //      update of W is a no-op)
       u32x4 gt;
       {
-        const float eta = tile_eta(L.st, blk, tb, c);
         const bool valid = p * 16 + c < T;
         f32x4 eg;
         if (LN) {
-          const float mr = s1[0] * (1.0f / D);
-          const float var = __builtin_fmaf(-mr, mr, s1[1] * (1.0f / D));
+          const f32x4 S = (xs[0] + xs[1]) + (xs[2] + xs[3]);
+          const float S4 = (su4[0] + su4[1]) + (su4[2] + su4[3]);
+          const float mr = S[0] * (1.0f / D);
+          const float var = __builtin_fmaf(-mr, mr, S[1] * (1.0f / D));
           const float rs = __frsqrt_rn(var + a.eps);
-          const float sge = __builtin_fmaf(-mr, Gam, s1[2]);
-          const float sue = __builtin_fmaf(-mr, s2[1], s2[0]);
-          const float sge2 = __builtin_fmaf(mr * mr, Gam, __builtin_fmaf(-2.f * mr, s1[2], s1[3]));
-          const float ma = (s2[1] + 2.f * rs * sge) * (1.0f / D);
-          const float mx = (rs * sue + 2.f * rs * rs * sge2) * (1.0f / D);
-          const float c1 = -eta * rs, c2 = -eta * rs * rs;
+          const float sge = __builtin_fmaf(-mr, Gam, S[2]);
+          const float sue = __builtin_fmaf(-mr, su, S4);
+          const float sge2 = __builtin_fmaf(mr * mr, Gam, __builtin_fmaf(-2.f * mr, S[2], S[3]));
+          const float ma = __builtin_fmaf(2.f * rs, sge, su) * (1.0f / D);
+          const float mx = __builtin_fmaf(2.f * rs, sge2, sue) * (rs * (1.0f / D));
+          const float c1 = -eta * rs, c2 = c1 * rs;
           const float b0 = -c1 * ma, c2mx = -c2 * mx;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -361,83 +403,15 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
                    pack_bf16(tl[2], tl[3])};
       }
       L.gtb[p & 1][w][lane] = gt;
-
-      // ---- z of tile p-2 (its output LN sums came with this exchange)
-      if (LN) {
-        const float mr = s2[2] * (1.0f / D);
-        const float var = __builtin_fmaf(-mr, mr, s2[3] * (1.0f / D));
-        const float rs = __frsqrt_rn(var + a.eps);
-        f32x4 zf;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) zf[i] = __builtin_fmaf(gam[i] * rs, eq2[i] - mr, qb2[i]);
-        zo.store((p - 2) * 16 + c, fo, zf);
-      }
-      // ---- output pre-activation of tile p-1:
-      //      H_q^T = (Q W_{p-2})^T + (-eta G_{p-1})^T tril(K Q^T)
-      f32x4 eq = {0.f, 0.f, 0.f, 0.f};
+      // ---- gradient point of tile p+1 and its LN sums (at p >= n-1 the
+      //      tile does not exist: stale rows, unused)
       {
-        f32x4 hq = L.qwb[(p - 1) & 1][w][lane];
-        hq = mfma16(hi_of(gtm1), m1.hi, hq);
-        hq = mfma16(lo_of(gtm1), m1.hi, hq);
-        if (LO) hq = mfma16(hi_of(gtm1), m1.lo, hq);
-        if (LN) {
+        h = corr(zero_unless(MB16 || mbs(p + 1), gt), s1, h);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) eq[i] = hq[i] - muq1;
-        } else {
-          zo.store((p - 1) * 16 + c, fo, qb1 + hq);
-        }
-      }
-      // ---- gradient point of tile p+1 and the exchange of its LN sums
-      //      (with the output sums of tile p-1)
-      {
-        f32x4 h = L.bkb[(p - 1) & 1][w][lane];  // K_{p+1} W_{p-2}
-        h = corr(zero_unless(MB16 || mbs(p + 1) || mbs(p), gtm1), nx.p2, h);
-        h = corr(zero_unless(MB16 || mbs(p + 1), gt), nx.p1, h);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) ep[i] = h[i] - nx.mu;
-        uc = nx.u;
-        if (LN) {
-          f32x4 ge;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) ge[i] = gsq[i] * ep[i];
-          const float q0 = (ep[0] + ep[1]) + (ep[2] + ep[3]);
-          const float q2 = (ge[0] + ge[1]) + (ge[2] + ge[3]);
-          const float q6 = (eq[0] + eq[1]) + (eq[2] + eq[3]);
-          float q1 = ep[0] * ep[0], q3 = ge[0] * ep[0], q4 = uc[0] * ep[0], q7 = eq[0] * eq[0];
-#pragma unroll
-          for (int i = 1; i < 4; ++i) {
-            q1 = __builtin_fmaf(ep[i], ep[i], q1);
-            q3 = __builtin_fmaf(ge[i], ep[i], q3);
-            q4 = __builtin_fmaf(uc[i], ep[i], q4);
-            q7 = __builtin_fmaf(eq[i], eq[i], q7);
-          }
-          reinterpret_cast<float*>(&L.xc[(p + 1) & 1][w][0][c])[rs4_slot(g)] =
-              group_reduce_scatter4(q0, q1, q2, q3);
-          reinterpret_cast<float*>(&L.xc[(p + 1) & 1][w][1][c])[rs4_slot(g)] =
-              group_reduce_scatter4(q4, nx.su, q6, q7);
-        }
-      }
-      // ---- tile p: output-side inputs; tile p+2: gradient inputs (past
-      //      the end: stale rows, unused)
-      {
-        const E* Qp = tile_rows(L.st, 0, blk, tb);
-        const Rows qr = rows8<BF16>(Qp, c, g);
-        const Rows kp = rows8<BF16>(tile_rows(L.st, 1, blk, tb), c, g);
-        const Rows kp1 = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 1), c, g);
-        f32x4 M = gram<LO>(kp, qr);  // K_p Q_p^T
-#pragma unroll
-        for (int i = 0; i < 4; ++i) M[i] = causal[i] ? M[i] : 0.f;
-        qb2 = qb1;
-        eq2 = eq;
-        if (LO) m1 = split4(M);
-        else m1.hi = u32x2{pack_bf16(M[0], M[1]), pack_bf16(M[2], M[3])};
-        muq1 = LN ? shift_of(wb, qr) : 0.f;
-        const f32x4 qv = val4(Qp + lds_off<BF16>(c, fo));
-#pragma unroll
-        for (int i = 0; i < 4; ++i) qb1[i] = (RES ? qv[i] : 0.f) + (LN ? bet[i] : 0.f);
-        nx = prepare<BF16, LN, RES>(tile_rows(L.st, 1, blk, tb + 2),
-                                    tile_rows(L.st, 2, blk, tb + 2), kp1, kp, wb, twog, twogb,
-                                    c, g, fo);
+        for (int i = 0; i < 4; ++i) ep[i] = LN ? h[i] - tk.x : h[i];
+        uc = un;
+        su = tk.y;
+        publish((p + 1) & 1, ep, uc);
       }
       gtm1 = gt;
       lds_barrier();
@@ -446,8 +420,9 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
 }
 
 // ---------------------------------------------------------------------------
+// Update waves: the state, its products, and the input copies.
 template <bool BF16, bool LN, bool RES, bool MB16>
-__device__ __forceinline__ void state_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x) {
+__device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x) {
   constexpr int TB = LinCfg<BF16>::TB;
   constexpr bool LO = !BF16;
   const int lane = x.lane, g = x.g, c = x.c, w = x.w, n = x.n, T = x.T;
@@ -461,24 +436,28 @@ __device__ __forceinline__ void state_part(LinLds<BF16>& L, const LinearArgs& a,
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int i = 0; i < 4; ++i) Wc[r][i] = w0[feat(r, 4 * g + i) * D + 16 * w + c];
-  if (LN && w == 0) {
-    float s = 0.f;
-    for (int j = 0; j < D; ++j) s += w0[lane * D + j];
-    L.wbar[lane] = s * (1.0f / D);
+  if (LN && w == 0) {  // w_bar rows of the dot-product operand, as bf16 hi/lo
+    float v = 0.f;
+    for (int j = 0; j < D; ++j) v += w0[lane * D + j];
+    v *= 1.0f / D;
+    const uint32_t h = bf16_bits(v);
+    L.cst[0][lane] = (uint16_t)h;
+    L.cst[2][lane] = (uint16_t)bf16_bits(v - __builtin_bit_cast(float, h << 16));
   }
-  // "tile -1": no update and a zero output in period 0
+  // "tile -1": no update in period 0
   L.gtb[1][w][lane] = u32x4{0u, 0u, 0u, 0u};
   L.qwb[1][w][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const u32x2 ident = ident_op(g, c);
   // The tiles past the end are read from stale staging rows (their
   // gradient is zero, but 0 * Inf would not be): buffer 1 starts as zeros
   // in case the sequence never loads it.
   {
     constexpr int N16 = sizeof(L.st.qkv[1]) / 16;
+    const int t = threadIdx.x - 256;
     u32x4* b1 = reinterpret_cast<u32x4*>(&L.st.qkv[1][0][0]);
-    for (int i = threadIdx.x - 256; i < N16; i += 256) b1[i] = u32x4{0u, 0u, 0u, 0u};
-    for (int i = threadIdx.x - 256; i < LinCfg<BF16>::TB * 16; i += 256) L.st.eta[1][i] = 0.f;
+    for (int i = t; i < N16; i += 256) b1[i] = u32x4{0u, 0u, 0u, 0u};
+    for (int i = t; i < TB * 16; i += 256) L.st.eta[1][i] = 0.f;
   }
-
   stage_issue<BF16, TB>(L.st, a.q, a.k, a.v, a.eta, x.row0, 0, T, 0, w);
   wait_vmem();
   lds_barrier();  // A
@@ -488,8 +467,12 @@ __device__ __forceinline__ void state_part(LinLds<BF16>& L, const LinearArgs& a,
     Ab[0] = Ac[0];
     Ab[1] = Ac[1];
   }
-  L.bkb[0][w][lane] = times_state<LO>(Ac, rows8<BF16>(tile_rows(L.st, 1, 0, 0), c, g));
-  L.bkb[1][w][lane] = times_state<LO>(Ac, rows8<BF16>(tile_rows(L.st, 1, 0, 1), c, g));
+  // rows of K_p and K_{p+1}, carried from the period that loaded them as
+  // the rows of K_{p+2}
+  Rows kc0 = rows8<BF16>(tile_rows(L.st, 1, 0, 0), c, g);
+  Rows kc1 = rows8<BF16>(tile_rows(L.st, 1, 0, 1), c, g);
+  L.bkb[0][w][lane] = times_state<LO>(Ac, kc0);
+  L.bkb[1][w][lane] = times_state<LO>(Ac, kc1);
   lds_barrier();  // B
   lds_barrier();  // period 0 starts
 
@@ -503,8 +486,15 @@ __device__ __forceinline__ void state_part(LinLds<BF16>& L, const LinearArgs& a,
       // refill the other buffer: nobody reads tiles before p any more
       if (tb == 0 && next_block)
         stage_issue<BF16, TB>(L.st, a.q, a.k, a.v, a.eta, x.row0, blk + 1, T, (blk + 1) & 1, w);
+      // every LDS read of the period first
+      const auto* Kp = tile_rows(L.st, 1, blk, tb);
       const u32x4 g1 = L.gtb[(p - 1) & 1][w][lane];  // (-eta G_{p-1})^T as [hi, lo]
-      // ---- state update with tile p-1: W += K^T (-eta G)
+      const Rows qr = rows8<BF16>(tile_rows(L.st, 0, blk, tb), c, g);
+      const Rows kn = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 2), c, g);
+      Op4 ktn[4];
+      if constexpr (!BF16) cols8<BF16>(ktn, Kp, c, g);
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- W += K_{p-1}^T (-eta G_{p-1})
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         Wc[r] = mfma16(kt1[r].hi, hi_of(g1), Wc[r]);
@@ -517,13 +507,27 @@ __device__ __forceinline__ void state_part(LinLds<BF16>& L, const LinearArgs& a,
         Ab[1] = Ac[1];
       }
       // ---- products of W_{p-1} (past the end: stale rows, unused)
-      const auto* Kp = tile_rows(L.st, 1, blk, tb);
-      L.qwb[p & 1][w][lane] = times_state<LO>(Ac, rows8<BF16>(tile_rows(L.st, 0, blk, tb), c, g));
-      cols8<BF16>(kt1, Kp, c, g);
+      L.qwb[p & 1][w][lane] = times_state<LO>(Ac, qr);
+      if constexpr (BF16) {
+        // K_p^T for the next update from the rows of K_p: half of a row
+        // operand times the identity is the transposed 16x16 block, whose
+        // rows are the state's features feat(r, c)
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const u32x4 h = kc0.p[r >> 1].hi;
+          const f32x4 t = mfma16((r & 1) ? u32x2{h.z, h.w} : u32x2{h.x, h.y}, ident, zero);
+          kt1[r] = Op4{u32x2{pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])}, u32x2{0u, 0u}};
+        }
+        kc0 = kc1;
+        kc1 = kn;
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kt1[r] = ktn[r];
+      }
       {
         // gradient point two tiles ahead: K_{p+2} W_{p-1}, or the
         // mini-batch's own gradient point when no update reaches it
-        const Rows kn = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 2), c, g);
         f32x4 bk;
         if (MB16 || mbs(p + 2) || mbs(p + 1)) bk = times_state<LO>(Ac, kn);
         else bk = times_state<LO>(Ab, kn);
@@ -545,15 +549,192 @@ __device__ __forceinline__ void state_part(LinLds<BF16>& L, const LinearArgs& a,
   }
 }
 
+// ---------------------------------------------------------------------------
+// Output waves: z, and (one wave per item) the column-independent inputs.
+template <bool BF16, bool LN, bool RES, bool MB16>
+__device__ __forceinline__ void output_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x) {
+  constexpr int TB = LinCfg<BF16>::TB;
+  constexpr bool LO = !BF16;
+  const int lane = x.lane, g = x.g, c = x.c, w = x.w, fo = x.fo, n = x.n, T = x.T;
+
+  f32x4 gam = {1.f, 1.f, 1.f, 1.f}, bet = {0.f, 0.f, 0.f, 0.f};
+  float s2gb = 0.f;  // sum_f 2 gamma beta
+  if (LN) {
+    const float* gp = a.gamma + (size_t)x.head * D;
+    const float* bp = a.beta + (size_t)x.head * D;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gam[i] = gp[fo + i];
+      bet[i] = bp[fo + i];
+    }
+    for (int j = 0; j < D; ++j) s2gb += 2.f * gp[j] * bp[j];
+    if (w == 1) {  // 2 gamma rows of the dot-product operand, as bf16 hi/lo
+      const float v = 2.f * gp[lane];
+      const uint32_t h = bf16_bits(v);
+      L.cst[1][lane] = (uint16_t)h;
+      L.cst[3][lane] = (uint16_t)bf16_bits(v - __builtin_bit_cast(float, h << 16));
+    }
+  }
+  if (w == 3) {  // "tile -1": zero output in period 0
+    L.mqb[1][lane] = u32x4{0u, 0u, 0u, 0u};
+    if (lane < 16) L.mqm[1][lane] = 0.f;
+  }
+  bool causal[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) causal[i] = (4 * g + i) <= c;
+  const u32x2 ident = ident_op(g, c);
+  const ZOut<BF16> zo(a.z, x.row0, T);
+
+  lds_barrier();  // A
+  u32x4 ast[2] = {};
+  if (LN) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      ast[p] = *reinterpret_cast<const u32x4*>(&L.cst[c & 3][32 * p + 8 * g]);
+  }
+  // (k . w_bar, sum_f u_f) of a tile from its rows of k and v, one product
+  // per tensor
+  auto token_inputs = [&](const Rows& kr, const Rows& vr) -> f32x2 {
+    const f32x4 sk = stats<LO>(ast, kr);
+    const f32x4 sv = stats<LO>(ast, vr);
+    const float su = ((RES ? sk[1] + sk[3] : 0.f) - (sv[1] + sv[3])) + s2gb;
+    return f32x2{sk[0] + sk[2], su};
+  };
+  if (w == 0) {
+    if (LN) {
+      L.tkb[0][c] = token_inputs(rows8<BF16>(tile_rows(L.st, 1, 0, 0), c, g),
+                                 rows8<BF16>(tile_rows(L.st, 2, 0, 0), c, g));
+      L.tkb[1][c] = token_inputs(rows8<BF16>(tile_rows(L.st, 1, 0, 1), c, g),
+                                 rows8<BF16>(tile_rows(L.st, 2, 0, 1), c, g));
+    }
+  } else if (w == 1) {
+    L.grb[1][0][lane] = hilo(split4(gram<LO>(rows8<BF16>(tile_rows(L.st, 1, 0, 0), c, g),
+                                             rows8<BF16>(tile_rows(L.st, 1, 0, 1), c, g))));
+  } else if (w == 2) {
+    L.grb[1][1][lane] = u32x4{0u, 0u, 0u, 0u};
+  }
+  lds_barrier();  // B
+  lds_barrier();  // period 0 starts
+
+  f32x4 qb1 = {0.f, 0.f, 0.f, 0.f}, qb2 = qb1;  // q + beta (residual part of z), tiles p-1, p-2
+  f32x4 eq2 = qb1;                              // output pre-activation around its shift, tile p-2
+  for (int blk = 0; blk * TB <= n + 1; ++blk) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int p = blk * TB + tb;
+      if (p > n + 1) break;
+      // every LDS read of the period first
+      const u32x4 g1 = L.gtb[(p - 1) & 1][w][lane];  // (-eta G_{p-1})^T as [hi, lo]
+      f32x4 s01 = {}, s23 = {};
+      float muq = 0.f;
+      if (LN) {
+        s01 = *reinterpret_cast<const f32x4*>(&L.xo[(p - 1) & 1][c][0]);
+        s23 = *reinterpret_cast<const f32x4*>(&L.xo[(p - 1) & 1][c][2]);
+        muq = L.mqm[(p - 1) & 1][c];
+      }
+      const u32x4 m = L.mqb[(p - 1) & 1][lane];
+      const f32x4 qw = L.qwb[(p - 1) & 1][w][lane];
+      const auto* Qp = tile_rows(L.st, 0, blk, tb);
+      const auto* Kp = tile_rows(L.st, 1, blk, tb);
+      const auto* K2 = tile_rows(L.st, 1, blk, tb + 2);
+      u32x2 q4 = {0u, 0u};
+      f32x4 qv = {0.f, 0.f, 0.f, 0.f};
+      if constexpr (BF16) q4 = quad(Qp, c, fo);
+      else qv = val4(Qp + lds_off<false>(c, fo));
+      // operands of this wave's column-independent item
+      Rows ra, rb;
+      if (w == 0) {
+        ra = rows8<BF16>(K2, c, g);
+        rb = rows8<BF16>(tile_rows(L.st, 2, blk, tb + 2), c, g);
+      } else if (w == 1) {
+        ra = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 1), c, g);
+        rb = rows8<BF16>(K2, c, g);
+      } else if (w == 2) {
+        ra = rows8<BF16>(Kp, c, g);
+        rb = rows8<BF16>(K2, c, g);
+      } else {
+        ra = rows8<BF16>(Kp, c, g);
+        rb = rows8<BF16>(Qp, c, g);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- z of tile p-2 (its output LN sums came with the last barrier)
+      if (LN) {
+        const f32x4 s = s01 + s23;
+        const float mr = (s[0] + s[2]) * (1.0f / D);
+        const float var = __builtin_fmaf(-mr, mr, (s[1] + s[3]) * (1.0f / D));
+        const float rs = __frsqrt_rn(var + a.eps);
+        f32x4 zf;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) zf[i] = __builtin_fmaf(gam[i] * rs, eq2[i] - mr, qb2[i]);
+        zo.store((p - 2) * 16 + c, fo, zf);
+      }
+      // ---- output of tile p-1: H_q^T = (Q W_{p-2})^T + (-eta G_{p-1})^T tril(K Q^T)
+      {
+        f32x4 d = mfma16(hi_of(g1), hi_of(m), f32x4{0.f, 0.f, 0.f, 0.f});
+        d = mfma16(lo_of(g1), hi_of(m), d);
+        if (LO) d = mfma16(hi_of(g1), lo_of(m), d);
+        const f32x4 hq = qw + d;
+        if (LN) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) eq2[i] = hq[i] - muq;
+          const float q6 = (eq2[0] + eq2[1]) + (eq2[2] + eq2[3]);
+          float q7 = eq2[0] * eq2[0];
+#pragma unroll
+          for (int i = 1; i < 4; ++i) q7 = __builtin_fmaf(eq2[i], eq2[i], q7);
+          const float t = swap32_sum(q6, q7);
+          // groups 0, 1 hold the sum of q6, groups 2, 3 that of q7
+          reinterpret_cast<float*>(&L.xo[p & 1][c][w])[g >> 1] = swap16_sum(t, t);
+        } else {
+          zo.store((p - 1) * 16 + c, fo, qb1 + hq);
+        }
+        qb2 = qb1;
+      }
+      // ---- tile p (past the end: stale rows, unused)
+      if constexpr (BF16) {
+        qb1 = RES ? mfma16(ident, q4, bet) : bet;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) qb1[i] = (RES ? qv[i] : 0.f) + bet[i];
+      }
+      // ---- column-independent inputs, one wave each: (k . w_bar,
+      //      sum_f u_f) of tile p+2, the score tiles K_{p+1} K_{p+2}^T and
+      //      K_p K_{p+2}^T, and tril(K_p Q_p^T), q . w_bar of tile p
+      if (w == 0) {
+        if (LN) L.tkb[p & 1][c] = token_inputs(ra, rb);
+      } else if (w == 1 || w == 2) {
+        L.grb[p & 1][w - 1][lane] = hilo(split4(gram<LO>(ra, rb)));
+      } else {
+        const Rows& qr = rb;
+        f32x4 M = gram<LO>(ra, qr);  // K_p Q_p^T
+#pragma unroll
+        for (int i = 0; i < 4; ++i) M[i] = causal[i] ? M[i] : 0.f;
+        if (LO) {
+          L.mqb[p & 1][lane] = hilo(split4(M));
+        } else {
+          L.mqb[p & 1][lane] = u32x4{pack_bf16(M[0], M[1]), pack_bf16(M[2], M[3]), 0u, 0u};
+        }
+        if (LN) {
+          const f32x4 sq = stats<LO>(ast, qr);
+          L.mqm[p & 1][c] = sq[0] + sq[2];
+        }
+      }
+      lds_barrier();
+    }
+  }
+}
+
 template <bool BF16, bool LN, bool RES, bool MB16>
 __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
   __shared__ LinLds<BF16> L;
   Ctx x;
   const int tid = threadIdx.x;
+  // the wave index is uniform across a wave: keep it (and the branches on
+  // the wave's role) scalar
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   x.lane = tid & 63;
   x.g = x.lane >> 4;
   x.c = x.lane & 15;
-  x.w = (tid >> 6) & 3;
+  x.w = wave & 3;
   x.fo = 16 * x.w + 4 * x.g;
   x.unit = blockIdx.x;
   x.head = x.unit % a.H;
@@ -561,8 +742,9 @@ __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
   x.n = (a.T + 15) / 16;
   x.tpm = MB16 ? 1 : a.tiles_per_mb;
   x.row0 = (size_t)x.unit * a.T;
-  if (tid < 256) chain_part<BF16, LN, RES, MB16>(L, a, x);
-  else state_part<BF16, LN, RES, MB16>(L, a, x);
+  if (wave < 4) chain_part<BF16, LN, RES, MB16>(L, a, x);
+  else if (wave < 8) update_part<BF16, LN, RES, MB16>(L, a, x);
+  else output_part<BF16, LN, RES, MB16>(L, a, x);
 }
 
 template <bool BF16, bool LN, bool RES>
