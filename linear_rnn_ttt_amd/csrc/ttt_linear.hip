@@ -19,7 +19,7 @@
 // three kinds of waves; wave w of each kind owns output columns
 // 16(w mod 4)..+15, and one wave of each kind shares each SIMD, so the
 // others fill the issue slots while one waits on the barrier, the LDS or
-// the matrix unit (the chain waves run at a higher wave priority).
+// the matrix unit (the update and chain waves run at a higher wave priority).
 //   * Waves 0-3 ("chain") run only the serial part of the scan.  With the
 //     gradient point K_{t+1} W_{t-2} and the score tiles K_{t-1} K_{t+1}^T,
 //     K_t K_{t+1}^T prepared for them, they form
@@ -30,12 +30,14 @@
 //     gradient -> transpose.
 //   * Waves 4-7 ("update") keep W[:, 16w:16w+16] as four 16x16 fp32 MFMA
 //     accumulators.  In period t they apply the update of tile t-1, split
-//     W_{t-1} into bf16 hi/lo and form Q_t W_{t-1} and K_{t+2} W_{t-1}; they
-//     also issue the input copies.
-//   * Waves 8-11 ("output") finish the outputs (tril(K Q^T) correction,
-//     output LN, z) and, one wave per item, the column-independent inputs:
-//     the two score tiles and (k . w_bar, sum_f u_f) of tile t+2, and
-//     tril(K_t Q_t^T), q . w_bar of tile t.
+//     W_{t-1} into bf16 hi/lo, form Q_t W_{t-1} and K_{t+2} W_{t-1}, add
+//     the tril(K Q^T) correction of tile t-1 to its Q W product, and, one
+//     wave per item, prepare the column-independent inputs of tile t+2 for
+//     the chain (the two score tiles, k . w_bar and sum_f u_f).  All of
+//     these use row operands the wave reads once per period.
+//   * Waves 8-11 ("output") take the output pre-activation of tile t-2,
+//     exchange its LN sums and store z of tile t-3.  They also issue the
+//     input copies, spread over several tiles.
 //   * H is produced transposed (H^T = W^T K^T): a lane holds 4 features of
 //     ONE token, so LN row sums are in-lane adds plus a reduce-scatter over
 //     the 4 lane groups (v_permlane16/32_swap).
@@ -61,7 +63,7 @@
 //     toolchain a result of one shape fed back to back as the C operand of
 //     the other came out wrong in two of its four registers.
 //   * q, k, v, eta stream from HBM to LDS in blocks of TB tiles
-//     (global_load_lds, double-buffered), issued by the update waves.
+//     (global_load_lds, double-buffered).
 //   * One barrier per tile orders every exchange.  Both loops are free of
 //     branches within a tile (past the end: stale rows, gradient forced to
 //     zero, z stores dropped by the buffer range check).
@@ -89,11 +91,10 @@ struct LinLds {
   f32x4 xu[2][16];
   u32x4 gtb[2][4][64];  // (-eta G_t)^T as [hi, lo], chain wave -> update and output waves
   f32x4 bkb[2][4][64];  // (K_{t+2} W_{t-1})^T, update wave -> chain wave
-  f32x4 qwb[2][4][64];  // (Q_t W_{t-1})^T, update wave -> output wave
   u32x4 grb[2][2][64];  // K_{t+1} K_{t+2}^T, K_t K_{t+2}^T as [hi, lo]
   f32x2 tkb[2][16];     // per token of tile t+2: (k . w_bar, sum_f u_f)
-  u32x4 mqb[2][64];     // tril(K_t Q_t^T) as [hi, lo]
-  float mqm[2][16];     // q . w_bar per token of tile t
+  f32x4 hqb[2][4][64];  // output pre-activation of tile t-1 around its shift,
+                        // update wave -> output wave
   f32x2 xo[2][16][4];   // output LN: (sum e, sum e^2) per token and wave
   uint16_t cst[4][D];   // bf16 rows: w_bar hi, 2 gamma hi, w_bar lo, 2 gamma lo
 };
@@ -191,6 +192,23 @@ __device__ __forceinline__ f32x4 stats(const u32x4 ast[2], const Rows& x) {
     if (LO) d = mfma32(ast[p], x.p[p].lo, d);
   }
   return d;
+}
+
+// The state as 16x16x32 A operands of W^T (see split_state), with the lo
+// part W - bf16(W) formed on the matrix unit: -I times the packed hi tile,
+// accumulated onto W, is exact in fp32 (W - bf16(W) has at most 16
+// significant bits), so only the two conversions per pair stay on the VALU.
+__device__ __forceinline__ void split_state_mm(Op8 A[2], const f32x4 W[4], u32x2 neg_ident) {
+  u32x2 hi[4], lo[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) hi[r] = u32x2{pack_bf16(W[r][0], W[r][1]), pack_bf16(W[r][2], W[r][3])};
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const f32x4 d = mfma16(neg_ident, hi[r], W[r]);
+    lo[r] = u32x2{pack_bf16(d[0], d[1]), pack_bf16(d[2], d[3])};
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) A[p] = Op8{cat(hi[2 * p], hi[2 * p + 1]), cat(lo[2 * p], lo[2 * p + 1])};
 }
 
 // A diagonal 16x16 tile diag(x_{16w + m}) as a 16x16x16 A operand: lane
@@ -340,11 +358,11 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
   lds_barrier();  // period 0 starts
   u32x4 gtm1 = {};  // (-eta G_{p-1})^T as [hi, lo]
 
-  for (int blk = 0; blk * TB <= n + 1; ++blk) {
+  for (int blk = 0; blk * TB <= n + 2; ++blk) {
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int p = blk * TB + tb;
-      if (p > n + 1) break;
+      if (p > n + 2) break;
       // ---- every LDS read of the period first, so that their latencies
       //      overlap: the exchanged sums of tile p and the inputs of tile
       //      p+1 prepared in the last period
@@ -420,7 +438,9 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
 }
 
 // ---------------------------------------------------------------------------
-// Update waves: the state, its products, and the input copies.
+// Update waves: the state, every product with it, the output correction,
+// the column-independent inputs of the chain (one wave each), and the input
+// copies.  Every row operand of a period is read once, at its start.
 template <bool BF16, bool LN, bool RES, bool MB16>
 __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x) {
   constexpr int TB = LinCfg<BF16>::TB;
@@ -436,18 +456,29 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
   for (int r = 0; r < 4; ++r)
 #pragma unroll
     for (int i = 0; i < 4; ++i) Wc[r][i] = w0[feat(r, 4 * g + i) * D + 16 * w + c];
-  if (LN && w == 0) {  // w_bar rows of the dot-product operand, as bf16 hi/lo
-    float v = 0.f;
-    for (int j = 0; j < D; ++j) v += w0[lane * D + j];
-    v *= 1.0f / D;
-    const uint32_t h = bf16_bits(v);
-    L.cst[0][lane] = (uint16_t)h;
-    L.cst[2][lane] = (uint16_t)bf16_bits(v - __builtin_bit_cast(float, h << 16));
+  float s2gb = 0.f;  // sum_f 2 gamma beta
+  if (LN) {
+    const float* gp = a.gamma + (size_t)x.head * D;
+    const float* bp = a.beta + (size_t)x.head * D;
+    for (int j = 0; j < D; ++j) s2gb += 2.f * gp[j] * bp[j];
+    // constant rows of the dot-product operand, as bf16 hi/lo: w_bar
+    // (wave 0) and 2 gamma (wave 1)
+    if (w < 2) {
+      float v;
+      if (w == 0) {
+        v = 0.f;
+        for (int j = 0; j < D; ++j) v += w0[lane * D + j];
+        v *= 1.0f / D;
+      } else {
+        v = 2.f * gp[lane];
+      }
+      const uint32_t h = bf16_bits(v);
+      L.cst[w][lane] = (uint16_t)h;
+      L.cst[w + 2][lane] = (uint16_t)bf16_bits(v - __builtin_bit_cast(float, h << 16));
+    }
   }
   // "tile -1": no update in period 0
   L.gtb[1][w][lane] = u32x4{0u, 0u, 0u, 0u};
-  L.qwb[1][w][lane] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const u32x2 ident = ident_op(g, c);
   // The tiles past the end are read from stale staging rows (their
   // gradient is zero, but 0 * Inf would not be): buffer 1 starts as zeros
   // in case the sequence never loads it.
@@ -458,9 +489,28 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
     for (int i = t; i < N16; i += 256) b1[i] = u32x4{0u, 0u, 0u, 0u};
     for (int i = t; i < TB * 16; i += 256) L.st.eta[1][i] = 0.f;
   }
+  const u32x2 ident = ident_op(g, c);
+  const u32x2 neg_ident = diag_op(g, c, 0xBF80u);  // -1 on the diagonal
+  bool causal[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) causal[i] = (4 * g + i) <= c;
+
   stage_issue<BF16, TB>(L.st, a.q, a.k, a.v, a.eta, x.row0, 0, T, 0, w);
   wait_vmem();
   lds_barrier();  // A
+  u32x4 ast[2] = {};
+  if (LN) {
+#pragma unroll
+    for (int p = 0; p < 2; ++p)
+      ast[p] = *reinterpret_cast<const u32x4*>(&L.cst[c & 3][32 * p + 8 * g]);
+  }
+  // (k . w_bar, sum_f u_f) of a tile from its rows of k and v
+  auto token_inputs = [&](const Rows& kr, const Rows& vr) -> f32x2 {
+    const f32x4 sk = stats<LO>(ast, kr);
+    const f32x4 sv = stats<LO>(ast, vr);
+    const float su = ((RES ? sk[1] + sk[3] : 0.f) - (sv[1] + sv[3])) + s2gb;
+    return f32x2{sk[0] + sk[2], su};
+  };
   Op8 Ac[2], Ab[2];
   split_state(Ac, Wc);
   if (!MB16) {
@@ -473,27 +523,49 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
   Rows kc1 = rows8<BF16>(tile_rows(L.st, 1, 0, 1), c, g);
   L.bkb[0][w][lane] = times_state<LO>(Ac, kc0);
   L.bkb[1][w][lane] = times_state<LO>(Ac, kc1);
+  if (w == 0) {
+    L.grb[1][0][lane] = hilo(split4(gram<LO>(kc0, kc1)));
+  } else if (w == 1) {
+    L.grb[1][1][lane] = u32x4{0u, 0u, 0u, 0u};
+  } else if (w == 3 && LN) {
+    L.tkb[0][c] = token_inputs(kc0, rows8<BF16>(tile_rows(L.st, 2, 0, 0), c, g));
+    L.tkb[1][c] = token_inputs(kc1, rows8<BF16>(tile_rows(L.st, 2, 0, 1), c, g));
+  }
   lds_barrier();  // B
   lds_barrier();  // period 0 starts
 
-  Op4 kt1[4] = {};  // K_{p-1}^T (16x16x16 A operands)
-  for (int blk = 0; blk * TB <= n + 1; ++blk) {
-    const bool next_block = (blk + 1) * TB < n;
+  // the update waves' work of a period is the longest: they go first
+  __builtin_amdgcn_s_setprio(3);
+  Op4 kt1[4] = {};                   // K_{p-1}^T (16x16x16 A operands)
+  f32x4 qw1 = {0.f, 0.f, 0.f, 0.f};  // (Q_{p-1} W_{p-2})^T
+  Split4 m1 = {};                    // tril(K_{p-1} Q_{p-1}^T) (hi only for bf16 data)
+  float muq1 = 0.f;                  // q . w_bar, tile p-1
+  for (int blk = 0; blk * TB <= n + 2; ++blk) {
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int p = blk * TB + tb;
-      if (p > n + 1) break;
-      // refill the other buffer: nobody reads tiles before p any more
-      if (tb == 0 && next_block)
-        stage_issue<BF16, TB>(L.st, a.q, a.k, a.v, a.eta, x.row0, blk + 1, T, (blk + 1) & 1, w);
+      if (p > n + 2) break;
       // every LDS read of the period first
       const auto* Kp = tile_rows(L.st, 1, blk, tb);
       const u32x4 g1 = L.gtb[(p - 1) & 1][w][lane];  // (-eta G_{p-1})^T as [hi, lo]
       const Rows qr = rows8<BF16>(tile_rows(L.st, 0, blk, tb), c, g);
       const Rows kn = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 2), c, g);
+      Rows vn;
+      if (w == 3 && LN) vn = rows8<BF16>(tile_rows(L.st, 2, blk, tb + 2), c, g);
       Op4 ktn[4];
       if constexpr (!BF16) cols8<BF16>(ktn, Kp, c, g);
       __builtin_amdgcn_sched_barrier(0);
+      // ---- output pre-activation of tile p-1 around its shift:
+      //      (Q W_{p-2})^T + (-eta G_{p-1})^T tril(K Q^T) - q . w_bar
+      {
+        f32x4 d = mfma16(hi_of(g1), m1.hi, f32x4{0.f, 0.f, 0.f, 0.f});
+        d = mfma16(lo_of(g1), m1.hi, d);
+        if (LO) d = mfma16(hi_of(g1), m1.lo, d);
+        f32x4 e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = (qw1[i] + d[i]) - muq1;
+        L.hqb[p & 1][w][lane] = e;
+      }
       // ---- W += K_{p-1}^T (-eta G_{p-1})
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -501,30 +573,13 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         Wc[r] = mfma16(kt1[r].hi, lo_of(g1), Wc[r]);
         if (LO) Wc[r] = mfma16(kt1[r].lo, hi_of(g1), Wc[r]);
       }
-      split_state(Ac, Wc);  // W_{p-1}
+      split_state_mm(Ac, Wc, neg_ident);  // W_{p-1}
       if (!MB16 && mbs(p)) {
         Ab[0] = Ac[0];
         Ab[1] = Ac[1];
       }
       // ---- products of W_{p-1} (past the end: stale rows, unused)
-      L.qwb[p & 1][w][lane] = times_state<LO>(Ac, qr);
-      if constexpr (BF16) {
-        // K_p^T for the next update from the rows of K_p: half of a row
-        // operand times the identity is the transposed 16x16 block, whose
-        // rows are the state's features feat(r, c)
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const u32x4 h = kc0.p[r >> 1].hi;
-          const f32x4 t = mfma16((r & 1) ? u32x2{h.z, h.w} : u32x2{h.x, h.y}, ident, zero);
-          kt1[r] = Op4{u32x2{pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])}, u32x2{0u, 0u}};
-        }
-        kc0 = kc1;
-        kc1 = kn;
-      } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) kt1[r] = ktn[r];
-      }
+      qw1 = times_state<LO>(Ac, qr);
       {
         // gradient point two tiles ahead: K_{p+2} W_{p-1}, or the
         // mini-batch's own gradient point when no update reaches it
@@ -533,9 +588,45 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         else bk = times_state<LO>(Ab, kn);
         L.bkb[p & 1][w][lane] = bk;
       }
-      // the next block must be visible by the barrier that opens the period
-      // reading its first tile two ahead
-      if (tb == TB - 3 && next_block) wait_vmem();
+      // ---- tile p: its output score tile and shift, for the next period
+      {
+        f32x4 M = gram<LO>(kc0, qr);  // K_p Q_p^T
+#pragma unroll
+        for (int i = 0; i < 4; ++i) M[i] = causal[i] ? M[i] : 0.f;
+        if (LO) m1 = split4(M);
+        else m1.hi = u32x2{pack_bf16(M[0], M[1]), pack_bf16(M[2], M[3])};
+        if (LN) {
+          const f32x4 sq = stats<LO>(ast, qr);
+          muq1 = sq[0] + sq[2];
+        }
+      }
+      // ---- column-independent inputs of tile p+2 for the chain, one wave
+      //      each: the score tiles K_{p+1} K_{p+2}^T, K_p K_{p+2}^T and
+      //      (k . w_bar, sum_f u_f)
+      if (w == 0) {
+        L.grb[p & 1][0][lane] = hilo(split4(gram<LO>(kc1, kn)));
+      } else if (w == 1) {
+        L.grb[p & 1][1][lane] = hilo(split4(gram<LO>(kc0, kn)));
+      } else if (w == 3 && LN) {
+        L.tkb[p & 1][c] = token_inputs(kn, vn);
+      }
+      // ---- K_p^T for the next update
+      if constexpr (BF16) {
+        // half of a row operand times the identity is the transposed 16x16
+        // block, whose rows are the state's features feat(r, c)
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const u32x4 h = kc0.p[r >> 1].hi;
+          const f32x4 t = mfma16((r & 1) ? u32x2{h.z, h.w} : u32x2{h.x, h.y}, ident, zero);
+          kt1[r] = Op4{u32x2{pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])}, u32x2{0u, 0u}};
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kt1[r] = ktn[r];
+      }
+      kc0 = kc1;
+      kc1 = kn;
       lds_barrier();
     }
   }
@@ -550,174 +641,92 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
 }
 
 // ---------------------------------------------------------------------------
-// Output waves: z, and (one wave per item) the column-independent inputs.
+// Output waves: output LN and z.  Period p receives the pre-activation of
+// tile p-2 (around its shift), exchanges its LN sums, and stores z of tile
+// p-3.
 template <bool BF16, bool LN, bool RES, bool MB16>
 __device__ __forceinline__ void output_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x) {
   constexpr int TB = LinCfg<BF16>::TB;
-  constexpr bool LO = !BF16;
   const int lane = x.lane, g = x.g, c = x.c, w = x.w, fo = x.fo, n = x.n, T = x.T;
 
   f32x4 gam = {1.f, 1.f, 1.f, 1.f}, bet = {0.f, 0.f, 0.f, 0.f};
-  float s2gb = 0.f;  // sum_f 2 gamma beta
   if (LN) {
-    const float* gp = a.gamma + (size_t)x.head * D;
-    const float* bp = a.beta + (size_t)x.head * D;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      gam[i] = gp[fo + i];
-      bet[i] = bp[fo + i];
-    }
-    for (int j = 0; j < D; ++j) s2gb += 2.f * gp[j] * bp[j];
-    if (w == 1) {  // 2 gamma rows of the dot-product operand, as bf16 hi/lo
-      const float v = 2.f * gp[lane];
-      const uint32_t h = bf16_bits(v);
-      L.cst[1][lane] = (uint16_t)h;
-      L.cst[3][lane] = (uint16_t)bf16_bits(v - __builtin_bit_cast(float, h << 16));
+      gam[i] = a.gamma[(size_t)x.head * D + fo + i];
+      bet[i] = a.beta[(size_t)x.head * D + fo + i];
     }
   }
-  if (w == 3) {  // "tile -1": zero output in period 0
-    L.mqb[1][lane] = u32x4{0u, 0u, 0u, 0u};
-    if (lane < 16) L.mqm[1][lane] = 0.f;
-  }
-  bool causal[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) causal[i] = (4 * g + i) <= c;
+  L.hqb[1][w][lane] = f32x4{0.f, 0.f, 0.f, 0.f};  // "tile -2"
   const u32x2 ident = ident_op(g, c);
   const ZOut<BF16> zo(a.z, x.row0, T);
 
   lds_barrier();  // A
-  u32x4 ast[2] = {};
-  if (LN) {
-#pragma unroll
-    for (int p = 0; p < 2; ++p)
-      ast[p] = *reinterpret_cast<const u32x4*>(&L.cst[c & 3][32 * p + 8 * g]);
-  }
-  // (k . w_bar, sum_f u_f) of a tile from its rows of k and v, one product
-  // per tensor
-  auto token_inputs = [&](const Rows& kr, const Rows& vr) -> f32x2 {
-    const f32x4 sk = stats<LO>(ast, kr);
-    const f32x4 sv = stats<LO>(ast, vr);
-    const float su = ((RES ? sk[1] + sk[3] : 0.f) - (sv[1] + sv[3])) + s2gb;
-    return f32x2{sk[0] + sk[2], su};
-  };
-  if (w == 0) {
-    if (LN) {
-      L.tkb[0][c] = token_inputs(rows8<BF16>(tile_rows(L.st, 1, 0, 0), c, g),
-                                 rows8<BF16>(tile_rows(L.st, 2, 0, 0), c, g));
-      L.tkb[1][c] = token_inputs(rows8<BF16>(tile_rows(L.st, 1, 0, 1), c, g),
-                                 rows8<BF16>(tile_rows(L.st, 2, 0, 1), c, g));
-    }
-  } else if (w == 1) {
-    L.grb[1][0][lane] = hilo(split4(gram<LO>(rows8<BF16>(tile_rows(L.st, 1, 0, 0), c, g),
-                                             rows8<BF16>(tile_rows(L.st, 1, 0, 1), c, g))));
-  } else if (w == 2) {
-    L.grb[1][1][lane] = u32x4{0u, 0u, 0u, 0u};
-  }
   lds_barrier();  // B
   lds_barrier();  // period 0 starts
 
-  f32x4 qb1 = {0.f, 0.f, 0.f, 0.f}, qb2 = qb1;  // q + beta (residual part of z), tiles p-1, p-2
-  f32x4 eq2 = qb1;                              // output pre-activation around its shift, tile p-2
-  for (int blk = 0; blk * TB <= n + 1; ++blk) {
+  // q + beta (the residual part of z) of tiles p-1, p-2 and p-3; the
+  // pre-activation of tile p-3 around its shift
+  f32x4 qb1 = {0.f, 0.f, 0.f, 0.f}, qb2 = qb1, qb3 = qb1, eq3 = qb1;
+  constexpr int PARTS = TB >= 7 ? 4 : 1;  // periods over which a refill is issued
+  for (int blk = 0; blk * TB <= n + 2; ++blk) {
+    const bool next_block = (blk + 1) * TB < n;
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
       const int p = blk * TB + tb;
-      if (p > n + 1) break;
+      if (p > n + 2) break;
+      // refill the other buffer (nobody reads tiles before p any more), a
+      // part per period so that no period carries all the copy instructions
+      if (tb < PARTS && next_block)
+        stage_issue<BF16, TB>(L.st, a.q, a.k, a.v, a.eta, x.row0, blk + 1, T, (blk + 1) & 1, w,
+                              tb, PARTS);
       // every LDS read of the period first
-      const u32x4 g1 = L.gtb[(p - 1) & 1][w][lane];  // (-eta G_{p-1})^T as [hi, lo]
+      const f32x4 e = L.hqb[(p - 1) & 1][w][lane];  // tile p-2
       f32x4 s01 = {}, s23 = {};
-      float muq = 0.f;
       if (LN) {
         s01 = *reinterpret_cast<const f32x4*>(&L.xo[(p - 1) & 1][c][0]);
         s23 = *reinterpret_cast<const f32x4*>(&L.xo[(p - 1) & 1][c][2]);
-        muq = L.mqm[(p - 1) & 1][c];
       }
-      const u32x4 m = L.mqb[(p - 1) & 1][lane];
-      const f32x4 qw = L.qwb[(p - 1) & 1][w][lane];
       const auto* Qp = tile_rows(L.st, 0, blk, tb);
-      const auto* Kp = tile_rows(L.st, 1, blk, tb);
-      const auto* K2 = tile_rows(L.st, 1, blk, tb + 2);
       u32x2 q4 = {0u, 0u};
       f32x4 qv = {0.f, 0.f, 0.f, 0.f};
       if constexpr (BF16) q4 = quad(Qp, c, fo);
       else qv = val4(Qp + lds_off<false>(c, fo));
-      // operands of this wave's column-independent item
-      Rows ra, rb;
-      if (w == 0) {
-        ra = rows8<BF16>(K2, c, g);
-        rb = rows8<BF16>(tile_rows(L.st, 2, blk, tb + 2), c, g);
-      } else if (w == 1) {
-        ra = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 1), c, g);
-        rb = rows8<BF16>(K2, c, g);
-      } else if (w == 2) {
-        ra = rows8<BF16>(Kp, c, g);
-        rb = rows8<BF16>(K2, c, g);
-      } else {
-        ra = rows8<BF16>(Kp, c, g);
-        rb = rows8<BF16>(Qp, c, g);
-      }
       __builtin_amdgcn_sched_barrier(0);
-      // ---- z of tile p-2 (its output LN sums came with the last barrier)
       if (LN) {
+        // ---- z of tile p-3 (its LN sums came with the last barrier)
         const f32x4 s = s01 + s23;
         const float mr = (s[0] + s[2]) * (1.0f / D);
         const float var = __builtin_fmaf(-mr, mr, (s[1] + s[3]) * (1.0f / D));
         const float rs = __frsqrt_rn(var + a.eps);
         f32x4 zf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) zf[i] = __builtin_fmaf(gam[i] * rs, eq2[i] - mr, qb2[i]);
-        zo.store((p - 2) * 16 + c, fo, zf);
-      }
-      // ---- output of tile p-1: H_q^T = (Q W_{p-2})^T + (-eta G_{p-1})^T tril(K Q^T)
-      {
-        f32x4 d = mfma16(hi_of(g1), hi_of(m), f32x4{0.f, 0.f, 0.f, 0.f});
-        d = mfma16(lo_of(g1), hi_of(m), d);
-        if (LO) d = mfma16(hi_of(g1), lo_of(m), d);
-        const f32x4 hq = qw + d;
-        if (LN) {
+        for (int i = 0; i < 4; ++i) zf[i] = __builtin_fmaf(gam[i] * rs, eq3[i] - mr, qb3[i]);
+        zo.store((p - 3) * 16 + c, fo, zf);
+        // ---- LN sums of tile p-2
+        const float q6 = (e[0] + e[1]) + (e[2] + e[3]);
+        float q7 = e[0] * e[0];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) eq2[i] = hq[i] - muq;
-          const float q6 = (eq2[0] + eq2[1]) + (eq2[2] + eq2[3]);
-          float q7 = eq2[0] * eq2[0];
-#pragma unroll
-          for (int i = 1; i < 4; ++i) q7 = __builtin_fmaf(eq2[i], eq2[i], q7);
-          const float t = swap32_sum(q6, q7);
-          // groups 0, 1 hold the sum of q6, groups 2, 3 that of q7
-          reinterpret_cast<float*>(&L.xo[p & 1][c][w])[g >> 1] = swap16_sum(t, t);
-        } else {
-          zo.store((p - 1) * 16 + c, fo, qb1 + hq);
-        }
-        qb2 = qb1;
+        for (int i = 1; i < 4; ++i) q7 = __builtin_fmaf(e[i], e[i], q7);
+        const float t = swap32_sum(q6, q7);
+        // groups 0, 1 hold the sum of q6, groups 2, 3 that of q7
+        reinterpret_cast<float*>(&L.xo[p & 1][c][w])[g >> 1] = swap16_sum(t, t);
+      } else {
+        zo.store((p - 2) * 16 + c, fo, qb2 + e);
       }
-      // ---- tile p (past the end: stale rows, unused)
+      eq3 = e;
+      qb3 = qb2;
+      qb2 = qb1;
+      // ---- q + beta of tile p (past the end: stale rows, unused)
       if constexpr (BF16) {
         qb1 = RES ? mfma16(ident, q4, bet) : bet;
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) qb1[i] = (RES ? qv[i] : 0.f) + bet[i];
       }
-      // ---- column-independent inputs, one wave each: (k . w_bar,
-      //      sum_f u_f) of tile p+2, the score tiles K_{p+1} K_{p+2}^T and
-      //      K_p K_{p+2}^T, and tril(K_p Q_p^T), q . w_bar of tile p
-      if (w == 0) {
-        if (LN) L.tkb[p & 1][c] = token_inputs(ra, rb);
-      } else if (w == 1 || w == 2) {
-        L.grb[p & 1][w - 1][lane] = hilo(split4(gram<LO>(ra, rb)));
-      } else {
-        const Rows& qr = rb;
-        f32x4 M = gram<LO>(ra, qr);  // K_p Q_p^T
-#pragma unroll
-        for (int i = 0; i < 4; ++i) M[i] = causal[i] ? M[i] : 0.f;
-        if (LO) {
-          L.mqb[p & 1][lane] = hilo(split4(M));
-        } else {
-          L.mqb[p & 1][lane] = u32x4{pack_bf16(M[0], M[1]), pack_bf16(M[2], M[3]), 0u, 0u};
-        }
-        if (LN) {
-          const f32x4 sq = stats<LO>(ast, qr);
-          L.mqm[p & 1][c] = sq[0] + sq[2];
-        }
-      }
+      // the next block must be visible by the barrier that opens the period
+      // reading its first tile two ahead
+      if (tb == TB - 3 && next_block) wait_vmem();
       lds_barrier();
     }
   }

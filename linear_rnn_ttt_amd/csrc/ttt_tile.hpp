@@ -50,10 +50,13 @@ struct Stage {
 // moves 1 KB per instruction; lane l lands at byte 16 l of it, so the lane
 // picks the source chunk that belongs in that swizzled slot.  Rows past T
 // re-read row T-1 (finite data; their eta is ignored by the scan).
+// The share can be issued in `parts` calls (part = 0 .. parts-1), which
+// spreads the copy instructions of a block over several tiles.
 template <bool BF16, int TB>
 __device__ __forceinline__ void stage_issue(Stage<BF16, TB>& L, const void* q, const void* k,
                                             const void* v, const float* eta, size_t row0,
-                                            int blk, int T, int buf, int w) {
+                                            int blk, int T, int buf, int w, int part = 0,
+                                            int parts = 1) {
   using E = typename Io<BF16>::E;
   constexpr int TOK = TB * 16;
   constexpr int RB = D * sizeof(E);            // row bytes
@@ -71,12 +74,13 @@ __device__ __forceinline__ void stage_issue(Stage<BF16, TB>& L, const void* q, c
     const size_t goff = (row0 + tok) * (size_t)RB + j * 16;
 #pragma unroll
     for (int x = 0; x < 3; ++x) {
+      if ((3 * n + x) % parts != part) continue;
       TTT_LDS void* dst = (TTT_LDS void*)(reinterpret_cast<char*>(L.qkv[buf][x]) +
                                           (NI * w + n) * 1024);
       __builtin_amdgcn_global_load_lds(src[x] + goff, dst, 16, 0, 0);
     }
   }
-  if (w * 64 < TOK) {
+  if (part == 0 && w * 64 < TOK) {
     const int tok = min(tok0 + w * 64 + l, T - 1);
     TTT_LDS void* dst = (TTT_LDS void*)(&L.eta[buf][w * 64]);
     __builtin_amdgcn_global_load_lds(eta + row0 + tok, dst, 4, 0, 0);
