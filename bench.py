@@ -41,8 +41,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 KERNEL_SOURCES = {
-    "linear": ["ttt_linear.hip", "ttt_device.hpp", "ttt_kernels.hpp"],
-    "mlp": ["ttt_mlp.hip", "ttt_device.hpp", "ttt_kernels.hpp"],
+    "linear": ["ttt_linear.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp"],
+    "mlp": ["ttt_mlp.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp"],
 }
 KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd"}
 
