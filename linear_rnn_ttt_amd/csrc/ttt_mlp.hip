@@ -18,21 +18,32 @@
 //     W2 -= A_k^T (eta G_o), b2 -= 1^T (eta G_o)
 // (the "+ 1" terms are the bias updates seen by later tokens of the tile).
 //
-// Mapping onto one CU:
-//   * one 256-thread workgroup (4 waves) per (batch, head) unit; wave w owns
-//     hidden units 64w..64w+63: W1[:, 64w:64w+64], b1[64w:64w+64] and
-//     W2[64w:64w+64, :] stay in fp32 MFMA accumulator registers for the
-//     whole sequence (the biases as 16x16 tiles with equal columns, updated
-//     by a product with an all-ones operand);
-//   * the hidden pre-activations are produced transposed (lane: 4 hidden
-//     units of one token), the output pre-activations as per-wave partial
-//     sums over the wave's hidden units, added across waves in LDS; wave w
-//     then owns output features 16w..16w+15 for the LayerNorm, whose row
-//     sums are exchanged once per LN;
-//   * W2 is needed with either index contracted (A_k W2 and G_o W2^T): the
-//     W2^T operand is made each tile by a transpose on the matrix unit;
-//   * with bf16 inputs the products take plain bf16 operands (state kept in
+// Mapping onto one CU: one 512-thread workgroup (8 waves, two per SIMD) per
+// (batch, head) unit.
+//   * Wave w owns hidden units 32w..32w+31: W1[:, 32w:32w+32], b1[32w:32w+32]
+//     and W2[32w:32w+32, :] stay in fp32 MFMA accumulator registers for the
+//     whole sequence.  W2 is kept twice, as W2 and as W2^T: the forward
+//     product A W2 contracts the hidden index and the backward product
+//     G_o W2^T the feature index, and an accumulator tile only serves a
+//     contraction over its row index.  Both copies take the same rank-16
+//     update with the two operands swapped, which is cheaper than a
+//     transpose of W2 every tile.  b1 is held as 16x16 tiles with equal
+//     columns, updated by a product with an all-ones operand; b2 likewise,
+//     feature tile w % 4 in wave w.  Waves 0-3 add their b2 tile to their
+//     O_k partial sums, waves 4-7 to their O_q partial sums, so each sum
+//     holds b2 once.
+//   * Hidden pre-activations come out transposed (lane: 4 hidden units of
+//     one token), the output pre-activations as per-wave partial sums over
+//     the wave's hidden units, added up in LDS.
+//   * Waves 0-3 run the LayerNorm backward of O_k (wave w: output features
+//     16w..16w+15) and publish -eta G_o; waves 4-7 run the LayerNorm of the
+//     previous tile's O_q and store Z.  Deferring the output by one tile lets
+//     both LayerNorms share the three workgroup barriers of a tile.
+//   * With bf16 inputs the products take plain bf16 operands (state kept in
 //     fp32); with fp32 inputs every operand is a bf16 hi + lo pair.
+//   * 16x16x32 and 16x16x16 products never feed each other's accumulator
+//     input directly: mixed-shape accumulator chains gave wrong values on
+//     this toolchain, so such sums start from zero and are added with VALU.
 #include <math.h>
 
 #include "ttt_device.hpp"
@@ -42,53 +53,82 @@
 namespace tttk {
 namespace {
 
-constexpr int NT = 256;   // threads per workgroup
-constexpr int MH = 256;   // hidden width
-constexpr int TBM = 4;    // tiles per staged block
+constexpr int NW = 8;         // waves per workgroup
+constexpr int NT = 64 * NW;   // threads per workgroup
+constexpr int MH = 256;       // hidden width
+constexpr int HW = MH / NW;   // hidden units per wave
+
+// Tiles per staged block: 4 (bf16) or 2 (fp32) keep the workgroup's LDS
+// near 125 KB.
+template <bool BF16>
+constexpr int tiles_per_block() {
+  return BF16 ? 4 : 2;
+}
 
 template <bool BF16>
 struct MlpLds {
-  Stage<BF16, TBM> st;
-  f32x4 part[4][4][64];   // per-wave partial O^T tiles [wave][feature tile][lane]
-  f32x4 xch[4][2][16];    // LN partial sums [wave][round][token]
-  u32x4 gath[4][2][64];   // -eta G_o of each wave's feature tile: [wave][layout][lane]
+  Stage<BF16, tiles_per_block<BF16>()> st;
+  f32x4 pk[NW][4][64];    // partial O_k^T tiles [wave][feature tile][lane]
+  f32x4 pq[NW][4][64];    // partial O_q^T tiles, summed one tile later
+  f32x4 xk[4][2][16];     // LN partial sums of O_k [feature tile][round][token]
+  f32x4 xq[4][2][16];     // the same for O_q (round 0 only)
+  u32x4 gath[4][2][64];   // -eta G_o per feature tile, in two layouts
+  f32x4 gam[16], bet[16]; // LN gamma, beta of the head (4 features per entry)
+  f32x4 gsq;              // sum of gamma^2 over each 16-feature tile
 };
 
-// erf-form GELU and its derivative: GELU(x) = x Phi(x),
-// GELU'(x) = Phi(x) + x phi(x), Phi(x) = (1 + erf(x / sqrt 2)) / 2.
+// Phi(x) and e^{-x^2/2} with one exponential and one reciprocal.  For
+// y >= 0, erfc(y) is approximated by t (a1 + t (a2 + t (a3 + t (a4 + t a5))))
+// e^{-y^2} with t = 1 / (1 + p y) (Abramowitz and Stegun, Handbook of
+// Mathematical Functions, formula 7.1.26: absolute error at most 1.5e-7),
+// here at y = |x| / sqrt 2, so that e^{-y^2} is also the Gaussian factor of
+// GELU'.  In fp32 the result is within 3e-7 of Phi.
+struct PhiExp {
+  float phi, ex;
+};
+__device__ __forceinline__ PhiExp phi_exp(float x) {
+  constexpr float P = 0.3275911f * 0.70710678118654752f;   // p / sqrt 2
+  constexpr float A1 = 0.5f * 0.254829592f;                 // a_i / 2: Phi(-y) = erfc / 2
+  constexpr float A2 = 0.5f * -0.284496736f;
+  constexpr float A3 = 0.5f * 1.421413741f;
+  constexpr float A4 = 0.5f * -1.453152027f;
+  constexpr float A5 = 0.5f * 1.061405429f;
+  const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(x), P, 1.0f));
+  const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, A5, A4), A3), A2), A1);
+  const float ex = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);   // e^{-x^2/2}
+  const float h = poly * ex;                                                 // Phi(-|x|)
+  return PhiExp{x >= 0.f ? 1.0f - h : h, ex};
+}
+// GELU(x) = x Phi(x) and GELU'(x) = Phi(x) + x phi(x), phi the normal density.
 __device__ __forceinline__ void gelu2(float x, float& y, float& dy) {
-  const float ph = 0.5f * (1.0f + erff(x * 0.70710678118654752f));
-  y = x * ph;
-  dy = ph + x * 0.39894228040143268f * expf(-0.5f * x * x);
+  const PhiExp r = phi_exp(x);
+  y = x * r.phi;
+  dy = fmaf(x * r.ex, 0.39894228040143268f, r.phi);
 }
-__device__ __forceinline__ float gelu(float x) {
-  return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f));
-}
+__device__ __forceinline__ float gelu(float x) { return x * phi_exp(x).phi; }
 
-// Sums over 16 features of each token in the LN layout (lane (g,c): token
-// c, features 4g+i of the wave's tile), combined across the 4 waves through
-// LDS with local centring.  Returns, per token, the mean, 1/sigma and the
-// two means the LN backward needs (when `bwd`):
-//   ma = mean(gamma gy), mx = mean(gamma gy xhat) with gy = u + 2 gamma^2 xhat.
-struct LnStat {
-  float mean, rs, ma, mx;
-};
+// LayerNorm statistics of a 16-token x 64-feature tile spread over four
+// waves (lane (g,c) of the wave for feature tile ft: token c, features
+// 16 ft + 4g + i).  ln_publish writes the wave's sums over its 16 features,
+// centred on their local mean; after a barrier ln_combine merges the four
+// (parallel-variance update) into, per token, the mean, 1/sigma and, for the
+// backward (gy = u + 2 gamma^2 xhat), ma = mean(gamma gy) and
+// mx = mean(gamma gy xhat).
 template <bool BWD>
-__device__ __forceinline__ LnStat ln_stats(f32x4 (&xch)[4][2][16], f32x4 h, f32x4 u,
-                                           f32x4 gam2, const float (&Gam)[4], float eps, int w,
-                                           int g, int c) {
+__device__ __forceinline__ void ln_publish(f32x4 (&x)[4][2][16], int ft, f32x4 h, f32x4 u,
+                                           f32x4 gam, int g, int c) {
+  const f32x4 gam2 = gam * gam;
   const float s1 = group_sum(h[0] + h[1] + h[2] + h[3]);
   const float mw = s1 * (1.0f / 16.0f);
-  f32x4 e;
   float P = 0.f, A = 0.f, Bq = 0.f, C = 0.f, U = 0.f;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    e[i] = h[i] - mw;
-    P += e[i] * e[i];
+    const float e = h[i] - mw;
+    P += e * e;
     if (BWD) {
-      A += gam2[i] * e[i];
-      Bq += u[i] * e[i];
-      C += gam2[i] * e[i] * e[i];
+      A += gam2[i] * e;
+      Bq += u[i] * e;
+      C += gam2[i] * e * e;
       U += u[i];
     }
   }
@@ -100,15 +140,22 @@ __device__ __forceinline__ LnStat ln_stats(f32x4 (&xch)[4][2][16], f32x4 h, f32x
     U = group_sum(U);
   }
   if (g == 0) {
-    xch[w][0][c] = f32x4{s1, P, A, Bq};
-    xch[w][1][c] = f32x4{C, U, 0.f, 0.f};
+    x[ft][0][c] = f32x4{s1, P, A, Bq};
+    if (BWD) x[ft][1][c] = f32x4{C, U, 0.f, 0.f};
   }
-  lds_barrier();
+}
+
+struct LnStat {
+  float mean, rs, ma, mx;
+};
+template <bool BWD>
+__device__ __forceinline__ LnStat ln_combine(const f32x4 (&x)[4][2][16], f32x4 Gam, float eps,
+                                             int c) {
   f32x4 s0[4], s1v[4];
 #pragma unroll
   for (int ww = 0; ww < 4; ++ww) {
-    s0[ww] = xch[ww][0][c];
-    s1v[ww] = xch[ww][1][c];
+    s0[ww] = x[ww][0][c];
+    if (BWD) s1v[ww] = x[ww][1][c];
   }
   const float mu = (s0[0][0] + s0[1][0] + s0[2][0] + s0[3][0]) * (1.0f / 64.0f);
   float M2 = 0.f, SgE = 0.f, SuE = 0.f, SgE2 = 0.f, Su = 0.f;
@@ -126,19 +173,29 @@ __device__ __forceinline__ LnStat ln_stats(f32x4 (&xch)[4][2][16], f32x4 h, f32x
   LnStat r;
   r.mean = mu;
   r.rs = __frsqrt_rn(M2 * (1.0f / 64.0f) + eps);
-  r.ma = (Su + 2.0f * r.rs * SgE) * (1.0f / 64.0f);
-  r.mx = (r.rs * SuE + 2.0f * r.rs * r.rs * SgE2) * (1.0f / 64.0f);
+  r.ma = 0.f;
+  r.mx = 0.f;
+  if (BWD) {
+    r.ma = (Su + 2.0f * r.rs * SgE) * (1.0f / 64.0f);
+    r.mx = (r.rs * SuE + 2.0f * r.rs * r.rs * SgE2) * (1.0f / 64.0f);
+  }
   return r;
+}
+
+// Both bf16 halves of two accumulator tiles as one 16x16x32 operand.
+__device__ __forceinline__ Op8 pair_op(const Split4& a, const Split4& b) {
+  return Op8{cat(a.hi, b.hi), cat(a.lo, b.lo)};
 }
 
 template <bool BF16, bool LN, bool RES>
 __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
   using E = typename Io<BF16>::E;
-  constexpr bool SP = !BF16;  // hi + lo operands
+  constexpr bool SP = !BF16;   // hi + lo operands
+  constexpr int TBM = tiles_per_block<BF16>();
   __shared__ MlpLds<BF16> L;
 
   const int tid = threadIdx.x;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int lane = tid & 63;
   const int g = lane >> 4;
   const int c = lane & 15;
@@ -146,244 +203,85 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
   const int head = unit % a.H;
   const int T = a.T;
   const size_t row0 = (size_t)unit * T;
-  const int HB = 64 * w;          // the wave's hidden units
-  const int fo = 16 * w + 4 * g;  // LN layout: lane holds token c, features fo..fo+3
+  const int HB = HW * w;          // the wave's hidden units
+  const bool kside = w < 4;       // LN backward of O_k (else: LN of O_q and Z)
+  const int ft = w & 3;           // feature tile of the wave's LN role
+  const int fo = 16 * ft + 4 * g; // LN layout: lane holds token c, features fo..fo+3
   const size_t s0 = a.state0_per_batch ? (size_t)unit : (size_t)head;
 
   // ---- state --------------------------------------------------------------
   // W1c[r][n] lane (g,c) = W1[16r + 4g + i][HB + 16n + c]
   // W2c[n][f] lane (g,c) = W2[HB + 16n + 4g + i][16f + c]
+  // W2t[f][n] lane (g,c) = W2[HB + 16n + c][16f + 4g + i]
   // b1v[n]    lane (g,c) = b1[HB + 16n + 4g + i]      (any c)
-  // b2w       lane (g,c) = b2[16w + 4g + i]           (any c)
-  f32x4 W1c[4][4], W2c[4][4], b1v[4], b2w;
+  // b2q       lane (g,c) = b2[16ft + 4g + i]          (any c)
+  f32x4 W1c[4][2], W2c[2][4], W2t[4][2], b1v[2], b2q;
   {
     const float* w1 = a.w1 + s0 * D * MH;
     const float* w2 = a.w2 + s0 * MH * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           W1c[r][n][i] = w1[(16 * r + 4 * g + i) * MH + HB + 16 * n + c];
-          W2c[r][n][i] = w2[(HB + 16 * r + 4 * g + i) * D + 16 * n + c];
+          W2c[n][r][i] = w2[(HB + 16 * n + 4 * g + i) * D + 16 * r + c];
+          W2t[r][n][i] = w2[(HB + 16 * n + c) * D + 16 * r + 4 * g + i];
         }
 #pragma unroll
-    for (int n = 0; n < 4; ++n)
+    for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int i = 0; i < 4; ++i) b1v[n][i] = a.b1[s0 * MH + HB + 16 * n + 4 * g + i];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) b2w[i] = a.b2[s0 * D + fo + i];
+    for (int i = 0; i < 4; ++i) b2q[i] = a.b2[s0 * D + 16 * ft + 4 * g + i];
   }
 
-  f32x4 gam = {1.f, 1.f, 1.f, 1.f}, bet = {0.f, 0.f, 0.f, 0.f}, gam2 = gam;
-  float Gam[4] = {16.f, 16.f, 16.f, 16.f};
-  if (LN) {
+  // LN parameters in LDS (read where used: fewer live registers)
+  if (LN && w == 0) {
     const float* gp = a.gamma + (size_t)head * D;
     const float* bp = a.beta + (size_t)head * D;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      gam[i] = gp[fo + i];
-      bet[i] = bp[fo + i];
-      gam2[i] = gam[i] * gam[i];
-    }
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) {
+    reinterpret_cast<float*>(L.gam)[lane] = gp[lane];
+    reinterpret_cast<float*>(L.bet)[lane] = bp[lane];
+    if (lane < 4) {
       float s = 0.f;
-      for (int j = 0; j < 16; ++j) s += gp[16 * ww + j] * gp[16 * ww + j];
-      Gam[ww] = s;
+      for (int j = 0; j < 16; ++j) s += gp[16 * lane + j] * gp[16 * lane + j];
+      reinterpret_cast<float*>(&L.gsq)[lane] = s;
     }
   }
+  auto ln_gam = [&]() { return L.gam[fo >> 2]; };
+  auto ln_bet = [&]() { return L.bet[fo >> 2]; };
   bool causal[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) causal[i] = (4 * g + i) <= c;
   const u32x2 ident = ident_op(g, c);
   const Op4 ones = {ones_op(), u32x2{0u, 0u}};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 
-  const int n_tiles = (T + 15) / 16;
-  stage_issue<BF16, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, 0, T, 0, tid >> 6);
-  wait_vmem();
-  lds_barrier();
-
-  for (int tile = 0; tile < n_tiles; ++tile) {
-    const int blk = tile / TBM, tb = tile % TBM, buf = blk & 1;
-    const bool next_block = (blk + 1) * TBM < n_tiles;
-    if (tb == 0 && next_block) {
-      // every wave has passed the previous tile's barriers: the other buffer
-      // (previous block) is free
-      stage_issue<BF16, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, blk + 1, T, buf ^ 1,
-                             tid >> 6);
-    }
-    const E* Lq = L.st.qkv[buf][0];
-    const E* Lk = L.st.qkv[buf][1];
-    const E* Lv = L.st.qkv[buf][2];
-    const int t0 = tb * 16;
-    const int tok = tile * 16 + c;
-    const bool valid = tok < T;
-    const float eta = L.st.eta[buf][t0 + c];
-
-    const Rows kb = load_rows<BF16>(Lk, t0, c, g);
-    const Rows qb = load_rows<BF16>(Lq, t0, c, g);
-    Op4 kt[4];
-    load_cols<BF16>(kt, Lk, t0, c, g);
-    const f32x4 kres = val4(Lk + lds_off<BF16>(t0 + c, fo));
-    const f32x4 vres = val4(Lv + lds_off<BF16>(t0 + c, fo));
-    const f32x4 qres = val4(Lq + lds_off<BF16>(t0 + c, fo));
-
-    // ---- hidden pre-activations (transposed: lane = token c, hidden
-    //      HB + 16n + 4g + i) ------------------------------------------------
-    f32x4 Pk[4];
+  // Q side: O_q of a finished tile -> LN -> Z (waves 4-7).  Partial sums
+  // are summed and published before one barrier, normalised and stored
+  // after the next.
+  auto q_publish = [&](f32x4& oq) {
+    f32x4 s = zero;
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      Pk[n] = b1v[n];
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        Pk[n] = mma8<SP, SP>(split_pair(W1c[2 * p][n], W1c[2 * p + 1][n]), kb.p[p], Pk[n]);
-    }
-    f32x4 Ak[4], Dk[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float y, dy;
-        gelu2(Pk[n][i], y, dy);
-        Ak[n][i] = y;
-        Dk[n][i] = dy;
-      }
-
-    // W2 as the A operand of W2^T for feature tile f, hidden tiles 2q, 2q+1:
-    // slots -> hidden HB + 32q + 4g + j (j<4), HB + 32q + 16 + 4g + j - 4 (j>=4)
-    auto w2op = [&](int q, int f) { return split_pair(W2c[2 * q][f], W2c[2 * q + 1][f]); };
-
-    // ---- O_k: partial over the wave's hidden units, summed across waves --
-    {
-      Op8 Akop[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) Akop[q] = split_pair(Ak[2 * q], Ak[2 * q + 1]);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < 2; ++q) o = mma8<SP, SP>(w2op(q, f), Akop[q], o);
-        L.part[w][f][lane] = o;
-      }
-    }
-    lds_barrier();
-    f32x4 ok = b2w;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) ok += L.part[ww][w][lane];
-
-    // ---- dl/dO_k for the wave's 16 output features, times -eta ------------
-    f32x4 ego;
-    if (LN) {
-      f32x4 u;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u[i] = 2.f * gam[i] * ((RES ? kres[i] : 0.f) + bet[i] - vres[i]);
-      const LnStat st = ln_stats<true>(L.xch, ok, u, gam2, Gam, a.eps, w, g, c);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float xh = (ok[i] - st.mean) * st.rs;
-        const float av = u[i] + 2.f * gam2[i] * xh;
-        ego[i] = valid ? -eta * st.rs * (av - st.ma - xh * st.mx) : 0.f;  // padding: exactly 0
-      }
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ego[i] = valid ? -2.f * eta * (ok[i] + (RES ? kres[i] : 0.f) - vres[i]) : 0.f;
-    }
-
-    // ---- share -eta G_o of every feature tile with every wave ---------------
-    const Split4 es = split4(ego);
-    const Op4 got_own = transpose_op<SP>(es, ident);   // lane: token 4g+i, feature 16w+c
-    L.gath[w][0][lane] = cat(es.hi, es.lo);
-    L.gath[w][1][lane] = cat(got_own.hi, got_own.lo);
-    lds_barrier();
-    Op4 egoL[4], got[4];
-#pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const u32x4 x = L.gath[f][0][lane];
-      const u32x4 y = L.gath[f][1][lane];
-      egoL[f] = Op4{u32x2{x[0], x[1]}, u32x2{x[2], x[3]}};  // lane: token c, feats 16f+4g+i
-      got[f] = Op4{u32x2{y[0], y[1]}, u32x2{y[2], y[3]}};   // lane: token 4g+i, feat 16f+c
-    }
-
-    // ---- -eta dl/dP_k = ((-eta G_o) W2^T) * GELU'(P_k) ----------------------
-    f32x4 egp[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        const Op4 w2t = transpose_op<SP>(split4(W2c[n][f]), ident);  // lane: W2[HB+16n+c][16f+4g+i]
-        acc = mma4<SP, SP>(w2t, egoL[f], acc);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) egp[n][i] = acc[i] * Dk[n][i];
-    }
-    Op4 gpt[4];   // lane: token 4g+i, hidden HB+16n+c
-#pragma unroll
-    for (int n = 0; n < 4; ++n) gpt[n] = transpose_op<SP>(split4(egp[n]), ident);
-
-    // ---- output: P_q, A_q, O_q (state before this tile's update) ------------
-    f32x4 Pq[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      Pq[n] = b1v[n];
-#pragma unroll
-      for (int p = 0; p < 2; ++p)
-        Pq[n] = mma8<SP, SP>(split_pair(W1c[2 * p][n], W1c[2 * p + 1][n]), qb.p[p], Pq[n]);
-    }
-    {
-      f32x4 M = gram<SP>(kb, qb);   // lane: k_{4g+i} . q_c
-#pragma unroll
-      for (int i = 0; i < 4; ++i) M[i] = causal[i] ? M[i] + 1.f : 0.f;
-#pragma unroll
-      for (int n = 0; n < 4; ++n) Pq[n] = correct<SP>(gpt[n], M, Pq[n]);
-    }
-    f32x4 Aq[4];
-#pragma unroll
-    for (int n = 0; n < 4; ++n)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Aq[n][i] = gelu(Pq[n][i]);
-    {
-      // this wave's share of tril(A_q A_k^T + 1): lane M[s = 4g+i][t = c]
-      f32x4 Ma = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int n = 0; n < 4; ++n) {
-        const Split4 sk = split4(Ak[n]), sq = split4(Aq[n]);
-        Ma = mma4<SP, SP>(Op4{sk.hi, sk.lo}, Op4{sq.hi, sq.lo}, Ma);
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) Ma[i] = causal[i] ? Ma[i] + (w == 0 ? 1.f : 0.f) : 0.f;
-      Op8 Aqop[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) Aqop[q] = split_pair(Aq[2 * q], Aq[2 * q + 1]);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        f32x4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int q = 0; q < 2; ++q) o = mma8<SP, SP>(w2op(q, f), Aqop[q], o);
-        o = correct<SP>(got[f], Ma, o);
-        L.part[w][f][lane] = o;
-      }
-    }
-    lds_barrier();
-    f32x4 oq = b2w;
-#pragma unroll
-    for (int ww = 0; ww < 4; ++ww) oq += L.part[ww][w][lane];
+    for (int ww = 0; ww < NW; ++ww) s += L.pq[ww][ft][lane];
+    oq = s;
+    if (LN) ln_publish<false>(L.xq, ft, oq, zero, ln_gam(), g, c);
+  };
+  auto q_store = [&](f32x4 oq, f32x4 qres, int t_tile) {
     f32x4 zf;
     if (LN) {
-      const f32x4 none = {0.f, 0.f, 0.f, 0.f};
-      const LnStat st = ln_stats<false>(L.xch, oq, none, gam2, Gam, a.eps, w, g, c);
+      const LnStat st = ln_combine<false>(L.xq, L.gsq, a.eps, c);
+      const f32x4 gam = ln_gam(), bet = ln_bet();
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         zf[i] = (RES ? qres[i] : 0.f) + gam[i] * ((oq[i] - st.mean) * st.rs) + bet[i];
     } else {
 #pragma unroll
       for (int i = 0; i < 4; ++i) zf[i] = (RES ? qres[i] : 0.f) + oq[i];
-      lds_barrier();  // every wave has read the partials before they are rewritten
     }
-    if (valid) {
+    const int tok = 16 * t_tile + c;
+    if (tok < T) {
       if (BF16) {
         const u32x2 o = {pack_bf16(zf[0], zf[1]), pack_bf16(zf[2], zf[3])};
         *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.z) + (row0 + tok) * D + fo) = o;
@@ -391,19 +289,214 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
         *reinterpret_cast<f32x4*>(static_cast<float*>(a.z) + (row0 + tok) * D + fo) = zf;
       }
     }
+  };
 
-    // ---- state update ---------------------------------------------------------
+  const int n_tiles = (T + 15) / 16;
+  stage_issue<BF16, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, 0, T, 0, w & 3, w >> 2, 2);
+  wait_vmem();
+  lds_barrier();
+
+  f32x4 qprev = zero;   // Q side: residual rows of the previous tile
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int blk = tile / TBM, tb = tile % TBM, buf = blk & 1;
+    const bool next_block = (blk + 1) * TBM < n_tiles;
+    if (tb == 0 && next_block) {
+      // every wave has passed the previous tile's last barrier, after which
+      // nothing reads the other buffer (previous block)
+      stage_issue<BF16, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, blk + 1, T, buf ^ 1, w & 3,
+                             w >> 2, 2);
+    }
+    const E* Lq = L.st.qkv[buf][0];
+    const E* Lk = L.st.qkv[buf][1];
+    const E* Lv = L.st.qkv[buf][2];
+    const int t0 = tb * 16;
+
+    // ================= phase A: K-side forward, O_k partials ==============
+    const Rows kb = load_rows<BF16>(Lk, t0, c, g);
+    const Rows qb = load_rows<BF16>(Lq, t0, c, g);
+
+    // W1 as the A operand of W1^T (two 32-deep halves of the features)
+    Op8 w1op[2][2];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-      Op4 akt;   // lane: token 4g+i, hidden HB+16n+c
-      akt = transpose_op<SP>(split4(Ak[n]), ident);
+    for (int p = 0; p < 2; ++p)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) w1op[p][n] = split_pair(W1c[2 * p][n], W1c[2 * p + 1][n]);
+
+    // hidden pre-activations, transposed: lane = token c, hidden HB + 16n + 4g + i
+    f32x4 Ak[2], Dk[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      f32x4 acc = zero;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) acc = mma8<SP, SP>(w1op[p][n], kb.p[p], acc);
+      acc += b1v[n];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float y, dy;
+        gelu2(acc[i], y, dy);
+        Ak[n][i] = y;
+        Dk[n][i] = dy;
+      }
+    }
+    const Split4 ak0 = split4(Ak[0]), ak1 = split4(Ak[1]);
+    const Op8 akop = pair_op(ak0, ak1);   // A_k over the wave's 32 hidden units
+
+    // W2 as the A operand of W2^T for feature tile f (32 hidden deep)
+    Op8 w2op[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      w2op[f] = split_pair(W2c[0][f], W2c[1][f]);
+      f32x4 o = mma8<SP, SP>(w2op[f], akop, zero);
+      if (kside && f == ft) o += b2q;
+      L.pk[w][f][lane] = o;
+    }
+
+    // the output side's products that need no gradient: Q W1 + b1, Q K^T
+    f32x4 Pq[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      f32x4 acc = zero;
+#pragma unroll
+      for (int p = 0; p < 2; ++p) acc = mma8<SP, SP>(w1op[p][n], qb.p[p], acc);
+      Pq[n] = acc + b1v[n];
+    }
+    f32x4 M = gram<SP>(kb, qb);   // lane: k_{4g+i} . q_c
+#pragma unroll
+    for (int i = 0; i < 4; ++i) M[i] = causal[i] ? M[i] + 1.f : 0.f;
+    // A_k^T tiles for the W2 update: lane = token 4g+i, hidden HB + 16n + c
+    const Op4 akt[2] = {transpose_op<SP>(ak0, ident), transpose_op<SP>(ak1, ident)};
+
+    lds_barrier();   // (1) O_k partials of this tile, O_q partials of the last
+
+    // ================= phase B: LN sums ===================================
+    f32x4 ok = zero, oq = zero, u = zero;   // u: the part of gamma dl/dy that is not in xhat
+    if (kside) {
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) ok += L.pk[ww][ft][lane];
+      const f32x4 kres = val4(Lk + lds_off<BF16>(t0 + c, fo));
+      const f32x4 vres = val4(Lv + lds_off<BF16>(t0 + c, fo));
+      if (LN) {
+        const f32x4 gam = ln_gam(), bet = ln_bet();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = 2.f * gam[i] * ((RES ? kres[i] : 0.f) + bet[i] - vres[i]);
+        ln_publish<true>(L.xk, ft, ok, u, gam, g, c);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) u[i] = (RES ? kres[i] : 0.f) - vres[i];
+      }
+    } else if (tile > 0) {
+      q_publish(oq);
+    }
+    if (LN) lds_barrier();   // (2) LN partial sums
+
+    // ================= phase C: -eta G_o (K side), Z of the last tile (Q side)
+    if (kside) {
+      const bool valid = 16 * tile + c < T;
+      const float eta = L.st.eta[buf][t0 + c];
+      f32x4 ego;
+      if (LN) {
+        const LnStat st = ln_combine<true>(L.xk, L.gsq, a.eps, c);
+        const f32x4 gam = ln_gam();
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float xh = (ok[i] - st.mean) * st.rs;
+          const float gy = u[i] + 2.f * gam[i] * gam[i] * xh;   // gamma dl/dy
+          ego[i] = valid ? -eta * st.rs * (gy - st.ma - xh * st.mx) : 0.f;   // padding: exactly 0
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ego[i] = valid ? -2.f * eta * (ok[i] + u[i]) : 0.f;
+      }
+      const Split4 es = split4(ego);
+      const Op4 got_own = transpose_op<SP>(es, ident);   // lane: token 4g+i, feature 16ft+c
+      L.gath[ft][0][lane] = cat(es.hi, es.lo);
+      L.gath[ft][1][lane] = cat(got_own.hi, got_own.lo);
+    } else {
+      if (tile > 0) q_store(oq, qprev, tile - 1);
+      qprev = val4(Lq + lds_off<BF16>(t0 + c, fo));
+    }
+    lds_barrier();   // (3) -eta G_o of every feature tile
+
+    // ================= phase D: backprop, output partials, update =========
+    Op4 egoL[4], got[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) {
+      const u32x4 x = L.gath[f][0][lane];
+      const u32x4 y = L.gath[f][1][lane];
+      egoL[f] = Op4{u32x2{x[0], x[1]}, u32x2{x[2], x[3]}};   // lane: token c, feats 16f+4g+i
+      got[f] = Op4{u32x2{y[0], y[1]}, u32x2{y[2], y[3]}};    // lane: token 4g+i, feat 16f+c
+    }
+
+    // -eta dl/dP_k = ((-eta G_o) W2^T) * GELU'(P_k), transposed like P_k
+    Op4 gpt[2];   // lane: token 4g+i, hidden HB + 16n + c
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      f32x4 acc = zero;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) acc = mma4<SP, SP>(op4_of(W2t[f][n]), egoL[f], acc);
+      gpt[n] = transpose_op<SP>(split4(acc * Dk[n]), ident);
+    }
+
+    // K^T tiles (lane: token 4g+i, feature 16r+c) from the rows by a
+    // product with the identity (exact: bf16 parts)
+    Op4 kt[4];
+    {
+      const Rows kr = load_rows<BF16>(Lk, t0, c, g);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int p = r >> 1, h = r & 1;
+        const Split4 part = {u32x2{kr.p[p].hi[2 * h], kr.p[p].hi[2 * h + 1]},
+                             u32x2{kr.p[p].lo[2 * h], kr.p[p].lo[2 * h + 1]}};
+        kt[r] = transpose_op<SP>(part, ident);
+      }
+    }
+    // W1 and b1 first: the next tile's first products wait on them
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) W1c[r][n] = mma4<SP, SP>(kt[r], gpt[n], W1c[r][n]);
       b1v[n] = mma4<SP, false>(gpt[n], ones, b1v[n]);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) W2c[n][f] = mma4<SP, SP>(akt, got[f], W2c[n][f]);
     }
-    b2w = mma4<SP, false>(got_own, ones, b2w);
+
+    // output: P_q, A_q, this wave's share of O_q (state before this tile's update)
+    f32x4 Aq[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const f32x4 p = correct<SP>(gpt[n], M, Pq[n]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Aq[n][i] = gelu(p[i]);
+    }
+    const Op8 aqop = pair_op(split4(Aq[0]), split4(Aq[1]));
+    // W2 operands again (cheaper than holding them since the first use)
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) asm volatile("" : "+v"(W2c[n][f]));
+#pragma unroll
+    for (int f = 0; f < 4; ++f) w2op[f] = split_pair(W2c[0][f], W2c[1][f]);
+    {
+      // this wave's share of tril(A_q A_k^T + 1): lane M[s = 4g+i][t = c]
+      f32x4 Ma = mma8<SP, SP>(akop, aqop, zero);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Ma[i] = causal[i] ? Ma[i] + (w == 0 ? 1.f : 0.f) : 0.f;
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        f32x4 o = mma8<SP, SP>(w2op[f], aqop, zero);
+        o = correct<SP>(got[f], Ma, o);
+        if (!kside && f == ft) o += b2q;
+        L.pq[w][f][lane] = o;
+      }
+    }
+
+    // W2 (both layouts) and b2
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        W2c[n][f] = mma4<SP, SP>(akt[n], got[f], W2c[n][f]);
+        W2t[f][n] = mma4<SP, SP>(got[f], akt[n], W2t[f][n]);
+      }
+    b2q = mma4<SP, false>(got[ft], ones, b2q);
 
     // the next block must be visible to every wave before its first tile
     if (tb == TBM - 1 && next_block) {
@@ -412,26 +505,39 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
     }
   }
 
+  // ---- Z of the last tile -----------------------------------------------------
+  lds_barrier();
+  f32x4 oq = zero;
+  if (!kside) q_publish(oq);
+  if (LN) lds_barrier();
+  if (!kside) q_store(oq, qprev, n_tiles - 1);
+
   // ---- final state ------------------------------------------------------------
   if (a.w1_out) {
+    // fresh lane indices: keeps the compiler from holding the prologue's
+    // per-lane state offsets live through the loop for these stores
+    int g = lane >> 4, c = lane & 15;
+    asm volatile("" : "+v"(g), "+v"(c));
     float* w1 = a.w1_out + (size_t)unit * D * MH;
     float* w2 = a.w2_out + (size_t)unit * MH * D;
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           w1[(16 * r + 4 * g + i) * MH + HB + 16 * n + c] = W1c[r][n][i];
-          w2[(HB + 16 * r + 4 * g + i) * D + 16 * n + c] = W2c[r][n][i];
+          w2[(HB + 16 * n + 4 * g + i) * D + 16 * r + c] = W2c[n][r][i];
         }
     if (c == 0) {
 #pragma unroll
-      for (int n = 0; n < 4; ++n)
+      for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) a.b1_out[(size_t)unit * MH + HB + 16 * n + 4 * g + i] = b1v[n][i];
+      if (kside) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a.b2_out[(size_t)unit * D + fo + i] = b2w[i];
+        for (int i = 0; i < 4; ++i) a.b2_out[(size_t)unit * D + 16 * ft + 4 * g + i] = b2q[i];
+      }
     }
   }
 }

@@ -80,7 +80,7 @@ __device__ __forceinline__ void stage_issue(Stage<BF16, TB>& L, const void* q, c
       __builtin_amdgcn_global_load_lds(src[x] + goff, dst, 16, 0, 0);
     }
   }
-  if (part == 0 && w * 64 < TOK) {
+  if (part == 0 && w * 64 + l < TOK) {   // blocks of fewer than 64 tokens: the lanes past TOK idle
     const int tok = min(tok0 + w * 64 + l, T - 1);
     TTT_LDS void* dst = (TTT_LDS void*)(&L.eta[buf][w * 64]);
     __builtin_amdgcn_global_load_lds(eta + row0 + tok, dst, 4, 0, 0);
