@@ -67,6 +67,20 @@ def test_ragged_lengths(T, io):
     _check("ragged T=%d %s" % (T, io), inp, io)
 
 
+@pytest.mark.parametrize("case", ["eta0", "gamma0"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_special_cases(case, io):
+    """eta = 0: every token sees W0, z = q + LN(q W0); gamma = 0: every
+    gradient is exactly zero, so the state stays W0 bit for bit and
+    z = q + beta."""
+    base = WORKLOADS["linear_b1h1_t256_f32" if io == "f32" else "linear_125m_b8h12_t2k"]
+    inp = make_inputs(base, B=1, H=2, T=70)
+    inp["eta" if case == "eta0" else "gamma"][:] = 0
+    z, w = _check("%s %s" % (case, io), inp, io)
+    if case == "gamma0":
+        np.testing.assert_array_equal(w[0], inp["w0"])
+
+
 @pytest.mark.parametrize("b", [32, 64, 256])
 def test_larger_minibatches(b):
     inp = make_inputs(WORKLOADS["linear_b1h1_t256_f32"], B=1, H=2, T=200)

@@ -70,6 +70,20 @@ def test_flags(ln, res, io):
     _check("mlp ln=%d res=%d %s" % (ln, res, io), inp, io, layer_norm=ln, residual=res)
 
 
+@pytest.mark.parametrize("case", ["eta0", "gamma0"])
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_special_cases(case, io):
+    """eta = 0: every token sees the initial state (the inner model's plain
+    forward, GELU included); gamma = 0: every gradient is exactly zero, so the
+    state stays put bit for bit and z = q + beta."""
+    inp = make_inputs(MLP if io == "bf16" else MLP32, B=1, H=2, T=40)
+    inp["eta" if case == "eta0" else "gamma"][:] = 0
+    z, S = _check("mlp %s %s" % (case, io), inp, io)
+    if case == "gamma0":
+        for a, s in zip(S, STATE):
+            np.testing.assert_array_equal(a[0], inp[s])
+
+
 def test_per_batch_state_and_eps():
     inp = make_inputs(MLP, B=2, H=2, T=64)
     rng = np.random.default_rng(7)

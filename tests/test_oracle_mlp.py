@@ -150,6 +150,21 @@ def test_mlp_eta_zero_closed_form():
             np.testing.assert_array_equal(S[3][bb, h], b2[h].astype(np.float64))
 
 
+def test_mlp_gamma_zero_freezes_state():
+    """gamma = 0 makes LN(o) = beta for every input, so the loss has no
+    gradient with respect to the state: the state stays S0 and z = q + beta
+    (closed form, LN and residual as in "Key takeaways" item 5)."""
+    rng = np.random.default_rng(66)
+    q, k, v, eta, w1, b1, w2, b2, gamma, beta = _problem(rng, B=1, H=2, T=20)
+    gamma[:] = 0
+    z, S = oracle.mlp(q, k, v, eta, w1, b1, w2, b2, gamma, beta, mini_batch=4)
+    for h in range(2):
+        for got, s0 in zip(S, (w1, b1, w2, b2)):
+            np.testing.assert_array_equal(got[0, h], s0[h].astype(np.float64))
+        np.testing.assert_allclose(z[0, h], q[0, h].astype(np.float64) + beta[h][None].astype(np.float64),
+                                   rtol=0, atol=1e-15)
+
+
 def test_mlp_segment_split_and_permutation():
     rng = np.random.default_rng(65)
     q, k, v, eta, w1, b1, w2, b2, gamma, beta = _problem(rng, B=2, H=2, T=16)
