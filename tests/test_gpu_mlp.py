@@ -7,9 +7,9 @@ import torch
 
 import oracle
 from linear_rnn_ttt_amd import ttt_mlp_forward
-from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs, unit_slice
+from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs
 
-from _parity import TOL, from_dev, state_err, to_dev, z_err
+from _parity import TOL, check_units, from_dev, perturbed_eta, state_err, to_dev, z_err
 
 pytestmark = pytest.mark.gpu
 
@@ -125,23 +125,18 @@ def test_deterministic():
         assert np.array_equal(x, y)
 
 
-@pytest.mark.parametrize("name,units", [
-    ("mlp_125m_b8h12_t2k", [(0, 0), (7, 11)]),
-    ("mlp_long_b1h32_t32k", [(0, 17)]),
-])
-def test_full_size_sampled_units(name, units):
+@pytest.mark.parametrize("name", ["mlp_125m_b8h12_t2k", "mlp_long_b1h32_t32k"])
+def test_full_size_all_units(name):
+    """The full workload as the benchmark runs it, every (batch, head) unit
+    against the oracle, with the conditioning-aware bound of check_units."""
     w = WORKLOADS[name]
     inp = make_inputs(w)
     z, S = _gpu(inp, w.io)
-    sub = unit_slice(inp, units, w.H)
-    zr, Sr = oracle.mlp(sub["q"], sub["k"], sub["v"], sub["eta"], *(sub[s] for s in STATE),
-                        sub["gamma"], sub["beta"], state0_per_batch=True)
-    bs, hs = [u[0] for u in units], [u[1] for u in units]
-    ez = z_err(z[bs, hs][None], zr)
-    es = [state_err(a[bs, hs][None].reshape(1, len(units), -1), b.reshape(1, len(units), -1))
-          for a, b in zip(S, Sr)]
-    print("%s units %s: z err %.3e, state errs %s" % (name, units, ez,
-                                                      " ".join("%.2e" % e for e in es)),
-          flush=True)
-    assert ez <= TOL[w.io] and max(es) <= TOL[w.io]
     assert np.isfinite(z).all()
+    run = lambda eta: oracle.mlp(inp["q"], inp["k"], inp["v"], eta, *(inp[s] for s in STATE),
+                                 inp["gamma"], inp["beta"])
+    zr, Sr = run(inp["eta"])
+    pert = [run(perturbed_eta(inp["eta"], seed)) for seed in (1, 2)]
+    flat = lambda X: [x.reshape(x.shape[:2] + (-1,)) for x in X]
+    check_units(name, z, zr, [p[0] for p in pert], flat(S), flat(Sr), [flat(p[1]) for p in pert],
+                TOL[w.io])

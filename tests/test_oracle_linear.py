@@ -295,3 +295,26 @@ def test_nan_propagates():
     assert np.isfinite(z[0, 0, :8]).all()
     assert np.isnan(z[0, 0, 9:]).all()
     assert np.isnan(w).all()
+
+
+def test_long_scan_is_ill_conditioned_on_some_units():
+    """The recurrence can amplify perturbations along the sequence.  On the
+    1.3B-shaped workload (B4 H32 T8192, seeded inputs) unit (0, 14) is such a
+    case: a 1e-7 relative perturbation of eta moves the fp64 oracle's z by
+    more than 1e-3 (row-normalised max) by the end of the sequence, growing
+    steadily along it, while unit (0, 0) moves by less than 1e-5.  No
+    finite-precision evaluation can be held to a fixed tolerance on such a
+    unit; the GPU parity bound therefore scales with this sensitivity."""
+    from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs, unit_slice
+    w = WORKLOADS["linear_1p3b_b4h32_t8k"]
+    sub = unit_slice(make_inputs(w), [(0, 14), (0, 0)], w.H)
+    rng = np.random.default_rng(0)
+    eta2 = (sub["eta"].astype(np.float64) * (1 + 1e-7 * rng.standard_normal(sub["eta"].shape))
+            ).astype(np.float32)
+    run = lambda eta: oracle.linear(sub["q"], sub["k"], sub["v"], eta, sub["w0"], sub["gamma"],
+                                    sub["beta"], state0_per_batch=True)[0]
+    z1, z2 = run(sub["eta"]), run(eta2)
+    d = np.abs(z2 - z1).max(-1) / np.abs(z1).max(-1)   # [1, 2, T]
+    assert d[0, 0].max() > 1e-3
+    assert d[0, 0, -1024:].max() > 10 * d[0, 0, 1024:2048].max()   # grows along the sequence
+    assert d[0, 1].max() < 1e-5
