@@ -41,9 +41,10 @@
 //     both LayerNorms share the three workgroup barriers of a tile.
 //   * With bf16 inputs the products take plain bf16 operands (state kept in
 //     fp32); with fp32 inputs every operand is a bf16 hi + lo pair.
-//   * 16x16x32 and 16x16x16 products never feed each other's accumulator
-//     input directly: mixed-shape accumulator chains gave wrong values on
-//     this toolchain, so such sums start from zero and are added with VALU.
+//   * Every product is a 16x16x16 chain (the score tile K Q^T aside, a
+//     16x16x32 product from zero): mixed-shape accumulator chains gave wrong
+//     values on this toolchain.  P_k, P_q and the O partials accumulate onto
+//     the bias tiles, so the biases cost no VALU adds.
 #include <math.h>
 
 #include "ttt_device.hpp"

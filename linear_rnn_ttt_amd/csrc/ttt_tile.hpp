@@ -155,21 +155,6 @@ __device__ __forceinline__ Rows load_rows(const typename Io<BF16>::E* X, int t0,
   }
   return r;
 }
-// K^T of a staged tile as 16x16x16 A operands: kt[r] lane (g,c) holds
-// K[t0 + 4g + i][16r + c].
-template <bool BF16>
-__device__ __forceinline__ void load_cols(Op4 kt[4], const typename Io<BF16>::E* X, int t0, int c,
-                                          int g) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const auto e0 = X[lds_off<BF16>(t0 + 4 * g + 0, 16 * r + c)];
-    const auto e1 = X[lds_off<BF16>(t0 + 4 * g + 1, 16 * r + c)];
-    const auto e2 = X[lds_off<BF16>(t0 + 4 * g + 2, 16 * r + c)];
-    const auto e3 = X[lds_off<BF16>(t0 + 4 * g + 3, 16 * r + c)];
-    if constexpr (BF16) kt[r] = op4_of(e0, e1, e2, e3);
-    else kt[r] = op4_of(f32x4{e0, e1, e2, e3});
-  }
-}
 // The state W (four accumulator tiles of one wave) as A operands of W^T.
 __device__ __forceinline__ void split_state(Op8 A[2], const f32x4 W[4]) {
 #pragma unroll
@@ -192,24 +177,6 @@ __device__ __forceinline__ f32x4 gram(const Rows& X, const Rows& Y) {
   for (int p = 0; p < 2; ++p) acc = mma8<LO, LO>(X.p[p], Y.p[p], acc);
   return acc;
 }
-// acc + (-eta G)^T S for a 16x16 token-by-token tile S in accumulator
-// layout (split here into bf16 hi/lo when LO): the correction products of
-// the chunked form.  The 16x16x16 products start from zero and are added to
-// acc with VALU.  acc usually comes straight from 16x16x32 products, and on
-// this toolchain such a result fed as the C operand of a 16x16x16 product
-// issued right behind them gave wrong values (the first two accumulator
-// registers of the tile).
-template <bool LO>
-__device__ __forceinline__ f32x4 correct(const Op4& gt, f32x4 S, f32x4 acc) {
-  const Split4 sp = split4(S);
-  f32x4 d = mfma16(gt.hi, sp.hi, f32x4{0.f, 0.f, 0.f, 0.f});
-  if (LO) {
-    d = mfma16(gt.lo, sp.hi, d);
-    d = mfma16(gt.hi, sp.lo, d);
-  }
-  return acc + d;
-}
-
 template <bool ALO, bool BLO>
 __device__ __forceinline__ f32x4 mma4(const Op4& a, const Op4& b, f32x4 acc) {
   acc = mfma16(a.hi, b.hi, acc);
