@@ -91,7 +91,7 @@ struct MlpLds {
 // against the oracle, although GELU values only enter the matrix unit as
 // bf16 operands: its error is systematic, not rounding noise.)
 struct PhiExp {
-  float phi, ex;
+  float h, ex;   // Phi(-|x|), e^{-x^2/2}
 };
 __device__ __forceinline__ PhiExp phi_exp(float x) {
   constexpr float P = 0.3275911f * 0.70710678118654752f;   // p / sqrt 2
@@ -103,16 +103,19 @@ __device__ __forceinline__ PhiExp phi_exp(float x) {
   const float t = __builtin_amdgcn_rcpf(fmaf(fabsf(x), P, 1.0f));
   const float poly = t * fmaf(t, fmaf(t, fmaf(t, fmaf(t, A5, A4), A3), A2), A1);
   const float ex = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);   // e^{-x^2/2}
-  const float h = poly * ex;                                                 // Phi(-|x|)
-  return PhiExp{x >= 0.f ? 1.0f - h : h, ex};
+  return PhiExp{poly * ex, ex};
 }
 // GELU(x) = x Phi(x) and GELU'(x) = Phi(x) + x phi(x), phi the normal density.
 __device__ __forceinline__ void gelu2(float x, float& y, float& dy) {
   const PhiExp r = phi_exp(x);
-  y = x * r.phi;
-  dy = fmaf(x * r.ex, 0.39894228040143268f, r.phi);
+  const float phi = x >= 0.f ? 1.0f - r.h : r.h;
+  y = x * phi;
+  dy = fmaf(x * r.ex, 0.39894228040143268f, phi);
 }
-__device__ __forceinline__ float gelu(float x) { return x * phi_exp(x).phi; }
+// GELU alone: x Phi(x) = max(x, 0) - |x| Phi(-|x|) for either sign of x.
+__device__ __forceinline__ float gelu(float x) {
+  return fmaf(-fabsf(x), phi_exp(x).h, fmaxf(x, 0.f));
+}
 
 // LayerNorm statistics of a 16-token x 64-feature tile spread over four
 // waves (lane (g,c) of the wave for feature tile ft: token c, features
