@@ -94,7 +94,7 @@ typedef struct {
  *   w_out  [B,H,d,d] fp32 final state, or NULL to skip it.
  * Supported: d = 64, mini_batch a positive multiple of 16 (values >= T
  * give batch GD over the causal prefix), both io dtypes, any flags.
- * gfx950 kernel: one 256-thread workgroup per (batch, head) unit; the state
+ * gfx950 kernel: one 768-thread workgroup per (batch, head) unit; the state
  * stays in registers across the whole sequence.
  */
 ttt_status ttt_linear_forward(const ttt_params* p,
@@ -110,6 +110,8 @@ ttt_status ttt_linear_forward(const ttt_params* p,
  *   w1_out, b1_out, w2_out, b2_out: [B,H,...] fp32, all NULL or all set.
  * Supported: d = 64, hidden = 256, mini_batch = 16, both io dtypes, any
  * flags.
+ * gfx950 kernel: one 512-thread workgroup per (batch, head) unit; the state
+ * stays in registers across the whole sequence.
  */
 ttt_status ttt_mlp_forward(const ttt_params* p, int32_t hidden,
                            const void* q, const void* k, const void* v,
