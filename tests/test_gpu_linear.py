@@ -81,6 +81,12 @@ def test_special_cases(case, io):
         np.testing.assert_array_equal(w[0], inp["w0"])
 
 
+def test_more_units_than_compute_units():
+    """B*H = 320 units, more workgroups than the GPU holds at once."""
+    inp = make_inputs(WORKLOADS["linear_125m_b8h12_t2k"], B=10, H=32, T=80)
+    _check("B10 H32 T80 bf16", inp, "bf16")
+
+
 @pytest.mark.parametrize("b", [32, 64, 256])
 def test_larger_minibatches(b):
     inp = make_inputs(WORKLOADS["linear_b1h1_t256_f32"], B=1, H=2, T=200)

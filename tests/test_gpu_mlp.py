@@ -84,6 +84,11 @@ def test_special_cases(case, io):
             np.testing.assert_array_equal(a[0], inp[s])
 
 
+def test_more_units_than_compute_units():
+    """B*H = 320 units, more workgroups than the GPU holds at once."""
+    _check("mlp B10 H32 T40 bf16", make_inputs(MLP, B=10, H=32, T=40), "bf16")
+
+
 def test_per_batch_state_and_eps():
     inp = make_inputs(MLP, B=2, H=2, T=64)
     rng = np.random.default_rng(7)
