@@ -439,8 +439,9 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
 
 // ---------------------------------------------------------------------------
 // Update waves: the state, every product with it, the output correction,
-// the column-independent inputs of the chain (one wave each), and the input
-// copies.  Every row operand of a period is read once, at its start.
+// the column-independent inputs of the chain (one wave each), and the copy
+// of the first input block (the output waves issue the later ones).  Every
+// row operand of a period is read once, at its start.
 template <bool BF16, bool LN, bool RES, bool MB16>
 __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x) {
   constexpr int TB = LinCfg<BF16>::TB;
