@@ -66,6 +66,14 @@ constexpr int tiles_per_block() {
   return BF16 ? 4 : 2;
 }
 
+// Phi(-y) for y in [0, 5] is read from a table in LDS (filled at start from
+// phi_exp) and interpolated linearly between steps of 1/384: within 2.1e-7
+// of the table's function, so within 5e-7 of Phi; beyond y = 5 the table's
+// last step is used (Phi(-5) = 2.9e-7).  This takes the reciprocal and the
+// exponential of GELU off the VALU.
+constexpr int PHI_STEPS = 384;
+constexpr int PHI_N = 5 * PHI_STEPS;
+
 template <bool BF16>
 struct MlpLds {
   Stage<BF16, tiles_per_block<BF16>()> st;
@@ -79,6 +87,7 @@ struct MlpLds {
   // tiles every wave needs, formed by one wave [tile parity]:
   u32x4 mq[2][64];        // tril(K Q^T + 1) as [hi, lo]
   u32x4 ktb[2][4][64];    // K^T tiles (lane: token 4g+i, feature 16r+c) as [hi, lo]
+  f32x2 phit[PHI_N];      // Phi(-y) at y = i / PHI_STEPS: (value, next - value)
 };
 
 // Phi(x) and e^{-x^2/2} with one exponential and one reciprocal.  For
@@ -105,16 +114,23 @@ __device__ __forceinline__ PhiExp phi_exp(float x) {
   const float ex = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);   // e^{-x^2/2}
   return PhiExp{poly * ex, ex};
 }
-// GELU(x) = x Phi(x) and GELU'(x) = Phi(x) + x phi(x), phi the normal density.
-__device__ __forceinline__ void gelu2(float x, float& y, float& dy) {
-  const PhiExp r = phi_exp(x);
-  const float phi = x >= 0.f ? 1.0f - r.h : r.h;
+// Phi(-|x|) from the table.
+__device__ __forceinline__ float phi_neg_tab(const f32x2* tab, float x) {
+  const float u = fminf(fabsf(x) * (float)PHI_STEPS, (float)PHI_N - 0.001f);
+  const f32x2 e = tab[(int)u];
+  return fmaf(__builtin_amdgcn_fractf(u), e.y, e.x);
+}
+// GELU and GELU' (GELU'(x) = Phi(x) + x phi(x); phi from one exponential).
+__device__ __forceinline__ void gelu2(const f32x2* tab, float x, float& y, float& dy) {
+  const float h = phi_neg_tab(tab, x);
+  const float phi = x >= 0.f ? 1.0f - h : h;
   y = x * phi;
-  dy = fmaf(x * r.ex, 0.39894228040143268f, phi);
+  const float ex = __builtin_amdgcn_exp2f(x * x * -0.72134752044448170f);   // e^{-x^2/2}
+  dy = fmaf(x * ex, 0.39894228040143268f, phi);
 }
 // GELU alone: x Phi(x) = max(x, 0) - |x| Phi(-|x|) for either sign of x.
-__device__ __forceinline__ float gelu(float x) {
-  return fmaf(-fabsf(x), phi_exp(x).h, fmaxf(x, 0.f));
+__device__ __forceinline__ float gelu(const f32x2* tab, float x) {
+  return fmaf(-fabsf(x), phi_neg_tab(tab, x), fmaxf(x, 0.f));
 }
 
 // LayerNorm statistics of a 16-token x 64-feature tile spread over four
@@ -308,6 +324,12 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
     }
   };
 
+  for (int i = tid; i < PHI_N; i += NT) {
+    const float t0 = phi_exp((float)i / (float)PHI_STEPS).h;
+    const float t1 = phi_exp((float)(i + 1) / (float)PHI_STEPS).h;
+    L.phit[i] = f32x2{t0, t1 - t0};
+  }
+
   const int n_tiles = (T + 15) / 16;
   stage_issue<BF16, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, 0, T, 0, w & 3, w >> 2, 2);
   wait_vmem();
@@ -351,7 +373,7 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         float y, dy;
-        gelu2(acc[i], y, dy);
+        gelu2(L.phit, acc[i], y, dy);
         Ak[n][i] = y;
         Dk[n][i] = dy;
       }
@@ -491,7 +513,7 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
     for (int n = 0; n < 2; ++n) {
       const f32x4 p = mma4<SP, SP>(gpt[n], Mq, Pq[n]);   // - tril(Q K^T + 1) (eta G_p)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Aq[n][i] = gelu(p[i]);
+      for (int i = 0; i < 4; ++i) Aq[n][i] = gelu(L.phit, p[i]);
     }
     const Op4 aq[2] = {op4_of(Aq[0]), op4_of(Aq[1])};
     // W2 operands again (cheaper than holding them since the first use)
