@@ -87,6 +87,17 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// The same barrier for a wave whose global-to-LDS copies (global_load_lds)
+// are still in flight into a buffer that no wave reads before a later
+// barrier.  The release fence above counts such copies as LDS writes and
+// would wait for them (vmcnt(0)), holding the whole workgroup at the barrier
+// for a memory round trip; here only the wave's own LDS accesses are waited
+// for.  The "memory" clobber keeps the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void lds_barrier_copies_in_flight() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 __device__ __forceinline__ uint32_t fbits(float x) { return __builtin_bit_cast(uint32_t, x); }
 __device__ __forceinline__ float bitsf(uint32_t x) { return __builtin_bit_cast(float, x); }
 

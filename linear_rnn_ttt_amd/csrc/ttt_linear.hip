@@ -731,9 +731,10 @@ __device__ __forceinline__ void output_part(LinLds<BF16>& L, const LinearArgs& a
         for (int i = 0; i < 4; ++i) qb1[i] = (RES ? qv[i] : 0.f) + bet[i];
       }
       // the next block must be visible by the barrier that opens the period
-      // reading its first tile two ahead
+      // reading its first tile two ahead; until then the copies stay in
+      // flight across the barriers
       if (tb == TB - 3 && next_block) wait_vmem();
-      lds_barrier();
+      lds_barrier_copies_in_flight();
     }
   }
 }
