@@ -25,10 +25,10 @@
  * linear model of Theorem 1, item 3).
  *
  * Conventions shared by every entry point
- *  - Pointers q, k, v, eta, states, gamma, beta, z and the *_out buffers are
- *    DEVICE pointers (HIP global memory of the current device), owned by
- *    the caller.  The library allocates no memory and keeps no global
- *    mutable state; calls are thread-safe and reentrant.
+ *  - Pointers q, k, v, eta, states, gamma, beta, z, the *_out buffers and
+ *    workspaces are DEVICE pointers (HIP global memory of the current
+ *    device), owned by the caller.  The library allocates no memory and
+ *    keeps no global mutable state; calls are thread-safe and reentrant.
  *  - Layout: contiguous, row-major, feature dimension fastest.
  *      q, k, v, z  [B,H,T,d] of io_dtype     eta  [B,H,T] fp32
  *      gamma, beta [H,d] fp32 (not read with TTT_NO_LN; may be NULL then)
@@ -59,16 +59,18 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 1
+#define TTT_ABI_VERSION 2
 
 typedef enum {
   TTT_OK = 0,
   TTT_ERR_NULL = 1,         /* a required pointer is NULL */
-  TTT_ERR_SHAPE = 2,        /* B, H, T, d, mini_batch or hidden out of range */
-  TTT_ERR_UNSUPPORTED = 3,  /* valid for the method, not built for gfx950 */
+  TTT_ERR_SHAPE = 2,        /* B, H, T, d, mini_batch or hidden out of range, or a
+                               workspace smaller than its query returned */
+  TTT_ERR_UNSUPPORTED = 3,  /* valid for the method, not built for gfx950 (or a split
+                               launch on more units than half the compute units) */
   TTT_ERR_ALIAS = 4,        /* forbidden overlap between buffers */
   TTT_ERR_DEVICE = 5,       /* HIP reported an error at launch */
-  TTT_ERR_ARG = 6           /* bad dtype, flag or epsilon */
+  TTT_ERR_ARG = 6           /* bad dtype, flag or epsilon, or a misaligned workspace */
 } ttt_status;
 
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
@@ -102,6 +104,42 @@ ttt_status ttt_linear_forward(const ttt_params* p,
                               const float* eta, const float* w0,
                               const float* ln_gamma, const float* ln_beta,
                               void* z, float* w_out, void* hip_stream);
+
+/*
+ * Bytes of device workspace that ttt_linear_forward_split needs for these
+ * parameters: 256 bytes per unit plus 256, and 4 KB per unit and 16-token
+ * tile (0 if p fails the common checks).
+ */
+uint64_t ttt_linear_split_workspace_bytes(const ttt_params* p);
+
+/*
+ * TTT-Linear forward scan, same method, arguments and results as
+ * ttt_linear_forward (bit for bit), on two workgroups per (batch, head)
+ * unit: one runs the serial part of the scan (the gradient of every
+ * 16-token tile) and streams each tile's gradient through `workspace` to
+ * the other, on another compute unit, which replays the state updates and
+ * forms z.  Unit count B*H at most half the device's compute units
+ * (TTT_ERR_UNSUPPORTED otherwise; use ttt_linear_forward).
+ *   workspace  device memory, 256-byte aligned, at least
+ *              ttt_linear_split_workspace_bytes(p) bytes, owned by the
+ *              caller, overlapping no other argument (TTT_ERR_SHAPE /
+ *              TTT_ERR_ARG / TTT_ERR_ALIAS).  Its contents need no
+ *              initialisation and are scratch after the call; it serves one
+ *              call at a time (calls that overlap in time must use distinct
+ *              workspaces).
+ * The launch is two kernels on hip_stream (a fill of the workspace's
+ * counters, then the scan).  Should the second workgroup of a unit wait
+ * for the first for seconds (the two not resident together), it gives up
+ * and writes NaN to that unit's z instead of hanging; the final state is
+ * always correct.
+ */
+ttt_status ttt_linear_forward_split(const ttt_params* p,
+                                    const void* q, const void* k, const void* v,
+                                    const float* eta, const float* w0,
+                                    const float* ln_gamma, const float* ln_beta,
+                                    void* z, float* w_out,
+                                    void* workspace, uint64_t workspace_bytes,
+                                    void* hip_stream);
 
 /*
  * TTT-MLP forward scan, hidden width `hidden` (m).

@@ -47,30 +47,28 @@ ttt_status check_common(const ttt_params* p, uint64_t* elems) {
   return TTT_OK;
 }
 
-}  // namespace
+// Workspace of a split Linear launch: publication counters (two 128-byte
+// lines per unit), 32 error words, then the gradient stream (4 KB per
+// 16-token tile and unit).
+struct SplitLayout {
+  uint64_t stream_offset, total;
+};
 
-extern "C" {
-
-const char* ttt_status_string(ttt_status s) {
-  switch (s) {
-    case TTT_OK: return "ok";
-    case TTT_ERR_NULL: return "a required pointer is NULL";
-    case TTT_ERR_SHAPE: return "B, H, T, d, mini_batch or hidden out of range";
-    case TTT_ERR_UNSUPPORTED:
-      return "configuration not built for gfx950 (needs d = 64; Linear: mini_batch a multiple "
-             "of 16; MLP: hidden = 256, mini_batch = 16)";
-    case TTT_ERR_ALIAS: return "an output buffer overlaps an input or another output";
-    case TTT_ERR_DEVICE: return "HIP reported an error at kernel launch";
-    case TTT_ERR_ARG: return "bad io_dtype, flags, ln_eps or state0_per_batch";
-  }
-  return "unknown ttt_status";
+SplitLayout split_layout(const ttt_params* p) {
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t tiles = (static_cast<uint64_t>(p->T) + 15) / 16;
+  SplitLayout ly;
+  ly.stream_offset = (units * 256 + 128 + 255) / 256 * 256;
+  ly.total = ly.stream_offset + units * tiles * 4096;
+  return ly;
 }
 
-int32_t ttt_abi_version(void) { return TTT_ABI_VERSION; }
-
-ttt_status ttt_linear_forward(const ttt_params* p, const void* q, const void* k, const void* v,
-                              const float* eta, const float* w0, const float* ln_gamma,
-                              const float* ln_beta, void* z, float* w_out, void* hip_stream) {
+// Validation shared by the Linear entry points; fills *a.  A non-null
+// workspace is checked for size, alignment and overlap.
+ttt_status linear_args(const ttt_params* p, const void* q, const void* k, const void* v,
+                       const float* eta, const float* w0, const float* ln_gamma,
+                       const float* ln_beta, void* z, float* w_out, void* workspace,
+                       uint64_t workspace_bytes, tttk::LinearArgs* a) {
   uint64_t elems = 0;
   ttt_status st = check_common(p, &elems);
   if (st != TTT_OK) return st;
@@ -90,35 +88,113 @@ ttt_status ttt_linear_forward(const ttt_params* p, const void* q, const void* k,
   if (overlap(rz, rq) || overlap(rz, rk) || overlap(rz, rv) || overlap(rz, re) ||
       overlap(rz, rw0) || overlap(rz, rg) || overlap(rz, rb))
     return TTT_ERR_ALIAS;
+  const Range rwo = span(w_out, units * dd * 4);
   if (w_out) {
-    const Range rwo = span(w_out, units * dd * 4);
     const bool in_place = p->state0_per_batch == 1 && static_cast<const void*>(w_out) == w0;
     if (overlap(rwo, rq) || overlap(rwo, rk) || overlap(rwo, rv) || overlap(rwo, re) ||
         overlap(rwo, rz) || overlap(rwo, rg) || overlap(rwo, rb) ||
         (!in_place && overlap(rwo, rw0)))
       return TTT_ERR_ALIAS;
   }
+  if (workspace) {
+    if (workspace_bytes < split_layout(p).total) return TTT_ERR_SHAPE;
+    if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TTT_ERR_ARG;
+    const Range rws = span(workspace, workspace_bytes);
+    const Range all[] = {rq, rk, rv, re, rz, rw0, rg, rb, rwo};
+    for (const Range& r : all)
+      if (overlap(rws, r)) return TTT_ERR_ALIAS;
+  }
 
-  tttk::LinearArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.eta = eta;
-  a.w0 = w0;
-  a.gamma = ln_gamma;
-  a.beta = ln_beta;
-  a.z = z;
-  a.w_out = w_out;
-  a.B = p->B;
-  a.H = p->H;
-  a.T = p->T;
-  a.tiles_per_mb = p->mini_batch / 16;
-  a.eps = p->ln_eps;
-  a.state0_per_batch = p->state0_per_batch;
-  const hipError_t e = tttk::launch_linear(a, p->io_dtype == TTT_BF16, ln,
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->eta = eta;
+  a->w0 = w0;
+  a->gamma = ln_gamma;
+  a->beta = ln_beta;
+  a->z = z;
+  a->w_out = w_out;
+  a->B = p->B;
+  a->H = p->H;
+  a->T = p->T;
+  a->tiles_per_mb = p->mini_batch / 16;
+  a->eps = p->ln_eps;
+  a->state0_per_batch = p->state0_per_batch;
+  a->ws_g = nullptr;
+  a->ws_flags = nullptr;
+  a->split = 0;
+  return TTT_OK;
+}
+
+ttt_status linear_launch(const ttt_params* p, const tttk::LinearArgs& a, void* hip_stream) {
+  const hipError_t e = tttk::launch_linear(a, p->io_dtype == TTT_BF16, !(p->flags & TTT_NO_LN),
                                            !(p->flags & TTT_NO_RESIDUAL),
                                            static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ttt_status_string(ttt_status s) {
+  switch (s) {
+    case TTT_OK: return "ok";
+    case TTT_ERR_NULL: return "a required pointer is NULL";
+    case TTT_ERR_SHAPE:
+      return "B, H, T, d, mini_batch or hidden out of range, or the workspace is too small";
+    case TTT_ERR_UNSUPPORTED:
+      return "configuration not built for gfx950 (needs d = 64; Linear: mini_batch a multiple "
+             "of 16; MLP: hidden = 256, mini_batch = 16; split Linear: 2*B*H at most the "
+             "compute units)";
+    case TTT_ERR_ALIAS: return "an output buffer or workspace overlaps another argument";
+    case TTT_ERR_DEVICE: return "HIP reported an error at kernel launch";
+    case TTT_ERR_ARG:
+      return "bad io_dtype, flags, ln_eps or state0_per_batch, or a misaligned workspace";
+  }
+  return "unknown ttt_status";
+}
+
+int32_t ttt_abi_version(void) { return TTT_ABI_VERSION; }
+
+ttt_status ttt_linear_forward(const ttt_params* p, const void* q, const void* k, const void* v,
+                              const float* eta, const float* w0, const float* ln_gamma,
+                              const float* ln_beta, void* z, float* w_out, void* hip_stream) {
+  tttk::LinearArgs a;
+  const ttt_status st = linear_args(p, q, k, v, eta, w0, ln_gamma, ln_beta, z, w_out, nullptr, 0, &a);
+  if (st != TTT_OK) return st;
+  return linear_launch(p, a, hip_stream);
+}
+
+uint64_t ttt_linear_split_workspace_bytes(const ttt_params* p) {
+  uint64_t elems = 0;
+  if (check_common(p, &elems) != TTT_OK) return 0;
+  return split_layout(p).total;
+}
+
+ttt_status ttt_linear_forward_split(const ttt_params* p, const void* q, const void* k,
+                                    const void* v, const float* eta, const float* w0,
+                                    const float* ln_gamma, const float* ln_beta, void* z,
+                                    float* w_out, void* workspace, uint64_t workspace_bytes,
+                                    void* hip_stream) {
+  if (!workspace) return TTT_ERR_NULL;
+  tttk::LinearArgs a;
+  const ttt_status st = linear_args(p, q, k, v, eta, w0, ln_gamma, ln_beta, z, w_out, workspace,
+                                    workspace_bytes, &a);
+  if (st != TTT_OK) return st;
+  // both workgroups of every unit must be resident at once
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return TTT_ERR_DEVICE;
+  if (2ull * static_cast<uint64_t>(p->B) * p->H > static_cast<uint64_t>(cus))
+    return TTT_ERR_UNSUPPORTED;
+  const SplitLayout ly = split_layout(p);
+  char* base = static_cast<char*>(workspace);
+  a.ws_flags = reinterpret_cast<uint32_t*>(base);
+  a.ws_g = reinterpret_cast<uint32_t*>(base + ly.stream_offset);
+  a.split = 1;
+  return linear_launch(p, a, hip_stream);
 }
 
 ttt_status ttt_mlp_forward(const ttt_params* p, int32_t hidden, const void* q, const void* k,

@@ -22,6 +22,13 @@ struct LinearArgs {
   int32_t tiles_per_mb;   // mini-batch size / 16
   float eps;
   int32_t state0_per_batch;
+  // Two workgroups per unit (see ttt_linear.hip) when split != 0: the
+  // gradient stream [units][T/16 tiles][4][64] x 16 B and the publication
+  // counters [units][2][32] u32 (zeroed before the launch), followed by 32
+  // u32 of error words.
+  uint32_t* ws_g;
+  uint32_t* ws_flags;
+  int32_t split;
 };
 
 struct MlpArgs {

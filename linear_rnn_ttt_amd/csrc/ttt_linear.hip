@@ -96,7 +96,30 @@ struct LinLds {
   f32x4 hqb[2][4][64];  // output pre-activation of tile t-1 around its shift,
                         // update wave -> output wave
   f32x2 xo[2][16][4];   // output LN: (sum e, sum e^2) per token and wave
+  u32x4 mqb[2][64];     // tril(K_t Q_t^T) as [hi, lo] (hi only for bf16 data),
+                        // update wave 2 -> every update wave
+  float mqm[2][16];     // q . w_bar per token of tile t, update wave 2 -> every update wave
   uint16_t cst[4][D];   // bf16 rows: w_bar hi, 2 gamma hi, w_bar lo, 2 gamma lo
+};
+
+// LDS of the output workgroup of a split unit: q and k staged in blocks of
+// TB tiles, the unit's gradient stream staged in the same blocks, and the
+// exchanges of the output side.
+template <bool BF16>
+struct OutLds {
+  Stage<BF16, LinCfg<BF16>::TB, 2> st;    // q, k
+  u32x4 gst[2][LinCfg<BF16>::TB][4][64];  // (-eta G)^T as [hi, lo]: [buffer][tile][column block][lane]
+  f32x4 hqb[2][4][64];
+  f32x2 xo[2][16][4];
+  u32x4 mqb[2][64];
+  float mqm[2][16];
+  uint16_t cst[4][D];
+};
+
+template <bool BF16>
+union SplitLds {
+  LinLds<BF16> c;  // chain workgroup
+  OutLds<BF16> o;  // output workgroup
 };
 
 struct Ctx {
@@ -107,13 +130,13 @@ struct Ctx {
 
 // Staged rows of the tile `tb` tiles after the first tile of block `blk`
 // (tb may run past the block, into the other buffer).
-template <bool BF16, int TB>
-__device__ __forceinline__ const typename Io<BF16>::E* tile_rows(const Stage<BF16, TB>& st,
+template <bool BF16, int TB, int NX>
+__device__ __forceinline__ const typename Io<BF16>::E* tile_rows(const Stage<BF16, TB, NX>& st,
                                                                  int x, int blk, int tb) {
   return st.qkv[(blk + tb / TB) & 1][x] + (tb % TB) * 16 * D;
 }
-template <bool BF16, int TB>
-__device__ __forceinline__ float tile_eta(const Stage<BF16, TB>& st, int blk, int tb, int c) {
+template <bool BF16, int TB, int NX>
+__device__ __forceinline__ float tile_eta(const Stage<BF16, TB, NX>& st, int blk, int tb, int c) {
   return st.eta[(blk + tb / TB) & 1][(tb % TB) * 16 + c];
 }
 
@@ -441,8 +464,10 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
 // Update waves: the state, every product with it, the output correction,
 // the column-independent inputs of the chain (one wave each), and the copy
 // of the first input block (the output waves issue the later ones).  Every
-// row operand of a period is read once, at its start.
-template <bool BF16, bool LN, bool RES, bool MB16>
+// row operand of a period is read once, at its start.  SPLIT: the output
+// side (q products and output correction) is left to the unit's second
+// workgroup, and q is not staged.
+template <bool BF16, bool LN, bool RES, bool MB16, bool SPLIT>
 __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x) {
   constexpr int TB = LinCfg<BF16>::TB;
   constexpr bool LO = !BF16;
@@ -478,8 +503,12 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       L.cst[w + 2][lane] = (uint16_t)bf16_bits(v - __builtin_bit_cast(float, h << 16));
     }
   }
-  // "tile -1": no update in period 0
+  // "tile -1": no update and no output correction in period 0
   L.gtb[1][w][lane] = u32x4{0u, 0u, 0u, 0u};
+  if (w == 2) {
+    L.mqb[1][lane] = u32x4{0u, 0u, 0u, 0u};
+    if (lane < 16) L.mqm[1][lane] = 0.f;
+  }
   // The tiles past the end are read from stale staging rows (their
   // gradient is zero, but 0 * Inf would not be): buffer 1 starts as zeros
   // in case the sequence never loads it.
@@ -496,7 +525,7 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
 #pragma unroll
   for (int i = 0; i < 4; ++i) causal[i] = (4 * g + i) <= c;
 
-  stage_issue<BF16, TB>(L.st, a.q, a.k, a.v, a.eta, x.row0, 0, T, 0, w);
+  stage_issue<BF16, TB>(L.st, SPLIT ? nullptr : a.q, a.k, a.v, a.eta, x.row0, 0, T, 0, w);
   wait_vmem();
   lds_barrier();  // A
   u32x4 ast[2] = {};
@@ -539,8 +568,6 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
   __builtin_amdgcn_s_setprio(3);
   Op4 kt1[4] = {};                   // K_{p-1}^T (16x16x16 A operands)
   f32x4 qw1 = {0.f, 0.f, 0.f, 0.f};  // (Q_{p-1} W_{p-2})^T
-  Split4 m1 = {};                    // tril(K_{p-1} Q_{p-1}^T) (hi only for bf16 data)
-  float muq1 = 0.f;                  // q . w_bar, tile p-1
   for (int blk = 0; blk * TB <= n + 2; ++blk) {
 #pragma unroll
     for (int tb = 0; tb < TB; ++tb) {
@@ -554,16 +581,24 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       // every LDS read of the period first
       const auto* Kp = tile_rows(L.st, 1, blk, tb);
       const u32x4 g1 = L.gtb[(p - 1) & 1][w][lane];  // (-eta G_{p-1})^T as [hi, lo]
-      const Rows qr = rows8<BF16>(tile_rows(L.st, 0, blk, tb), c, g);
+      Rows qr = {};
+      if constexpr (!SPLIT) qr = rows8<BF16>(tile_rows(L.st, 0, blk, tb), c, g);
       const Rows kn = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 2), c, g);
       Rows vn;
       if (w == 3 && LN) vn = rows8<BF16>(tile_rows(L.st, 2, blk, tb + 2), c, g);
+      u32x4 mq = {};     // tril(K_{p-1} Q_{p-1}^T)
+      float muq1 = 0.f;  // q . w_bar, tile p-1
+      if constexpr (!SPLIT) {
+        mq = L.mqb[(p - 1) & 1][lane];
+        if (LN) muq1 = L.mqm[(p - 1) & 1][c];
+      }
+      const Split4 m1 = {hi_of(mq), lo_of(mq)};
       Op4 ktn[4];
       if constexpr (!BF16) cols8<BF16>(ktn, Kp, c, g);
       __builtin_amdgcn_sched_barrier(0);
       // ---- output pre-activation of tile p-1 around its shift:
       //      (Q W_{p-2})^T + (-eta G_{p-1})^T tril(K Q^T) - q . w_bar
-      {
+      if constexpr (!SPLIT) {
         f32x4 d = mfma16(hi_of(g1), m1.hi, f32x4{0.f, 0.f, 0.f, 0.f});
         d = mfma16(lo_of(g1), m1.hi, d);
         if (LO) d = mfma16(hi_of(g1), m1.lo, d);
@@ -585,7 +620,7 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         Ab[1] = Ac[1];
       }
       // ---- products of W_{p-1} (past the end: stale rows, unused)
-      qw1 = times_state<LO>(Ac, qr);
+      if constexpr (!SPLIT) qw1 = times_state<LO>(Ac, qr);
       {
         // gradient point two tiles ahead: K_{p+2} W_{p-1}, or the
         // mini-batch's own gradient point when no update reaches it
@@ -594,16 +629,18 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         else bk = times_state<LO>(Ab, kn);
         L.bkb[p & 1][w][lane] = bk;
       }
-      // ---- tile p: its output score tile and shift, for the next period
-      {
+      // ---- tile p: its output score tile and shift, for every update
+      //      wave in the next period (one wave: they do not depend on the
+      //      column block)
+      if (!SPLIT && w == 2) {
         f32x4 M = gram<LO>(kc0, qr);  // K_p Q_p^T
 #pragma unroll
         for (int i = 0; i < 4; ++i) M[i] = causal[i] ? M[i] : 0.f;
-        if (LO) m1 = split4(M);
-        else m1.hi = u32x2{pack_bf16(M[0], M[1]), pack_bf16(M[2], M[3])};
+        L.mqb[p & 1][lane] = LO ? hilo(split4(M))
+                                : u32x4{pack_bf16(M[0], M[1]), pack_bf16(M[2], M[3]), 0u, 0u};
         if (LN) {
           const f32x4 sq = stats<LO>(ast, qr);
-          muq1 = sq[0] + sq[2];
+          if (g == 0) L.mqm[p & 1][c] = sq[0] + sq[2];
         }
       }
       // ---- column-independent inputs of tile p+2 for the chain, one wave
@@ -649,9 +686,9 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
 // ---------------------------------------------------------------------------
 // Output waves: output LN and z.  Period p receives the pre-activation of
 // tile p-2 (around its shift), exchanges its LN sums, and stores z of tile
-// p-3.
-template <bool BF16, bool LN, bool RES, bool MB16>
-__device__ __forceinline__ void output_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x) {
+// p-3.  With COPIES they also issue the input copies of the later blocks.
+template <bool BF16, bool LN, bool RES, bool COPIES, class Lds>
+__device__ __forceinline__ void output_part(Lds& L, const LinearArgs& a, const Ctx& x) {
   constexpr int TB = LinCfg<BF16>::TB;
   const int lane = x.lane, g = x.g, c = x.c, w = x.w, fo = x.fo, n = x.n, T = x.T;
 
@@ -683,7 +720,7 @@ __device__ __forceinline__ void output_part(LinLds<BF16>& L, const LinearArgs& a
       if (p > n + 2) break;
       // refill the other buffer (nobody reads tiles before p any more), a
       // part per period so that no period carries all the copy instructions
-      if (tb < PARTS && next_block)
+      if (COPIES && tb < PARTS && next_block)
         stage_issue<BF16, TB>(L.st, a.q, a.k, a.v, a.eta, x.row0, blk + 1, T, (blk + 1) & 1, w,
                               tb, PARTS);
       // every LDS read of the period first
@@ -733,44 +770,358 @@ __device__ __forceinline__ void output_part(LinLds<BF16>& L, const LinearArgs& a
       // the next block must be visible by the barrier that opens the period
       // reading its first tile two ahead; until then the copies stay in
       // flight across the barriers
+      if constexpr (COPIES) {
+        if (tb == TB - 3 && next_block) wait_vmem();
+        lds_barrier_copies_in_flight();
+      } else {
+        lds_barrier();
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Split units: two workgroups per (batch, head) unit.  The first (the chain
+// workgroup) runs the chain and update waves as above without the output
+// side; it publishes every tile's (-eta G)^T to a gradient stream in device
+// memory.  The second (the output workgroup, on another CU) replays the
+// state updates from that stream and forms the outputs.  Only the output
+// workgroup ever waits for the other, so the pair cannot deadlock.
+//
+// Gradient stream of a unit: tile t, column block b, lane l at byte
+// ((4 t + b) * 64 + l) * 16, the [hi, lo] bf16 pairs of the chain's gtb.
+// Publication: wave h (0, 1) of the chain workgroup's hand-off pair owns
+// column blocks 2h, 2h+1 and a counter of complete tiles.
+
+constexpr int KLAG = 3;              // periods between a tile's stores and its publication
+constexpr uint32_t SC1 = 16;         // cache policy: agent-coherent access
+constexpr int SPIN_LIMIT = 1 << 21;  // polls (about 1 us each) before giving up
+
+// Chain workgroup, waves 8-9: the copies of k, v and eta for the blocks
+// after the first (two of the four shares each).
+template <bool BF16>
+__device__ __forceinline__ void feed_copy_part(LinLds<BF16>& L, const LinearArgs& a,
+                                               const Ctx& x, int cw) {
+  constexpr int TB = LinCfg<BF16>::TB;
+  constexpr int PARTS = TB >= 7 ? 4 : 1;
+  const int n = x.n, T = x.T;
+  lds_barrier();  // A
+  lds_barrier();  // B
+  lds_barrier();  // period 0 starts
+  for (int blk = 0; blk * TB <= n + 2; ++blk) {
+    const bool next_block = (blk + 1) * TB < n;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int p = blk * TB + tb;
+      if (p > n + 2) break;
+      if (tb < PARTS && next_block) {
+#pragma unroll
+        for (int sh = 0; sh < 2; ++sh)
+          stage_issue<BF16, TB>(L.st, nullptr, a.k, a.v, a.eta, x.row0, blk + 1, T,
+                                (blk + 1) & 1, 2 * cw + sh, tb, PARTS);
+      }
       if (tb == TB - 3 && next_block) wait_vmem();
       lds_barrier_copies_in_flight();
     }
   }
 }
 
-template <bool BF16, bool LN, bool RES, bool MB16>
+// Chain workgroup, waves 10-11: the hand-off.  In period p the gradient of
+// tile p-1 (published by the chain waves at the barrier that opened the
+// period) goes from LDS to the stream with agent-coherent stores.  This
+// wave issues no other memory instruction, and its vector memory counter
+// retires stores in order, so after the two stores of tile p-1 the stores
+// of tile p-1-KLAG are complete once at most 3 KLAG instructions remain
+// outstanding (two stores and one counter store per later period); the
+// counter then publishes tiles 0 .. p-1-KLAG.  The lag keeps the wait from
+// ever holding the barrier.
+template <bool BF16>
+__device__ __forceinline__ void handoff_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x,
+                                             int h) {
+  static_assert(KLAG == 3, "the vmcnt below is 3 KLAG");
+  const int lane = x.lane, n = x.n;
+  const __amdgpu_buffer_rsrc_t gs = __builtin_amdgcn_make_buffer_rsrc(
+      a.ws_g + (size_t)x.unit * n * 1024, (short)0, n * 4096, 0x00020000);
+  uint32_t* cnt = a.ws_flags + ((size_t)x.unit * 2 + h) * 32;
+  lds_barrier();  // A
+  lds_barrier();  // B
+  lds_barrier();  // period 0 starts
+  for (int p = 0; p <= n + 2; ++p) {
+    if (p >= 1 && p - 1 < n) {
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const int b = 2 * h + j;
+        const u32x4 v = L.gtb[(p - 1) & 1][b][lane];
+        __builtin_amdgcn_raw_buffer_store_b128(v, gs, (((p - 1) * 4 + b) * 64 + lane) * 16, 0, SC1);
+      }
+      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      if (lane == 0)
+        __hip_atomic_store(cnt, (uint32_t)max(p - KLAG, 0), __ATOMIC_RELAXED,
+                           __HIP_MEMORY_SCOPE_AGENT);
+    }
+    lds_barrier();
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  if (lane == 0) __hip_atomic_store(cnt, (uint32_t)n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Output workgroup, waves 0-3: the state, replayed from the gradient stream,
+// and the output pre-activation of every tile, as the update waves of the
+// one-workgroup kernel form them (same periods, same products).
+template <bool BF16, bool LN, bool RES>
+__device__ __forceinline__ void out_state_part(OutLds<BF16>& L, const LinearArgs& a,
+                                               const Ctx& x) {
+  constexpr int TB = LinCfg<BF16>::TB;
+  constexpr bool LO = !BF16;
+  const int lane = x.lane, g = x.g, c = x.c, w = x.w, n = x.n;
+
+  f32x4 Wc[4];  // lane (g,c) of tile r: W[feat(r, 4g + i)][16w + c]
+  const float* w0 = a.w0 + (size_t)(a.state0_per_batch ? x.unit : x.head) * D * D;
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Wc[r][i] = w0[feat(r, 4 * g + i) * D + 16 * w + c];
+  if (LN && w < 2) {
+    // constant rows of the dot-product operand: w_bar (wave 0), 2 gamma (wave 1)
+    float v;
+    if (w == 0) {
+      v = 0.f;
+      for (int j = 0; j < D; ++j) v += w0[lane * D + j];
+      v *= 1.0f / D;
+    } else {
+      v = 2.f * a.gamma[(size_t)x.head * D + lane];
+    }
+    const uint32_t h = bf16_bits(v);
+    L.cst[w][lane] = (uint16_t)h;
+    L.cst[w + 2][lane] = (uint16_t)bf16_bits(v - __builtin_bit_cast(float, h << 16));
+  }
+  if (w == 2) {  // "tile -1": no output correction in period 0
+    L.mqb[1][lane] = u32x4{0u, 0u, 0u, 0u};
+    if (lane < 16) L.mqm[1][lane] = 0.f;
+  }
+  {
+    // the tiles past the end are read from stale staging rows: buffer 1
+    // starts as zeros in case the sequence never loads it
+    constexpr int N16 = sizeof(L.st.qkv[1]) / 16;
+    u32x4* b1 = reinterpret_cast<u32x4*>(&L.st.qkv[1][0][0]);
+    for (int i = threadIdx.x; i < N16; i += 256) b1[i] = u32x4{0u, 0u, 0u, 0u};
+  }
+  const u32x2 ident = ident_op(g, c);
+  const u32x2 neg_ident = diag_op(g, c, 0xBF80u);
+  bool causal[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) causal[i] = (4 * g + i) <= c;
+
+  lds_barrier();  // A: block 0 of q, k and of the gradient stream staged
+  u32x4 ast[2] = {};
+  if (LN) {
+#pragma unroll
+    for (int pp = 0; pp < 2; ++pp)
+      ast[pp] = *reinterpret_cast<const u32x4*>(&L.cst[c & 3][32 * pp + 8 * g]);
+  }
+  lds_barrier();  // B
+  lds_barrier();  // period 0 starts
+
+  Op4 kt1[4] = {};                   // K_{p-1}^T (16x16x16 A operands)
+  f32x4 qw1 = {0.f, 0.f, 0.f, 0.f};  // (Q_{p-1} W_{p-2})^T
+  Op8 Ac[2];
+  for (int blk = 0; blk * TB <= n + 2; ++blk) {
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int p = blk * TB + tb;
+      if (p > n + 2) break;
+      // every LDS read of the period first: (-eta G_{p-1})^T (zero before
+      // the first tile and past the last), the rows of tile p, the output
+      // score tile and shift of tile p-1
+      const int tp = max(p - 1, 0);
+      const u32x4 g1 = zero_unless(p >= 1 && p - 1 < n, L.gst[(tp / TB) & 1][tp % TB][w][lane]);
+      const auto* Kp = tile_rows(L.st, 1, blk, tb);
+      const Rows qr = rows8<BF16>(tile_rows(L.st, 0, blk, tb), c, g);
+      const Rows kr = rows8<BF16>(Kp, c, g);
+      const u32x4 mq = L.mqb[(p - 1) & 1][lane];
+      const float muq1 = LN ? L.mqm[(p - 1) & 1][c] : 0.f;
+      const Split4 m1 = {hi_of(mq), lo_of(mq)};
+      Op4 ktn[4];
+      if constexpr (!BF16) cols8<BF16>(ktn, Kp, c, g);
+      __builtin_amdgcn_sched_barrier(0);
+      // ---- output pre-activation of tile p-1 around its shift
+      {
+        f32x4 d = mfma16(hi_of(g1), m1.hi, f32x4{0.f, 0.f, 0.f, 0.f});
+        d = mfma16(lo_of(g1), m1.hi, d);
+        if (LO) d = mfma16(hi_of(g1), m1.lo, d);
+        f32x4 e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = (qw1[i] + d[i]) - muq1;
+        L.hqb[p & 1][w][lane] = e;
+      }
+      // ---- W += K_{p-1}^T (-eta G_{p-1})
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        Wc[r] = mfma16(kt1[r].hi, hi_of(g1), Wc[r]);
+        Wc[r] = mfma16(kt1[r].hi, lo_of(g1), Wc[r]);
+        if (LO) Wc[r] = mfma16(kt1[r].lo, hi_of(g1), Wc[r]);
+      }
+      split_state_mm(Ac, Wc, neg_ident);  // W_{p-1}
+      qw1 = times_state<LO>(Ac, qr);      // past the end: stale rows, unused
+      // ---- tile p: output score tile and shift for the next period
+      if (w == 2) {
+        f32x4 M = gram<LO>(kr, qr);  // K_p Q_p^T
+#pragma unroll
+        for (int i = 0; i < 4; ++i) M[i] = causal[i] ? M[i] : 0.f;
+        L.mqb[p & 1][lane] = LO ? hilo(split4(M))
+                                : u32x4{pack_bf16(M[0], M[1]), pack_bf16(M[2], M[3]), 0u, 0u};
+        if (LN) {
+          const f32x4 sq = stats<LO>(ast, qr);
+          if (g == 0) L.mqm[p & 1][c] = sq[0] + sq[2];
+        }
+      }
+      // ---- K_p^T for the next update
+      if constexpr (BF16) {
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const u32x4 hh = kr.p[r >> 1].hi;
+          const f32x4 t = mfma16((r & 1) ? u32x2{hh.z, hh.w} : u32x2{hh.x, hh.y}, ident, zero);
+          kt1[r] = Op4{u32x2{pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])}, u32x2{0u, 0u}};
+        }
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kt1[r] = ktn[r];
+      }
+      lds_barrier();
+    }
+  }
+}
+
+// Output workgroup, waves 8-11: copies of q and k, and of the gradient
+// stream once the chain workgroup has published it.  Block b of the stream
+// is copied in period 1 of block b-1 (nobody reads its buffer after period
+// 0 of that block) and waited for, with q and k, by the end of block b-1.
+// If the chain workgroup does not publish within the spin limit (about two
+// seconds; a block takes microseconds), this and every later block is
+// filled with NaN instead and an error word is set, so that the failure
+// shows in z.
+template <bool BF16>
+__device__ __forceinline__ void out_copy_part(OutLds<BF16>& L, const LinearArgs& a,
+                                              const Ctx& x, int cw) {
+  constexpr int TB = LinCfg<BF16>::TB;
+  constexpr int PARTS = TB >= 7 ? 4 : 1;
+  const int lane = x.lane, n = x.n, T = x.T;
+  const uint32_t* gsrc = a.ws_g + (size_t)x.unit * n * 1024;
+  bool ok = true;  // cleared for good by a spin that reaches the limit
+  auto stage_grad = [&](int b, int buf) {
+    const uint32_t need = (uint32_t)min(n, (b + 1) * TB);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t* f = a.ws_flags + ((size_t)x.unit * 2 + h) * 32;
+      int spins = 0;
+      while (ok && __hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < need) {
+        if (++spins > SPIN_LIMIT) ok = false;
+        __builtin_amdgcn_s_sleep(2);
+      }
+    }
+    for (int i = cw; i < TB; i += 4) {
+      const int t = min(b * TB + i, n - 1);
+#pragma unroll
+      for (int cb = 0; cb < 4; ++cb) {
+        if (ok) {
+          TTT_LDS void* dst = (TTT_LDS void*)&L.gst[buf][i][cb][0];
+          __builtin_amdgcn_global_load_lds(gsrc + ((size_t)(4 * t + cb) * 64 + lane) * 4, dst, 16,
+                                           0, SC1);
+        } else {
+          L.gst[buf][i][cb][lane] = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+        }
+      }
+    }
+    if (!ok && lane == 0) a.ws_flags[(size_t)a.B * a.H * 64] = 1u;
+  };
+  stage_issue<BF16, TB>(L.st, a.q, a.k, nullptr, nullptr, x.row0, 0, T, 0, cw);
+  stage_grad(0, 0);
+  wait_vmem();
+  lds_barrier();  // A
+  lds_barrier();  // B
+  lds_barrier();  // period 0 starts
+  for (int blk = 0; blk * TB <= n + 2; ++blk) {
+    const bool next_block = (blk + 1) * TB < n;
+#pragma unroll
+    for (int tb = 0; tb < TB; ++tb) {
+      const int p = blk * TB + tb;
+      if (p > n + 2) break;
+      if (tb < PARTS && next_block)
+        stage_issue<BF16, TB>(L.st, a.q, a.k, nullptr, nullptr, x.row0, blk + 1, T,
+                              (blk + 1) & 1, cw, tb, PARTS);
+      if (tb == 1 && next_block) stage_grad(blk + 1, (blk + 1) & 1);
+      if (tb == TB - 1 && next_block) wait_vmem();
+      lds_barrier_copies_in_flight();
+    }
+  }
+}
+
+template <bool BF16, bool LN, bool RES, bool MB16, bool SPLIT>
 __global__ __launch_bounds__(NT, 1) void ttt_linear_fwd(LinearArgs a) {
-  __shared__ LinLds<BF16> L;
   Ctx x;
   const int tid = threadIdx.x;
   // the wave index is uniform across a wave: keep it (and the branches on
   // the wave's role) scalar
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int units = a.B * a.H;
+  const bool out_wg = SPLIT && (int)blockIdx.x >= units;
   x.lane = tid & 63;
   x.g = x.lane >> 4;
   x.c = x.lane & 15;
   x.w = wave & 3;
   x.fo = 16 * x.w + 4 * x.g;
-  x.unit = blockIdx.x;
+  x.unit = out_wg ? (int)blockIdx.x - units : (int)blockIdx.x;
   x.head = x.unit % a.H;
   x.T = a.T;
   x.n = (a.T + 15) / 16;
   x.tpm = MB16 ? 1 : a.tiles_per_mb;
   x.row0 = (size_t)x.unit * a.T;
-  if (wave < 4) chain_part<BF16, LN, RES, MB16>(L, a, x);
-  else if (wave < 8) update_part<BF16, LN, RES, MB16>(L, a, x);
-  else output_part<BF16, LN, RES, MB16>(L, a, x);
+  if constexpr (!SPLIT) {
+    __shared__ LinLds<BF16> L;
+    if (wave < 4) chain_part<BF16, LN, RES, MB16>(L, a, x);
+    else if (wave < 8) update_part<BF16, LN, RES, MB16, false>(L, a, x);
+    else output_part<BF16, LN, RES, true>(L, a, x);
+  } else {
+    __shared__ SplitLds<BF16> S;
+    if (!out_wg) {
+      if (wave < 4) chain_part<BF16, LN, RES, MB16>(S.c, a, x);
+      else if (wave < 8) update_part<BF16, LN, RES, MB16, true>(S.c, a, x);
+      else if (wave < 10) feed_copy_part<BF16>(S.c, a, x, wave - 8);
+      else handoff_part<BF16>(S.c, a, x, wave - 10);
+    } else {
+      if (wave < 4) out_state_part<BF16, LN, RES>(S.o, a, x);
+      else if (wave < 8) output_part<BF16, LN, RES, false>(S.o, a, x);
+      else out_copy_part<BF16>(S.o, a, x, wave - 8);
+    }
+  }
+}
+
+__global__ void zero_words(uint32_t* p, int n) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+template <bool BF16, bool LN, bool RES, bool SPLIT>
+hipError_t launch4(const LinearArgs& a, hipStream_t s) {
+  const int units = a.B * a.H;
+  const dim3 grid(SPLIT ? 2 * units : units), block(NT);
+  if (SPLIT) {
+    // publication counters and error words start at zero (a fill kernel
+    // rather than a memset, so that the launch can be captured in a graph)
+    const int words = units * 64 + 32;
+    hipLaunchKernelGGL(zero_words, dim3((words + 255) / 256), dim3(256), 0, s, a.ws_flags, words);
+  }
+  if (a.tiles_per_mb == 1)
+    hipLaunchKernelGGL((ttt_linear_fwd<BF16, LN, RES, true, SPLIT>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((ttt_linear_fwd<BF16, LN, RES, false, SPLIT>), grid, block, 0, s, a);
+  return hipGetLastError();
 }
 
 template <bool BF16, bool LN, bool RES>
 hipError_t launch3(const LinearArgs& a, hipStream_t s) {
-  const dim3 grid(a.B * a.H), block(NT);
-  if (a.tiles_per_mb == 1)
-    hipLaunchKernelGGL((ttt_linear_fwd<BF16, LN, RES, true>), grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL((ttt_linear_fwd<BF16, LN, RES, false>), grid, block, 0, s, a);
-  return hipGetLastError();
+  return a.split ? launch4<BF16, LN, RES, true>(a, s) : launch4<BF16, LN, RES, false>(a, s);
 }
 
 template <bool BF16>

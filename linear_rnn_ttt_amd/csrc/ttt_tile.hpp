@@ -33,12 +33,13 @@ __device__ __forceinline__ int lds_off(int t, int col) {  // element offset
   return t * D + (((col / EPC) ^ (t & 7)) * EPC) + (col % EPC);
 }
 
-// Double-buffered staging area: blocks of TB tiles of q, k, v and eta.
-template <bool BF16, int TB>
+// Double-buffered staging area: blocks of TB tiles of NX tensors (q, k, v
+// in that order, the first NX of them) and eta.
+template <bool BF16, int TB, int NX = 3>
 struct Stage {
   using E = typename Io<BF16>::E;
   static constexpr int TOK = TB * 16;
-  E qkv[2][3][TOK * D];
+  E qkv[2][NX][TOK * D];
   float eta[2][TOK];
 };
 
@@ -51,9 +52,10 @@ struct Stage {
 // picks the source chunk that belongs in that swizzled slot.  Rows past T
 // re-read row T-1 (finite data; their eta is ignored by the scan).
 // The share can be issued in `parts` calls (part = 0 .. parts-1), which
-// spreads the copy instructions of a block over several tiles.
-template <bool BF16, int TB>
-__device__ __forceinline__ void stage_issue(Stage<BF16, TB>& L, const void* q, const void* k,
+// spreads the copy instructions of a block over several tiles.  A null
+// tensor (or eta) is not copied.
+template <bool BF16, int TB, int NX>
+__device__ __forceinline__ void stage_issue(Stage<BF16, TB, NX>& L, const void* q, const void* k,
                                             const void* v, const float* eta, size_t row0,
                                             int blk, int T, int buf, int w, int part = 0,
                                             int parts = 1) {
@@ -73,14 +75,14 @@ __device__ __forceinline__ void stage_issue(Stage<BF16, TB>& L, const void* q, c
     const int tok = min(tok0 + t, T - 1);
     const size_t goff = (row0 + tok) * (size_t)RB + j * 16;
 #pragma unroll
-    for (int x = 0; x < 3; ++x) {
-      if ((3 * n + x) % parts != part) continue;
+    for (int x = 0; x < NX; ++x) {
+      if (!src[x] || (3 * n + x) % parts != part) continue;
       TTT_LDS void* dst = (TTT_LDS void*)(reinterpret_cast<char*>(L.qkv[buf][x]) +
                                           (NI * w + n) * 1024);
       __builtin_amdgcn_global_load_lds(src[x] + goff, dst, 16, 0, 0);
     }
   }
-  if (part == 0 && w * 64 + l < TOK) {   // blocks of fewer than 64 tokens: the lanes past TOK idle
+  if (eta && part == 0 && w * 64 + l < TOK) {   // blocks of fewer than 64 tokens: the lanes past TOK idle
     const int tok = min(tok0 + w * 64 + l, T - 1);
     TTT_LDS void* dst = (TTT_LDS void*)(&L.eta[buf][w * 64]);
     __builtin_amdgcn_global_load_lds(eta + row0 + tok, dst, 4, 0, 0);

@@ -56,15 +56,33 @@ def _stream(q, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
+# Shortest sequence for which the two-workgroup launch is chosen by default
+# (below it the second workgroup's lag behind the first is a visible share
+# of the run).
+SPLIT_MIN_T = 1024
+
+
+def _compute_units(dev) -> int:
+    return torch.cuda.get_device_properties(dev).multi_processor_count
+
+
 def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,
                        w0: torch.Tensor, ln_gamma: Optional[torch.Tensor] = None,
                        ln_beta: Optional[torch.Tensor] = None, *, mini_batch: int = 16,
                        eps: float = 1e-6, layer_norm: bool = True, residual: bool = True,
                        state0_per_batch: bool = False, z: Optional[torch.Tensor] = None,
                        w_out: Optional[torch.Tensor] = None, return_state: bool = True,
+                       split: Optional[bool] = None, workspace: Optional[torch.Tensor] = None,
                        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """TTT-Linear forward scan on the GPU; returns (z [B,H,T,d], W_final
-    [B,H,d,d] fp32 or None).  See include/ttt.h for the semantics."""
+    [B,H,d,d] fp32 or None).  See include/ttt.h for the semantics.
+
+    split: True runs ttt_linear_forward_split (two workgroups per unit, a
+    device workspace), False ttt_linear_forward; None picks the split launch
+    when B*H is at most half the compute units and T >= SPLIT_MIN_T.  The
+    results are the same either way.  workspace: a uint8 GPU tensor of at
+    least ttt_linear_split_workspace_bytes bytes to use instead of a fresh
+    one."""
     _dev_tensor("q", q)
     B, H, T, d = q.shape
     _dev_tensor("k", k, q.dtype, q.shape)
@@ -84,10 +102,21 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
     if w_out is not None:
         _dev_tensor("w_out", w_out, torch.float32, (B, H, d, d))
     p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
-    rc = _lib.lib().ttt_linear_forward(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
-                                       _ptr(w0), _ptr(ln_gamma), _ptr(ln_beta), _ptr(z),
-                                       _ptr(w_out), _stream(q, stream))
-    _lib.check("ttt_linear_forward", rc)
+    if split is None:
+        split = 2 * B * H <= _compute_units(q.device) and T >= SPLIT_MIN_T
+    args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), _ptr(ln_gamma),
+            _ptr(ln_beta), _ptr(z), _ptr(w_out))
+    if split:
+        need = int(_lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(p)))
+        if workspace is None:
+            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+        _dev_tensor("workspace", workspace, torch.uint8)
+        rc = _lib.lib().ttt_linear_forward_split(*args, _ptr(workspace),
+                                                 workspace.numel(), _stream(q, stream))
+        _lib.check("ttt_linear_forward_split", rc)
+    else:
+        rc = _lib.lib().ttt_linear_forward(*args, _stream(q, stream))
+        _lib.check("ttt_linear_forward", rc)
     return z, w_out
 
 

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 1
+    assert _lib.abi_version() == 2
     for code in range(7):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
@@ -123,3 +123,39 @@ def test_mlp_rejects_null_and_partial_outputs_and_aliasing():
     assert _mlp(_params(), z=_addr(2)) == _lib.TTT_ERR_ALIAS
     assert _mlp(_params(), w2o=_addr(12)) == _lib.TTT_ERR_ALIAS            # w2_out == w1_out
     assert _mlp(_params(), b2o=_addr(8)) == _lib.TTT_ERR_ALIAS             # b2_out == b2
+
+
+def _split(p, ws=None, ws_bytes=None, **ptrs):
+    names = ["q", "k", "v", "eta", "w0", "g", "b", "z", "w_out"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    if ws is None:
+        ws = _addr(20)
+    if ws_bytes is None:
+        ws_bytes = _lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(p)) if p else 1 << 30
+    return _lib.lib().ttt_linear_forward_split(ctypes.byref(p) if p is not None else None, *args,
+                                               ws, ws_bytes, None)
+
+
+def test_split_workspace_size():
+    # 256 B of counters per unit, 256 B of error words (rounded), 4 KB per tile and unit
+    p = _params(B=2, H=3, T=100)
+    units, tiles = 6, 7
+    assert _lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(p)) == \
+        units * 256 + 256 + units * tiles * 4096
+    assert _lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(_params(T=0))) == 0
+    assert _lib.lib().ttt_linear_split_workspace_bytes(None) == 0
+
+
+def test_split_rejects_bad_arguments():
+    p = _params()
+    need = _lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(p))
+    assert _split(None) == _lib.TTT_ERR_NULL
+    assert _split(p, ws=ctypes.c_void_p(0)) == _lib.TTT_ERR_NULL
+    assert _split(p, ws_bytes=need - 1) == _lib.TTT_ERR_SHAPE
+    assert _split(p, ws=ctypes.c_void_p(BASE + 20 * GAP + 128)) == _lib.TTT_ERR_ARG
+    assert _split(p, ws=_addr(8)) == _lib.TTT_ERR_ALIAS                    # workspace == z
+    assert _split(p, ws=ctypes.c_void_p(BASE + 1 * GAP - 4096)) == _lib.TTT_ERR_ALIAS  # runs into q
+    assert _split(_params(mini_batch=8)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _split(_params(d=32)) == _lib.TTT_ERR_UNSUPPORTED
+    for name in ["q", "k", "v", "eta", "w0", "z", "g", "b"]:
+        assert _split(p, **{name: None}) == _lib.TTT_ERR_NULL, name
