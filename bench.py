@@ -2,8 +2,10 @@
 """Benchmark of the TTT-layer forward scan on one MI355X.
 
 A step is one forward scan over the whole workload (every (batch, head)
-unit, every token): one call of ttt_linear_forward (or ttt_mlp_forward),
-i.e. one launch of the scan kernel, on inputs already resident in HBM.
+unit, every token): one call of the Python op ttt_linear_forward (or
+ttt_mlp_forward) as a user makes it, on inputs already resident in HBM.  For
+TTT-Linear the op picks the one- or the two-workgroup launch by the unit
+count and length (linear_uses_split); the JSON line names the one used.
 
 Default workload: TTT-Linear at the 1.3B-model layer shape, B = 4, H = 32,
 d = 64, T = 8192, mini-batch 16, bf16 q/k/v/z, fp32 state and eta (seeded
@@ -135,6 +137,15 @@ def make_step(w, dev):
     return step, z
 
 
+def launch_desc(w) -> str:
+    if w.kind == "linear":
+        from linear_rnn_ttt_amd.ops import linear_uses_split
+        if linear_uses_split(w.B, w.H, w.T):
+            return "ttt_linear_forward_split: two workgroups per (batch, head) unit"
+        return "ttt_linear_forward: one workgroup per (batch, head) unit"
+    return "ttt_mlp_forward: one workgroup per (batch, head) unit"
+
+
 def cpu_baseline(w, inp, budget_s: float):
     """The fp64 oracle as it stands, on the host cores (at most 16 threads,
     the host share of one GPU).  The whole workload when it fits the
@@ -250,7 +261,7 @@ def run(args) -> dict:
                                                                  else "MLP"),
                    "B": w.B, "H": w.H, "T": w.T, "d": w.d, "mini_batch": w.mini_batch,
                    "io": w.io, "state": "fp32", "ln_eps": w.eps, "global_batch": w.B,
-                   "seq_len": w.T, "parallelism": "none (1 GPU, one workgroup per unit)"},
+                   "seq_len": w.T, "parallelism": "none (1 GPU)", "launch": launch_desc(w)},
         "roofline": roof,
         "outputs_finite": ok,
     }

@@ -99,6 +99,8 @@ struct LinLds {
   u32x4 mqb[2][64];     // tril(K_t Q_t^T) as [hi, lo] (hi only for bf16 data),
                         // update wave 2 -> every update wave
   float mqm[2][16];     // q . w_bar per token of tile t, update wave 2 -> every update wave
+  u32x2 ktb[2][4][64];  // K_t^T as 16x16x16 A operands (bf16 data, split units),
+                        // update wave 2 -> every update wave
   uint16_t cst[4][D];   // bf16 rows: w_bar hi, 2 gamma hi, w_bar lo, 2 gamma lo
 };
 
@@ -503,11 +505,16 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       L.cst[w + 2][lane] = (uint16_t)bf16_bits(v - __builtin_bit_cast(float, h << 16));
     }
   }
+  // K^T shared through LDS by one wave (bf16 data, split units: wave 2 has
+  // no other item there)
+  constexpr bool KTS = SPLIT && BF16;
   // "tile -1": no update and no output correction in period 0
   L.gtb[1][w][lane] = u32x4{0u, 0u, 0u, 0u};
   if (w == 2) {
     L.mqb[1][lane] = u32x4{0u, 0u, 0u, 0u};
     if (lane < 16) L.mqm[1][lane] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) L.ktb[1][r][lane] = u32x2{0u, 0u};
   }
   // The tiles past the end are read from stale staging rows (their
   // gradient is zero, but 0 * Inf would not be): buffer 1 starts as zeros
@@ -595,6 +602,10 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       const Split4 m1 = {hi_of(mq), lo_of(mq)};
       Op4 ktn[4];
       if constexpr (!BF16) cols8<BF16>(ktn, Kp, c, g);
+      if constexpr (KTS) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) kt1[r] = Op4{L.ktb[(p - 1) & 1][r][lane], u32x2{0u, 0u}};
+      }
       __builtin_amdgcn_sched_barrier(0);
       // ---- output pre-activation of tile p-1 around its shift:
       //      (Q W_{p-2})^T + (-eta G_{p-1})^T tril(K Q^T) - q . w_bar
@@ -657,12 +668,16 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       if constexpr (BF16) {
         // half of a row operand times the identity is the transposed 16x16
         // block, whose rows are the state's features feat(r, c)
-        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        if (!KTS || w == 2) {
+          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const u32x4 h = kc0.p[r >> 1].hi;
-          const f32x4 t = mfma16((r & 1) ? u32x2{h.z, h.w} : u32x2{h.x, h.y}, ident, zero);
-          kt1[r] = Op4{u32x2{pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])}, u32x2{0u, 0u}};
+          for (int r = 0; r < 4; ++r) {
+            const u32x4 h = kc0.p[r >> 1].hi;
+            const f32x4 t = mfma16((r & 1) ? u32x2{h.z, h.w} : u32x2{h.x, h.y}, ident, zero);
+            const u32x2 kt = {pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])};
+            if constexpr (KTS) L.ktb[p & 1][r][lane] = kt;
+            else kt1[r] = Op4{kt, u32x2{0u, 0u}};
+          }
         }
       } else {
 #pragma unroll

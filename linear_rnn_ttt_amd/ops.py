@@ -56,10 +56,18 @@ def _stream(q, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-# Shortest sequence for which the two-workgroup launch is chosen by default
-# (below it the second workgroup's lag behind the first is a visible share
-# of the run).
-SPLIT_MIN_T = 1024
+# When the two-workgroup launch is chosen by default.  Measured on MI355X
+# (256 CUs) at T = 8192: 32 units 8 % faster, 64 units 6 %, 96 units 5 %,
+# 128 units (every CU busy) no gain, since the shader clock drops with the
+# load; T = 2048 loses about 2 % to the second workgroup's lag.
+SPLIT_MAX_UNIT_SHARE = 3 / 8   # B*H at most this share of the compute units
+SPLIT_MIN_T = 4096
+
+
+def linear_uses_split(B: int, H: int, T: int, device=None) -> bool:
+    """The launch ttt_linear_forward picks when split=None."""
+    cus = _compute_units(torch.device("cuda") if device is None else device)
+    return B * H <= SPLIT_MAX_UNIT_SHARE * cus and T >= SPLIT_MIN_T
 
 
 def _compute_units(dev) -> int:
@@ -78,9 +86,9 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
     [B,H,d,d] fp32 or None).  See include/ttt.h for the semantics.
 
     split: True runs ttt_linear_forward_split (two workgroups per unit, a
-    device workspace), False ttt_linear_forward; None picks the split launch
-    when B*H is at most half the compute units and T >= SPLIT_MIN_T.  The
-    results are the same either way.  workspace: a uint8 GPU tensor of at
+    device workspace; B*H at most half the compute units), False
+    ttt_linear_forward; None decides by linear_uses_split.  The results are
+    the same either way.  workspace: a uint8 GPU tensor of at
     least ttt_linear_split_workspace_bytes bytes to use instead of a fresh
     one."""
     _dev_tensor("q", q)
@@ -103,7 +111,7 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
         _dev_tensor("w_out", w_out, torch.float32, (B, H, d, d))
     p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
     if split is None:
-        split = 2 * B * H <= _compute_units(q.device) and T >= SPLIT_MIN_T
+        split = linear_uses_split(B, H, T, q.device)
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), _ptr(ln_gamma),
             _ptr(ln_beta), _ptr(z), _ptr(w_out))
     if split:
