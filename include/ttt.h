@@ -114,7 +114,8 @@ uint64_t ttt_linear_split_workspace_bytes(const ttt_params* p);
 
 /*
  * TTT-Linear forward scan, same method, arguments and results as
- * ttt_linear_forward (bit for bit), on two workgroups per (batch, head)
+ * ttt_linear_forward (bit for bit; but no in-place resume: w_out == w0 is
+ * TTT_ERR_ALIAS here), on two workgroups per (batch, head)
  * unit: one runs the serial part of the scan (the gradient of every
  * 16-token tile) and streams each tile's gradient through `workspace` to
  * the other, on another compute unit, which replays the state updates and

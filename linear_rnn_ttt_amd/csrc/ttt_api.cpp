@@ -182,6 +182,10 @@ ttt_status ttt_linear_forward_split(const ttt_params* p, const void* q, const vo
   const ttt_status st = linear_args(p, q, k, v, eta, w0, ln_gamma, ln_beta, z, w_out, workspace,
                                     workspace_bytes, &a);
   if (st != TTT_OK) return st;
+  // no in-place resume: the second workgroup of a unit reads the initial
+  // state at its own start, which may come after the first has written the
+  // final state
+  if (w_out && static_cast<const void*>(w_out) == w0) return TTT_ERR_ALIAS;
   // both workgroups of every unit must be resident at once
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||

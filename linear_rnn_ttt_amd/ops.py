@@ -110,8 +110,9 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
     if w_out is not None:
         _dev_tensor("w_out", w_out, torch.float32, (B, H, d, d))
     p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
-    if split is None:
-        split = linear_uses_split(B, H, T, q.device)
+    if split is None:   # the split launch has no in-place form
+        split = (linear_uses_split(B, H, T, q.device) and
+                 (w_out is None or w_out.data_ptr() != w0.data_ptr()))
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), _ptr(ln_gamma),
             _ptr(ln_beta), _ptr(z), _ptr(w_out))
     if split:

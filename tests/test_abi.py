@@ -159,3 +159,6 @@ def test_split_rejects_bad_arguments():
     assert _split(_params(d=32)) == _lib.TTT_ERR_UNSUPPORTED
     for name in ["q", "k", "v", "eta", "w0", "z", "g", "b"]:
         assert _split(p, **{name: None}) == _lib.TTT_ERR_NULL, name
+    # no in-place resume in the split launch (the one-workgroup launch allows it)
+    p1 = _params(state0_per_batch=1)
+    assert _split(p1, w_out=_addr(5)) == _lib.TTT_ERR_ALIAS                 # w_out == w0

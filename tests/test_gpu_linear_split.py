@@ -100,3 +100,17 @@ def test_split_rejects_more_units_than_half_the_compute_units():
     with pytest.raises(_lib.TTTArgumentError) as e:
         ttt_linear_forward(*_dev(inp, "bf16"), split=True)
     assert e.value.code == _lib.TTT_ERR_UNSUPPORTED
+
+
+def test_split_refuses_in_place_resume_and_auto_falls_back():
+    inp = make_inputs(BASE, B=1, H=2, T=4096)
+    inp["w0"] = np.ascontiguousarray(np.stack([inp["w0"]])).astype(np.float32)
+    args = _dev(inp, "bf16")
+    w0 = args[4]
+    with pytest.raises(_lib.TTTArgumentError) as e:
+        ttt_linear_forward(*args, split=True, state0_per_batch=True, w_out=w0)
+    assert e.value.code == _lib.TTT_ERR_ALIAS
+    ref_z, ref_w = ttt_linear_forward(*args, split=False, state0_per_batch=True)
+    z, wf = ttt_linear_forward(*args, state0_per_batch=True, w_out=w0)   # auto: one workgroup
+    torch.cuda.synchronize()
+    assert torch.equal(z, ref_z) and torch.equal(wf, ref_w) and wf.data_ptr() == w0.data_ptr()
