@@ -67,6 +67,11 @@
 //   * One barrier per tile orders every exchange.  Both loops are free of
 //     branches within a tile (past the end: stale rows, gradient forced to
 //     zero, z stores dropped by the buffer range check).
+//   * SPLIT instances run each unit on two workgroups: the output side (q
+//     products, output correction, output LN, z) moves to a second
+//     workgroup on another CU, which replays the state from the gradients
+//     the first streams to it through device memory (see "Split units"
+//     below).
 #include "ttt_device.hpp"
 #include "ttt_kernels.hpp"
 #include "ttt_tile.hpp"
