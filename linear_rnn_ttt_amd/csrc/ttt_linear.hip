@@ -593,11 +593,21 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       // every LDS read of the period first
       const auto* Kp = tile_rows(L.st, 1, blk, tb);
       const u32x4 g1 = L.gtb[(p - 1) & 1][w][lane];  // (-eta G_{p-1})^T as [hi, lo]
-      Rows qr = {};
-      if constexpr (!SPLIT) qr = rows8<BF16>(tile_rows(L.st, 0, blk, tb), c, g);
-      const Rows kn = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 2), c, g);
-      Rows vn;
-      if (w == 3 && LN) vn = rows8<BF16>(tile_rows(L.st, 2, blk, tb + 2), c, g);
+      // rows of q_p, k_{p+2}, v_{p+2}: read here for bf16 data; for fp32
+      // data (hi/lo rows, twice the registers) just before their first use
+      Rows qr = {}, kn, vn;
+      auto read_q = [&] {
+        if constexpr (!SPLIT) qr = rows8<BF16>(tile_rows(L.st, 0, blk, tb), c, g);
+      };
+      auto read_kn = [&] { kn = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 2), c, g); };
+      auto read_vn = [&] {
+        if (w == 3 && LN) vn = rows8<BF16>(tile_rows(L.st, 2, blk, tb + 2), c, g);
+      };
+      if constexpr (BF16) {
+        read_q();
+        read_kn();
+        read_vn();
+      }
       u32x4 mq = {};     // tril(K_{p-1} Q_{p-1}^T)
       float muq1 = 0.f;  // q . w_bar, tile p-1
       if constexpr (!SPLIT) {
@@ -605,8 +615,17 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         if (LN) muq1 = L.mqm[(p - 1) & 1][c];
       }
       const Split4 m1 = {hi_of(mq), lo_of(mq)};
-      Op4 ktn[4];
-      if constexpr (!BF16) cols8<BF16>(ktn, Kp, c, g);
+      // rows of K_p and K_{p+1}: carried from the period that read them as
+      // K_{p+2} (bf16 data), re-read where used (fp32 data, whose hi/lo rows
+      // would not fit in the registers besides the state)
+      Rows k0, k1;
+      if constexpr (BF16) {
+        k0 = kc0;
+        k1 = kc1;
+      } else {
+        if (w == 1 || (!SPLIT && w == 2)) k0 = rows8<BF16>(Kp, c, g);
+        if (w == 0) k1 = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 1), c, g);
+      }
       if constexpr (KTS) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) kt1[r] = Op4{L.ktb[(p - 1) & 1][r][lane], u32x2{0u, 0u}};
@@ -636,6 +655,10 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         Ab[1] = Ac[1];
       }
       // ---- products of W_{p-1} (past the end: stale rows, unused)
+      if constexpr (!BF16) {
+        read_q();
+        read_kn();
+      }
       if constexpr (!SPLIT) qw1 = times_state<LO>(Ac, qr);
       {
         // gradient point two tiles ahead: K_{p+2} W_{p-1}, or the
@@ -649,7 +672,7 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       //      wave in the next period (one wave: they do not depend on the
       //      column block)
       if (!SPLIT && w == 2) {
-        f32x4 M = gram<LO>(kc0, qr);  // K_p Q_p^T
+        f32x4 M = gram<LO>(k0, qr);  // K_p Q_p^T
 #pragma unroll
         for (int i = 0; i < 4; ++i) M[i] = causal[i] ? M[i] : 0.f;
         L.mqb[p & 1][lane] = LO ? hilo(split4(M))
@@ -663,10 +686,11 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       //      each: the score tiles K_{p+1} K_{p+2}^T, K_p K_{p+2}^T and
       //      (k . w_bar, sum_f u_f)
       if (w == 0) {
-        L.grb[p & 1][0][lane] = hilo(split4(gram<LO>(kc1, kn)));
+        L.grb[p & 1][0][lane] = hilo(split4(gram<LO>(k1, kn)));
       } else if (w == 1) {
-        L.grb[p & 1][1][lane] = hilo(split4(gram<LO>(kc0, kn)));
+        L.grb[p & 1][1][lane] = hilo(split4(gram<LO>(k0, kn)));
       } else if (w == 3 && LN) {
+        if constexpr (!BF16) read_vn();
         L.tkb[p & 1][c] = token_inputs(kn, vn);
       }
       // ---- K_p^T for the next update
@@ -677,7 +701,7 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
           const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            const u32x4 h = kc0.p[r >> 1].hi;
+            const u32x4 h = k0.p[r >> 1].hi;
             const f32x4 t = mfma16((r & 1) ? u32x2{h.z, h.w} : u32x2{h.x, h.y}, ident, zero);
             const u32x2 kt = {pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])};
             if constexpr (KTS) L.ktb[p & 1][r][lane] = kt;
@@ -685,11 +709,12 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
           }
         }
       } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) kt1[r] = ktn[r];
+        cols8<BF16>(kt1, Kp, c, g);
       }
-      kc0 = kc1;
-      kc1 = kn;
+      if constexpr (BF16) {
+        kc0 = kc1;
+        kc1 = kn;
+      }
       lds_barrier();
     }
   }
@@ -961,8 +986,6 @@ __device__ __forceinline__ void out_state_part(OutLds<BF16>& L, const LinearArgs
       const u32x4 mq = L.mqb[(p - 1) & 1][lane];
       const float muq1 = LN ? L.mqm[(p - 1) & 1][c] : 0.f;
       const Split4 m1 = {hi_of(mq), lo_of(mq)};
-      Op4 ktn[4];
-      if constexpr (!BF16) cols8<BF16>(ktn, Kp, c, g);
       __builtin_amdgcn_sched_barrier(0);
       // ---- output pre-activation of tile p-1 around its shift
       {
@@ -1005,8 +1028,7 @@ __device__ __forceinline__ void out_state_part(OutLds<BF16>& L, const LinearArgs
           kt1[r] = Op4{u32x2{pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])}, u32x2{0u, 0u}};
         }
       } else {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) kt1[r] = ktn[r];
+        cols8<BF16>(kt1, Kp, c, g);
       }
       lds_barrier();
     }
