@@ -140,7 +140,9 @@ def make_step(w, dev):
 def launch_desc(w) -> str:
     if w.kind == "linear":
         from linear_rnn_ttt_amd.ops import linear_uses_split
-        if linear_uses_split(w.B, w.H, w.T):
+        import torch
+        if linear_uses_split(w.B, w.H, w.T,
+                             dtype=torch.bfloat16 if w.io == "bf16" else torch.float32):
             return "ttt_linear_forward_split: two workgroups per (batch, head) unit"
         return "ttt_linear_forward: one workgroup per (batch, head) unit"
     return "ttt_mlp_forward: one workgroup per (batch, head) unit"

@@ -56,18 +56,21 @@ def _stream(q, stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(s.cuda_stream)
 
 
-# When the two-workgroup launch is chosen by default.  Measured on MI355X
-# (256 CUs) at T = 8192: 32 units 8 % faster, 64 units 6 %, 96 units 5 %,
-# 128 units (every CU busy) no gain, since the shader clock drops with the
-# load; T = 2048 loses about 2 % to the second workgroup's lag.
-SPLIT_MAX_UNIT_SHARE = 3 / 8   # B*H at most this share of the compute units
-SPLIT_MIN_T = 4096
+# When the two-workgroup launch is chosen by default (measured on MI355X,
+# 256 CUs, steady state).  bf16 data at T = 8192: 32 units 8 % faster, 64
+# units 6 %, 96 units 5 %, 128 units (every CU busy) no gain, since the
+# shader clock drops with the load; at T = 2048 it loses about 2 % to the
+# second workgroup's lag.  fp32 data, whose update waves carry 1.5x the
+# matrix products of bf16 data and so delay the chain more: 24 % faster at
+# 128 units, 31 % at 64, 26 % at 96 units with T = 2048.
+SPLIT_POLICY = {"bf16": (3 / 8, 4096), "f32": (1 / 2, 1024)}  # (max B*H / CUs, min T)
 
 
-def linear_uses_split(B: int, H: int, T: int, device=None) -> bool:
+def linear_uses_split(B: int, H: int, T: int, device=None, dtype=torch.bfloat16) -> bool:
     """The launch ttt_linear_forward picks when split=None."""
     cus = _compute_units(torch.device("cuda") if device is None else device)
-    return B * H <= SPLIT_MAX_UNIT_SHARE * cus and T >= SPLIT_MIN_T
+    share, min_t = SPLIT_POLICY["bf16" if dtype == torch.bfloat16 else "f32"]
+    return B * H <= share * cus and T >= min_t
 
 
 def _compute_units(dev) -> int:
@@ -111,7 +114,7 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
         _dev_tensor("w_out", w_out, torch.float32, (B, H, d, d))
     p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
     if split is None:   # the split launch has no in-place form
-        split = (linear_uses_split(B, H, T, q.device) and
+        split = (linear_uses_split(B, H, T, q.device, q.dtype) and
                  (w_out is None or w_out.data_ptr() != w0.data_ptr()))
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), _ptr(ln_gamma),
             _ptr(ln_beta), _ptr(z), _ptr(w_out))
