@@ -18,11 +18,13 @@ __all__ = ["ttt_linear_forward", "ttt_mlp_forward"]
 HEAD_DIM = 64
 
 
-def _dev_tensor(name, t, dtype=None, shape=None):
+def _dev_tensor(name, t, dtype=None, shape=None, device=None):
     if not isinstance(t, torch.Tensor):
         raise TypeError("%s must be a torch.Tensor" % name)
     if t.device.type != "cuda":
         raise ValueError("%s must be a GPU tensor (got %s)" % (name, t.device))
+    if device is not None and t.device != device:
+        raise ValueError("%s must be on %s, like q (got %s)" % (name, device, t.device))
     if dtype is not None and t.dtype != dtype:
         raise ValueError("%s must be %s (got %s)" % (name, dtype, t.dtype))
     if shape is not None and tuple(t.shape) != tuple(shape):
@@ -96,39 +98,41 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
     one."""
     _dev_tensor("q", q)
     B, H, T, d = q.shape
-    _dev_tensor("k", k, q.dtype, q.shape)
-    _dev_tensor("v", v, q.dtype, q.shape)
-    _dev_tensor("eta", eta, torch.float32, (B, H, T))
-    _dev_tensor("w0", w0, torch.float32, (B, H, d, d) if state0_per_batch else (H, d, d))
+    _dev_tensor("k", k, q.dtype, q.shape, device=q.device)
+    _dev_tensor("v", v, q.dtype, q.shape, device=q.device)
+    _dev_tensor("eta", eta, torch.float32, (B, H, T), device=q.device)
+    _dev_tensor("w0", w0, torch.float32, (B, H, d, d) if state0_per_batch else (H, d, d),
+                device=q.device)
     if layer_norm:
-        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d))
-        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d))
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d), device=q.device)
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d), device=q.device)
     else:
         ln_gamma = ln_beta = None
     if z is None:
         z = torch.empty_like(q)
-    _dev_tensor("z", z, q.dtype, q.shape)
+    _dev_tensor("z", z, q.dtype, q.shape, device=q.device)
     if w_out is None and return_state:
         w_out = torch.empty((B, H, d, d), dtype=torch.float32, device=q.device)
     if w_out is not None:
-        _dev_tensor("w_out", w_out, torch.float32, (B, H, d, d))
+        _dev_tensor("w_out", w_out, torch.float32, (B, H, d, d), device=q.device)
     p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
     if split is None:   # the split launch has no in-place form
         split = (linear_uses_split(B, H, T, q.device, q.dtype) and
                  (w_out is None or w_out.data_ptr() != w0.data_ptr()))
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), _ptr(ln_gamma),
             _ptr(ln_beta), _ptr(z), _ptr(w_out))
-    if split:
-        need = int(_lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(p)))
-        if workspace is None:
-            workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
-        _dev_tensor("workspace", workspace, torch.uint8)
-        rc = _lib.lib().ttt_linear_forward_split(*args, _ptr(workspace),
-                                                 workspace.numel(), _stream(q, stream))
-        _lib.check("ttt_linear_forward_split", rc)
-    else:
-        rc = _lib.lib().ttt_linear_forward(*args, _stream(q, stream))
-        _lib.check("ttt_linear_forward", rc)
+    with torch.cuda.device(q.device):   # the library launches on the current device
+        if split:
+            need = int(_lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(p)))
+            if workspace is None:
+                workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+            _dev_tensor("workspace", workspace, torch.uint8, device=q.device)
+            rc = _lib.lib().ttt_linear_forward_split(*args, _ptr(workspace),
+                                                     workspace.numel(), _stream(q, stream))
+            _lib.check("ttt_linear_forward_split", rc)
+        else:
+            rc = _lib.lib().ttt_linear_forward(*args, _stream(q, stream))
+            _lib.check("ttt_linear_forward", rc)
     return z, w_out
 
 
@@ -144,22 +148,22 @@ def ttt_mlp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torc
     _dev_tensor("q", q)
     B, H, T, d = q.shape
     m = w1.shape[-1]
-    _dev_tensor("k", k, q.dtype, q.shape)
-    _dev_tensor("v", v, q.dtype, q.shape)
-    _dev_tensor("eta", eta, torch.float32, (B, H, T))
+    _dev_tensor("k", k, q.dtype, q.shape, device=q.device)
+    _dev_tensor("v", v, q.dtype, q.shape, device=q.device)
+    _dev_tensor("eta", eta, torch.float32, (B, H, T), device=q.device)
     lead = (B, H) if state0_per_batch else (H,)
-    _dev_tensor("w1", w1, torch.float32, lead + (d, m))
-    _dev_tensor("b1", b1, torch.float32, lead + (m,))
-    _dev_tensor("w2", w2, torch.float32, lead + (m, d))
-    _dev_tensor("b2", b2, torch.float32, lead + (d,))
+    _dev_tensor("w1", w1, torch.float32, lead + (d, m), device=q.device)
+    _dev_tensor("b1", b1, torch.float32, lead + (m,), device=q.device)
+    _dev_tensor("w2", w2, torch.float32, lead + (m, d), device=q.device)
+    _dev_tensor("b2", b2, torch.float32, lead + (d,), device=q.device)
     if layer_norm:
-        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d))
-        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d))
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d), device=q.device)
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d), device=q.device)
     else:
         ln_gamma = ln_beta = None
     if z is None:
         z = torch.empty_like(q)
-    _dev_tensor("z", z, q.dtype, q.shape)
+    _dev_tensor("z", z, q.dtype, q.shape, device=q.device)
     if state_out is None and return_state:
         f = dict(dtype=torch.float32, device=q.device)
         state_out = (torch.empty((B, H, d, m), **f), torch.empty((B, H, m), **f),
@@ -167,12 +171,13 @@ def ttt_mlp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torc
     if state_out is not None:
         for name, t, shp in zip(("w1_out", "b1_out", "w2_out", "b2_out"), state_out,
                                 ((B, H, d, m), (B, H, m), (B, H, m, d), (B, H, d))):
-            _dev_tensor(name, t, torch.float32, shp)
+            _dev_tensor(name, t, torch.float32, shp, device=q.device)
     outs = state_out if state_out is not None else (None,) * 4
     p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
-    rc = _lib.lib().ttt_mlp_forward(ctypes.byref(p), int(m), _ptr(q), _ptr(k), _ptr(v),
-                                    _ptr(eta), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
-                                    _ptr(ln_gamma), _ptr(ln_beta), _ptr(z),
-                                    *[_ptr(t) for t in outs], _stream(q, stream))
+    with torch.cuda.device(q.device):   # the library launches on the current device
+        rc = _lib.lib().ttt_mlp_forward(ctypes.byref(p), int(m), _ptr(q), _ptr(k), _ptr(v),
+                                        _ptr(eta), _ptr(w1), _ptr(b1), _ptr(w2), _ptr(b2),
+                                        _ptr(ln_gamma), _ptr(ln_beta), _ptr(z),
+                                        *[_ptr(t) for t in outs], _stream(q, stream))
     _lib.check("ttt_mlp_forward", rc)
     return z, state_out
