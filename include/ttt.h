@@ -81,7 +81,7 @@ enum {
 };
 
 typedef struct {
-  int32_t B, H, T, d;        /* B, H >= 1; T >= 1; d == 64 on gfx950 */
+  int32_t B, H, T, d;        /* B, H >= 1; 1 <= T <= 4194304; d == 64 on gfx950 */
   int32_t mini_batch;        /* b: Linear 16*n (n >= 1; b >= T allowed); MLP 16 */
   int32_t io_dtype;          /* ttt_dtype of q, k, v and z */
   uint32_t flags;            /* TTT_NO_LN | TTT_NO_RESIDUAL */

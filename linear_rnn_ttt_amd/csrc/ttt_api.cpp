@@ -15,6 +15,7 @@ namespace {
 
 constexpr int32_t kHeadDim = 64;
 constexpr int32_t kMlpHidden = 256;
+constexpr int32_t kMaxT = 1 << 22;  // tokens per unit
 
 struct Range {
   uintptr_t lo, hi;  // [lo, hi)
@@ -38,6 +39,9 @@ ttt_status check_common(const ttt_params* p, uint64_t* elems) {
   if (!(p->ln_eps >= 0.0f) || !std::isfinite(p->ln_eps)) return TTT_ERR_ARG;
   if (p->state0_per_batch != 0 && p->state0_per_batch != 1) return TTT_ERR_ARG;
   if (p->B < 1 || p->H < 1 || p->T < 1 || p->d < 1 || p->mini_batch < 1) return TTT_ERR_SHAPE;
+  // the kernels address one unit's rows (and its gradient stream) through
+  // 32-bit buffer ranges
+  if (p->T > kMaxT) return TTT_ERR_SHAPE;
   if (p->d != kHeadDim) return TTT_ERR_UNSUPPORTED;
   const uint64_t units = static_cast<uint64_t>(p->B) * static_cast<uint64_t>(p->H);
   if (units > 0x7fffffffull) return TTT_ERR_SHAPE;  // one workgroup per unit

@@ -66,6 +66,7 @@ def _mlp(p, hidden=256, **ptrs):
     (dict(d=32), _lib.TTT_ERR_UNSUPPORTED),
     (dict(d=0), _lib.TTT_ERR_SHAPE),
     (dict(T=0), _lib.TTT_ERR_SHAPE),
+    (dict(T=(1 << 22) + 1), _lib.TTT_ERR_SHAPE),
     (dict(B=0), _lib.TTT_ERR_SHAPE),
     (dict(H=-1), _lib.TTT_ERR_SHAPE),
     (dict(mini_batch=0), _lib.TTT_ERR_SHAPE),
