@@ -16,6 +16,8 @@ mlp(q, k, v, eta, w1, b1, w2, b2, gamma, beta, ...) -> (z, (w1, b1, w2, b2))
 linear_loss_grad(W, k, v, gamma, beta, ...) -> (loss, dW)
 mlp_loss_grad(W1, b1, W2, b2, k, v, gamma, beta, ...) -> (loss, grads)
 linear_apply / mlp_apply: the inner model f for one token.
+linear_decode_step(W, W_base, q, k, v, eta, gamma, beta, pos=...) -> (z, W, W_base):
+    one token of the TTT-Linear scan for one unit, the streaming form.
 build(): compile ``libttt_oracle.so`` with gcc.
 """
 from __future__ import annotations
@@ -219,3 +221,21 @@ def mlp_apply(W1, b1, W2, b2, x, gamma=None, beta=None, *, layer_norm=True,
                              _ptr(_f64(gamma) if layer_norm else None),
                              _ptr(_f64(beta) if layer_norm else None), _ptr(out))
     return out
+
+
+def linear_decode_step(W, W_base, q, k, v, eta, gamma=None, beta=None, *, pos,
+                       layer_norm=True, residual=True, eps=1e-6):
+    """One token of the TTT-Linear scan for one unit, carrying the stream's
+    state W, its mini-batch base W_base and the token's position pos in its
+    mini-batch (the LIT-801 record, "Key takeaways" items 1, 2 and 5: every
+    gradient of a mini-batch is taken at the state the mini-batch started
+    from, the state takes the tokens one by one, z uses the state after its
+    own token).  A new mini-batch (pos == 0) starts from the current W.
+    Returns (z, W_new, base) in fp64; base is the W_base to carry."""
+    W = _f64(W)
+    base = W if pos == 0 else _f64(W_base)
+    _, g = linear_loss_grad(base, k, v, gamma, beta, layer_norm=layer_norm,
+                            residual=residual, eps=eps)
+    W_new = W - float(eta) * g
+    z = linear_apply(W_new, q, gamma, beta, layer_norm=layer_norm, residual=residual, eps=eps)
+    return z, W_new, base.copy()

@@ -318,3 +318,54 @@ def test_long_scan_is_ill_conditioned_on_some_units():
     assert d[0, 0].max() > 1e-3
     assert d[0, 0, -1024:].max() > 10 * d[0, 0, 1024:2048].max()   # grows along the sequence
     assert d[0, 1].max() < 1e-5
+
+
+# --- streaming (decode) step -------------------------------------------------
+
+def _decode_run(q, k, v, eta, W, Wb, gamma, beta, b, t0=0, ln=True, res=True):
+    z = np.empty(q.shape, np.float64)
+    for t in range(q.shape[0]):
+        z[t], W, Wb = oracle.linear_decode_step(W, Wb, q[t], k[t], v[t], eta[t], gamma, beta,
+                                                pos=(t0 + t) % b, layer_norm=ln,
+                                                residual=res)
+    return z, W, Wb
+
+
+@pytest.mark.parametrize("b,ln,res", [(1, True, True), (4, True, True), (8, True, False),
+                                      (8, False, True), (40, True, True)])
+def test_decode_step_loop_is_the_scan(b, ln, res):
+    """Stepping token by token with pos = t mod b reproduces the mini-batch
+    scan: against the autograd scan (independent of the oracle's code) and
+    the oracle's own forward."""
+    rng = np.random.default_rng(71 + b)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, B=1, H=1, T=40, d=8)
+    q, k, v, eta, w0 = q[0, 0], k[0, 0], v[0, 0], eta[0, 0], w0[0]
+    z, W, _ = _decode_run(q, k, v, eta, w0, np.zeros_like(w0), gamma[0], beta[0], b,
+                          ln=ln, res=res)
+    zt, Wt = _scan_torch(_t(q), _t(k), _t(v), _t(eta), _t(w0), _t(gamma[0]), _t(beta[0]), b,
+                         ln, res)
+    assert np.abs(z - zt.numpy()).max() <= 1e-10 * np.abs(zt.numpy()).max()
+    assert np.abs(W - Wt.numpy()).max() <= 1e-10 * np.abs(Wt.numpy()).max()
+    zo, Wo = oracle.linear(q[None, None], k[None, None], v[None, None], eta[None, None],
+                           w0[None], gamma[:1], beta[:1], mini_batch=b, layer_norm=ln,
+                           residual=res)
+    assert np.abs(z - zo[0, 0]).max() <= 1e-12 * np.abs(zo).max()
+    assert np.abs(W - Wo[0, 0]).max() <= 1e-12 * np.abs(Wo).max()
+
+
+def test_decode_resumes_mid_minibatch():
+    """A stream cut inside a mini-batch continues exactly when it carries
+    the base along with the state: the position alone is not enough."""
+    rng = np.random.default_rng(83)
+    q, k, v, eta, w0, gamma, beta = _rand_problem(rng, B=1, H=1, T=40, d=8)
+    q, k, v, eta, w0, g, bt = q[0, 0], k[0, 0], v[0, 0], eta[0, 0], w0[0], gamma[0], beta[0]
+    b, T1 = 8, 21                              # cut after 5 of 8 tokens of a mini-batch
+    z, W, _ = _decode_run(q, k, v, eta, w0, np.zeros_like(w0), g, bt, b)
+    z1, W1, Wb1 = _decode_run(q[:T1], k[:T1], v[:T1], eta[:T1], w0, np.zeros_like(w0),
+                              g, bt, b)
+    z2, W2, _ = _decode_run(q[T1:], k[T1:], v[T1:], eta[T1:], W1, Wb1, g, bt, b, t0=T1)
+    np.testing.assert_array_equal(np.concatenate([z1, z2]), z)
+    np.testing.assert_array_equal(W2, W)
+    # dropping the base (restarting the mini-batch at the cut) changes the result
+    z3, _, _ = _decode_run(q[T1:], k[T1:], v[T1:], eta[T1:], W1, W1, g, bt, b, t0=0)
+    assert np.abs(z3 - z[T1:]).max() > 1e-6
