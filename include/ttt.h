@@ -59,7 +59,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 2
+#define TTT_ABI_VERSION 3
 
 typedef enum {
   TTT_OK = 0,
@@ -141,6 +141,31 @@ ttt_status ttt_linear_forward_split(const ttt_params* p,
                                     void* z, float* w_out,
                                     void* workspace, uint64_t workspace_bytes,
                                     void* hip_stream);
+
+/*
+ * One token of the TTT-Linear scan per (batch, head) unit: the streaming
+ * (decode) step.  Within a mini-batch every gradient is taken at the state
+ * the mini-batch started from (its base), so a stream carries the state W,
+ * the base W_base and the position `pos` (0 <= pos < mini_batch) of the next
+ * token in its mini-batch.  The step takes the gradient at
+ * base = (pos == 0 ? W : W_base), updates W <- W - eta_t * gradient, writes
+ * z_t = f(q_t; W) and, when pos == 0, stores base into W_base.  Calling it
+ * for t = 0, 1, ... with pos = t mod mini_batch, starting from W = W0,
+ * reproduces ttt_linear_forward (the LIT-801 record, "Key takeaways" items
+ * 1, 2 and 5).
+ *   p        T must be 1; mini_batch any b >= 1; state0_per_batch unused.
+ *   q, k, v  [B,H,d] io_dtype;  eta [B,H] fp32;  z [B,H,d] io_dtype (out).
+ *   w        [B,H,d,d] fp32, read and written (in place).
+ *   w_base   [B,H,d,d] fp32: read when pos > 0, written when pos == 0.
+ * w, w_base and z overlap nothing else (TTT_ERR_ALIAS); pos out of range is
+ * TTT_ERR_ARG.  gfx950 kernel: one 256-thread workgroup per unit, fp32
+ * arithmetic; bound by moving the state (about 48 KB per unit and token).
+ */
+ttt_status ttt_linear_decode_step(const ttt_params* p, int32_t pos,
+                                  const void* q, const void* k, const void* v,
+                                  const float* eta, float* w, float* w_base,
+                                  const float* ln_gamma, const float* ln_beta,
+                                  void* z, void* hip_stream);
 
 /*
  * TTT-MLP forward scan, hidden width `hidden` (m).

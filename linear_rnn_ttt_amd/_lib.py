@@ -16,7 +16,7 @@ TTT_F32, TTT_BF16 = 0, 1
 TTT_NO_LN, TTT_NO_RESIDUAL = 1, 2
 
 EXPORTS = ("ttt_linear_forward", "ttt_linear_split_workspace_bytes", "ttt_linear_forward_split",
-           "ttt_mlp_forward", "ttt_status_string", "ttt_abi_version")
+           "ttt_linear_decode_step", "ttt_mlp_forward", "ttt_status_string", "ttt_abi_version")
 
 
 class TTTParams(ctypes.Structure):
@@ -49,6 +49,8 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_forward_split.argtypes = ([ctypes.POINTER(TTTParams)] + [P] * 10 +
                                            [ctypes.c_uint64, P])
     L.ttt_linear_forward_split.restype = ctypes.c_int
+    L.ttt_linear_decode_step.argtypes = [ctypes.POINTER(TTTParams), ctypes.c_int32] + [P] * 10
+    L.ttt_linear_decode_step.restype = ctypes.c_int
     L.ttt_mlp_forward.argtypes = [ctypes.POINTER(TTTParams), ctypes.c_int32] + [P] * 16
     L.ttt_mlp_forward.restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int]

@@ -205,6 +205,52 @@ ttt_status ttt_linear_forward_split(const ttt_params* p, const void* q, const vo
   return linear_launch(p, a, hip_stream);
 }
 
+ttt_status ttt_linear_decode_step(const ttt_params* p, int32_t pos, const void* q,
+                                  const void* k, const void* v, const float* eta, float* w,
+                                  float* w_base, const float* ln_gamma, const float* ln_beta,
+                                  void* z, void* hip_stream) {
+  uint64_t elems = 0;
+  const ttt_status st = check_common(p, &elems);
+  if (st != TTT_OK) return st;
+  if (p->T != 1) return TTT_ERR_SHAPE;  // one token per unit
+  if (pos < 0 || pos >= p->mini_batch) return TTT_ERR_ARG;
+  const bool ln = !(p->flags & TTT_NO_LN);
+  if (!q || !k || !v || !eta || !w || !w_base || !z) return TTT_ERR_NULL;
+  if (ln && (!ln_gamma || !ln_beta)) return TTT_ERR_NULL;
+
+  const uint64_t es = p->io_dtype == TTT_BF16 ? 2 : 4;
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t dd = static_cast<uint64_t>(kHeadDim) * kHeadDim;
+  const Range rq = span(q, elems * es), rk = span(k, elems * es), rv = span(v, elems * es);
+  const Range re = span(eta, units * 4), rz = span(z, elems * es);
+  const Range rw = span(w, units * dd * 4), rb = span(w_base, units * dd * 4);
+  const Range rg = span(ln ? ln_gamma : nullptr, p->H * 256ull);
+  const Range rbe = span(ln ? ln_beta : nullptr, p->H * 256ull);
+  const Range inputs[] = {rq, rk, rv, re, rg, rbe};
+  for (const Range& r : inputs)
+    if (overlap(rz, r) || overlap(rw, r) || overlap(rb, r)) return TTT_ERR_ALIAS;
+  if (overlap(rz, rw) || overlap(rz, rb) || overlap(rw, rb)) return TTT_ERR_ALIAS;
+
+  tttk::DecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.eta = eta;
+  a.w = w;
+  a.w_base = w_base;
+  a.gamma = ln_gamma;
+  a.beta = ln_beta;
+  a.z = z;
+  a.B = p->B;
+  a.H = p->H;
+  a.pos = pos;
+  a.eps = p->ln_eps;
+  const hipError_t e = tttk::launch_linear_decode(a, p->io_dtype == TTT_BF16, ln,
+                                                  !(p->flags & TTT_NO_RESIDUAL),
+                                                  static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
+}
+
 ttt_status ttt_mlp_forward(const ttt_params* p, int32_t hidden, const void* q, const void* k,
                            const void* v, const float* eta, const float* w1_0, const float* b1_0,
                            const float* w2_0, const float* b2_0, const float* ln_gamma,

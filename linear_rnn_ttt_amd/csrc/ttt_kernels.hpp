@@ -52,10 +52,28 @@ struct MlpArgs {
   int32_t state0_per_batch;
 };
 
+// One token of the TTT-Linear scan per unit (ttt_decode.hip).
+struct DecodeArgs {
+  const void* q;          // [B,H,64] bf16 or fp32
+  const void* k;
+  const void* v;
+  const float* eta;       // [B,H]
+  float* w;               // [B,H,64,64] state, read and written
+  float* w_base;          // [B,H,64,64] mini-batch base: read (pos > 0) or written (pos == 0)
+  const float* gamma;     // [H,64] (unused without LN)
+  const float* beta;
+  void* z;                // [B,H,64]
+  int32_t B, H;
+  int32_t pos;            // position of the token in its mini-batch
+  float eps;
+};
+
 // Each returns the hipError_t of the launch.
 hipError_t launch_linear(const LinearArgs& a, bool bf16, bool ln, bool residual,
                          hipStream_t stream);
 hipError_t launch_mlp(const MlpArgs& a, bool bf16, bool ln, bool residual,
                       hipStream_t stream);
+hipError_t launch_linear_decode(const DecodeArgs& a, bool bf16, bool ln, bool residual,
+                                hipStream_t stream);
 
 }  // namespace tttk

@@ -13,7 +13,7 @@ import torch
 
 from . import _lib
 
-__all__ = ["ttt_linear_forward", "ttt_mlp_forward"]
+__all__ = ["ttt_linear_forward", "ttt_linear_decode_step", "ttt_mlp_forward"]
 
 HEAD_DIM = 64
 
@@ -134,6 +134,44 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
             rc = _lib.lib().ttt_linear_forward(*args, _stream(q, stream))
             _lib.check("ttt_linear_forward", rc)
     return z, w_out
+
+
+def ttt_linear_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                           eta: torch.Tensor, w: torch.Tensor, w_base: torch.Tensor,
+                           ln_gamma: Optional[torch.Tensor] = None,
+                           ln_beta: Optional[torch.Tensor] = None, *, pos: int,
+                           mini_batch: int = 16, eps: float = 1e-6, layer_norm: bool = True,
+                           residual: bool = True, z: Optional[torch.Tensor] = None,
+                           stream=None) -> torch.Tensor:
+    """One token per (batch, head) unit of the TTT-Linear scan (streaming
+    step); returns z [B,H,d].  w and w_base [B,H,d,d] fp32 are the stream's
+    state and mini-batch base, updated in place; pos is the token's position
+    in its mini-batch (t mod mini_batch).  See include/ttt.h."""
+    _dev_tensor("q", q)
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d] (one token per unit)")
+    B, H, d = q.shape
+    _dev_tensor("k", k, q.dtype, q.shape, device=q.device)
+    _dev_tensor("v", v, q.dtype, q.shape, device=q.device)
+    _dev_tensor("eta", eta, torch.float32, (B, H), device=q.device)
+    _dev_tensor("w", w, torch.float32, (B, H, d, d), device=q.device)
+    _dev_tensor("w_base", w_base, torch.float32, (B, H, d, d), device=q.device)
+    if layer_norm:
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d), device=q.device)
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d), device=q.device)
+    else:
+        ln_gamma = ln_beta = None
+    if z is None:
+        z = torch.empty_like(q)
+    _dev_tensor("z", z, q.dtype, q.shape, device=q.device)
+    p = _params(q.unsqueeze(2), mini_batch, eps, layer_norm, residual, True)
+    with torch.cuda.device(q.device):   # the library launches on the current device
+        rc = _lib.lib().ttt_linear_decode_step(ctypes.byref(p), int(pos), _ptr(q), _ptr(k),
+                                               _ptr(v), _ptr(eta), _ptr(w), _ptr(w_base),
+                                               _ptr(ln_gamma), _ptr(ln_beta), _ptr(z),
+                                               _stream(q, stream))
+    _lib.check("ttt_linear_decode_step", rc)
+    return z
 
 
 def ttt_mlp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 2
+    assert _lib.abi_version() == 3
     for code in range(7):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
@@ -163,3 +163,24 @@ def test_split_rejects_bad_arguments():
     # no in-place resume in the split launch (the one-workgroup launch allows it)
     p1 = _params(state0_per_batch=1)
     assert _split(p1, w_out=_addr(5)) == _lib.TTT_ERR_ALIAS                 # w_out == w0
+
+
+def _decode(p, pos=0, **ptrs):
+    names = ["q", "k", "v", "eta", "w", "wb", "g", "b", "z"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    return _lib.lib().ttt_linear_decode_step(ctypes.byref(p) if p is not None else None, pos,
+                                             *args, None)
+
+
+def test_decode_step_rejects_bad_arguments():
+    p = _params(T=1)
+    assert _decode(None) == _lib.TTT_ERR_NULL
+    assert _decode(_params(T=2)) == _lib.TTT_ERR_SHAPE                    # one token per unit
+    assert _decode(p, pos=-1) == _lib.TTT_ERR_ARG
+    assert _decode(p, pos=16) == _lib.TTT_ERR_ARG                         # pos < mini_batch
+    assert _decode(_params(T=1, d=32)) == _lib.TTT_ERR_UNSUPPORTED
+    for name in ["q", "k", "v", "eta", "w", "wb", "z", "g", "b"]:
+        assert _decode(p, **{name: None}) == _lib.TTT_ERR_NULL, name
+    assert _decode(p, wb=_addr(5)) == _lib.TTT_ERR_ALIAS                  # w_base == w
+    assert _decode(p, z=_addr(1)) == _lib.TTT_ERR_ALIAS                   # z == q
+    assert _decode(p, w=_addr(2)) == _lib.TTT_ERR_ALIAS                   # w == k
