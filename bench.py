@@ -45,8 +45,11 @@ COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 KERNEL_SOURCES = {
     "linear": ["ttt_linear.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp"],
     "mlp": ["ttt_mlp.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp"],
+    "decode": ["ttt_decode.hip", "ttt_device.hpp", "ttt_kernels.hpp"],
 }
-KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd"}
+KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k"}
+DECODE_METRIC = ("TTT-Linear streaming step tokens/s (one token per (batch, head) unit per "
+                 "launch); % HBM roofline")
 
 
 def kernel_hash(kind: str) -> str:
@@ -190,6 +193,19 @@ def cpu_baseline(w, inp, budget_s: float):
             % (len(times), dt)}
 
 
+def copy_calibration():
+    """A plain copy of known size, outside the timed region, for scaling the
+    rocprofv3 FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def run(args) -> dict:
     import torch
 
@@ -206,14 +222,7 @@ def run(args) -> dict:
     torch.cuda.synchronize()
 
     if args.copy_calibration:
-        # a plain copy of known size, outside the timed region, for scaling
-        # the rocprofv3 FETCH_SIZE / WRITE_SIZE counters
-        src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
-        dst = torch.empty_like(src)
-        torch.cuda.synchronize()
-        dst.copy_(src)
-        torch.cuda.synchronize()
-        del src, dst
+        copy_calibration()
 
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
@@ -272,6 +281,145 @@ def run(args) -> dict:
     return out
 
 
+def decode_workload(args):
+    """The streaming step's shape: the named workload's heads and head size
+    with --batch streams (default: the workload's own batch)."""
+    from linear_rnn_ttt_amd.inputs import WORKLOADS
+
+    w = WORKLOADS[args.workload]
+    if w.kind != "linear":
+        raise SystemExit("bench.py: the streaming step is TTT-Linear's (workload %s is %s)"
+                         % (w.name, w.kind))
+    if args.batch:
+        w = w.with_(B=args.batch)
+    return w
+
+
+def decode_tag(w) -> str:
+    """Profile name of a streaming-step shape: streams, heads, I/O type."""
+    return "streaming_b%dh%d_%s" % (w.B, w.H, w.io)
+
+
+def decode_bytes(w) -> int:
+    """Algorithmic bytes of one streaming step over all units: the state read
+    and written (2 d^2 fp32), the mini-batch base read or written (d^2 fp32),
+    q, k, v read and z written (4 d io elements), eta (4 B)."""
+    es = 2 if w.io == "bf16" else 4
+    return w.B * w.H * (3 * w.d * w.d * 4 + 4 * w.d * es + 4)
+
+
+def run_decode(args) -> dict:
+    """Streaming steps: B streams of H heads each take `steps` consecutive
+    tokens, one ttt_linear_decode_step launch per token (pos = t mod the
+    mini-batch size), with inputs and state resident in HBM.  The warm-up
+    tokens run eagerly; the timed tokens are captured once into a HIP graph
+    and replayed, as a generation loop launches them, so that the host's
+    per-call argument checks stay out of the per-step time.  The launch time
+    is the replay's event time over the steps (it includes the graph's
+    launch gaps, so the bandwidth it gives is a lower bound)."""
+    import torch
+
+    from linear_rnn_ttt_amd import ttt_linear_decode_step
+    from linear_rnn_ttt_amd.inputs import make_inputs
+
+    w = decode_workload(args)
+    n_tok = args.warmup + args.steps
+    inp = make_inputs(w, T=max(w.mini_batch, n_tok))
+    dev = upload(inp, w.io)
+    B, H, d = w.B, w.H, w.d
+    toks = [[dev[x][:, :, t].contiguous() for x in ("q", "k", "v", "eta")]
+            for t in range(n_tok)]
+    W = dev["w0"].expand(B, H, d, d).contiguous()
+    Wb = torch.zeros_like(W)
+    z = torch.empty((B, H, d), dtype=dev["q"].dtype, device="cuda")
+
+    def step(t):
+        q, k, v, eta = toks[t]
+        ttt_linear_decode_step(q, k, v, eta, W, Wb, dev["gamma"], dev["beta"],
+                               pos=t % w.mini_batch, mini_batch=w.mini_batch, eps=w.eps, z=z)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration()
+
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(args.warmup, n_tok):
+            step(t)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    start.record(stream)
+    graph.replay()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_launch_s = start.elapsed_time(end) / args.steps / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    byts = decode_bytes(w)
+    achieved = byts / avg_launch_s / 1e9
+    out = {
+        "metric": DECODE_METRIC,
+        "value": round(B / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": decode_tag(w), "inner_model": "TTT-Linear", "streams": B,
+                   "H": H, "d": d, "mini_batch": w.mini_batch, "io": w.io, "state": "fp32",
+                   "parallelism": "none (1 GPU)",
+                   "launch": "ttt_linear_decode_step: one 256-thread workgroup per (stream, "
+                             "head) unit, steps replayed from one HIP graph"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
+                     "traffic": read_traffic("decode", decode_tag(w)),
+                     "kernel": KERNEL_NAME["decode"],
+                     "avg_launch_ms": round(avg_launch_s * 1e3, 5),
+                     "algorithmic_bytes_per_launch": byts},
+        "outputs_finite": bool(torch.isfinite(z.float()).all().item()),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline_decode(w, inp, args.cpu_budget)
+    return out
+
+
+def cpu_baseline_decode(w, inp, budget_s: float):
+    """The oracle's fp64 streaming step (one unit at a time, one core) over
+    every unit for consecutive tokens, until the budget is spent (the drawn
+    tokens are reused in turn once the stream runs past them)."""
+    import numpy as np
+
+    import oracle
+
+    B, H, d = w.B, w.H, w.d
+    W = np.broadcast_to(inp["w0"].astype(np.float64), (B, H, d, d)).copy()
+    Wb = np.zeros_like(W)
+    t, t0 = 0, time.perf_counter()
+    n_drawn = inp["q"].shape[2]
+    while time.perf_counter() - t0 < budget_s:
+        i = t % n_drawn
+        for b in range(B):
+            for h in range(H):
+                _, W[b, h], Wb[b, h] = oracle.linear_decode_step(
+                    W[b, h], Wb[b, h], inp["q"][b, h, i], inp["k"][b, h, i], inp["v"][b, h, i],
+                    inp["eta"][b, h, i], inp["gamma"][h], inp["beta"][h], pos=t % w.mini_batch,
+                    eps=w.eps)
+        t += 1
+    dt = time.perf_counter() - t0
+    return {"value": round(B * t / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%d consecutive tokens of all %d units, %.2f s wall, fp64" % (
+                t, B * H, dt)}
+
+
 # ---------------------------------------------------------------------------
 # rocprofv3 summaries (rocprofv3 writes an SQLite database, run_results.db)
 
@@ -293,40 +441,48 @@ def _counter_per_dispatch(d, counter):
         "where counter_name = ? group by dispatch_id order by dispatch_id", (counter,)).fetchall()
 
 
-def summarize_trace(d, workload, cmd):
+def _profiled(args):
+    """(kind, profile name, algorithmic bytes, algorithmic flops) per launch
+    of the profiled kernel."""
     from linear_rnn_ttt_amd.inputs import WORKLOADS
 
-    w = WORKLOADS[workload]
+    if args.decode:
+        w = decode_workload(args)
+        return "decode", decode_tag(w), decode_bytes(w), 6 * w.d * w.d * w.B * w.H
+    w = WORKLOADS[args.workload]
+    alg = algorithmic(w)
+    return w.kind, w.name, alg["bytes"], alg["flops"]
+
+
+def summarize_trace(d, args, cmd):
+    kind, name, alg_bytes, alg_flops = _profiled(args)
     con = _db(d)
     rows = con.execute("select name, total_calls, total_duration, average, percentage from "
                        "top_kernels order by total_duration desc limit 8").fetchall()
     lines = ["# Kernel trace: %s on %s (rocprofv3 --kernel-trace --stats)" % (
-        KERNEL_NAME[w.kind], workload), "", "Command:", "", "    " + cmd, "",
-        "- kernel_source_sha256: `%s`" % kernel_hash(w.kind), "",
+        KERNEL_NAME[kind], name), "", "Command:", "", "    " + cmd, "",
+        "- kernel_source_sha256: `%s`" % kernel_hash(kind), "",
         "| kernel | calls | total (us) | average (us) | % of GPU time |", "|---|---|---|---|---|"]
     for name, calls, tot, avg, pct in rows:
         short = name if len(name) < 70 else name[:67] + "..."
         lines.append("| `%s` | %d | %.1f | %.2f | %.1f |" % (short, calls, tot, avg, pct))
     k = con.execute("select count(*), avg(duration), min(duration), max(duration) from kernels "
-                    "where name like ?", ("%" + KERNEL_NAME[w.kind] + "%",)).fetchone()
+                    "where name like ?", ("%" + KERNEL_NAME[kind] + "%",)).fetchone()
     if k and k[0]:
         avg_us = k[1] / 1e3
-        alg = algorithmic(w)
-        lines += ["", "Scan kernel: %d launches, average %.2f us (min %.2f, max %.2f)." % (
-            k[0], avg_us, k[2] / 1e3, k[3] / 1e3)]
+        lines += ["", "Kernel %s: %d launches, average %.2f us (min %.2f, max %.2f)." % (
+            KERNEL_NAME[kind], k[0], avg_us, k[2] / 1e3, k[3] / 1e3)]
         lines += ["", "Average %.2f us per launch; %d algorithmic bytes per launch "
                   "-> %.1f GB/s (%.2f%% of 8 TB/s); %.3e algorithmic flops -> %.2f TFLOP/s." % (
-                      avg_us, alg["bytes"], alg["bytes"] / avg_us / 1e3,
-                      100 * alg["bytes"] / avg_us / 1e3 / HBM_PEAK_GBS, alg["flops"],
-                      alg["flops"] / avg_us / 1e6)]
+                      avg_us, alg_bytes, alg_bytes / avg_us / 1e3,
+                      100 * alg_bytes / avg_us / 1e3 / HBM_PEAK_GBS, alg_flops,
+                      alg_flops / avg_us / 1e6)]
     return "\n".join(lines) + "\n"
 
 
-def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write):
-    from linear_rnn_ttt_amd.inputs import WORKLOADS
-
-    w = WORKLOADS[workload]
-    kname = KERNEL_NAME[w.kind]
+def summarize_pmc(fetch_dir, write_dir, args, cmd_fetch, cmd_write):
+    kind, name, alg, _ = _profiled(args)
+    kname = KERNEL_NAME[kind]
     fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
     kf = [v for n, _, v in fetch if kname in n]
@@ -339,9 +495,8 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write):
     fetch_kib = sum(kf) / len(kf)
     write_kib = sum(kw) / len(kw)
     traffic = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
-    alg = algorithmic(w)["bytes"]
     lines = [
-        "# HBM traffic of `%s` on %s (rocprofv3 --pmc)" % (kname, workload),
+        "# HBM traffic of `%s` on %s (rocprofv3 --pmc)" % (kname, name),
         "",
         "Two counter runs of the benchmark (kernel launches plus one plain 1 GiB",
         "device-to-device copy whose counters scale the kernel's):",
@@ -349,7 +504,7 @@ def summarize_pmc(fetch_dir, write_dir, workload, cmd_fetch, cmd_write):
         "    " + cmd_fetch,
         "    " + cmd_write,
         "",
-        "- kernel_source_sha256: `%s`" % kernel_hash(w.kind),
+        "- kernel_source_sha256: `%s`" % kernel_hash(kind),
         "- dispatches_measured: %d (FETCH_SIZE), %d (WRITE_SIZE)" % (len(kf), len(kw)),
         "- fetch_kib_per_dispatch: %.1f" % fetch_kib,
         "- write_kib_per_dispatch: %.1f" % write_kib,
@@ -373,6 +528,10 @@ def main(argv=None):
                     help="seconds of oracle wall time for the CPU baseline sample")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run one 1 GiB copy before the timed region (counter scaling)")
+    ap.add_argument("--decode", action="store_true",
+                    help="time the TTT-Linear streaming step instead of the scan")
+    ap.add_argument("--batch", type=int, default=0,
+                    help="streams for --decode (default: the workload's batch)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-commands", nargs=2, default=["", ""])
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
@@ -380,11 +539,11 @@ def main(argv=None):
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
-        sys.stdout.write(summarize_trace(args.summarize_trace, args.workload, args.trace_command))
+        sys.stdout.write(summarize_trace(args.summarize_trace, args, args.trace_command))
         return 0
     if args.summarize_pmc:
         sys.stdout.write(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
-                                       args.workload, *args.pmc_commands))
+                                       args, *args.pmc_commands))
         return 0
     if args.gpus != 1:
         print("bench.py: this build runs on exactly one GPU (the scan shards over "
@@ -394,7 +553,7 @@ def main(argv=None):
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
-    out = run(args)
+    out = run_decode(args) if args.decode else run(args)
     print(json.dumps(out), flush=True)
     return 0
 

@@ -103,3 +103,84 @@ def test_decode_pos0_records_the_base_and_pos_checked():
                                dev["eta"][:, :, 0].contiguous(), W, Wb, dev["gamma"],
                                dev["beta"], pos=16, mini_batch=16)
     assert e.value.code == _lib.TTT_ERR_ARG
+
+
+def _tokens(dev, T):
+    return [[dev[x][:, :, t].contiguous() for x in ("q", "k", "v", "eta")] for t in range(T)]
+
+
+def test_decode_graph_replays_match_eager():
+    """Two mini-batches of steps captured into one HIP graph, replayed three
+    times from the same starting state (reset by eager copies between the
+    replays): every replay equals the eager steps bit for bit."""
+    inp = make_inputs(BF, B=2, H=3, T=40)
+    dev = {x: to_dev(inp[x], "bf16" if x in "qkv" else None) for x in inp}
+    toks = _tokens(dev, 40)
+    W0 = to_dev(np.broadcast_to(inp["w0"], (2, 3, 64, 64)).copy())
+    W, Wb = W0.clone(), torch.zeros_like(W0)
+    zs = torch.empty((40, 2, 3, 64), dtype=torch.bfloat16, device="cuda")
+
+    def steps():
+        for t in range(40):
+            ttt_linear_decode_step(*toks[t][:4], W, Wb, dev["gamma"], dev["beta"], pos=t % 16,
+                                   z=zs[t])
+
+    steps()
+    torch.cuda.synchronize()
+    z_ref, W_ref, Wb_ref = zs.clone(), W.clone(), Wb.clone()
+    W.copy_(W0)
+    Wb.zero_()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        steps()
+    torch.cuda.synchronize()
+    for r in range(3):
+        W.copy_(W0)
+        Wb.zero_()
+        zs.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(zs, z_ref) and torch.equal(W, W_ref) and torch.equal(Wb, Wb_ref), r
+
+
+@pytest.mark.parametrize("streams", [4, 256])
+def test_decode_bench_shape_sampled_units(streams):
+    """The streaming step at the 1.3B layer shape (H = 32) with 4 and 256
+    streams, 20 tokens (a mini-batch and a ragged tail), launched from a
+    graph as the benchmark does: sampled units against the oracle's step."""
+    wl = WORKLOADS["linear_1p3b_b4h32_t8k"].with_(B=streams)
+    T = 20
+    inp = make_inputs(wl, T=T)
+    dev = {x: to_dev(inp[x], "bf16" if x in "qkv" else None) for x in inp}
+    toks = _tokens(dev, T)
+    W = to_dev(np.broadcast_to(inp["w0"], (streams, 32, 64, 64)).copy())
+    Wb = torch.zeros_like(W)
+    zs = torch.empty((T, streams, 32, 64), dtype=torch.bfloat16, device="cuda")
+    ttt_linear_decode_step(*toks[0], W, Wb, dev["gamma"], dev["beta"], pos=0, z=zs[0])
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for t in range(1, T):
+            ttt_linear_decode_step(*toks[t], W, Wb, dev["gamma"], dev["beta"], pos=t % 16,
+                                   z=zs[t])
+    graph.replay()
+    torch.cuda.synchronize()
+    z = from_dev(zs)
+    Wg = from_dev(W)
+    rng = np.random.default_rng(7)
+    units = [(0, 0), (streams - 1, 31)] + [tuple(u) for u in
+                                          zip(rng.integers(0, streams, 6), rng.integers(0, 32, 6))]
+    worst = 0.0
+    for b, h in units:
+        Wr, Wbr = inp["w0"][h].astype(np.float64), None
+        zr = np.empty((T, 64))
+        for t in range(T):
+            zr[t], Wr, Wbr = oracle.linear_decode_step(
+                Wr, Wbr, inp["q"][b, h, t], inp["k"][b, h, t], inp["v"][b, h, t],
+                inp["eta"][b, h, t], inp["gamma"][h], inp["beta"][h], pos=t % 16, eps=wl.eps)
+        ez = z_err(z[:, b, h][None, None], zr[None, None])
+        ew = state_err(Wg[b, h][None, None], Wr[None, None])
+        worst = max(worst, ez, ew)
+        assert ez <= TOL["bf16"] and ew <= TOL["bf16"], (b, h, ez, ew)
+    print("streams=%d: %d sampled units, worst err %.3e" % (streams, len(units), worst),
+          flush=True)
