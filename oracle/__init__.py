@@ -19,6 +19,10 @@ linear_apply / mlp_apply: the inner model f for one token.
 linear_decode_step(W, W_base, q, k, v, eta, gamma, beta, pos=...) -> (z, W, W_base):
     one token of the TTT-Linear scan for one unit, the streaming form.
 build(): compile ``libttt_oracle.so`` with gcc.
+
+The backward pass of the TTT-Linear scan (its vector-Jacobian product) is in
+``oracle/backward.py`` (fp64 torch autograd through the scan written out
+token by token).
 """
 from __future__ import annotations
 
