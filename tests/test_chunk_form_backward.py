@@ -1,0 +1,132 @@
+"""The chunked adjoint equations the HIP backward kernel evaluates, written in
+fp64 numpy and checked against the backward oracle (autograd through the
+token-by-token scan).
+
+Forward, per mini-batch with base W and rows k_s, v_s, q_i, eta_s (the
+dmarx.github.io record LIT-801, "Key takeaways" items 1, 2 and 5):
+
+    h_s = k_s W,  x_s = LN-normalised h_s (1/sigma_s = rho_s),
+    t_s = v_s - beta - res k_s,   a_s = 2 gamma (gamma x_s - t_s),
+    g_s = rho_s (a_s - mean(a_s) - x_s mean(a_s x_s))        (dl/dh at the base)
+    W_i = W - sum_{s<=i} eta_s k_s^T g_s,   o_i = q_i W_i
+        = Q W - (tril(Q K^T) * eta) G                         (row i)
+    z_i = res q_i + gamma LN(o_i) + beta;   next base = W_b.
+
+Backward with A = the adjoint of the next base (dW_T for the last one):
+
+    DO    = LN backward of dz (dgamma += dz x_o, dbeta += dz)
+    dQ    = res dZ + DO W^T - (tril(DO G^T) * eta) K
+    KA_s  = k_s A + sum_{i>=s} (q_i . k_s) do_i        (= k_s A_s)
+    GA_s  = g_s A^T + sum_{i>=s} (do_i . g_s) q_i      (= g_s A_s^T)
+            where A_s = A + sum_{i>=s} q_i^T do_i is the adjoint of the
+            update term eta_s k_s^T g_s (with a minus sign)
+    deta_s = -KA_s . g_s,   dg_s = -eta_s KA_s
+    g backward (u = dg_s):
+      drho = u . (a - mean a - x mean(a x))
+      da   = rho (u - mean u - x mean(u x))
+      dx   = -rho (mean(a x) u + a mean(u x)) + 2 gamma^2 da
+      dt   = -2 gamma da,   dgamma += 2 (2 gamma x - t) da
+      dh   = rho (dx - mean dx - x mean(dx x)) - drho rho^2 x / d
+      (no LN: g = 2 (h - t), dh = 2u, dt = -2u)
+    dv_s = dt_s,  dbeta -= dt_s,  dK = DH W^T - eta GA - res dT
+    A    <- A + Q^T DO + K^T DH       (the adjoint of this mini-batch's base)
+    dW0  = A after the first mini-batch.
+"""
+import numpy as np
+import pytest
+
+from oracle.backward import linear_backward
+
+
+def _grad_rows(W, K, V, gamma, beta, ln, res, eps):
+    d = W.shape[0]
+    H = K @ W
+    if not ln:
+        t = V - (K if res else 0)
+        return 2 * (H - t), None
+    mu = H.mean(-1, keepdims=True)
+    rho = 1 / np.sqrt(((H - mu) ** 2).mean(-1, keepdims=True) + eps)
+    x = (H - mu) * rho
+    t = V - beta - (K if res else 0)
+    a = 2 * gamma * (gamma * x - t)
+    ma, mx = a.mean(-1, keepdims=True), (a * x).mean(-1, keepdims=True)
+    g = rho * (a - ma - x * mx)
+    return g, (x, rho, t, a, ma, mx)
+
+
+def chunk_backward(q, k, v, eta, W0, gamma, beta, dz, dWT, b, ln, res, eps):
+    T, d = q.shape
+    bases, W = [], W0.copy()
+    for c0 in range(0, T, b):
+        bases.append(W.copy())
+        sl = slice(c0, min(T, c0 + b))
+        G, _ = _grad_rows(W, k[sl], v[sl], gamma, beta, ln, res, eps)
+        W = W - k[sl].T @ (eta[sl, None] * G)
+    A = np.zeros((d, d)) if dWT is None else dWT.copy()
+    dq, dk, dv = (np.zeros((T, d)) for _ in range(3))
+    deta = np.zeros(T)
+    dgam, dbet = np.zeros(d), np.zeros(d)
+    for c, c0 in reversed(list(enumerate(range(0, T, b)))):
+        W = bases[c]
+        sl = slice(c0, min(T, c0 + b))
+        Q, K, V, DZ, E = q[sl], k[sl], v[sl], dz[sl], eta[sl]
+        G, st = _grad_rows(W, K, V, gamma, beta, ln, res, eps)
+        M1 = np.tril(Q @ K.T) * E[None, :]
+        O = Q @ W - M1 @ G
+        if ln:
+            mu = O.mean(-1, keepdims=True)
+            rho_o = 1 / np.sqrt(((O - mu) ** 2).mean(-1, keepdims=True) + eps)
+            xo = (O - mu) * rho_o
+            dgam += (DZ * xo).sum(0)
+            dbet += DZ.sum(0)
+            dxo = gamma * DZ
+            DO = rho_o * (dxo - dxo.mean(-1, keepdims=True)
+                          - xo * (dxo * xo).mean(-1, keepdims=True))
+        else:
+            DO = DZ
+        dq[sl] = (DZ if res else 0) + DO @ W.T - (np.tril(DO @ G.T) * E[None, :]) @ K
+        KA = K @ A + np.triu(K @ Q.T) @ DO
+        GA = G @ A.T + np.triu(G @ DO.T) @ Q
+        deta[sl] = -(KA * G).sum(-1)
+        u = -E[:, None] * KA
+        if ln:
+            x, rho, t, a, ma, mx = st
+            drho = (u * (a - ma - x * mx)).sum(-1, keepdims=True)
+            mux = (u * x).mean(-1, keepdims=True)
+            da = rho * (u - u.mean(-1, keepdims=True) - x * mux)
+            dx = -rho * (mx * u + a * mux) + 2 * gamma ** 2 * da
+            dt = -2 * gamma * da
+            dgam += (2 * (2 * gamma * x - t) * da).sum(0)
+            dH = (rho * (dx - dx.mean(-1, keepdims=True) - x * (dx * x).mean(-1, keepdims=True))
+                  - drho * rho ** 2 * x / d)
+            dbet -= dt.sum(0)
+        else:
+            dH, dt = 2 * u, -2 * u
+        dv[sl] = dt
+        dk[sl] = dH @ W.T - E[:, None] * GA - (dt if res else 0)
+        A = A + Q.T @ DO + K.T @ dH
+    return dict(dq=dq, dk=dk, dv=dv, deta=deta, dw0=A, dgamma=dgam, dbeta=dbet)
+
+
+@pytest.mark.parametrize("ln,res", [(True, True), (True, False), (False, True),
+                                    (False, False)])
+@pytest.mark.parametrize("b,T,final", [(16, 50, True), (4, 23, False), (16, 16, True),
+                                       (16, 7, False)])
+def test_chunk_adjoint_equals_the_oracle(ln, res, b, T, final):
+    rng = np.random.default_rng(300 + b + T + 2 * ln + res)
+    H, d = 1, 16
+    q, k, v = (rng.standard_normal((1, H, T, d)) / np.sqrt(d) for _ in range(3))
+    eta = 1 / (1 + np.exp(-rng.standard_normal((1, H, T)))) / d * 4
+    w0 = 0.3 * rng.standard_normal((H, d, d))
+    gamma = 1 + 0.3 * rng.standard_normal((H, d))
+    beta = 0.3 * rng.standard_normal((H, d))
+    dz = rng.standard_normal((1, H, T, d))
+    dwT = rng.standard_normal((1, H, d, d)) if final else None
+    want = linear_backward(q, k, v, eta, w0, gamma, beta, dz, dwT, mini_batch=b,
+                           layer_norm=ln, residual=res, eps=1e-6)
+    got = chunk_backward(q[0, 0], k[0, 0], v[0, 0], eta[0, 0], w0[0], gamma[0], beta[0],
+                         dz[0, 0], None if dwT is None else dwT[0, 0], b, ln, res, 1e-6)
+    for name in want:
+        w = want[name].reshape(got[name].shape)
+        err = np.abs(got[name] - w).max() / max(np.abs(w).max(), 1e-30)
+        assert err <= 1e-11 or (not ln and name in ("dgamma", "dbeta")), (name, err)
