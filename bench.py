@@ -46,8 +46,12 @@ KERNEL_SOURCES = {
     "linear": ["ttt_linear.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp"],
     "mlp": ["ttt_mlp.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp"],
     "decode": ["ttt_decode.hip", "ttt_device.hpp", "ttt_kernels.hpp"],
+    "backward": ["ttt_backward.hip", "ttt_backward.hpp", "ttt_device.hpp"],
 }
-KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k"}
+KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k",
+               "backward": "ttt_linear_bwd_k"}
+BACKWARD_METRIC = "TTT-Linear backward tokens/s at 1.3B shape T=8k; % fp32 ALU roofline"
+FP32_VECTOR_PEAK_TFS = 157.3   # MI355X fp32 vector (packed); non-packed FMA issue is half
 DECODE_METRIC = ("TTT-Linear streaming step tokens/s (one token per (batch, head) unit per "
                  "launch); % HBM roofline")
 
@@ -420,6 +424,134 @@ def cpu_baseline_decode(w, inp, budget_s: float):
                 t, B * H, dt)}
 
 
+def backward_alg(w) -> dict:
+    """What the backward itself must move and compute per launch.
+
+    Bytes per token-head: q, k, v and dz read and dq, dk, dv written (7 d io
+    elements), eta read and deta written (8 B); per head W0, gamma, beta read
+    and their gradients written.  The mini-batch bases the kernel stores and
+    reloads (2 x 16 KB per 16 tokens and unit) are its own choice and are not
+    counted.  Flops per token-head: 10 d x d matrix-vector products, 2 flops
+    per multiply-add -- the forward replay of the bases (k W and the update)
+    and the eight products of the chunked adjoint (k W, q W, dO W^T, k A,
+    g A^T, dh W^T, and the rank-1 updates q^T dO and k^T dh of A)."""
+    es = 2 if w.io == "bf16" else 4
+    th = w.B * w.H * w.T
+    d = w.d
+    per_th = 7 * d * es + 8
+    per_head = 2 * (d * d + 2 * d) * 4
+    return {"bytes": th * per_th + w.H * per_head, "bytes_per_token_head": per_th,
+            "flops": th * 20 * d * d, "flops_per_token_head": 20 * d * d,
+            "bases_bytes": 2 * w.B * w.H * ((w.T + 15) // 16) * d * d * 4}
+
+
+def run_backward(args) -> dict:
+    """One call of ttt_linear_backward over the whole workload per step
+    (cotangent dz seeded N(0, 1) in the io dtype, no cotangent on the final
+    state, as in a language model), inputs and a preallocated workspace
+    resident in HBM.  The launch time is the event time of the call on its
+    stream (the scan kernel and the small batch-sum kernel)."""
+    import numpy as np
+    import torch
+
+    from linear_rnn_ttt_amd import _lib, ttt_linear_backward
+    from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs
+
+    w = WORKLOADS[args.workload]
+    if w.kind != "linear":
+        raise SystemExit("bench.py: the backward is TTT-Linear's (workload %s is %s)"
+                         % (w.name, w.kind))
+    inp = make_inputs(w)
+    dev = upload(inp, w.io)
+    dz = np.random.default_rng(w.seed + 1000).standard_normal(inp["q"].shape).astype(np.float32)
+    dz_dev = torch.from_numpy(dz).cuda().to(dev["q"].dtype)
+    p = _lib.TTTParams(w.B, w.H, w.T, w.d, w.mini_batch,
+                       _lib.TTT_BF16 if w.io == "bf16" else _lib.TTT_F32, 0, w.eps, 0)
+    import ctypes
+    ws = torch.empty(int(_lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p))),
+                     dtype=torch.uint8, device="cuda")
+    args_ = (dev["q"], dev["k"], dev["v"], dev["eta"], dev["w0"], dev["gamma"], dev["beta"],
+             dz_dev)
+
+    def step():
+        return ttt_linear_backward(*args_, mini_batch=w.mini_batch, eps=w.eps, workspace=ws)
+
+    for _ in range(args.warmup):
+        out = step()
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_, e_ in ev:
+        s_.record(stream)
+        out = step()
+        e_.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_launch_s = sum(s_.elapsed_time(e_) for s_, e_ in ev) / len(ev) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    alg = backward_alg(w)
+    tflops = alg["flops"] / avg_launch_s / 1e12
+    res = {
+        "metric": BACKWARD_METRIC,
+        "value": round(w.tokens / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name + "_backward", "inner_model": "TTT-Linear", "B": w.B,
+                   "H": w.H, "T": w.T, "d": w.d, "mini_batch": w.mini_batch, "io": w.io,
+                   "parallelism": "none (1 GPU)",
+                   "launch": "ttt_linear_backward: one 256-thread workgroup per (batch, head) "
+                             "unit, fp32 VALU arithmetic, mini-batch bases in a workspace"},
+        "roofline": {"bound": "alu", "achieved": round(tflops, 3),
+                     "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP32_VECTOR_PEAK_TFS, 5),
+                     "traffic": read_traffic("backward", w.name),
+                     "kernel": KERNEL_NAME["backward"],
+                     "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                     "algorithmic_flops_per_launch": alg["flops"],
+                     "algorithmic_bytes_per_launch": alg["bytes"],
+                     "hbm_gbs_algorithmic": round(alg["bytes"] / avg_launch_s / 1e9, 1)},
+        "outputs_finite": bool(all(torch.isfinite(t.float()).all().item() for t in out[:4])),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_backward(w, inp, dz, args.cpu_budget)
+    return res
+
+
+def cpu_baseline_backward(w, inp, dz, budget_s: float):
+    """The fp64 backward oracle on one unit (batch 0, head 0) for the first
+    T_s tokens, T_s doubled from 256 until a run takes a quarter of the
+    budget; scaled to the metric's unit (one unit is 1/H of a token)."""
+    from oracle.backward import linear_backward
+
+    T_s, dt = 128, 0.0
+    while dt < budget_s / 4 and T_s < w.T:
+        T_s *= 2
+        sl = (slice(0, 1), slice(0, 1), slice(0, T_s))
+        t0 = time.perf_counter()
+        linear_backward(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["eta"][sl],
+                        inp["w0"][:1], inp["gamma"][:1], inp["beta"][:1], dz[sl],
+                        mini_batch=w.mini_batch, eps=w.eps)
+        dt = time.perf_counter() - t0
+    import torch
+    return {"value": round(T_s / w.H / dt, 2), "unit": "tokens/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": "unit (0, 0), first %d tokens, %.2f s wall, fp64 torch autograd" % (
+                T_s, dt)}
+
+
 # ---------------------------------------------------------------------------
 # rocprofv3 summaries (rocprofv3 writes an SQLite database, run_results.db)
 
@@ -449,6 +581,10 @@ def _profiled(args):
     if args.decode:
         w = decode_workload(args)
         return "decode", decode_tag(w), decode_bytes(w), 6 * w.d * w.d * w.B * w.H
+    if args.backward:
+        w = WORKLOADS[args.workload]
+        alg = backward_alg(w)
+        return "backward", w.name, alg["bytes"], alg["flops"]
     w = WORKLOADS[args.workload]
     alg = algorithmic(w)
     return w.kind, w.name, alg["bytes"], alg["flops"]
@@ -530,6 +666,8 @@ def main(argv=None):
                     help="run one 1 GiB copy before the timed region (counter scaling)")
     ap.add_argument("--decode", action="store_true",
                     help="time the TTT-Linear streaming step instead of the scan")
+    ap.add_argument("--backward", action="store_true",
+                    help="time the TTT-Linear backward pass instead of the forward scan")
     ap.add_argument("--batch", type=int, default=0,
                     help="streams for --decode (default: the workload's batch)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -553,7 +691,8 @@ def main(argv=None):
     if args.steps < 1 or args.warmup < 0:
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
-    out = run_decode(args) if args.decode else run(args)
+    out = (run_decode(args) if args.decode else
+           run_backward(args) if args.backward else run(args))
     print(json.dumps(out), flush=True)
     return 0
 

@@ -1,5 +1,6 @@
 /*
- * ttt.h -- C ABI of the MI355X (gfx950) TTT-layer forward scan.
+ * ttt.h -- C ABI of the MI355X (gfx950) TTT-layer forward scan, its
+ * streaming (decode) step and the TTT-Linear backward pass.
  *
  * The method (arXiv 2407.04620, "Learning to (Learn at Test Time): RNNs with
  * Expressive Hidden States"; summarised in the dmarx.github.io record
@@ -59,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 3
+#define TTT_ABI_VERSION 4
 
 typedef enum {
   TTT_OK = 0,
@@ -166,6 +167,54 @@ ttt_status ttt_linear_decode_step(const ttt_params* p, int32_t pos,
                                   const float* eta, float* w, float* w_base,
                                   const float* ln_gamma, const float* ln_beta,
                                   void* z, void* hip_stream);
+
+/*
+ * Bytes of device workspace that ttt_linear_backward needs for these
+ * parameters: 16 KB per unit and 16-token mini-batch (the base of every
+ * mini-batch), plus 16 KB + 512 bytes per unit, rounded up to 256 bytes
+ * (0 if p fails the common checks).  About 1 GB for B = 4, H = 32,
+ * T = 8192.
+ */
+uint64_t ttt_linear_backward_workspace_bytes(const ttt_params* p);
+
+/*
+ * Backward pass of the TTT-Linear forward scan: the vector-Jacobian product
+ * that training needs, since the outer loop trains the projections behind
+ * q, k and v, the initial state and the per-token learning rate (the
+ * LIT-801 record, "Key takeaways" item 2), and the LN parameters of f.
+ * For cotangents dz (and dw_final on the final state) it writes the
+ * gradients of  L = sum_t <dz_t, z_t> + <dw_final, W_T>  with respect to
+ * every input of ttt_linear_forward (same p, same inputs).
+ *   dz        [B,H,T,d] io_dtype.
+ *   dw_final  [B,H,d,d] fp32, or NULL for zero.
+ *   dq, dk, dv  [B,H,T,d] io_dtype (out; rounded once from fp32).
+ *   deta      [B,H,T] fp32 (out).
+ *   dw0       w0's shape, fp32 (out): summed over the batch when w0 is
+ *             shared ([H,d,d]).
+ *   dln_gamma, dln_beta  [H,d] fp32 (out), summed over batch and tokens;
+ *             required with LN; without LN NULL, or written with zeros.
+ *   workspace  device memory, 256-byte aligned, at least
+ *             ttt_linear_backward_workspace_bytes(p) bytes, owned by the
+ *             caller; no initialisation needed; scratch after the call; one
+ *             call at a time.
+ * Outputs and the workspace overlap no input and no other output
+ * (TTT_ERR_ALIAS).  Supported: d = 64, mini_batch = 16 (else
+ * TTT_ERR_UNSUPPORTED), both io dtypes, any flags.
+ * gfx950: two kernels on hip_stream.  One 256-thread workgroup per unit
+ * first replays the forward recurrence and stores every mini-batch base in
+ * the workspace, then walks the mini-batches in reverse (fp32 arithmetic);
+ * a second kernel sums dw0 (shared w0), dln_gamma and dln_beta over the
+ * batch in a fixed order.  Results are deterministic.
+ */
+ttt_status ttt_linear_backward(const ttt_params* p,
+                               const void* q, const void* k, const void* v,
+                               const float* eta, const float* w0,
+                               const float* ln_gamma, const float* ln_beta,
+                               const void* dz, const float* dw_final,
+                               void* dq, void* dk, void* dv, float* deta,
+                               float* dw0, float* dln_gamma, float* dln_beta,
+                               void* workspace, uint64_t workspace_bytes,
+                               void* hip_stream);
 
 /*
  * TTT-MLP forward scan, hidden width `hidden` (m).

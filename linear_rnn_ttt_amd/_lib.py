@@ -16,7 +16,8 @@ TTT_F32, TTT_BF16 = 0, 1
 TTT_NO_LN, TTT_NO_RESIDUAL = 1, 2
 
 EXPORTS = ("ttt_linear_forward", "ttt_linear_split_workspace_bytes", "ttt_linear_forward_split",
-           "ttt_linear_decode_step", "ttt_mlp_forward", "ttt_status_string", "ttt_abi_version")
+           "ttt_linear_decode_step", "ttt_linear_backward_workspace_bytes", "ttt_linear_backward",
+           "ttt_mlp_forward", "ttt_status_string", "ttt_abi_version")
 
 
 class TTTParams(ctypes.Structure):
@@ -51,6 +52,11 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_forward_split.restype = ctypes.c_int
     L.ttt_linear_decode_step.argtypes = [ctypes.POINTER(TTTParams), ctypes.c_int32] + [P] * 10
     L.ttt_linear_decode_step.restype = ctypes.c_int
+    L.ttt_linear_backward_workspace_bytes.argtypes = [ctypes.POINTER(TTTParams)]
+    L.ttt_linear_backward_workspace_bytes.restype = ctypes.c_uint64
+    L.ttt_linear_backward.argtypes = ([ctypes.POINTER(TTTParams)] + [P] * 17 +
+                                      [ctypes.c_uint64, P])
+    L.ttt_linear_backward.restype = ctypes.c_int
     L.ttt_mlp_forward.argtypes = [ctypes.POINTER(TTTParams), ctypes.c_int32] + [P] * 16
     L.ttt_mlp_forward.restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int]

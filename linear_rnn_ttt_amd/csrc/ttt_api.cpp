@@ -9,6 +9,7 @@
 #include <cmath>
 #include <cstdint>
 
+#include "ttt_backward.hpp"
 #include "ttt_kernels.hpp"
 
 namespace {
@@ -130,6 +131,24 @@ ttt_status linear_args(const ttt_params* p, const void* q, const void* k, const 
   return TTT_OK;
 }
 
+// Workspace of the backward scan: every mini-batch base of every unit
+// (16 KB per 16-token tile and unit), the per-unit dW0 (16 KB per unit) and
+// the per-unit LN parameter gradients (512 B per unit).
+struct BackwardLayout {
+  uint64_t dw0_offset, dln_offset, total;
+};
+
+BackwardLayout backward_layout(const ttt_params* p) {
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t tiles = (static_cast<uint64_t>(p->T) + 15) / 16;
+  const uint64_t dd4 = static_cast<uint64_t>(kHeadDim) * kHeadDim * 4;
+  BackwardLayout ly;
+  ly.dw0_offset = units * tiles * dd4;
+  ly.dln_offset = ly.dw0_offset + units * dd4;
+  ly.total = (ly.dln_offset + units * 2 * kHeadDim * 4 + 255) / 256 * 256;
+  return ly;
+}
+
 ttt_status linear_launch(const ttt_params* p, const tttk::LinearArgs& a, void* hip_stream) {
   const hipError_t e = tttk::launch_linear(a, p->io_dtype == TTT_BF16, !(p->flags & TTT_NO_LN),
                                            !(p->flags & TTT_NO_RESIDUAL),
@@ -248,6 +267,84 @@ ttt_status ttt_linear_decode_step(const ttt_params* p, int32_t pos, const void* 
   const hipError_t e = tttk::launch_linear_decode(a, p->io_dtype == TTT_BF16, ln,
                                                   !(p->flags & TTT_NO_RESIDUAL),
                                                   static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
+}
+
+uint64_t ttt_linear_backward_workspace_bytes(const ttt_params* p) {
+  uint64_t elems = 0;
+  if (check_common(p, &elems) != TTT_OK) return 0;
+  return backward_layout(p).total;
+}
+
+ttt_status ttt_linear_backward(const ttt_params* p, const void* q, const void* k, const void* v,
+                               const float* eta, const float* w0, const float* ln_gamma,
+                               const float* ln_beta, const void* dz, const float* dw_final,
+                               void* dq, void* dk, void* dv, float* deta, float* dw0,
+                               float* dln_gamma, float* dln_beta, void* workspace,
+                               uint64_t workspace_bytes, void* hip_stream) {
+  uint64_t elems = 0;
+  const ttt_status st = check_common(p, &elems);
+  if (st != TTT_OK) return st;
+  const bool ln = !(p->flags & TTT_NO_LN);
+  if (!q || !k || !v || !eta || !w0 || !dz || !dq || !dk || !dv || !deta || !dw0 || !workspace)
+    return TTT_ERR_NULL;
+  if (ln && (!ln_gamma || !ln_beta || !dln_gamma || !dln_beta)) return TTT_ERR_NULL;
+  if ((dln_gamma == nullptr) != (dln_beta == nullptr)) return TTT_ERR_NULL;
+  if (p->mini_batch != 16) return TTT_ERR_UNSUPPORTED;
+  const BackwardLayout ly = backward_layout(p);
+  if (workspace_bytes < ly.total) return TTT_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TTT_ERR_ARG;
+
+  const uint64_t es = p->io_dtype == TTT_BF16 ? 2 : 4;
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t dd = static_cast<uint64_t>(kHeadDim) * kHeadDim;
+  const uint64_t w0_bytes = (p->state0_per_batch ? units : p->H) * dd * 4;
+  const Range inputs[] = {
+      span(q, elems * es), span(k, elems * es), span(v, elems * es),
+      span(eta, units * p->T * 4), span(w0, w0_bytes),
+      span(ln ? ln_gamma : nullptr, p->H * 256ull), span(ln ? ln_beta : nullptr, p->H * 256ull),
+      span(dz, elems * es), span(dw_final, units * dd * 4)};
+  const Range outputs[] = {
+      span(dq, elems * es), span(dk, elems * es), span(dv, elems * es),
+      span(deta, units * p->T * 4), span(dw0, w0_bytes), span(dln_gamma, p->H * 256ull),
+      span(dln_beta, p->H * 256ull), span(workspace, workspace_bytes)};
+  const int n_out = sizeof(outputs) / sizeof(outputs[0]);
+  for (int i = 0; i < n_out; ++i) {
+    for (const Range& r : inputs)
+      if (overlap(outputs[i], r)) return TTT_ERR_ALIAS;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outputs[i], outputs[j])) return TTT_ERR_ALIAS;
+  }
+
+  tttk::BackwardArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.eta = eta;
+  a.w0 = w0;
+  a.gamma = ln_gamma;
+  a.beta = ln_beta;
+  a.dz = dz;
+  a.dw_final = dw_final;
+  a.dq = dq;
+  a.dk = dk;
+  a.dv = dv;
+  a.deta = deta;
+  a.dw0 = dw0;
+  a.dgamma = dln_gamma;
+  a.dbeta = dln_beta;
+  char* base = static_cast<char*>(workspace);
+  a.ws_base = reinterpret_cast<float*>(base);
+  a.ws_dw0 = reinterpret_cast<float*>(base + ly.dw0_offset);
+  a.ws_dln = reinterpret_cast<float*>(base + ly.dln_offset);
+  a.B = p->B;
+  a.H = p->H;
+  a.T = p->T;
+  a.eps = p->ln_eps;
+  a.state0_per_batch = p->state0_per_batch;
+  const hipError_t e = tttk::launch_linear_backward(a, p->io_dtype == TTT_BF16, ln,
+                                                    !(p->flags & TTT_NO_RESIDUAL),
+                                                    static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
 }
 

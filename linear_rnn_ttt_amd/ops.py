@@ -13,7 +13,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["ttt_linear_forward", "ttt_linear_decode_step", "ttt_mlp_forward"]
+__all__ = ["ttt_linear_forward", "ttt_linear_decode_step", "ttt_linear_backward",
+           "ttt_mlp_forward"]
 
 HEAD_DIM = 64
 
@@ -172,6 +173,57 @@ def ttt_linear_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                                _stream(q, stream))
     _lib.check("ttt_linear_decode_step", rc)
     return z
+
+
+def ttt_linear_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,
+                        w0: torch.Tensor, ln_gamma: Optional[torch.Tensor],
+                        ln_beta: Optional[torch.Tensor], dz: torch.Tensor,
+                        dw_final: Optional[torch.Tensor] = None, *, mini_batch: int = 16,
+                        eps: float = 1e-6, layer_norm: bool = True, residual: bool = True,
+                        state0_per_batch: bool = False, workspace: Optional[torch.Tensor] = None,
+                        stream=None) -> Tuple[torch.Tensor, ...]:
+    """Backward pass of the TTT-Linear scan for cotangents dz [B,H,T,d] (and
+    dw_final [B,H,d,d] on the final state, or None); same inputs and options
+    as ttt_linear_forward.  Returns (dq, dk, dv, deta, dw0, dln_gamma,
+    dln_beta); dw0 has w0's shape (summed over the batch when w0 is shared),
+    the LN gradients are [H,d] (zeros without LN).  workspace: a uint8 GPU
+    tensor of at least ttt_linear_backward_workspace_bytes bytes to use
+    instead of a fresh one.  See include/ttt.h."""
+    _dev_tensor("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("dz", dz)):
+        _dev_tensor(name, t, q.dtype, q.shape, device=dev)
+    _dev_tensor("eta", eta, torch.float32, (B, H, T), device=dev)
+    w0_shape = (B, H, d, d) if state0_per_batch else (H, d, d)
+    _dev_tensor("w0", w0, torch.float32, w0_shape, device=dev)
+    if layer_norm:
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d), device=dev)
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d), device=dev)
+    else:
+        ln_gamma = ln_beta = None
+    if dw_final is not None:
+        _dev_tensor("dw_final", dw_final, torch.float32, (B, H, d, d), device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    deta = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dw0 = torch.empty(w0_shape, dtype=torch.float32, device=dev)
+    dgamma = torch.empty((H, d), dtype=torch.float32, device=dev)
+    dbeta = torch.empty((H, d), dtype=torch.float32, device=dev)
+    p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
+    need = int(_lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, torch.uint8, device=dev)
+    with torch.cuda.device(dev):   # the library launches on the current device
+        rc = _lib.lib().ttt_linear_backward(
+            ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), _ptr(ln_gamma),
+            _ptr(ln_beta), _ptr(dz), _ptr(dw_final), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta),
+            _ptr(dw0), _ptr(dgamma), _ptr(dbeta), _ptr(workspace), workspace.numel(),
+            _stream(q, stream))
+    _lib.check("ttt_linear_backward", rc)
+    return dq, dk, dv, deta, dw0, dgamma, dbeta
 
 
 def ttt_mlp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,

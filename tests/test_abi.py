@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 3
+    assert _lib.abi_version() == 4
     for code in range(7):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
@@ -184,3 +184,49 @@ def test_decode_step_rejects_bad_arguments():
     assert _decode(p, wb=_addr(5)) == _lib.TTT_ERR_ALIAS                  # w_base == w
     assert _decode(p, z=_addr(1)) == _lib.TTT_ERR_ALIAS                   # z == q
     assert _decode(p, w=_addr(2)) == _lib.TTT_ERR_ALIAS                   # w == k
+
+
+def _backward(p, ws=None, ws_bytes=None, **ptrs):
+    names = ["q", "k", "v", "eta", "w0", "g", "b", "dz", "dwT", "dq", "dk", "dv", "deta",
+             "dw0", "dg", "db"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    if ws is None:
+        ws = _addr(30)
+    if ws_bytes is None:
+        ws_bytes = (_lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p))
+                    if p is not None else 1 << 30)
+    return _lib.lib().ttt_linear_backward(ctypes.byref(p) if p is not None else None, *args,
+                                          ws, ws_bytes, None)
+
+
+def test_backward_workspace_size():
+    # 16 KB per 16-token tile and unit (the bases), 16 KB + 512 B per unit, 256-byte rounding
+    p = _params(B=2, H=3, T=100)
+    units, tiles = 6, 7
+    want = units * tiles * 16384 + units * 16384 + units * 512
+    assert _lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p)) == \
+        (want + 255) // 256 * 256
+    assert _lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(_params(d=16))) == 0
+    assert _lib.lib().ttt_linear_backward_workspace_bytes(None) == 0
+
+
+def test_backward_rejects_bad_arguments():
+    p = _params()
+    need = _lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p))
+    assert _backward(None) == _lib.TTT_ERR_NULL
+    assert _backward(p, ws=ctypes.c_void_p(0)) == _lib.TTT_ERR_NULL
+    for name in ["q", "k", "v", "eta", "w0", "dz", "dq", "dk", "dv", "deta", "dw0", "g", "b",
+                 "dg", "db"]:
+        assert _backward(p, **{name: None}) == _lib.TTT_ERR_NULL, name
+    assert _backward(_params(flags=_lib.TTT_NO_LN), dg=None) == _lib.TTT_ERR_NULL  # pair
+    assert _backward(p, ws_bytes=need - 1) == _lib.TTT_ERR_SHAPE
+    assert _backward(p, ws=ctypes.c_void_p(BASE + 30 * GAP + 64)) == _lib.TTT_ERR_ARG
+    assert _backward(_params(mini_batch=32)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _backward(_params(d=32)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _backward(_params(T=0)) == _lib.TTT_ERR_SHAPE
+    assert _backward(p, dq=_addr(1)) == _lib.TTT_ERR_ALIAS          # dq == q
+    assert _backward(p, dw0=_addr(5)) == _lib.TTT_ERR_ALIAS         # dw0 == w0
+    assert _backward(p, dk=_addr(10)) == _lib.TTT_ERR_ALIAS         # dk == dq
+    assert _backward(p, deta=_addr(8)) == _lib.TTT_ERR_ALIAS        # deta == dz
+    assert _backward(p, ws=_addr(12)) == _lib.TTT_ERR_ALIAS         # workspace == dv
+    assert _backward(p, dwT=_addr(14)) == _lib.TTT_ERR_ALIAS        # dw_final == dw0
