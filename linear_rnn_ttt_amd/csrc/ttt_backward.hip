@@ -17,23 +17,29 @@
 //
 // Backward, mini-batches in reverse, A = adjoint of the next base:
 //   DO  = LN backward of dZ                      (dgamma, dbeta partials)
-//   dQ  = [dZ] + DO W^T - (tril(DO G^T) * eta) K
-//   KA  = K A + triu(K Q^T) DO,   GA = G A^T + triu(G DO^T) Q
+//   dQ  = [dZ] + DO W^T - M2 K,        M2 = tril(DO G^T) * eta
+//   KA  = K A + U1 DO,                 U1 = triu(K Q^T)
+//   GA  = G A^T + U2 Q,                U2 = triu(G DO^T)
 //   deta_s = -KA_s . g_s,  dg_s = -eta_s KA_s  -> backward of g_s -> dh_s, dt_s
 //   dV  = dT,  dK = DH W^T - eta GA - [dT],  A <- A + Q^T DO + K^T DH
-// and dW0 = A after the first mini-batch.  ([.] = only with the residual.)
+// and dW0 = A after the first mini-batch.  ([.] = only with the residual;
+// o uses M1 = tril(Q K^T) * eta the same way.)
 //
-// Kernel: one 256-thread workgroup per (batch, head) unit.  Phase 1 replays
-// the forward recurrence of the bases and stores each mini-batch's base in
-// the workspace (16 KB per mini-batch: the device has room for every base,
-// so nothing is recomputed); phase 2 walks the mini-batches in reverse.
-// Lane f of wave w holds column f of rows 16w..16w+15 of W, of W^T, of A and
-// of A^T; a product X M of a 16-token tile X (LDS) with such a matrix is
-// formed as four 16-row shares reduced through LDS, after which wave w owns
-// token rows 4w..4w+3 (lane f = feature f) for the per-token LN algebra,
-// whose sums are butterflies over the wave.  fp32 arithmetic throughout.
-// Tokens past T (a last partial mini-batch) are zero rows with zero
-// gradient factors; they add nothing and nothing is stored for them.
+// Kernel: one 256-thread workgroup (4 waves) per (batch, head) unit.  Phase 1
+// replays the forward recurrence of the bases and stores each mini-batch's
+// base in the workspace (16 KB per mini-batch: the device has room for every
+// base, so nothing is recomputed); phase 2 walks the mini-batches in reverse.
+// Every product is a 16x16x16 bf16 matrix-unit chain on hi/lo splits of
+// both fp32 operands (hi*hi + hi*lo + lo*hi, about 16 significant bits),
+// accumulated in fp32: wave w forms output columns 16w..16w+15 of each
+// token-tile product and holds columns 16w.. of W, W^T, A and A^T (A and A^T
+// as fp32 accumulators, updated in place).  The 16x16 Gram tiles are formed
+// in both orientations by every wave, so each masked coefficient tile is
+// already in the matrix unit's A-operand layout.  Product tiles go through
+// LDS to the token-row algebra (LN forward and backward), where wave w owns
+// token rows 4w..4w+3 with lane f holding feature f and sums are DPP/permlane
+// butterflies over the wave.  Tokens past T (a last partial mini-batch) are
+// zero rows with zero gradient factors; nothing is stored for them.
 #include "ttt_backward.hpp"
 #include "ttt_device.hpp"
 
@@ -42,11 +48,9 @@ namespace {
 
 constexpr int DD = 64;         // head dimension
 constexpr int NW = 4;          // waves per unit
-constexpr int RW = DD / NW;    // rows of the state per wave
 constexpr int TB = 16;         // tokens per mini-batch tile
 constexpr int RO = TB / NW;    // token rows owned per wave
-constexpr int LS = 68;         // LDS row stride of token tiles (16-byte rows, 2-way Gram reads)
-constexpr int WS = 65;         // LDS row stride of the state tile (conflict-free transpose)
+constexpr int LS = 68;         // LDS row stride (floats): 16-byte rows, spread banks
 constexpr float INV_D = 1.0f / DD;
 
 struct __attribute__((aligned(16))) BwdLds {
@@ -55,11 +59,8 @@ struct __attribute__((aligned(16))) BwdLds {
   float g[TB][LS];
   float dO[TB][LS];
   float dh[TB][LS];
-  float w[DD][WS];
-  float red[3][NW][TB][DD];   // per-wave shares of up to three products
-  // masked, scaled Gram tiles (see gram_masks)
-  float m1[TB][TB + 1], u1[TB][TB + 1];   // from Q K^T
-  float m2[TB][TB + 1], u2[TB][TB + 1];   // from DO G^T
+  float w[DD][LS];            // the base of the current mini-batch
+  float t[3][TB][LS];         // product tiles on their way to the token-row algebra
   float eta[TB];
   float dln[2][NW][DD];
 };
@@ -83,74 +84,78 @@ __device__ __forceinline__ void st_io(void* p, size_t i, float x) {
   }
 }
 
-// Rows row0..row0+15 of a [.., 64] io tensor into an LDS tile; rows at or
-// past `valid` are zero.  Thread tid moves 4 consecutive features.
+// Tiles are fetched a mini-batch ahead into registers and stored to LDS
+// when they are due.  The loads are unconditional -- rows at or past the
+// last valid token re-read that token -- and the zero rows are made when
+// the data is used: a load under a branch would be waited for at the end
+// of the branch, which is what the prefetch is there to avoid.
+
+// Thread tid's share of rows row0..row0+15 of a [.., 64] io tensor: 4
+// consecutive features of row tid / 16 (raw; see put_fetched).
 template <bool BF16>
-__device__ __forceinline__ void load_tile(float (*dst)[LS], const void* src, size_t row0,
-                                          int valid, int tid) {
-  const int i = tid >> 4, c = (tid & 15) * 4;
-  float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
-  if (i < valid) {
-    const size_t e = (row0 + i) * DD + c;
-    if constexpr (BF16) {
-      const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + e);
-      x = make_float4(bf16_lo_to_f32(u.x), bf16_hi_to_f32(u.x), bf16_lo_to_f32(u.y),
-                      bf16_hi_to_f32(u.y));
-    } else {
-      x = *reinterpret_cast<const float4*>(static_cast<const float*>(src) + e);
-    }
+__device__ __forceinline__ uint4 fetch_tile(const void* src, size_t row0, int valid, int tid) {
+  const int i = min(tid >> 4, valid - 1), c = (tid & 15) * 4;
+  const size_t e = (row0 + i) * DD + c;
+  if constexpr (BF16) {
+    const uint2 u = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(src) + e);
+    return make_uint4(u.x, u.y, 0u, 0u);
+  } else {
+    return *reinterpret_cast<const uint4*>(static_cast<const float*>(src) + e);
   }
-  *reinterpret_cast<float4*>(&dst[i][c]) = x;
 }
 
-// This wave's share of the product X M for the 16 token rows of X, into
-// red[slot][w]: sum_r X[i][16w + r] M[r], M[r] = column f of row 16w + r.
-// (The row loop is only partly unrolled so that the LDS reads of X are not
-// all hoisted into registers at once.)
-__device__ __forceinline__ void share_rows(BwdLds& L, int slot, const float (*X)[LS],
-                                           const float (&M)[RW], int w, int f) {
-#pragma unroll 2
-  for (int i = 0; i < TB; ++i) {
-    const float4* x = reinterpret_cast<const float4*>(&X[i][RW * w]);
-    float acc = 0.f;
+// Store a fetched share, zero for rows at or past `valid`.
+template <bool BF16>
+__device__ __forceinline__ void put_fetched(float (*dst)[LS], int tid, uint4 u, int valid) {
+  float4 x;
+  if constexpr (BF16)
+    x = make_float4(bf16_lo_to_f32(u.x), bf16_hi_to_f32(u.x), bf16_lo_to_f32(u.y),
+                    bf16_hi_to_f32(u.y));
+  else
+    x = make_float4(bitsf(u.x), bitsf(u.y), bitsf(u.z), bitsf(u.w));
+  if ((tid >> 4) >= valid) x = make_float4(0.f, 0.f, 0.f, 0.f);
+  *reinterpret_cast<float4*>(&dst[tid >> 4][(tid & 15) * 4]) = x;
+}
+
+// What one mini-batch tile needs from global memory, per thread (raw).
+struct Fetch {
+  uint4 k, q;        // token-tile shares
+  float4 w[4];       // share of the stored base (phase 2)
+  float eta;         // eta of token tid % 16
+  float v[4], dz[4];  // this wave's token rows, feature f
+};
+
+// ---- matrix-unit fragments (lane l: g = l / 16, c = l % 16) ---------------
+// A operand of a 16x16x16 product: lane holds A[c][4g + i]; B operand:
+// B[4g + i][c]; accumulator: D[4g + i][c] (see ttt_device.hpp).
+
+__device__ __forceinline__ f32x4 f4(float a, float b, float c, float d) {
+  return f32x4{a, b, c, d};
+}
+
+// D += A B with both operands given as hi/lo bf16 splits.
+__device__ __forceinline__ f32x4 mma3(const Split4& a, const Split4& b, f32x4 d) {
+  d = mfma16(a.lo, b.hi, d);
+  d = mfma16(a.hi, b.lo, d);
+  return mfma16(a.hi, b.hi, d);
+}
+
+// Row fragment: X[c][col0 .. col0+3] (A operand of X, or B operand of X^T).
+__device__ __forceinline__ Split4 row_frag(const float (*X)[LS], int c, int col0) {
+  const float4 x = *reinterpret_cast<const float4*>(&X[c][col0]);
+  return split4(f4(x.x, x.y, x.z, x.w));
+}
+
+// Column fragment: X[r0 + i][col] for i = 0..3 (B operand of X, or A
+// operand of X^T).
+__device__ __forceinline__ Split4 col_frag(const float (*X)[LS], int r0, int col) {
+  return split4(f4(X[r0][col], X[r0 + 1][col], X[r0 + 2][col], X[r0 + 3][col]));
+}
+
+// Store an accumulator tile D[4g + i][c] at rows 0..15, columns col0 + c.
+__device__ __forceinline__ void put_tile(float (*T)[LS], int g, int c, int col0, f32x4 d) {
 #pragma unroll
-    for (int m = 0; m < RW / 4; ++m) {
-      const float4 y = x[m];
-      acc = __builtin_fmaf(y.x, M[4 * m + 0], acc);
-      acc = __builtin_fmaf(y.y, M[4 * m + 1], acc);
-      acc = __builtin_fmaf(y.z, M[4 * m + 2], acc);
-      acc = __builtin_fmaf(y.w, M[4 * m + 3], acc);
-    }
-    L.red[slot][w][i][f] = acc;
-  }
-}
-
-__device__ __forceinline__ float red_sum(const BwdLds& L, int slot, int i, int f) {
-  return (L.red[slot][0][i][f] + L.red[slot][1][i][f]) +
-         (L.red[slot][2][i][f] + L.red[slot][3][i][f]);
-}
-
-// Row Gram matrix S[i][s] = X_i . Y_s of two 16-token tiles, stored as the
-// two masked forms the token-row sums use:
-//   M[i][s] = eta_s S[i][s] for s <= i (else 0)   -- sums over s <= i
-//   U[s][i] = S[i][s]       for i >= s (else 0)   -- sums over i >= s
-// Thread tid forms entry (tid / 16, tid % 16).
-__device__ __forceinline__ void gram_masks(const float (*X)[LS], const float (*Y)[LS],
-                                           const float* eta, float (*M)[TB + 1],
-                                           float (*U)[TB + 1], int tid) {
-  const int i = tid >> 4, s = tid & 15;
-  float acc = 0.f;
-#pragma unroll 4
-  for (int m = 0; m < DD / 4; ++m) {
-    const float4 x = *reinterpret_cast<const float4*>(&X[i][4 * m]);
-    const float4 y = *reinterpret_cast<const float4*>(&Y[s][4 * m]);
-    acc = __builtin_fmaf(x.x, y.x, acc);
-    acc = __builtin_fmaf(x.y, y.y, acc);
-    acc = __builtin_fmaf(x.z, y.z, acc);
-    acc = __builtin_fmaf(x.w, y.w, acc);
-  }
-  M[i][s] = s <= i ? eta[s] * acc : 0.f;
-  U[s][i] = i >= s ? acc : 0.f;
+  for (int i = 0; i < 4; ++i) T[4 * g + i][col0 + c] = d[i];
 }
 
 // x from another lane of the same 16-lane row (DPP control CTRL).
@@ -231,8 +236,10 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   const int unit = blockIdx.x;
   const int head = unit % a.H;
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int f = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // column block of the products
+  const int f = tid & 63;                                   // feature of the token-row algebra
+  const int g = f >> 4, c = f & 15;                         // matrix-unit lane coordinates
+  const int col = 16 * w + c;                               // this lane's product column
   const int T = a.T;
   const int tiles = (T + TB - 1) / TB;
   const size_t row_unit = static_cast<size_t>(unit) * T;   // first token row of the unit
@@ -246,117 +253,170 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   }
 
   // ---- phase 1: the bases of every mini-batch ------------------------------
-  float Wr[RW];
+  // Wacc[rt][i] = W[16 rt + 4g + i][col]
+  f32x4 Wacc[4];
 #pragma unroll
-  for (int r = 0; r < RW; ++r) Wr[r] = w0[(RW * w + r) * DD + f];
-  for (int c = 0; c < tiles; ++c) {
-    const int t0 = c * TB;
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Wacc[rt][i] = w0[(16 * rt + 4 * g + i) * DD + col];
+  // tile ct's k, eta and v rows, fetched while tile ct - 1 computes
+  auto fetch1 = [&](int ct, Fetch& F) {
+    const int t0 = ct * TB;
     const int nv = min(TB, T - t0);
-    load_tile<BF16>(L.k, a.k, row_unit + t0, nv, tid);
-    if (tid < TB) L.eta[tid] = tid < nv ? a.eta[row_unit + t0 + tid] : 0.f;
+    F.k = fetch_tile<BF16>(a.k, row_unit + t0, nv, tid);
+    F.eta = a.eta[row_unit + t0 + min(tid & 15, nv - 1)];
+#pragma unroll
+    for (int j = 0; j < RO; ++j)
+      F.v[j] = ld_io<BF16>(a.v, (row_unit + t0 + min(RO * w + j, nv - 1)) * DD + f);
+  };
+  Fetch F;
+  fetch1(0, F);
+  for (int ct = 0; ct < tiles; ++ct) {
+    const int t0 = ct * TB;
+    const int nv = min(TB, T - t0);
+    float* base = bases + static_cast<size_t>(ct) * DD * DD;
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) base[(16 * rt + 4 * g + i) * DD + col] = Wacc[rt][i];
+    put_fetched<BF16>(L.k, tid, F.k, nv);
+    if (tid < TB) L.eta[tid] = tid < nv ? F.eta : 0.f;
     float vr[RO];
 #pragma unroll
-    for (int j = 0; j < RO; ++j) {
-      const int i = RO * w + j;
-      vr[j] = i < nv ? ld_io<BF16>(a.v, (row_unit + t0 + i) * DD + f) : 0.f;
-    }
-    float* base = bases + static_cast<size_t>(c) * DD * DD;
-#pragma unroll
-    for (int r = 0; r < RW; ++r) base[(RW * w + r) * DD + f] = Wr[r];
+    for (int j = 0; j < RO; ++j) vr[j] = RO * w + j < nv ? F.v[j] : 0.f;
+    if (ct + 1 < tiles) fetch1(ct + 1, F);
     lds_barrier();
-    share_rows(L, 0, L.k, Wr, w, f);
-    lds_barrier();
-    float h[RO], kr[RO];
+    {
+      f32x4 h = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int j = 0; j < RO; ++j) {
-      h[j] = red_sum(L, 0, RO * w + j, f);
-      kr[j] = L.k[RO * w + j][f];
-    }
-    Inner R;
-    inner_grad<LN, RES>(h, vr, kr, gam, bet, a.eps, R);
-#pragma unroll
-    for (int j = 0; j < RO; ++j) {
-      const int i = RO * w + j;
-      L.g[i][f] = i < nv ? L.eta[i] * R.g[j] : 0.f;
+      for (int kt = 0; kt < 4; ++kt)
+        h = mma3(row_frag(L.k, c, 16 * kt + 4 * g), split4(Wacc[kt]), h);
+      put_tile(L.t[0], g, c, 16 * w, h);
     }
     lds_barrier();
-    // W <- W - sum_s k_s^T (eta_s g_s) on this wave's rows
-#pragma unroll 2
-    for (int s = 0; s < TB; ++s) {
-      const float gs = L.g[s][f];
-      const float4* kk = reinterpret_cast<const float4*>(&L.k[s][RW * w]);
+    {
+      float h[RO], kr[RO];
 #pragma unroll
-      for (int m = 0; m < RW / 4; ++m) {
-        const float4 y = kk[m];
-        Wr[4 * m + 0] = __builtin_fmaf(-y.x, gs, Wr[4 * m + 0]);
-        Wr[4 * m + 1] = __builtin_fmaf(-y.y, gs, Wr[4 * m + 1]);
-        Wr[4 * m + 2] = __builtin_fmaf(-y.z, gs, Wr[4 * m + 2]);
-        Wr[4 * m + 3] = __builtin_fmaf(-y.w, gs, Wr[4 * m + 3]);
+      for (int j = 0; j < RO; ++j) {
+        h[j] = L.t[0][RO * w + j][f];
+        kr[j] = L.k[RO * w + j][f];
+      }
+      Inner R;
+      inner_grad<LN, RES>(h, vr, kr, gam, bet, a.eps, R);
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        const int i = RO * w + j;
+        L.g[i][f] = i < nv ? -L.eta[i] * R.g[j] : 0.f;   // -eta g: the update's right factor
       }
     }
     lds_barrier();
+    {
+      // W[:, cols] += K^T (-eta G)[:, cols]; row tile rt of W takes the
+      // A operand K^T[16 rt + c][4g + i] = K[4g + i][16 rt + c]
+      const Split4 ug = col_frag(L.g, 4 * g, col);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt)
+        Wacc[rt] = mma3(col_frag(L.k, 4 * g, 16 * rt + c), ug, Wacc[rt]);
+    }
+    lds_barrier();
   }
+  __syncthreads();   // every base stored before any wave reads one back
 
   // ---- phase 2: the mini-batches in reverse ---------------------------------
-  float Ar[RW], At[RW];
+  // Aa[rt][i] = A[16 rt + 4g + i][col],  At[rt][i] = A[col][16 rt + 4g + i]
+  f32x4 Aa[4], At[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    Aa[rt] = f4(0.f, 0.f, 0.f, 0.f);
+    At[rt] = f4(0.f, 0.f, 0.f, 0.f);
+  }
   if (a.dw_final) {
     const float* A0 = a.dw_final + static_cast<size_t>(unit) * DD * DD;
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      Ar[r] = A0[(RW * w + r) * DD + f];
-      At[r] = A0[f * DD + RW * w + r];
-    }
-  } else {
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int r = 0; r < RW; ++r) Ar[r] = At[r] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        Aa[rt][i] = A0[(16 * rt + 4 * g + i) * DD + col];
+        At[rt][i] = A0[col * DD + 16 * rt + 4 * g + i];
+      }
   }
-  float dgam = 0.f, dbet = 0.f;
-  for (int c = tiles - 1; c >= 0; --c) {
-    const int t0 = c * TB;
+  // tile ct's base, k, q, eta, v and dz rows, fetched while tile ct + 1
+  // computes (float4 e of the base: row e / 16, columns 4 (e % 16) ..)
+  auto fetch2 = [&](int ct, Fetch& F) {
+    const int t0 = ct * TB;
     const int nv = min(TB, T - t0);
-    const float* base = bases + static_cast<size_t>(c) * DD * DD;
+    const float4* base =
+        reinterpret_cast<const float4*>(bases + static_cast<size_t>(ct) * DD * DD);
 #pragma unroll
-    for (int r = 0; r < RW; ++r) {
-      Wr[r] = base[(RW * w + r) * DD + f];   // written by this thread in phase 1
-      L.w[RW * w + r][f] = Wr[r];
+    for (int m = 0; m < 4; ++m) F.w[m] = base[tid + 256 * m];
+    F.k = fetch_tile<BF16>(a.k, row_unit + t0, nv, tid);
+    F.q = fetch_tile<BF16>(a.q, row_unit + t0, nv, tid);
+    F.eta = a.eta[row_unit + t0 + min(tid & 15, nv - 1)];
+#pragma unroll
+    for (int j = 0; j < RO; ++j) {
+      const size_t row = row_unit + t0 + min(RO * w + j, nv - 1);
+      F.v[j] = ld_io<BF16>(a.v, row * DD + f);
+      F.dz[j] = ld_io<BF16>(a.dz, row * DD + f);
     }
-    load_tile<BF16>(L.k, a.k, row_unit + t0, nv, tid);
-    load_tile<BF16>(L.q, a.q, row_unit + t0, nv, tid);
-    if (tid < TB) L.eta[tid] = tid < nv ? a.eta[row_unit + t0 + tid] : 0.f;
+  };
+  float dgam = 0.f, dbet = 0.f;
+  fetch2(tiles - 1, F);
+  for (int ct = tiles - 1; ct >= 0; --ct) {
+    const int t0 = ct * TB;
+    const int nv = min(TB, T - t0);
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int e = tid + 256 * m;
+      *reinterpret_cast<float4*>(&L.w[e >> 4][4 * (e & 15)]) = F.w[m];
+    }
+    put_fetched<BF16>(L.k, tid, F.k, nv);
+    put_fetched<BF16>(L.q, tid, F.q, nv);
+    if (tid < TB) L.eta[tid] = tid < nv ? F.eta : 0.f;
     float vr[RO], dzr[RO];
     bool ok[RO];
 #pragma unroll
     for (int j = 0; j < RO; ++j) {
-      const int i = RO * w + j;
-      ok[j] = i < nv;
-      vr[j] = ok[j] ? ld_io<BF16>(a.v, (row_unit + t0 + i) * DD + f) : 0.f;
-      dzr[j] = ok[j] ? ld_io<BF16>(a.dz, (row_unit + t0 + i) * DD + f) : 0.f;
+      ok[j] = RO * w + j < nv;
+      vr[j] = ok[j] ? F.v[j] : 0.f;
+      dzr[j] = ok[j] ? F.dz[j] : 0.f;
     }
-    lds_barrier();  // B1: W, K, Q, eta tiles
+    if (ct > 0) fetch2(ct - 1, F);
+    lds_barrier();  // B1: W, K, Q, eta
 
-    float Wt[RW];
+    // W and W^T column blocks (B operands), K W and Q W, the two Q/K Grams
+    Split4 Wb[4], Wt[4];
 #pragma unroll
-    for (int r = 0; r < RW; ++r) Wt[r] = L.w[f][RW * w + r];
+    for (int kt = 0; kt < 4; ++kt) {
+      Wb[kt] = col_frag(L.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
+      Wt[kt] = row_frag(L.w, col, 16 * kt + 4 * g);   // W^T[16kt + 4g + i][col]
+    }
+    f32x4 qw = f4(0.f, 0.f, 0.f, 0.f), s1 = qw, s1t = qw;
+    {
+      f32x4 h = qw;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const Split4 kf = row_frag(L.k, c, 16 * kt + 4 * g);
+        const Split4 qf = row_frag(L.q, c, 16 * kt + 4 * g);
+        h = mma3(kf, Wb[kt], h);
+        qw = mma3(qf, Wb[kt], qw);
+        s1 = mma3(qf, kf, s1);     // s1[i]  = q_{4g+i} . k_c
+        s1t = mma3(kf, qf, s1t);   // s1t[i] = k_{4g+i} . q_c
+      }
+      put_tile(L.t[0], g, c, 16 * w, h);
+    }
     float kr[RO], er[RO];
 #pragma unroll
     for (int j = 0; j < RO; ++j) {
       kr[j] = L.k[RO * w + j][f];
       er[j] = L.eta[RO * w + j];
     }
-    share_rows(L, 0, L.k, Wr, w, f);   // K W
-    share_rows(L, 1, L.q, Wr, w, f);   // Q W
-    gram_masks(L.q, L.k, L.eta, L.m1, L.u1, tid);
-    lds_barrier();  // B2: shares of K W and Q W, S1
+    lds_barrier();  // B2: K W
 
-    float qw[RO];
     Inner R;
     {
       float h[RO];
 #pragma unroll
-      for (int j = 0; j < RO; ++j) {
-        h[j] = red_sum(L, 0, RO * w + j, f);
-        qw[j] = red_sum(L, 1, RO * w + j, f);
-      }
+      for (int j = 0; j < RO; ++j) h[j] = L.t[0][RO * w + j][f];
       inner_grad<LN, RES>(h, vr, kr, gam, bet, a.eps, R);
     }
 #pragma unroll
@@ -366,22 +426,27 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
     lds_barrier();  // B3: G
 
-    // o_i = (Q W)_i - sum_{s<=i} eta_s S1[i][s] g_s, then the output LN backward
-    float dO[RO];
+    // o = Q W - M1 G with M1[c][s] = eta_s (q_c . k_s) for s <= c, whose
+    // A-layout entries (row c, column s = 4g + i) are s1t
     {
-      float o[RO];
+      float m[4];
 #pragma unroll
-      for (int j = 0; j < RO; ++j) {
-        const int i = RO * w + j;
-        float acc = qw[j];
-#pragma unroll
-        for (int s = 0; s < TB; ++s) acc = __builtin_fmaf(-L.m1[i][s], L.g[s][f], acc);
-        o[j] = acc;
+      for (int i = 0; i < 4; ++i) {
+        const int s = 4 * g + i;
+        m[i] = s <= c ? -L.eta[s] * s1t[i] : 0.f;
       }
+      const f32x4 o = mma3(split4(f4(m[0], m[1], m[2], m[3])), col_frag(L.g, 4 * g, col), qw);
+      put_tile(L.t[1], g, c, 16 * w, o);
+    }
+    lds_barrier();  // B4: o
+
+    // output LN backward on this wave's rows
+    {
+      float dO[RO];
       if constexpr (LN) {
-        float s[RO], xc[RO];
+        float o[RO], s[RO], xc[RO];
 #pragma unroll
-        for (int j = 0; j < RO; ++j) s[j] = o[j];
+        for (int j = 0; j < RO; ++j) s[j] = o[j] = L.t[1][RO * w + j][f];
         wave_sums(s);
 #pragma unroll
         for (int j = 0; j < RO; ++j) {
@@ -389,8 +454,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
           s[j] = xc[j] * xc[j];
         }
         wave_sums(s);
-        float xo[RO], dx[RO], s2[2 * RO];
-        float rho_o[RO];
+        float xo[RO], dx[RO], s2[2 * RO], rho_o[RO];
 #pragma unroll
         for (int j = 0; j < RO; ++j) {
           rho_o[j] = 1.0f / __builtin_sqrtf(s[j] * INV_D + a.eps);
@@ -411,34 +475,56 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
 #pragma unroll
         for (int j = 0; j < RO; ++j) dO[j] = dzr[j];
       }
-    }
 #pragma unroll
-    for (int j = 0; j < RO; ++j) L.dO[RO * w + j][f] = dO[j];
-    lds_barrier();  // B4: DO
+      for (int j = 0; j < RO; ++j) L.dO[RO * w + j][f] = dO[j];
+    }
+    lds_barrier();  // B5: DO
 
-    share_rows(L, 0, L.dO, Wt, w, f);   // DO W^T
-    share_rows(L, 1, L.k, Ar, w, f);    // K A
-    share_rows(L, 2, L.g, At, w, f);    // G A^T
-    gram_masks(L.dO, L.g, L.eta, L.m2, L.u2, tid);
-    lds_barrier();  // B5: shares, S2
-
-    float ga[RO], dt[RO], dh[RO];
+    // dQ' = DO W^T - M2 K, KA = K A + U1 DO, GA = G A^T + U2 Q, with the
+    // DO/G Grams; M2, U1, U2 in A layout (row c, column s = 4g + i)
+    Split4 dOb, kb, qb;
     {
-      float ka[RO];
+      f32x4 pdq = f4(0.f, 0.f, 0.f, 0.f), pka = pdq, pga = pdq, s2 = pdq, s2t = pdq;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const Split4 df = row_frag(L.dO, c, 16 * kt + 4 * g);
+        const Split4 gf = row_frag(L.g, c, 16 * kt + 4 * g);
+        const Split4 kf = row_frag(L.k, c, 16 * kt + 4 * g);
+        pdq = mma3(df, Wt[kt], pdq);
+        pka = mma3(kf, split4(Aa[kt]), pka);
+        pga = mma3(gf, split4(At[kt]), pga);
+        s2 = mma3(df, gf, s2);     // s2[i]  = do_{4g+i} . g_c
+        s2t = mma3(gf, df, s2t);   // s2t[i] = g_{4g+i} . do_c
+      }
+      float m2[4], u1[4], u2[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 4 * g + i;
+        m2[i] = s <= c ? -L.eta[s] * s2t[i] : 0.f;   // -eta_s (do_c . g_s), s <= c
+        u1[i] = s >= c ? s1[i] : 0.f;                // q_s . k_c, s >= c
+        u2[i] = s >= c ? s2[i] : 0.f;                // do_s . g_c, s >= c
+      }
+      dOb = col_frag(L.dO, 4 * g, col);
+      kb = col_frag(L.k, 4 * g, col);
+      qb = col_frag(L.q, 4 * g, col);
+      pdq = mma3(split4(f4(m2[0], m2[1], m2[2], m2[3])), kb, pdq);
+      pka = mma3(split4(f4(u1[0], u1[1], u1[2], u1[3])), dOb, pka);
+      pga = mma3(split4(f4(u2[0], u2[1], u2[2], u2[3])), qb, pga);
+      put_tile(L.t[0], g, c, 16 * w, pdq);
+      put_tile(L.t[1], g, c, 16 * w, pka);
+      put_tile(L.t[2], g, c, 16 * w, pga);
+    }
+    lds_barrier();  // B6: dQ', KA, GA
+
+    float ga[RO], dt[RO];
+    {
+      float ka[RO], dh[RO];
 #pragma unroll
       for (int j = 0; j < RO; ++j) {
         const int i = RO * w + j;
-        float dq = red_sum(L, 0, i, f) + (RES ? dzr[j] : 0.f);
-        float kacc = red_sum(L, 1, i, f);
-        float gacc = red_sum(L, 2, i, f);
-#pragma unroll 4
-        for (int s = 0; s < TB; ++s) {
-          dq = __builtin_fmaf(-L.m2[i][s], L.k[s][f], dq);      // tokens s <= i
-          kacc = __builtin_fmaf(L.u1[i][s], L.dO[s][f], kacc);  // tokens s >= i
-          gacc = __builtin_fmaf(L.u2[i][s], L.q[s][f], gacc);
-        }
-        ka[j] = kacc;
-        ga[j] = gacc;
+        const float dq = L.t[0][i][f] + (RES ? dzr[j] : 0.f);
+        ka[j] = L.t[1][i][f];
+        ga[j] = L.t[2][i][f];
         if (ok[j]) st_io<BF16>(a.dq, (row_unit + t0 + i) * DD + f, dq);
       }
       // deta_i = -KA_i . g_i and the backward of g_i for u = -eta_i KA_i
@@ -504,35 +590,30 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         L.dh[i][f] = dh[j];
       }
     }
-    lds_barrier();  // B6: DH
+    lds_barrier();  // B7: DH
 
-    share_rows(L, 0, L.dh, Wt, w, f);   // DH W^T
-    // A <- A + Q^T DO + K^T DH (rows 16w + r, column f), and the same for A^T
-#pragma unroll 2
-    for (int i = 0; i < TB; ++i) {
-      const float dOf = L.dO[i][f], dhf = L.dh[i][f], qf = L.q[i][f], kf = L.k[i][f];
-      const float4* qq = reinterpret_cast<const float4*>(&L.q[i][RW * w]);
-      const float4* kk = reinterpret_cast<const float4*>(&L.k[i][RW * w]);
-      const float4* oo = reinterpret_cast<const float4*>(&L.dO[i][RW * w]);
-      const float4* hh = reinterpret_cast<const float4*>(&L.dh[i][RW * w]);
+    {
+      // DH W^T, then A += Q^T DO + K^T DH and A^T += DO^T Q + DH^T K; the
+      // A operand of row tile rt of X^T is X[4g + i][16 rt + c]
+      f32x4 pdk = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int m = 0; m < RW / 4; ++m) {
-        const float4 q4 = qq[m], k4 = kk[m], o4 = oo[m], h4 = hh[m];
-        Ar[4 * m + 0] = __builtin_fmaf(k4.x, dhf, __builtin_fmaf(q4.x, dOf, Ar[4 * m + 0]));
-        Ar[4 * m + 1] = __builtin_fmaf(k4.y, dhf, __builtin_fmaf(q4.y, dOf, Ar[4 * m + 1]));
-        Ar[4 * m + 2] = __builtin_fmaf(k4.z, dhf, __builtin_fmaf(q4.z, dOf, Ar[4 * m + 2]));
-        Ar[4 * m + 3] = __builtin_fmaf(k4.w, dhf, __builtin_fmaf(q4.w, dOf, Ar[4 * m + 3]));
-        At[4 * m + 0] = __builtin_fmaf(h4.x, kf, __builtin_fmaf(o4.x, qf, At[4 * m + 0]));
-        At[4 * m + 1] = __builtin_fmaf(h4.y, kf, __builtin_fmaf(o4.y, qf, At[4 * m + 1]));
-        At[4 * m + 2] = __builtin_fmaf(h4.z, kf, __builtin_fmaf(o4.z, qf, At[4 * m + 2]));
-        At[4 * m + 3] = __builtin_fmaf(h4.w, kf, __builtin_fmaf(o4.w, qf, At[4 * m + 3]));
+      for (int kt = 0; kt < 4; ++kt) pdk = mma3(row_frag(L.dh, c, 16 * kt + 4 * g), Wt[kt], pdk);
+      put_tile(L.t[0], g, c, 16 * w, pdk);
+      const Split4 dhb = col_frag(L.dh, 4 * g, col);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        const int fc = 16 * rt + c;
+        Aa[rt] = mma3(col_frag(L.q, 4 * g, fc), dOb, Aa[rt]);
+        Aa[rt] = mma3(col_frag(L.k, 4 * g, fc), dhb, Aa[rt]);
+        At[rt] = mma3(col_frag(L.dO, 4 * g, fc), qb, At[rt]);
+        At[rt] = mma3(col_frag(L.dh, 4 * g, fc), kb, At[rt]);
       }
     }
-    lds_barrier();  // B7: shares of DH W^T; every tile read done
+    lds_barrier();  // B8: DH W^T; every tile read done
 #pragma unroll
     for (int j = 0; j < RO; ++j) {
       const int i = RO * w + j;
-      const float dk = red_sum(L, 0, i, f) - er[j] * ga[j] - (RES ? dt[j] : 0.f);
+      const float dk = L.t[0][i][f] - er[j] * ga[j] - (RES ? dt[j] : 0.f);
       if (ok[j]) st_io<BF16>(a.dk, (row_unit + t0 + i) * DD + f, dk);
     }
   }
@@ -540,7 +621,9 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   // ---- dW0 of this unit and its LN-parameter partial sums --------------------
   float* dst = (a.state0_per_batch ? a.dw0 : a.ws_dw0) + static_cast<size_t>(unit) * DD * DD;
 #pragma unroll
-  for (int r = 0; r < RW; ++r) dst[(RW * w + r) * DD + f] = Ar[r];
+  for (int rt = 0; rt < 4; ++rt)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g + i) * DD + col] = Aa[rt][i];
   L.dln[0][w][f] = dgam;
   L.dln[1][w][f] = dbet;
   lds_barrier();
