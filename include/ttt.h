@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 4
+#define TTT_ABI_VERSION 5
 
 typedef enum {
   TTT_OK = 0,
@@ -78,7 +78,8 @@ typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
 
 enum {
   TTT_NO_LN = 1u << 0,        /* f(x) = [x +] g(x) */
-  TTT_NO_RESIDUAL = 1u << 1   /* f(x) = [LN](g(x)) */
+  TTT_NO_RESIDUAL = 1u << 1,  /* f(x) = [LN](g(x)) */
+  TTT_BASES_SAVED = 1u << 2   /* ttt_linear_backward only: see there */
 };
 
 typedef struct {
@@ -169,6 +170,27 @@ ttt_status ttt_linear_decode_step(const ttt_params* p, int32_t pos,
                                   void* z, void* hip_stream);
 
 /*
+ * TTT-Linear forward scan for training: ttt_linear_forward (same arguments
+ * and results, bit for bit, on the one-workgroup launch) that also stores
+ * the base of every 16-token mini-batch -- the state the mini-batch's
+ * gradients are taken at, which the forward holds anyway -- into
+ * `workspace`, for a later ttt_linear_backward with TTT_BASES_SAVED.
+ *   workspace  as for ttt_linear_backward (at least
+ *              ttt_linear_backward_workspace_bytes(p) bytes, 256-byte
+ *              aligned, overlapping no other argument); its base region is
+ *              written, the rest untouched.
+ * Supported: mini_batch = 16 (else TTT_ERR_UNSUPPORTED).  Adds 16 KB of
+ * stores per unit and mini-batch to the forward.
+ */
+ttt_status ttt_linear_forward_save(const ttt_params* p,
+                                   const void* q, const void* k, const void* v,
+                                   const float* eta, const float* w0,
+                                   const float* ln_gamma, const float* ln_beta,
+                                   void* z, float* w_out,
+                                   void* workspace, uint64_t workspace_bytes,
+                                   void* hip_stream);
+
+/*
  * Bytes of device workspace that ttt_linear_backward needs for these
  * parameters: 16 KB per unit and 16-token mini-batch (the base of every
  * mini-batch), plus 16 KB + 512 bytes per unit, rounded up to 256 bytes
@@ -200,6 +222,11 @@ uint64_t ttt_linear_backward_workspace_bytes(const ttt_params* p);
  * Outputs and the workspace overlap no input and no other output
  * (TTT_ERR_ALIAS).  Supported: d = 64, mini_batch = 16 (else
  * TTT_ERR_UNSUPPORTED), both io dtypes, any flags.
+ * With TTT_BASES_SAVED in p->flags the workspace must hold the mini-batch
+ * bases that ttt_linear_forward_save stored for the same parameters (that
+ * flag aside) and inputs; the backward then skips replaying the forward
+ * recurrence.  The library cannot check this: stale bases give wrong
+ * gradients.
  * gfx950: two kernels on hip_stream.  One 256-thread workgroup per unit
  * first replays the forward recurrence and stores every mini-batch base in
  * the workspace, then walks the mini-batches in reverse (fp32 arithmetic);

@@ -13,10 +13,11 @@ LIB_PATH = os.path.join(PKG, "libttt_amd.so")
 TTT_OK, TTT_ERR_NULL, TTT_ERR_SHAPE, TTT_ERR_UNSUPPORTED = 0, 1, 2, 3
 TTT_ERR_ALIAS, TTT_ERR_DEVICE, TTT_ERR_ARG = 4, 5, 6
 TTT_F32, TTT_BF16 = 0, 1
-TTT_NO_LN, TTT_NO_RESIDUAL = 1, 2
+TTT_NO_LN, TTT_NO_RESIDUAL, TTT_BASES_SAVED = 1, 2, 4
 
 EXPORTS = ("ttt_linear_forward", "ttt_linear_split_workspace_bytes", "ttt_linear_forward_split",
-           "ttt_linear_decode_step", "ttt_linear_backward_workspace_bytes", "ttt_linear_backward",
+           "ttt_linear_decode_step", "ttt_linear_forward_save",
+           "ttt_linear_backward_workspace_bytes", "ttt_linear_backward",
            "ttt_mlp_forward", "ttt_status_string", "ttt_abi_version")
 
 
@@ -52,6 +53,9 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_forward_split.restype = ctypes.c_int
     L.ttt_linear_decode_step.argtypes = [ctypes.POINTER(TTTParams), ctypes.c_int32] + [P] * 10
     L.ttt_linear_decode_step.restype = ctypes.c_int
+    L.ttt_linear_forward_save.argtypes = ([ctypes.POINTER(TTTParams)] + [P] * 10 +
+                                          [ctypes.c_uint64, P])
+    L.ttt_linear_forward_save.restype = ctypes.c_int
     L.ttt_linear_backward_workspace_bytes.argtypes = [ctypes.POINTER(TTTParams)]
     L.ttt_linear_backward_workspace_bytes.restype = ctypes.c_uint64
     L.ttt_linear_backward.argtypes = ([ctypes.POINTER(TTTParams)] + [P] * 17 +

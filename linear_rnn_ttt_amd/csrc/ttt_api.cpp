@@ -128,6 +128,7 @@ ttt_status linear_args(const ttt_params* p, const void* q, const void* k, const 
   a->ws_g = nullptr;
   a->ws_flags = nullptr;
   a->split = 0;
+  a->bases = nullptr;
   return TTT_OK;
 }
 
@@ -270,6 +271,38 @@ ttt_status ttt_linear_decode_step(const ttt_params* p, int32_t pos, const void* 
   return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
 }
 
+ttt_status ttt_linear_forward_save(const ttt_params* p, const void* q, const void* k,
+                                   const void* v, const float* eta, const float* w0,
+                                   const float* ln_gamma, const float* ln_beta, void* z,
+                                   float* w_out, void* workspace, uint64_t workspace_bytes,
+                                   void* hip_stream) {
+  tttk::LinearArgs a;
+  const ttt_status st = linear_args(p, q, k, v, eta, w0, ln_gamma, ln_beta, z, w_out, nullptr,
+                                    0, &a);
+  if (st != TTT_OK) return st;
+  if (!workspace) return TTT_ERR_NULL;
+  if (p->mini_batch != 16) return TTT_ERR_UNSUPPORTED;
+  if (workspace_bytes < backward_layout(p).total) return TTT_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TTT_ERR_ARG;
+  uint64_t elems = 0;
+  check_common(p, &elems);
+  const uint64_t es = p->io_dtype == TTT_BF16 ? 2 : 4;
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t dd = static_cast<uint64_t>(kHeadDim) * kHeadDim;
+  const bool ln = !(p->flags & TTT_NO_LN);
+  const Range rws = span(workspace, workspace_bytes);
+  const Range all[] = {span(q, elems * es), span(k, elems * es), span(v, elems * es),
+                       span(eta, units * p->T * 4),
+                       span(w0, (p->state0_per_batch ? units : p->H) * dd * 4),
+                       span(ln ? ln_gamma : nullptr, p->H * 256ull),
+                       span(ln ? ln_beta : nullptr, p->H * 256ull), span(z, elems * es),
+                       span(w_out, units * dd * 4)};
+  for (const Range& r : all)
+    if (overlap(rws, r)) return TTT_ERR_ALIAS;
+  a.bases = static_cast<float*>(workspace);
+  return linear_launch(p, a, hip_stream);
+}
+
 uint64_t ttt_linear_backward_workspace_bytes(const ttt_params* p) {
   uint64_t elems = 0;
   if (check_common(p, &elems) != TTT_OK) return 0;
@@ -282,6 +315,12 @@ ttt_status ttt_linear_backward(const ttt_params* p, const void* q, const void* k
                                void* dq, void* dk, void* dv, float* deta, float* dw0,
                                float* dln_gamma, float* dln_beta, void* workspace,
                                uint64_t workspace_bytes, void* hip_stream) {
+  if (!p) return TTT_ERR_NULL;
+  // TTT_BASES_SAVED is this entry point's own flag; the rest are checked as usual
+  const bool saved = (p->flags & TTT_BASES_SAVED) != 0;
+  ttt_params pc = *p;
+  pc.flags &= ~static_cast<uint32_t>(TTT_BASES_SAVED);
+  p = &pc;
   uint64_t elems = 0;
   const ttt_status st = check_common(p, &elems);
   if (st != TTT_OK) return st;
@@ -342,6 +381,7 @@ ttt_status ttt_linear_backward(const ttt_params* p, const void* q, const void* k
   a.T = p->T;
   a.eps = p->ln_eps;
   a.state0_per_batch = p->state0_per_batch;
+  a.bases_saved = saved ? 1 : 0;
   const hipError_t e = tttk::launch_linear_backward(a, p->io_dtype == TTT_BF16, ln,
                                                     !(p->flags & TTT_NO_RESIDUAL),
                                                     static_cast<hipStream_t>(hip_stream));

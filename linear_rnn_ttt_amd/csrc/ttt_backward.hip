@@ -270,8 +270,8 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       F.v[j] = ld_io<BF16>(a.v, (row_unit + t0 + min(RO * w + j, nv - 1)) * DD + f);
   };
   Fetch F;
-  fetch1(0, F);
-  for (int ct = 0; ct < tiles; ++ct) {
+  if (!a.bases_saved) fetch1(0, F);
+  for (int ct = 0; ct < tiles && !a.bases_saved; ++ct) {
     const int t0 = ct * TB;
     const int nv = min(TB, T - t0);
     float* base = bases + static_cast<size_t>(ct) * DD * DD;

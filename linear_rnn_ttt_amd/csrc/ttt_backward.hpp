@@ -35,6 +35,7 @@ struct BackwardArgs {
   int32_t B, H, T;
   float eps;
   int32_t state0_per_batch;
+  int32_t bases_saved;      // the forward stored the bases already: no replay
 };
 
 // Two kernels on `stream`: the scan (one workgroup per unit) and the sums

@@ -29,6 +29,9 @@ struct LinearArgs {
   uint32_t* ws_g;
   uint32_t* ws_flags;
   int32_t split;
+  // When set (mini-batch 16): the base of every tile, [units][tiles][64][64],
+  // stored for the backward pass.
+  float* bases;
 };
 
 struct MlpArgs {

@@ -650,6 +650,14 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         if (LO) Wc[r] = mfma16(kt1[r].lo, hi_of(g1), Wc[r]);
       }
       split_state_mm(Ac, Wc, neg_ident);  // W_{p-1}
+      // with b = 16 this is the base of tile p: stored for the backward
+      if (a.bases && p < n) {
+        float* bp = a.bases + ((size_t)x.unit * n + p) * D * D;
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) bp[feat(r, 4 * g + i) * D + 16 * w + c] = Wc[r][i];
+      }
       if (!MB16 && mbs(p)) {
         Ab[0] = Ac[0];
         Ab[1] = Ac[1];

@@ -87,6 +87,7 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
                        state0_per_batch: bool = False, z: Optional[torch.Tensor] = None,
                        w_out: Optional[torch.Tensor] = None, return_state: bool = True,
                        split: Optional[bool] = None, workspace: Optional[torch.Tensor] = None,
+                       save_for_backward: Optional[torch.Tensor] = None,
                        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
     """TTT-Linear forward scan on the GPU; returns (z [B,H,T,d], W_final
     [B,H,d,d] fp32 or None).  See include/ttt.h for the semantics.
@@ -96,7 +97,13 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
     ttt_linear_forward; None decides by linear_uses_split.  The results are
     the same either way.  workspace: a uint8 GPU tensor of at
     least ttt_linear_split_workspace_bytes bytes to use instead of a fresh
-    one."""
+    one.
+
+    save_for_backward: a uint8 GPU tensor of at least
+    ttt_linear_backward_workspace_bytes bytes; the scan then runs as
+    ttt_linear_forward_save (one workgroup per unit, mini-batch 16) and
+    stores every mini-batch base there, for ttt_linear_backward(...,
+    workspace=that tensor, bases_saved=True)."""
     _dev_tensor("q", q)
     B, H, T, d = q.shape
     _dev_tensor("k", k, q.dtype, q.shape, device=q.device)
@@ -123,7 +130,13 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
     args = (ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), _ptr(ln_gamma),
             _ptr(ln_beta), _ptr(z), _ptr(w_out))
     with torch.cuda.device(q.device):   # the library launches on the current device
-        if split:
+        if save_for_backward is not None:
+            _dev_tensor("save_for_backward", save_for_backward, torch.uint8, device=q.device)
+            rc = _lib.lib().ttt_linear_forward_save(*args, _ptr(save_for_backward),
+                                                    save_for_backward.numel(),
+                                                    _stream(q, stream))
+            _lib.check("ttt_linear_forward_save", rc)
+        elif split:
             need = int(_lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(p)))
             if workspace is None:
                 workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
@@ -181,14 +194,17 @@ def ttt_linear_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: 
                         dw_final: Optional[torch.Tensor] = None, *, mini_batch: int = 16,
                         eps: float = 1e-6, layer_norm: bool = True, residual: bool = True,
                         state0_per_batch: bool = False, workspace: Optional[torch.Tensor] = None,
-                        stream=None) -> Tuple[torch.Tensor, ...]:
+                        bases_saved: bool = False, stream=None) -> Tuple[torch.Tensor, ...]:
     """Backward pass of the TTT-Linear scan for cotangents dz [B,H,T,d] (and
     dw_final [B,H,d,d] on the final state, or None); same inputs and options
     as ttt_linear_forward.  Returns (dq, dk, dv, deta, dw0, dln_gamma,
     dln_beta); dw0 has w0's shape (summed over the batch when w0 is shared),
     the LN gradients are [H,d] (zeros without LN).  workspace: a uint8 GPU
     tensor of at least ttt_linear_backward_workspace_bytes bytes to use
-    instead of a fresh one.  See include/ttt.h."""
+    instead of a fresh one.  bases_saved: the workspace holds the bases a
+    ttt_linear_forward(..., save_for_backward=workspace) call stored for
+    these inputs (TTT_BASES_SAVED): the backward skips replaying them.  See
+    include/ttt.h."""
     _dev_tensor("q", q)
     if q.dim() != 4:
         raise ValueError("q must be [B, H, T, d]")
@@ -213,6 +229,10 @@ def ttt_linear_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: 
     dbeta = torch.empty((H, d), dtype=torch.float32, device=dev)
     p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
     need = int(_lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p)))
+    if bases_saved:
+        if workspace is None:
+            raise ValueError("bases_saved needs the workspace the forward saved them in")
+        p.flags |= _lib.TTT_BASES_SAVED
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     _dev_tensor("workspace", workspace, torch.uint8, device=dev)

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 4
+    assert _lib.abi_version() == 5
     for code in range(7):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
@@ -230,3 +230,28 @@ def test_backward_rejects_bad_arguments():
     assert _backward(p, deta=_addr(8)) == _lib.TTT_ERR_ALIAS        # deta == dz
     assert _backward(p, ws=_addr(12)) == _lib.TTT_ERR_ALIAS         # workspace == dv
     assert _backward(p, dwT=_addr(14)) == _lib.TTT_ERR_ALIAS        # dw_final == dw0
+
+
+def test_forward_save_rejects_bad_arguments():
+    p = _params()
+    need = _lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p))
+    names = ["q", "k", "v", "eta", "w0", "g", "b", "z", "w_out"]
+
+    def call(p, ws=_addr(30), ws_bytes=need, **ptrs):
+        args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+        return _lib.lib().ttt_linear_forward_save(ctypes.byref(p) if p is not None else None,
+                                                  *args, ws, ws_bytes, None)
+    assert call(None) == _lib.TTT_ERR_NULL
+    assert call(p, ws=None) == _lib.TTT_ERR_NULL
+    assert call(p, ws_bytes=need - 1) == _lib.TTT_ERR_SHAPE
+    assert call(p, ws=ctypes.c_void_p(BASE + 30 * GAP + 16)) == _lib.TTT_ERR_ARG
+    assert call(_params(mini_batch=32)) == _lib.TTT_ERR_UNSUPPORTED
+    assert call(p, ws=_addr(8)) == _lib.TTT_ERR_ALIAS                  # workspace == z
+    assert call(p, z=_addr(1)) == _lib.TTT_ERR_ALIAS                   # z == q
+    assert call(_params(flags=_lib.TTT_BASES_SAVED)) == _lib.TTT_ERR_ARG   # backward's flag
+
+
+def test_backward_accepts_the_saved_bases_flag_only_there():
+    p = _params(flags=_lib.TTT_BASES_SAVED | _lib.TTT_NO_RESIDUAL, d=32)
+    assert _backward(p) == _lib.TTT_ERR_UNSUPPORTED       # flag accepted; d = 32 refused
+    assert _linear(_params(flags=_lib.TTT_BASES_SAVED)) == _lib.TTT_ERR_ARG

@@ -10,7 +10,8 @@ import numpy as np
 import pytest
 import torch
 
-from linear_rnn_ttt_amd import _lib, ttt_linear_backward
+import oracle
+from linear_rnn_ttt_amd import _lib, ttt_linear_backward, ttt_linear_forward
 from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs
 from oracle.backward import linear_backward
 
@@ -147,3 +148,94 @@ def test_backward_full_size_sampled_heads():
         print("head %d: %s" % (h, " ".join("%s %.1e" % kv for kv in e.items())), flush=True)
         for n, v in e.items():
             assert v <= TOL["bf16"], (h, n, v)
+
+
+@pytest.mark.parametrize("io,T", [("bf16", 77), ("f32", 50), ("bf16", 16)])
+def test_forward_save_is_the_forward_and_stores_the_bases(io, T):
+    """ttt_linear_forward_save: z and the final state bit for bit those of
+    the one-workgroup forward; the stored base of mini-batch c equals the
+    oracle's state after the first 16 c tokens."""
+    wl = BF if io == "bf16" else F32
+    B, H = 2, 2
+    inp = make_inputs(wl, B=B, H=H, T=T)
+    dev = {x: to_dev(inp[x], io if x in "qkv" else None) for x in inp}
+    args = (dev["q"], dev["k"], dev["v"], dev["eta"], dev["w0"], dev["gamma"], dev["beta"])
+    p = _lib.TTTParams(B, H, T, 64, 16, _lib.TTT_BF16 if io == "bf16" else _lib.TTT_F32, 0,
+                       1e-6, 0)
+    import ctypes
+    need = int(_lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p)))
+    ws = torch.zeros(need, dtype=torch.uint8, device="cuda")
+    z0, w0 = ttt_linear_forward(*args, split=False)
+    z1, w1 = ttt_linear_forward(*args, save_for_backward=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(z0, z1) and torch.equal(w0, w1)
+    tiles = (T + 15) // 16
+    bases = from_dev(ws[:B * H * tiles * 4096 * 4].view(torch.float32)).reshape(
+        B, H, tiles, 64, 64)
+    worst = 0.0
+    for c in range(tiles):
+        if c == 0:
+            ref = np.broadcast_to(inp["w0"].astype(np.float64), (B, H, 64, 64))
+        else:
+            cut = {x: inp[x][:, :, :16 * c] for x in ("q", "k", "v", "eta")}
+            _, ref = oracle.linear(cut["q"], cut["k"], cut["v"], cut["eta"], inp["w0"],
+                                   inp["gamma"], inp["beta"])
+        worst = max(worst, unit_err(bases[:, :, c], ref, (B, H)))
+    print("%s T=%d: bases err %.2e" % (io, T, worst), flush=True)
+    assert worst <= 1e-4
+
+
+@pytest.mark.parametrize("case", [("f32", F32, 50, {}), ("bf16", BF, 70, {}),
+                                  ("f32 no LN", F32, 33, dict(ln=False))],
+                         ids=lambda c: c[0])
+def test_backward_from_saved_bases_matches_the_oracle(case):
+    name, wl, T, kw = case
+    io = "bf16" if wl is BF else "f32"
+    ln = kw.get("ln", True)
+    B, H = 2, 3
+    inp = make_inputs(wl, B=B, H=H, T=T)
+    dz, dwT = cotangents(inp, io, seed=T + 5)
+    dev = {x: to_dev(inp[x], io if x in "qkv" else None) for x in inp}
+    args = (dev["q"], dev["k"], dev["v"], dev["eta"], dev["w0"], dev["gamma"], dev["beta"])
+    ws = torch.full((1 << 22,), 255, dtype=torch.uint8, device="cuda")
+    ttt_linear_forward(*args, layer_norm=ln, save_for_backward=ws)
+    out = ttt_linear_backward(*args, to_dev(dz, io), to_dev(dwT), layer_norm=ln, workspace=ws,
+                              bases_saved=True)
+    torch.cuda.synchronize()
+    got = dict(zip(NAMES, (from_dev(t) for t in out)))
+    want = linear_backward(inp["q"], inp["k"], inp["v"], inp["eta"], inp["w0"], inp["gamma"],
+                           inp["beta"], dz, dwT, layer_norm=ln)
+    e = errors(got, want, B, H)
+    print("%s: %s" % (name, " ".join("%s %.1e" % kv for kv in e.items())), flush=True)
+    for n, v in e.items():
+        if n in ("dgamma", "dbeta") and not ln:
+            continue
+        assert v <= TOL[io], (n, v)
+
+
+def test_backward_from_saved_bases_full_size_one_head():
+    """Forward with saved bases, then the backward without the replay, at
+    the 1.3B-layer workload; head 5 (all four batch entries) vs the oracle."""
+    wl = WORKLOADS["linear_1p3b_b4h32_t8k"]
+    inp = make_inputs(wl)
+    dz, _ = cotangents(inp, "bf16", seed=43, final=False)
+    dev = {x: to_dev(inp[x], "bf16" if x in "qkv" else None) for x in inp}
+    args = (dev["q"], dev["k"], dev["v"], dev["eta"], dev["w0"], dev["gamma"], dev["beta"])
+    import ctypes
+    p = _lib.TTTParams(4, 32, 8192, 64, 16, _lib.TTT_BF16, 0, 1e-6, 0)
+    ws = torch.empty(int(_lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p))),
+                     dtype=torch.uint8, device="cuda")
+    ttt_linear_forward(*args, save_for_backward=ws)
+    out = ttt_linear_backward(*args, to_dev(dz, "bf16"), workspace=ws, bases_saved=True)
+    torch.cuda.synchronize()
+    got = dict(zip(NAMES, (from_dev(t) for t in out)))
+    h, sl = 5, slice(5, 6)
+    want = linear_backward(inp["q"][:, sl], inp["k"][:, sl], inp["v"][:, sl], inp["eta"][:, sl],
+                           inp["w0"][sl], inp["gamma"][sl], inp["beta"][sl], dz[:, sl])
+    part = {n: (got[n][:, sl] if n in ("dq", "dk", "dv", "deta") else got[n][sl])
+            for n in NAMES}
+    e = errors(part, want, 4, 1)
+    print("head %d from saved bases: %s" % (h, " ".join("%s %.1e" % kv for kv in e.items())),
+          flush=True)
+    for n, v in e.items():
+        assert v <= TOL["bf16"], (n, v)
