@@ -84,6 +84,29 @@ __device__ __forceinline__ void st_io(void* p, size_t i, float x) {
   }
 }
 
+// Per-token outputs of one unit go through a buffer resource whose range
+// ends at the unit's last token: rows past T are dropped by the hardware, so
+// the stores need no branch (a store under a branch makes the compiler wait
+// for every outstanding memory operation at the loop head, the prefetch
+// loads' wait included).
+struct UnitOut {
+  __amdgpu_buffer_rsrc_t r;
+  __device__ __forceinline__ UnitOut(void* base, size_t first, uint32_t bytes) {
+    r = __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(base) + first, (short)0,
+                                          static_cast<int>(bytes), 0x00020000);
+  }
+};
+
+// Element (token row `row` of the unit, feature f) of a [.., 64] io output.
+template <bool BF16>
+__device__ __forceinline__ void store_row(const UnitOut& o, int row, int f, float x) {
+  if constexpr (BF16)
+    __builtin_amdgcn_raw_buffer_store_b16(static_cast<uint16_t>(pack_bf16(x, 0.f) & 0xffffu),
+                                          o.r, (row * DD + f) * 2, 0, 0);
+  else
+    __builtin_amdgcn_raw_buffer_store_b32(fbits(x), o.r, (row * DD + f) * 4, 0, 0);
+}
+
 // Tiles are fetched a mini-batch ahead into registers and stored to LDS
 // when they are due.  The loads are unconditional -- rows at or past the
 // last valid token re-read that token -- and the zero rows are made when
@@ -284,7 +307,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     float vr[RO];
 #pragma unroll
     for (int j = 0; j < RO; ++j) vr[j] = RO * w + j < nv ? F.v[j] : 0.f;
-    if (ct + 1 < tiles) fetch1(ct + 1, F);
+    fetch1(min(ct + 1, tiles - 1), F);   // unconditional: the last one re-reads a tile
     lds_barrier();
     {
       f32x4 h = f4(0.f, 0.f, 0.f, 0.f);
@@ -323,21 +346,27 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   __syncthreads();   // every base stored before any wave reads one back
 
   // ---- phase 2: the mini-batches in reverse ---------------------------------
+  constexpr uint32_t ES = BF16 ? 2 : 4;
+  const UnitOut o_dq(a.dq, row_unit * DD * ES, static_cast<uint32_t>(T) * DD * ES);
+  const UnitOut o_dk(a.dk, row_unit * DD * ES, static_cast<uint32_t>(T) * DD * ES);
+  const UnitOut o_dv(a.dv, row_unit * DD * ES, static_cast<uint32_t>(T) * DD * ES);
+  const UnitOut o_de(a.deta, row_unit * 4, static_cast<uint32_t>(T) * 4);
   // Aa[rt][i] = A[16 rt + 4g + i][col],  At[rt][i] = A[col][16 rt + 4g + i]
+  // from dw_final through a buffer resource of zero range when it is NULL
+  // (reads return zero): no branch around the loads
   f32x4 Aa[4], At[4];
-#pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    Aa[rt] = f4(0.f, 0.f, 0.f, 0.f);
-    At[rt] = f4(0.f, 0.f, 0.f, 0.f);
-  }
-  if (a.dw_final) {
-    const float* A0 = a.dw_final + static_cast<size_t>(unit) * DD * DD;
+  {
+    const float* A0 = a.dw_final ? a.dw_final + static_cast<size_t>(unit) * DD * DD : a.w0;
+    const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(A0), (short)0, a.dw_final ? DD * DD * 4 : 0, 0x00020000);
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Aa[rt][i] = A0[(16 * rt + 4 * g + i) * DD + col];
-        At[rt][i] = A0[col * DD + 16 * rt + 4 * g + i];
+        Aa[rt][i] = bitsf(__builtin_amdgcn_raw_buffer_load_b32(
+            ra, ((16 * rt + 4 * g + i) * DD + col) * 4, 0, 0));
+        At[rt][i] = bitsf(__builtin_amdgcn_raw_buffer_load_b32(
+            ra, (col * DD + 16 * rt + 4 * g + i) * 4, 0, 0));
       }
   }
   // tile ct's base, k, q, eta, v and dz rows, fetched while tile ct + 1
@@ -380,7 +409,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       vr[j] = ok[j] ? F.v[j] : 0.f;
       dzr[j] = ok[j] ? F.dz[j] : 0.f;
     }
-    if (ct > 0) fetch2(ct - 1, F);
+    fetch2(max(ct - 1, 0), F);   // unconditional: the last one re-reads a tile
     lds_barrier();  // B1: W, K, Q, eta
 
     // W and W^T column blocks (B operands), K W and Q W, the two Q/K Grams
@@ -525,7 +554,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         const float dq = L.t[0][i][f] + (RES ? dzr[j] : 0.f);
         ka[j] = L.t[1][i][f];
         ga[j] = L.t[2][i][f];
-        if (ok[j]) st_io<BF16>(a.dq, (row_unit + t0 + i) * DD + f, dq);
+        store_row<BF16>(o_dq, t0 + i, f, dq);
       }
       // deta_i = -KA_i . g_i and the backward of g_i for u = -eta_i KA_i
       float u[RO];
@@ -562,10 +591,10 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
           dgam += ok[j] ? 2.f * (2.f * gam * R.x[j] - R.t[j]) * da[j] : 0.f;
           dbet -= dt[j];
         }
-        if (f == 0) {
-#pragma unroll
-          for (int j = 0; j < RO; ++j)
-            if (ok[j]) a.deta[row_unit + t0 + RO * w + j] = -s[j];
+        {
+          const float de = f == 0 ? s[0] : f == 1 ? s[1] : f == 2 ? s[2] : s[3];
+          const int off = f < RO ? (t0 + RO * w + f) * 4 : 0x7ffffff0;   // others dropped
+          __builtin_amdgcn_raw_buffer_store_b32(fbits(-de), o_de.r, off, 0, 0);
         }
       } else {
         float s[RO];
@@ -577,16 +606,16 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
           dh[j] = ok[j] ? 2.f * u[j] : 0.f;
           dt[j] = ok[j] ? -2.f * u[j] : 0.f;
         }
-        if (f == 0) {
-#pragma unroll
-          for (int j = 0; j < RO; ++j)
-            if (ok[j]) a.deta[row_unit + t0 + RO * w + j] = -s[j];
+        {
+          const float de = f == 0 ? s[0] : f == 1 ? s[1] : f == 2 ? s[2] : s[3];
+          const int off = f < RO ? (t0 + RO * w + f) * 4 : 0x7ffffff0;   // others dropped
+          __builtin_amdgcn_raw_buffer_store_b32(fbits(-de), o_de.r, off, 0, 0);
         }
       }
 #pragma unroll
       for (int j = 0; j < RO; ++j) {
         const int i = RO * w + j;
-        if (ok[j]) st_io<BF16>(a.dv, (row_unit + t0 + i) * DD + f, dt[j]);
+        store_row<BF16>(o_dv, t0 + i, f, dt[j]);
         L.dh[i][f] = dh[j];
       }
     }
@@ -614,7 +643,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     for (int j = 0; j < RO; ++j) {
       const int i = RO * w + j;
       const float dk = L.t[0][i][f] - er[j] * ga[j] - (RES ? dt[j] : 0.f);
-      if (ok[j]) st_io<BF16>(a.dk, (row_unit + t0 + i) * DD + f, dk);
+      store_row<BF16>(o_dk, t0 + i, f, dk);
     }
   }
 
