@@ -47,7 +47,7 @@ namespace tttk {
 namespace {
 
 constexpr int DD = 64;         // head dimension
-constexpr int NW = 4;          // waves per unit
+constexpr int NW = 8;          // waves per unit (two per SIMD)
 constexpr int TB = 16;         // tokens per mini-batch tile
 constexpr int RO = TB / NW;    // token rows owned per wave
 constexpr int LS = 68;         // LDS row stride (floats): 16-byte rows, spread banks
@@ -142,8 +142,8 @@ __device__ __forceinline__ void put_fetched(float (*dst)[LS], int tid, uint4 u, 
 
 // What one mini-batch tile needs from global memory, per thread (raw).
 struct Fetch {
-  uint4 k, q;        // token-tile shares
-  float4 w[4];       // share of the stored base (phase 2)
+  uint4 k;           // token-tile share (k, or q for threads 256-511 in phase 2)
+  float4 w[2];       // share of the stored base (phase 2)
   float eta;         // eta of token tid % 16
   float v[4], dz[4];  // this wave's token rows, feature f
 };
@@ -259,10 +259,14 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   const int unit = blockIdx.x;
   const int head = unit % a.H;
   const int tid = threadIdx.x;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // column block of the products
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // waves 0-3 hold W and A (column block w), waves 4-7 W^T and A^T (column
+  // block w - 4); wave w shares its SIMD with wave w +- 4
+  const bool primal = w < 4;
+  const int cb = w & 3;
   const int f = tid & 63;                                   // feature of the token-row algebra
   const int g = f >> 4, c = f & 15;                         // matrix-unit lane coordinates
-  const int col = 16 * w + c;                               // this lane's product column
+  const int col = 16 * cb + c;                              // this lane's product column
   const int T = a.T;
   const int tiles = (T + TB - 1) / TB;
   const size_t row_unit = static_cast<size_t>(unit) * T;   // first token row of the unit
@@ -274,19 +278,24 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     gam = a.gamma[head * DD + f];
     bet = a.beta[head * DD + f];
   }
+  const int tq = tid & 255;              // share of a token tile (threads 0-255: k, 256-511: q)
 
   // ---- phase 1: the bases of every mini-batch ------------------------------
-  // Wacc[rt][i] = W[16 rt + 4g + i][col]
+  // Wacc[rt][i] = W[16 rt + 4g + i][col] (updated by the primal waves only;
+  // the base stores of the dual waves go to a zero-range resource)
   f32x4 Wacc[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
     for (int i = 0; i < 4; ++i) Wacc[rt][i] = w0[(16 * rt + 4 * g + i) * DD + col];
+  const __amdgpu_buffer_rsrc_t rbase = __builtin_amdgcn_make_buffer_rsrc(
+      bases, (short)0, primal ? static_cast<int>(static_cast<uint32_t>(tiles) * DD * DD * 4) : 0,
+      0x00020000);
   // tile ct's k, eta and v rows, fetched while tile ct - 1 computes
   auto fetch1 = [&](int ct, Fetch& F) {
     const int t0 = ct * TB;
     const int nv = min(TB, T - t0);
-    F.k = fetch_tile<BF16>(a.k, row_unit + t0, nv, tid);
+    F.k = fetch_tile<BF16>(a.k, row_unit + t0, nv, tq);
     F.eta = a.eta[row_unit + t0 + min(tid & 15, nv - 1)];
 #pragma unroll
     for (int j = 0; j < RO; ++j)
@@ -297,24 +306,25 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   for (int ct = 0; ct < tiles && !a.bases_saved; ++ct) {
     const int t0 = ct * TB;
     const int nv = min(TB, T - t0);
-    float* base = bases + static_cast<size_t>(ct) * DD * DD;
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) base[(16 * rt + 4 * g + i) * DD + col] = Wacc[rt][i];
-    put_fetched<BF16>(L.k, tid, F.k, nv);
+      for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_raw_buffer_store_b32(
+            fbits(Wacc[rt][i]), rbase, ((ct * DD + 16 * rt + 4 * g + i) * DD + col) * 4, 0, 0);
+    if (tid < 256) put_fetched<BF16>(L.k, tq, F.k, nv);
     if (tid < TB) L.eta[tid] = tid < nv ? F.eta : 0.f;
     float vr[RO];
 #pragma unroll
     for (int j = 0; j < RO; ++j) vr[j] = RO * w + j < nv ? F.v[j] : 0.f;
     fetch1(min(ct + 1, tiles - 1), F);   // unconditional: the last one re-reads a tile
     lds_barrier();
-    {
+    if (primal) {
       f32x4 h = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         h = mma3(row_frag(L.k, c, 16 * kt + 4 * g), split4(Wacc[kt]), h);
-      put_tile(L.t[0], g, c, 16 * w, h);
+      put_tile(L.t[0], g, c, 16 * cb, h);
     }
     lds_barrier();
     {
@@ -333,7 +343,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       }
     }
     lds_barrier();
-    {
+    if (primal) {
       // W[:, cols] += K^T (-eta G)[:, cols]; row tile rt of W takes the
       // A operand K^T[16 rt + c][4g + i] = K[4g + i][16 rt + c]
       const Split4 ug = col_frag(L.g, 4 * g, col);
@@ -351,10 +361,10 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   const UnitOut o_dk(a.dk, row_unit * DD * ES, static_cast<uint32_t>(T) * DD * ES);
   const UnitOut o_dv(a.dv, row_unit * DD * ES, static_cast<uint32_t>(T) * DD * ES);
   const UnitOut o_de(a.deta, row_unit * 4, static_cast<uint32_t>(T) * 4);
-  // Aa[rt][i] = A[16 rt + 4g + i][col],  At[rt][i] = A[col][16 rt + 4g + i]
-  // from dw_final through a buffer resource of zero range when it is NULL
-  // (reads return zero): no branch around the loads
-  f32x4 Aa[4], At[4];
+  // Am: the primal waves' A[16 rt + 4g + i][col], the dual waves'
+  // A^T[16 rt + 4g + i][col] = A[col][16 rt + 4g + i]; from dw_final through
+  // a buffer resource of zero range when it is NULL (reads return zero)
+  f32x4 Am[4];
   {
     const float* A0 = a.dw_final ? a.dw_final + static_cast<size_t>(unit) * DD * DD : a.w0;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
@@ -363,23 +373,23 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        Aa[rt][i] = bitsf(__builtin_amdgcn_raw_buffer_load_b32(
-            ra, ((16 * rt + 4 * g + i) * DD + col) * 4, 0, 0));
-        At[rt][i] = bitsf(__builtin_amdgcn_raw_buffer_load_b32(
-            ra, (col * DD + 16 * rt + 4 * g + i) * 4, 0, 0));
+        const int r = 16 * rt + 4 * g + i;
+        Am[rt][i] = bitsf(__builtin_amdgcn_raw_buffer_load_b32(
+            ra, (primal ? r * DD + col : col * DD + r) * 4, 0, 0));
       }
   }
-  // tile ct's base, k, q, eta, v and dz rows, fetched while tile ct + 1
-  // computes (float4 e of the base: row e / 16, columns 4 (e % 16) ..)
+  // tile ct's base, k (threads 0-255) or q (256-511), eta, v and dz rows,
+  // fetched while tile ct + 1 computes (float4 e of the base: row e / 16,
+  // columns 4 (e % 16) ..)
+  const void* kq = tid < 256 ? a.k : a.q;
   auto fetch2 = [&](int ct, Fetch& F) {
     const int t0 = ct * TB;
     const int nv = min(TB, T - t0);
     const float4* base =
         reinterpret_cast<const float4*>(bases + static_cast<size_t>(ct) * DD * DD);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) F.w[m] = base[tid + 256 * m];
-    F.k = fetch_tile<BF16>(a.k, row_unit + t0, nv, tid);
-    F.q = fetch_tile<BF16>(a.q, row_unit + t0, nv, tid);
+    for (int m = 0; m < 2; ++m) F.w[m] = base[tid + NW * 64 * m];
+    F.k = fetch_tile<BF16>(kq, row_unit + t0, nv, tq);
     F.eta = a.eta[row_unit + t0 + min(tid & 15, nv - 1)];
 #pragma unroll
     for (int j = 0; j < RO; ++j) {
@@ -394,12 +404,11 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     const int t0 = ct * TB;
     const int nv = min(TB, T - t0);
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int e = tid + 256 * m;
+    for (int m = 0; m < 2; ++m) {
+      const int e = tid + NW * 64 * m;
       *reinterpret_cast<float4*>(&L.w[e >> 4][4 * (e & 15)]) = F.w[m];
     }
-    put_fetched<BF16>(L.k, tid, F.k, nv);
-    put_fetched<BF16>(L.q, tid, F.q, nv);
+    put_fetched<BF16>(tid < 256 ? L.k : L.q, tq, F.k, nv);
     if (tid < TB) L.eta[tid] = tid < nv ? F.eta : 0.f;
     float vr[RO], dzr[RO];
     bool ok[RO];
@@ -412,26 +421,26 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     fetch2(max(ct - 1, 0), F);   // unconditional: the last one re-reads a tile
     lds_barrier();  // B1: W, K, Q, eta
 
-    // W and W^T column blocks (B operands), K W and Q W, the two Q/K Grams
-    Split4 Wb[4], Wt[4];
-#pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
-      Wb[kt] = col_frag(L.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
-      Wt[kt] = row_frag(L.w, col, 16 * kt + 4 * g);   // W^T[16kt + 4g + i][col]
-    }
+    // primal: K W (to the row algebra), Q W, and the two Q/K Grams; dual:
+    // its W^T column block (B operand) for DO W^T and DH W^T
     f32x4 qw = f4(0.f, 0.f, 0.f, 0.f), s1 = qw, s1t = qw;
-    {
+    Split4 Wt[4];
+    if (primal) {
       f32x4 h = qw;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
+        const Split4 wb = col_frag(L.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
         const Split4 kf = row_frag(L.k, c, 16 * kt + 4 * g);
         const Split4 qf = row_frag(L.q, c, 16 * kt + 4 * g);
-        h = mma3(kf, Wb[kt], h);
-        qw = mma3(qf, Wb[kt], qw);
+        h = mma3(kf, wb, h);
+        qw = mma3(qf, wb, qw);
         s1 = mma3(qf, kf, s1);     // s1[i]  = q_{4g+i} . k_c
         s1t = mma3(kf, qf, s1t);   // s1t[i] = k_{4g+i} . q_c
       }
-      put_tile(L.t[0], g, c, 16 * w, h);
+      put_tile(L.t[0], g, c, 16 * cb, h);
+    } else {
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) Wt[kt] = row_frag(L.w, col, 16 * kt + 4 * g);
     }
     float kr[RO], er[RO];
 #pragma unroll
@@ -457,7 +466,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
 
     // o = Q W - M1 G with M1[c][s] = eta_s (q_c . k_s) for s <= c, whose
     // A-layout entries (row c, column s = 4g + i) are s1t
-    {
+    if (primal) {
       float m[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -465,7 +474,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         m[i] = s <= c ? -L.eta[s] * s1t[i] : 0.f;
       }
       const f32x4 o = mma3(split4(f4(m[0], m[1], m[2], m[3])), col_frag(L.g, 4 * g, col), qw);
-      put_tile(L.t[1], g, c, 16 * w, o);
+      put_tile(L.t[1], g, c, 16 * cb, o);
     }
     lds_barrier();  // B4: o
 
@@ -509,39 +518,41 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
     lds_barrier();  // B5: DO
 
-    // dQ' = DO W^T - M2 K, KA = K A + U1 DO, GA = G A^T + U2 Q, with the
-    // DO/G Grams; M2, U1, U2 in A layout (row c, column s = 4g + i)
-    Split4 dOb, kb, qb;
-    {
-      f32x4 pdq = f4(0.f, 0.f, 0.f, 0.f), pka = pdq, pga = pdq, s2 = pdq, s2t = pdq;
+    // primal: KA = K A + U1 DO; dual: dQ' = DO W^T - M2 K and
+    // GA = G A^T + U2 Q with the DO/G Grams.  M2, U1, U2 in A layout (row c,
+    // column s = 4g + i).
+    if (primal) {
+      f32x4 pka = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        pka = mma3(row_frag(L.k, c, 16 * kt + 4 * g), split4(Am[kt]), pka);
+      float u1[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) u1[i] = 4 * g + i >= c ? s1[i] : 0.f;   // q_s . k_c, s >= c
+      pka = mma3(split4(f4(u1[0], u1[1], u1[2], u1[3])), col_frag(L.dO, 4 * g, col), pka);
+      put_tile(L.t[1], g, c, 16 * cb, pka);
+    } else {
+      f32x4 pdq = f4(0.f, 0.f, 0.f, 0.f), pga = pdq, s2 = pdq, s2t = pdq;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const Split4 df = row_frag(L.dO, c, 16 * kt + 4 * g);
         const Split4 gf = row_frag(L.g, c, 16 * kt + 4 * g);
-        const Split4 kf = row_frag(L.k, c, 16 * kt + 4 * g);
         pdq = mma3(df, Wt[kt], pdq);
-        pka = mma3(kf, split4(Aa[kt]), pka);
-        pga = mma3(gf, split4(At[kt]), pga);
+        pga = mma3(gf, split4(Am[kt]), pga);
         s2 = mma3(df, gf, s2);     // s2[i]  = do_{4g+i} . g_c
         s2t = mma3(gf, df, s2t);   // s2t[i] = g_{4g+i} . do_c
       }
-      float m2[4], u1[4], u2[4];
+      float m2[4], u2[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 4 * g + i;
         m2[i] = s <= c ? -L.eta[s] * s2t[i] : 0.f;   // -eta_s (do_c . g_s), s <= c
-        u1[i] = s >= c ? s1[i] : 0.f;                // q_s . k_c, s >= c
         u2[i] = s >= c ? s2[i] : 0.f;                // do_s . g_c, s >= c
       }
-      dOb = col_frag(L.dO, 4 * g, col);
-      kb = col_frag(L.k, 4 * g, col);
-      qb = col_frag(L.q, 4 * g, col);
-      pdq = mma3(split4(f4(m2[0], m2[1], m2[2], m2[3])), kb, pdq);
-      pka = mma3(split4(f4(u1[0], u1[1], u1[2], u1[3])), dOb, pka);
-      pga = mma3(split4(f4(u2[0], u2[1], u2[2], u2[3])), qb, pga);
-      put_tile(L.t[0], g, c, 16 * w, pdq);
-      put_tile(L.t[1], g, c, 16 * w, pka);
-      put_tile(L.t[2], g, c, 16 * w, pga);
+      pdq = mma3(split4(f4(m2[0], m2[1], m2[2], m2[3])), col_frag(L.k, 4 * g, col), pdq);
+      pga = mma3(split4(f4(u2[0], u2[1], u2[2], u2[3])), col_frag(L.q, 4 * g, col), pga);
+      put_tile(L.t[0], g, c, 16 * cb, pdq);
+      put_tile(L.t[2], g, c, 16 * cb, pga);
     }
     lds_barrier();  // B6: dQ', KA, GA
 
@@ -557,7 +568,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         store_row<BF16>(o_dq, t0 + i, f, dq);
       }
       // deta_i = -KA_i . g_i and the backward of g_i for u = -eta_i KA_i
-      float u[RO];
+      float u[RO], de[RO];
 #pragma unroll
       for (int j = 0; j < RO; ++j) u[j] = -er[j] * ka[j];
       if constexpr (LN) {
@@ -573,6 +584,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         float dx[RO], da[RO], s2[2 * RO];
 #pragma unroll
         for (int j = 0; j < RO; ++j) {
+          de[j] = -s[j];
           const float mu_u = s[2 * RO + j] * INV_D, mux = s[3 * RO + j] * INV_D;
           da[j] = R.rho[j] * (u[j] - mu_u - R.x[j] * mux);
           dx[j] = -R.rho[j] * (R.mx[j] * u[j] + R.a[j] * mux) + 2.f * gam * gam * da[j];
@@ -591,11 +603,6 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
           dgam += ok[j] ? 2.f * (2.f * gam * R.x[j] - R.t[j]) * da[j] : 0.f;
           dbet -= dt[j];
         }
-        {
-          const float de = f == 0 ? s[0] : f == 1 ? s[1] : f == 2 ? s[2] : s[3];
-          const int off = f < RO ? (t0 + RO * w + f) * 4 : 0x7ffffff0;   // others dropped
-          __builtin_amdgcn_raw_buffer_store_b32(fbits(-de), o_de.r, off, 0, 0);
-        }
       } else {
         float s[RO];
 #pragma unroll
@@ -603,14 +610,16 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         wave_sums(s);
 #pragma unroll
         for (int j = 0; j < RO; ++j) {
+          de[j] = -s[j];
           dh[j] = ok[j] ? 2.f * u[j] : 0.f;
           dt[j] = ok[j] ? -2.f * u[j] : 0.f;
         }
-        {
-          const float de = f == 0 ? s[0] : f == 1 ? s[1] : f == 2 ? s[2] : s[3];
-          const int off = f < RO ? (t0 + RO * w + f) * 4 : 0x7ffffff0;   // others dropped
-          __builtin_amdgcn_raw_buffer_store_b32(fbits(-de), o_de.r, off, 0, 0);
-        }
+      }
+      {
+        // lanes 0 .. RO-1 store this wave's rows (the others are dropped)
+        const int off = f < RO ? (t0 + RO * w + f) * 4 : 0x7ffffff0;
+        __builtin_amdgcn_raw_buffer_store_b32(fbits(f == 0 ? de[0] : de[RO - 1]), o_de.r, off,
+                                              0, 0);
       }
 #pragma unroll
       for (int j = 0; j < RO; ++j) {
@@ -621,21 +630,26 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
     lds_barrier();  // B7: DH
 
-    {
-      // DH W^T, then A += Q^T DO + K^T DH and A^T += DO^T Q + DH^T K; the
-      // A operand of row tile rt of X^T is X[4g + i][16 rt + c]
+    if (primal) {
+      // A += Q^T DO + K^T DH; the A operand of row tile rt of X^T is
+      // X[4g + i][16 rt + c]
+      const Split4 dob = col_frag(L.dO, 4 * g, col), dhb = col_frag(L.dh, 4 * g, col);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        Am[rt] = mma3(col_frag(L.q, 4 * g, 16 * rt + c), dob, Am[rt]);
+        Am[rt] = mma3(col_frag(L.k, 4 * g, 16 * rt + c), dhb, Am[rt]);
+      }
+    } else {
+      // DH W^T, and A^T += DO^T Q + DH^T K
       f32x4 pdk = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) pdk = mma3(row_frag(L.dh, c, 16 * kt + 4 * g), Wt[kt], pdk);
-      put_tile(L.t[0], g, c, 16 * w, pdk);
-      const Split4 dhb = col_frag(L.dh, 4 * g, col);
+      put_tile(L.t[0], g, c, 16 * cb, pdk);
+      const Split4 qb = col_frag(L.q, 4 * g, col), kb = col_frag(L.k, 4 * g, col);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        const int fc = 16 * rt + c;
-        Aa[rt] = mma3(col_frag(L.q, 4 * g, fc), dOb, Aa[rt]);
-        Aa[rt] = mma3(col_frag(L.k, 4 * g, fc), dhb, Aa[rt]);
-        At[rt] = mma3(col_frag(L.dO, 4 * g, fc), qb, At[rt]);
-        At[rt] = mma3(col_frag(L.dh, 4 * g, fc), kb, At[rt]);
+        Am[rt] = mma3(col_frag(L.dO, 4 * g, 16 * rt + c), qb, Am[rt]);
+        Am[rt] = mma3(col_frag(L.dh, 4 * g, 16 * rt + c), kb, Am[rt]);
       }
     }
     lds_barrier();  // B8: DH W^T; every tile read done
@@ -648,18 +662,26 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   }
 
   // ---- dW0 of this unit and its LN-parameter partial sums --------------------
-  float* dst = (a.state0_per_batch ? a.dw0 : a.ws_dw0) + static_cast<size_t>(unit) * DD * DD;
+  if (primal) {
+    float* dst = (a.state0_per_batch ? a.dw0 : a.ws_dw0) + static_cast<size_t>(unit) * DD * DD;
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt)
+    for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g + i) * DD + col] = Aa[rt][i];
+      for (int i = 0; i < 4; ++i) dst[(16 * rt + 4 * g + i) * DD + col] = Am[rt][i];
+  }
   L.dln[0][w][f] = dgam;
   L.dln[1][w][f] = dbet;
   lds_barrier();
   if (w == 0) {
+    float sg = 0.f, sb = 0.f;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) {
+      sg += L.dln[0][v][f];
+      sb += L.dln[1][v][f];
+    }
     float* p = a.ws_dln + static_cast<size_t>(unit) * 2 * DD;
-    p[f] = (L.dln[0][0][f] + L.dln[0][1][f]) + (L.dln[0][2][f] + L.dln[0][3][f]);
-    p[DD + f] = (L.dln[1][0][f] + L.dln[1][1][f]) + (L.dln[1][2][f] + L.dln[1][3][f]);
+    p[f] = sg;
+    p[DD + f] = sb;
   }
 }
 
