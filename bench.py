@@ -51,6 +51,8 @@ KERNEL_SOURCES = {
 KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k",
                "backward": "ttt_linear_bwd_k"}
 BACKWARD_METRIC = "TTT-Linear backward tokens/s at 1.3B shape T=8k; % fp32 ALU roofline"
+TRAIN_METRIC = ("TTT-Linear training step (forward saving the bases + backward) tokens/s at "
+                "1.3B shape T=8k; % fp32 ALU roofline of the backward")
 FP32_VECTOR_PEAK_TFS = 157.3   # MI355X fp32 vector (packed); non-packed FMA issue is half
 DECODE_METRIC = ("TTT-Linear streaming step tokens/s (one token per (batch, head) unit per "
                  "launch); % HBM roofline")
@@ -450,7 +452,12 @@ def run_backward(args) -> dict:
     (cotangent dz seeded N(0, 1) in the io dtype, no cotangent on the final
     state, as in a language model), inputs and a preallocated workspace
     resident in HBM.  The launch time is the event time of the call on its
-    stream (the scan kernel and the small batch-sum kernel)."""
+    stream (the scan kernel and the small batch-sum kernel).
+
+    With --train a step is the training step instead: the forward that
+    stores the mini-batch bases (ttt_linear_forward_save, z and W_T written)
+    and the backward from those bases (TTT_BASES_SAVED); the roofline is the
+    backward call's, timed with events around it inside the step."""
     import numpy as np
     import torch
 
@@ -473,23 +480,35 @@ def run_backward(args) -> dict:
     args_ = (dev["q"], dev["k"], dev["v"], dev["eta"], dev["w0"], dev["gamma"], dev["beta"],
              dz_dev)
 
-    def step():
-        return ttt_linear_backward(*args_, mini_batch=w.mini_batch, eps=w.eps, workspace=ws)
+    train = bool(getattr(args, "train", False))
+    from linear_rnn_ttt_amd import ttt_linear_forward
+    z = torch.empty_like(dev["q"])
+    w_T = torch.empty((w.B, w.H, w.d, w.d), dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step(s_=None, e_=None):
+        if train:
+            ttt_linear_forward(*args_[:7], mini_batch=w.mini_batch, eps=w.eps, z=z, w_out=w_T,
+                               save_for_backward=ws)
+        if s_ is not None:
+            s_.record(stream)
+        out = ttt_linear_backward(*args_, mini_batch=w.mini_batch, eps=w.eps, workspace=ws,
+                                  bases_saved=train)
+        if e_ is not None:
+            e_.record(stream)
+        return out
 
     for _ in range(args.warmup):
         out = step()
     torch.cuda.synchronize()
     if args.copy_calibration:
         copy_calibration()
-    stream = torch.cuda.current_stream()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s_, e_ in ev:
-        s_.record(stream)
-        out = step()
-        e_.record(stream)
+        out = step(s_, e_)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     avg_launch_s = sum(s_.elapsed_time(e_) for s_, e_ in ev) / len(ev) / 1e3
@@ -497,7 +516,7 @@ def run_backward(args) -> dict:
     alg = backward_alg(w)
     tflops = alg["flops"] / avg_launch_s / 1e12
     res = {
-        "metric": BACKWARD_METRIC,
+        "metric": TRAIN_METRIC if train else BACKWARD_METRIC,
         "value": round(w.tokens / (ms_per_step / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -507,17 +526,21 @@ def run_backward(args) -> dict:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "bf16",   # matrix-unit products on bf16 hi/lo splits, fp32 accumulation
         "data": "synthetic",
-        "config": {"workload": w.name + "_backward", "inner_model": "TTT-Linear", "B": w.B,
+        "config": {"workload": w.name + ("_train_step" if train else "_backward"),
+                   "inner_model": "TTT-Linear", "B": w.B,
                    "H": w.H, "T": w.T, "d": w.d, "mini_batch": w.mini_batch, "io": w.io,
                    "parallelism": "none (1 GPU)",
-                   "launch": "ttt_linear_backward: one 256-thread workgroup per (batch, head) "
-                             "unit, fp32 VALU arithmetic, mini-batch bases in a workspace"},
+                   "launch": ("ttt_linear_forward_save (one 768-thread workgroup per unit) + "
+                              if train else "") +
+                             "ttt_linear_backward: one 512-thread workgroup per (batch, head) "
+                             "unit, bf16 hi/lo matrix-unit products, mini-batch bases in a "
+                             "workspace" + (" stored by the forward" if train else "")},
         "roofline": {"bound": "alu", "achieved": round(tflops, 3),
                      "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tflops / FP32_VECTOR_PEAK_TFS, 5),
-                     "traffic": read_traffic("backward", w.name),
+                     "traffic": read_traffic("backward", w.name + ("_train" if train else "")),
                      "kernel": KERNEL_NAME["backward"],
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4),
                      "algorithmic_flops_per_launch": alg["flops"],
@@ -584,7 +607,7 @@ def _profiled(args):
     if args.backward:
         w = WORKLOADS[args.workload]
         alg = backward_alg(w)
-        return "backward", w.name, alg["bytes"], alg["flops"]
+        return "backward", w.name + ("_train" if args.train else ""), alg["bytes"], alg["flops"]
     w = WORKLOADS[args.workload]
     alg = algorithmic(w)
     return w.kind, w.name, alg["bytes"], alg["flops"]
@@ -668,6 +691,8 @@ def main(argv=None):
                     help="time the TTT-Linear streaming step instead of the scan")
     ap.add_argument("--backward", action="store_true",
                     help="time the TTT-Linear backward pass instead of the forward scan")
+    ap.add_argument("--train", action="store_true",
+                    help="with --backward: time forward (saving the bases) + backward")
     ap.add_argument("--batch", type=int, default=0,
                     help="streams for --decode (default: the workload's batch)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
