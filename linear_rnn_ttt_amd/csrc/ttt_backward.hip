@@ -53,15 +53,20 @@ constexpr int RO = TB / NW;    // token rows owned per wave
 constexpr int LS = 68;         // LDS row stride (floats): 16-byte rows, spread banks
 constexpr float INV_D = 1.0f / DD;
 
-struct __attribute__((aligned(16))) BwdLds {
+// One mini-batch's tiles in LDS (two in flight in phase 2).
+struct __attribute__((aligned(16))) TileBuf {
   float k[TB][LS];
   float q[TB][LS];
   float g[TB][LS];
   float dO[TB][LS];
   float dh[TB][LS];
-  float w[DD][LS];            // the base of the current mini-batch
+  float w[DD][LS];            // the mini-batch's base
   float t[3][TB][LS];         // product tiles on their way to the token-row algebra
   float eta[TB];
+};
+
+struct __attribute__((aligned(16))) BwdLds {
+  TileBuf b[2];
   float dln[2][NW][DD];
 };
 
@@ -212,6 +217,17 @@ struct Inner {
   float x[RO], rho[RO], t[RO], a[RO], ma[RO], mx[RO], g[RO];
 };
 
+// One mini-batch's per-wave registers between its phase-2 steps.
+struct TileRegs {
+  int t0, nv;
+  bool ok[RO];
+  float vr[RO], dzr[RO], kr[RO], er[RO];
+  f32x4 qw, s1, s1t;   // primal waves
+  Split4 Wt[4];        // dual waves
+  Inner R;
+  float ga[RO], dt[RO];
+};
+
 template <bool LN, bool RES>
 __device__ __forceinline__ void inner_grad(const float (&h)[RO], const float (&vr)[RO],
                                            const float (&kr)[RO], float gam, float bet,
@@ -312,8 +328,8 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       for (int i = 0; i < 4; ++i)
         __builtin_amdgcn_raw_buffer_store_b32(
             fbits(Wacc[rt][i]), rbase, ((ct * DD + 16 * rt + 4 * g + i) * DD + col) * 4, 0, 0);
-    if (tid < 256) put_fetched<BF16>(L.k, tq, F.k, nv);
-    if (tid < TB) L.eta[tid] = tid < nv ? F.eta : 0.f;
+    if (tid < 256) put_fetched<BF16>(L.b[0].k, tq, F.k, nv);
+    if (tid < TB) L.b[0].eta[tid] = tid < nv ? F.eta : 0.f;
     float vr[RO];
 #pragma unroll
     for (int j = 0; j < RO; ++j) vr[j] = RO * w + j < nv ? F.v[j] : 0.f;
@@ -323,39 +339,48 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       f32x4 h = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        h = mma3(row_frag(L.k, c, 16 * kt + 4 * g), split4(Wacc[kt]), h);
-      put_tile(L.t[0], g, c, 16 * cb, h);
+        h = mma3(row_frag(L.b[0].k, c, 16 * kt + 4 * g), split4(Wacc[kt]), h);
+      put_tile(L.b[0].t[0], g, c, 16 * cb, h);
     }
     lds_barrier();
     {
       float h[RO], kr[RO];
 #pragma unroll
       for (int j = 0; j < RO; ++j) {
-        h[j] = L.t[0][RO * w + j][f];
-        kr[j] = L.k[RO * w + j][f];
+        h[j] = L.b[0].t[0][RO * w + j][f];
+        kr[j] = L.b[0].k[RO * w + j][f];
       }
       Inner R;
       inner_grad<LN, RES>(h, vr, kr, gam, bet, a.eps, R);
 #pragma unroll
       for (int j = 0; j < RO; ++j) {
         const int i = RO * w + j;
-        L.g[i][f] = i < nv ? -L.eta[i] * R.g[j] : 0.f;   // -eta g: the update's right factor
+        L.b[0].g[i][f] = i < nv ? -L.b[0].eta[i] * R.g[j] : 0.f;   // -eta g: the update's right factor
       }
     }
     lds_barrier();
     if (primal) {
       // W[:, cols] += K^T (-eta G)[:, cols]; row tile rt of W takes the
       // A operand K^T[16 rt + c][4g + i] = K[4g + i][16 rt + c]
-      const Split4 ug = col_frag(L.g, 4 * g, col);
+      const Split4 ug = col_frag(L.b[0].g, 4 * g, col);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-        Wacc[rt] = mma3(col_frag(L.k, 4 * g, 16 * rt + c), ug, Wacc[rt]);
+        Wacc[rt] = mma3(col_frag(L.b[0].k, 4 * g, 16 * rt + c), ug, Wacc[rt]);
     }
     lds_barrier();
   }
   __syncthreads();   // every base stored before any wave reads one back
 
-  // ---- phase 2: the mini-batches in reverse ---------------------------------
+  // ---- phase 2: the mini-batches in reverse, two in flight ------------------
+  // Only part of a mini-batch's work needs A, the adjoint carried between
+  // mini-batches (K A, G A^T, the LN-gradient backward, the A update, dK);
+  // the front part of the next (earlier) mini-batch -- its loads, K W, Q W,
+  // the Grams and both LNs -- does not.  Each barrier interval pairs a
+  // token-row step of one mini-batch with a matrix-unit step of the other,
+  // in separate LDS buffers:
+  //   I1: back S5(c)  + front S0(c-1)      I2: back S6(c) + front S1(c-1)
+  //   I3: back S7(c)  + front S2(c-1)      I4: back S8(c) + front S3(c-1)
+  //   I5: front S4(c-1)
   constexpr uint32_t ES = BF16 ? 2 : 4;
   const UnitOut o_dq(a.dq, row_unit * DD * ES, static_cast<uint32_t>(T) * DD * ES);
   const UnitOut o_dk(a.dk, row_unit * DD * ES, static_cast<uint32_t>(T) * DD * ES);
@@ -379,8 +404,8 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       }
   }
   // tile ct's base, k (threads 0-255) or q (256-511), eta, v and dz rows,
-  // fetched while tile ct + 1 computes (float4 e of the base: row e / 16,
-  // columns 4 (e % 16) ..)
+  // fetched two stages ahead (float4 e of the base: row e / 16, columns
+  // 4 (e % 16) ..)
   const void* kq = tid < 256 ? a.k : a.q;
   auto fetch2 = [&](int ct, Fetch& F) {
     const int t0 = ct * TB;
@@ -399,145 +424,141 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
   };
   float dgam = 0.f, dbet = 0.f;
-  fetch2(tiles - 1, F);
-  for (int ct = tiles - 1; ct >= 0; --ct) {
-    const int t0 = ct * TB;
-    const int nv = min(TB, T - t0);
+
+  // S0: the prefetched tile ct into buffer X, its rows into S; fetch ct - 1
+  auto S0 = [&](int ct, TileBuf& X, TileRegs& S) {
+    S.t0 = ct * TB;
+    S.nv = min(TB, T - S.t0);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int e = tid + NW * 64 * m;
-      *reinterpret_cast<float4*>(&L.w[e >> 4][4 * (e & 15)]) = F.w[m];
+      *reinterpret_cast<float4*>(&X.w[e >> 4][4 * (e & 15)]) = F.w[m];
     }
-    put_fetched<BF16>(tid < 256 ? L.k : L.q, tq, F.k, nv);
-    if (tid < TB) L.eta[tid] = tid < nv ? F.eta : 0.f;
-    float vr[RO], dzr[RO];
-    bool ok[RO];
+    put_fetched<BF16>(tid < 256 ? X.k : X.q, tq, F.k, S.nv);
+    if (tid < TB) X.eta[tid] = tid < S.nv ? F.eta : 0.f;
 #pragma unroll
     for (int j = 0; j < RO; ++j) {
-      ok[j] = RO * w + j < nv;
-      vr[j] = ok[j] ? F.v[j] : 0.f;
-      dzr[j] = ok[j] ? F.dz[j] : 0.f;
+      S.ok[j] = RO * w + j < S.nv;
+      S.vr[j] = S.ok[j] ? F.v[j] : 0.f;
+      S.dzr[j] = S.ok[j] ? F.dz[j] : 0.f;
     }
     fetch2(max(ct - 1, 0), F);   // unconditional: the last one re-reads a tile
-    lds_barrier();  // B1: W, K, Q, eta
-
-    // primal: K W (to the row algebra), Q W, and the two Q/K Grams; dual:
-    // its W^T column block (B operand) for DO W^T and DH W^T
-    f32x4 qw = f4(0.f, 0.f, 0.f, 0.f), s1 = qw, s1t = qw;
-    Split4 Wt[4];
+  };
+  // S1: primal: K W (to the row algebra), Q W, the two Q/K Grams; dual: its
+  // W^T column block (B operand) for DO W^T and DH W^T
+  auto S1 = [&](TileBuf& X, TileRegs& S) {
     if (primal) {
-      f32x4 h = qw;
+      f32x4 h = f4(0.f, 0.f, 0.f, 0.f);
+      S.qw = h;
+      S.s1 = h;
+      S.s1t = h;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const Split4 wb = col_frag(L.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
-        const Split4 kf = row_frag(L.k, c, 16 * kt + 4 * g);
-        const Split4 qf = row_frag(L.q, c, 16 * kt + 4 * g);
+        const Split4 wb = col_frag(X.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
+        const Split4 kf = row_frag(X.k, c, 16 * kt + 4 * g);
+        const Split4 qf = row_frag(X.q, c, 16 * kt + 4 * g);
         h = mma3(kf, wb, h);
-        qw = mma3(qf, wb, qw);
-        s1 = mma3(qf, kf, s1);     // s1[i]  = q_{4g+i} . k_c
-        s1t = mma3(kf, qf, s1t);   // s1t[i] = k_{4g+i} . q_c
+        S.qw = mma3(qf, wb, S.qw);
+        S.s1 = mma3(qf, kf, S.s1);     // s1[i]  = q_{4g+i} . k_c
+        S.s1t = mma3(kf, qf, S.s1t);   // s1t[i] = k_{4g+i} . q_c
       }
-      put_tile(L.t[0], g, c, 16 * cb, h);
+      put_tile(X.t[0], g, c, 16 * cb, h);
     } else {
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt) Wt[kt] = row_frag(L.w, col, 16 * kt + 4 * g);
-    }
-    float kr[RO], er[RO];
-#pragma unroll
-    for (int j = 0; j < RO; ++j) {
-      kr[j] = L.k[RO * w + j][f];
-      er[j] = L.eta[RO * w + j];
-    }
-    lds_barrier();  // B2: K W
-
-    Inner R;
-    {
-      float h[RO];
-#pragma unroll
-      for (int j = 0; j < RO; ++j) h[j] = L.t[0][RO * w + j][f];
-      inner_grad<LN, RES>(h, vr, kr, gam, bet, a.eps, R);
+      for (int kt = 0; kt < 4; ++kt) S.Wt[kt] = row_frag(X.w, col, 16 * kt + 4 * g);
     }
 #pragma unroll
     for (int j = 0; j < RO; ++j) {
-      R.g[j] = ok[j] ? R.g[j] : 0.f;
-      L.g[RO * w + j][f] = R.g[j];
+      S.kr[j] = X.k[RO * w + j][f];
+      S.er[j] = X.eta[RO * w + j];
     }
-    lds_barrier();  // B3: G
-
-    // o = Q W - M1 G with M1[c][s] = eta_s (q_c . k_s) for s <= c, whose
-    // A-layout entries (row c, column s = 4g + i) are s1t
+  };
+  // S2: the inner LN gradient G on this wave's rows
+  auto S2 = [&](TileBuf& X, TileRegs& S) {
+    float h[RO];
+#pragma unroll
+    for (int j = 0; j < RO; ++j) h[j] = X.t[0][RO * w + j][f];
+    inner_grad<LN, RES>(h, S.vr, S.kr, gam, bet, a.eps, S.R);
+#pragma unroll
+    for (int j = 0; j < RO; ++j) {
+      S.R.g[j] = S.ok[j] ? S.R.g[j] : 0.f;
+      X.g[RO * w + j][f] = S.R.g[j];
+    }
+  };
+  // S3: o = Q W - M1 G with M1[c][s] = eta_s (q_c . k_s) for s <= c, whose
+  // A-layout entries (row c, column s = 4g + i) are s1t
+  auto S3 = [&](TileBuf& X, TileRegs& S) {
     if (primal) {
       float m[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 4 * g + i;
-        m[i] = s <= c ? -L.eta[s] * s1t[i] : 0.f;
+        m[i] = s <= c ? -X.eta[s] * S.s1t[i] : 0.f;
       }
-      const f32x4 o = mma3(split4(f4(m[0], m[1], m[2], m[3])), col_frag(L.g, 4 * g, col), qw);
-      put_tile(L.t[1], g, c, 16 * cb, o);
+      const f32x4 o =
+          mma3(split4(f4(m[0], m[1], m[2], m[3])), col_frag(X.g, 4 * g, col), S.qw);
+      put_tile(X.t[1], g, c, 16 * cb, o);
     }
-    lds_barrier();  // B4: o
-
-    // output LN backward on this wave's rows
-    {
-      float dO[RO];
-      if constexpr (LN) {
-        float o[RO], s[RO], xc[RO];
+  };
+  // S4: the output LN backward on this wave's rows
+  auto S4 = [&](TileBuf& X, TileRegs& S) {
+    float dO[RO];
+    if constexpr (LN) {
+      float o[RO], s[RO], xc[RO];
 #pragma unroll
-        for (int j = 0; j < RO; ++j) s[j] = o[j] = L.t[1][RO * w + j][f];
-        wave_sums(s);
+      for (int j = 0; j < RO; ++j) s[j] = o[j] = X.t[1][RO * w + j][f];
+      wave_sums(s);
 #pragma unroll
-        for (int j = 0; j < RO; ++j) {
-          xc[j] = o[j] - s[j] * INV_D;
-          s[j] = xc[j] * xc[j];
-        }
-        wave_sums(s);
-        float xo[RO], dx[RO], s2[2 * RO], rho_o[RO];
-#pragma unroll
-        for (int j = 0; j < RO; ++j) {
-          rho_o[j] = 1.0f / __builtin_sqrtf(s[j] * INV_D + a.eps);
-          xo[j] = xc[j] * rho_o[j];
-          dx[j] = gam * dzr[j];
-          s2[j] = dx[j];
-          s2[RO + j] = dx[j] * xo[j];
-          dgam += ok[j] ? dzr[j] * xo[j] : 0.f;
-          dbet += dzr[j];
-        }
-        wave_sums(s2);
-#pragma unroll
-        for (int j = 0; j < RO; ++j) {
-          const float d = rho_o[j] * (dx[j] - s2[j] * INV_D - xo[j] * (s2[RO + j] * INV_D));
-          dO[j] = ok[j] ? d : 0.f;
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < RO; ++j) dO[j] = dzr[j];
+      for (int j = 0; j < RO; ++j) {
+        xc[j] = o[j] - s[j] * INV_D;
+        s[j] = xc[j] * xc[j];
       }
+      wave_sums(s);
+      float xo[RO], dx[RO], s2[2 * RO], rho_o[RO];
 #pragma unroll
-      for (int j = 0; j < RO; ++j) L.dO[RO * w + j][f] = dO[j];
+      for (int j = 0; j < RO; ++j) {
+        rho_o[j] = 1.0f / __builtin_sqrtf(s[j] * INV_D + a.eps);
+        xo[j] = xc[j] * rho_o[j];
+        dx[j] = gam * S.dzr[j];
+        s2[j] = dx[j];
+        s2[RO + j] = dx[j] * xo[j];
+        dgam += S.ok[j] ? S.dzr[j] * xo[j] : 0.f;
+        dbet += S.dzr[j];
+      }
+      wave_sums(s2);
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        const float d = rho_o[j] * (dx[j] - s2[j] * INV_D - xo[j] * (s2[RO + j] * INV_D));
+        dO[j] = S.ok[j] ? d : 0.f;
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < RO; ++j) dO[j] = S.dzr[j];
     }
-    lds_barrier();  // B5: DO
-
-    // primal: KA = K A + U1 DO; dual: dQ' = DO W^T - M2 K and
-    // GA = G A^T + U2 Q with the DO/G Grams.  M2, U1, U2 in A layout (row c,
-    // column s = 4g + i).
+#pragma unroll
+    for (int j = 0; j < RO; ++j) X.dO[RO * w + j][f] = dO[j];
+  };
+  // S5: primal: KA = K A + U1 DO; dual: dQ' = DO W^T - M2 K and
+  // GA = G A^T + U2 Q with the DO/G Grams.  M2, U1, U2 in A layout (row c,
+  // column s = 4g + i).
+  auto S5 = [&](TileBuf& X, TileRegs& S) {
     if (primal) {
       f32x4 pka = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        pka = mma3(row_frag(L.k, c, 16 * kt + 4 * g), split4(Am[kt]), pka);
+        pka = mma3(row_frag(X.k, c, 16 * kt + 4 * g), split4(Am[kt]), pka);
       float u1[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) u1[i] = 4 * g + i >= c ? s1[i] : 0.f;   // q_s . k_c, s >= c
-      pka = mma3(split4(f4(u1[0], u1[1], u1[2], u1[3])), col_frag(L.dO, 4 * g, col), pka);
-      put_tile(L.t[1], g, c, 16 * cb, pka);
+      for (int i = 0; i < 4; ++i) u1[i] = 4 * g + i >= c ? S.s1[i] : 0.f;   // q_s . k_c, s >= c
+      pka = mma3(split4(f4(u1[0], u1[1], u1[2], u1[3])), col_frag(X.dO, 4 * g, col), pka);
+      put_tile(X.t[1], g, c, 16 * cb, pka);
     } else {
       f32x4 pdq = f4(0.f, 0.f, 0.f, 0.f), pga = pdq, s2 = pdq, s2t = pdq;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const Split4 df = row_frag(L.dO, c, 16 * kt + 4 * g);
-        const Split4 gf = row_frag(L.g, c, 16 * kt + 4 * g);
-        pdq = mma3(df, Wt[kt], pdq);
+        const Split4 df = row_frag(X.dO, c, 16 * kt + 4 * g);
+        const Split4 gf = row_frag(X.g, c, 16 * kt + 4 * g);
+        pdq = mma3(df, S.Wt[kt], pdq);
         pga = mma3(gf, split4(Am[kt]), pga);
         s2 = mma3(df, gf, s2);     // s2[i]  = do_{4g+i} . g_c
         s2t = mma3(gf, df, s2t);   // s2t[i] = g_{4g+i} . do_c
@@ -546,119 +567,168 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int s = 4 * g + i;
-        m2[i] = s <= c ? -L.eta[s] * s2t[i] : 0.f;   // -eta_s (do_c . g_s), s <= c
+        m2[i] = s <= c ? -X.eta[s] * s2t[i] : 0.f;   // -eta_s (do_c . g_s), s <= c
         u2[i] = s >= c ? s2[i] : 0.f;                // do_s . g_c, s >= c
       }
-      pdq = mma3(split4(f4(m2[0], m2[1], m2[2], m2[3])), col_frag(L.k, 4 * g, col), pdq);
-      pga = mma3(split4(f4(u2[0], u2[1], u2[2], u2[3])), col_frag(L.q, 4 * g, col), pga);
-      put_tile(L.t[0], g, c, 16 * cb, pdq);
-      put_tile(L.t[2], g, c, 16 * cb, pga);
+      pdq = mma3(split4(f4(m2[0], m2[1], m2[2], m2[3])), col_frag(X.k, 4 * g, col), pdq);
+      pga = mma3(split4(f4(u2[0], u2[1], u2[2], u2[3])), col_frag(X.q, 4 * g, col), pga);
+      put_tile(X.t[0], g, c, 16 * cb, pdq);
+      put_tile(X.t[2], g, c, 16 * cb, pga);
     }
-    lds_barrier();  // B6: dQ', KA, GA
-
-    float ga[RO], dt[RO];
-    {
-      float ka[RO], dh[RO];
-#pragma unroll
-      for (int j = 0; j < RO; ++j) {
-        const int i = RO * w + j;
-        const float dq = L.t[0][i][f] + (RES ? dzr[j] : 0.f);
-        ka[j] = L.t[1][i][f];
-        ga[j] = L.t[2][i][f];
-        store_row<BF16>(o_dq, t0 + i, f, dq);
-      }
-      // deta_i = -KA_i . g_i and the backward of g_i for u = -eta_i KA_i
-      float u[RO], de[RO];
-#pragma unroll
-      for (int j = 0; j < RO; ++j) u[j] = -er[j] * ka[j];
-      if constexpr (LN) {
-        float s[4 * RO];
-#pragma unroll
-        for (int j = 0; j < RO; ++j) {
-          s[j] = ka[j] * R.g[j];
-          s[RO + j] = u[j] * (R.a[j] - R.ma[j] - R.x[j] * R.mx[j]);
-          s[2 * RO + j] = u[j];
-          s[3 * RO + j] = u[j] * R.x[j];
-        }
-        wave_sums(s);
-        float dx[RO], da[RO], s2[2 * RO];
-#pragma unroll
-        for (int j = 0; j < RO; ++j) {
-          de[j] = -s[j];
-          const float mu_u = s[2 * RO + j] * INV_D, mux = s[3 * RO + j] * INV_D;
-          da[j] = R.rho[j] * (u[j] - mu_u - R.x[j] * mux);
-          dx[j] = -R.rho[j] * (R.mx[j] * u[j] + R.a[j] * mux) + 2.f * gam * gam * da[j];
-          dt[j] = -2.f * gam * da[j];
-          s2[j] = dx[j];
-          s2[RO + j] = dx[j] * R.x[j];
-        }
-        wave_sums(s2);
-#pragma unroll
-        for (int j = 0; j < RO; ++j) {
-          const float drho = s[RO + j];
-          const float d = R.rho[j] * (dx[j] - s2[j] * INV_D - R.x[j] * (s2[RO + j] * INV_D)) -
-                          drho * R.rho[j] * R.rho[j] * R.x[j] * INV_D;
-          dh[j] = ok[j] ? d : 0.f;
-          dt[j] = ok[j] ? dt[j] : 0.f;
-          dgam += ok[j] ? 2.f * (2.f * gam * R.x[j] - R.t[j]) * da[j] : 0.f;
-          dbet -= dt[j];
-        }
-      } else {
-        float s[RO];
-#pragma unroll
-        for (int j = 0; j < RO; ++j) s[j] = ka[j] * R.g[j];
-        wave_sums(s);
-#pragma unroll
-        for (int j = 0; j < RO; ++j) {
-          de[j] = -s[j];
-          dh[j] = ok[j] ? 2.f * u[j] : 0.f;
-          dt[j] = ok[j] ? -2.f * u[j] : 0.f;
-        }
-      }
-      {
-        // lanes 0 .. RO-1 store this wave's rows (the others are dropped)
-        const int off = f < RO ? (t0 + RO * w + f) * 4 : 0x7ffffff0;
-        __builtin_amdgcn_raw_buffer_store_b32(fbits(f == 0 ? de[0] : de[RO - 1]), o_de.r, off,
-                                              0, 0);
-      }
-#pragma unroll
-      for (int j = 0; j < RO; ++j) {
-        const int i = RO * w + j;
-        store_row<BF16>(o_dv, t0 + i, f, dt[j]);
-        L.dh[i][f] = dh[j];
-      }
-    }
-    lds_barrier();  // B7: DH
-
-    if (primal) {
-      // A += Q^T DO + K^T DH; the A operand of row tile rt of X^T is
-      // X[4g + i][16 rt + c]
-      const Split4 dob = col_frag(L.dO, 4 * g, col), dhb = col_frag(L.dh, 4 * g, col);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        Am[rt] = mma3(col_frag(L.q, 4 * g, 16 * rt + c), dob, Am[rt]);
-        Am[rt] = mma3(col_frag(L.k, 4 * g, 16 * rt + c), dhb, Am[rt]);
-      }
-    } else {
-      // DH W^T, and A^T += DO^T Q + DH^T K
-      f32x4 pdk = f4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int kt = 0; kt < 4; ++kt) pdk = mma3(row_frag(L.dh, c, 16 * kt + 4 * g), Wt[kt], pdk);
-      put_tile(L.t[0], g, c, 16 * cb, pdk);
-      const Split4 qb = col_frag(L.q, 4 * g, col), kb = col_frag(L.k, 4 * g, col);
-#pragma unroll
-      for (int rt = 0; rt < 4; ++rt) {
-        Am[rt] = mma3(col_frag(L.dO, 4 * g, 16 * rt + c), qb, Am[rt]);
-        Am[rt] = mma3(col_frag(L.dh, 4 * g, 16 * rt + c), kb, Am[rt]);
-      }
-    }
-    lds_barrier();  // B8: DH W^T; every tile read done
+  };
+  // S6: dq, deta and the LN-gradient backward on this wave's rows: DH, dv
+  auto S6 = [&](TileBuf& X, TileRegs& S) {
+    const int t0 = S.t0;
+    float ka[RO], dh[RO];
 #pragma unroll
     for (int j = 0; j < RO; ++j) {
       const int i = RO * w + j;
-      const float dk = L.t[0][i][f] - er[j] * ga[j] - (RES ? dt[j] : 0.f);
-      store_row<BF16>(o_dk, t0 + i, f, dk);
+      const float dq = X.t[0][i][f] + (RES ? S.dzr[j] : 0.f);
+      ka[j] = X.t[1][i][f];
+      S.ga[j] = X.t[2][i][f];
+      store_row<BF16>(o_dq, t0 + i, f, dq);
     }
+    // deta_i = -KA_i . g_i and the backward of g_i for u = -eta_i KA_i
+    float u[RO], de[RO];
+#pragma unroll
+    for (int j = 0; j < RO; ++j) u[j] = -S.er[j] * ka[j];
+    const Inner& R = S.R;
+    if constexpr (LN) {
+      float s[4 * RO];
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        s[j] = ka[j] * R.g[j];
+        s[RO + j] = u[j] * (R.a[j] - R.ma[j] - R.x[j] * R.mx[j]);
+        s[2 * RO + j] = u[j];
+        s[3 * RO + j] = u[j] * R.x[j];
+      }
+      wave_sums(s);
+      float dx[RO], da[RO], s2[2 * RO];
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        de[j] = -s[j];
+        const float mu_u = s[2 * RO + j] * INV_D, mux = s[3 * RO + j] * INV_D;
+        da[j] = R.rho[j] * (u[j] - mu_u - R.x[j] * mux);
+        dx[j] = -R.rho[j] * (R.mx[j] * u[j] + R.a[j] * mux) + 2.f * gam * gam * da[j];
+        S.dt[j] = -2.f * gam * da[j];
+        s2[j] = dx[j];
+        s2[RO + j] = dx[j] * R.x[j];
+      }
+      wave_sums(s2);
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        const float drho = s[RO + j];
+        const float d = R.rho[j] * (dx[j] - s2[j] * INV_D - R.x[j] * (s2[RO + j] * INV_D)) -
+                        drho * R.rho[j] * R.rho[j] * R.x[j] * INV_D;
+        dh[j] = S.ok[j] ? d : 0.f;
+        S.dt[j] = S.ok[j] ? S.dt[j] : 0.f;
+        dgam += S.ok[j] ? 2.f * (2.f * gam * R.x[j] - R.t[j]) * da[j] : 0.f;
+        dbet -= S.dt[j];
+      }
+    } else {
+      float s[RO];
+#pragma unroll
+      for (int j = 0; j < RO; ++j) s[j] = ka[j] * R.g[j];
+      wave_sums(s);
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        de[j] = -s[j];
+        dh[j] = S.ok[j] ? 2.f * u[j] : 0.f;
+        S.dt[j] = S.ok[j] ? -2.f * u[j] : 0.f;
+      }
+    }
+    {
+      // lanes 0 .. RO-1 store this wave's rows (the others are dropped)
+      const int off = f < RO ? (t0 + RO * w + f) * 4 : 0x7ffffff0;
+      __builtin_amdgcn_raw_buffer_store_b32(fbits(f == 0 ? de[0] : de[RO - 1]), o_de.r, off, 0,
+                                            0);
+    }
+#pragma unroll
+    for (int j = 0; j < RO; ++j) {
+      const int i = RO * w + j;
+      store_row<BF16>(o_dv, t0 + i, f, S.dt[j]);
+      X.dh[i][f] = dh[j];
+    }
+  };
+  // S7: primal: A += Q^T DO + K^T DH; dual: DH W^T, and A^T += DO^T Q +
+  // DH^T K.  The A operand of row tile rt of X^T is X[4g + i][16 rt + c].
+  auto S7 = [&](TileBuf& X, TileRegs& S) {
+    if (primal) {
+      const Split4 dob = col_frag(X.dO, 4 * g, col), dhb = col_frag(X.dh, 4 * g, col);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        Am[rt] = mma3(col_frag(X.q, 4 * g, 16 * rt + c), dob, Am[rt]);
+        Am[rt] = mma3(col_frag(X.k, 4 * g, 16 * rt + c), dhb, Am[rt]);
+      }
+    } else {
+      f32x4 pdk = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        pdk = mma3(row_frag(X.dh, c, 16 * kt + 4 * g), S.Wt[kt], pdk);
+      put_tile(X.t[0], g, c, 16 * cb, pdk);
+      const Split4 qb = col_frag(X.q, 4 * g, col), kb = col_frag(X.k, 4 * g, col);
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        Am[rt] = mma3(col_frag(X.dO, 4 * g, 16 * rt + c), qb, Am[rt]);
+        Am[rt] = mma3(col_frag(X.dh, 4 * g, 16 * rt + c), kb, Am[rt]);
+      }
+    }
+  };
+  // S8: dk on this wave's rows
+  auto S8 = [&](TileBuf& X, TileRegs& S) {
+#pragma unroll
+    for (int j = 0; j < RO; ++j) {
+      const int i = RO * w + j;
+      const float dk = X.t[0][i][f] - S.er[j] * S.ga[j] - (RES ? S.dt[j] : 0.f);
+      store_row<BF16>(o_dk, S.t0 + i, f, dk);
+    }
+  };
+
+  TileRegs Sb, Sf;
+  fetch2(tiles - 1, F);
+  {
+    // prologue: the front half of the last mini-batch
+    TileBuf& X = L.b[(tiles - 1) & 1];
+    S0(tiles - 1, X, Sb);
+    lds_barrier();
+    S1(X, Sb);
+    lds_barrier();
+    S2(X, Sb);
+    lds_barrier();
+    S3(X, Sb);
+    lds_barrier();
+    S4(X, Sb);
+    lds_barrier();
+  }
+  for (int ct = tiles - 1; ct >= 1; --ct) {
+    TileBuf& Xb = L.b[ct & 1];         // the back half of mini-batch ct
+    TileBuf& Xf = L.b[(ct - 1) & 1];   // the front half of mini-batch ct - 1
+    S5(Xb, Sb);
+    S0(ct - 1, Xf, Sf);
+    lds_barrier();  // I1
+    S6(Xb, Sb);
+    S1(Xf, Sf);
+    lds_barrier();  // I2
+    S7(Xb, Sb);
+    S2(Xf, Sf);
+    lds_barrier();  // I3
+    S8(Xb, Sb);
+    S3(Xf, Sf);
+    lds_barrier();  // I4
+    S4(Xf, Sf);
+    lds_barrier();  // I5
+    Sb = Sf;
+  }
+  {
+    // epilogue: the back half of the first mini-batch
+    TileBuf& X = L.b[0];
+    S5(X, Sb);
+    lds_barrier();
+    S6(X, Sb);
+    lds_barrier();
+    S7(X, Sb);
+    lds_barrier();
+    S8(X, Sb);
   }
 
   // ---- dW0 of this unit and its LN-parameter partial sums --------------------
