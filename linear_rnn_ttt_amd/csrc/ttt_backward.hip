@@ -30,7 +30,8 @@
 // base in the workspace (16 KB per mini-batch: the device has room for every
 // base, so nothing is recomputed); phase 2 walks the mini-batches in reverse.
 // Every product is a 16x16x16 bf16 matrix-unit chain on hi/lo splits of
-// both fp32 operands (hi*hi + hi*lo + lo*hi, about 16 significant bits),
+// both fp32 operands (hi*hi + hi*lo + lo*hi, about 16 significant bits;
+// the bf16 input rows k and q are exact in bf16 and enter as hi only),
 // accumulated in fp32: wave w forms output columns 16w..16w+15 of each
 // token-tile product and holds columns 16w.. of W, W^T, A and A^T (A and A^T
 // as fp32 accumulators, updated in place).  The 16x16 Gram tiles are formed
@@ -161,23 +162,44 @@ __device__ __forceinline__ f32x4 f4(float a, float b, float c, float d) {
   return f32x4{a, b, c, d};
 }
 
-// D += A B with both operands given as hi/lo bf16 splits.
-__device__ __forceinline__ f32x4 mma3(const Split4& a, const Split4& b, f32x4 d) {
-  d = mfma16(a.lo, b.hi, d);
-  d = mfma16(a.hi, b.lo, d);
+// D += A B with both operands given as hi/lo bf16 splits.  An operand that
+// is exact in bf16 (AX / BX: the bf16 input rows k and q) has a zero lo part,
+// so its hi*lo products are skipped -- the same sums, fewer instructions.
+template <bool AX = false, bool BX = false>
+__device__ __forceinline__ f32x4 mma(const Split4& a, const Split4& b, f32x4 d) {
+  if constexpr (!AX) d = mfma16(a.lo, b.hi, d);
+  if constexpr (!BX) d = mfma16(a.hi, b.lo, d);
   return mfma16(a.hi, b.hi, d);
+}
+__device__ __forceinline__ f32x4 mma3(const Split4& a, const Split4& b, f32x4 d) {
+  return mma<false, false>(a, b, d);
+}
+
+// Four fp32 values as an operand: hi/lo split, or hi only when exact in bf16.
+template <bool EXACT>
+__device__ __forceinline__ Split4 frag4(f32x4 x) {
+  if constexpr (EXACT) {
+    Split4 r;
+    r.hi = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+    r.lo = u32x2{0u, 0u};
+    return r;
+  } else {
+    return split4(x);
+  }
 }
 
 // Row fragment: X[c][col0 .. col0+3] (A operand of X, or B operand of X^T).
+template <bool EXACT = false>
 __device__ __forceinline__ Split4 row_frag(const float (*X)[LS], int c, int col0) {
   const float4 x = *reinterpret_cast<const float4*>(&X[c][col0]);
-  return split4(f4(x.x, x.y, x.z, x.w));
+  return frag4<EXACT>(f4(x.x, x.y, x.z, x.w));
 }
 
 // Column fragment: X[r0 + i][col] for i = 0..3 (B operand of X, or A
 // operand of X^T).
+template <bool EXACT = false>
 __device__ __forceinline__ Split4 col_frag(const float (*X)[LS], int r0, int col) {
-  return split4(f4(X[r0][col], X[r0 + 1][col], X[r0 + 2][col], X[r0 + 3][col]));
+  return frag4<EXACT>(f4(X[r0][col], X[r0 + 1][col], X[r0 + 2][col], X[r0 + 3][col]));
 }
 
 // Store an accumulator tile D[4g + i][c] at rows 0..15, columns col0 + c.
@@ -339,7 +361,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       f32x4 h = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        h = mma3(row_frag(L.b[0].k, c, 16 * kt + 4 * g), split4(Wacc[kt]), h);
+        h = mma<BF16, false>(row_frag<BF16>(L.b[0].k, c, 16 * kt + 4 * g), split4(Wacc[kt]), h);
       put_tile(L.b[0].t[0], g, c, 16 * cb, h);
     }
     lds_barrier();
@@ -365,7 +387,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       const Split4 ug = col_frag(L.b[0].g, 4 * g, col);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-        Wacc[rt] = mma3(col_frag(L.b[0].k, 4 * g, 16 * rt + c), ug, Wacc[rt]);
+        Wacc[rt] = mma<BF16, false>(col_frag<BF16>(L.b[0].k, 4 * g, 16 * rt + c), ug, Wacc[rt]);
     }
     lds_barrier();
   }
@@ -455,12 +477,12 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const Split4 wb = col_frag(X.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
-        const Split4 kf = row_frag(X.k, c, 16 * kt + 4 * g);
-        const Split4 qf = row_frag(X.q, c, 16 * kt + 4 * g);
-        h = mma3(kf, wb, h);
-        S.qw = mma3(qf, wb, S.qw);
-        S.s1 = mma3(qf, kf, S.s1);     // s1[i]  = q_{4g+i} . k_c
-        S.s1t = mma3(kf, qf, S.s1t);   // s1t[i] = k_{4g+i} . q_c
+        const Split4 kf = row_frag<BF16>(X.k, c, 16 * kt + 4 * g);
+        const Split4 qf = row_frag<BF16>(X.q, c, 16 * kt + 4 * g);
+        h = mma<BF16, false>(kf, wb, h);
+        S.qw = mma<BF16, false>(qf, wb, S.qw);
+        S.s1 = mma<BF16, BF16>(qf, kf, S.s1);     // s1[i]  = q_{4g+i} . k_c
+        S.s1t = mma<BF16, BF16>(kf, qf, S.s1t);   // s1t[i] = k_{4g+i} . q_c
       }
       put_tile(X.t[0], g, c, 16 * cb, h);
     } else {
@@ -546,7 +568,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       f32x4 pka = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        pka = mma3(row_frag(X.k, c, 16 * kt + 4 * g), split4(Am[kt]), pka);
+        pka = mma<BF16, false>(row_frag<BF16>(X.k, c, 16 * kt + 4 * g), split4(Am[kt]), pka);
       float u1[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) u1[i] = 4 * g + i >= c ? S.s1[i] : 0.f;   // q_s . k_c, s >= c
@@ -570,8 +592,10 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         m2[i] = s <= c ? -X.eta[s] * s2t[i] : 0.f;   // -eta_s (do_c . g_s), s <= c
         u2[i] = s >= c ? s2[i] : 0.f;                // do_s . g_c, s >= c
       }
-      pdq = mma3(split4(f4(m2[0], m2[1], m2[2], m2[3])), col_frag(X.k, 4 * g, col), pdq);
-      pga = mma3(split4(f4(u2[0], u2[1], u2[2], u2[3])), col_frag(X.q, 4 * g, col), pga);
+      pdq = mma<false, BF16>(split4(f4(m2[0], m2[1], m2[2], m2[3])),
+                             col_frag<BF16>(X.k, 4 * g, col), pdq);
+      pga = mma<false, BF16>(split4(f4(u2[0], u2[1], u2[2], u2[3])),
+                             col_frag<BF16>(X.q, 4 * g, col), pga);
       put_tile(X.t[0], g, c, 16 * cb, pdq);
       put_tile(X.t[2], g, c, 16 * cb, pga);
     }
@@ -657,8 +681,8 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       const Split4 dob = col_frag(X.dO, 4 * g, col), dhb = col_frag(X.dh, 4 * g, col);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        Am[rt] = mma3(col_frag(X.q, 4 * g, 16 * rt + c), dob, Am[rt]);
-        Am[rt] = mma3(col_frag(X.k, 4 * g, 16 * rt + c), dhb, Am[rt]);
+        Am[rt] = mma<BF16, false>(col_frag<BF16>(X.q, 4 * g, 16 * rt + c), dob, Am[rt]);
+        Am[rt] = mma<BF16, false>(col_frag<BF16>(X.k, 4 * g, 16 * rt + c), dhb, Am[rt]);
       }
     } else {
       f32x4 pdk = f4(0.f, 0.f, 0.f, 0.f);
@@ -666,11 +690,11 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       for (int kt = 0; kt < 4; ++kt)
         pdk = mma3(row_frag(X.dh, c, 16 * kt + 4 * g), S.Wt[kt], pdk);
       put_tile(X.t[0], g, c, 16 * cb, pdk);
-      const Split4 qb = col_frag(X.q, 4 * g, col), kb = col_frag(X.k, 4 * g, col);
+      const Split4 qb = col_frag<BF16>(X.q, 4 * g, col), kb = col_frag<BF16>(X.k, 4 * g, col);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        Am[rt] = mma3(col_frag(X.dO, 4 * g, 16 * rt + c), qb, Am[rt]);
-        Am[rt] = mma3(col_frag(X.dh, 4 * g, 16 * rt + c), kb, Am[rt]);
+        Am[rt] = mma<false, BF16>(col_frag(X.dO, 4 * g, 16 * rt + c), qb, Am[rt]);
+        Am[rt] = mma<false, BF16>(col_frag(X.dh, 4 * g, 16 * rt + c), kb, Am[rt]);
       }
     }
   };
