@@ -196,7 +196,7 @@ def cpu_baseline(w, inp, budget_s: float):
               "all %d units, first %d of %d tokens each" % (units, T_s, w.T))
     return {"value": round(w.B * T_s / dt, 1), "unit": "tokens/s", "cores": cores,
             "kind": "oracle", "sample": sample + ", median of %d runs of %.2f s wall, fp64"
-            % (len(times), dt)}
+            % (len(times), dt), **host_info()}
 
 
 def copy_calibration():
@@ -210,6 +210,55 @@ def copy_calibration():
     dst.copy_(src)
     torch.cuda.synchronize()
     del src, dst
+
+
+def host_info() -> dict:
+    """The host the CPU baseline ran on: logical CPUs and the CPU model."""
+    model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"nproc": os.cpu_count(), "cpu_model": model}
+
+
+def side_measurements(step, stream, n: int = 5) -> dict:
+    """Measurements beside the timed steps (not part of `value`):
+    - cold launches: a 512 MB buffer is written before each launch (outside
+      the launch's events), so the 256 MB MALL holds none of the inputs;
+    - the achievable HBM bandwidth of a plain 1 GiB device-to-device copy,
+      a second denominator beside the 8 TB/s peak."""
+    import torch
+
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+    cold = []
+    for _ in range(n):
+        flush.fill_(1)
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record(stream)
+        step()
+        e_.record(stream)
+        torch.cuda.synchronize()
+        cold.append(s_.elapsed_time(e_))
+    del flush
+    src = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_.record(stream)
+    for _ in range(n):
+        dst.copy_(src)
+    e_.record(stream)
+    torch.cuda.synchronize()
+    copy_gbs = 2 * COPY_BYTES * n / (s_.elapsed_time(e_) / 1e3) / 1e9   # read + write
+    del src, dst
+    cold.sort()
+    return {"cold_median_launch_ms": round(cold[len(cold) // 2], 4),
+            "hbm_copy_gbs": round(copy_gbs, 1)}
 
 
 def run(args) -> dict:
@@ -242,6 +291,8 @@ def run(args) -> dict:
     wall = time.perf_counter() - t0
     launch_ms = [s.elapsed_time(e) for s, e in ev]
     avg_launch_s = sum(launch_ms) / len(launch_ms) / 1e3
+    median_launch_ms = sorted(launch_ms)[len(launch_ms) // 2]
+    side = side_measurements(step, stream)
     ms_per_step = wall / args.steps * 1e3
     ok = bool(torch.isfinite(z.float()).all().item())
 
@@ -249,22 +300,32 @@ def run(args) -> dict:
     if w.kind == "linear":
         achieved = alg["bytes"] / avg_launch_s / 1e9
         traffic = read_traffic(w.kind, w.name)
+        cold_gbs = alg["bytes"] / (side["cold_median_launch_ms"] / 1e3) / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5), "traffic": traffic,
                 "kernel": KERNEL_NAME[w.kind], "avg_launch_ms": round(avg_launch_s * 1e3, 4),
-                "algorithmic_bytes_per_launch": alg["bytes"]}
+                "median_launch_ms": round(median_launch_ms, 4),
+                "algorithmic_bytes_per_launch": alg["bytes"],
+                "cold_median_launch_ms": side["cold_median_launch_ms"],
+                "cold_frac": round(cold_gbs / HBM_PEAK_GBS, 5),
+                "hbm_copy_gbs": side["hbm_copy_gbs"],
+                "frac_of_copy": round(achieved / side["hbm_copy_gbs"], 5)}
     else:
         achieved = alg["flops"] / avg_launch_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 3), "peak": BF16_MFMA_PEAK_TFS,
                 "unit": "TFLOP/s", "frac": round(achieved / BF16_MFMA_PEAK_TFS, 5),
                 "traffic": read_traffic(w.kind, w.name), "kernel": KERNEL_NAME[w.kind],
                 "avg_launch_ms": round(avg_launch_s * 1e3, 4),
-                "algorithmic_flops_per_launch": alg["flops"]}
+                "median_launch_ms": round(median_launch_ms, 4),
+                "algorithmic_flops_per_launch": alg["flops"],
+                "cold_median_launch_ms": side["cold_median_launch_ms"],
+                "hbm_copy_gbs": side["hbm_copy_gbs"]}
 
     out = {
         "metric": METRIC,
         "value": round(w.B * w.T / (ms_per_step / 1e3), 1),
         "unit": "tokens/s",
+        "token_heads_per_s": round(w.B * w.H * w.T / (ms_per_step / 1e3), 1),
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -587,13 +648,60 @@ def _db(d: str):
     return sqlite3.connect(sorted(files)[-1])
 
 
-def _counter_per_dispatch(d, counter):
-    """[(kernel name, dispatch id, value)] for one counter (summed over the
-    counter's instances within a dispatch)."""
+def _counter_per_dispatch(d, counter, reduce="sum"):
+    """[(kernel name, dispatch id, value)] for one counter (summed, or the
+    maximum, over the counter's instances within a dispatch)."""
     con = _db(d)
     return con.execute(
-        "select kernel_name, dispatch_id, sum(value) from counters_collection "
-        "where counter_name = ? group by dispatch_id order by dispatch_id", (counter,)).fetchall()
+        "select kernel_name, dispatch_id, %s(value) from counters_collection "
+        "where counter_name = ? group by dispatch_id order by dispatch_id" % reduce,
+        (counter,)).fetchall()
+
+
+PIPE_COUNTERS = ["SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_INST_LDS",
+                 "SQ_LDS_BANK_CONFLICT", "SQ_BUSY_CU_CYCLES", "SQ_WAVE_CYCLES", "SQ_INSTS_VALU",
+                 "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"]
+
+
+def summarize_pipes(d, args, cmd, workgroups: int):
+    """Pipe utilisation of the profiled kernel from one `rocprofv3 --pmc`
+    pass of PIPE_COUNTERS.  The busy fractions are per busy CU: the active
+    cycles of a pipe over SQ_BUSY_CU_CYCLES (the sum over the CUs of the
+    cycles they hold work, about workgroups x kernel cycles here).
+    GRBM_GUI_ACTIVE reads about 8x the kernel's cycles on this device (one
+    count per XCD), so rocprofv3's derived VALUBusy / MfmaUtil formulas,
+    which divide by it, read low by that factor; it is shown for the check."""
+    kind, name, _, _ = _profiled(args)
+    kname = KERNEL_NAME[kind]
+    vals = {}
+    for ctr in PIPE_COUNTERS:
+        rows = [v for n, _, v in _counter_per_dispatch(
+            d, ctr, "max" if ctr.startswith("GRBM") else "sum") if kname in n]
+        vals[ctr] = sum(rows) / len(rows)
+    busy = vals["SQ_BUSY_CU_CYCLES"]
+    per_cu = busy / workgroups
+    lines = [
+        "# Pipe utilisation of `%s` on %s (rocprofv3 --pmc)" % (kname, name), "",
+        "One counter pass of the benchmark:", "", "    " + cmd, "",
+        "- kernel_source_sha256: `%s`" % kernel_hash(kind),
+        "- counters (mean per dispatch): " + ", ".join(
+            "%s %.4g" % (k, v) for k, v in vals.items()),
+        "- workgroups per launch: %d (one per CU)" % workgroups,
+        "- busy cycles per CU: %.4g (SQ_BUSY_CU_CYCLES / workgroups); GRBM_GUI_ACTIVE / 8 "
+        "XCDs: %.4g" % (per_cu, vals["GRBM_GUI_ACTIVE"] / 8), "",
+        "| pipe, per busy CU | fraction of cycles |", "|---|---|",
+        "| VALU issuing (SQ_ACTIVE_INST_VALU) | %.1f %% |" % (
+            100 * vals["SQ_ACTIVE_INST_VALU"] / busy),
+        "| matrix unit busy, per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 4 SIMDs) | %.1f %% |" % (
+            100 * vals["SQ_VALU_MFMA_BUSY_CYCLES"] / (4 * busy)),
+        "| LDS instructions active (SQ_ACTIVE_INST_LDS) | %.1f %% |" % (
+            100 * vals["SQ_ACTIVE_INST_LDS"] / busy),
+        "| LDS stalled on bank conflicts (SQ_LDS_BANK_CONFLICT) | %.1f %% |" % (
+            100 * vals["SQ_LDS_BANK_CONFLICT"] / busy),
+        "", "Instructions per workgroup and launch: VALU %.0f, MFMA %.0f." % (
+            vals["SQ_INSTS_VALU"] / workgroups, vals["SQ_INSTS_MFMA"] / workgroups),
+    ]
+    return "\n".join(lines) + "\n"
 
 
 def _profiled(args):
@@ -698,11 +806,16 @@ def main(argv=None):
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
     ap.add_argument("--pmc-commands", nargs=2, default=["", ""])
     ap.add_argument("--summarize-trace", metavar="TRACE_DIR")
+    ap.add_argument("--summarize-pipes", nargs=2, metavar=("PMC_DIR", "WORKGROUPS"))
     ap.add_argument("--trace-command", default="")
     args = ap.parse_args(argv)
 
     if args.summarize_trace:
         sys.stdout.write(summarize_trace(args.summarize_trace, args, args.trace_command))
+        return 0
+    if args.summarize_pipes:
+        sys.stdout.write(summarize_pipes(args.summarize_pipes[0], args, args.trace_command,
+                                         int(args.summarize_pipes[1])))
         return 0
     if args.summarize_pmc:
         sys.stdout.write(summarize_pmc(args.summarize_pmc[0], args.summarize_pmc[1],
