@@ -47,9 +47,10 @@ KERNEL_SOURCES = {
     "mlp": ["ttt_mlp.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp"],
     "decode": ["ttt_decode.hip", "ttt_device.hpp", "ttt_kernels.hpp"],
     "backward": ["ttt_backward.hip", "ttt_backward.hpp", "ttt_device.hpp"],
+    "decode_compact": ["ttt_decode_compact.hip", "ttt_stream.hpp", "ttt_device.hpp"],
 }
 KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k",
-               "backward": "ttt_linear_bwd_k"}
+               "backward": "ttt_linear_bwd_k", "decode_compact": "ttt_linear_decode_compact_k"}
 BACKWARD_METRIC = "TTT-Linear backward tokens/s at 1.3B shape T=8k; % fp32 ALU roofline"
 TRAIN_METRIC = ("TTT-Linear training step (forward saving the bases + backward) tokens/s at "
                 "1.3B shape T=8k; % fp32 ALU roofline of the backward")
@@ -362,9 +363,23 @@ def decode_workload(args):
     return w
 
 
-def decode_tag(w) -> str:
+def decode_tag(w, compact=False) -> str:
     """Profile name of a streaming-step shape: streams, heads, I/O type."""
-    return "streaming_b%dh%d_%s" % (w.B, w.H, w.io)
+    return "streaming_b%dh%d_%s%s" % (w.B, w.H, w.io, "_compact" if compact else "")
+
+
+def decode_compact_bytes(w) -> int:
+    """Algorithmic bytes of one compact streaming step over all units,
+    averaged over the b positions of a mini-batch: the base read (d^2 fp32),
+    the history rows s < j read and row j written (2 d fp32 each), at j = 0
+    the fold (all b rows read, the base written), q, k, v read and z written
+    (4 d io elements), eta (4 B)."""
+    es = 2 if w.io == "bf16" else 4
+    b, d = w.mini_batch, w.d
+    row = 2 * d * 4
+    per_pos = [d * d * 4 + (d * d * 4 + b * row if j == 0 else j * row) + row
+               for j in range(b)]
+    return w.B * w.H * (sum(per_pos) // b + 4 * d * es + 4)
 
 
 def decode_bytes(w) -> int:
@@ -386,10 +401,11 @@ def run_decode(args) -> dict:
     launch gaps, so the bandwidth it gives is a lower bound)."""
     import torch
 
-    from linear_rnn_ttt_amd import ttt_linear_decode_step
+    from linear_rnn_ttt_amd import ttt_linear_decode_step, ttt_linear_decode_step_compact
     from linear_rnn_ttt_amd.inputs import make_inputs
 
     w = decode_workload(args)
+    compact = bool(getattr(args, "compact", False))
     n_tok = args.warmup + args.steps
     inp = make_inputs(w, T=max(w.mini_batch, n_tok))
     dev = upload(inp, w.io)
@@ -398,12 +414,19 @@ def run_decode(args) -> dict:
             for t in range(n_tok)]
     W = dev["w0"].expand(B, H, d, d).contiguous()
     Wb = torch.zeros_like(W)
+    hist = torch.zeros((B, H, w.mini_batch, 2, d), dtype=torch.float32, device="cuda")
     z = torch.empty((B, H, d), dtype=dev["q"].dtype, device="cuda")
 
     def step(t):
         q, k, v, eta = toks[t]
-        ttt_linear_decode_step(q, k, v, eta, W, Wb, dev["gamma"], dev["beta"],
-                               pos=t % w.mini_batch, mini_batch=w.mini_batch, eps=w.eps, z=z)
+        if compact:   # W holds the base, hist the mini-batch's rows
+            ttt_linear_decode_step_compact(q, k, v, eta, W, hist, dev["gamma"], dev["beta"],
+                                           pos=t % w.mini_batch, mini_batch=w.mini_batch,
+                                           eps=w.eps, z=z)
+        else:
+            ttt_linear_decode_step(q, k, v, eta, W, Wb, dev["gamma"], dev["beta"],
+                                   pos=t % w.mini_batch, mini_batch=w.mini_batch, eps=w.eps,
+                                   z=z)
 
     for t in range(args.warmup):
         step(t)
@@ -426,7 +449,8 @@ def run_decode(args) -> dict:
     wall = time.perf_counter() - t0
     avg_launch_s = start.elapsed_time(end) / args.steps / 1e3
     ms_per_step = wall / args.steps * 1e3
-    byts = decode_bytes(w)
+    byts = decode_compact_bytes(w) if compact else decode_bytes(w)
+    kind = "decode_compact" if compact else "decode"
     achieved = byts / avg_launch_s / 1e9
     out = {
         "metric": DECODE_METRIC,
@@ -441,15 +465,19 @@ def run_decode(args) -> dict:
         "vs_baseline": None,
         "dtype": "bf16" if w.io == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": decode_tag(w), "inner_model": "TTT-Linear", "streams": B,
+        "config": {"workload": decode_tag(w, compact), "inner_model": "TTT-Linear", "streams": B,
                    "H": H, "d": d, "mini_batch": w.mini_batch, "io": w.io, "state": "fp32",
                    "parallelism": "none (1 GPU)",
-                   "launch": "ttt_linear_decode_step: one 256-thread workgroup per (stream, "
-                             "head) unit, steps replayed from one HIP graph"},
+                   "pending_state": ("compact: base + the mini-batch's (k, u) rows" if compact
+                                     else "W and W_base"),
+                   "launch": ("ttt_linear_decode_step_compact" if compact else
+                              "ttt_linear_decode_step") +
+                             ": one 256-thread workgroup per (stream, head) unit, steps "
+                             "replayed from one HIP graph"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
-                     "traffic": read_traffic("decode", decode_tag(w)),
-                     "kernel": KERNEL_NAME["decode"],
+                     "traffic": read_traffic(kind, decode_tag(w, compact)),
+                     "kernel": KERNEL_NAME[kind],
                      "avg_launch_ms": round(avg_launch_s * 1e3, 5),
                      "algorithmic_bytes_per_launch": byts},
         "outputs_finite": bool(torch.isfinite(z.float()).all().item()),
@@ -711,6 +739,9 @@ def _profiled(args):
 
     if args.decode:
         w = decode_workload(args)
+        if args.compact:
+            return ("decode_compact", decode_tag(w, True), decode_compact_bytes(w),
+                    6 * w.d * w.d * w.B * w.H)
         return "decode", decode_tag(w), decode_bytes(w), 6 * w.d * w.d * w.B * w.H
     if args.backward:
         w = WORKLOADS[args.workload]
@@ -799,6 +830,8 @@ def main(argv=None):
                     help="time the TTT-Linear streaming step instead of the scan")
     ap.add_argument("--backward", action="store_true",
                     help="time the TTT-Linear backward pass instead of the forward scan")
+    ap.add_argument("--compact", action="store_true",
+                    help="with --decode: the compact pending state (base + mini-batch rows)")
     ap.add_argument("--train", action="store_true",
                     help="with --backward: time forward (saving the bases) + backward")
     ap.add_argument("--batch", type=int, default=0,

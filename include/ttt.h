@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 5
+#define TTT_ABI_VERSION 6
 
 typedef enum {
   TTT_OK = 0,
@@ -168,6 +168,29 @@ ttt_status ttt_linear_decode_step(const ttt_params* p, int32_t pos,
                                   const float* eta, float* w, float* w_base,
                                   const float* ln_gamma, const float* ln_beta,
                                   void* z, void* hip_stream);
+
+/*
+ * The streaming step of ttt_linear_decode_step with a compact pending
+ * state: the same tokens, the same z (up to rounding order).  Within a
+ * mini-batch the state after the tokens s < pos is
+ *     W = w_base + sum_{s<pos} k_s^T u_s,    u_s = -eta_s * gradient_s,
+ * so the stream carries the base and the mini-batch's rows instead of W:
+ *   w_base  [B,H,d,d] fp32, read; at pos == 0 first replaced by
+ *           w_base + sum over all mini_batch history slots (the previous
+ *           mini-batch; zeros at the start of a stream).
+ *   hist    [B,H,mini_batch,2,d] fp32: slot s holds k_s then u_s; slot
+ *           pos is written.  Zero it when a stream starts.
+ * About 22 KB move per unit and token for mini_batch = 16 (48 KB for the
+ * (W, W_base) form).  The final state of a ttt_linear_forward over a whole
+ * number of mini-batches starts a stream as w_base with a zero history.
+ *   p   T must be 1; mini_batch at most 64 (TTT_ERR_UNSUPPORTED).
+ * Other arguments, aliasing and errors as ttt_linear_decode_step.
+ */
+ttt_status ttt_linear_decode_step_compact(const ttt_params* p, int32_t pos,
+                                          const void* q, const void* k, const void* v,
+                                          const float* eta, float* w_base, float* hist,
+                                          const float* ln_gamma, const float* ln_beta,
+                                          void* z, void* hip_stream);
 
 /*
  * TTT-Linear forward scan for training: ttt_linear_forward (same arguments

@@ -6,10 +6,11 @@ The scan runs in hand-written HIP kernels behind the C ABI of
 argument marshalling, with PyTorch supplying device memory and streams.
 """
 from ._lib import TTTArgumentError, TTTError, abi_version, status_string  # noqa: F401
-from .ops import (ttt_linear_backward, ttt_linear_decode_step, ttt_linear_forward,  # noqa: F401
-                  ttt_mlp_forward)
+from .ops import (ttt_linear_backward, ttt_linear_decode_step,  # noqa: F401
+                  ttt_linear_decode_step_compact, ttt_linear_forward, ttt_mlp_forward)
 
-__all__ = ["ttt_linear_forward", "ttt_linear_decode_step", "ttt_linear_backward", "ttt_mlp_forward",
+__all__ = ["ttt_linear_forward", "ttt_linear_decode_step", "ttt_linear_decode_step_compact",
+           "ttt_linear_backward", "ttt_mlp_forward",
            "abi_version",
            "status_string",
            "TTTError", "TTTArgumentError"]

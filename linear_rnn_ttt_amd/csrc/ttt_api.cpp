@@ -11,6 +11,7 @@
 
 #include "ttt_backward.hpp"
 #include "ttt_kernels.hpp"
+#include "ttt_stream.hpp"
 
 namespace {
 
@@ -268,6 +269,55 @@ ttt_status ttt_linear_decode_step(const ttt_params* p, int32_t pos, const void* 
   const hipError_t e = tttk::launch_linear_decode(a, p->io_dtype == TTT_BF16, ln,
                                                   !(p->flags & TTT_NO_RESIDUAL),
                                                   static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
+}
+
+ttt_status ttt_linear_decode_step_compact(const ttt_params* p, int32_t pos, const void* q,
+                                          const void* k, const void* v, const float* eta,
+                                          float* w_base, float* hist, const float* ln_gamma,
+                                          const float* ln_beta, void* z, void* hip_stream) {
+  uint64_t elems = 0;
+  const ttt_status st = check_common(p, &elems);
+  if (st != TTT_OK) return st;
+  if (p->T != 1) return TTT_ERR_SHAPE;  // one token per unit
+  if (p->mini_batch > 64) return TTT_ERR_UNSUPPORTED;
+  if (pos < 0 || pos >= p->mini_batch) return TTT_ERR_ARG;
+  const bool ln = !(p->flags & TTT_NO_LN);
+  if (!q || !k || !v || !eta || !w_base || !hist || !z) return TTT_ERR_NULL;
+  if (ln && (!ln_gamma || !ln_beta)) return TTT_ERR_NULL;
+
+  const uint64_t es = p->io_dtype == TTT_BF16 ? 2 : 4;
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t dd = static_cast<uint64_t>(kHeadDim) * kHeadDim;
+  const Range rq = span(q, elems * es), rk = span(k, elems * es), rv = span(v, elems * es);
+  const Range re = span(eta, units * 4), rz = span(z, elems * es);
+  const Range rw = span(w_base, units * dd * 4);
+  const Range rh = span(hist, units * static_cast<uint64_t>(p->mini_batch) * 2 * kHeadDim * 4);
+  const Range rg = span(ln ? ln_gamma : nullptr, p->H * 256ull);
+  const Range rbe = span(ln ? ln_beta : nullptr, p->H * 256ull);
+  const Range inputs[] = {rq, rk, rv, re, rg, rbe};
+  for (const Range& r : inputs)
+    if (overlap(rz, r) || overlap(rw, r) || overlap(rh, r)) return TTT_ERR_ALIAS;
+  if (overlap(rz, rw) || overlap(rz, rh) || overlap(rw, rh)) return TTT_ERR_ALIAS;
+
+  tttk::CompactArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.eta = eta;
+  a.w_base = w_base;
+  a.hist = hist;
+  a.gamma = ln_gamma;
+  a.beta = ln_beta;
+  a.z = z;
+  a.B = p->B;
+  a.H = p->H;
+  a.pos = pos;
+  a.mb = p->mini_batch;
+  a.eps = p->ln_eps;
+  const hipError_t e = tttk::launch_linear_decode_compact(
+      a, p->io_dtype == TTT_BF16, ln, !(p->flags & TTT_NO_RESIDUAL),
+      static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
 }
 

@@ -53,11 +53,35 @@ __device__ __forceinline__ void st_io(void* p, size_t i, float x) {
   }
 }
 
-// Sum over the 64 lanes of the wave, in every lane (butterfly).
-__device__ __forceinline__ float wave_sum(float x) {
+// x from another lane of the same 16-lane row (DPP control CTRL).
+template <int CTRL>
+__device__ __forceinline__ float dpp(float x) {
+  return bitsf(static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(fbits(x)), CTRL, 0xf, 0xf, false)));
+}
+
+// N sums over the 64 lanes of the wave at once, in every lane: butterflies
+// within each 16-lane row on DPP (lanes l^1, l^2, then the mirrored lane of
+// the half row and of the row), then across the four rows with permlane
+// swaps -- all VALU, no LDS round trip.
+template <int N>
+__device__ __forceinline__ void wave_sums(float (&x)[N]) {
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, 64);
-  return x;
+  for (int j = 0; j < N; ++j) x[j] += dpp<0xB1>(x[j]);    // quad_perm 1,0,3,2
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp<0x4E>(x[j]);    // quad_perm 2,3,0,1
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp<0x141>(x[j]);   // row_half_mirror
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += dpp<0x140>(x[j]);   // row_mirror
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] = group_sum(x[j]);
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+  float s[1] = {x};
+  wave_sums(s);
+  return s[0];
 }
 
 // LN over the 64 features held one per lane: x_hat and 1 / sigma.
@@ -124,9 +148,9 @@ __global__ __launch_bounds__(DW * 64) void ttt_linear_decode_k(DecodeArgs a) {
     ln_stats(hk, a.eps, xh, rs);
     const float gy = 2.f * ((RES ? kf : 0.f) + __builtin_fmaf(gam, xh, bet) - vf);
     const float gg = gam * gy;
-    const float m1 = wave_sum(gg) * (1.0f / DD);
-    const float m2 = wave_sum(gg * xh) * (1.0f / DD);
-    g = (gg - m1 - xh * m2) * rs;
+    float m[2] = {gg, gg * xh};
+    wave_sums(m);
+    g = (gg - m[0] * (1.0f / DD) - xh * (m[1] * (1.0f / DD))) * rs;
   } else {
     g = 2.f * ((RES ? kf : 0.f) + hk - vf);
   }

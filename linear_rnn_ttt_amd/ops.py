@@ -13,8 +13,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["ttt_linear_forward", "ttt_linear_decode_step", "ttt_linear_backward",
-           "ttt_mlp_forward"]
+__all__ = ["ttt_linear_forward", "ttt_linear_decode_step", "ttt_linear_decode_step_compact",
+           "ttt_linear_backward", "ttt_mlp_forward"]
 
 HEAD_DIM = 64
 
@@ -185,6 +185,43 @@ def ttt_linear_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                                _ptr(ln_gamma), _ptr(ln_beta), _ptr(z),
                                                _stream(q, stream))
     _lib.check("ttt_linear_decode_step", rc)
+    return z
+
+
+def ttt_linear_decode_step_compact(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                   eta: torch.Tensor, w_base: torch.Tensor, hist: torch.Tensor,
+                                   ln_gamma: Optional[torch.Tensor] = None,
+                                   ln_beta: Optional[torch.Tensor] = None, *, pos: int,
+                                   mini_batch: int = 16, eps: float = 1e-6,
+                                   layer_norm: bool = True, residual: bool = True,
+                                   z: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The streaming step with a compact pending state; returns z [B,H,d].
+    w_base [B,H,d,d] fp32 (the mini-batch's base) and hist
+    [B,H,mini_batch,2,d] fp32 (its rows k_s, u_s; zero at a stream's start)
+    are updated in place.  See include/ttt.h."""
+    _dev_tensor("q", q)
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d] (one token per unit)")
+    B, H, d = q.shape
+    _dev_tensor("k", k, q.dtype, q.shape, device=q.device)
+    _dev_tensor("v", v, q.dtype, q.shape, device=q.device)
+    _dev_tensor("eta", eta, torch.float32, (B, H), device=q.device)
+    _dev_tensor("w_base", w_base, torch.float32, (B, H, d, d), device=q.device)
+    _dev_tensor("hist", hist, torch.float32, (B, H, mini_batch, 2, d), device=q.device)
+    if layer_norm:
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d), device=q.device)
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d), device=q.device)
+    else:
+        ln_gamma = ln_beta = None
+    if z is None:
+        z = torch.empty_like(q)
+    _dev_tensor("z", z, q.dtype, q.shape, device=q.device)
+    p = _params(q.unsqueeze(2), mini_batch, eps, layer_norm, residual, True)
+    with torch.cuda.device(q.device):
+        rc = _lib.lib().ttt_linear_decode_step_compact(
+            ctypes.byref(p), int(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w_base),
+            _ptr(hist), _ptr(ln_gamma), _ptr(ln_beta), _ptr(z), _stream(q, stream))
+    _lib.check("ttt_linear_decode_step_compact", rc)
     return z
 
 

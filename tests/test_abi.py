@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 5
+    assert _lib.abi_version() == 6
     for code in range(7):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
@@ -255,3 +255,25 @@ def test_backward_accepts_the_saved_bases_flag_only_there():
     p = _params(flags=_lib.TTT_BASES_SAVED | _lib.TTT_NO_RESIDUAL, d=32)
     assert _backward(p) == _lib.TTT_ERR_UNSUPPORTED       # flag accepted; d = 32 refused
     assert _linear(_params(flags=_lib.TTT_BASES_SAVED)) == _lib.TTT_ERR_ARG
+
+
+def _compact(p, pos=0, **ptrs):
+    names = ["q", "k", "v", "eta", "wb", "hist", "g", "b", "z"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    return _lib.lib().ttt_linear_decode_step_compact(ctypes.byref(p) if p is not None else None,
+                                                     pos, *args, None)
+
+
+def test_compact_step_rejects_bad_arguments():
+    p = _params(T=1)
+    assert _compact(None) == _lib.TTT_ERR_NULL
+    assert _compact(_params(T=3)) == _lib.TTT_ERR_SHAPE                    # one token per unit
+    assert _compact(p, pos=-1) == _lib.TTT_ERR_ARG
+    assert _compact(p, pos=16) == _lib.TTT_ERR_ARG                         # pos < mini_batch
+    assert _compact(_params(T=1, mini_batch=65), pos=0) == _lib.TTT_ERR_UNSUPPORTED
+    assert _compact(_params(T=1, d=32)) == _lib.TTT_ERR_UNSUPPORTED
+    for name in ["q", "k", "v", "eta", "wb", "hist", "z", "g", "b"]:
+        assert _compact(p, **{name: None}) == _lib.TTT_ERR_NULL, name
+    assert _compact(p, hist=_addr(5)) == _lib.TTT_ERR_ALIAS                # hist == w_base
+    assert _compact(p, z=_addr(3)) == _lib.TTT_ERR_ALIAS                   # z == v
+    assert _compact(p, wb=_addr(4)) == _lib.TTT_ERR_ALIAS                  # w_base == eta
