@@ -18,6 +18,8 @@ mlp_loss_grad(W1, b1, W2, b2, k, v, gamma, beta, ...) -> (loss, grads)
 linear_apply / mlp_apply: the inner model f for one token.
 linear_decode_step(W, W_base, q, k, v, eta, gamma, beta, pos=...) -> (z, W, W_base):
     one token of the TTT-Linear scan for one unit, the streaming form.
+mlp_decode_step(S, S_base, q, k, v, eta, gamma, beta, pos=...) -> (z, S, S_base):
+    the same for TTT-MLP, S = (W1, b1, W2, b2).
 build(): compile ``libttt_oracle.so`` with gcc.
 
 The backward pass of the TTT-Linear scan (its vector-Jacobian product) is in
@@ -243,3 +245,18 @@ def linear_decode_step(W, W_base, q, k, v, eta, gamma=None, beta=None, *, pos,
     W_new = W - float(eta) * g
     z = linear_apply(W_new, q, gamma, beta, layer_norm=layer_norm, residual=residual, eps=eps)
     return z, W_new, base.copy()
+
+
+def mlp_decode_step(S, S_base, q, k, v, eta, gamma=None, beta=None, *, pos,
+                    layer_norm=True, residual=True, eps=1e-6):
+    """One token of the TTT-MLP scan for one unit, carrying the stream's state
+    S = (W1, b1, W2, b2), its mini-batch base S_base and the token's position
+    pos in its mini-batch (the LIT-801 record, "Key takeaways" items 1, 2 and
+    5, as linear_decode_step).  Returns (z, S_new, base) in fp64."""
+    S = tuple(_f64(x) for x in S)
+    base = S if pos == 0 else tuple(_f64(x) for x in S_base)
+    _, grads = mlp_loss_grad(*base, k, v, gamma, beta, layer_norm=layer_norm,
+                             residual=residual, eps=eps)
+    S_new = tuple(x - float(eta) * gx for x, gx in zip(S, grads))
+    z = mlp_apply(*S_new, q, gamma, beta, layer_norm=layer_norm, residual=residual, eps=eps)
+    return z, S_new, tuple(x.copy() for x in base)

@@ -193,3 +193,31 @@ def test_mlp_ragged_tail_equals_zero_eta_padding():
     np.testing.assert_array_equal(z, rz[:, :, :13])
     for a, b in zip(S, rS):
         np.testing.assert_array_equal(a, b)
+
+
+@pytest.mark.parametrize("b,ln,res", [(16, True, True), (4, True, True), (1, False, True),
+                                      (5, True, False)])
+def test_mlp_decode_step_loop_is_the_scan(b, ln, res):
+    """The streaming step looped over a sequence (pos = t mod b) reproduces
+    the oracle's scan: z of every token and the final state."""
+    rng = np.random.default_rng(70 + b)
+    H, T, d, m = 2, 23, 8, 32
+    q, k, v = (rng.standard_normal((1, H, T, d)).astype(np.float32) for _ in range(3))
+    eta = (0.1 * rng.random((1, H, T))).astype(np.float32)
+    w1 = (0.3 * rng.standard_normal((H, d, m))).astype(np.float32)
+    b1 = (0.1 * rng.standard_normal((H, m))).astype(np.float32)
+    w2 = (0.3 * rng.standard_normal((H, m, d))).astype(np.float32)
+    b2 = (0.1 * rng.standard_normal((H, d))).astype(np.float32)
+    gamma = (1 + 0.2 * rng.standard_normal((H, d))).astype(np.float32)
+    beta = (0.2 * rng.standard_normal((H, d))).astype(np.float32)
+    kw = dict(layer_norm=ln, residual=res, eps=1e-6)
+    zr, (w1r, b1r, w2r, b2r) = oracle.mlp(q, k, v, eta, w1, b1, w2, b2, gamma, beta,
+                                          mini_batch=b, **kw)
+    for h in range(H):
+        S, Sb = (w1[h], b1[h], w2[h], b2[h]), None
+        for t in range(T):
+            z, S, Sb = oracle.mlp_decode_step(S, Sb, q[0, h, t], k[0, h, t], v[0, h, t],
+                                              eta[0, h, t], gamma[h], beta[h], pos=t % b, **kw)
+            np.testing.assert_allclose(z, zr[0, h, t], rtol=1e-12, atol=1e-12)
+        for got, want in zip(S, (w1r[0, h], b1r[0, h], w2r[0, h], b2r[0, h])):
+            np.testing.assert_allclose(got, want, rtol=1e-12, atol=1e-12)
