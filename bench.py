@@ -48,15 +48,19 @@ KERNEL_SOURCES = {
     "decode": ["ttt_decode.hip", "ttt_device.hpp", "ttt_kernels.hpp"],
     "backward": ["ttt_backward.hip", "ttt_backward.hpp", "ttt_device.hpp"],
     "decode_compact": ["ttt_decode_compact.hip", "ttt_stream.hpp", "ttt_device.hpp"],
+    "mlp_decode": ["ttt_mlp_decode.hip", "ttt_stream.hpp", "ttt_device.hpp"],
 }
 KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k",
-               "backward": "ttt_linear_bwd_k", "decode_compact": "ttt_linear_decode_compact_k"}
+               "backward": "ttt_linear_bwd_k", "decode_compact": "ttt_linear_decode_compact_k",
+               "mlp_decode": "ttt_mlp_decode_k"}
 BACKWARD_METRIC = "TTT-Linear backward tokens/s at 1.3B shape T=8k; % fp32 ALU roofline"
 TRAIN_METRIC = ("TTT-Linear training step (forward saving the bases + backward) tokens/s at "
                 "1.3B shape T=8k; % fp32 ALU roofline of the backward")
 FP32_VECTOR_PEAK_TFS = 157.3   # MI355X fp32 vector (packed); non-packed FMA issue is half
 DECODE_METRIC = ("TTT-Linear streaming step tokens/s (one token per (batch, head) unit per "
                  "launch); % HBM roofline")
+MLP_DECODE_METRIC = ("TTT-MLP streaming step tokens/s (one token per (batch, head) unit per "
+                     "launch); % HBM roofline")
 
 
 def kernel_hash(kind: str) -> str:
@@ -355,9 +359,9 @@ def decode_workload(args):
     from linear_rnn_ttt_amd.inputs import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    if w.kind != "linear":
-        raise SystemExit("bench.py: the streaming step is TTT-Linear's (workload %s is %s)"
-                         % (w.name, w.kind))
+    if w.kind != "linear" and getattr(args, "compact", False):
+        raise SystemExit("bench.py: the compact streaming step is TTT-Linear's (workload %s is "
+                         "%s)" % (w.name, w.kind))
     if args.batch:
         w = w.with_(B=args.batch)
     return w
@@ -365,7 +369,8 @@ def decode_workload(args):
 
 def decode_tag(w, compact=False) -> str:
     """Profile name of a streaming-step shape: streams, heads, I/O type."""
-    return "streaming_b%dh%d_%s%s" % (w.B, w.H, w.io, "_compact" if compact else "")
+    return "streaming_%sb%dh%d_%s%s" % ("mlp_" if w.kind == "mlp" else "", w.B, w.H, w.io,
+                                         "_compact" if compact else "")
 
 
 def decode_compact_bytes(w) -> int:
@@ -384,10 +389,20 @@ def decode_compact_bytes(w) -> int:
 
 def decode_bytes(w) -> int:
     """Algorithmic bytes of one streaming step over all units: the state read
-    and written (2 d^2 fp32), the mini-batch base read or written (d^2 fp32),
-    q, k, v read and z written (4 d io elements), eta (4 B)."""
+    and written, the mini-batch base read or written (3 x the state: d^2
+    fp32 for TTT-Linear, 2 d m + m + d fp32 for TTT-MLP), q, k, v read and z
+    written (4 d io elements), eta (4 B)."""
     es = 2 if w.io == "bf16" else 4
-    return w.B * w.H * (3 * w.d * w.d * 4 + 4 * w.d * es + 4)
+    state = w.d * w.d if w.kind == "linear" else 2 * w.d * w.hidden + w.hidden + w.d
+    return w.B * w.H * (3 * state * 4 + 4 * w.d * es + 4)
+
+
+def decode_flops(w) -> int:
+    """Multiply-adds x 2 of one streaming step over all units: TTT-Linear
+    3 d^2 (k W, the update, q W); TTT-MLP 7 d m (k W1 and q W1, a W2 at the
+    base and a_q W2 after the update, g W2^T, the two rank-1 updates)."""
+    per = 3 * w.d * w.d if w.kind == "linear" else 7 * w.d * w.hidden
+    return 2 * per * w.B * w.H
 
 
 def run_decode(args) -> dict:
@@ -401,7 +416,8 @@ def run_decode(args) -> dict:
     launch gaps, so the bandwidth it gives is a lower bound)."""
     import torch
 
-    from linear_rnn_ttt_amd import ttt_linear_decode_step, ttt_linear_decode_step_compact
+    from linear_rnn_ttt_amd import (ttt_linear_decode_step, ttt_linear_decode_step_compact,
+                                    ttt_mlp_decode_step)
     from linear_rnn_ttt_amd.inputs import make_inputs
 
     w = decode_workload(args)
@@ -412,14 +428,23 @@ def run_decode(args) -> dict:
     B, H, d = w.B, w.H, w.d
     toks = [[dev[x][:, :, t].contiguous() for x in ("q", "k", "v", "eta")]
             for t in range(n_tok)]
-    W = dev["w0"].expand(B, H, d, d).contiguous()
-    Wb = torch.zeros_like(W)
-    hist = torch.zeros((B, H, w.mini_batch, 2, d), dtype=torch.float32, device="cuda")
+    mlp = w.kind == "mlp"
+    if mlp:
+        S = [dev[x].expand((B, H) + dev[x].shape[1:]).contiguous()
+             for x in ("w1", "b1", "w2", "b2")]
+        Sb = [torch.zeros_like(x) for x in S]
+    else:
+        W = dev["w0"].expand(B, H, d, d).contiguous()
+        Wb = torch.zeros_like(W)
+        hist = torch.zeros((B, H, w.mini_batch, 2, d), dtype=torch.float32, device="cuda")
     z = torch.empty((B, H, d), dtype=dev["q"].dtype, device="cuda")
 
     def step(t):
         q, k, v, eta = toks[t]
-        if compact:   # W holds the base, hist the mini-batch's rows
+        if mlp:
+            ttt_mlp_decode_step(q, k, v, eta, S, Sb, dev["gamma"], dev["beta"],
+                                pos=t % w.mini_batch, mini_batch=w.mini_batch, eps=w.eps, z=z)
+        elif compact:   # W holds the base, hist the mini-batch's rows
             ttt_linear_decode_step_compact(q, k, v, eta, W, hist, dev["gamma"], dev["beta"],
                                            pos=t % w.mini_batch, mini_batch=w.mini_batch,
                                            eps=w.eps, z=z)
@@ -450,10 +475,18 @@ def run_decode(args) -> dict:
     avg_launch_s = start.elapsed_time(end) / args.steps / 1e3
     ms_per_step = wall / args.steps * 1e3
     byts = decode_compact_bytes(w) if compact else decode_bytes(w)
-    kind = "decode_compact" if compact else "decode"
+    kind = "decode_compact" if compact else ("mlp_decode" if mlp else "decode")
     achieved = byts / avg_launch_s / 1e9
+    if mlp:
+        launch, pending = ("ttt_mlp_decode_step: one 1024-thread workgroup per (stream, head) "
+                           "unit, steps replayed from one HIP graph", "S and S_base")
+    else:
+        launch = (("ttt_linear_decode_step_compact" if compact else "ttt_linear_decode_step") +
+                  ": one 256-thread workgroup per (stream, head) unit, steps replayed from one "
+                  "HIP graph")
+        pending = ("compact: base + the mini-batch's (k, u) rows" if compact else "W and W_base")
     out = {
-        "metric": DECODE_METRIC,
+        "metric": MLP_DECODE_METRIC if mlp else DECODE_METRIC,
         "value": round(B / (ms_per_step / 1e3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -465,15 +498,10 @@ def run_decode(args) -> dict:
         "vs_baseline": None,
         "dtype": "bf16" if w.io == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": decode_tag(w, compact), "inner_model": "TTT-Linear", "streams": B,
+        "config": {"workload": decode_tag(w, compact),
+                   "inner_model": "TTT-MLP" if mlp else "TTT-Linear", "streams": B,
                    "H": H, "d": d, "mini_batch": w.mini_batch, "io": w.io, "state": "fp32",
-                   "parallelism": "none (1 GPU)",
-                   "pending_state": ("compact: base + the mini-batch's (k, u) rows" if compact
-                                     else "W and W_base"),
-                   "launch": ("ttt_linear_decode_step_compact" if compact else
-                              "ttt_linear_decode_step") +
-                             ": one 256-thread workgroup per (stream, head) unit, steps "
-                             "replayed from one HIP graph"},
+                   "parallelism": "none (1 GPU)", "pending_state": pending, "launch": launch},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 5),
                      "traffic": read_traffic(kind, decode_tag(w, compact)),
@@ -496,18 +524,27 @@ def cpu_baseline_decode(w, inp, budget_s: float):
     import oracle
 
     B, H, d = w.B, w.H, w.d
-    W = np.broadcast_to(inp["w0"].astype(np.float64), (B, H, d, d)).copy()
-    Wb = np.zeros_like(W)
+    if w.kind == "mlp":
+        S = [[tuple(inp[x][h].astype(np.float64) for x in ("w1", "b1", "w2", "b2"))
+              for h in range(H)] for _ in range(B)]
+        Sb = [[None] * H for _ in range(B)]
+    else:
+        W = np.broadcast_to(inp["w0"].astype(np.float64), (B, H, d, d)).copy()
+        Wb = np.zeros_like(W)
     t, t0 = 0, time.perf_counter()
     n_drawn = inp["q"].shape[2]
     while time.perf_counter() - t0 < budget_s:
         i = t % n_drawn
         for b in range(B):
             for h in range(H):
-                _, W[b, h], Wb[b, h] = oracle.linear_decode_step(
-                    W[b, h], Wb[b, h], inp["q"][b, h, i], inp["k"][b, h, i], inp["v"][b, h, i],
-                    inp["eta"][b, h, i], inp["gamma"][h], inp["beta"][h], pos=t % w.mini_batch,
-                    eps=w.eps)
+                tok = (inp["q"][b, h, i], inp["k"][b, h, i], inp["v"][b, h, i],
+                       inp["eta"][b, h, i], inp["gamma"][h], inp["beta"][h])
+                if w.kind == "mlp":
+                    _, S[b][h], Sb[b][h] = oracle.mlp_decode_step(
+                        S[b][h], Sb[b][h], *tok, pos=t % w.mini_batch, eps=w.eps)
+                else:
+                    _, W[b, h], Wb[b, h] = oracle.linear_decode_step(
+                        W[b, h], Wb[b, h], *tok, pos=t % w.mini_batch, eps=w.eps)
         t += 1
     dt = time.perf_counter() - t0
     return {"value": round(B * t / dt, 1), "unit": "tokens/s", "cores": 1, "kind": "oracle",
@@ -741,8 +778,9 @@ def _profiled(args):
         w = decode_workload(args)
         if args.compact:
             return ("decode_compact", decode_tag(w, True), decode_compact_bytes(w),
-                    6 * w.d * w.d * w.B * w.H)
-        return "decode", decode_tag(w), decode_bytes(w), 6 * w.d * w.d * w.B * w.H
+                    decode_flops(w))
+        return ("mlp_decode" if w.kind == "mlp" else "decode", decode_tag(w), decode_bytes(w),
+                decode_flops(w))
     if args.backward:
         w = WORKLOADS[args.workload]
         alg = backward_alg(w)

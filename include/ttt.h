@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 6
+#define TTT_ABI_VERSION 7
 
 typedef enum {
   TTT_OK = 0,
@@ -284,6 +284,36 @@ ttt_status ttt_mlp_forward(const ttt_params* p, int32_t hidden,
                            const float* ln_gamma, const float* ln_beta,
                            void* z, float* w1_out, float* b1_out,
                            float* w2_out, float* b2_out, void* hip_stream);
+
+/*
+ * One token of the TTT-MLP scan per (batch, head) unit: the streaming
+ * (decode) step, as ttt_linear_decode_step with the state
+ * S = (W1, b1, W2, b2).  The gradient is taken at base = (pos == 0 ? S :
+ * S_base), S <- S - eta_t * gradient, z_t = f(q_t; S) and, when pos == 0,
+ * base is stored into S_base.  Calling it for t = 0, 1, ... with
+ * pos = t mod mini_batch, starting from S = S0, reproduces ttt_mlp_forward
+ * (the codewithpapers.app record of arXiv 2407.04620, TTT-MLP; the LIT-801
+ * record, "Key takeaways" items 1, 2 and 5).
+ *   p        T must be 1; mini_batch any b >= 1; state0_per_batch unused.
+ *   hidden   m; 256 supported (TTT_ERR_UNSUPPORTED otherwise).
+ *   q, k, v  [B,H,d] io_dtype;  eta [B,H] fp32;  z [B,H,d] io_dtype (out).
+ *   w1 [B,H,d,m], b1 [B,H,m], w2 [B,H,m,d], b2 [B,H,d] fp32: the state,
+ *            read and written in place.
+ *   w1_base, b1_base, w2_base, b2_base: the base, same shapes; read when
+ *            pos > 0, written when pos == 0.
+ * None of the eight state buffers and z overlaps another or an input
+ * (TTT_ERR_ALIAS); pos out of range is TTT_ERR_ARG.  gfx950 kernel: one
+ * 1024-thread workgroup per unit holding its state in registers, fp32
+ * arithmetic; bound by moving the state (about 397 KB per unit and token).
+ */
+ttt_status ttt_mlp_decode_step(const ttt_params* p, int32_t hidden, int32_t pos,
+                               const void* q, const void* k, const void* v,
+                               const float* eta,
+                               float* w1, float* b1, float* w2, float* b2,
+                               float* w1_base, float* b1_base,
+                               float* w2_base, float* b2_base,
+                               const float* ln_gamma, const float* ln_beta,
+                               void* z, void* hip_stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* ttt_status_string(ttt_status s);

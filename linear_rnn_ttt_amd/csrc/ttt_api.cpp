@@ -321,6 +321,72 @@ ttt_status ttt_linear_decode_step_compact(const ttt_params* p, int32_t pos, cons
   return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
 }
 
+ttt_status ttt_mlp_decode_step(const ttt_params* p, int32_t hidden, int32_t pos, const void* q,
+                               const void* k, const void* v, const float* eta, float* w1,
+                               float* b1, float* w2, float* b2, float* w1_base, float* b1_base,
+                               float* w2_base, float* b2_base, const float* ln_gamma,
+                               const float* ln_beta, void* z, void* hip_stream) {
+  uint64_t elems = 0;
+  const ttt_status st = check_common(p, &elems);
+  if (st != TTT_OK) return st;
+  if (p->T != 1) return TTT_ERR_SHAPE;  // one token per unit
+  if (hidden < 1) return TTT_ERR_SHAPE;
+  if (hidden != kMlpHidden) return TTT_ERR_UNSUPPORTED;
+  if (pos < 0 || pos >= p->mini_batch) return TTT_ERR_ARG;
+  const bool ln = !(p->flags & TTT_NO_LN);
+  float* state[8] = {w1, b1, w2, b2, w1_base, b1_base, w2_base, b2_base};
+  if (!q || !k || !v || !eta || !z) return TTT_ERR_NULL;
+  for (float* s : state)
+    if (!s) return TTT_ERR_NULL;
+  if (ln && (!ln_gamma || !ln_beta)) return TTT_ERR_NULL;
+
+  const uint64_t es = p->io_dtype == TTT_BF16 ? 2 : 4;
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t dm = static_cast<uint64_t>(kHeadDim) * hidden;
+  const uint64_t sizes[4] = {units * dm * 4, units * hidden * 4ull, units * dm * 4,
+                             units * kHeadDim * 4ull};
+  const Range rq = span(q, elems * es), rk = span(k, elems * es), rv = span(v, elems * es);
+  const Range re = span(eta, units * 4), rz = span(z, elems * es);
+  const Range rg = span(ln ? ln_gamma : nullptr, p->H * 256ull);
+  const Range rbe = span(ln ? ln_beta : nullptr, p->H * 256ull);
+  Range rs[9];
+  for (int i = 0; i < 8; ++i) rs[i] = span(state[i], sizes[i % 4]);
+  rs[8] = rz;
+  const Range inputs[] = {rq, rk, rv, re, rg, rbe};
+  for (const Range& w : rs) {
+    for (const Range& r : inputs)
+      if (overlap(w, r)) return TTT_ERR_ALIAS;
+  }
+  for (int i = 0; i < 9; ++i)
+    for (int j = i + 1; j < 9; ++j)
+      if (overlap(rs[i], rs[j])) return TTT_ERR_ALIAS;
+
+  tttk::MlpDecodeArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.eta = eta;
+  a.w1 = w1;
+  a.b1 = b1;
+  a.w2 = w2;
+  a.b2 = b2;
+  a.w1_base = w1_base;
+  a.b1_base = b1_base;
+  a.w2_base = w2_base;
+  a.b2_base = b2_base;
+  a.gamma = ln_gamma;
+  a.beta = ln_beta;
+  a.z = z;
+  a.B = p->B;
+  a.H = p->H;
+  a.pos = pos;
+  a.eps = p->ln_eps;
+  const hipError_t e = tttk::launch_mlp_decode(a, p->io_dtype == TTT_BF16, ln,
+                                               !(p->flags & TTT_NO_RESIDUAL),
+                                               static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
+}
+
 ttt_status ttt_linear_forward_save(const ttt_params* p, const void* q, const void* k,
                                    const void* v, const float* eta, const float* w0,
                                    const float* ln_gamma, const float* ln_beta, void* z,

@@ -188,6 +188,49 @@ def ttt_linear_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     return z
 
 
+def ttt_mlp_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,
+                        state, base, ln_gamma: Optional[torch.Tensor] = None,
+                        ln_beta: Optional[torch.Tensor] = None, *, pos: int,
+                        mini_batch: int = 16, eps: float = 1e-6, layer_norm: bool = True,
+                        residual: bool = True, z: Optional[torch.Tensor] = None,
+                        stream=None) -> torch.Tensor:
+    """One token per (batch, head) unit of the TTT-MLP scan (streaming step);
+    returns z [B,H,d].  state and base are (w1 [B,H,d,m], b1 [B,H,m],
+    w2 [B,H,m,d], b2 [B,H,d]) fp32, the stream's state and mini-batch base,
+    updated in place; pos is the token's position in its mini-batch.  See
+    include/ttt.h."""
+    _dev_tensor("q", q)
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d] (one token per unit)")
+    B, H, d = q.shape
+    _dev_tensor("k", k, q.dtype, q.shape, device=q.device)
+    _dev_tensor("v", v, q.dtype, q.shape, device=q.device)
+    _dev_tensor("eta", eta, torch.float32, (B, H), device=q.device)
+    if len(state) != 4 or len(base) != 4:
+        raise ValueError("state and base are (w1, b1, w2, b2)")
+    m = state[0].shape[-1] if state[0].dim() == 4 else -1
+    shapes = ((B, H, d, m), (B, H, m), (B, H, m, d), (B, H, d))
+    for tag, group in (("", state), ("_base", base)):
+        for name, t, shp in zip(("w1", "b1", "w2", "b2"), group, shapes):
+            _dev_tensor(name + tag, t, torch.float32, shp, device=q.device)
+    if layer_norm:
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d), device=q.device)
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d), device=q.device)
+    else:
+        ln_gamma = ln_beta = None
+    if z is None:
+        z = torch.empty_like(q)
+    _dev_tensor("z", z, q.dtype, q.shape, device=q.device)
+    p = _params(q.unsqueeze(2), mini_batch, eps, layer_norm, residual, True)
+    with torch.cuda.device(q.device):   # the library launches on the current device
+        rc = _lib.lib().ttt_mlp_decode_step(ctypes.byref(p), int(m), int(pos), _ptr(q), _ptr(k),
+                                            _ptr(v), _ptr(eta), *[_ptr(t) for t in state],
+                                            *[_ptr(t) for t in base], _ptr(ln_gamma),
+                                            _ptr(ln_beta), _ptr(z), _stream(q, stream))
+    _lib.check("ttt_mlp_decode_step", rc)
+    return z
+
+
 def ttt_linear_decode_step_compact(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                    eta: torch.Tensor, w_base: torch.Tensor, hist: torch.Tensor,
                                    ln_gamma: Optional[torch.Tensor] = None,

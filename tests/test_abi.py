@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 6
+    assert _lib.abi_version() == 7
     for code in range(7):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
@@ -277,3 +277,30 @@ def test_compact_step_rejects_bad_arguments():
     assert _compact(p, hist=_addr(5)) == _lib.TTT_ERR_ALIAS                # hist == w_base
     assert _compact(p, z=_addr(3)) == _lib.TTT_ERR_ALIAS                   # z == v
     assert _compact(p, wb=_addr(4)) == _lib.TTT_ERR_ALIAS                  # w_base == eta
+
+
+def _mlp_step(p, hidden=256, pos=0, **ptrs):
+    names = ["q", "k", "v", "eta", "w1", "b1", "w2", "b2", "w1b", "b1b", "w2b", "b2b", "g", "b",
+             "z"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    return _lib.lib().ttt_mlp_decode_step(ctypes.byref(p) if p is not None else None, hidden,
+                                          pos, *args, None)
+
+
+def test_mlp_step_rejects_bad_arguments():
+    p = _params(T=1)
+    assert _mlp_step(None) == _lib.TTT_ERR_NULL
+    assert _mlp_step(_params(T=2)) == _lib.TTT_ERR_SHAPE                    # one token per unit
+    assert _mlp_step(p, hidden=0) == _lib.TTT_ERR_SHAPE
+    assert _mlp_step(p, hidden=128) == _lib.TTT_ERR_UNSUPPORTED
+    assert _mlp_step(_params(T=1, d=32)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _mlp_step(p, pos=-1) == _lib.TTT_ERR_ARG
+    assert _mlp_step(p, pos=16) == _lib.TTT_ERR_ARG                         # pos < mini_batch
+    for name in ["q", "k", "v", "eta", "w1", "b1", "w2", "b2", "w1b", "b1b", "w2b", "b2b", "z",
+                 "g", "b"]:
+        assert _mlp_step(p, **{name: None}) == _lib.TTT_ERR_NULL, name
+    assert _mlp_step(p, z=_addr(3)) == _lib.TTT_ERR_ALIAS                   # z == v
+    assert _mlp_step(p, w1=_addr(2)) == _lib.TTT_ERR_ALIAS                  # w1 == k
+    assert _mlp_step(p, b2b=_addr(7)) == _lib.TTT_ERR_ALIAS                 # b2 base == w2
+    assert _mlp_step(p, w1b=_addr(5)) == _lib.TTT_ERR_ALIAS                 # w1 base == w1
+    assert _mlp_step(p, b1=_addr(13)) == _lib.TTT_ERR_ALIAS                 # b1 == gamma
