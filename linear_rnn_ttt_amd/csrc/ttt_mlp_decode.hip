@@ -25,11 +25,13 @@
 //   W1 (64 x 256): wave w, lane l holds column n = 64 (w % 4) + l, rows
 //                  16 (w / 4) .. +16 (the thread's feature quarter);
 //   W2 (256 x 64): wave w holds rows 16 w .. +16, lane l column l.
-// Every load and store of a wave covers one contiguous 256-byte row.
-// Products over features reduce the four quarters through LDS; products
-// over hidden units reduce the sixteen waves through LDS; g_o W2^T (over
-// the features of a W2 row) is a sum across a wave's lanes, on DPP.
-// fp32 arithmetic throughout.
+// Every load and store of a wave covers one contiguous 256-byte row; the
+// state goes through buffer resources, the row offset (wave-uniform) in the
+// scalar offset, so no per-access address arithmetic is needed.  Products
+// over features reduce the four quarters through LDS; products over hidden
+// units reduce the sixteen waves through LDS; g_o W2^T (over the features
+// of a W2 row) is a reduce-scatter across a wave's lanes.  fp32 arithmetic
+// throughout.
 #include "ttt_device.hpp"
 #include "ttt_stream.hpp"
 
@@ -99,6 +101,43 @@ __device__ __forceinline__ void ln_stats(float h, float eps, float& xh, float& r
   xh = xc * rs;
 }
 
+// Buffer resource over `bytes` bytes from `base`; accesses past the end read
+// zero and write nothing.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(float* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(base, (short)0, static_cast<int>(bytes), 0x00020000);
+}
+__device__ __forceinline__ float ld(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff) {
+  return bitsf(__builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0));
+}
+__device__ __forceinline__ void st(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                   float x) {
+  __builtin_amdgcn_raw_buffer_store_b32(fbits(x), r, voff, soff, 0);
+}
+
+// Reduce-scatter of 16 per-lane values over the 64 lanes of the wave: the
+// returned value of lane l is the wave's total of x[l / 4].  Halves of the
+// wave (permlane32 swaps), then its 16-lane rows (permlane16 swaps) take
+// 8 + 4 sums; within a row lanes l and l ^ 8 (rotation by 8), then the
+// mirrored lanes of each half row (they differ in bit 2), then the lanes of
+// a quad finish the sum.
+__device__ __forceinline__ float wave_reduce_scatter16(const float (&x)[16], int l) {
+  float y[8], z[4];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) y[i] = swap32_sum(x[i], x[i + 8]);   // lanes < 32: i, else i + 8
+#pragma unroll
+  for (int i = 0; i < 4; ++i) z[i] = swap16_sum(y[i], y[i + 4]);   // row rho: i + 4 rho
+  const bool b3 = (l >> 3) & 1, b2 = (l >> 2) & 1;
+  const float k0 = b3 ? z[2] : z[0], s0 = b3 ? z[0] : z[2];
+  const float k1 = b3 ? z[3] : z[1], s1 = b3 ? z[1] : z[3];
+  const float u0 = k0 + dpp<0x128>(s0);                            // row_ror:8
+  const float u1 = k1 + dpp<0x128>(s1);
+  const float kk = b2 ? u1 : u0, ss = b2 ? u0 : u1;
+  float v = kk + dpp<0x141>(ss);                                   // row_half_mirror
+  v += dpp<0xB1>(v);
+  v += dpp<0x4E>(v);
+  return v;
+}
+
 // x of lane `src` (wave-uniform) in every lane.
 __device__ __forceinline__ float lane_of(float x, int src) {
   return bitsf(static_cast<uint32_t>(
@@ -118,7 +157,8 @@ __device__ __forceinline__ void gelu2(float x, float& y, float& dy) {
 }
 
 template <bool BF16, bool LN, bool RES>
-__global__ __launch_bounds__(NWV * 64) void ttt_mlp_decode_k(MlpDecodeArgs a) {
+__global__ __launch_bounds__(NWV * 64) __attribute__((amdgpu_waves_per_eu(8)))
+void ttt_mlp_decode_k(MlpDecodeArgs a) {
   __shared__ float sp[2][4][HM];   // per-quarter partials of k W1b and q W1
   __shared__ float sak[HM];        // a = GELU(p) at the base
   __shared__ float saq[HM];        // GELU of the output's hidden layer
@@ -133,33 +173,34 @@ __global__ __launch_bounds__(NWV * 64) void ttt_mlp_decode_k(MlpDecodeArgs a) {
   const int nr = HR * w;             // W2 rows nr .. +HR
   const size_t row = (size_t)unit * DD;
   const size_t o1 = (size_t)unit * DD * HM;
-  float* W1 = a.w1 + o1;
-  float* W2 = a.w2 + o1;
-  float* W1b = a.w1_base + o1;
-  float* W2b = a.w2_base + o1;
+  // this thread's rows: W1 rows FR fq .. +FR, W2 rows nr .. +HR; element
+  // (row r of them, column n of W1 or l of W2) at a constant offset
+  const size_t q1 = o1 + (size_t)FR * fq * HM, q2 = o1 + (size_t)nr * DD;
+  constexpr uint32_t MB1 = FR * HM * 4, MB2 = HR * DD * 4;
+  const auto W1 = rsrc(a.w1 + q1, MB1), W2 = rsrc(a.w2 + q2, MB2);
+  const auto W1b = rsrc(a.w1_base + q1, MB1), W2b = rsrc(a.w2_base + q2, MB2);
+  const uint32_t v1 = n * 4, v2 = l * 4;
+  auto s1 = [](int r) { return static_cast<uint32_t>(r * HM * 4); };
+  auto s2 = [](int r) { return static_cast<uint32_t>(r * DD * 4); };
   float* b1 = a.b1 + (size_t)unit * HM;
   float* b1b = a.b1_base + (size_t)unit * HM;
   float* b2 = a.b2 + row;
   float* b2b = a.b2_base + row;
   const bool fresh = a.pos == 0;
+  // the gradient's base: the state itself when a mini-batch starts
+  const auto R1 = fresh ? W1 : W1b, R2 = fresh ? W2 : W2b;
+  const float* b1s = fresh ? b1 : b1b;
+  const float* b2s = fresh ? b2 : b2b;
 
-  // every load first: the state, the base (j > 0) and the token
-  float w1r[FR], w2r[HR], w1b[FR], w2b[HR];
+  // the base and the token first; the state's rows are loaded as the base's
+  // registers free up, so that two units fit a compute unit's registers
+  float w1b[FR], w2b[HR];
 #pragma unroll
-  for (int r = 0; r < FR; ++r) w1r[r] = W1[(FR * fq + r) * HM + n];
+  for (int r = 0; r < FR; ++r) w1b[r] = ld(R1, v1, s1(r));
 #pragma unroll
-  for (int r = 0; r < HR; ++r) w2r[r] = W2[(nr + r) * DD + l];
-  const float b1n = b1[n];
-  const float b2f = b2[l];
-  float b1bn, b2bf;
-  if (!fresh) {
-#pragma unroll
-    for (int r = 0; r < FR; ++r) w1b[r] = W1b[(FR * fq + r) * HM + n];
-#pragma unroll
-    for (int r = 0; r < HR; ++r) w2b[r] = W2b[(nr + r) * DD + l];
-    b1bn = b1b[n];
-    b2bf = b2b[l];
-  }
+  for (int r = 0; r < HR; ++r) w2b[r] = ld(R2, v2, s2(r));
+  const float b1bn = b1s[n];
+  const float b2bf = b2s[l];
   const float kf = ld_io<BF16>(a.k, row + l);
   const float vf = ld_io<BF16>(a.v, row + l);
   const float qf = ld_io<BF16>(a.q, row + l);
@@ -169,25 +210,26 @@ __global__ __launch_bounds__(NWV * 64) void ttt_mlp_decode_k(MlpDecodeArgs a) {
     gam = a.gamma[(size_t)head * DD + l];
     bet = a.beta[(size_t)head * DD + l];
   }
-  if (fresh) {
+  if (fresh) {   // the state becomes the new mini-batch's base
 #pragma unroll
-    for (int r = 0; r < FR; ++r) w1b[r] = w1r[r];
+    for (int r = 0; r < FR; ++r) st(W1b, v1, s1(r), w1b[r]);
 #pragma unroll
-    for (int r = 0; r < HR; ++r) w2b[r] = w2r[r];
-    b1bn = b1n;
-    b2bf = b2f;
+    for (int r = 0; r < HR; ++r) st(W2b, v2, s2(r), w2b[r]);
+    if (fq == 0) b1b[n] = b1bn;
+    if (w == 0) b2b[l] = b2bf;
   }
 
-  // k W1b and q W1 over this thread's feature quarter (k and q of those
-  // features from the lanes that hold them)
-  float pk = 0.f, pq = 0.f;
+  // k W1b over this thread's feature quarter (k of those features from the
+  // lanes that hold them)
+  float pk = 0.f;
 #pragma unroll
-  for (int r = 0; r < FR; ++r) {
-    pk = __builtin_fmaf(lane_of(kf, FR * fq + r), w1b[r], pk);
-    pq = __builtin_fmaf(lane_of(qf, FR * fq + r), w1r[r], pq);
-  }
+  for (int r = 0; r < FR; ++r) pk = __builtin_fmaf(lane_of(kf, FR * fq + r), w1b[r], pk);
   sp[0][fq][n] = pk;
-  sp[1][fq][n] = pq;
+  // the state's W1 rows (at a mini-batch's start the rows just read, again:
+  // a second read from the cache costs less than holding both copies)
+  float w1r[FR];
+#pragma unroll
+  for (int r = 0; r < FR; ++r) w1r[r] = ld(W1, v1, s1(r));
   __syncthreads();
   const float p = ((sp[0][0][n] + sp[0][1][n]) + (sp[0][2][n] + sp[0][3][n])) + b1bn;
   float an, dn;
@@ -223,41 +265,31 @@ __global__ __launch_bounds__(NWV * 64) void ttt_mlp_decode_k(MlpDecodeArgs a) {
   const float uo = -eta * go;
 
   // g_o W2b^T on this wave's rows (sums over the lanes)
+  static_assert(HR == 16, "one reduce-scatter per wave's W2 rows");
   float gw[HR];
 #pragma unroll
   for (int r = 0; r < HR; ++r) gw[r] = go * w2b[r];
-  wave_sums(gw);
-  if (l == 0) {
+  const float gws = wave_reduce_scatter16(gw, l);
+  if ((l & 3) == 0) sgw[nr + (l >> 2)] = gws;
+  float w2r[HR];   // the state's W2 rows
 #pragma unroll
-    for (int r = 0; r < HR; ++r) sgw[nr + r] = gw[r];
-  }
-
-  // W2 += a^T u_o and b2 += u_o; the base first when a mini-batch starts
+  for (int r = 0; r < HR; ++r) w2r[r] = ld(W2, v2, s2(r));
+  // q W1 over the quarter, from the state before the update
+  float pq = 0.f;
 #pragma unroll
-  for (int r = 0; r < HR; ++r) {
-    if (fresh) W2b[(nr + r) * DD + l] = w2r[r];
-    w2r[r] = __builtin_fmaf(sak[nr + r], uo, w2r[r]);
-    W2[(nr + r) * DD + l] = w2r[r];
-  }
-  const float b2n = b2f + uo;
-  if (w == 0) {
-    if (fresh) b2b[l] = b2f;
-    b2[l] = b2n;
-  }
+  for (int r = 0; r < FR; ++r) pq = __builtin_fmaf(lane_of(qf, FR * fq + r), w1r[r], pq);
+  sp[1][fq][n] = pq;
+  const float b1n = b1[n];   // the state's biases
+  const float b2f = b2[l];
   __syncthreads();
 
   // u_p = -eta (g_o W2b^T) * GELU'(p); W1 += k^T u_p, b1 += u_p
   const float up = -eta * (sgw[n] * dn);
 #pragma unroll
-  for (int r = 0; r < FR; ++r) {
-    if (fresh) W1b[(FR * fq + r) * HM + n] = w1r[r];
-    W1[(FR * fq + r) * HM + n] = __builtin_fmaf(lane_of(kf, FR * fq + r), up, w1r[r]);
-  }
+  for (int r = 0; r < FR; ++r)
+    st(W1, v1, s1(r), __builtin_fmaf(lane_of(kf, FR * fq + r), up, w1r[r]));
   const float b1new = b1n + up;
-  if (fq == 0) {
-    if (fresh) b1b[n] = b1n;
-    b1[n] = b1new;
-  }
+  if (fq == 0) b1[n] = b1new;
   // the output's hidden layer from the old W1 and the rank-1 change
   const float pqn = ((sp[1][0][n] + sp[1][1][n]) + (sp[1][2][n] + sp[1][3][n])) +
                     __builtin_fmaf(qk, up, b1new);
@@ -265,6 +297,14 @@ __global__ __launch_bounds__(NWV * 64) void ttt_mlp_decode_k(MlpDecodeArgs a) {
   gelu2(pqn, aq, daq);
   (void)daq;
   if (fq == 0) saq[n] = aq;
+  // W2 += a^T u_o and b2 += u_o
+#pragma unroll
+  for (int r = 0; r < HR; ++r) {
+    w2r[r] = __builtin_fmaf(sak[nr + r], uo, w2r[r]);
+    st(W2, v2, s2(r), w2r[r]);
+  }
+  const float b2n = b2f + uo;
+  if (w == 0) b2[l] = b2n;
   __syncthreads();
 
   float oq = 0.f;
