@@ -49,10 +49,13 @@ KERNEL_SOURCES = {
     "backward": ["ttt_backward.hip", "ttt_backward.hpp", "ttt_device.hpp"],
     "decode_compact": ["ttt_decode_compact.hip", "ttt_stream.hpp", "ttt_device.hpp"],
     "mlp_decode": ["ttt_mlp_decode.hip", "ttt_stream.hpp", "ttt_device.hpp"],
+    "mlp_decode_compact": ["ttt_mlp_decode_compact.hip", "ttt_mlp_compact.hpp",
+                           "ttt_device.hpp"],
 }
 KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k",
                "backward": "ttt_linear_bwd_k", "decode_compact": "ttt_linear_decode_compact_k",
-               "mlp_decode": "ttt_mlp_decode_k"}
+               "mlp_decode": "ttt_mlp_decode_k",
+               "mlp_decode_compact": "ttt_mlp_decode_compact_k"}
 BACKWARD_METRIC = "TTT-Linear backward tokens/s at 1.3B shape T=8k; % fp32 ALU roofline"
 TRAIN_METRIC = ("TTT-Linear training step (forward saving the bases + backward) tokens/s at "
                 "1.3B shape T=8k; % fp32 ALU roofline of the backward")
@@ -359,9 +362,6 @@ def decode_workload(args):
     from linear_rnn_ttt_amd.inputs import WORKLOADS
 
     w = WORKLOADS[args.workload]
-    if w.kind != "linear" and getattr(args, "compact", False):
-        raise SystemExit("bench.py: the compact streaming step is TTT-Linear's (workload %s is "
-                         "%s)" % (w.name, w.kind))
     if args.batch:
         w = w.with_(B=args.batch)
     return w
@@ -375,15 +375,18 @@ def decode_tag(w, compact=False) -> str:
 
 def decode_compact_bytes(w) -> int:
     """Algorithmic bytes of one compact streaming step over all units,
-    averaged over the b positions of a mini-batch: the base read (d^2 fp32),
-    the history rows s < j read and row j written (2 d fp32 each), at j = 0
-    the fold (all b rows read, the base written), q, k, v read and z written
-    (4 d io elements), eta (4 B)."""
+    averaged over the b positions of a mini-batch: the base read (d^2 fp32
+    for TTT-Linear, 2 d m + m + d for TTT-MLP), the history rows s < j read
+    and row j written (2 d fp32 each for TTT-Linear, 2 d + 2 m for TTT-MLP),
+    at j = 0 the fold (all b rows read, the base written), q, k, v read and z
+    written (4 d io elements), eta (4 B)."""
     es = 2 if w.io == "bf16" else 4
     b, d = w.mini_batch, w.d
-    row = 2 * d * 4
-    per_pos = [d * d * 4 + (d * d * 4 + b * row if j == 0 else j * row) + row
-               for j in range(b)]
+    if w.kind == "linear":
+        base, row = d * d * 4, 2 * d * 4
+    else:
+        base, row = (2 * d * w.hidden + w.hidden + d) * 4, (2 * d + 2 * w.hidden) * 4
+    per_pos = [base + (base + b * row if j == 0 else j * row) + row for j in range(b)]
     return w.B * w.H * (sum(per_pos) // b + 4 * d * es + 4)
 
 
@@ -417,7 +420,7 @@ def run_decode(args) -> dict:
     import torch
 
     from linear_rnn_ttt_amd import (ttt_linear_decode_step, ttt_linear_decode_step_compact,
-                                    ttt_mlp_decode_step)
+                                    ttt_mlp_decode_step, ttt_mlp_decode_step_compact)
     from linear_rnn_ttt_amd.inputs import make_inputs
 
     w = decode_workload(args)
@@ -433,6 +436,8 @@ def run_decode(args) -> dict:
         S = [dev[x].expand((B, H) + dev[x].shape[1:]).contiguous()
              for x in ("w1", "b1", "w2", "b2")]
         Sb = [torch.zeros_like(x) for x in S]
+        hist = torch.zeros((B, H, w.mini_batch, 2 * d + 2 * w.hidden), dtype=torch.float32,
+                           device="cuda")
     else:
         W = dev["w0"].expand(B, H, d, d).contiguous()
         Wb = torch.zeros_like(W)
@@ -441,7 +446,11 @@ def run_decode(args) -> dict:
 
     def step(t):
         q, k, v, eta = toks[t]
-        if mlp:
+        if mlp and compact:   # S holds the base, hist the mini-batch's rows
+            ttt_mlp_decode_step_compact(q, k, v, eta, S, hist, dev["gamma"], dev["beta"],
+                                        pos=t % w.mini_batch, mini_batch=w.mini_batch, eps=w.eps,
+                                        z=z)
+        elif mlp:
             ttt_mlp_decode_step(q, k, v, eta, S, Sb, dev["gamma"], dev["beta"],
                                 pos=t % w.mini_batch, mini_batch=w.mini_batch, eps=w.eps, z=z)
         elif compact:   # W holds the base, hist the mini-batch's rows
@@ -475,11 +484,14 @@ def run_decode(args) -> dict:
     avg_launch_s = start.elapsed_time(end) / args.steps / 1e3
     ms_per_step = wall / args.steps * 1e3
     byts = decode_compact_bytes(w) if compact else decode_bytes(w)
-    kind = "decode_compact" if compact else ("mlp_decode" if mlp else "decode")
+    kind = ("mlp_" if mlp else "") + ("decode_compact" if compact else "decode")
     achieved = byts / avg_launch_s / 1e9
     if mlp:
-        launch, pending = ("ttt_mlp_decode_step: one 1024-thread workgroup per (stream, head) "
-                           "unit, steps replayed from one HIP graph", "S and S_base")
+        launch = (("ttt_mlp_decode_step_compact" if compact else "ttt_mlp_decode_step") +
+                  ": one 1024-thread workgroup per (stream, head) unit, steps replayed from one "
+                  "HIP graph")
+        pending = ("compact: base + the mini-batch's (k, u1, a, u2) rows" if compact
+                   else "S and S_base")
     else:
         launch = (("ttt_linear_decode_step_compact" if compact else "ttt_linear_decode_step") +
                   ": one 256-thread workgroup per (stream, head) unit, steps replayed from one "
@@ -777,8 +789,8 @@ def _profiled(args):
     if args.decode:
         w = decode_workload(args)
         if args.compact:
-            return ("decode_compact", decode_tag(w, True), decode_compact_bytes(w),
-                    decode_flops(w))
+            return (("mlp_" if w.kind == "mlp" else "") + "decode_compact", decode_tag(w, True),
+                    decode_compact_bytes(w), decode_flops(w))
         return ("mlp_decode" if w.kind == "mlp" else "decode", decode_tag(w), decode_bytes(w),
                 decode_flops(w))
     if args.backward:

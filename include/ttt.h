@@ -60,7 +60,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 7
+#define TTT_ABI_VERSION 8
 
 typedef enum {
   TTT_OK = 0,
@@ -314,6 +314,34 @@ ttt_status ttt_mlp_decode_step(const ttt_params* p, int32_t hidden, int32_t pos,
                                float* w2_base, float* b2_base,
                                const float* ln_gamma, const float* ln_beta,
                                void* z, void* hip_stream);
+
+/*
+ * The TTT-MLP streaming step of ttt_mlp_decode_step with a compact pending
+ * state: the same tokens, the same z (up to rounding order).  Within a
+ * mini-batch the state after the tokens s < pos is the base plus rank-1
+ * terms, W1 = w1_base + sum_s k_s^T u1_s, b1 = b1_base + sum_s u1_s,
+ * W2 = w2_base + sum_s a_s^T u2_s, b2 = b2_base + sum_s u2_s, with
+ * u1 = -eta * dl/dp, u2 = -eta * dl/do and a = GELU(k W1 + b1), all at the
+ * base; the stream carries the base and these rows instead of the state:
+ *   w1_base [B,H,d,m], b1_base [B,H,m], w2_base [B,H,m,d], b2_base [B,H,d]
+ *           fp32, read; at pos == 0 first replaced by the base plus all
+ *           mini_batch history slots (the previous mini-batch).
+ *   hist    [B,H,mini_batch,2d+2m] fp32: slot s holds k_s[d], u1_s[m],
+ *           a_s[m], u2_s[d]; slot pos is written.  Zero it when a stream
+ *           starts.
+ * About 165 KB move per unit and token for mini_batch = 16 (397 KB for the
+ * (S, S_base) form).  The final state of a ttt_mlp_forward over a whole
+ * number of mini-batches starts a stream as the base with a zero history.
+ *   p   T must be 1; mini_batch at most 16 (TTT_ERR_UNSUPPORTED).
+ * Other arguments, aliasing and errors as ttt_mlp_decode_step.
+ */
+ttt_status ttt_mlp_decode_step_compact(const ttt_params* p, int32_t hidden, int32_t pos,
+                                       const void* q, const void* k, const void* v,
+                                       const float* eta,
+                                       float* w1_base, float* b1_base,
+                                       float* w2_base, float* b2_base, float* hist,
+                                       const float* ln_gamma, const float* ln_beta,
+                                       void* z, void* hip_stream);
 
 /* Static, NUL-terminated description of a status code. */
 const char* ttt_status_string(ttt_status s);

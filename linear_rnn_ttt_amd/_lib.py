@@ -18,7 +18,8 @@ TTT_NO_LN, TTT_NO_RESIDUAL, TTT_BASES_SAVED = 1, 2, 4
 EXPORTS = ("ttt_linear_forward", "ttt_linear_split_workspace_bytes", "ttt_linear_forward_split",
            "ttt_linear_decode_step", "ttt_linear_decode_step_compact", "ttt_linear_forward_save",
            "ttt_linear_backward_workspace_bytes", "ttt_linear_backward",
-           "ttt_mlp_forward", "ttt_mlp_decode_step", "ttt_status_string", "ttt_abi_version")
+           "ttt_mlp_forward", "ttt_mlp_decode_step",
+           "ttt_mlp_decode_step_compact", "ttt_status_string", "ttt_abi_version")
 
 
 class TTTParams(ctypes.Structure):
@@ -59,6 +60,9 @@ def lib() -> ctypes.CDLL:
     L.ttt_mlp_decode_step.argtypes = ([ctypes.POINTER(TTTParams), ctypes.c_int32, ctypes.c_int32]
                                       + [P] * 16)
     L.ttt_mlp_decode_step.restype = ctypes.c_int
+    L.ttt_mlp_decode_step_compact.argtypes = ([ctypes.POINTER(TTTParams), ctypes.c_int32,
+                                               ctypes.c_int32] + [P] * 13)
+    L.ttt_mlp_decode_step_compact.restype = ctypes.c_int
     L.ttt_linear_forward_save.argtypes = ([ctypes.POINTER(TTTParams)] + [P] * 10 +
                                           [ctypes.c_uint64, P])
     L.ttt_linear_forward_save.restype = ctypes.c_int

@@ -14,7 +14,8 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libttt_amd.so")
 SOURCES = ["ttt_api.cpp", "ttt_linear.hip", "ttt_mlp.hip", "ttt_decode.hip", "ttt_decode_compact.hip", "ttt_backward.hip",
-           "ttt_mlp_decode.hip"]
+           "ttt_mlp_decode.hip",
+           "ttt_mlp_decode_compact.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU instructions are disabled on purpose: the kernels are

@@ -12,6 +12,7 @@
 #include "ttt_backward.hpp"
 #include "ttt_kernels.hpp"
 #include "ttt_stream.hpp"
+#include "ttt_mlp_compact.hpp"
 
 namespace {
 
@@ -384,6 +385,73 @@ ttt_status ttt_mlp_decode_step(const ttt_params* p, int32_t hidden, int32_t pos,
   const hipError_t e = tttk::launch_mlp_decode(a, p->io_dtype == TTT_BF16, ln,
                                                !(p->flags & TTT_NO_RESIDUAL),
                                                static_cast<hipStream_t>(hip_stream));
+  return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
+}
+
+ttt_status ttt_mlp_decode_step_compact(const ttt_params* p, int32_t hidden, int32_t pos,
+                                       const void* q, const void* k, const void* v,
+                                       const float* eta, float* w1_base, float* b1_base,
+                                       float* w2_base, float* b2_base, float* hist,
+                                       const float* ln_gamma, const float* ln_beta, void* z,
+                                       void* hip_stream) {
+  uint64_t elems = 0;
+  const ttt_status st = check_common(p, &elems);
+  if (st != TTT_OK) return st;
+  if (p->T != 1) return TTT_ERR_SHAPE;  // one token per unit
+  if (hidden < 1) return TTT_ERR_SHAPE;
+  if (hidden != kMlpHidden || p->mini_batch > 16) return TTT_ERR_UNSUPPORTED;
+  if (pos < 0 || pos >= p->mini_batch) return TTT_ERR_ARG;
+  const bool ln = !(p->flags & TTT_NO_LN);
+  float* state[5] = {w1_base, b1_base, w2_base, b2_base, hist};
+  if (!q || !k || !v || !eta || !z) return TTT_ERR_NULL;
+  for (float* s : state)
+    if (!s) return TTT_ERR_NULL;
+  if (ln && (!ln_gamma || !ln_beta)) return TTT_ERR_NULL;
+
+  const uint64_t es = p->io_dtype == TTT_BF16 ? 2 : 4;
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t dm = static_cast<uint64_t>(kHeadDim) * hidden;
+  const uint64_t slot = 2ull * kHeadDim + 2ull * hidden;
+  const uint64_t sizes[5] = {units * dm * 4, units * hidden * 4ull, units * dm * 4,
+                             units * kHeadDim * 4ull,
+                             units * static_cast<uint64_t>(p->mini_batch) * slot * 4};
+  const Range rq = span(q, elems * es), rk = span(k, elems * es), rv = span(v, elems * es);
+  const Range re = span(eta, units * 4), rz = span(z, elems * es);
+  const Range rg = span(ln ? ln_gamma : nullptr, p->H * 256ull);
+  const Range rbe = span(ln ? ln_beta : nullptr, p->H * 256ull);
+  Range rs[6];
+  for (int i = 0; i < 5; ++i) rs[i] = span(state[i], sizes[i]);
+  rs[5] = rz;
+  const Range inputs[] = {rq, rk, rv, re, rg, rbe};
+  for (const Range& w : rs) {
+    for (const Range& r : inputs)
+      if (overlap(w, r)) return TTT_ERR_ALIAS;
+  }
+  for (int i = 0; i < 6; ++i)
+    for (int j = i + 1; j < 6; ++j)
+      if (overlap(rs[i], rs[j])) return TTT_ERR_ALIAS;
+
+  tttk::MlpCompactArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.eta = eta;
+  a.w1_base = w1_base;
+  a.b1_base = b1_base;
+  a.w2_base = w2_base;
+  a.b2_base = b2_base;
+  a.hist = hist;
+  a.gamma = ln_gamma;
+  a.beta = ln_beta;
+  a.z = z;
+  a.B = p->B;
+  a.H = p->H;
+  a.pos = pos;
+  a.mb = p->mini_batch;
+  a.eps = p->ln_eps;
+  const hipError_t e = tttk::launch_mlp_decode_compact(a, p->io_dtype == TTT_BF16, ln,
+                                                       !(p->flags & TTT_NO_RESIDUAL),
+                                                       static_cast<hipStream_t>(hip_stream));
   return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
 }
 

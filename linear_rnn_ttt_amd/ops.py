@@ -231,6 +231,49 @@ def ttt_mlp_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: 
     return z
 
 
+def ttt_mlp_decode_step_compact(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                eta: torch.Tensor, base, hist: torch.Tensor,
+                                ln_gamma: Optional[torch.Tensor] = None,
+                                ln_beta: Optional[torch.Tensor] = None, *, pos: int,
+                                mini_batch: int = 16, eps: float = 1e-6,
+                                layer_norm: bool = True, residual: bool = True,
+                                z: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """The TTT-MLP streaming step with a compact pending state; returns z
+    [B,H,d].  base = (w1, b1, w2, b2) fp32 (the mini-batch's base) and hist
+    [B,H,mini_batch,2d+2m] fp32 (its rows k, u1, a, u2; zero at a stream's
+    start) are updated in place.  See include/ttt.h."""
+    _dev_tensor("q", q)
+    if q.dim() != 3:
+        raise ValueError("q must be [B, H, d] (one token per unit)")
+    B, H, d = q.shape
+    _dev_tensor("k", k, q.dtype, q.shape, device=q.device)
+    _dev_tensor("v", v, q.dtype, q.shape, device=q.device)
+    _dev_tensor("eta", eta, torch.float32, (B, H), device=q.device)
+    if len(base) != 4:
+        raise ValueError("base is (w1, b1, w2, b2)")
+    m = base[0].shape[-1] if base[0].dim() == 4 else -1
+    shapes = ((B, H, d, m), (B, H, m), (B, H, m, d), (B, H, d))
+    for name, t, shp in zip(("w1", "b1", "w2", "b2"), base, shapes):
+        _dev_tensor(name + "_base", t, torch.float32, shp, device=q.device)
+    _dev_tensor("hist", hist, torch.float32, (B, H, mini_batch, 2 * d + 2 * m), device=q.device)
+    if layer_norm:
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d), device=q.device)
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d), device=q.device)
+    else:
+        ln_gamma = ln_beta = None
+    if z is None:
+        z = torch.empty_like(q)
+    _dev_tensor("z", z, q.dtype, q.shape, device=q.device)
+    p = _params(q.unsqueeze(2), mini_batch, eps, layer_norm, residual, True)
+    with torch.cuda.device(q.device):   # the library launches on the current device
+        rc = _lib.lib().ttt_mlp_decode_step_compact(
+            ctypes.byref(p), int(m), int(pos), _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+            *[_ptr(t) for t in base], _ptr(hist), _ptr(ln_gamma), _ptr(ln_beta), _ptr(z),
+            _stream(q, stream))
+    _lib.check("ttt_mlp_decode_step_compact", rc)
+    return z
+
+
 def ttt_linear_decode_step_compact(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
                                    eta: torch.Tensor, w_base: torch.Tensor, hist: torch.Tensor,
                                    ln_gamma: Optional[torch.Tensor] = None,

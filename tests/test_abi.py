@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 7
+    assert _lib.abi_version() == 8
     for code in range(7):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
@@ -304,3 +304,27 @@ def test_mlp_step_rejects_bad_arguments():
     assert _mlp_step(p, b2b=_addr(7)) == _lib.TTT_ERR_ALIAS                 # b2 base == w2
     assert _mlp_step(p, w1b=_addr(5)) == _lib.TTT_ERR_ALIAS                 # w1 base == w1
     assert _mlp_step(p, b1=_addr(13)) == _lib.TTT_ERR_ALIAS                 # b1 == gamma
+
+
+def _mlp_compact(p, hidden=256, pos=0, **ptrs):
+    names = ["q", "k", "v", "eta", "w1b", "b1b", "w2b", "b2b", "hist", "g", "b", "z"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    return _lib.lib().ttt_mlp_decode_step_compact(ctypes.byref(p) if p is not None else None,
+                                                  hidden, pos, *args, None)
+
+
+def test_mlp_compact_step_rejects_bad_arguments():
+    p = _params(T=1)
+    assert _mlp_compact(None) == _lib.TTT_ERR_NULL
+    assert _mlp_compact(_params(T=2)) == _lib.TTT_ERR_SHAPE
+    assert _mlp_compact(p, hidden=0) == _lib.TTT_ERR_SHAPE
+    assert _mlp_compact(p, hidden=512) == _lib.TTT_ERR_UNSUPPORTED
+    assert _mlp_compact(_params(T=1, mini_batch=17)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _mlp_compact(_params(T=1, d=32)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _mlp_compact(p, pos=-1) == _lib.TTT_ERR_ARG
+    assert _mlp_compact(p, pos=16) == _lib.TTT_ERR_ARG
+    for name in ["q", "k", "v", "eta", "w1b", "b1b", "w2b", "b2b", "hist", "z", "g", "b"]:
+        assert _mlp_compact(p, **{name: None}) == _lib.TTT_ERR_NULL, name
+    assert _mlp_compact(p, hist=_addr(5)) == _lib.TTT_ERR_ALIAS             # hist == w1 base
+    assert _mlp_compact(p, z=_addr(1)) == _lib.TTT_ERR_ALIAS                # z == q
+    assert _mlp_compact(p, b2b=_addr(4)) == _lib.TTT_ERR_ALIAS              # b2 base == eta
