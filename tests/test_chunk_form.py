@@ -174,3 +174,63 @@ def test_mlp_chunk_form_matches_oracle(T):
     assert np.abs(zc - z[0, 0]).max() <= 1e-12 * np.abs(z).max()
     for a, c in zip(S, Sc):
         assert np.abs(a[0, 0] - c).max() <= 1e-12 * max(np.abs(a).max(), 1e-30)
+
+
+def compact_mlp_stream(q, k, v, eta, S0, gamma, beta, b, eps):
+    """The TTT-MLP streaming step with a compact pending state, one token at a
+    time in fp64, as the compact kernel keeps its books: the stream carries
+    the base and one row (k, u1, a, u2) per token of the current mini-batch;
+    at position 0 the rows fold into the base (zero rows at the start); the
+    output adds the rank-1 terms of the rows s <= j to the base's products.
+    Returns z, the base and the rows still pending."""
+    W1, b1, W2, b2 = (s.copy() for s in S0)
+    T, d = q.shape
+    m = W1.shape[1]
+    rows = np.zeros((b, 2 * d + 2 * m))
+    z = np.zeros_like(q)
+    for t in range(T):
+        j = t % b
+        if j == 0:
+            K, U1 = rows[:, :d], rows[:, d:d + m]
+            A, U2 = rows[:, d + m:d + 2 * m], rows[:, d + 2 * m:]
+            W1, b1 = W1 + K.T @ U1, b1 + U1.sum(0)
+            W2, b2 = W2 + A.T @ U2, b2 + U2.sum(0)
+        p = k[t] @ W1 + b1
+        a = _gelu(p)
+        y, xh, sig = _ln(a @ W2 + b2, gamma, beta, eps)
+        go = _ln_bwd(2 * (k[t] + y - v[t]), xh, sig, gamma)
+        u1 = -eta[t] * (W2 @ go) * _gelu_grad(p)
+        u2 = -eta[t] * go
+        rows[j] = np.concatenate([k[t], u1, a, u2])
+        R = rows[:j + 1]
+        pq = q[t] @ W1 + b1 + (R[:, :d] @ q[t] + 1) @ R[:, d:d + m]
+        aq = _gelu(pq)
+        oq = aq @ W2 + b2 + (R[:, d + m:d + 2 * m] @ aq + 1) @ R[:, d + 2 * m:]
+        z[t] = q[t] + _ln(oq, gamma, beta, eps)[0]
+    return z, (W1, b1, W2, b2), rows[:(T - 1) % b + 1]
+
+
+@pytest.mark.parametrize("T,b", [(45, 16), (48, 16), (23, 5), (9, 1)])
+def test_mlp_compact_stream_matches_oracle(T, b):
+    """The compact stream's bookkeeping (the fold at position 0, zero rows at
+    the start, the pending rows at the end) reproduces the oracle's scan: z of
+    every token, and the final state rebuilt from the base and pending rows."""
+    rng = np.random.default_rng(75 + b)
+    d, m = 16, 64
+    q, k, v, eta = _inputs(rng, T, d, 0.5)
+    S0 = [(0.1 * rng.standard_normal(s)).astype(np.float32)
+          for s in ((1, d, m), (1, m), (1, m, d), (1, d))]
+    gamma = (1 + 0.1 * rng.standard_normal((1, d))).astype(np.float32)
+    beta = (0.1 * rng.standard_normal((1, d))).astype(np.float32)
+    z, S = oracle.mlp(q, k, v, eta, *S0, gamma, beta, mini_batch=b)
+    f = lambda a: a.astype(np.float64)
+    zc, base, rows = compact_mlp_stream(f(q[0, 0]), f(k[0, 0]), f(v[0, 0]), f(eta[0, 0]),
+                                        [f(s[0]) for s in S0], f(gamma[0]), f(beta[0]), b,
+                                        1e-6)
+    assert np.abs(zc - z[0, 0]).max() <= 1e-12 * np.abs(z).max()
+    K, U1 = rows[:, :d], rows[:, d:d + m]
+    A, U2 = rows[:, d + m:d + 2 * m], rows[:, d + 2 * m:]
+    rebuilt = (base[0] + K.T @ U1, base[1] + U1.sum(0), base[2] + A.T @ U2,
+               base[3] + U2.sum(0))
+    for a, c in zip(S, rebuilt):
+        assert np.abs(a[0, 0] - c).max() <= 1e-12 * max(np.abs(a).max(), 1e-30)
