@@ -128,7 +128,8 @@ def test_mlp_decode_bench_shape(streams):
     assert ez <= TOL["bf16"] and max(es) <= TOL["bf16"]
 
 
-def test_mlp_decode_graph_replay():
+@pytest.mark.parametrize("compact", [False, True], ids=["S_base", "compact"])
+def test_mlp_decode_graph_replay(compact):
     """Steps captured into a HIP graph and replayed give the eager steps'
     results bit for bit (the replay is how a generation loop runs them)."""
     inp = make_inputs(MLP, B=2, H=3, T=20)
@@ -136,13 +137,19 @@ def test_mlp_decode_graph_replay():
     toks = [[dev[x][:, :, t].contiguous() for x in ("q", "k", "v", "eta")] for t in range(20)]
     S0 = _initial(inp, 2, 3)
 
-    def run(S, base, z, t_from, t_to):
+    def run(S, aux, z, t_from, t_to):
         for t in range(t_from, t_to):
-            ttt_mlp_decode_step(*toks[t], S, base, dev["gamma"], dev["beta"], pos=t % 16,
-                                z=z[t])
+            if compact:
+                ttt_mlp_decode_step_compact(*toks[t], S, aux[0], dev["gamma"], dev["beta"],
+                                            pos=t % 16, z=z[t])
+            else:
+                ttt_mlp_decode_step(*toks[t], S, aux, dev["gamma"], dev["beta"], pos=t % 16,
+                                    z=z[t])
 
     def fresh():
-        return ([s.clone() for s in S0], [torch.zeros_like(s) for s in S0],
+        aux = ([torch.zeros((2, 3, 16, 640), dtype=torch.float32, device="cuda")] if compact
+               else [torch.zeros_like(s) for s in S0])
+        return ([s.clone() for s in S0], aux,
                 torch.empty((20,) + toks[0][0].shape, dtype=torch.bfloat16, device="cuda"))
 
     Se, be, ze = fresh()
