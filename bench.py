@@ -905,7 +905,7 @@ def main(argv=None):
                                        args, *args.pmc_commands))
         return 0
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU (the scan shards over "
+        print("bench.py: the benchmark runs on exactly one GPU (the scan shards over "
               "independent (batch, head) units with no exchange; multi-GPU runs are not "
               "provided). Use --gpus 1.", file=sys.stderr)
         return 2
