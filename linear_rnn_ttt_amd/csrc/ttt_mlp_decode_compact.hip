@@ -41,6 +41,7 @@ constexpr int MBM = 16;        // history slots held in LDS (mini-batch <= 16)
 constexpr int SLOT = 2 * DD + 2 * HM;                              // floats per slot
 constexpr int OK = 0, OU1 = DD, OA = DD + HM, OU2 = DD + 2 * HM;   // k, u1, a, u2
 static_assert(MBM == NWV, "wave w takes the dot product with slot w");
+using LdsPtr = __attribute__((address_space(3))) void*;
 
 template <bool BF16>
 __device__ __forceinline__ float ld_io(const void* p, size_t i) {
@@ -187,7 +188,16 @@ void ttt_mlp_decode_compact_k(MlpCompactArgs a) {
   for (int r = 0; r < HR; ++r) w2b[r] = ld(W2b, v2, s2(r));
   float b1bn = b1b[n];
   float b2bf = b2b[l];
-  for (int e = tid; e < nh * SLOT; e += NWV * 64) hs[e / SLOT][e % SLOT] = hist[e];
+  {  // the slots, contiguous in LDS as in memory, copied straight from memory
+     // into LDS (global_load_lds: lane l of a wave lands at word l of the
+     // wave's 64-word chunk; no registers, and every chunk in flight at once)
+    const int ne = nh * SLOT;
+    for (int i = 0; i * NWV * 64 < ne; ++i) {
+      const int e = i * NWV * 64 + tid;
+      LdsPtr dst = (LdsPtr)(&hs[0][0] + i * NWV * 64 + w * 64);
+      if (e < ne) __builtin_amdgcn_global_load_lds(hist + e, dst, 4, 0, 0);
+    }
+  }
   const float kf = ld_io<BF16>(a.k, row + l);
   const float vf = ld_io<BF16>(a.v, row + l);
   const float qf = ld_io<BF16>(a.q, row + l);
