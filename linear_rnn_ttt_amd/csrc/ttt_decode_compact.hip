@@ -31,6 +31,7 @@ constexpr int DD = 64;
 constexpr int DW = 4;
 constexpr int RW = DD / DW;
 constexpr int MB_MAX = 64;   // history slots of the largest instance
+using LdsPtr = __attribute__((address_space(3))) void*;
 
 template <bool BF16>
 __device__ __forceinline__ float ld_io(const void* p, size_t i) {
@@ -118,9 +119,11 @@ __global__ __launch_bounds__(DW * 64) void ttt_linear_decode_compact_k(CompactAr
     kr[r] = ld_io<BF16>(a.k, row + w * RW + r);
     qr[r] = ld_io<BF16>(a.q, row + w * RW + r);
   }
-  for (int e = tid; e < nh * DD; e += DW * 64) {
-    hk[e / DD][e % DD] = hist[(e / DD) * 2 * DD + e % DD];
-    hu[e / DD][e % DD] = hist[(e / DD) * 2 * DD + DD + e % DD];
+  // the history rows straight from memory into LDS (global_load_lds: lane f
+  // of the wave lands at word f of the row; all rows in flight at once)
+  for (int s = w; s < nh; s += DW) {
+    __builtin_amdgcn_global_load_lds(hist + s * 2 * DD + f, (LdsPtr)&hk[s][0], 4, 0, 0);
+    __builtin_amdgcn_global_load_lds(hist + s * 2 * DD + DD + f, (LdsPtr)&hu[s][0], 4, 0, 0);
   }
   const float kf = ld_io<BF16>(a.k, row + f);
   const float vf = ld_io<BF16>(a.v, row + f);
