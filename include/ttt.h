@@ -109,7 +109,7 @@ ttt_status ttt_linear_forward(const ttt_params* p,
 
 /*
  * Bytes of device workspace that ttt_linear_forward_split needs for these
- * parameters: 256 bytes per unit plus 256, and 4 KB per unit and 16-token
+ * parameters: 256 bytes per unit plus 256, and 6 KB per unit and 16-token
  * tile (0 if p fails the common checks).
  */
 uint64_t ttt_linear_split_workspace_bytes(const ttt_params* p);

@@ -55,7 +55,7 @@ ttt_status check_common(const ttt_params* p, uint64_t* elems) {
 }
 
 // Workspace of a split Linear launch: publication counters (two 128-byte
-// lines per unit), 32 error words, then the gradient stream (4 KB per
+// lines per unit), 32 error words, then the gradient stream (6 KB per
 // 16-token tile and unit).
 struct SplitLayout {
   uint64_t stream_offset, total;
@@ -66,7 +66,7 @@ SplitLayout split_layout(const ttt_params* p) {
   const uint64_t tiles = (static_cast<uint64_t>(p->T) + 15) / 16;
   SplitLayout ly;
   ly.stream_offset = (units * 256 + 128 + 255) / 256 * 256;
-  ly.total = ly.stream_offset + units * tiles * 4096;
+  ly.total = ly.stream_offset + units * tiles * 6144;
   return ly;
 }
 

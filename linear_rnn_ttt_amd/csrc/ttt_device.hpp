@@ -75,6 +75,30 @@ __device__ __forceinline__ Split4 split4(f32x4 x) {
   return s;
 }
 
+// x = hi + mid + lo, each part the bf16 rounding of what the parts before it
+// leave: about 24 significant bits (fp32 precision) in three bf16 operands.
+struct Split4x3 {
+  u32x2 hi, mid, lo;
+};
+__device__ __forceinline__ Split4x3 split4x3(f32x4 x) {
+  Split4x3 s;
+  s.hi.x = pack_bf16(x[0], x[1]);
+  s.hi.y = pack_bf16(x[2], x[3]);
+  float r0 = x[0] - bf16_lo_to_f32(s.hi.x);
+  float r1 = x[1] - bf16_hi_to_f32(s.hi.x);
+  float r2 = x[2] - bf16_lo_to_f32(s.hi.y);
+  float r3 = x[3] - bf16_hi_to_f32(s.hi.y);
+  s.mid.x = pack_bf16(r0, r1);
+  s.mid.y = pack_bf16(r2, r3);
+  r0 -= bf16_lo_to_f32(s.mid.x);
+  r1 -= bf16_hi_to_f32(s.mid.x);
+  r2 -= bf16_lo_to_f32(s.mid.y);
+  r3 -= bf16_hi_to_f32(s.mid.y);
+  s.lo.x = pack_bf16(r0, r1);
+  s.lo.y = pack_bf16(r2, r3);
+  return s;
+}
+
 __device__ __forceinline__ u32x4 cat(u32x2 a, u32x2 b) { return u32x4{a.x, a.y, b.x, b.y}; }
 
 // Workgroup barrier that orders LDS only (release/acquire fences on the

@@ -51,10 +51,18 @@
 //   * Per-feature scalings are products with diagonal tiles on the matrix
 //     unit (u = 2 gamma (k - v) + 2 gamma beta, q + beta); dot products of a
 //     row with w_bar and 2 gamma are one product with a constant A operand.
-//   * fp32 operands enter the bf16 matrix unit as hi + lo bf16 pairs (about
-//     16 significant bits); bf16 inputs are exact.  The output correction of
-//     bf16 data uses the hi part of the score tile only: its error does not
-//     feed back into the state.
+//   * fp32 operands enter the bf16 matrix unit as sums of bf16 parts; bf16
+//     inputs are exact.  Everything that feeds back into the state carries
+//     three parts (hi + mid + lo, about 24 significant bits, fp32 level):
+//     W in the gradient point K W, -eta G in the update K^T (-eta G), and
+//     both operands of the chain's corrections (score tile and -eta G, six
+//     products paired into three 16x16x32 products).  With two parts (about
+//     16 bits) the rounding was amplified along the sequence on
+//     ill-conditioned units (1.3B-shaped layer at T = 8192: z error 1e-1
+//     where a plain fp32 evaluation of the same chunked form stays near the
+//     bf16 floor of z).  The output side does not feed back: Q W uses
+//     hi + mid, the output correction of bf16 data the hi part of the score
+//     tile only.
 //   * Row m of the state's accumulator tile r holds input feature
 //     32 (r/2) + 8 (m/4) + 4 (r%2) + m%4, so the 8 contraction slots of a
 //     lane in a 16x16x32 product with W are 8 consecutive features: every
@@ -88,15 +96,18 @@ struct LinCfg {
 
 template <bool BF16>
 struct LinLds {
-  Stage<BF16, LinCfg<BF16>::TB> st;
+  static constexpr int TB = LinCfg<BF16>::TB;
+  Stage<BF16, TB> st;
   // chain LN partial sums around the shift [parity][wave][token]: (sum e,
   // sum e^2, sum gamma^2 e, sum gamma^2 e^2); lane c reads the 16-byte row
   // of token c.  xu[parity][token][wave]: sum u e.
   f32x4 xc[2][4][16];
   f32x4 xu[2][16];
-  u32x4 gtb[2][4][64];  // (-eta G_t)^T as [hi, lo], chain wave -> update and output waves
+  u32x4 gtb[2][4][64];  // (-eta G_t)^T as [hi, mid], chain wave -> update and output waves
+  u32x2 gtl[2][4][64];  // its lo part
   f32x4 bkb[2][4][64];  // (K_{t+2} W_{t-1})^T, update wave -> chain wave
-  u32x4 grb[2][2][64];  // K_{t+1} K_{t+2}^T, K_t K_{t+2}^T as [hi, lo]
+  u32x4 grb[2][2][64];  // K_{t+1} K_{t+2}^T, K_t K_{t+2}^T as [hi, mid]
+  u32x2 grl[2][2][64];  // their lo parts
   f32x2 tkb[2][16];     // per token of tile t+2: (k . w_bar, sum_f u_f)
   f32x4 hqb[2][4][64];  // output pre-activation of tile t-1 around its shift,
                         // update wave -> output wave
@@ -106,16 +117,19 @@ struct LinLds {
   float mqm[2][16];     // q . w_bar per token of tile t, update wave 2 -> every update wave
   u32x2 ktb[2][4][64];  // K_t^T as 16x16x16 A operands (bf16 data, split units),
                         // update wave 2 -> every update wave
-  uint16_t cst[4][D];   // bf16 rows: w_bar hi, 2 gamma hi, w_bar lo, 2 gamma lo
+  uint16_t cst[8][D];   // bf16 rows: w_bar hi, 2 gamma hi, w_bar mid, 2 gamma mid,
+                        // w_bar lo, 2 gamma lo, zero, zero
 };
 
 // LDS of the output workgroup of a split unit: q and k staged in blocks of
-// TB tiles, the unit's gradient stream staged in the same blocks, and the
-// exchanges of the output side.
+// TB = 4 tiles, the unit's gradient stream staged in the same blocks, and
+// the exchanges of the output side.
 template <bool BF16>
 struct OutLds {
-  Stage<BF16, LinCfg<BF16>::TB, 2> st;    // q, k
-  u32x4 gst[2][LinCfg<BF16>::TB][4][64];  // (-eta G)^T as [hi, lo]: [buffer][tile][column block][lane]
+  static constexpr int TB = 4;
+  Stage<BF16, TB, 2> st;    // q, k
+  u32x4 gst[2][TB][4][64];  // (-eta G)^T as [hi, mid]: [buffer][tile][column block][lane]
+  u32x4 gsl[2][TB][2][64];  // lo parts, column blocks (2j, 2j+1) as [lo, lo]
   f32x4 hqb[2][4][64];
   f32x2 xo[2][16][4];
   u32x4 mqb[2][64];
@@ -197,18 +211,37 @@ __device__ __forceinline__ u32x4 zero_unless(bool keep, u32x4 x) {
   const u32x4 z = {0u, 0u, 0u, 0u};
   return keep ? x : z;
 }
+__device__ __forceinline__ u32x2 zero_unless(bool keep, u32x2 x) {
+  const u32x2 z = {0u, 0u};
+  return keep ? x : z;
+}
+// [first, second] part of a 4-register operand tuple: [hi, lo] of a
+// two-part split, [hi, mid] of a three-part one
 __device__ __forceinline__ u32x2 hi_of(u32x4 g) { return u32x2{g.x, g.y}; }
 __device__ __forceinline__ u32x2 lo_of(u32x4 g) { return u32x2{g.z, g.w}; }
+__device__ __forceinline__ u32x2 mid_of(u32x4 g) { return u32x2{g.z, g.w}; }
 __device__ __forceinline__ u32x4 hilo(const Split4& s) { return cat(s.hi, s.lo); }
 
-// acc + (-eta G)^T S for a score tile S (tokens x tokens) and G, both given
-// as [hi, lo]: the hi*hi, lo*hi and hi*lo terms as a chain of 16x16x16
-// products on sub-operands of the two tuples (acc may come from LDS).
-__device__ __forceinline__ f32x4 corr(u32x4 gt, u32x4 s, f32x4 acc) {
-  acc = mfma16(hi_of(gt), hi_of(s), acc);
-  acc = mfma16(lo_of(gt), hi_of(s), acc);
-  acc = mfma16(hi_of(gt), lo_of(s), acc);
+// acc + (-eta G)^T S for a score tile S (tokens x tokens) and G, each as
+// three bf16 parts ([hi, mid] tuple and lo): the six products down to a
+// relative size of 2^-16 (hi hi, mid hi, hi mid, lo hi, hi lo, mid mid),
+// paired into three 16x16x32 products whose slots 0-3 and 4-7 hold the two
+// 16-deep operands (acc may come from LDS).
+__device__ __forceinline__ f32x4 corr6(u32x4 gt, u32x2 gl, u32x4 s, u32x2 sl, f32x4 acc) {
+  const u32x2 uh = hi_of(gt), um = mid_of(gt), sh = hi_of(s), sm = mid_of(s);
+  acc = mfma32(cat(uh, um), cat(sh, sh), acc);
+  acc = mfma32(cat(uh, gl), cat(sm, sh), acc);
+  acc = mfma32(cat(uh, um), cat(sl, sm), acc);
   return acc;
+}
+// A 16x16 fp32 tile (accumulator layout) as three bf16 parts: [hi, mid] and lo.
+struct Tile3 {
+  u32x4 hm;
+  u32x2 lo;
+};
+__device__ __forceinline__ Tile3 tile3(f32x4 x) {
+  const Split4x3 s = split4x3(x);
+  return Tile3{cat(s.hi, s.mid), s.lo};
 }
 
 // Dot products of the rows of X with the constant rows (w_bar hi, 2 gamma hi,
@@ -222,6 +255,57 @@ __device__ __forceinline__ f32x4 stats(const u32x4 ast[2], const Rows& x) {
     if (LO) d = mfma32(ast[p], x.p[p].lo, d);
   }
   return d;
+}
+
+// The state as 16x16x32 A operands of W^T in three bf16 parts: A = [hi,
+// mid] (as split_state_mm) and Al = lo.  Each remainder is formed on the
+// matrix unit: -I times the packed part, accumulated onto what is left, is
+// exact in fp32.
+__device__ __forceinline__ void split_state_mm3(Op8 A[2], u32x4 Al[2], const f32x4 W[4],
+                                                u32x2 neg_ident) {
+  u32x2 hi[4], mid[4], lo[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) hi[r] = u32x2{pack_bf16(W[r][0], W[r][1]), pack_bf16(W[r][2], W[r][3])};
+  f32x4 d[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    d[r] = mfma16(neg_ident, hi[r], W[r]);
+    mid[r] = u32x2{pack_bf16(d[r][0], d[r][1]), pack_bf16(d[r][2], d[r][3])};
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const f32x4 e = mfma16(neg_ident, mid[r], d[r]);
+    lo[r] = u32x2{pack_bf16(e[0], e[1]), pack_bf16(e[2], e[3])};
+  }
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    A[p] = Op8{cat(hi[2 * p], hi[2 * p + 1]), cat(mid[2 * p], mid[2 * p + 1])};
+    Al[p] = cat(lo[2 * p], lo[2 * p + 1]);
+  }
+}
+// The same split on the VALU (prologue).
+__device__ __forceinline__ void split_state3(Op8 A[2], u32x4 Al[2], const f32x4 W[4]) {
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const Split4x3 a = split4x3(W[2 * p]), b = split4x3(W[2 * p + 1]);
+    A[p] = Op8{cat(a.hi, b.hi), cat(a.mid, b.mid)};
+    Al[p] = cat(a.lo, b.lo);
+  }
+}
+// X W with W in three parts (the gradient point; see times_state for the
+// layout): hi, mid and lo of W against the rows' hi part, plus hi of W
+// against the rows' lo part for fp32 data.
+template <bool LO>
+__device__ __forceinline__ f32x4 times_state3(const Op8 A[2], const u32x4 Al[2], const Rows& X) {
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    acc = mfma32(A[p].hi, X.p[p].hi, acc);
+    acc = mfma32(A[p].lo, X.p[p].hi, acc);
+    acc = mfma32(Al[p], X.p[p].hi, acc);
+    if (LO) acc = mfma32(A[p].hi, X.p[p].lo, acc);
+  }
+  return acc;
 }
 
 // The state as 16x16x32 A operands of W^T (see split_state), with the lo
@@ -300,16 +384,23 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
   }
   const u32x2 ident = ident_op(g, c);
   // u^T = diag(2 gamma) (k - v)^T + 2 gamma beta on the matrix unit (bf16
-  // data): diag(2 gamma) as a bf16 hi/lo pair and its negation.
-  u32x2 dph = ident, dpl = {0u, 0u}, dnh, dnl = {0u, 0u};
+  // data): diag(2 gamma) in three bf16 parts (fp32 precision: u enters the
+  // gradient, and with two parts its rounding was amplified along the
+  // sequence like that of the state) and their negations.
+  u32x2 dph = ident, dpm = {0u, 0u}, dpl = {0u, 0u}, dnh, dnm = {0u, 0u}, dnl = {0u, 0u};
   if (LN) {
     const float t2 = 2.f * a.gamma[(size_t)x.head * D + 16 * w + c];
     const uint32_t h = bf16_bits(t2);
-    const uint32_t l = bf16_bits(t2 - __builtin_bit_cast(float, h << 16));
+    const float r1 = t2 - __builtin_bit_cast(float, h << 16);
+    const uint32_t m = bf16_bits(r1);
+    const uint32_t l = bf16_bits(r1 - __builtin_bit_cast(float, m << 16));
+    auto neg = [](uint32_t b) { return b ? (b ^ 0x8000u) : 0u; };
     dph = diag_op(g, c, h);
+    dpm = diag_op(g, c, m);
     dpl = diag_op(g, c, l);
-    dnh = diag_op(g, c, h ? (h ^ 0x8000u) : 0u);
-    dnl = diag_op(g, c, l ? (l ^ 0x8000u) : 0u);
+    dnh = diag_op(g, c, neg(h));
+    dnm = diag_op(g, c, neg(m));
+    dnl = diag_op(g, c, neg(l));
   } else {
     dnh = diag_op(g, c, 0xBF80u);  // -1
   }
@@ -336,10 +427,16 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
       f32x4 u = LN ? twogb : f32x4{0.f, 0.f, 0.f, 0.f};
       if (RES) {
         u = mfma16(dph, k4, u);
-        if (LN) u = mfma16(dpl, k4, u);
+        if (LN) {
+          u = mfma16(dpm, k4, u);
+          u = mfma16(dpl, k4, u);
+        }
       }
       u = mfma16(dnh, v4, u);
-      if (LN) u = mfma16(dnl, v4, u);
+      if (LN) {
+        u = mfma16(dnm, v4, u);
+        u = mfma16(dnl, v4, u);
+      }
       return u;
     } else {
       const f32x4 kk = __builtin_bit_cast(f32x4, kv.k), vv = __builtin_bit_cast(f32x4, kv.v);
@@ -386,7 +483,8 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
     publish(0, ep, uc);
   }
   lds_barrier();  // period 0 starts
-  u32x4 gtm1 = {};  // (-eta G_{p-1})^T as [hi, lo]
+  u32x4 gtm1 = {};  // (-eta G_{p-1})^T as [hi, mid]
+  u32x2 gltm1 = {};  // and its lo part
 
   for (int blk = 0; blk * TB <= n + 2; ++blk) {
 #pragma unroll
@@ -405,17 +503,21 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
       const float eta = tile_eta(L.st, blk, tb, c);
       const f32x4 bk = L.bkb[(p - 1) & 1][w][lane];  // K_{p+1} W_{p-2}
       const u32x4 s1 = L.grb[(p - 1) & 1][0][lane];  // K_p K_{p+1}^T
+      const u32x2 s1l = L.grl[(p - 1) & 1][0][lane];
       const u32x4 s2 = L.grb[(p - 1) & 1][1][lane];  // K_{p-1} K_{p+1}^T
+      const u32x2 s2l = L.grl[(p - 1) & 1][1][lane];
       const f32x2 tk = L.tkb[(p - 1) & 1][c];
       const KV kvn = kv_of(blk, tb + 1);
       __builtin_amdgcn_sched_barrier(0);
       // ---- independent of tile p's gradient: u of tile p+1, the
       //      correction of K_{p+1} W_{p-2} by tile p-1
       const f32x4 un = u_of(kvn);
-      f32x4 h = corr(zero_unless(MB16 || mbs(p + 1) || mbs(p), gtm1), s2, bk);
+      const bool keep2 = MB16 || mbs(p + 1) || mbs(p);
+      f32x4 h = corr6(zero_unless(keep2, gtm1), zero_unless(keep2, gltm1), s2, s2l, bk);
       // ---- gradient of tile p (zero for rows past T, so past the end the
       //      update of W is a no-op)
       u32x4 gt;
+      u32x2 gl;
       {
         const bool valid = p * 16 + c < T;
         f32x4 eg;
@@ -443,18 +545,23 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) eg[i] = valid ? eg[i] : 0.f;
-        const Split4 s = split4(eg);
+        // three bf16 parts, each transposed on the matrix unit (exact)
+        const Split4x3 s = split4x3(eg);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
         const f32x4 th = mfma16(s.hi, ident, zero);
+        const f32x4 tm = mfma16(s.mid, ident, zero);
         const f32x4 tl = mfma16(s.lo, ident, zero);
-        gt = u32x4{pack_bf16(th[0], th[1]), pack_bf16(th[2], th[3]), pack_bf16(tl[0], tl[1]),
-                   pack_bf16(tl[2], tl[3])};
+        gt = u32x4{pack_bf16(th[0], th[1]), pack_bf16(th[2], th[3]), pack_bf16(tm[0], tm[1]),
+                   pack_bf16(tm[2], tm[3])};
+        gl = u32x2{pack_bf16(tl[0], tl[1]), pack_bf16(tl[2], tl[3])};
       }
       L.gtb[p & 1][w][lane] = gt;
+      L.gtl[p & 1][w][lane] = gl;
       // ---- gradient point of tile p+1 and its LN sums (at p >= n-1 the
       //      tile does not exist: stale rows, unused)
       {
-        h = corr(zero_unless(MB16 || mbs(p + 1), gt), s1, h);
+        const bool keep1 = MB16 || mbs(p + 1);
+        h = corr6(zero_unless(keep1, gt), zero_unless(keep1, gl), s1, s1l, h);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ep[i] = LN ? h[i] - tk.x : h[i];
         uc = un;
@@ -462,6 +569,7 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
         publish((p + 1) & 1, ep, uc);
       }
       gtm1 = gt;
+      gltm1 = gl;
       lds_barrier();
     }
   }
@@ -494,7 +602,7 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
     const float* gp = a.gamma + (size_t)x.head * D;
     const float* bp = a.beta + (size_t)x.head * D;
     for (int j = 0; j < D; ++j) s2gb += 2.f * gp[j] * bp[j];
-    // constant rows of the dot-product operand, as bf16 hi/lo: w_bar
+    // constant rows of the dot-product operands, in three bf16 parts: w_bar
     // (wave 0) and 2 gamma (wave 1)
     if (w < 2) {
       float v;
@@ -506,8 +614,12 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         v = 2.f * gp[lane];
       }
       const uint32_t h = bf16_bits(v);
+      const float r1 = v - __builtin_bit_cast(float, h << 16);
+      const uint32_t m = bf16_bits(r1);
       L.cst[w][lane] = (uint16_t)h;
-      L.cst[w + 2][lane] = (uint16_t)bf16_bits(v - __builtin_bit_cast(float, h << 16));
+      L.cst[w + 2][lane] = (uint16_t)m;
+      L.cst[w + 4][lane] = (uint16_t)bf16_bits(r1 - __builtin_bit_cast(float, m << 16));
+      L.cst[w + 6][lane] = 0;
     }
   }
   // K^T shared through LDS by one wave (bf16 data, split units: wave 2 has
@@ -515,6 +627,7 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
   constexpr bool KTS = SPLIT && BF16;
   // "tile -1": no update and no output correction in period 0
   L.gtb[1][w][lane] = u32x4{0u, 0u, 0u, 0u};
+  L.gtl[1][w][lane] = u32x2{0u, 0u};
   if (w == 2) {
     L.mqb[1][lane] = u32x4{0u, 0u, 0u, 0u};
     if (lane < 16) L.mqm[1][lane] = 0.f;
@@ -540,35 +653,50 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
   stage_issue<BF16, TB>(L.st, SPLIT ? nullptr : a.q, a.k, a.v, a.eta, x.row0, 0, T, 0, w);
   wait_vmem();
   lds_barrier();  // A
-  u32x4 ast[2] = {};
+  // A operands of the dot products with the constant rows: [w_bar, 2 gamma]
+  // x [hi, mid] (ast) and [w_bar lo, 2 gamma lo, 0, 0] (ast3)
+  u32x4 ast[2] = {}, ast3[2] = {};
   if (LN) {
 #pragma unroll
-    for (int p = 0; p < 2; ++p)
+    for (int p = 0; p < 2; ++p) {
       ast[p] = *reinterpret_cast<const u32x4*>(&L.cst[c & 3][32 * p + 8 * g]);
+      ast3[p] = *reinterpret_cast<const u32x4*>(&L.cst[4 + (c & 3)][32 * p + 8 * g]);
+    }
   }
-  // (k . w_bar, sum_f u_f) of a tile from its rows of k and v
+  // (k . w_bar, sum_f u_f) of a tile from its rows of k and v (the sum of u
+  // with 2 gamma in three parts)
   auto token_inputs = [&](const Rows& kr, const Rows& vr) -> f32x2 {
     const f32x4 sk = stats<LO>(ast, kr);
     const f32x4 sv = stats<LO>(ast, vr);
-    const float su = ((RES ? sk[1] + sk[3] : 0.f) - (sv[1] + sv[3])) + s2gb;
+    const f32x4 sk3 = stats<false>(ast3, kr);
+    const f32x4 sv3 = stats<false>(ast3, vr);
+    const float su = ((RES ? (sk[1] + sk[3]) + sk3[1] : 0.f) - ((sv[1] + sv[3]) + sv3[1])) + s2gb;
     return f32x2{sk[0] + sk[2], su};
   };
+  // the state as [hi, mid] (Ac: also the two parts of the output product)
+  // and lo (Al); Ab, Abl: the mini-batch base (b > 16)
   Op8 Ac[2], Ab[2];
-  split_state(Ac, Wc);
+  u32x4 Al[2], Abl[2];
+  split_state3(Ac, Al, Wc);
   if (!MB16) {
     Ab[0] = Ac[0];
     Ab[1] = Ac[1];
+    Abl[0] = Al[0];
+    Abl[1] = Al[1];
   }
   // rows of K_p and K_{p+1}, carried from the period that loaded them as
   // the rows of K_{p+2}
   Rows kc0 = rows8<BF16>(tile_rows(L.st, 1, 0, 0), c, g);
   Rows kc1 = rows8<BF16>(tile_rows(L.st, 1, 0, 1), c, g);
-  L.bkb[0][w][lane] = times_state<LO>(Ac, kc0);
-  L.bkb[1][w][lane] = times_state<LO>(Ac, kc1);
+  L.bkb[0][w][lane] = times_state3<LO>(Ac, Al, kc0);
+  L.bkb[1][w][lane] = times_state3<LO>(Ac, Al, kc1);
   if (w == 0) {
-    L.grb[1][0][lane] = hilo(split4(gram<LO>(kc0, kc1)));
+    const Tile3 s01 = tile3(gram<LO>(kc0, kc1));
+    L.grb[1][0][lane] = s01.hm;
+    L.grl[1][0][lane] = s01.lo;
   } else if (w == 1) {
     L.grb[1][1][lane] = u32x4{0u, 0u, 0u, 0u};
+    L.grl[1][1][lane] = u32x2{0u, 0u};
   } else if (w == 3 && LN) {
     L.tkb[0][c] = token_inputs(kc0, rows8<BF16>(tile_rows(L.st, 2, 0, 0), c, g));
     L.tkb[1][c] = token_inputs(kc1, rows8<BF16>(tile_rows(L.st, 2, 0, 1), c, g));
@@ -592,7 +720,8 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       if constexpr (BF16) __builtin_amdgcn_s_sleep(4);
       // every LDS read of the period first
       const auto* Kp = tile_rows(L.st, 1, blk, tb);
-      const u32x4 g1 = L.gtb[(p - 1) & 1][w][lane];  // (-eta G_{p-1})^T as [hi, lo]
+      const u32x4 g1 = L.gtb[(p - 1) & 1][w][lane];  // (-eta G_{p-1})^T as [hi, mid]
+      const u32x2 gl1 = L.gtl[(p - 1) & 1][w][lane];  // and lo
       // rows of q_p, k_{p+2}, v_{p+2}: read here for bf16 data; for fp32
       // data (hi/lo rows, twice the registers) just before their first use
       Rows qr = {}, kn, vn;
@@ -642,14 +771,15 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         for (int i = 0; i < 4; ++i) e[i] = (qw1[i] + d[i]) - muq1;
         L.hqb[p & 1][w][lane] = e;
       }
-      // ---- W += K_{p-1}^T (-eta G_{p-1})
+      // ---- W += K_{p-1}^T (-eta G_{p-1}), the gradient in three parts
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         Wc[r] = mfma16(kt1[r].hi, hi_of(g1), Wc[r]);
-        Wc[r] = mfma16(kt1[r].hi, lo_of(g1), Wc[r]);
+        Wc[r] = mfma16(kt1[r].hi, mid_of(g1), Wc[r]);
+        Wc[r] = mfma16(kt1[r].hi, gl1, Wc[r]);
         if (LO) Wc[r] = mfma16(kt1[r].lo, hi_of(g1), Wc[r]);
       }
-      split_state_mm(Ac, Wc, neg_ident);  // W_{p-1}
+      split_state_mm3(Ac, Al, Wc, neg_ident);  // W_{p-1}
       // with b = 16 this is the base of tile p: stored for the backward
       if (a.bases && p < n) {
         float* bp = a.bases + ((size_t)x.unit * n + p) * D * D;
@@ -661,6 +791,8 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       if (!MB16 && mbs(p)) {
         Ab[0] = Ac[0];
         Ab[1] = Ac[1];
+        Abl[0] = Al[0];
+        Abl[1] = Al[1];
       }
       // ---- products of W_{p-1} (past the end: stale rows, unused)
       if constexpr (!BF16) {
@@ -672,8 +804,8 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
         // gradient point two tiles ahead: K_{p+2} W_{p-1}, or the
         // mini-batch's own gradient point when no update reaches it
         f32x4 bk;
-        if (MB16 || mbs(p + 2) || mbs(p + 1)) bk = times_state<LO>(Ac, kn);
-        else bk = times_state<LO>(Ab, kn);
+        if (MB16 || mbs(p + 2) || mbs(p + 1)) bk = times_state3<LO>(Ac, Al, kn);
+        else bk = times_state3<LO>(Ab, Abl, kn);
         L.bkb[p & 1][w][lane] = bk;
       }
       // ---- tile p: its output score tile and shift, for every update
@@ -694,9 +826,13 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       //      each: the score tiles K_{p+1} K_{p+2}^T, K_p K_{p+2}^T and
       //      (k . w_bar, sum_f u_f)
       if (w == 0) {
-        L.grb[p & 1][0][lane] = hilo(split4(gram<LO>(k1, kn)));
+        const Tile3 sc = tile3(gram<LO>(k1, kn));
+        L.grb[p & 1][0][lane] = sc.hm;
+        L.grl[p & 1][0][lane] = sc.lo;
       } else if (w == 1) {
-        L.grb[p & 1][1][lane] = hilo(split4(gram<LO>(k0, kn)));
+        const Tile3 sc = tile3(gram<LO>(k0, kn));
+        L.grb[p & 1][1][lane] = sc.hm;
+        L.grl[p & 1][1][lane] = sc.lo;
       } else if (w == 3 && LN) {
         if constexpr (!BF16) read_vn();
         L.tkb[p & 1][c] = token_inputs(kn, vn);
@@ -742,7 +878,7 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
 // p-3.  With COPIES they also issue the input copies of the later blocks.
 template <bool BF16, bool LN, bool RES, bool COPIES, class Lds>
 __device__ __forceinline__ void output_part(Lds& L, const LinearArgs& a, const Ctx& x) {
-  constexpr int TB = LinCfg<BF16>::TB;
+  constexpr int TB = Lds::TB;
   const int lane = x.lane, g = x.g, c = x.c, w = x.w, fo = x.fo, n = x.n, T = x.T;
 
   f32x4 gam = {1.f, 1.f, 1.f, 1.f}, bet = {0.f, 0.f, 0.f, 0.f};
@@ -841,8 +977,11 @@ __device__ __forceinline__ void output_part(Lds& L, const LinearArgs& a, const C
 // state updates from that stream and forms the outputs.  Only the output
 // workgroup ever waits for the other, so the pair cannot deadlock.
 //
-// Gradient stream of a unit: tile t, column block b, lane l at byte
-// ((4 t + b) * 64 + l) * 16, the [hi, lo] bf16 pairs of the chain's gtb.
+// Gradient stream of a unit (6 KB per tile, n tiles): tile t, column block
+// b, lane l at byte ((4 t + b) * 64 + l) * 16, the [hi, mid] bf16 pairs of
+// the chain's gtb; then, from byte 4096 n, tile t, column-block pair j,
+// lane l at byte 4096 n + ((2 t + j) * 64 + l) * 16, the lo parts (gtl) of
+// column blocks 2j and 2j+1.
 // Publication: wave h (0, 1) of the chain workgroup's hand-off pair owns
 // column blocks 2h, 2h+1 and a counter of complete tiles.
 
@@ -883,18 +1022,18 @@ __device__ __forceinline__ void feed_copy_part(LinLds<BF16>& L, const LinearArgs
 // tile p-1 (published by the chain waves at the barrier that opened the
 // period) goes from LDS to the stream with agent-coherent stores.  This
 // wave issues no other memory instruction, and its vector memory counter
-// retires stores in order, so after the two stores of tile p-1 the stores
-// of tile p-1-KLAG are complete once at most 3 KLAG instructions remain
-// outstanding (two stores and one counter store per later period); the
+// retires stores in order, so after the three stores of tile p-1 the stores
+// of tile p-1-KLAG are complete once at most 4 KLAG instructions remain
+// outstanding (three stores and one counter store per later period); the
 // counter then publishes tiles 0 .. p-1-KLAG.  The lag keeps the wait from
 // ever holding the barrier.
 template <bool BF16>
 __device__ __forceinline__ void handoff_part(LinLds<BF16>& L, const LinearArgs& a, const Ctx& x,
                                              int h) {
-  static_assert(KLAG == 3, "the vmcnt below is 3 KLAG");
+  static_assert(KLAG == 3, "the vmcnt below is 4 KLAG");
   const int lane = x.lane, n = x.n;
   const __amdgpu_buffer_rsrc_t gs = __builtin_amdgcn_make_buffer_rsrc(
-      a.ws_g + (size_t)x.unit * n * 1024, (short)0, n * 4096, 0x00020000);
+      a.ws_g + (size_t)x.unit * n * 1536, (short)0, n * 6144, 0x00020000);
   uint32_t* cnt = a.ws_flags + ((size_t)x.unit * 2 + h) * 32;
   lds_barrier();  // A
   lds_barrier();  // B
@@ -907,7 +1046,10 @@ __device__ __forceinline__ void handoff_part(LinLds<BF16>& L, const LinearArgs& 
         const u32x4 v = L.gtb[(p - 1) & 1][b][lane];
         __builtin_amdgcn_raw_buffer_store_b128(v, gs, (((p - 1) * 4 + b) * 64 + lane) * 16, 0, SC1);
       }
-      asm volatile("s_waitcnt vmcnt(9)" ::: "memory");
+      const u32x4 lo = cat(L.gtl[(p - 1) & 1][2 * h][lane], L.gtl[(p - 1) & 1][2 * h + 1][lane]);
+      __builtin_amdgcn_raw_buffer_store_b128(lo, gs, n * 4096 + (((p - 1) * 2 + h) * 64 + lane) * 16,
+                                             0, SC1);
+      asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
       if (lane == 0)
         __hip_atomic_store(cnt, (uint32_t)max(p - KLAG, 0), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
@@ -924,7 +1066,7 @@ __device__ __forceinline__ void handoff_part(LinLds<BF16>& L, const LinearArgs& 
 template <bool BF16, bool LN, bool RES>
 __device__ __forceinline__ void out_state_part(OutLds<BF16>& L, const LinearArgs& a,
                                                const Ctx& x) {
-  constexpr int TB = LinCfg<BF16>::TB;
+  constexpr int TB = OutLds<BF16>::TB;
   constexpr bool LO = !BF16;
   const int lane = x.lane, g = x.g, c = x.c, w = x.w, n = x.n;
 
@@ -987,7 +1129,10 @@ __device__ __forceinline__ void out_state_part(OutLds<BF16>& L, const LinearArgs
       // the first tile and past the last), the rows of tile p, the output
       // score tile and shift of tile p-1
       const int tp = max(p - 1, 0);
-      const u32x4 g1 = zero_unless(p >= 1 && p - 1 < n, L.gst[(tp / TB) & 1][tp % TB][w][lane]);
+      const bool live = p >= 1 && p - 1 < n;
+      const u32x4 g1 = zero_unless(live, L.gst[(tp / TB) & 1][tp % TB][w][lane]);
+      const u32x4 gl2 = L.gsl[(tp / TB) & 1][tp % TB][w >> 1][lane];
+      const u32x2 gl1 = zero_unless(live, (w & 1) ? u32x2{gl2.z, gl2.w} : u32x2{gl2.x, gl2.y});
       const auto* Kp = tile_rows(L.st, 1, blk, tb);
       const Rows qr = rows8<BF16>(tile_rows(L.st, 0, blk, tb), c, g);
       const Rows kr = rows8<BF16>(Kp, c, g);
@@ -1005,14 +1150,15 @@ __device__ __forceinline__ void out_state_part(OutLds<BF16>& L, const LinearArgs
         for (int i = 0; i < 4; ++i) e[i] = (qw1[i] + d[i]) - muq1;
         L.hqb[p & 1][w][lane] = e;
       }
-      // ---- W += K_{p-1}^T (-eta G_{p-1})
+      // ---- W += K_{p-1}^T (-eta G_{p-1}), the gradient in three parts
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         Wc[r] = mfma16(kt1[r].hi, hi_of(g1), Wc[r]);
-        Wc[r] = mfma16(kt1[r].hi, lo_of(g1), Wc[r]);
+        Wc[r] = mfma16(kt1[r].hi, mid_of(g1), Wc[r]);
+        Wc[r] = mfma16(kt1[r].hi, gl1, Wc[r]);
         if (LO) Wc[r] = mfma16(kt1[r].lo, hi_of(g1), Wc[r]);
       }
-      split_state_mm(Ac, Wc, neg_ident);  // W_{p-1}
+      split_state_mm(Ac, Wc, neg_ident);  // W_{p-1} as [hi, mid], as the update waves form it
       qw1 = times_state<LO>(Ac, qr);      // past the end: stale rows, unused
       // ---- tile p: output score tile and shift for the next period
       if (w == 2) {
@@ -1054,10 +1200,11 @@ __device__ __forceinline__ void out_state_part(OutLds<BF16>& L, const LinearArgs
 template <bool BF16>
 __device__ __forceinline__ void out_copy_part(OutLds<BF16>& L, const LinearArgs& a,
                                               const Ctx& x, int cw) {
-  constexpr int TB = LinCfg<BF16>::TB;
+  constexpr int TB = OutLds<BF16>::TB;
   constexpr int PARTS = TB >= 7 ? 4 : 1;
   const int lane = x.lane, n = x.n, T = x.T;
-  const uint32_t* gsrc = a.ws_g + (size_t)x.unit * n * 1024;
+  const uint32_t* gsrc = a.ws_g + (size_t)x.unit * n * 1536;
+  const uint32_t* lsrc = gsrc + (size_t)n * 1024;  // lo parts
   bool ok = true;  // cleared for good by a spin that reaches the limit
   auto stage_grad = [&](int b, int buf) {
     const uint32_t need = (uint32_t)min(n, (b + 1) * TB);
@@ -1070,6 +1217,7 @@ __device__ __forceinline__ void out_copy_part(OutLds<BF16>& L, const LinearArgs&
         __builtin_amdgcn_s_sleep(2);
       }
     }
+    const u32x4 nan4 = {0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
     for (int i = cw; i < TB; i += 4) {
       const int t = min(b * TB + i, n - 1);
 #pragma unroll
@@ -1079,7 +1227,17 @@ __device__ __forceinline__ void out_copy_part(OutLds<BF16>& L, const LinearArgs&
           __builtin_amdgcn_global_load_lds(gsrc + ((size_t)(4 * t + cb) * 64 + lane) * 4, dst, 16,
                                            0, SC1);
         } else {
-          L.gst[buf][i][cb][lane] = u32x4{0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u, 0x7fc07fc0u};
+          L.gst[buf][i][cb][lane] = nan4;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (ok) {
+          TTT_LDS void* dst = (TTT_LDS void*)&L.gsl[buf][i][j][0];
+          __builtin_amdgcn_global_load_lds(lsrc + ((size_t)(2 * t + j) * 64 + lane) * 4, dst, 16,
+                                           0, SC1);
+        } else {
+          L.gsl[buf][i][j][lane] = nan4;
         }
       }
     }

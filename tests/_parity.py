@@ -7,19 +7,14 @@ Metrics (the tolerance is on the maximum relative error):
   * state: per unit max |S - S_ref| / max |S_ref|, maxed over units.
 Tolerances: 1e-4 for fp32 inputs, 2e-2 for bf16 inputs (fp32 state).
 
-Conditioning.  For some (batch, head) units of the long workloads the scan
-itself is ill-conditioned: the fp64 oracle's own output moves by orders of
-magnitude more than a perturbation of its inputs (a 1e-7 relative change of
-eta moves z by ~3e-3 on the worst unit at T = 8192 and by O(1) at T = 32768;
-most units move by ~1e-6).  Rounding is amplified the same way, so no
-finite-precision evaluation can meet a fixed tolerance on such units.  Per
-unit, the sensitivity S is the error metric between the oracle and the
-oracle with eta perturbed by 1e-7 (relative, two independent draws, the
-larger kept).  A unit passes when its error is within the tolerance or
-within AMP * S: AMP = 1000 corresponds to a per-step relative error of 1e-4,
-ten times the operand precision of the kernels (bf16 hi/lo pairs, ~1e-5), so
-well-conditioned units (AMP * S below the tolerance) are held to the
-tolerance itself."""
+Conditioning.  For a few (batch, head) units of the long-context workload
+the scan itself amplifies rounding along the sequence so strongly that a
+plain fp32 evaluation of it (the oracle's own algorithm compiled with fp32
+arithmetic, tests/_oracle_f32.py) misses the tolerance against the fp64
+oracle.  Only such units may be exempted from the tolerance, and only in the
+tests that allow it (strict=False); an exempted unit is still held to
+FP32_MULT times the fp32 evaluation's error on that unit.  Every other unit
+is held to the tolerance itself."""
 import numpy as np
 import torch
 
@@ -54,8 +49,7 @@ def state_err(s, sref):
     return float((d / m).max())
 
 
-PERTURB = 1e-7
-AMP = 1000.0
+FP32_MULT = 8.0
 
 
 def per_unit(err_fn, a, b):
@@ -65,28 +59,30 @@ def per_unit(err_fn, a, b):
                      for i in range(B)])
 
 
-def perturbed_eta(eta, seed):
-    rng = np.random.default_rng(seed)
-    e = np.asarray(eta, np.float64)
-    return (e * (1.0 + PERTURB * rng.standard_normal(e.shape))).astype(np.float32)
-
-
-def check_units(name, z, zref, zs, s, sref, ss, tol):
-    """z, s: GPU output and state; zref, sref: the oracle's; zs, ss: lists of
-    the perturbed oracle's.  Asserts every unit's z and state error is within
-    max(tol, AMP * sensitivity)."""
+def check_units(name, z, zref, z32, s, sref, s32, tol, strict=True):
+    """z, s: GPU output and list of state tensors; zref, sref: the fp64
+    oracle's; z32, s32: the fp32 evaluation's (z32 already rounded to the I/O
+    type).  Asserts every unit's z and state error is within tol, except,
+    with strict=False, on units where the fp32 evaluation itself misses tol:
+    there within FP32_MULT times the fp32 evaluation's error."""
     ez = per_unit(z_err, z, zref)
-    sz = np.max([per_unit(z_err, x, zref) for x in zs], axis=0)
     es = np.max([per_unit(state_err, a, b) for a, b in zip(s, sref)], axis=0)
-    ss_ = np.max([np.max([per_unit(state_err, a, b) for a, b in zip(x, sref)], axis=0)
-                  for x in ss], axis=0)
-    bz, bs = np.maximum(tol, AMP * sz), np.maximum(tol, AMP * ss_)
-    well = (AMP * sz <= tol) & (AMP * ss_ <= tol)
-    print("%s: %d units, %d ill-conditioned; z err max %.3e (well-conditioned %.3e, median %.3e); "
-          "state err max %.3e; worst error/bound %.2f" % (
-              name, ez.size, (~well).sum(), ez.max(), ez[well].max() if well.any() else 0.0,
-              np.median(ez), es.max(), max((ez / bz).max(), (es / bs).max())), flush=True)
-    for i, j in zip(*np.nonzero(~well)):
-        print("   unit (%d,%d): sensitivity z %.2e state %.2e; error z %.2e state %.2e"
-              % (i, j, sz[i, j], ss_[i, j], ez[i, j], es[i, j]), flush=True)
+    fz = per_unit(z_err, z32, zref)
+    fs = np.max([per_unit(state_err, a, b) for a, b in zip(s32, sref)], axis=0)
+    exempt = np.zeros(ez.shape, bool) if strict else (fz > tol) | (fs > tol)
+    bz = np.where(exempt, np.maximum(tol, FP32_MULT * fz), tol)
+    bs = np.where(exempt, np.maximum(tol, FP32_MULT * fs), tol)
+    held = ~exempt
+    print("%s: %d units, %d exempt (fp32 evaluation misses %.0e); z err max %.3e (held units "
+          "%.3e, median %.3e); state err max %.3e; fp32 evaluation z err max %.3e; worst "
+          "error/bound %.2f" % (
+              name, ez.size, exempt.sum(), tol, ez.max(), ez[held].max() if held.any() else 0.0,
+              np.median(ez), es.max(), fz.max(), max((ez / bz).max(), (es / bs).max())),
+          flush=True)
+    worst = np.argsort(ez.ravel())[::-1][:4]
+    for u in sorted(set(worst.tolist()) | set(np.flatnonzero(exempt).tolist())):
+        i, j = divmod(u, ez.shape[1])
+        print("   unit (%d,%d)%s: error z %.2e state %.2e; fp32 evaluation z %.2e state %.2e"
+              % (i, j, " exempt" if exempt[i, j] else "", ez[i, j], es[i, j], fz[i, j],
+                 fs[i, j]), flush=True)
     assert (ez <= bz).all() and (es <= bs).all()

@@ -138,11 +138,11 @@ def _split(p, ws=None, ws_bytes=None, **ptrs):
 
 
 def test_split_workspace_size():
-    # 256 B of counters per unit, 256 B of error words (rounded), 4 KB per tile and unit
+    # 256 B of counters per unit, 256 B of error words (rounded), 6 KB per tile and unit
     p = _params(B=2, H=3, T=100)
     units, tiles = 6, 7
     assert _lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(p)) == \
-        units * 256 + 256 + units * tiles * 4096
+        units * 256 + 256 + units * tiles * 6144
     assert _lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(_params(T=0))) == 0
     assert _lib.lib().ttt_linear_split_workspace_bytes(None) == 0
 

@@ -3,18 +3,18 @@ against the fp64 oracle on the same seeded inputs.
 
 Small cases compare every output; the full-size workloads (125M- and
 1.3B-shaped layers, 32k context) run in the configuration the benchmark
-times and compare sampled (batch, head) units, which the oracle computes on
-their own (units are independent).  Tolerances: 1e-4 max relative error for
-fp32 inputs, 2e-2 for bf16 inputs."""
+times and compare every (batch, head) unit.  Tolerances: 1e-4 max relative
+error for fp32 inputs, 2e-2 for bf16 inputs."""
 import numpy as np
 import pytest
 import torch
 
 import oracle
 from linear_rnn_ttt_amd import ttt_linear_forward
-from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs
+from linear_rnn_ttt_amd.inputs import WORKLOADS, bf16_round, make_inputs
 
-from _parity import TOL, check_units, from_dev, perturbed_eta, state_err, to_dev, z_err
+import _oracle_f32
+from _parity import TOL, check_units, from_dev, state_err, to_dev, z_err
 
 pytestmark = pytest.mark.gpu
 
@@ -144,19 +144,24 @@ def test_deterministic():
     assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
-@pytest.mark.parametrize("name", ["linear_125m_b8h12_t2k", "linear_1p3b_b4h32_t8k",
-                                  "linear_long_b1h32_t32k"])
-def test_full_size_all_units(name):
+@pytest.mark.parametrize("name,strict", [("linear_125m_b8h12_t2k", True),
+                                         ("linear_1p3b_b4h32_t8k", True),
+                                         ("linear_long_b1h32_t32k", False)])
+def test_full_size_all_units(name, strict):
     """The full workload as the benchmark runs it, every (batch, head) unit
-    against the oracle, with the conditioning-aware bound of check_units
-    (some units of the long workloads are ill-conditioned)."""
+    against the oracle.  The 125M- and 1.3B-shaped layers: every unit within
+    the tolerance.  The 32k-token layer: every unit within the tolerance
+    except where a plain fp32 evaluation of the scan itself misses it (two
+    units whose scan amplifies rounding to O(1)); those are held to a small
+    multiple of the fp32 evaluation's error (check_units)."""
     w = WORKLOADS[name]
     inp = make_inputs(w)
     z, wf = _gpu(inp, w.io)
     assert np.isfinite(z).all()
-    run = lambda eta: oracle.linear(inp["q"], inp["k"], inp["v"], eta, inp["w0"], inp["gamma"],
-                                    inp["beta"])
-    zr, wr = run(inp["eta"])
-    pert = [run(perturbed_eta(inp["eta"], seed)) for seed in (1, 2)]
-    check_units(name, z, zr, [p[0] for p in pert], [wf], [wr], [[p[1]] for p in pert],
-                TOL[w.io])
+    args = [inp[x] for x in ("q", "k", "v", "eta", "w0", "gamma", "beta")]
+    zr, wr = oracle.linear(*args)
+    z32, w32 = _oracle_f32.linear(*args)
+    if w.io == "bf16":
+        z32 = bf16_round(z32)
+    check_units(name, z, zr, z32.astype(np.float64), [wf], [wr], [w32.astype(np.float64)],
+                TOL[w.io], strict=strict)

@@ -298,16 +298,26 @@ def test_nan_propagates():
 
 
 def test_long_scan_is_ill_conditioned_on_some_units():
-    """The recurrence can amplify perturbations along the sequence.  On the
-    1.3B-shaped workload (B4 H32 T8192, seeded inputs) unit (0, 14) is such a
-    case: a 1e-7 relative perturbation of eta moves the fp64 oracle's z by
-    more than 1e-3 (row-normalised max) by the end of the sequence, growing
-    steadily along it, while unit (0, 0) moves by less than 1e-5.  No
-    finite-precision evaluation can be held to a fixed tolerance on such a
-    unit; the GPU parity bound therefore scales with this sensitivity."""
-    from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs, unit_slice
-    w = WORKLOADS["linear_1p3b_b4h32_t8k"]
-    sub = unit_slice(make_inputs(w), [(0, 14), (0, 0)], w.H)
+    """The recurrence can amplify rounding along the sequence.  On the
+    32k-token workload (B1 H32 T32768, seeded inputs) a plain fp32
+    evaluation of the oracle's own algorithm (tests/_oracle_f32.py) misses
+    the bf16 tolerance (2e-2, z rounded to bf16 as the GPU's is) against the
+    fp64 oracle on exactly two units, (0, 6) and (0, 22), and meets it on
+    the other 30: these are the only units the GPU parity test may exempt
+    from the tolerance.  The amplification is the method's, not the code's:
+    a 1e-7 relative perturbation of eta moves the fp64 oracle's own z on
+    unit (0, 6) by more than 1e-2 by the end of the sequence, and on unit
+    (0, 0) by less than 1e-5."""
+    import _oracle_f32
+    from linear_rnn_ttt_amd.inputs import WORKLOADS, bf16_round, make_inputs, unit_slice
+    w = WORKLOADS["linear_long_b1h32_t32k"]
+    inp = make_inputs(w)
+    args = [inp[x] for x in ("q", "k", "v", "eta", "w0", "gamma", "beta")]
+    zr, _ = oracle.linear(*args)
+    z32 = bf16_round(_oracle_f32.linear(*args)[0]).astype(np.float64)
+    err = (np.abs(z32 - zr).max(-1) / np.abs(zr).max(-1)).max(-1)[0]   # per head
+    assert sorted(np.flatnonzero(err > 2e-2).tolist()) == [6, 22], err
+    sub = unit_slice(inp, [(0, 6), (0, 0)], w.H)
     rng = np.random.default_rng(0)
     eta2 = (sub["eta"].astype(np.float64) * (1 + 1e-7 * rng.standard_normal(sub["eta"].shape))
             ).astype(np.float32)
@@ -315,8 +325,7 @@ def test_long_scan_is_ill_conditioned_on_some_units():
                                     sub["beta"], state0_per_batch=True)[0]
     z1, z2 = run(sub["eta"]), run(eta2)
     d = np.abs(z2 - z1).max(-1) / np.abs(z1).max(-1)   # [1, 2, T]
-    assert d[0, 0].max() > 1e-3
-    assert d[0, 0, -1024:].max() > 10 * d[0, 0, 1024:2048].max()   # grows along the sequence
+    assert d[0, 0].max() > 1e-2
     assert d[0, 1].max() < 1e-5
 
 
