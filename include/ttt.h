@@ -29,7 +29,9 @@
  *  - Pointers q, k, v, eta, states, gamma, beta, z, the *_out buffers and
  *    workspaces are DEVICE pointers (HIP global memory of the current
  *    device), owned by the caller.  The library allocates no memory and
- *    keeps no global mutable state; calls are thread-safe and reentrant.
+ *    keeps no global mutable state (one exception: the per-device address
+ *    of the fixed scratch array of ttt_linear_forward_split_noalloc, looked
+ *    up once per device under a lock); calls are thread-safe and reentrant.
  *  - Layout: contiguous, row-major, feature dimension fastest.
  *      q, k, v, z  [B,H,T,d] of io_dtype     eta  [B,H,T] fp32
  *      gamma, beta [H,d] fp32 (not read with TTT_NO_LN; may be NULL then)
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 8
+#define TTT_ABI_VERSION 9
 
 typedef enum {
   TTT_OK = 0,
@@ -71,7 +73,9 @@ typedef enum {
                                launch on more units than half the compute units) */
   TTT_ERR_ALIAS = 4,        /* forbidden overlap between buffers */
   TTT_ERR_DEVICE = 5,       /* HIP reported an error at launch */
-  TTT_ERR_ARG = 6           /* bad dtype, flag or epsilon, or a misaligned workspace */
+  TTT_ERR_ARG = 6,          /* bad dtype, flag or epsilon, or a misaligned workspace */
+  TTT_ERR_TOO_LARGE = 7     /* the problem needs more scratch than the fixed array of
+                               ttt_linear_forward_split_noalloc holds */
 } ttt_status;
 
 typedef enum { TTT_F32 = 0, TTT_BF16 = 1 } ttt_dtype;
@@ -143,6 +147,35 @@ ttt_status ttt_linear_forward_split(const ttt_params* p,
                                     void* z, float* w_out,
                                     void* workspace, uint64_t workspace_bytes,
                                     void* hip_stream);
+
+/*
+ * ttt_linear_forward_split without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Same method, arguments, results (bit for bit) and restrictions as
+ * ttt_linear_forward_split; the gradient stream and the publication
+ * counters live in a fixed array in the library's device code instead of a
+ * caller workspace:
+ *  - its size is TTT_NOALLOC_SCRATCH_BYTES (128 MiB) per device; a problem
+ *    whose ttt_linear_split_workspace_bytes exceeds it (256 bytes per unit,
+ *    256, and 6 KB per unit and 16-token tile; e.g. B*H = 32 units up to
+ *    T = 10912) returns TTT_ERR_TOO_LARGE before anything runs;
+ *  - every GPU the library runs on holds its own copy of the array (device
+ *    memory taken when the library's code is loaded on that device, kept
+ *    until the process ends); its address is looked up once per device, on
+ *    the first call with that device current;
+ *  - every call on one device shares that device's array, and the counters
+ *    are cleared by the call's own fill kernel: calls on one device must not
+ *    overlap in time (enqueue them on one stream, or order the streams);
+ *    overlapping calls race and give wrong results.
+ * No hipMalloc, hipFree or allocating library routine is called.
+ */
+#define TTT_NOALLOC_SCRATCH_BYTES (128ull << 20)
+ttt_status ttt_linear_forward_split_noalloc(const ttt_params* p,
+                                            const void* q, const void* k, const void* v,
+                                            const float* eta, const float* w0,
+                                            const float* ln_gamma, const float* ln_beta,
+                                            void* z, float* w_out, void* hip_stream);
 
 /*
  * One token of the TTT-Linear scan per (batch, head) unit: the streaming

@@ -159,6 +159,29 @@ ttt_status linear_launch(const ttt_params* p, const tttk::LinearArgs& a, void* h
   return e == hipSuccess ? TTT_OK : TTT_ERR_DEVICE;
 }
 
+// The split launch on validated arguments, with its workspace (counters and
+// gradient stream, split_layout) at `workspace`.
+ttt_status split_launch(const ttt_params* p, tttk::LinearArgs a, const float* w0,
+                        void* workspace, void* hip_stream) {
+  // no in-place resume: the second workgroup of a unit reads the initial
+  // state at its own start, which may come after the first has written the
+  // final state
+  if (a.w_out && static_cast<const void*>(a.w_out) == w0) return TTT_ERR_ALIAS;
+  // both workgroups of every unit must be resident at once
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return TTT_ERR_DEVICE;
+  if (2ull * static_cast<uint64_t>(p->B) * p->H > static_cast<uint64_t>(cus))
+    return TTT_ERR_UNSUPPORTED;
+  const SplitLayout ly = split_layout(p);
+  char* base = static_cast<char*>(workspace);
+  a.ws_flags = reinterpret_cast<uint32_t*>(base);
+  a.ws_g = reinterpret_cast<uint32_t*>(base + ly.stream_offset);
+  a.split = 1;
+  return linear_launch(p, a, hip_stream);
+}
+
 }  // namespace
 
 extern "C" {
@@ -177,6 +200,9 @@ const char* ttt_status_string(ttt_status s) {
     case TTT_ERR_DEVICE: return "HIP reported an error at kernel launch";
     case TTT_ERR_ARG:
       return "bad io_dtype, flags, ln_eps or state0_per_batch, or a misaligned workspace";
+    case TTT_ERR_TOO_LARGE:
+      return "the problem needs more scratch than the no-allocation entry point's fixed array "
+             "(TTT_NOALLOC_SCRATCH_BYTES per device) holds";
   }
   return "unknown ttt_status";
 }
@@ -208,23 +234,22 @@ ttt_status ttt_linear_forward_split(const ttt_params* p, const void* q, const vo
   const ttt_status st = linear_args(p, q, k, v, eta, w0, ln_gamma, ln_beta, z, w_out, workspace,
                                     workspace_bytes, &a);
   if (st != TTT_OK) return st;
-  // no in-place resume: the second workgroup of a unit reads the initial
-  // state at its own start, which may come after the first has written the
-  // final state
-  if (w_out && static_cast<const void*>(w_out) == w0) return TTT_ERR_ALIAS;
-  // both workgroups of every unit must be resident at once
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    return TTT_ERR_DEVICE;
-  if (2ull * static_cast<uint64_t>(p->B) * p->H > static_cast<uint64_t>(cus))
-    return TTT_ERR_UNSUPPORTED;
-  const SplitLayout ly = split_layout(p);
-  char* base = static_cast<char*>(workspace);
-  a.ws_flags = reinterpret_cast<uint32_t*>(base);
-  a.ws_g = reinterpret_cast<uint32_t*>(base + ly.stream_offset);
-  a.split = 1;
-  return linear_launch(p, a, hip_stream);
+  return split_launch(p, a, w0, workspace, hip_stream);
+}
+
+ttt_status ttt_linear_forward_split_noalloc(const ttt_params* p, const void* q, const void* k,
+                                            const void* v, const float* eta, const float* w0,
+                                            const float* ln_gamma, const float* ln_beta,
+                                            void* z, float* w_out, void* hip_stream) {
+  static_assert(TTT_NOALLOC_SCRATCH_BYTES == 128ull << 20, "header and library disagree");
+  tttk::LinearArgs a;
+  ttt_status st = linear_args(p, q, k, v, eta, w0, ln_gamma, ln_beta, z, w_out, nullptr, 0, &a);
+  if (st != TTT_OK) return st;
+  if (w_out && static_cast<const void*>(w_out) == w0) return TTT_ERR_ALIAS;  // as the split launch
+  if (split_layout(p).total > tttk::kLinearScratchBytes) return TTT_ERR_TOO_LARGE;
+  void* scratch = nullptr;
+  if (tttk::linear_scratch(&scratch) != hipSuccess) return TTT_ERR_DEVICE;
+  return split_launch(p, a, w0, scratch, hip_stream);
 }
 
 ttt_status ttt_linear_decode_step(const ttt_params* p, int32_t pos, const void* q,

@@ -71,6 +71,11 @@ struct DecodeArgs {
   float eps;
 };
 
+// Device address of the fixed scratch array of the no-allocation split
+// launch on the current device (looked up once per device), and its size.
+hipError_t linear_scratch(void** ptr);
+extern const uint64_t kLinearScratchBytes;
+
 // Each returns the hipError_t of the launch.
 hipError_t launch_linear(const LinearArgs& a, bool bf16, bool ln, bool residual,
                          hipStream_t stream);

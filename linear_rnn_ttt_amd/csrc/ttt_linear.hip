@@ -80,6 +80,8 @@
 //     workgroup on another CU, which replays the state from the gradients
 //     the first streams to it through device memory (see "Split units"
 //     below).
+#include <mutex>
+
 #include "ttt_device.hpp"
 #include "ttt_kernels.hpp"
 #include "ttt_tile.hpp"
@@ -1338,7 +1340,37 @@ hipError_t launch1(const LinearArgs& a, bool ln, bool res, hipStream_t s) {
   return res ? launch3<BF16, false, true>(a, s) : launch3<BF16, false, false>(a, s);
 }
 
+// Scratch of the no-allocation split launch: gradient stream and counters
+// in one fixed array per device, for callers that cannot allocate.
+constexpr uint64_t SCRATCH_BYTES = 128ull << 20;
+static __device__ __align__(256) uint8_t scratch[SCRATCH_BYTES];
+
+constexpr int MAX_DEVICES = 64;
+std::mutex scratch_mu;
+void* scratch_ptr[MAX_DEVICES] = {};
+
 }  // namespace
+
+const uint64_t kLinearScratchBytes = SCRATCH_BYTES;
+
+hipError_t linear_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= MAX_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    // the array's name is a host-side stand-in: its device address on the
+    // current device comes from the runtime, once per device
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    scratch_ptr[dev] = p;
+  }
+  *ptr = scratch_ptr[dev];
+  return hipSuccess;
+}
 
 hipError_t launch_linear(const LinearArgs& a, bool bf16, bool ln, bool residual,
                          hipStream_t stream) {

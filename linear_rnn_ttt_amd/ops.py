@@ -13,8 +13,8 @@ import torch
 
 from . import _lib
 
-__all__ = ["ttt_linear_forward", "ttt_linear_decode_step", "ttt_linear_decode_step_compact",
-           "ttt_linear_backward", "ttt_mlp_forward"]
+__all__ = ["ttt_linear_forward", "ttt_linear_forward_split_noalloc", "ttt_linear_decode_step",
+           "ttt_linear_decode_step_compact", "ttt_linear_backward", "ttt_mlp_forward"]
 
 HEAD_DIM = 64
 
@@ -148,6 +148,41 @@ def ttt_linear_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: t
             rc = _lib.lib().ttt_linear_forward(*args, _stream(q, stream))
             _lib.check("ttt_linear_forward", rc)
     return z, w_out
+
+
+def ttt_linear_forward_split_noalloc(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                                     eta: torch.Tensor, w0: torch.Tensor,
+                                     ln_gamma: Optional[torch.Tensor] = None,
+                                     ln_beta: Optional[torch.Tensor] = None, *,
+                                     z: torch.Tensor, w_out: Optional[torch.Tensor] = None,
+                                     mini_batch: int = 16, eps: float = 1e-6,
+                                     layer_norm: bool = True, residual: bool = True,
+                                     state0_per_batch: bool = False, stream=None) -> None:
+    """ttt_linear_forward_split_noalloc of include/ttt.h: the two-workgroup
+    TTT-Linear scan with its scratch in the library's fixed per-device array
+    instead of a workspace.  Nothing is allocated here either: the caller
+    passes z [B,H,T,d] and, optionally, w_out [B,H,d,d] fp32."""
+    _dev_tensor("q", q)
+    B, H, T, d = q.shape
+    _dev_tensor("k", k, q.dtype, q.shape, device=q.device)
+    _dev_tensor("v", v, q.dtype, q.shape, device=q.device)
+    _dev_tensor("eta", eta, torch.float32, (B, H, T), device=q.device)
+    _dev_tensor("w0", w0, torch.float32, (B, H, d, d) if state0_per_batch else (H, d, d),
+                device=q.device)
+    if layer_norm:
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d), device=q.device)
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d), device=q.device)
+    else:
+        ln_gamma = ln_beta = None
+    _dev_tensor("z", z, q.dtype, q.shape, device=q.device)
+    if w_out is not None:
+        _dev_tensor("w_out", w_out, torch.float32, (B, H, d, d), device=q.device)
+    p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
+    with torch.cuda.device(q.device):   # the library launches on the current device
+        rc = _lib.lib().ttt_linear_forward_split_noalloc(
+            ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(eta), _ptr(w0), _ptr(ln_gamma),
+            _ptr(ln_beta), _ptr(z), _ptr(w_out), _stream(q, stream))
+    _lib.check("ttt_linear_forward_split_noalloc", rc)
 
 
 def ttt_linear_decode_step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,

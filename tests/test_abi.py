@@ -26,8 +26,8 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 8
-    for code in range(7):
+    assert _lib.abi_version() == 9
+    for code in range(8):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
 
@@ -145,6 +145,32 @@ def test_split_workspace_size():
         units * 256 + 256 + units * tiles * 6144
     assert _lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(_params(T=0))) == 0
     assert _lib.lib().ttt_linear_split_workspace_bytes(None) == 0
+
+
+def _noalloc(p, **ptrs):
+    names = ["q", "k", "v", "eta", "w0", "g", "b", "z", "w_out"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    return _lib.lib().ttt_linear_forward_split_noalloc(
+        ctypes.byref(p) if p is not None else None, *args, None)
+
+
+def test_noalloc_rejects_bad_arguments_and_oversized_problems():
+    """The no-allocation split entry point checks its arguments like the
+    split launch, then the problem's scratch need against the fixed array
+    (TTT_NOALLOC_SCRATCH_BYTES), all before any HIP call."""
+    ws = lambda **kw: _lib.lib().ttt_linear_split_workspace_bytes(ctypes.byref(_params(**kw)))
+    assert _noalloc(None) == _lib.TTT_ERR_NULL
+    for name in ["q", "k", "v", "eta", "w0", "z", "g", "b"]:
+        assert _noalloc(_params(), **{name: None}) == _lib.TTT_ERR_NULL, name
+    assert _noalloc(_params(mini_batch=8)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _noalloc(_params(d=32)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _noalloc(_params(), z=_addr(1)) == _lib.TTT_ERR_ALIAS            # z == q
+    assert _noalloc(_params(state0_per_batch=1), w_out=_addr(5)) == _lib.TTT_ERR_ALIAS
+    # the limit: 32 units fit up to T = 10912 (682 tiles of 6 KB per unit), not 10913
+    assert ws(B=1, H=32, T=10912) <= _lib.TTT_NOALLOC_SCRATCH_BYTES < ws(B=1, H=32, T=10913)
+    assert _noalloc(_params(B=1, H=32, T=10913)) == _lib.TTT_ERR_TOO_LARGE
+    assert _noalloc(_params(B=4, H=32, T=8192)) == _lib.TTT_ERR_TOO_LARGE
+    assert "scratch" in _lib.status_string(_lib.TTT_ERR_TOO_LARGE)
 
 
 def test_split_rejects_bad_arguments():
