@@ -108,8 +108,8 @@ struct LinLds {
   u32x4 gtb[2][4][64];  // (-eta G_t)^T as [hi, mid], chain wave -> update and output waves
   u32x2 gtl[2][4][64];  // its lo part
   f32x4 bkb[2][4][64];  // (K_{t+2} W_{t-1})^T, update wave -> chain wave
-  u32x4 grb[2][2][64];  // K_{t+1} K_{t+2}^T, K_t K_{t+2}^T as [hi, mid]
-  u32x2 grl[2][2][64];  // their lo parts
+  u32x4 grp[2][2][3][64];  // K_{t+1} K_{t+2}^T, K_t K_{t+2}^T in three bf16 parts,
+                           // packed as the three B operands of corr6
   f32x2 tkb[2][16];     // per token of tile t+2: (k . w_bar, sum_f u_f)
   f32x4 hqb[2][4][64];  // output pre-activation of tile t-1 around its shift,
                         // update wave -> output wave
@@ -117,8 +117,6 @@ struct LinLds {
   u32x4 mqb[2][64];     // tril(K_t Q_t^T) as [hi, lo] (hi only for bf16 data),
                         // update wave 2 -> every update wave
   float mqm[2][16];     // q . w_bar per token of tile t, update wave 2 -> every update wave
-  u32x2 ktb[2][4][64];  // K_t^T as 16x16x16 A operands (bf16 data, split units),
-                        // update wave 2 -> every update wave
   uint16_t cst[8][D];   // bf16 rows: w_bar hi, 2 gamma hi, w_bar mid, 2 gamma mid,
                         // w_bar lo, 2 gamma lo, zero, zero
 };
@@ -225,25 +223,30 @@ __device__ __forceinline__ u32x2 mid_of(u32x4 g) { return u32x2{g.z, g.w}; }
 __device__ __forceinline__ u32x4 hilo(const Split4& s) { return cat(s.hi, s.lo); }
 
 // acc + (-eta G)^T S for a score tile S (tokens x tokens) and G, each as
-// three bf16 parts ([hi, mid] tuple and lo): the six products down to a
-// relative size of 2^-16 (hi hi, mid hi, hi mid, lo hi, hi lo, mid mid),
-// paired into three 16x16x32 products whose slots 0-3 and 4-7 hold the two
-// 16-deep operands (acc may come from LDS).
-__device__ __forceinline__ f32x4 corr6(u32x4 gt, u32x2 gl, u32x4 s, u32x2 sl, f32x4 acc) {
-  const u32x2 uh = hi_of(gt), um = mid_of(gt), sh = hi_of(s), sm = mid_of(s);
-  acc = mfma32(cat(uh, um), cat(sh, sh), acc);
-  acc = mfma32(cat(uh, gl), cat(sm, sh), acc);
-  acc = mfma32(cat(uh, um), cat(sl, sm), acc);
+// three bf16 parts: the six products down to a relative size of 2^-16 (hi
+// hi, mid hi, lo hi, hi mid, hi lo, mid mid), paired into three 16x16x32
+// products whose slots 0-3 and 4-7 hold the two 16-deep operands.  G comes
+// as the tuples [hi, mid] and [lo, hi], S as the packed B operands
+// [hi, hi], [hi, mid], [lo, mid] (ScoreOps), so that no operand needs a
+// register copy (acc may come from LDS).
+struct ScoreOps {
+  u32x4 b[3];
+};
+__device__ __forceinline__ f32x4 corr6(u32x4 ghm, u32x4 glh, const ScoreOps& s, f32x4 acc) {
+  acc = mfma32(ghm, s.b[0], acc);  // hi hi + mid hi
+  acc = mfma32(glh, s.b[1], acc);  // lo hi + hi mid
+  acc = mfma32(ghm, s.b[2], acc);  // hi lo + mid mid
   return acc;
 }
-// A 16x16 fp32 tile (accumulator layout) as three bf16 parts: [hi, mid] and lo.
-struct Tile3 {
-  u32x4 hm;
-  u32x2 lo;
-};
-__device__ __forceinline__ Tile3 tile3(f32x4 x) {
-  const Split4x3 s = split4x3(x);
-  return Tile3{cat(s.hi, s.mid), s.lo};
+__device__ __forceinline__ ScoreOps score_ops(const Split4x3& s) {
+  return ScoreOps{{cat(s.hi, s.hi), cat(s.hi, s.mid), cat(s.lo, s.mid)}};
+}
+__device__ __forceinline__ ScoreOps read_score(const u32x4 (&g)[3][64], int lane) {
+  return ScoreOps{{g[0][lane], g[1][lane], g[2][lane]}};
+}
+__device__ __forceinline__ void write_score(u32x4 (&g)[3][64], int lane, const ScoreOps& s) {
+#pragma unroll
+  for (int i = 0; i < 3; ++i) g[i][lane] = s.b[i];
 }
 
 // Dot products of the rows of X with the constant rows (w_bar hi, 2 gamma hi,
@@ -485,8 +488,8 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
     publish(0, ep, uc);
   }
   lds_barrier();  // period 0 starts
-  u32x4 gtm1 = {};  // (-eta G_{p-1})^T as [hi, mid]
-  u32x2 gltm1 = {};  // and its lo part
+  u32x4 gtm1 = {};   // (-eta G_{p-1})^T as [hi, mid]
+  u32x4 glhm1 = {};  // and as [lo, hi]
 
   for (int blk = 0; blk * TB <= n + 2; ++blk) {
 #pragma unroll
@@ -504,10 +507,8 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
       }
       const float eta = tile_eta(L.st, blk, tb, c);
       const f32x4 bk = L.bkb[(p - 1) & 1][w][lane];  // K_{p+1} W_{p-2}
-      const u32x4 s1 = L.grb[(p - 1) & 1][0][lane];  // K_p K_{p+1}^T
-      const u32x2 s1l = L.grl[(p - 1) & 1][0][lane];
-      const u32x4 s2 = L.grb[(p - 1) & 1][1][lane];  // K_{p-1} K_{p+1}^T
-      const u32x2 s2l = L.grl[(p - 1) & 1][1][lane];
+      const ScoreOps s1 = read_score(L.grp[(p - 1) & 1][0], lane);  // K_p K_{p+1}^T
+      const ScoreOps s2 = read_score(L.grp[(p - 1) & 1][1], lane);  // K_{p-1} K_{p+1}^T
       const f32x2 tk = L.tkb[(p - 1) & 1][c];
       const KV kvn = kv_of(blk, tb + 1);
       __builtin_amdgcn_sched_barrier(0);
@@ -515,13 +516,13 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
       //      correction of K_{p+1} W_{p-2} by tile p-1
       const f32x4 un = u_of(kvn);
       const bool keep2 = MB16 || mbs(p + 1) || mbs(p);
-      f32x4 h = corr6(zero_unless(keep2, gtm1), zero_unless(keep2, gltm1), s2, s2l, bk);
+      f32x4 h = corr6(zero_unless(keep2, gtm1), zero_unless(keep2, glhm1), s2, bk);
       // ---- gradient of tile p (zero for rows past T, so past the end the
       //      update of W is a no-op)
-      u32x4 gt;
-      u32x2 gl;
+      u32x4 gt, glh;
       {
-        const bool valid = p * 16 + c < T;
+        // rows past T: eta taken as zero, so their gradient is zero
+        const float etav = p * 16 + c < T ? eta : 0.f;
         f32x4 eg;
         if (LN) {
           const f32x4 S = (xs[0] + xs[1]) + (xs[2] + xs[3]);
@@ -534,7 +535,7 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
           const float sge2 = __builtin_fmaf(mr * mr, Gam, __builtin_fmaf(-2.f * mr, S[2], S[3]));
           const float ma = __builtin_fmaf(2.f * rs, sge, su) * (1.0f / D);
           const float mx = __builtin_fmaf(2.f * rs, sge2, sue) * (rs * (1.0f / D));
-          const float c1 = -eta * rs, c2 = c1 * rs;
+          const float c1 = -etav * rs, c2 = c1 * rs;
           const float b0 = -c1 * ma, c2mx = -c2 * mx;
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -543,10 +544,8 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
           }
         } else {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) eg[i] = -2.f * eta * (ep[i] + uc[i]);
+          for (int i = 0; i < 4; ++i) eg[i] = -2.f * etav * (ep[i] + uc[i]);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) eg[i] = valid ? eg[i] : 0.f;
         // three bf16 parts, each transposed on the matrix unit (exact)
         const Split4x3 s = split4x3(eg);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
@@ -555,15 +554,15 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
         const f32x4 tl = mfma16(s.lo, ident, zero);
         gt = u32x4{pack_bf16(th[0], th[1]), pack_bf16(th[2], th[3]), pack_bf16(tm[0], tm[1]),
                    pack_bf16(tm[2], tm[3])};
-        gl = u32x2{pack_bf16(tl[0], tl[1]), pack_bf16(tl[2], tl[3])};
+        glh = u32x4{pack_bf16(tl[0], tl[1]), pack_bf16(tl[2], tl[3]), gt.x, gt.y};
       }
       L.gtb[p & 1][w][lane] = gt;
-      L.gtl[p & 1][w][lane] = gl;
+      L.gtl[p & 1][w][lane] = u32x2{glh.x, glh.y};
       // ---- gradient point of tile p+1 and its LN sums (at p >= n-1 the
       //      tile does not exist: stale rows, unused)
       {
         const bool keep1 = MB16 || mbs(p + 1);
-        h = corr6(zero_unless(keep1, gt), zero_unless(keep1, gl), s1, s1l, h);
+        h = corr6(zero_unless(keep1, gt), zero_unless(keep1, glh), s1, h);
 #pragma unroll
         for (int i = 0; i < 4; ++i) ep[i] = LN ? h[i] - tk.x : h[i];
         uc = un;
@@ -571,7 +570,7 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
         publish((p + 1) & 1, ep, uc);
       }
       gtm1 = gt;
-      gltm1 = gl;
+      glhm1 = glh;
       lds_barrier();
     }
   }
@@ -624,17 +623,12 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       L.cst[w + 6][lane] = 0;
     }
   }
-  // K^T shared through LDS by one wave (bf16 data, split units: wave 2 has
-  // no other item there)
-  constexpr bool KTS = SPLIT && BF16;
   // "tile -1": no update and no output correction in period 0
   L.gtb[1][w][lane] = u32x4{0u, 0u, 0u, 0u};
   L.gtl[1][w][lane] = u32x2{0u, 0u};
   if (w == 2) {
     L.mqb[1][lane] = u32x4{0u, 0u, 0u, 0u};
     if (lane < 16) L.mqm[1][lane] = 0.f;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) L.ktb[1][r][lane] = u32x2{0u, 0u};
   }
   // The tiles past the end are read from stale staging rows (their
   // gradient is zero, but 0 * Inf would not be): buffer 1 starts as zeros
@@ -646,7 +640,6 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
     for (int i = t; i < N16; i += 256) b1[i] = u32x4{0u, 0u, 0u, 0u};
     for (int i = t; i < TB * 16; i += 256) L.st.eta[1][i] = 0.f;
   }
-  const u32x2 ident = ident_op(g, c);
   const u32x2 neg_ident = diag_op(g, c, 0xBF80u);  // -1 on the diagonal
   bool causal[4];
 #pragma unroll
@@ -693,12 +686,9 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
   L.bkb[0][w][lane] = times_state3<LO>(Ac, Al, kc0);
   L.bkb[1][w][lane] = times_state3<LO>(Ac, Al, kc1);
   if (w == 0) {
-    const Tile3 s01 = tile3(gram<LO>(kc0, kc1));
-    L.grb[1][0][lane] = s01.hm;
-    L.grl[1][0][lane] = s01.lo;
+    write_score(L.grp[1][0], lane, score_ops(split4x3(gram<LO>(kc0, kc1))));
   } else if (w == 1) {
-    L.grb[1][1][lane] = u32x4{0u, 0u, 0u, 0u};
-    L.grl[1][1][lane] = u32x2{0u, 0u};
+    write_score(L.grp[1][1], lane, ScoreOps{});
   } else if (w == 3 && LN) {
     L.tkb[0][c] = token_inputs(kc0, rows8<BF16>(tile_rows(L.st, 2, 0, 0), c, g));
     L.tkb[1][c] = token_inputs(kc1, rows8<BF16>(tile_rows(L.st, 2, 0, 1), c, g));
@@ -756,10 +746,6 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       } else {
         if (w == 1 || (!SPLIT && w == 2)) k0 = rows8<BF16>(Kp, c, g);
         if (w == 0) k1 = rows8<BF16>(tile_rows(L.st, 1, blk, tb + 1), c, g);
-      }
-      if constexpr (KTS) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) kt1[r] = Op4{L.ktb[(p - 1) & 1][r][lane], u32x2{0u, 0u}};
       }
       __builtin_amdgcn_sched_barrier(0);
       // ---- output pre-activation of tile p-1 around its shift:
@@ -828,13 +814,9 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       //      each: the score tiles K_{p+1} K_{p+2}^T, K_p K_{p+2}^T and
       //      (k . w_bar, sum_f u_f)
       if (w == 0) {
-        const Tile3 sc = tile3(gram<LO>(k1, kn));
-        L.grb[p & 1][0][lane] = sc.hm;
-        L.grl[p & 1][0][lane] = sc.lo;
+        write_score(L.grp[p & 1][0], lane, score_ops(split4x3(gram<LO>(k1, kn))));
       } else if (w == 1) {
-        const Tile3 sc = tile3(gram<LO>(k0, kn));
-        L.grb[p & 1][1][lane] = sc.hm;
-        L.grl[p & 1][1][lane] = sc.lo;
+        write_score(L.grp[p & 1][1], lane, score_ops(split4x3(gram<LO>(k0, kn))));
       } else if (w == 3 && LN) {
         if constexpr (!BF16) read_vn();
         L.tkb[p & 1][c] = token_inputs(kn, vn);
@@ -843,16 +825,13 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
       if constexpr (BF16) {
         // half of a row operand times the identity is the transposed 16x16
         // block, whose rows are the state's features feat(r, c)
-        if (!KTS || w == 2) {
-          const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+        const u32x2 ident = ident_op(g, c);
+        const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const u32x4 h = k0.p[r >> 1].hi;
-            const f32x4 t = mfma16((r & 1) ? u32x2{h.z, h.w} : u32x2{h.x, h.y}, ident, zero);
-            const u32x2 kt = {pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])};
-            if constexpr (KTS) L.ktb[p & 1][r][lane] = kt;
-            else kt1[r] = Op4{kt, u32x2{0u, 0u}};
-          }
+        for (int r = 0; r < 4; ++r) {
+          const u32x4 h = k0.p[r >> 1].hi;
+          const f32x4 t = mfma16((r & 1) ? u32x2{h.z, h.w} : u32x2{h.x, h.y}, ident, zero);
+          kt1[r] = Op4{u32x2{pack_bf16(t[0], t[1]), pack_bf16(t[2], t[3])}, u32x2{0u, 0u}};
         }
       } else {
         cols8<BF16>(kt1, Kp, c, g);
@@ -1103,7 +1082,6 @@ __device__ __forceinline__ void out_state_part(OutLds<BF16>& L, const LinearArgs
     u32x4* b1 = reinterpret_cast<u32x4*>(&L.st.qkv[1][0][0]);
     for (int i = threadIdx.x; i < N16; i += 256) b1[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  const u32x2 ident = ident_op(g, c);
   const u32x2 neg_ident = diag_op(g, c, 0xBF80u);
   bool causal[4];
 #pragma unroll
@@ -1176,6 +1154,7 @@ __device__ __forceinline__ void out_state_part(OutLds<BF16>& L, const LinearArgs
       }
       // ---- K_p^T for the next update
       if constexpr (BF16) {
+        const u32x2 ident = ident_op(g, c);
         const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
