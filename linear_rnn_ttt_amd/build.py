@@ -13,7 +13,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libttt_amd.so")
-SOURCES = ["ttt_api.cpp", "ttt_linear.hip", "ttt_mlp.hip", "ttt_decode.hip", "ttt_decode_compact.hip", "ttt_backward.hip",
+SOURCES = ["ttt_api.cpp", "ttt_validate.cpp", "ttt_linear.hip", "ttt_mlp.hip", "ttt_decode.hip", "ttt_decode_compact.hip", "ttt_backward.hip",
            "ttt_mlp_decode.hip",
            "ttt_mlp_decode_compact.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
