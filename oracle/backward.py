@@ -1,4 +1,4 @@
-"""fp64 CPU oracle of the TTT-Linear scan's backward pass.
+"""fp64 CPU oracle of the TTT-Linear and TTT-MLP scans' backward passes.
 
 TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and
 the CPU-baseline leg of ``bench.py`` may import this module.  It shares no
@@ -23,6 +23,12 @@ inner gradient grad l is taken by autograd with its graph kept
 (create_graph), and torch.autograd.grad differentiates L through the whole
 scan.  No blocking, reordering or hand-written adjoint: the tests pin it by
 central differences of the C oracle's forward and by closed forms.
+
+``mlp_backward`` does the same for the TTT-MLP scan (inner model
+f(x) = x + LN(GELU(x W1 + b1) W2 + b2), the codewithpapers.app record's
+"abstract"; state S = (W1, b1, W2, b2), exact erf GELU): the gradients of
+sum_t <dz_t, z_t> + <dS_T, S_T> with respect to q, k, v, eta, the initial
+state and gamma, beta.
 """
 from __future__ import annotations
 
@@ -85,6 +91,65 @@ def linear_backward(q, k, v, eta, w0, gamma, beta, dz, dw_final=None, *, mini_ba
     out = {}
     for name, g, like in zip(("dq", "dk", "dv", "deta", "dw0", "dgamma", "dbeta"), grads,
                              (Q, K, V, E, W0, G, Bt)):
+        out[name] = (torch.zeros_like(like) if g is None else g).detach().numpy()
+    if not layer_norm:
+        out["dgamma"] = np.zeros((H, d))
+        out["dbeta"] = np.zeros((H, d))
+    return out
+
+
+def _gelu(x):
+    """GELU, exact erf form: x Phi(x)."""
+    return 0.5 * x * (1.0 + torch.erf(x / np.sqrt(2.0)))
+
+
+def _f_mlp(x, W1, b1, W2, b2, gamma, beta, layer_norm, residual, eps):
+    """The TTT-MLP inner model on a row x [..., d]: x + LN(GELU(x W1 + b1) W2 + b2)."""
+    a = _gelu((x.unsqueeze(-2) @ W1).squeeze(-2) + b1)
+    y = (a.unsqueeze(-2) @ W2).squeeze(-2) + b2
+    if layer_norm:
+        y = _layer_norm(y, gamma, beta, eps)
+    return x + y if residual else y
+
+
+def mlp_backward(q, k, v, eta, w1, b1, w2, b2, gamma, beta, dz, dstate_final=None, *,
+                 mini_batch=16, layer_norm=True, residual=True, eps=1e-6,
+                 state0_per_batch=False):
+    """Gradients of L = sum <dz, z> + <dS_T, S_T> for the TTT-MLP scan.
+
+    q, k, v, dz [B,H,T,d]; eta [B,H,T]; w1 [H,d,m], b1 [H,m], w2 [H,m,d],
+    b2 [H,d] (leading [B,H] with state0_per_batch); gamma, beta [H,d]
+    (ignored without LN); dstate_final None or a tuple of four cotangents
+    with the final state's shapes [B,H,...].  Returns a dict of fp64
+    arrays: dq, dk, dv, deta, dw1, db1, dw2, db2 (the initial state's
+    shapes, summed over the batch when shared), dgamma, dbeta [H,d]."""
+    B, H, T, d = np.shape(q)
+    Q, K, V = _t(q, True), _t(k, True), _t(v, True)
+    E = _t(eta, True)
+    S0 = [_t(x, True) for x in (w1, b1, w2, b2)]
+    G = _t(gamma if layer_norm else np.ones((H, d)), True)
+    Bt = _t(beta if layer_norm else np.zeros((H, d)), True)
+    S = S0 if state0_per_batch else [x.unsqueeze(0).expand((B,) + tuple(x.shape)) for x in S0]
+    f = lambda x, St: _f_mlp(x, *St, G, Bt, layer_norm, residual, eps)
+
+    z = []
+    for t0 in range(0, T, mini_batch):
+        base = S
+        for t in range(t0, min(t0 + mini_batch, T)):
+            loss = ((f(K[:, :, t], base) - V[:, :, t]) ** 2).sum()
+            grads = torch.autograd.grad(loss, base, create_graph=True)
+            e = E[:, :, t]
+            S = [x - e.reshape(e.shape + (1,) * (x.dim() - 2)) * gx for x, gx in zip(S, grads)]
+            z.append(f(Q[:, :, t], S))
+    Z = torch.stack(z, 2)
+    L = (Z * _t(dz)).sum()
+    if dstate_final is not None:
+        for x, dx in zip(S, dstate_final):
+            L = L + (x * _t(dx)).sum()
+    grads = torch.autograd.grad(L, [Q, K, V, E] + S0 + [G, Bt], allow_unused=True)
+    out = {}
+    names = ("dq", "dk", "dv", "deta", "dw1", "db1", "dw2", "db2", "dgamma", "dbeta")
+    for name, g, like in zip(names, grads, [Q, K, V, E] + S0 + [G, Bt]):
         out[name] = (torch.zeros_like(like) if g is None else g).detach().numpy()
     if not layer_norm:
         out["dgamma"] = np.zeros((H, d))
