@@ -1,6 +1,6 @@
 /*
  * ttt.h -- C ABI of the MI355X (gfx950) TTT-layer forward scan, its
- * streaming (decode) step and the TTT-Linear backward pass.
+ * streaming (decode) step and its backward pass.
  *
  * The method (arXiv 2407.04620, "Learning to (Learn at Test Time): RNNs with
  * Expressive Hidden States"; summarised in the dmarx.github.io record
@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 9
+#define TTT_ABI_VERSION 10
 
 typedef enum {
   TTT_OK = 0,
@@ -378,6 +378,54 @@ ttt_status ttt_mlp_decode_step_compact(const ttt_params* p, int32_t hidden, int3
 
 /* Static, NUL-terminated description of a status code. */
 const char* ttt_status_string(ttt_status s);
+
+/*
+ * Bytes of device workspace that ttt_mlp_backward needs: per unit, the base
+ * of every 16-token mini-batch (132,352 bytes each) plus one more state and
+ * 180,736 bytes of per-mini-batch intermediates, rounded up to 256 bytes
+ * (0 if p fails the common checks or hidden != 256).  About 1.7 GB for
+ * B = 8, H = 12, T = 2048.
+ */
+uint64_t ttt_mlp_backward_workspace_bytes(const ttt_params* p, int32_t hidden);
+
+/*
+ * Backward pass of the TTT-MLP forward scan (ttt_mlp_forward: same p,
+ * hidden and inputs): the vector-Jacobian product that training needs (the
+ * LIT-801 record, "Key takeaways" item 2).  For cotangents dz (and the four
+ * d*_final on the final state) it writes the gradients of
+ *   L = sum_t <dz_t, z_t> + <dW1_T, W1_T> + <db1_T, b1_T> + <dW2_T, W2_T> + <db2_T, b2_T>
+ * with respect to q, k, v, eta, the initial state and gamma, beta.
+ *   dz          [B,H,T,d] io_dtype.
+ *   d*_final    [B,H,...] fp32 (the final state's shapes), all four or all NULL (zero).
+ *   dq, dk, dv  [B,H,T,d] io_dtype (out; rounded once from fp32);  deta [B,H,T] fp32.
+ *   dw1, db1, dw2, db2  fp32, the initial state's shapes: [H,...] summed over
+ *               the batch, or [B,H,...] with state0_per_batch.
+ *   dln_gamma, dln_beta  [H,d] fp32, summed over batch and tokens; required
+ *               with LN, may be NULL (both) without it.
+ *   workspace   device memory, 256-byte aligned, at least
+ *               ttt_mlp_backward_workspace_bytes(p, hidden) bytes, owned by the
+ *               caller; no initialisation needed; scratch after the call; one
+ *               call at a time.
+ * Outputs and the workspace overlap no input and no other output
+ * (TTT_ERR_ALIAS).  Supported: d = 64, hidden = 256, mini_batch = 16 (else
+ * TTT_ERR_UNSUPPORTED), both io dtypes, any flags.  Products run in fp32 on
+ * the matrix unit; the forward recurrence is replayed in the same call.  Two
+ * kernels on hip_stream (the scan, then the sums over the batch).
+ */
+ttt_status ttt_mlp_backward(const ttt_params* p, int32_t hidden,
+                            const void* q, const void* k, const void* v,
+                            const float* eta,
+                            const float* w1_0, const float* b1_0,
+                            const float* w2_0, const float* b2_0,
+                            const float* ln_gamma, const float* ln_beta,
+                            const void* dz,
+                            const float* dw1_final, const float* db1_final,
+                            const float* dw2_final, const float* db2_final,
+                            void* dq, void* dk, void* dv, float* deta,
+                            float* dw1, float* db1, float* dw2, float* db2,
+                            float* dln_gamma, float* dln_beta,
+                            void* workspace, uint64_t workspace_bytes,
+                            void* hip_stream);
 
 /* TTT_ABI_VERSION of the built library. */
 int32_t ttt_abi_version(void);

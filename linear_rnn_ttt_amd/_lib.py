@@ -20,6 +20,7 @@ EXPORTS = ("ttt_linear_forward", "ttt_linear_split_workspace_bytes", "ttt_linear
            "ttt_linear_forward_split_noalloc",
            "ttt_linear_decode_step", "ttt_linear_decode_step_compact", "ttt_linear_forward_save",
            "ttt_linear_backward_workspace_bytes", "ttt_linear_backward",
+           "ttt_mlp_backward_workspace_bytes", "ttt_mlp_backward",
            "ttt_mlp_forward", "ttt_mlp_decode_step",
            "ttt_mlp_decode_step_compact", "ttt_status_string", "ttt_abi_version")
 
@@ -75,6 +76,11 @@ def lib() -> ctypes.CDLL:
     L.ttt_linear_backward.argtypes = ([ctypes.POINTER(TTTParams)] + [P] * 17 +
                                       [ctypes.c_uint64, P])
     L.ttt_linear_backward.restype = ctypes.c_int
+    L.ttt_mlp_backward_workspace_bytes.argtypes = [ctypes.POINTER(TTTParams), ctypes.c_int32]
+    L.ttt_mlp_backward_workspace_bytes.restype = ctypes.c_uint64
+    L.ttt_mlp_backward.argtypes = ([ctypes.POINTER(TTTParams), ctypes.c_int32] + [P] * 26 +
+                                   [ctypes.c_uint64, P])
+    L.ttt_mlp_backward.restype = ctypes.c_int
     L.ttt_mlp_forward.argtypes = [ctypes.POINTER(TTTParams), ctypes.c_int32] + [P] * 16
     L.ttt_mlp_forward.restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int]

@@ -10,6 +10,7 @@
 
 #include "ttt_backward.hpp"
 #include "ttt_kernels.hpp"
+#include "ttt_mlp_backward.hpp"
 #include "ttt_mlp_compact.hpp"
 #include "ttt_stream.hpp"
 #include "ttt_validate.hpp"
@@ -208,6 +209,31 @@ ttt_status ttt_mlp_forward(const ttt_params* p, int32_t hidden, const void* q, c
   if (st != TTT_OK) return st;
   return status_of(tttk::launch_mlp(a, bf16_of(p), ln_of(p), res_of(p),
                                     static_cast<hipStream_t>(hip_stream)));
+}
+
+uint64_t ttt_mlp_backward_workspace_bytes(const ttt_params* p, int32_t hidden) {
+  uint64_t elems = 0;
+  if (tttv::check_common(p, &elems) != TTT_OK || hidden != 256) return 0;
+  return tttv::mlp_backward_workspace_bytes(p);
+}
+
+ttt_status ttt_mlp_backward(const ttt_params* p, int32_t hidden, const void* q, const void* k,
+                            const void* v, const float* eta, const float* w1_0,
+                            const float* b1_0, const float* w2_0, const float* b2_0,
+                            const float* ln_gamma, const float* ln_beta, const void* dz,
+                            const float* dw1_final, const float* db1_final,
+                            const float* dw2_final, const float* db2_final, void* dq, void* dk,
+                            void* dv, float* deta, float* dw1, float* db1, float* dw2,
+                            float* db2, float* dln_gamma, float* dln_beta, void* workspace,
+                            uint64_t workspace_bytes, void* hip_stream) {
+  tttk::MlpBackwardArgs a;
+  const ttt_status st = tttv::mlp_backward(
+      p, hidden, q, k, v, eta, w1_0, b1_0, w2_0, b2_0, ln_gamma, ln_beta, dz, dw1_final,
+      db1_final, dw2_final, db2_final, dq, dk, dv, deta, dw1, db1, dw2, db2, dln_gamma, dln_beta,
+      workspace, workspace_bytes, &a);
+  if (st != TTT_OK) return st;
+  return status_of(tttk::launch_mlp_backward(a, bf16_of(p), ln_of(p), res_of(p),
+                                             static_cast<hipStream_t>(hip_stream)));
 }
 
 }  // extern "C"

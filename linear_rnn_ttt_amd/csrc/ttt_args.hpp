@@ -156,4 +156,46 @@ struct MlpCompactArgs {
   float eps;
 };
 
+// Backward of the TTT-MLP scan (ttt_mlp_backward.hip).
+struct MlpBackwardArgs {
+  const void* q;            // [B,H,T,64] bf16 or fp32
+  const void* k;
+  const void* v;
+  const float* eta;         // [B,H,T]
+  const float* w1;          // initial state [H,64,256] / [H,256] / [H,256,64] / [H,64]
+  const float* b1;          //   (leading [B,H] with state0_per_batch)
+  const float* w2;
+  const float* b2;
+  const float* gamma;       // [H,64] (unused without LN)
+  const float* beta;
+  const void* dz;           // [B,H,T,64], like q
+  const float* dw1_final;   // cotangent of the final state [B,H,...], all four or none
+  const float* db1_final;
+  const float* dw2_final;
+  const float* db2_final;
+  void* dq;                 // [B,H,T,64], like q
+  void* dk;
+  void* dv;
+  float* deta;              // [B,H,T]
+  float* dw1;               // like the initial state (summed over the batch when shared)
+  float* db1;
+  float* dw2;
+  float* db2;
+  float* dgamma;            // [H,64] or nullptr (no LN)
+  float* dbeta;
+  // workspace: per unit, unit_floats floats: the base of every 16-token
+  // mini-batch (MLP_BWD_STATE_FLOATS each), the adjoint state, per-tile
+  // intermediates (MLP_BWD_TILE_FLOATS) ending in the unit's dgamma, dbeta
+  float* ws;
+  uint64_t unit_floats;
+  int32_t B, H, T;
+  float eps;
+  int32_t state0_per_batch;
+};
+
+// Floats of one TTT-MLP state (W1 64x256, b1 256, W2 256x64, b2 64) and of
+// the backward's per-tile intermediates of one unit.
+constexpr uint64_t MLP_BWD_STATE_FLOATS = 64 * 256 + 256 + 256 * 64 + 64;
+constexpr uint64_t MLP_BWD_TILE_FLOATS = 8 * 16 * 256 + 12 * 16 * 64 + 2 * 64;
+
 }  // namespace tttk

@@ -1,0 +1,765 @@
+// ttt_mlp_backward.hip -- backward pass of the TTT-MLP forward scan for gfx950.
+//
+// The outer loop trains the projections behind q, k and v, the initial
+// state and the per-token learning rate (dmarx.github.io record LIT-801,
+// "Key takeaways" item 2), so training needs the vector-Jacobian product of
+// the scan: for cotangents dz (and optionally dS_T on the final state) the
+// gradients of  L = sum_t <dz_t, z_t> + <dS_T, S_T>  with respect to q, k,
+// v, eta, the initial state S = (W1, b1, W2, b2) and the LN gamma, beta, for
+// the inner model f(x) = x + LN(GELU(x W1 + b1) W2 + b2) (the
+// codewithpapers.app record's "abstract"; exact erf GELU) with 16-token
+// mini-batches.
+//
+// Per mini-batch (base S, rows k, v, q, eta; n <= 16 tokens), the forward
+// is, exactly,
+//     P = K W1 + b1, A = GELU(P), O = A W2 + b2, x = LN-normalised O,
+//     t = V - beta - res K, a = 2 gamma (gamma x - t),
+//     G_o = rho (a - mean a - x mean(a x)),  U = G_o W2^T,  G_p = U GELU'(P),
+//     PQ = Q W1 + b1 - (tril(Q K^T + 1) eta) G_p,  AQ = GELU(PQ),
+//     OQ = AQ W2 + b2 - (tril(AQ A^T + 1) eta) G_o,  z = res Q + LN(OQ),
+//     next base = S - (K^T (eta G_p), sum eta G_p, A^T (eta G_o), sum eta G_o),
+// and its adjoint, walked over the mini-batches in reverse with the adjoint
+// (A1, a1, A2, a2) of the next base, is
+//     DOq = LN backward of dz,  dPQ = (DOq W2^T - (tril(DOq G_o^T) eta) A) GELU'(PQ),
+//     dQ = res dz + dPQ W1^T - (tril(dPQ G_p^T) eta) K,
+//     KA = K A1 + a1 + triu(K Q^T + 1) dPQ,   AA = A A2 + a2 + triu(A AQ^T + 1) DOq,
+//     GA1 = G_p A1^T + triu(G_p dPQ^T) Q,   GA2 = G_o A2^T + triu(G_o DOq^T) AQ,
+//     deta = -rowsum(KA G_p) - rowsum(AA G_o),
+//     dU = -eta KA GELU'(P),  dG_o = -eta AA + dU W2,  LN-gradient backward -> dO, dt,
+//     dV = dt,  dP = (-eta GA2 + dO W2^T) GELU'(P) - eta KA U GELU''(P),
+//     dK = dP W1^T - eta GA1 - res dt,
+//     A1 += Q^T dPQ + K^T dP,  a1 += sum(dPQ + dP),
+//     A2 += AQ^T DOq + A^T dO + dU^T G_o,  a2 += sum(DOq + dO)
+// (the same equations in fp64 numpy are checked against the autograd oracle
+// on the CPU).  After the first mini-batch (A1, a1, A2, a2) is the gradient
+// of the initial state.
+//
+// Mapping: one 512-thread workgroup (8 waves) per (batch, head) unit, two
+// phases.  Phase 1 replays the forward recurrence and stores the base of
+// every mini-batch in the unit's workspace; phase 2 walks the mini-batches
+// in reverse.  Every product is a set of 16x16 output tiles on the matrix
+// unit in fp32 (v_mfma_f32_16x16x4_f32: exact fp32 products, fp32
+// accumulation), dealt round-robin to the waves, with operands read from the
+// unit's workspace (bases, adjoint, per-tile intermediates: about 17 MB per
+// unit at T = 2048, resident in L2 while the unit runs) and the small masked
+// coefficient tiles from LDS.  Row-wise work (GELU, both LNs and the
+// LN-gradient backward) runs on the VALU between the products, one
+// workgroup barrier per dependent step.  Rows past T have eta = 0 and
+// dz = 0 and zero inputs, so they add nothing; their outputs are not stored.
+#include <hip/hip_runtime.h>
+
+#include "ttt_device.hpp"
+#include "ttt_mlp_backward.hpp"
+
+namespace tttk {
+namespace {
+
+constexpr int D = 64;    // head dimension
+constexpr int M = 256;   // hidden width
+constexpr int NB = 16;   // tokens per mini-batch
+constexpr int NT = 512;  // threads per workgroup
+constexpr int NWV = NT / 64;
+constexpr int SZ = D * M + M + M * D + D;  // floats of one state (W1, b1, W2, b2)
+constexpr int OB1 = D * M, OW2 = D * M + M, OB2 = D * M + M + M * D;
+constexpr int NX = 8, NY = 12;             // per-tile intermediates: 16x256 and 16x64
+static_assert(SZ == MLP_BWD_STATE_FLOATS && NX * NB * M + NY * NB * D + 2 * D == MLP_BWD_TILE_FLOATS,
+              "workspace layout and host size disagree");
+
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+// C[m][n] = sum_k a(m, k) b(k, n) for an R x C output (multiples of 16) over
+// K (multiple of 16): 16x16 tiles dealt to waves w0, w0 + nw, ... of the
+// workgroup; epi(m0, n0, acc) gets tile (m0, n0) with acc[i] at lane (g,c)
+// = C[m0 + 4g + i][n0 + c].  Operand fetches: a(m0 + c, k + g) and
+// b(k + g, n0 + c) for each group of 4 k, issued 16 k at a time ahead of
+// their four products.
+template <int R, int C, int K, class FA, class FB, class EPI>
+__device__ __forceinline__ void gemm(int wave, int w0, int nw, FA a, FB b, EPI epi) {
+  static_assert(R % 16 == 0 && C % 16 == 0 && K % 16 == 0, "tile multiples");
+  // lane indices behind an empty asm: the operand addresses derived from
+  // them are formed here, at each product, instead of being hoisted out of
+  // the mini-batch loop and held live in registers for every product site
+  int g = (threadIdx.x & 63) >> 4, c = threadIdx.x & 15;
+  asm volatile("" : "+v"(g), "+v"(c));
+  constexpr int TN = C / 16, TILES = (R / 16) * TN;
+  if (wave < w0 || wave >= w0 + nw) return;
+#pragma unroll 1
+  for (int t = wave - w0; t < TILES; t += nw) {
+    const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      float av[4], bv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        av[j] = a(m0 + c, k0 + 4 * j + g);
+        bv[j] = b(k0 + 4 * j + g, n0 + c);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
+    }
+    epi(m0, n0, acc);
+  }
+}
+
+// Sum over the 32 lanes of a half-wave.
+__device__ __forceinline__ float sum32(float x) {
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// GELU(x) = x Phi(x), GELU'(x) = Phi(x) + x phi(x), GELU''(x) = phi(x) (2 - x^2).
+__device__ __forceinline__ float phi_cdf(float x) { return 0.5f * (1.f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float phi_pdf(float x) { return 0.39894228040143268f * expf(-0.5f * x * x); }
+__device__ __forceinline__ float gelu(float x) { return x * phi_cdf(x); }
+__device__ __forceinline__ float gelu1(float x) { return phi_cdf(x) + x * phi_pdf(x); }
+__device__ __forceinline__ float gelu2(float x) { return phi_pdf(x) * (2.f - x * x); }
+
+template <bool BF16>
+__device__ __forceinline__ float ld_io(const void* p, size_t i) {
+  if constexpr (BF16) {
+    const uint16_t u = static_cast<const uint16_t*>(p)[i];
+    return __builtin_bit_cast(float, static_cast<uint32_t>(u) << 16);
+  } else {
+    return static_cast<const float*>(p)[i];
+  }
+}
+template <bool BF16>
+__device__ __forceinline__ void st_io(void* p, size_t i, float x) {
+  if constexpr (BF16) {
+    static_cast<uint16_t*>(p)[i] = static_cast<uint16_t>(pack_bf16(x, 0.f) & 0xffffu);
+  } else {
+    static_cast<float*>(p)[i] = x;
+  }
+}
+
+struct Lds {
+  float m[8][16][17];   // masked 16x16 coefficient tiles
+  float eta[16];
+  float rho[16], ma[16], mx[16];   // K-side LN: 1/sigma, mean(a), mean(a x)
+  float dln[16][2][D];             // dgamma, dbeta partials per token slot
+};
+
+template <bool BF16, bool LN, bool RES>
+__global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
+  __shared__ Lds L;
+  const int unit = blockIdx.x, head = unit % a.H;
+  const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int T = a.T, n = (T + 15) / 16;
+  float* ws = a.ws + static_cast<size_t>(unit) * a.unit_floats;
+  float* bases = ws;
+  float* adj = ws + static_cast<size_t>(n) * SZ;
+  float* Xb = adj + SZ;
+  float* Yb = Xb + NX * NB * M;
+  float* dln_out = ws + a.unit_floats - 2 * D;   // the unit's dgamma, dbeta
+  auto X = [&](int i) { return Xb + i * NB * M; };
+  auto Y = [&](int i) { return Yb + i * NB * D; };
+  const float* gam = a.gamma + static_cast<size_t>(head) * D;
+  const float* bet = a.beta + static_cast<size_t>(head) * D;
+  const size_t row0 = static_cast<size_t>(unit) * T;   // first token row of the unit
+
+  // ---- base 0 = the initial state; adjoint = dS_T (or zero); dln = 0
+  {
+    const size_t s0 = a.state0_per_batch ? unit : head;
+    const float* src[4] = {a.w1 + s0 * D * M, a.b1 + s0 * M, a.w2 + s0 * M * D, a.b2 + s0 * D};
+    const int off[4] = {0, OB1, OW2, OB2}, len[4] = {D * M, M, M * D, D};
+    for (int p = 0; p < 4; ++p)
+      for (int i = tid; i < len[p]; i += NT) bases[off[p] + i] = src[p][i];
+    const float* fin[4] = {a.dw1_final, a.db1_final, a.dw2_final, a.db2_final};
+    for (int p = 0; p < 4; ++p)
+      for (int i = tid; i < len[p]; i += NT)
+        adj[off[p] + i] = fin[p] ? fin[p][static_cast<size_t>(unit) * len[p] + i] : 0.f;
+  }
+  // dgamma, dbeta partials of this thread's token slot (2 wave + lane / 32)
+  // and features 2 (lane % 32), +1, summed over the tiles
+  float dg_acc[2] = {0.f, 0.f}, db_acc[2] = {0.f, 0.f};
+
+  // inputs of tile c as fp32 rows (zero past T): K -> Y0, Q -> Y1, V -> Y2,
+  // dz -> Y3 (with_dz), eta -> LDS (zero past T)
+  auto load_tile = [&](int c, bool with_dz) {
+    for (int i = tid; i < NB * D; i += NT) {
+      const int s = i / D, f = i % D, tok = c * NB + s;
+      const bool ok = tok < T;
+      const size_t e = (row0 + tok) * D + f;
+      Y(0)[i] = ok ? ld_io<BF16>(a.k, e) : 0.f;
+      Y(1)[i] = ok ? ld_io<BF16>(a.q, e) : 0.f;
+      Y(2)[i] = ok ? ld_io<BF16>(a.v, e) : 0.f;
+      if (with_dz) Y(3)[i] = ok ? ld_io<BF16>(a.dz, e) : 0.f;
+    }
+    if (tid < NB) L.eta[tid] = c * NB + tid < T ? a.eta[row0 + c * NB + tid] : 0.f;
+  };
+
+  // K side at base S (steps shared by both phases):
+  //   X0 = P, X1 = A, Y4 = O, Y5 = x, Y2 = t (overwrites v), Y6 = G_o,
+  //   X2 = U, X3 = G_p; LDS: rho, ma, mx.
+  auto kside = [&](const float* S) {
+    const float* W1 = S;
+    const float* b1 = S + OB1;
+    const float* W2 = S + OW2;
+    const float* b2 = S + OB2;
+    gemm<NB, M, D>(wave, 0, NWV, [&](int m, int k) { return Y(0)[m * D + k]; },
+                   [&](int k, int nn) { return W1[k * M + nn]; },
+                   [&](int m0, int n0, f32x4 acc) {
+                     const int nn = n0 + (lane & 15);
+#pragma unroll
+                     for (int i = 0; i < 4; ++i) {
+                       const float p = acc[i] + b1[nn];
+                       X(0)[(m0 + 4 * g + i) * M + nn] = p;
+                       X(1)[(m0 + 4 * g + i) * M + nn] = gelu(p);
+                     }
+                   });
+    __syncthreads();
+    gemm<NB, D, M>(wave, 0, NWV, [&](int m, int k) { return X(1)[m * M + k]; },
+                   [&](int k, int j) { return W2[k * D + j]; },
+                   [&](int m0, int n0, f32x4 acc) {
+                     const int j = n0 + (lane & 15);
+#pragma unroll
+                     for (int i = 0; i < 4; ++i) Y(4)[(m0 + 4 * g + i) * D + j] = acc[i] + b2[j];
+                   });
+    __syncthreads();
+    // LN of O and the loss gradient G_o: wave w has tokens 2w, 2w+1; lane
+    // half h, feature pair 2(l % 32), +1
+    {
+      const int s = 2 * wave + (lane >> 5), f = 2 * (lane & 31);
+      float o[2], t[2], x[2], av[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        o[u] = Y(4)[s * D + f + u];
+        const float kk = RES ? Y(0)[s * D + f + u] : 0.f;
+        t[u] = Y(2)[s * D + f + u] - (LN ? bet[f + u] : 0.f) - kk;
+      }
+      if (LN) {
+        const float mu = sum32(o[0] + o[1]) * (1.f / D);
+        const float var = sum32((o[0] - mu) * (o[0] - mu) + (o[1] - mu) * (o[1] - mu)) * (1.f / D);
+        const float rho = 1.f / sqrtf(var + a.eps);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          x[u] = (o[u] - mu) * rho;
+          av[u] = 2.f * gam[f + u] * (gam[f + u] * x[u] - t[u]);
+        }
+        const float ma = sum32(av[0] + av[1]) * (1.f / D);
+        const float mx = sum32(av[0] * x[0] + av[1] * x[1]) * (1.f / D);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          Y(5)[s * D + f + u] = x[u];
+          Y(6)[s * D + f + u] = rho * (av[u] - ma - x[u] * mx);
+        }
+        if ((lane & 31) == 0) {
+          L.rho[s] = rho;
+          L.ma[s] = ma;
+          L.mx[s] = mx;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) Y(6)[s * D + f + u] = 2.f * (o[u] - t[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) Y(2)[s * D + f + u] = t[u];
+    }
+    __syncthreads();
+    // U = G_o W2^T, G_p = U GELU'(P)
+    gemm<NB, M, D>(wave, 0, NWV, [&](int m, int k) { return Y(6)[m * D + k]; },
+                   [&](int k, int nn) { return W2[nn * D + k]; },
+                   [&](int m0, int n0, f32x4 acc) {
+                     const int nn = n0 + (lane & 15);
+#pragma unroll
+                     for (int i = 0; i < 4; ++i) {
+                       const int e = (m0 + 4 * g + i) * M + nn;
+                       X(2)[e] = acc[i];
+                       X(3)[e] = acc[i] * gelu1(X(0)[e]);
+                     }
+                   });
+    __syncthreads();
+  };
+
+  // ---- phase 1: replay the forward recurrence, storing every base
+  for (int c = 0; c + 1 < n; ++c) {
+    load_tile(c, false);
+    __syncthreads();
+    const float* S = bases + static_cast<size_t>(c) * SZ;
+    float* Sn = bases + static_cast<size_t>(c + 1) * SZ;
+    kside(S);
+    // W1' = W1 - K^T (eta G_p), W2' = W2 - A^T (eta G_o)
+    gemm<D, M, NB>(wave, 0, NWV, [&](int f, int s) { return Y(0)[s * D + f]; },
+                   [&](int s, int nn) { return L.eta[s] * X(3)[s * M + nn]; },
+                   [&](int m0, int n0, f32x4 acc) {
+                     const int nn = n0 + (lane & 15);
+#pragma unroll
+                     for (int i = 0; i < 4; ++i) {
+                       const int e = (m0 + 4 * g + i) * M + nn;
+                       Sn[e] = S[e] - acc[i];
+                     }
+                   });
+    gemm<M, D, NB>(wave, 0, NWV, [&](int nn, int s) { return X(1)[s * M + nn]; },
+                   [&](int s, int j) { return L.eta[s] * Y(6)[s * D + j]; },
+                   [&](int m0, int n0, f32x4 acc) {
+                     const int j = n0 + (lane & 15);
+#pragma unroll
+                     for (int i = 0; i < 4; ++i) {
+                       const int e = OW2 + (m0 + 4 * g + i) * D + j;
+                       Sn[e] = S[e] - acc[i];
+                     }
+                   });
+    for (int nn = tid; nn < M + D; nn += NT) {
+      float sum = 0.f;
+      if (nn < M) {
+        for (int s = 0; s < NB; ++s) sum += L.eta[s] * X(3)[s * M + nn];
+        Sn[OB1 + nn] = S[OB1 + nn] - sum;
+      } else {
+        const int j = nn - M;
+        for (int s = 0; s < NB; ++s) sum += L.eta[s] * Y(6)[s * D + j];
+        Sn[OB2 + j] = S[OB2 + j] - sum;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- phase 2: the mini-batches in reverse
+  for (int c = n - 1; c >= 0; --c) {
+    load_tile(c, true);
+    __syncthreads();
+    const float* S = bases + static_cast<size_t>(c) * SZ;
+    const float* W1 = S;
+    const float* b1 = S + OB1;
+    const float* W2 = S + OW2;
+    const float* b2 = S + OB2;
+    kside(S);
+    const float* K = Y(0);
+    const float* Q = Y(1);
+    const float* P = X(0);
+    const float* A = X(1);
+    const float* Gp = X(3);
+    const float* Go = Y(6);
+    auto tril_eta = [&](int idx, int i, int s, float v) {  // [i][s] for s <= i, scaled by eta_s
+      L.m[idx][i][s] = s <= i ? v * L.eta[s] : 0.f;
+    };
+    // M1 = tril(Q K^T + 1) eta
+    gemm<NB, NB, D>(wave, 0, 1, [&](int i, int f) { return Q[i * D + f]; },
+                    [&](int f, int s) { return K[s * D + f]; },
+                    [&](int m0, int n0, f32x4 acc) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i)
+                        tril_eta(0, 4 * g + i, lane & 15, acc[i] + 1.f);
+                    });
+    __syncthreads();
+    // PQ = Q W1 + b1 - M1 G_p -> X4, AQ = GELU(PQ) -> X5
+    gemm<NB, M, D + NB>(
+        wave, 0, NWV,
+        [&](int i, int k) { return k < D ? Q[i * D + k] : -L.m[0][i][k - D]; },
+        [&](int k, int nn) { return k < D ? W1[k * M + nn] : Gp[(k - D) * M + nn]; },
+        [&](int m0, int n0, f32x4 acc) {
+          const int nn = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float p = acc[i] + b1[nn];
+            X(4)[(m0 + 4 * g + i) * M + nn] = p;
+            X(5)[(m0 + 4 * g + i) * M + nn] = gelu(p);
+          }
+        });
+    __syncthreads();
+    const float* AQ = X(5);
+    // M2 = tril(AQ A^T + 1) eta
+    gemm<NB, NB, M>(wave, 0, 1, [&](int i, int k) { return AQ[i * M + k]; },
+                    [&](int k, int s) { return A[s * M + k]; },
+                    [&](int m0, int n0, f32x4 acc) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i)
+                        tril_eta(1, 4 * g + i, lane & 15, acc[i] + 1.f);
+                    });
+    __syncthreads();
+    // OQ = AQ W2 + b2 - M2 G_o -> Y7
+    gemm<NB, D, M + NB>(
+        wave, 0, NWV,
+        [&](int i, int k) { return k < M ? AQ[i * M + k] : -L.m[1][i][k - M]; },
+        [&](int k, int j) { return k < M ? W2[k * D + j] : Go[(k - M) * D + j]; },
+        [&](int m0, int n0, f32x4 acc) {
+          const int j = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Y(7)[(m0 + 4 * g + i) * D + j] = acc[i] + b2[j];
+        });
+    __syncthreads();
+    // output LN backward: DOq -> Y7; dgamma, dbeta
+    {
+      const int s = 2 * wave + (lane >> 5), f = 2 * (lane & 31);
+      float o[2], dz[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        o[u] = Y(7)[s * D + f + u];
+        dz[u] = Y(3)[s * D + f + u];
+      }
+      if (LN) {
+        const float mu = sum32(o[0] + o[1]) * (1.f / D);
+        const float var = sum32((o[0] - mu) * (o[0] - mu) + (o[1] - mu) * (o[1] - mu)) * (1.f / D);
+        const float rho = 1.f / sqrtf(var + a.eps);
+        float x[2], gd[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          x[u] = (o[u] - mu) * rho;
+          gd[u] = gam[f + u] * dz[u];
+        }
+        const float m1 = sum32(gd[0] + gd[1]) * (1.f / D);
+        const float m2 = sum32(gd[0] * x[0] + gd[1] * x[1]) * (1.f / D);
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          Y(7)[s * D + f + u] = rho * (gd[u] - m1 - x[u] * m2);
+          dg_acc[u] += dz[u] * x[u];
+          db_acc[u] += dz[u];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 2; ++u) Y(7)[s * D + f + u] = dz[u];
+      }
+    }
+    __syncthreads();
+    const float* DOq = Y(7);
+    // Mdo = tril(DOq G_o^T) eta
+    gemm<NB, NB, D>(wave, 0, 1, [&](int i, int j) { return DOq[i * D + j]; },
+                    [&](int j, int s) { return Go[s * D + j]; },
+                    [&](int m0, int n0, f32x4 acc) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) tril_eta(2, 4 * g + i, lane & 15, acc[i]);
+                    });
+    __syncthreads();
+    // dPQ = (DOq W2^T - Mdo A) GELU'(PQ) -> X4
+    gemm<NB, M, D + NB>(
+        wave, 0, NWV,
+        [&](int i, int k) { return k < D ? DOq[i * D + k] : -L.m[2][i][k - D]; },
+        [&](int k, int nn) { return k < D ? W2[nn * D + k] : A[(k - D) * M + nn]; },
+        [&](int m0, int n0, f32x4 acc) {
+          const int nn = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = (m0 + 4 * g + i) * M + nn;
+            X(4)[e] = acc[i] * gelu1(X(4)[e]);
+          }
+        });
+    __syncthreads();
+    const float* dPQ = X(4);
+    // the masked coefficient tiles that need dPQ / DOq, one wave each:
+    //   Mdp = tril(dPQ G_p^T) eta, Tk = triu(K Q^T + 1), Ta = triu(A AQ^T + 1),
+    //   Tgp = triu(G_p dPQ^T), Tgo = triu(G_o DOq^T)   ([s][i] for i >= s)
+    auto triu_put = [&](int idx, int s, int i, float v) { L.m[idx][s][i] = i >= s ? v : 0.f; };
+    gemm<NB, NB, M>(wave, 0, 1, [&](int i, int k) { return dPQ[i * M + k]; },
+                    [&](int k, int s) { return Gp[s * M + k]; },
+                    [&](int m0, int n0, f32x4 acc) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) tril_eta(3, 4 * g + i, lane & 15, acc[i]);
+                    });
+    gemm<NB, NB, D>(wave, 1, 1, [&](int s, int f) { return K[s * D + f]; },
+                    [&](int f, int i) { return Q[i * D + f]; },
+                    [&](int m0, int n0, f32x4 acc) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) triu_put(4, 4 * g + i, lane & 15, acc[i] + 1.f);
+                    });
+    gemm<NB, NB, M>(wave, 2, 1, [&](int s, int k) { return A[s * M + k]; },
+                    [&](int k, int i) { return AQ[i * M + k]; },
+                    [&](int m0, int n0, f32x4 acc) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) triu_put(5, 4 * g + i, lane & 15, acc[i] + 1.f);
+                    });
+    gemm<NB, NB, M>(wave, 3, 1, [&](int s, int k) { return Gp[s * M + k]; },
+                    [&](int k, int i) { return dPQ[i * M + k]; },
+                    [&](int m0, int n0, f32x4 acc) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) triu_put(6, 4 * g + i, lane & 15, acc[i]);
+                    });
+    gemm<NB, NB, D>(wave, 4, 1, [&](int s, int j) { return Go[s * D + j]; },
+                    [&](int j, int i) { return DOq[i * D + j]; },
+                    [&](int m0, int n0, f32x4 acc) {
+#pragma unroll
+                      for (int i = 0; i < 4; ++i) triu_put(7, 4 * g + i, lane & 15, acc[i]);
+                    });
+    __syncthreads();
+    const float* A1 = adj;
+    const float* a1 = adj + OB1;
+    const float* A2 = adj + OW2;
+    const float* a2 = adj + OB2;
+    // dQ = res dz + dPQ W1^T - Mdp K (stored); KA = K A1 + a1 + Tk dPQ -> X6;
+    // AA = A A2 + a2 + Ta DOq -> Y8; GA1 = G_p A1^T + Tgp Q -> Y9;
+    // GA2 = G_o A2^T + Tgo AQ -> X7
+    gemm<NB, D, M + NB>(
+        wave, 0, NWV,
+        [&](int i, int k) { return k < M ? dPQ[i * M + k] : -L.m[3][i][k - M]; },
+        [&](int k, int f) { return k < M ? W1[f * M + k] : K[(k - M) * D + f]; },
+        [&](int m0, int n0, f32x4 acc) {
+          const int f = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = m0 + 4 * g + i, tok = c * NB + s;
+            const float v = acc[i] + (RES ? Y(3)[s * D + f] : 0.f);
+            if (tok < T) st_io<BF16>(a.dq, (row0 + tok) * D + f, v);
+          }
+        });
+    gemm<NB, M, D + NB>(
+        wave, 0, NWV,
+        [&](int s, int k) { return k < D ? K[s * D + k] : L.m[4][s][k - D]; },
+        [&](int k, int nn) { return k < D ? A1[k * M + nn] : dPQ[(k - D) * M + nn]; },
+        [&](int m0, int n0, f32x4 acc) {
+          const int nn = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) X(6)[(m0 + 4 * g + i) * M + nn] = acc[i] + a1[nn];
+        });
+    gemm<NB, D, M + NB>(
+        wave, 0, NWV,
+        [&](int s, int k) { return k < M ? A[s * M + k] : L.m[5][s][k - M]; },
+        [&](int k, int j) { return k < M ? A2[k * D + j] : DOq[(k - M) * D + j]; },
+        [&](int m0, int n0, f32x4 acc) {
+          const int j = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Y(8)[(m0 + 4 * g + i) * D + j] = acc[i] + a2[j];
+        });
+    gemm<NB, D, M + NB>(
+        wave, 0, NWV,
+        [&](int s, int k) { return k < M ? Gp[s * M + k] : L.m[6][s][k - M]; },
+        [&](int k, int f) { return k < M ? A1[f * M + k] : Q[(k - M) * D + f]; },
+        [&](int m0, int n0, f32x4 acc) {
+          const int f = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) Y(9)[(m0 + 4 * g + i) * D + f] = acc[i];
+        });
+    gemm<NB, M, D + NB>(
+        wave, 0, NWV,
+        [&](int s, int k) { return k < D ? Go[s * D + k] : L.m[7][s][k - D]; },
+        [&](int k, int nn) { return k < D ? A2[nn * D + k] : AQ[(k - D) * M + nn]; },
+        [&](int m0, int n0, f32x4 acc) {
+          const int nn = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) X(7)[(m0 + 4 * g + i) * M + nn] = acc[i];
+        });
+    __syncthreads();
+    // deta = -rowsum(KA G_p) - rowsum(AA G_o); dU = -eta KA GELU'(P) -> X6;
+    // -eta KA U GELU''(P) -> X2
+    {
+      const int s = 2 * wave + (lane >> 5), l32 = lane & 31;
+      float acc = 0.f;
+      for (int nn = l32; nn < M; nn += 32) acc += X(6)[s * M + nn] * Gp[s * M + nn];
+      for (int j = l32; j < D; j += 32) acc += Y(8)[s * D + j] * Go[s * D + j];
+      acc = sum32(acc);
+      const int tok = c * NB + s;
+      if (l32 == 0 && tok < T) a.deta[row0 + tok] = -acc;
+    }
+    __syncthreads();
+    for (int e = tid; e < NB * M; e += NT) {
+      const int s = e / M;
+      const float p = P[e];
+      const float dgp = -L.eta[s] * X(6)[e];
+      X(2)[e] = dgp * X(2)[e] * gelu2(p);
+      X(6)[e] = dgp * gelu1(p);
+    }
+    __syncthreads();
+    const float* dU = X(6);
+    // dG_o = -eta AA + dU W2 -> Y8
+    gemm<NB, D, M>(wave, 0, NWV, [&](int s, int k) { return dU[s * M + k]; },
+                   [&](int k, int j) { return W2[k * D + j]; },
+                   [&](int m0, int n0, f32x4 acc) {
+                     const int j = n0 + (lane & 15);
+#pragma unroll
+                     for (int i = 0; i < 4; ++i) {
+                       const int s = m0 + 4 * g + i;
+                       Y(8)[s * D + j] = acc[i] - L.eta[s] * Y(8)[s * D + j];
+                     }
+                   });
+    __syncthreads();
+    // LN-gradient backward: dO -> Y10, dt -> Y11 (dv stored), dgamma, dbeta
+    {
+      const int s = 2 * wave + (lane >> 5), f = 2 * (lane & 31);
+      const int tok = c * NB + s;
+      float u[2], dO[2], dt[2];
+#pragma unroll
+      for (int v = 0; v < 2; ++v) u[v] = Y(8)[s * D + f + v];
+      if (LN) {
+        const float rho = L.rho[s], ma = L.ma[s], mx = L.mx[s];
+        float x[2], t[2], av[2];
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          x[v] = Y(5)[s * D + f + v];
+          t[v] = Y(2)[s * D + f + v];
+          av[v] = 2.f * gam[f + v] * (gam[f + v] * x[v] - t[v]);
+        }
+        const float drho = sum32(u[0] * (av[0] - ma - x[0] * mx) + u[1] * (av[1] - ma - x[1] * mx));
+        const float mu_ = sum32(u[0] + u[1]) * (1.f / D);
+        const float mux = sum32(u[0] * x[0] + u[1] * x[1]) * (1.f / D);
+        float da[2], dx[2];
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          da[v] = rho * (u[v] - mu_ - x[v] * mux);
+          dx[v] = -rho * (mx * u[v] + av[v] * mux) + 2.f * gam[f + v] * gam[f + v] * da[v];
+          dt[v] = -2.f * gam[f + v] * da[v];
+        }
+        const float mdx = sum32(dx[0] + dx[1]) * (1.f / D);
+        const float mdxx = sum32(dx[0] * x[0] + dx[1] * x[1]) * (1.f / D);
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          dO[v] = rho * (dx[v] - mdx - x[v] * mdxx) - drho * rho * rho * x[v] * (1.f / D);
+          dg_acc[v] += 2.f * (2.f * gam[f + v] * x[v] - t[v]) * da[v];
+          db_acc[v] -= dt[v];
+        }
+      } else {
+#pragma unroll
+        for (int v = 0; v < 2; ++v) {
+          dO[v] = 2.f * u[v];
+          dt[v] = -2.f * u[v];
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < 2; ++v) {
+        Y(10)[s * D + f + v] = dO[v];
+        Y(11)[s * D + f + v] = dt[v];
+        if (tok < T) st_io<BF16>(a.dv, (row0 + tok) * D + f + v, dt[v]);
+      }
+    }
+    __syncthreads();
+    const float* dOk = Y(10);
+    // dP = (-eta GA2 + dO W2^T) GELU'(P) + X2 -> X7
+    gemm<NB, M, D>(wave, 0, NWV, [&](int s, int k) { return dOk[s * D + k]; },
+                   [&](int k, int nn) { return W2[nn * D + k]; },
+                   [&](int m0, int n0, f32x4 acc) {
+                     const int nn = n0 + (lane & 15);
+#pragma unroll
+                     for (int i = 0; i < 4; ++i) {
+                       const int s = m0 + 4 * g + i, e = s * M + nn;
+                       X(7)[e] = (acc[i] - L.eta[s] * X(7)[e]) * gelu1(P[e]) + X(2)[e];
+                     }
+                   });
+    __syncthreads();
+    const float* dP = X(7);
+    // dK = dP W1^T - eta GA1 - res dt (stored)
+    gemm<NB, D, M>(wave, 0, NWV, [&](int s, int k) { return dP[s * M + k]; },
+                   [&](int k, int f) { return W1[f * M + k]; },
+                   [&](int m0, int n0, f32x4 acc) {
+                     const int f = n0 + (lane & 15);
+#pragma unroll
+                     for (int i = 0; i < 4; ++i) {
+                       const int s = m0 + 4 * g + i, tok = c * NB + s;
+                       const float v = acc[i] - L.eta[s] * Y(9)[s * D + f] -
+                                       (RES ? Y(11)[s * D + f] : 0.f);
+                       if (tok < T) st_io<BF16>(a.dk, (row0 + tok) * D + f, v);
+                     }
+                   });
+    // A1 += Q^T dPQ + K^T dP;  A2 += AQ^T DOq + A^T dO + dU^T G_o
+    float* A1w = adj;
+    float* A2w = adj + OW2;
+    gemm<D, M, 2 * NB>(
+        wave, 0, NWV,
+        [&](int f, int k) { return k < NB ? Q[k * D + f] : K[(k - NB) * D + f]; },
+        [&](int k, int nn) { return k < NB ? dPQ[k * M + nn] : dP[(k - NB) * M + nn]; },
+        [&](int m0, int n0, f32x4 acc) {
+          const int nn = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) A1w[(m0 + 4 * g + i) * M + nn] += acc[i];
+        });
+    gemm<M, D, 3 * NB>(
+        wave, 0, NWV,
+        [&](int nn, int k) {
+          return k < NB ? AQ[k * M + nn] : (k < 2 * NB ? A[(k - NB) * M + nn] : dU[(k - 2 * NB) * M + nn]);
+        },
+        [&](int k, int j) {
+          return k < NB ? DOq[k * D + j] : (k < 2 * NB ? dOk[(k - NB) * D + j] : Go[(k - 2 * NB) * D + j]);
+        },
+        [&](int m0, int n0, f32x4 acc) {
+          const int j = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) A2w[(m0 + 4 * g + i) * D + j] += acc[i];
+        });
+    for (int nn = tid; nn < M + D; nn += NT) {
+      float sum = 0.f;
+      if (nn < M) {
+        for (int s = 0; s < NB; ++s) sum += dPQ[s * M + nn] + dP[s * M + nn];
+        adj[OB1 + nn] += sum;
+      } else {
+        const int j = nn - M;
+        for (int s = 0; s < NB; ++s) sum += DOq[s * D + j] + dOk[s * D + j];
+        adj[OB2 + j] += sum;
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- the initial state's gradient (per batch: directly; shared: summed
+  // over the batch by the second kernel from the workspace) and dgamma, dbeta
+  if (a.state0_per_batch) {
+    float* dst[4] = {a.dw1 + static_cast<size_t>(unit) * D * M, a.db1 + static_cast<size_t>(unit) * M,
+                     a.dw2 + static_cast<size_t>(unit) * M * D, a.db2 + static_cast<size_t>(unit) * D};
+    const int off[4] = {0, OB1, OW2, OB2}, len[4] = {D * M, M, M * D, D};
+    for (int p = 0; p < 4; ++p)
+      for (int i = tid; i < len[p]; i += NT) dst[p][i] = adj[off[p] + i];
+  }
+  {
+    const int slot = 2 * wave + (lane >> 5), f = 2 * (lane & 31);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      L.dln[slot][0][f + u] = dg_acc[u];
+      L.dln[slot][1][f + u] = db_acc[u];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < 2 * D; i += NT) {   // slots summed in a fixed order
+    float sum = 0.f;
+    for (int sl = 0; sl < 16; ++sl) sum += L.dln[sl][i / D][i % D];
+    dln_out[i] = sum;
+  }
+}
+
+// Sums over the batch, one workgroup per head, in batch order
+// (deterministic): the gradient of a shared initial state, dgamma, dbeta.
+__global__ __launch_bounds__(256) void ttt_mlp_bwd_sum_k(MlpBackwardArgs a) {
+  const int h = blockIdx.x;
+  const int n = (a.T + 15) / 16;
+  auto unit_ws = [&](int b) {
+    return a.ws + static_cast<size_t>(b * a.H + h) * a.unit_floats;
+  };
+  if (!a.state0_per_batch) {
+    float* dst[4] = {a.dw1 + static_cast<size_t>(h) * D * M, a.db1 + static_cast<size_t>(h) * M,
+                     a.dw2 + static_cast<size_t>(h) * M * D, a.db2 + static_cast<size_t>(h) * D};
+    const int off[4] = {0, OB1, OW2, OB2}, len[4] = {D * M, M, M * D, D};
+    for (int p = 0; p < 4; ++p)
+      for (int i = threadIdx.x; i < len[p]; i += 256) {
+        float s = 0.f;
+        for (int b = 0; b < a.B; ++b) s += unit_ws(b)[static_cast<size_t>(n) * SZ + off[p] + i];
+        dst[p][i] = s;
+      }
+  }
+  if (a.dgamma) {
+    const size_t dln_off = a.unit_floats - 2 * D;
+    for (int e = threadIdx.x; e < 2 * D; e += 256) {
+      float s = 0.f;
+      for (int b = 0; b < a.B; ++b) s += unit_ws(b)[dln_off + e];
+      if (e < D)
+        a.dgamma[h * D + e] = s;
+      else
+        a.dbeta[h * D + e - D] = s;
+    }
+  }
+}
+
+template <bool BF16, bool LN>
+hipError_t launch_m2(const MlpBackwardArgs& a, bool res, hipStream_t s) {
+  const dim3 grid(a.B * a.H), block(NT);
+  if (res)
+    hipLaunchKernelGGL((ttt_mlp_bwd_k<BF16, LN, true>), grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL((ttt_mlp_bwd_k<BF16, LN, false>), grid, block, 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_mlp_backward(const MlpBackwardArgs& a, bool bf16, bool ln, bool residual,
+                               hipStream_t stream) {
+  hipError_t e;
+  if (bf16)
+    e = ln ? launch_m2<true, true>(a, residual, stream) : launch_m2<true, false>(a, residual, stream);
+  else
+    e = ln ? launch_m2<false, true>(a, residual, stream)
+           : launch_m2<false, false>(a, residual, stream);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(ttt_mlp_bwd_sum_k, dim3(a.H), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
+}  // namespace tttk

@@ -558,4 +558,99 @@ ttt_status mlp_forward(const ttt_params* p, int32_t hidden, const void* q, const
   return TTT_OK;
 }
 
+uint64_t mlp_backward_unit_floats(const ttt_params* p) {
+  const uint64_t n = (static_cast<uint64_t>(p->T) + 15) / 16;
+  return (n + 1) * tttk::MLP_BWD_STATE_FLOATS + tttk::MLP_BWD_TILE_FLOATS;
+}
+
+uint64_t mlp_backward_workspace_bytes(const ttt_params* p) {
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  return (units * mlp_backward_unit_floats(p) * 4 + 255) / 256 * 256;
+}
+
+ttt_status mlp_backward(const ttt_params* p, int32_t hidden, const void* q, const void* k,
+                        const void* v, const float* eta, const float* w1_0, const float* b1_0,
+                        const float* w2_0, const float* b2_0, const float* ln_gamma,
+                        const float* ln_beta, const void* dz, const float* dw1_final,
+                        const float* db1_final, const float* dw2_final, const float* db2_final,
+                        void* dq, void* dk, void* dv, float* deta, float* dw1, float* db1,
+                        float* dw2, float* db2, float* dln_gamma, float* dln_beta,
+                        void* workspace, uint64_t workspace_bytes, tttk::MlpBackwardArgs* a) {
+  uint64_t elems = 0;
+  const ttt_status st = check_common(p, &elems);
+  if (st != TTT_OK) return st;
+  if (hidden < 1) return TTT_ERR_SHAPE;
+  const bool ln = !(p->flags & TTT_NO_LN);
+  if (!q || !k || !v || !eta || !w1_0 || !b1_0 || !w2_0 || !b2_0 || !dz || !dq || !dk || !dv ||
+      !deta || !dw1 || !db1 || !dw2 || !db2 || !workspace)
+    return TTT_ERR_NULL;
+  if (ln && (!ln_gamma || !ln_beta || !dln_gamma || !dln_beta)) return TTT_ERR_NULL;
+  if ((dln_gamma == nullptr) != (dln_beta == nullptr)) return TTT_ERR_NULL;
+  const int n_fin = (dw1_final != nullptr) + (db1_final != nullptr) + (dw2_final != nullptr) +
+                    (db2_final != nullptr);
+  if (n_fin != 0 && n_fin != 4) return TTT_ERR_NULL;
+  if (hidden != kMlpHidden || p->mini_batch != 16) return TTT_ERR_UNSUPPORTED;
+  if (workspace_bytes < mlp_backward_workspace_bytes(p)) return TTT_ERR_SHAPE;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TTT_ERR_ARG;
+
+  const uint64_t es = p->io_dtype == TTT_BF16 ? 2 : 4;
+  const uint64_t units = static_cast<uint64_t>(p->B) * p->H;
+  const uint64_t s0 = p->state0_per_batch ? units : static_cast<uint64_t>(p->H);
+  const uint64_t dm = static_cast<uint64_t>(kHeadDim) * hidden;
+  const uint64_t ssz[4] = {dm * 4, static_cast<uint64_t>(hidden) * 4, dm * 4, kHeadDim * 4ull};
+  const Range inputs[] = {
+      span(q, elems * es), span(k, elems * es), span(v, elems * es),
+      span(eta, units * p->T * 4), span(w1_0, s0 * ssz[0]), span(b1_0, s0 * ssz[1]),
+      span(w2_0, s0 * ssz[2]), span(b2_0, s0 * ssz[3]),
+      span(ln ? ln_gamma : nullptr, p->H * 256ull), span(ln ? ln_beta : nullptr, p->H * 256ull),
+      span(dz, elems * es), span(dw1_final, units * ssz[0]), span(db1_final, units * ssz[1]),
+      span(dw2_final, units * ssz[2]), span(db2_final, units * ssz[3])};
+  const Range outputs[] = {
+      span(dq, elems * es), span(dk, elems * es), span(dv, elems * es),
+      span(deta, units * p->T * 4), span(dw1, s0 * ssz[0]), span(db1, s0 * ssz[1]),
+      span(dw2, s0 * ssz[2]), span(db2, s0 * ssz[3]), span(dln_gamma, p->H * 256ull),
+      span(dln_beta, p->H * 256ull), span(workspace, workspace_bytes)};
+  const int n_out = sizeof(outputs) / sizeof(outputs[0]);
+  for (int i = 0; i < n_out; ++i) {
+    for (const Range& r : inputs)
+      if (overlap(outputs[i], r)) return TTT_ERR_ALIAS;
+    for (int j = i + 1; j < n_out; ++j)
+      if (overlap(outputs[i], outputs[j])) return TTT_ERR_ALIAS;
+  }
+
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->eta = eta;
+  a->w1 = w1_0;
+  a->b1 = b1_0;
+  a->w2 = w2_0;
+  a->b2 = b2_0;
+  a->gamma = ln_gamma;
+  a->beta = ln_beta;
+  a->dz = dz;
+  a->dw1_final = dw1_final;
+  a->db1_final = db1_final;
+  a->dw2_final = dw2_final;
+  a->db2_final = db2_final;
+  a->dq = dq;
+  a->dk = dk;
+  a->dv = dv;
+  a->deta = deta;
+  a->dw1 = dw1;
+  a->db1 = db1;
+  a->dw2 = dw2;
+  a->db2 = db2;
+  a->dgamma = dln_gamma;
+  a->dbeta = dln_beta;
+  a->ws = static_cast<float*>(workspace);
+  a->unit_floats = mlp_backward_unit_floats(p);
+  a->B = p->B;
+  a->H = p->H;
+  a->T = p->T;
+  a->eps = p->ln_eps;
+  a->state0_per_batch = p->state0_per_batch;
+  return TTT_OK;
+}
+
 }  // namespace tttv

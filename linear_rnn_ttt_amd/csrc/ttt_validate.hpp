@@ -107,4 +107,19 @@ ttt_status mlp_forward(const ttt_params* p, int32_t hidden, const void* q, const
                        const float* ln_beta, void* z, float* w1_out, float* b1_out,
                        float* w2_out, float* b2_out, tttk::MlpArgs* a);
 
+// Workspace of the TTT-MLP backward: per unit, the base of every 16-token
+// mini-batch, the adjoint state and the per-tile intermediates.
+uint64_t mlp_backward_unit_floats(const ttt_params* p);
+uint64_t mlp_backward_workspace_bytes(const ttt_params* p);
+
+// ttt_mlp_backward.
+ttt_status mlp_backward(const ttt_params* p, int32_t hidden, const void* q, const void* k,
+                        const void* v, const float* eta, const float* w1_0, const float* b1_0,
+                        const float* w2_0, const float* b2_0, const float* ln_gamma,
+                        const float* ln_beta, const void* dz, const float* dw1_final,
+                        const float* db1_final, const float* dw2_final, const float* db2_final,
+                        void* dq, void* dk, void* dv, float* deta, float* dw1, float* db1,
+                        float* dw2, float* db2, float* dln_gamma, float* dln_beta,
+                        void* workspace, uint64_t workspace_bytes, tttk::MlpBackwardArgs* a);
+
 }  // namespace tttv

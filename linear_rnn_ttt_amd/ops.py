@@ -14,7 +14,8 @@ import torch
 from . import _lib
 
 __all__ = ["ttt_linear_forward", "ttt_linear_forward_split_noalloc", "ttt_linear_decode_step",
-           "ttt_linear_decode_step_compact", "ttt_linear_backward", "ttt_mlp_forward"]
+           "ttt_linear_decode_step_compact", "ttt_linear_backward", "ttt_mlp_forward",
+           "ttt_mlp_backward"]
 
 HEAD_DIM = 64
 
@@ -402,6 +403,67 @@ def ttt_linear_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: 
             _stream(q, stream))
     _lib.check("ttt_linear_backward", rc)
     return dq, dk, dv, deta, dw0, dgamma, dbeta
+
+
+def ttt_mlp_backward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,
+                     w1: torch.Tensor, b1: torch.Tensor, w2: torch.Tensor, b2: torch.Tensor,
+                     ln_gamma: Optional[torch.Tensor], ln_beta: Optional[torch.Tensor],
+                     dz: torch.Tensor, dstate_final=None, *, mini_batch: int = 16,
+                     eps: float = 1e-6, layer_norm: bool = True, residual: bool = True,
+                     state0_per_batch: bool = False, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> Tuple[torch.Tensor, ...]:
+    """Backward pass of the TTT-MLP scan for cotangents dz [B,H,T,d] (and
+    dstate_final, a tuple of four [B,H,...] fp32 cotangents of the final
+    state, or None); same inputs and options as ttt_mlp_forward.  Returns
+    (dq, dk, dv, deta, dw1, db1, dw2, db2, dln_gamma, dln_beta); the state
+    gradients have the initial state's shapes (summed over the batch when it
+    is shared), the LN gradients are [H,d] (zeros without LN).  workspace: a
+    uint8 GPU tensor of at least ttt_mlp_backward_workspace_bytes bytes to
+    use instead of a fresh one.  See include/ttt.h."""
+    _dev_tensor("q", q)
+    if q.dim() != 4:
+        raise ValueError("q must be [B, H, T, d]")
+    B, H, T, d = q.shape
+    m = w1.shape[-1]
+    dev = q.device
+    for name, t in (("k", k), ("v", v), ("dz", dz)):
+        _dev_tensor(name, t, q.dtype, q.shape, device=dev)
+    _dev_tensor("eta", eta, torch.float32, (B, H, T), device=dev)
+    lead = (B, H) if state0_per_batch else (H,)
+    shapes = [(d, m), (m,), (m, d), (d,)]
+    state = [w1, b1, w2, b2]
+    for name, t, sh in zip(("w1", "b1", "w2", "b2"), state, shapes):
+        _dev_tensor(name, t, torch.float32, lead + sh, device=dev)
+    if layer_norm:
+        _dev_tensor("ln_gamma", ln_gamma, torch.float32, (H, d), device=dev)
+        _dev_tensor("ln_beta", ln_beta, torch.float32, (H, d), device=dev)
+    else:
+        ln_gamma = ln_beta = None
+    fin = [None] * 4
+    if dstate_final is not None:
+        fin = list(dstate_final)
+        for name, t, sh in zip(("dw1_final", "db1_final", "dw2_final", "db2_final"), fin, shapes):
+            _dev_tensor(name, t, torch.float32, (B, H) + sh, device=dev)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    deta = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    dstate = [torch.empty(lead + sh, dtype=torch.float32, device=dev) for sh in shapes]
+    dgamma = torch.zeros((H, d), dtype=torch.float32, device=dev)
+    dbeta = torch.zeros((H, d), dtype=torch.float32, device=dev)
+    p = _params(q, mini_batch, eps, layer_norm, residual, state0_per_batch)
+    need = int(_lib.lib().ttt_mlp_backward_workspace_bytes(ctypes.byref(p), m))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _dev_tensor("workspace", workspace, torch.uint8, device=dev)
+    with torch.cuda.device(dev):   # the library launches on the current device
+        rc = _lib.lib().ttt_mlp_backward(
+            ctypes.byref(p), m, _ptr(q), _ptr(k), _ptr(v), _ptr(eta),
+            *[_ptr(t) for t in state], _ptr(ln_gamma), _ptr(ln_beta), _ptr(dz),
+            *[_ptr(t) for t in fin], _ptr(dq), _ptr(dk), _ptr(dv), _ptr(deta),
+            *[_ptr(t) for t in dstate], _ptr(dgamma if layer_norm else None),
+            _ptr(dbeta if layer_norm else None), _ptr(workspace), workspace.numel(),
+            _stream(q, stream))
+    _lib.check("ttt_mlp_backward", rc)
+    return (dq, dk, dv, deta, *dstate, dgamma, dbeta)
 
 
 def ttt_mlp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torch.Tensor,

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 9
+    assert _lib.abi_version() == 10
     for code in range(8):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
