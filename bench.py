@@ -51,15 +51,23 @@ KERNEL_SOURCES = {
     "mlp_decode": ["ttt_mlp_decode.hip", "ttt_stream.hpp", "ttt_device.hpp"],
     "mlp_decode_compact": ["ttt_mlp_decode_compact.hip", "ttt_mlp_compact.hpp",
                            "ttt_device.hpp"],
+    "mlp_backward": ["ttt_mlp_backward.hip", "ttt_mlp_backward.hpp", "ttt_args.hpp",
+                     "ttt_device.hpp"],
 }
 KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k",
                "backward": "ttt_linear_bwd_k", "decode_compact": "ttt_linear_decode_compact_k",
                "mlp_decode": "ttt_mlp_decode_k",
-               "mlp_decode_compact": "ttt_mlp_decode_compact_k"}
-BACKWARD_METRIC = "TTT-Linear backward tokens/s at 1.3B shape T=8k; % fp32 ALU roofline"
+               "mlp_decode_compact": "ttt_mlp_decode_compact_k",
+               "mlp_backward": "ttt_mlp_bwd_k"}
+BACKWARD_METRIC = "TTT-Linear backward tokens/s at 1.3B shape T=8k; % fp32 MFMA roofline"
 TRAIN_METRIC = ("TTT-Linear training step (forward saving the bases + backward) tokens/s at "
-                "1.3B shape T=8k; % fp32 ALU roofline of the backward")
-FP32_VECTOR_PEAK_TFS = 157.3   # MI355X fp32 vector (packed); non-packed FMA issue is half
+                "1.3B shape T=8k; % fp32 MFMA roofline of the backward")
+MLP_BACKWARD_METRIC = "TTT-MLP backward tokens/s at 125M shape T=2k; % fp32 MFMA roofline"
+# MI355X dense fp32 matrix (MFMA) rate: the roof of fp32-precision
+# contractions.  The MLP backward runs its products on it directly; the
+# Linear backward reaches fp32 precision with bf16 hi/lo products on the bf16
+# matrix unit instead (three bf16 products per fp32 product).
+FP32_MFMA_PEAK_TFS = 157.3
 DECODE_METRIC = ("TTT-Linear streaming step tokens/s (one token per (batch, head) unit per "
                  "launch); % HBM roofline")
 MLP_DECODE_METRIC = ("TTT-MLP streaming step tokens/s (one token per (batch, head) unit per "
@@ -603,9 +611,8 @@ def run_backward(args) -> dict:
     from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs
 
     w = WORKLOADS[args.workload]
-    if w.kind != "linear":
-        raise SystemExit("bench.py: the backward is TTT-Linear's (workload %s is %s)"
-                         % (w.name, w.kind))
+    if w.kind == "mlp":
+        return run_mlp_backward(args, w)
     inp = make_inputs(w)
     dev = upload(inp, w.io)
     dz = np.random.default_rng(w.seed + 1000).standard_normal(inp["q"].shape).astype(np.float32)
@@ -675,9 +682,9 @@ def run_backward(args) -> dict:
                              "ttt_linear_backward: one 512-thread workgroup per (batch, head) "
                              "unit, bf16 hi/lo matrix-unit products, mini-batch bases in a "
                              "workspace" + (" stored by the forward" if train else "")},
-        "roofline": {"bound": "alu", "achieved": round(tflops, 3),
-                     "peak": FP32_VECTOR_PEAK_TFS, "unit": "TFLOP/s",
-                     "frac": round(tflops / FP32_VECTOR_PEAK_TFS, 5),
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                     "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP32_MFMA_PEAK_TFS, 5),
                      "traffic": read_traffic("backward", w.name + ("_train" if train else "")),
                      "kernel": KERNEL_NAME["backward"],
                      "avg_launch_ms": round(avg_launch_s * 1e3, 4),
@@ -689,6 +696,132 @@ def run_backward(args) -> dict:
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline_backward(w, inp, dz, args.cpu_budget)
     return res
+
+
+def mlp_backward_alg(w) -> dict:
+    """What the TTT-MLP backward itself must move and compute per launch.
+
+    Bytes per token-head: q, k, v and dz read and dq, dk, dv written (7 d io
+    elements), eta read and deta written (8 B); per head the initial state
+    (W1, b1, W2, b2) and gamma, beta read and their gradients written.  The
+    mini-batch bases and intermediates the kernel keeps in its workspace are
+    its own choice and are not counted.  Flops per token-head: 22 products of
+    a row with a d x m (or m x d) matrix, 2 flops per multiply-add -- the
+    forward (k W1, a W2, g_o W2^T, q W1, a_q W2 and the two state updates)
+    and the fifteen of the chunked adjoint (dO_q W2^T, dp_q W1^T, k A1,
+    a A2, g_p A1^T, g_o A2^T, du W2, do W2^T, dp W1^T and the five rank-1
+    updates of the adjoint state)."""
+    es = 2 if w.io == "bf16" else 4
+    th = w.B * w.H * w.T
+    d, m = w.d, w.hidden
+    per_th = 7 * d * es + 8
+    per_head = 2 * (2 * d * m + m + d + 2 * d) * 4
+    return {"bytes": th * per_th + w.H * per_head, "bytes_per_token_head": per_th,
+            "flops": th * 44 * d * m, "flops_per_token_head": 44 * d * m}
+
+
+def run_mlp_backward(args, w) -> dict:
+    import ctypes
+
+    import numpy as np
+    import torch
+
+    from linear_rnn_ttt_amd import _lib, ttt_mlp_backward
+
+    from linear_rnn_ttt_amd.inputs import make_inputs
+
+    inp = make_inputs(w)
+    dev = upload(inp, w.io)
+    dz = np.random.default_rng(w.seed + 1000).standard_normal(inp["q"].shape).astype(np.float32)
+    dz_dev = torch.from_numpy(dz).cuda().to(dev["q"].dtype)
+    p = _lib.TTTParams(w.B, w.H, w.T, w.d, w.mini_batch,
+                       _lib.TTT_BF16 if w.io == "bf16" else _lib.TTT_F32, 0, w.eps, 0)
+    ws = torch.empty(int(_lib.lib().ttt_mlp_backward_workspace_bytes(ctypes.byref(p), w.hidden)),
+                     dtype=torch.uint8, device="cuda")
+    args_ = (dev["q"], dev["k"], dev["v"], dev["eta"], dev["w1"], dev["b1"], dev["w2"],
+             dev["b2"], dev["gamma"], dev["beta"], dz_dev)
+    stream = torch.cuda.current_stream()
+
+    def step(s_=None, e_=None):
+        if s_ is not None:
+            s_.record(stream)
+        out = ttt_mlp_backward(*args_, eps=w.eps, workspace=ws)
+        if e_ is not None:
+            e_.record(stream)
+        return out
+
+    for _ in range(args.warmup):
+        out = step()
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_, e_ in ev:
+        out = step(s_, e_)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_launch_s = sum(s_.elapsed_time(e_) for s_, e_ in ev) / len(ev) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    alg = mlp_backward_alg(w)
+    tflops = alg["flops"] / avg_launch_s / 1e12
+    res = {
+        "metric": MLP_BACKWARD_METRIC,
+        "value": round(w.tokens / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",   # fp32 matrix-unit products, fp32 accumulation
+        "data": "synthetic",
+        "config": {"workload": w.name + "_backward", "inner_model": "TTT-MLP", "B": w.B,
+                   "H": w.H, "T": w.T, "d": w.d, "hidden": w.hidden,
+                   "mini_batch": w.mini_batch, "io": w.io, "parallelism": "none (1 GPU)",
+                   "launch": "ttt_mlp_backward: one 512-thread workgroup per (batch, head) "
+                             "unit, forward replay then the reverse walk, fp32 matrix-unit "
+                             "products over a per-unit workspace"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                     "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tflops / FP32_MFMA_PEAK_TFS, 5),
+                     "traffic": read_traffic("mlp_backward", w.name),
+                     "kernel": KERNEL_NAME["mlp_backward"],
+                     "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                     "algorithmic_flops_per_launch": alg["flops"],
+                     "algorithmic_bytes_per_launch": alg["bytes"],
+                     "hbm_gbs_algorithmic": round(alg["bytes"] / avg_launch_s / 1e9, 1)},
+        "outputs_finite": bool(all(torch.isfinite(t.float()).all().item() for t in out[:4])),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_mlp_backward(w, inp, dz, args.cpu_budget)
+    return res
+
+
+def cpu_baseline_mlp_backward(w, inp, dz, budget_s: float):
+    """The fp64 TTT-MLP backward oracle on one unit (batch 0, head 0) for the
+    first T_s tokens, T_s doubled from 64 until a run takes a quarter of the
+    budget; scaled to the metric's unit (one unit is 1/H of a token)."""
+    from oracle.backward import mlp_backward
+
+    T_s, dt = 32, 0.0
+    while dt < budget_s / 4 and T_s < w.T:
+        T_s *= 2
+        sl = (slice(0, 1), slice(0, 1), slice(0, T_s))
+        t0 = time.perf_counter()
+        mlp_backward(inp["q"][sl], inp["k"][sl], inp["v"][sl], inp["eta"][sl], inp["w1"][:1],
+                     inp["b1"][:1], inp["w2"][:1], inp["b2"][:1], inp["gamma"][:1],
+                     inp["beta"][:1], dz[sl], mini_batch=w.mini_batch, eps=w.eps)
+        dt = time.perf_counter() - t0
+    import torch
+    return {"value": round(T_s / w.H / dt, 2), "unit": "tokens/s",
+            "cores": torch.get_num_threads(), "kind": "oracle",
+            "sample": "unit (0, 0), first %d tokens, %.2f s wall, fp64 torch autograd" % (
+                T_s, dt)}
 
 
 def cpu_baseline_backward(w, inp, dz, budget_s: float):
@@ -795,6 +928,9 @@ def _profiled(args):
                 decode_flops(w))
     if args.backward:
         w = WORKLOADS[args.workload]
+        if w.kind == "mlp":
+            alg = mlp_backward_alg(w)
+            return "mlp_backward", w.name, alg["bytes"], alg["flops"]
         alg = backward_alg(w)
         return "backward", w.name + ("_train" if args.train else ""), alg["bytes"], alg["flops"]
     w = WORKLOADS[args.workload]
@@ -879,7 +1015,8 @@ def main(argv=None):
     ap.add_argument("--decode", action="store_true",
                     help="time the TTT-Linear streaming step instead of the scan")
     ap.add_argument("--backward", action="store_true",
-                    help="time the TTT-Linear backward pass instead of the forward scan")
+                    help="time the backward pass (of the workload's inner model) instead of "
+                         "the forward scan")
     ap.add_argument("--compact", action="store_true",
                     help="with --decode: the compact pending state (base + mini-batch rows)")
     ap.add_argument("--train", action="store_true",
