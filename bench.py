@@ -43,14 +43,16 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E
 BF16_MFMA_PEAK_TFS = 2500.0    # MI355X dense bf16 matrix
 COPY_BYTES = 1 << 30           # calibration copy: 1 GiB read + 1 GiB written
 KERNEL_SOURCES = {
-    "linear": ["ttt_linear.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp"],
-    "mlp": ["ttt_mlp.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp"],
-    "decode": ["ttt_decode.hip", "ttt_device.hpp", "ttt_kernels.hpp"],
-    "backward": ["ttt_backward.hip", "ttt_backward.hpp", "ttt_device.hpp"],
-    "decode_compact": ["ttt_decode_compact.hip", "ttt_stream.hpp", "ttt_device.hpp"],
-    "mlp_decode": ["ttt_mlp_decode.hip", "ttt_stream.hpp", "ttt_device.hpp"],
+    "linear": ["ttt_linear.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp",
+               "ttt_args.hpp"],
+    "mlp": ["ttt_mlp.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp", "ttt_args.hpp"],
+    "decode": ["ttt_decode.hip", "ttt_device.hpp", "ttt_kernels.hpp", "ttt_args.hpp"],
+    "backward": ["ttt_backward.hip", "ttt_backward.hpp", "ttt_device.hpp", "ttt_args.hpp"],
+    "decode_compact": ["ttt_decode_compact.hip", "ttt_stream.hpp", "ttt_device.hpp",
+                       "ttt_args.hpp"],
+    "mlp_decode": ["ttt_mlp_decode.hip", "ttt_stream.hpp", "ttt_device.hpp", "ttt_args.hpp"],
     "mlp_decode_compact": ["ttt_mlp_decode_compact.hip", "ttt_mlp_compact.hpp",
-                           "ttt_device.hpp"],
+                           "ttt_device.hpp", "ttt_args.hpp"],
     "mlp_backward": ["ttt_mlp_backward.hip", "ttt_mlp_backward.hpp", "ttt_args.hpp",
                      "ttt_device.hpp"],
 }
