@@ -66,9 +66,7 @@ TRAIN_METRIC = ("TTT-Linear training step (forward saving the bases + backward) 
                 "1.3B shape T=8k; % fp32 MFMA roofline of the backward")
 MLP_BACKWARD_METRIC = "TTT-MLP backward tokens/s at 125M shape T=2k; % fp32 MFMA roofline"
 # MI355X dense fp32 matrix (MFMA) rate: the roof of fp32-precision
-# contractions.  The MLP backward runs its products on it directly; the
-# Linear backward reaches fp32 precision with bf16 hi/lo products on the bf16
-# matrix unit instead (three bf16 products per fp32 product).
+# contractions; both backward kernels run their products on it.
 FP32_MFMA_PEAK_TFS = 157.3
 DECODE_METRIC = ("TTT-Linear streaming step tokens/s (one token per (batch, head) unit per "
                  "launch); % HBM roofline")
@@ -673,7 +671,7 @@ def run_backward(args) -> dict:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",   # matrix-unit products on bf16 hi/lo splits, fp32 accumulation
+        "dtype": "f32",   # fp32 matrix-unit products, fp32 accumulation (bf16 io)
         "data": "synthetic",
         "config": {"workload": w.name + ("_train_step" if train else "_backward"),
                    "inner_model": "TTT-Linear", "B": w.B,
@@ -682,7 +680,7 @@ def run_backward(args) -> dict:
                    "launch": ("ttt_linear_forward_save (one 768-thread workgroup per unit) + "
                               if train else "") +
                              "ttt_linear_backward: one 512-thread workgroup per (batch, head) "
-                             "unit, bf16 hi/lo matrix-unit products, mini-batch bases in a "
+                             "unit, fp32 matrix-unit products, mini-batch bases in a "
                              "workspace" + (" stored by the forward" if train else "")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                      "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",

@@ -248,8 +248,8 @@ ttt_status ttt_linear_forward_save(const ttt_params* p,
 
 /*
  * Bytes of device workspace that ttt_linear_backward needs for these
- * parameters: 16 KB per unit and 16-token mini-batch (the base of every
- * mini-batch), plus 16 KB + 512 bytes per unit, rounded up to 256 bytes
+ * parameters: 16 KB per unit and 16-token tile (the state at every tile's
+ * start), plus 16 KB + 512 bytes per unit, rounded up to 256 bytes
  * (0 if p fails the common checks).  About 1 GB for B = 4, H = 32,
  * T = 8192.
  */
@@ -276,16 +276,19 @@ uint64_t ttt_linear_backward_workspace_bytes(const ttt_params* p);
  *             caller; no initialisation needed; scratch after the call; one
  *             call at a time.
  * Outputs and the workspace overlap no input and no other output
- * (TTT_ERR_ALIAS).  Supported: d = 64, mini_batch = 16 (else
- * TTT_ERR_UNSUPPORTED), both io dtypes, any flags.
- * With TTT_BASES_SAVED in p->flags the workspace must hold the mini-batch
- * bases that ttt_linear_forward_save stored for the same parameters (that
- * flag aside) and inputs; the backward then skips replaying the forward
+ * (TTT_ERR_ALIAS).  Supported: d = 64, mini_batch a positive multiple of
+ * 16 (b >= T: batch GD over the whole sequence, the LIT-801 record's item
+ * 3), else TTT_ERR_UNSUPPORTED; both io dtypes, any flags.
+ * With TTT_BASES_SAVED in p->flags (mini_batch = 16 only, else
+ * TTT_ERR_UNSUPPORTED) the workspace must hold the mini-batch bases that
+ * ttt_linear_forward_save stored for the same parameters (that flag aside)
+ * and inputs; the backward then skips replaying the forward
  * recurrence.  The library cannot check this: stale bases give wrong
  * gradients.
- * gfx950: two kernels on hip_stream.  One 256-thread workgroup per unit
- * first replays the forward recurrence and stores every mini-batch base in
- * the workspace, then walks the mini-batches in reverse (fp32 arithmetic);
+ * gfx950: two kernels on hip_stream.  One 512-thread workgroup per unit
+ * first replays the forward recurrence and stores the state at every
+ * 16-token tile's start in the workspace, then walks the tiles in reverse
+ * (fp32 arithmetic);
  * a second kernel sums dw0 (shared w0), dln_gamma and dln_beta over the
  * batch in a fixed order.  Results are deterministic.
  */

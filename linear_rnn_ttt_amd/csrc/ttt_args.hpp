@@ -132,6 +132,7 @@ struct BackwardArgs {
   float* ws_dw0;
   float* ws_dln;
   int32_t B, H, T;
+  int32_t tiles_per_mb;     // mini-batch / 16
   float eps;
   int32_t state0_per_batch;
   int32_t bases_saved;      // the forward stored the bases already: no replay

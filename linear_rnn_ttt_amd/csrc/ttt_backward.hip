@@ -25,22 +25,33 @@
 // and dW0 = A after the first mini-batch.  ([.] = only with the residual;
 // o uses M1 = tril(Q K^T) * eta the same way.)
 //
-// Kernel: one 256-thread workgroup (4 waves) per (batch, head) unit.  Phase 1
-// replays the forward recurrence of the bases and stores each mini-batch's
-// base in the workspace (16 KB per mini-batch: the device has room for every
-// base, so nothing is recomputed); phase 2 walks the mini-batches in reverse.
-// Every product is a 16x16x16 bf16 matrix-unit chain on hi/lo splits of
-// both fp32 operands (hi*hi + hi*lo + lo*hi, about 16 significant bits;
-// the bf16 input rows k and q are exact in bf16 and enter as hi only),
-// accumulated in fp32: wave w forms output columns 16w..16w+15 of each
-// token-tile product and holds columns 16w.. of W, W^T, A and A^T (A and A^T
-// as fp32 accumulators, updated in place).  The 16x16 Gram tiles are formed
-// in both orientations by every wave, so each masked coefficient tile is
-// already in the matrix unit's A-operand layout.  Product tiles go through
-// LDS to the token-row algebra (LN forward and backward), where wave w owns
-// token rows 4w..4w+3 with lane f holding feature f and sums are DPP/permlane
-// butterflies over the wave.  Tokens past T (a last partial mini-batch) are
-// zero rows with zero gradient factors; nothing is stored for them.
+// Mini-batches of 16 n tokens (n > 1; b >= T is batch GD over the whole
+// sequence, item 3) are walked one 16-token tile at a time: every tile's
+// gradients are taken at the mini-batch's base W_b, while its outputs see
+// the state W_c at the tile's start (W_b plus the earlier tiles' updates).
+// So K W, DH W^T use W_b and Q W, DO W^T use W_c, and the adjoint splits in
+// two: A, of the running state (A <- A + Q^T DO per tile), and B, of the
+// base (B <- B + K^T DH), folded into A at the mini-batch's first tile.
+// The workspace holds W_c of every tile; W_b is the first tile's.
+//
+// Kernel: one 512-thread workgroup (8 waves) per (batch, head) unit.  Phase 1
+// replays the forward recurrence and stores the state at every 16-token
+// tile's start in the workspace (16 KB per tile: the device has room for
+// all of them, so nothing is recomputed); phase 2 walks the tiles in reverse.
+// Every product runs on the fp32 matrix unit (16x16x4 products: exact fp32
+// products, fp32 accumulation): the recurrences of the states and of the
+// adjoint amplify rounding on ill-conditioned units, where products of bf16
+// hi/lo parts (about 16 significant bits) were not enough.  The four primal
+// waves (0-3) hold column block w of W and of A (fp32 accumulators, updated
+// in place) and form K W, Q W, the Q/K Grams, the output correction, K A and
+// the A update; the four dual waves (4-7) hold column block w - 4 of W^T and
+// A^T and form the DO/G Grams, DO W^T, G A^T, DH W^T and the A^T update.
+// Each Gram tile is formed in both orientations, so every masked coefficient
+// tile is already in the A-operand layout.  Product tiles go through LDS to
+// the token-row algebra (LN forward and backward), where wave w owns token
+// rows 2w, 2w+1 with lane f holding feature f and sums are DPP/permlane
+// butterflies over the wave.  Tokens past T (a last partial tile) are zero
+// rows with zero gradient factors; nothing is stored for them.
 #include "ttt_backward.hpp"
 #include "ttt_device.hpp"
 
@@ -61,7 +72,8 @@ struct __attribute__((aligned(16))) TileBuf {
   float g[TB][LS];
   float dO[TB][LS];
   float dh[TB][LS];
-  float w[DD][LS];            // the mini-batch's base
+  float w[DD][LS];            // the state at the tile's start
+  float wb[DD][LS];           // the mini-batch's base (mini-batches of several tiles)
   float t[3][TB][LS];         // product tiles on their way to the token-row algebra
   float eta[TB];
 };
@@ -149,57 +161,44 @@ __device__ __forceinline__ void put_fetched(float (*dst)[LS], int tid, uint4 u, 
 // What one mini-batch tile needs from global memory, per thread (raw).
 struct Fetch {
   uint4 k;           // token-tile share (k, or q for threads 256-511 in phase 2)
-  float4 w[2];       // share of the stored base (phase 2)
+  float4 w[2];       // share of the stored state at the tile's start (phase 2)
+  float4 wb[2];      // share of the mini-batch's base (phase 2, several tiles)
   float eta;         // eta of token tid % 16
   float v[4], dz[4];  // this wave's token rows, feature f
 };
 
 // ---- matrix-unit fragments (lane l: g = l / 16, c = l % 16) ---------------
-// A operand of a 16x16x16 product: lane holds A[c][4g + i]; B operand:
-// B[4g + i][c]; accumulator: D[4g + i][c] (see ttt_device.hpp).
+// A 16-deep product D += A B takes, per lane, the fragment A[c][4g + i] of
+// A and B[4g + i][c] of B (i = 0..3); the accumulator holds D[4g + i][c].
 
 __device__ __forceinline__ f32x4 f4(float a, float b, float c, float d) {
   return f32x4{a, b, c, d};
 }
 
-// D += A B with both operands given as hi/lo bf16 splits.  An operand that
-// is exact in bf16 (AX / BX: the bf16 input rows k and q) has a zero lo part,
-// so its hi*lo products are skipped -- the same sums, fewer instructions.
-template <bool AX = false, bool BX = false>
-__device__ __forceinline__ f32x4 mma(const Split4& a, const Split4& b, f32x4 d) {
-  if constexpr (!AX) d = mfma16(a.lo, b.hi, d);
-  if constexpr (!BX) d = mfma16(a.hi, b.lo, d);
-  return mfma16(a.hi, b.hi, d);
-}
-__device__ __forceinline__ f32x4 mma3(const Split4& a, const Split4& b, f32x4 d) {
-  return mma<false, false>(a, b, d);
-}
+// The four fp32 values of a fragment, as they are: every product runs on
+// the fp32 matrix unit (exact fp32 products, fp32 accumulation).
+using Frag = f32x4;
 
-// Four fp32 values as an operand: hi/lo split, or hi only when exact in bf16.
-template <bool EXACT>
-__device__ __forceinline__ Split4 frag4(f32x4 x) {
-  if constexpr (EXACT) {
-    Split4 r;
-    r.hi = u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
-    r.lo = u32x2{0u, 0u};
-    return r;
-  } else {
-    return split4(x);
-  }
+// D += A B over 16 k as four 16x16x4 fp32 products.  The j-th takes each
+// lane's own element j (k = 4g + j), so the fragment layout above serves
+// unchanged: the k order differs from the natural one, the sum does not.
+__device__ __forceinline__ f32x4 mma(const Frag& a, const Frag& b, f32x4 d) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) d = __builtin_amdgcn_mfma_f32_16x16x4f32(a[j], b[j], d, 0, 0, 0);
+  return d;
 }
+__device__ __forceinline__ Frag frag(f32x4 x) { return x; }
 
 // Row fragment: X[c][col0 .. col0+3] (A operand of X, or B operand of X^T).
-template <bool EXACT = false>
-__device__ __forceinline__ Split4 row_frag(const float (*X)[LS], int c, int col0) {
+__device__ __forceinline__ Frag row_frag(const float (*X)[LS], int c, int col0) {
   const float4 x = *reinterpret_cast<const float4*>(&X[c][col0]);
-  return frag4<EXACT>(f4(x.x, x.y, x.z, x.w));
+  return f4(x.x, x.y, x.z, x.w);
 }
 
 // Column fragment: X[r0 + i][col] for i = 0..3 (B operand of X, or A
 // operand of X^T).
-template <bool EXACT = false>
-__device__ __forceinline__ Split4 col_frag(const float (*X)[LS], int r0, int col) {
-  return frag4<EXACT>(f4(X[r0][col], X[r0 + 1][col], X[r0 + 2][col], X[r0 + 3][col]));
+__device__ __forceinline__ Frag col_frag(const float (*X)[LS], int r0, int col) {
+  return f4(X[r0][col], X[r0 + 1][col], X[r0 + 2][col], X[r0 + 3][col]);
 }
 
 // Store an accumulator tile D[4g + i][c] at rows 0..15, columns col0 + c.
@@ -245,7 +244,7 @@ struct TileRegs {
   bool ok[RO];
   float vr[RO], dzr[RO], kr[RO], er[RO];
   f32x4 qw, s1, s1t;   // primal waves
-  Split4 Wt[4];        // dual waves
+  Frag Wt[4];        // dual waves
   Inner R;
   float ga[RO], dt[RO];
 };
@@ -291,7 +290,7 @@ __device__ __forceinline__ void inner_grad(const float (&h)[RO], const float (&v
   }
 }
 
-template <bool BF16, bool LN, bool RES>
+template <bool BF16, bool LN, bool RES, bool MB16>
 __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   __shared__ BwdLds L;
   const int unit = blockIdx.x;
@@ -307,6 +306,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   const int col = 16 * cb + c;                              // this lane's product column
   const int T = a.T;
   const int tiles = (T + TB - 1) / TB;
+  const int nmb = MB16 ? 1 : a.tiles_per_mb;   // 16-token tiles per mini-batch
   const size_t row_unit = static_cast<size_t>(unit) * T;   // first token row of the unit
   float* bases = a.ws_base + static_cast<size_t>(unit) * tiles * DD * DD;
   const float* w0 = a.w0 + (a.state0_per_batch ? static_cast<size_t>(unit)
@@ -321,7 +321,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   // ---- phase 1: the bases of every mini-batch ------------------------------
   // Wacc[rt][i] = W[16 rt + 4g + i][col] (updated by the primal waves only;
   // the base stores of the dual waves go to a zero-range resource)
-  f32x4 Wacc[4];
+  f32x4 Wacc[4], Wb[4];   // the state and (several tiles per mini-batch) its base
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -344,6 +344,10 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   for (int ct = 0; ct < tiles && !a.bases_saved; ++ct) {
     const int t0 = ct * TB;
     const int nv = min(TB, T - t0);
+    if (!MB16 && ct % nmb == 0) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) Wb[rt] = Wacc[rt];
+    }
 #pragma unroll
     for (int rt = 0; rt < 4; ++rt)
 #pragma unroll
@@ -361,7 +365,8 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       f32x4 h = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        h = mma<BF16, false>(row_frag<BF16>(L.b[0].k, c, 16 * kt + 4 * g), split4(Wacc[kt]), h);
+        h = mma(row_frag(L.b[0].k, c, 16 * kt + 4 * g),
+                             frag(MB16 ? Wacc[kt] : Wb[kt]), h);
       put_tile(L.b[0].t[0], g, c, 16 * cb, h);
     }
     lds_barrier();
@@ -384,10 +389,10 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     if (primal) {
       // W[:, cols] += K^T (-eta G)[:, cols]; row tile rt of W takes the
       // A operand K^T[16 rt + c][4g + i] = K[4g + i][16 rt + c]
-      const Split4 ug = col_frag(L.b[0].g, 4 * g, col);
+      const Frag ug = col_frag(L.b[0].g, 4 * g, col);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt)
-        Wacc[rt] = mma<BF16, false>(col_frag<BF16>(L.b[0].k, 4 * g, 16 * rt + c), ug, Wacc[rt]);
+        Wacc[rt] = mma(col_frag(L.b[0].k, 4 * g, 16 * rt + c), ug, Wacc[rt]);
     }
     lds_barrier();
   }
@@ -411,7 +416,11 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   // Am: the primal waves' A[16 rt + 4g + i][col], the dual waves'
   // A^T[16 rt + 4g + i][col] = A[col][16 rt + 4g + i]; from dw_final through
   // a buffer resource of zero range when it is NULL (reads return zero)
-  f32x4 Am[4];
+  // Bm: the adjoint of the mini-batch's base from its tiles' gradients so
+  // far (several tiles per mini-batch), folded into Am at its first tile
+  f32x4 Am[4], Bm[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) Bm[rt] = f4(0.f, 0.f, 0.f, 0.f);
   {
     const float* A0 = a.dw_final ? a.dw_final + static_cast<size_t>(unit) * DD * DD : a.w0;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
@@ -436,6 +445,12 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         reinterpret_cast<const float4*>(bases + static_cast<size_t>(ct) * DD * DD);
 #pragma unroll
     for (int m = 0; m < 2; ++m) F.w[m] = base[tid + NW * 64 * m];
+    if (!MB16) {
+      const float4* mb = reinterpret_cast<const float4*>(
+          bases + static_cast<size_t>(ct - ct % nmb) * DD * DD);
+#pragma unroll
+      for (int m = 0; m < 2; ++m) F.wb[m] = mb[tid + NW * 64 * m];
+    }
     F.k = fetch_tile<BF16>(kq, row_unit + t0, nv, tq);
     F.eta = a.eta[row_unit + t0 + min(tid & 15, nv - 1)];
 #pragma unroll
@@ -455,6 +470,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     for (int m = 0; m < 2; ++m) {
       const int e = tid + NW * 64 * m;
       *reinterpret_cast<float4*>(&X.w[e >> 4][4 * (e & 15)]) = F.w[m];
+      if (!MB16) *reinterpret_cast<float4*>(&X.wb[e >> 4][4 * (e & 15)]) = F.wb[m];
     }
     put_fetched<BF16>(tid < 256 ? X.k : X.q, tq, F.k, S.nv);
     if (tid < TB) X.eta[tid] = tid < S.nv ? F.eta : 0.f;
@@ -476,13 +492,13 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       S.s1t = h;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const Split4 wb = col_frag(X.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
-        const Split4 kf = row_frag<BF16>(X.k, c, 16 * kt + 4 * g);
-        const Split4 qf = row_frag<BF16>(X.q, c, 16 * kt + 4 * g);
-        h = mma<BF16, false>(kf, wb, h);
-        S.qw = mma<BF16, false>(qf, wb, S.qw);
-        S.s1 = mma<BF16, BF16>(qf, kf, S.s1);     // s1[i]  = q_{4g+i} . k_c
-        S.s1t = mma<BF16, BF16>(kf, qf, S.s1t);   // s1t[i] = k_{4g+i} . q_c
+        const Frag wb = col_frag(X.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
+        const Frag kf = row_frag(X.k, c, 16 * kt + 4 * g);
+        const Frag qf = row_frag(X.q, c, 16 * kt + 4 * g);
+        h = mma(kf, MB16 ? wb : col_frag(X.wb, 16 * kt + 4 * g, col), h);
+        S.qw = mma(qf, wb, S.qw);
+        S.s1 = mma(qf, kf, S.s1);     // s1[i]  = q_{4g+i} . k_c
+        S.s1t = mma(kf, qf, S.s1t);   // s1t[i] = k_{4g+i} . q_c
       }
       put_tile(X.t[0], g, c, 16 * cb, h);
     } else {
@@ -518,7 +534,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         m[i] = s <= c ? -X.eta[s] * S.s1t[i] : 0.f;
       }
       const f32x4 o =
-          mma3(split4(f4(m[0], m[1], m[2], m[3])), col_frag(X.g, 4 * g, col), S.qw);
+          mma(frag(f4(m[0], m[1], m[2], m[3])), col_frag(X.g, 4 * g, col), S.qw);
       put_tile(X.t[1], g, c, 16 * cb, o);
     }
   };
@@ -568,22 +584,22 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       f32x4 pka = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        pka = mma<BF16, false>(row_frag<BF16>(X.k, c, 16 * kt + 4 * g), split4(Am[kt]), pka);
+        pka = mma(row_frag(X.k, c, 16 * kt + 4 * g), frag(Am[kt]), pka);
       float u1[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) u1[i] = 4 * g + i >= c ? S.s1[i] : 0.f;   // q_s . k_c, s >= c
-      pka = mma3(split4(f4(u1[0], u1[1], u1[2], u1[3])), col_frag(X.dO, 4 * g, col), pka);
+      pka = mma(frag(f4(u1[0], u1[1], u1[2], u1[3])), col_frag(X.dO, 4 * g, col), pka);
       put_tile(X.t[1], g, c, 16 * cb, pka);
     } else {
       f32x4 pdq = f4(0.f, 0.f, 0.f, 0.f), pga = pdq, s2 = pdq, s2t = pdq;
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
-        const Split4 df = row_frag(X.dO, c, 16 * kt + 4 * g);
-        const Split4 gf = row_frag(X.g, c, 16 * kt + 4 * g);
-        pdq = mma3(df, S.Wt[kt], pdq);
-        pga = mma3(gf, split4(Am[kt]), pga);
-        s2 = mma3(df, gf, s2);     // s2[i]  = do_{4g+i} . g_c
-        s2t = mma3(gf, df, s2t);   // s2t[i] = g_{4g+i} . do_c
+        const Frag df = row_frag(X.dO, c, 16 * kt + 4 * g);
+        const Frag gf = row_frag(X.g, c, 16 * kt + 4 * g);
+        pdq = mma(df, S.Wt[kt], pdq);
+        pga = mma(gf, frag(Am[kt]), pga);
+        s2 = mma(df, gf, s2);     // s2[i]  = do_{4g+i} . g_c
+        s2t = mma(gf, df, s2t);   // s2t[i] = g_{4g+i} . do_c
       }
       float m2[4], u2[4];
 #pragma unroll
@@ -592,10 +608,10 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         m2[i] = s <= c ? -X.eta[s] * s2t[i] : 0.f;   // -eta_s (do_c . g_s), s <= c
         u2[i] = s >= c ? s2[i] : 0.f;                // do_s . g_c, s >= c
       }
-      pdq = mma<false, BF16>(split4(f4(m2[0], m2[1], m2[2], m2[3])),
-                             col_frag<BF16>(X.k, 4 * g, col), pdq);
-      pga = mma<false, BF16>(split4(f4(u2[0], u2[1], u2[2], u2[3])),
-                             col_frag<BF16>(X.q, 4 * g, col), pga);
+      pdq = mma(frag(f4(m2[0], m2[1], m2[2], m2[3])),
+                             col_frag(X.k, 4 * g, col), pdq);
+      pga = mma(frag(f4(u2[0], u2[1], u2[2], u2[3])),
+                             col_frag(X.q, 4 * g, col), pga);
       put_tile(X.t[0], g, c, 16 * cb, pdq);
       put_tile(X.t[2], g, c, 16 * cb, pga);
     }
@@ -676,25 +692,42 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   };
   // S7: primal: A += Q^T DO + K^T DH; dual: DH W^T, and A^T += DO^T Q +
   // DH^T K.  The A operand of row tile rt of X^T is X[4g + i][16 rt + c].
+  // With several tiles per mini-batch the output term Q^T DO goes to the
+  // adjoint of the state at the tile's start and the gradient term K^T DH
+  // to that of the mini-batch's base (Bm); the two meet at its first tile.
   auto S7 = [&](TileBuf& X, TileRegs& S) {
     if (primal) {
-      const Split4 dob = col_frag(X.dO, 4 * g, col), dhb = col_frag(X.dh, 4 * g, col);
+      const Frag dob = col_frag(X.dO, 4 * g, col), dhb = col_frag(X.dh, 4 * g, col);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        Am[rt] = mma<BF16, false>(col_frag<BF16>(X.q, 4 * g, 16 * rt + c), dob, Am[rt]);
-        Am[rt] = mma<BF16, false>(col_frag<BF16>(X.k, 4 * g, 16 * rt + c), dhb, Am[rt]);
+        Am[rt] = mma(col_frag(X.q, 4 * g, 16 * rt + c), dob, Am[rt]);
+        if (MB16)
+          Am[rt] = mma(col_frag(X.k, 4 * g, 16 * rt + c), dhb, Am[rt]);
+        else
+          Bm[rt] = mma(col_frag(X.k, 4 * g, 16 * rt + c), dhb, Bm[rt]);
       }
     } else {
       f32x4 pdk = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
-        pdk = mma3(row_frag(X.dh, c, 16 * kt + 4 * g), S.Wt[kt], pdk);
+        pdk = mma(row_frag(X.dh, c, 16 * kt + 4 * g),
+                   MB16 ? S.Wt[kt] : row_frag(X.wb, col, 16 * kt + 4 * g), pdk);
       put_tile(X.t[0], g, c, 16 * cb, pdk);
-      const Split4 qb = col_frag<BF16>(X.q, 4 * g, col), kb = col_frag<BF16>(X.k, 4 * g, col);
+      const Frag qb = col_frag(X.q, 4 * g, col), kb = col_frag(X.k, 4 * g, col);
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
-        Am[rt] = mma<false, BF16>(col_frag(X.dO, 4 * g, 16 * rt + c), qb, Am[rt]);
-        Am[rt] = mma<false, BF16>(col_frag(X.dh, 4 * g, 16 * rt + c), kb, Am[rt]);
+        Am[rt] = mma(col_frag(X.dO, 4 * g, 16 * rt + c), qb, Am[rt]);
+        if (MB16)
+          Am[rt] = mma(col_frag(X.dh, 4 * g, 16 * rt + c), kb, Am[rt]);
+        else
+          Bm[rt] = mma(col_frag(X.dh, 4 * g, 16 * rt + c), kb, Bm[rt]);
+      }
+    }
+    if (!MB16 && (S.t0 / TB) % nmb == 0) {
+#pragma unroll
+      for (int rt = 0; rt < 4; ++rt) {
+        Am[rt] += Bm[rt];
+        Bm[rt] = f4(0.f, 0.f, 0.f, 0.f);
       }
     }
   };
@@ -804,14 +837,20 @@ __global__ __launch_bounds__(256) void ttt_linear_bwd_sum_k(BackwardArgs a) {
   }
 }
 
-template <bool BF16, bool LN>
-hipError_t launch_b2(const BackwardArgs& a, bool res, hipStream_t s) {
+template <bool BF16, bool LN, bool MB16>
+hipError_t launch_b3(const BackwardArgs& a, bool res, hipStream_t s) {
   const dim3 grid(a.B * a.H), block(NW * 64);
   if (res)
-    hipLaunchKernelGGL((ttt_linear_bwd_k<BF16, LN, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_bwd_k<BF16, LN, true, MB16>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((ttt_linear_bwd_k<BF16, LN, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_bwd_k<BF16, LN, false, MB16>), grid, block, 0, s, a);
   return hipGetLastError();
+}
+
+template <bool BF16, bool LN>
+hipError_t launch_b2(const BackwardArgs& a, bool res, hipStream_t s) {
+  return a.tiles_per_mb == 1 ? launch_b3<BF16, LN, true>(a, res, s)
+                             : launch_b3<BF16, LN, false>(a, res, s);
 }
 
 }  // namespace

@@ -430,7 +430,7 @@ ttt_status linear_backward(const ttt_params* p, const void* q, const void* k, co
     return TTT_ERR_NULL;
   if (ln && (!ln_gamma || !ln_beta || !dln_gamma || !dln_beta)) return TTT_ERR_NULL;
   if ((dln_gamma == nullptr) != (dln_beta == nullptr)) return TTT_ERR_NULL;
-  if (p->mini_batch != 16) return TTT_ERR_UNSUPPORTED;
+  if (p->mini_batch % 16 != 0 || (saved && p->mini_batch != 16)) return TTT_ERR_UNSUPPORTED;
   const BackwardLayout ly = backward_layout(p);
   if (workspace_bytes < ly.total) return TTT_ERR_SHAPE;
   if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0) return TTT_ERR_ARG;
@@ -479,6 +479,7 @@ ttt_status linear_backward(const ttt_params* p, const void* q, const void* k, co
   a->B = p->B;
   a->H = p->H;
   a->T = p->T;
+  a->tiles_per_mb = p->mini_batch / 16;
   a->eps = p->ln_eps;
   a->state0_per_batch = p->state0_per_batch;
   a->bases_saved = saved ? 1 : 0;

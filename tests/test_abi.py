@@ -247,7 +247,9 @@ def test_backward_rejects_bad_arguments():
     assert _backward(_params(flags=_lib.TTT_NO_LN), dg=None) == _lib.TTT_ERR_NULL  # pair
     assert _backward(p, ws_bytes=need - 1) == _lib.TTT_ERR_SHAPE
     assert _backward(p, ws=ctypes.c_void_p(BASE + 30 * GAP + 64)) == _lib.TTT_ERR_ARG
-    assert _backward(_params(mini_batch=32)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _backward(_params(mini_batch=24)) == _lib.TTT_ERR_UNSUPPORTED   # not 16 n
+    assert _backward(_params(mini_batch=32, flags=_lib.TTT_BASES_SAVED)) == \
+        _lib.TTT_ERR_UNSUPPORTED                                        # saved: 16 only
     assert _backward(_params(d=32)) == _lib.TTT_ERR_UNSUPPORTED
     assert _backward(_params(T=0)) == _lib.TTT_ERR_SHAPE
     assert _backward(p, dq=_addr(1)) == _lib.TTT_ERR_ALIAS          # dq == q
