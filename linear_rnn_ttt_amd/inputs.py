@@ -30,7 +30,7 @@ from typing import Dict, Optional
 import numpy as np
 
 __all__ = ["Workload", "WORKLOADS", "make_inputs", "bf16_round", "bf16_bits",
-           "unit_slice"]
+           "unit_slice", "InputWorkload", "INPUT_WORKLOADS", "make_input_side"]
 
 
 @dataclasses.dataclass(frozen=True)
@@ -157,3 +157,65 @@ def unit_slice(inp: Dict[str, np.ndarray], units, H: int) -> Dict[str, np.ndarra
     for key in ("gamma", "beta"):
         out[key] = np.ascontiguousarray(inp[key][hs])
     return out
+
+
+# ---- the input side: the layer input x and the projections that make q, k,
+# v and the learning-rate gate from it ----------------------------------------
+#
+# Stand-ins for a trained layer's weights, scaled so that the projections
+# have the statistics of the scan workloads above: x ~ N(0, 1) per feature
+# (the layer input after a normalisation), rows of theta_Q, theta_K, theta_V
+# ~ N(0, 1 / (D d)) so that q, k, v ~ N(0, 1/d), rows of theta_eta
+# ~ N(0, 1/D) and b_eta ~ N(0, 0.1^2) so that the gate's pre-activation is
+# about N(0, 1), and eta_base = 1/d (so eta = sigmoid(.) / d as above).
+# Draw order: x, the q/k/v rows, the eta rows, b_eta; x and the weights are
+# rounded to bf16.
+
+
+@dataclasses.dataclass(frozen=True)
+class InputWorkload:
+    name: str
+    B: int
+    T: int
+    D: int       # model width (the layer input's features)
+    H: int
+    d: int
+    seed: int
+
+    @property
+    def tokens(self) -> int:
+        return self.B * self.T
+
+    @property
+    def n_out(self) -> int:
+        """Rows of the stacked weight: q, k, v of every head, then one eta row per head."""
+        return 3 * self.H * self.d + self.H
+
+    def with_(self, **kw) -> "InputWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+INPUT_WORKLOADS: Dict[str, InputWorkload] = {
+    "input_125m_b8_t2k": InputWorkload("input_125m_b8_t2k", 8, 2048, 768, 12, 64, 6),
+    "input_1p3b_b4_t8k": InputWorkload("input_1p3b_b4_t8k", 4, 8192, 2048, 32, 64, 7),
+}
+
+
+def make_input_side(w: InputWorkload, *, B: Optional[int] = None, T: Optional[int] = None,
+                    D: Optional[int] = None, H: Optional[int] = None) -> Dict[str, np.ndarray]:
+    """Draw x [B,T,D], w_in [3 H d + H, D] (rows: theta_Q of heads 0..H-1,
+    d rows each, then theta_K, theta_V, then the eta row of each head),
+    b_eta [H] and eta_base (a 0-d array).  x and w_in hold bf16 values (as
+    fp32 arrays)."""
+    B = w.B if B is None else B
+    T = w.T if T is None else T
+    D = w.D if D is None else D
+    H = w.H if H is None else H
+    d = w.d
+    rng = np.random.default_rng(w.seed)
+    x = bf16_round(_normal(rng, (B, T, D)))
+    wq = _normal(rng, (3 * H * d, D), 1.0 / np.sqrt(D * d))
+    we = _normal(rng, (H, D), 1.0 / np.sqrt(D))
+    w_in = bf16_round(np.concatenate([wq, we], 0))
+    b_eta = _normal(rng, (H,), 0.1)
+    return {"x": x, "w_in": w_in, "b_eta": b_eta, "eta_base": np.float32(1.0 / d)}
