@@ -62,7 +62,7 @@
 extern "C" {
 #endif
 
-#define TTT_ABI_VERSION 10
+#define TTT_ABI_VERSION 11
 
 typedef enum {
   TTT_OK = 0,
@@ -429,6 +429,44 @@ ttt_status ttt_mlp_backward(const ttt_params* p, int32_t hidden,
                             float* dln_gamma, float* dln_beta,
                             void* workspace, uint64_t workspace_bytes,
                             void* hip_stream);
+
+/*
+ * The input side of a TTT layer: q, k, v of every head and the
+ * token-dependent learning rate eta, made from the layer input x.  The
+ * outer loop trains the projections theta_Q, theta_K, theta_V and a
+ * learning rate that depends on the token (the LIT-801 record, "Key
+ * takeaways" item 2; the nowfound.app launch page, "In the maker's words",
+ * names the QKV projection matrices).  With x [B,T,D] and the stacked
+ * weights w_in [3*H*d + H, D] (rows h*d .. h*d + d-1: theta_Q of head h as
+ * d rows over D; then theta_K and theta_V the same way; then row
+ * 3*H*d + h: the gate of head h):
+ *   q[b,h,t,f] = sum_j x[b,t,j] w_in[h*d + f, j]      (k: row H*d + h*d + f,
+ *                                                     v: row 2*H*d + h*d + f)
+ *   eta[b,h,t] = eta_base / (1 + exp(-(sum_j x[b,t,j] w_in[3*H*d + h, j] + b_eta[h])))
+ * The gate's form is a reading: the pages give none; this one is learned,
+ * depends on the token and keeps eta in (0, eta_base).
+ *   p        B, H, T, d of the scan that consumes the outputs (checked as
+ *            for the scan; mini_batch, flags and ln_eps are not used);
+ *            io_dtype TTT_BF16 and d = 64, else TTT_ERR_UNSUPPORTED.
+ *   d_model  D: a positive multiple of 64 (else TTT_ERR_UNSUPPORTED).
+ *   x        [B,T,D] bf16, 16-byte aligned (else TTT_ERR_ARG).
+ *   w_in     [3*H*d + H, D] bf16, 16-byte aligned (else TTT_ERR_ARG).
+ *   b_eta    [H] fp32.
+ *   eta_base finite and > 0 (else TTT_ERR_ARG).
+ *   q, k, v  [B,H,T,d] bf16 (out), 16-byte aligned (else TTT_ERR_ARG): the
+ *            scan's input layout, each rounded once (to nearest even) from
+ *            an fp32 accumulation over D.
+ *   eta      [B,H,T] fp32 (out).
+ * B*T at most 2^30 (else TTT_ERR_SHAPE).  Outputs overlap no input and no
+ * other output (TTT_ERR_ALIAS).
+ * gfx950: one kernel on hip_stream: bf16 matrix-unit products (16x16x32,
+ * fp32 accumulation), a 256 x 128 output tile per 512-thread workgroup.
+ */
+ttt_status ttt_input_projection(const ttt_params* p, int32_t d_model,
+                                const void* x, const void* w_in,
+                                const float* b_eta, float eta_base,
+                                void* q, void* k, void* v, float* eta,
+                                void* hip_stream);
 
 /* TTT_ABI_VERSION of the built library. */
 int32_t ttt_abi_version(void);

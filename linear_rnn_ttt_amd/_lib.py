@@ -22,7 +22,8 @@ EXPORTS = ("ttt_linear_forward", "ttt_linear_split_workspace_bytes", "ttt_linear
            "ttt_linear_backward_workspace_bytes", "ttt_linear_backward",
            "ttt_mlp_backward_workspace_bytes", "ttt_mlp_backward",
            "ttt_mlp_forward", "ttt_mlp_decode_step",
-           "ttt_mlp_decode_step_compact", "ttt_status_string", "ttt_abi_version")
+           "ttt_mlp_decode_step_compact", "ttt_input_projection", "ttt_status_string",
+           "ttt_abi_version")
 
 
 class TTTParams(ctypes.Structure):
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
     L.ttt_mlp_backward.restype = ctypes.c_int
     L.ttt_mlp_forward.argtypes = [ctypes.POINTER(TTTParams), ctypes.c_int32] + [P] * 16
     L.ttt_mlp_forward.restype = ctypes.c_int
+    L.ttt_input_projection.argtypes = ([ctypes.POINTER(TTTParams), ctypes.c_int32, P, P, P,
+                                        ctypes.c_float] + [P] * 5)
+    L.ttt_input_projection.restype = ctypes.c_int
     L.ttt_status_string.argtypes = [ctypes.c_int]
     L.ttt_status_string.restype = ctypes.c_char_p
     L.ttt_abi_version.argtypes = []

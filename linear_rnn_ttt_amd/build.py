@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libttt_amd.so")
 SOURCES = ["ttt_api.cpp", "ttt_validate.cpp", "ttt_linear.hip", "ttt_mlp.hip", "ttt_decode.hip", "ttt_decode_compact.hip", "ttt_backward.hip",
            "ttt_mlp_decode.hip",
-           "ttt_mlp_decode_compact.hip", "ttt_mlp_backward.hip"]
+           "ttt_mlp_decode_compact.hip", "ttt_mlp_backward.hip", "ttt_input.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 # Packed fp32 VALU instructions are disabled on purpose: the kernels are

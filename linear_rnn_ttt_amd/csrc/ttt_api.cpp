@@ -9,6 +9,7 @@
 #include <cstdint>
 
 #include "ttt_backward.hpp"
+#include "ttt_input.hpp"
 #include "ttt_kernels.hpp"
 #include "ttt_mlp_backward.hpp"
 #include "ttt_mlp_compact.hpp"
@@ -234,6 +235,16 @@ ttt_status ttt_mlp_backward(const ttt_params* p, int32_t hidden, const void* q, 
   if (st != TTT_OK) return st;
   return status_of(tttk::launch_mlp_backward(a, bf16_of(p), ln_of(p), res_of(p),
                                              static_cast<hipStream_t>(hip_stream)));
+}
+
+ttt_status ttt_input_projection(const ttt_params* p, int32_t d_model, const void* x,
+                                const void* w_in, const float* b_eta, float eta_base, void* q,
+                                void* k, void* v, float* eta, void* hip_stream) {
+  tttk::InputArgs a;
+  const ttt_status st =
+      tttv::input_projection(p, d_model, x, w_in, b_eta, eta_base, q, k, v, eta, &a);
+  if (st != TTT_OK) return st;
+  return status_of(tttk::launch_input(a, static_cast<hipStream_t>(hip_stream)));
 }
 
 }  // extern "C"

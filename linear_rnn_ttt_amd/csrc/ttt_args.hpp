@@ -199,4 +199,19 @@ struct MlpBackwardArgs {
 constexpr uint64_t MLP_BWD_STATE_FLOATS = 64 * 256 + 256 + 256 * 64 + 64;
 constexpr uint64_t MLP_BWD_TILE_FLOATS = 8 * 16 * 256 + 12 * 16 * 64 + 2 * 64;
 
+// The input side (ttt_input_projection): Y = x W_in^T, then per column the
+// q/k/v store or the learning-rate gate.
+struct InputArgs {
+  const void* x;          // [M = B T, D] bf16
+  const void* w;          // [N = 3 H 64 + H, D] bf16
+  const float* b_eta;     // [H]
+  void* q;                // [B, H, T, 64] bf16
+  void* k;
+  void* v;
+  float* eta;             // [B, H, T]
+  int32_t B, T, D, H;
+  float eta_base;
+};
+
 }  // namespace tttk
+

@@ -654,4 +654,46 @@ ttt_status mlp_backward(const ttt_params* p, int32_t hidden, const void* q, cons
   return TTT_OK;
 }
 
+ttt_status input_projection(const ttt_params* p, int32_t d_model, const void* x,
+                            const void* w_in, const float* b_eta, float eta_base, void* q,
+                            void* k, void* v, float* eta, tttk::InputArgs* a) {
+  uint64_t elems = 0;
+  const ttt_status st = check_common(p, &elems);
+  if (st != TTT_OK) return st;
+  if (!x || !w_in || !b_eta || !q || !k || !v || !eta) return TTT_ERR_NULL;
+  if (d_model < 1) return TTT_ERR_SHAPE;
+  if (p->io_dtype != TTT_BF16 || d_model % 64 != 0) return TTT_ERR_UNSUPPORTED;
+  if (!(eta_base > 0.0f) || !std::isfinite(eta_base)) return TTT_ERR_ARG;
+  for (const void* ptr : {x, w_in, static_cast<const void*>(q), static_cast<const void*>(k),
+                          static_cast<const void*>(v)})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0) return TTT_ERR_ARG;
+  const uint64_t tokens = static_cast<uint64_t>(p->B) * p->T;
+  if (tokens > (1ull << 30)) return TTT_ERR_SHAPE;   // the kernel indexes rows with int
+  const uint64_t n_out = 3ull * p->H * kHeadDim + p->H;
+  const Range inputs[] = {span(x, tokens * d_model * 2), span(w_in, n_out * d_model * 2),
+                          span(b_eta, p->H * 4ull)};
+  const Range outputs[] = {span(q, elems * 2), span(k, elems * 2), span(v, elems * 2),
+                           span(eta, tokens * p->H * 4ull)};
+  const int n_o = sizeof(outputs) / sizeof(outputs[0]);
+  for (int i = 0; i < n_o; ++i) {
+    for (const Range& r : inputs)
+      if (overlap(outputs[i], r)) return TTT_ERR_ALIAS;
+    for (int j2 = i + 1; j2 < n_o; ++j2)
+      if (overlap(outputs[i], outputs[j2])) return TTT_ERR_ALIAS;
+  }
+  a->x = x;
+  a->w = w_in;
+  a->b_eta = b_eta;
+  a->q = q;
+  a->k = k;
+  a->v = v;
+  a->eta = eta;
+  a->B = p->B;
+  a->T = p->T;
+  a->D = d_model;
+  a->H = p->H;
+  a->eta_base = eta_base;
+  return TTT_OK;
+}
+
 }  // namespace tttv

@@ -122,4 +122,9 @@ ttt_status mlp_backward(const ttt_params* p, int32_t hidden, const void* q, cons
                         float* dw2, float* db2, float* dln_gamma, float* dln_beta,
                         void* workspace, uint64_t workspace_bytes, tttk::MlpBackwardArgs* a);
 
+// ttt_input_projection.
+ttt_status input_projection(const ttt_params* p, int32_t d_model, const void* x,
+                            const void* w_in, const float* b_eta, float eta_base, void* q,
+                            void* k, void* v, float* eta, tttk::InputArgs* a);
+
 }  // namespace tttv

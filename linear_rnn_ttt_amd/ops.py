@@ -15,7 +15,8 @@ from . import _lib
 
 __all__ = ["ttt_linear_forward", "ttt_linear_forward_split_noalloc", "ttt_linear_decode_step",
            "ttt_linear_decode_step_compact", "ttt_linear_backward", "ttt_mlp_forward",
-           "ttt_mlp_backward"]
+           "ttt_mlp_backward", "ttt_mlp_decode_step", "ttt_mlp_decode_step_compact",
+           "ttt_input_projection"]
 
 HEAD_DIM = 64
 
@@ -511,3 +512,37 @@ def ttt_mlp_forward(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, eta: torc
                                         *[_ptr(t) for t in outs], _stream(q, stream))
     _lib.check("ttt_mlp_forward", rc)
     return z, state_out
+
+
+def ttt_input_projection(x: torch.Tensor, w_in: torch.Tensor, b_eta: torch.Tensor, *,
+                         heads: int, eta_base: float, head_dim: int = 64,
+                         out=None, stream=None) -> Tuple[torch.Tensor, ...]:
+    """The input side of a TTT layer on the GPU: from x [B,T,D] (bf16) and
+    the stacked weights w_in [3*H*d + H, D] (bf16; theta_Q, theta_K, theta_V
+    rows of every head, then one gate row per head) and b_eta [H] (fp32),
+    returns (q, k, v, eta): q, k, v [B,H,T,d] bf16 in the scan's layout and
+    eta = eta_base * sigmoid(x . w_gate + b_eta) [B,H,T] fp32.  out: an
+    optional tuple of four tensors to write instead.  See include/ttt.h."""
+    _dev_tensor("x", x, torch.bfloat16)
+    if x.dim() != 3:
+        raise ValueError("x must be [B, T, D]")
+    B, T, D = x.shape
+    H, d = int(heads), int(head_dim)
+    dev = x.device
+    _dev_tensor("w_in", w_in, torch.bfloat16, (3 * H * d + H, D), device=dev)
+    _dev_tensor("b_eta", b_eta, torch.float32, (H,), device=dev)
+    if out is None:
+        q, k, v = (torch.empty((B, H, T, d), dtype=torch.bfloat16, device=dev) for _ in range(3))
+        eta = torch.empty((B, H, T), dtype=torch.float32, device=dev)
+    else:
+        q, k, v, eta = out
+        for name, t in (("q", q), ("k", k), ("v", v)):
+            _dev_tensor(name, t, torch.bfloat16, (B, H, T, d), device=dev)
+        _dev_tensor("eta", eta, torch.float32, (B, H, T), device=dev)
+    p = _lib.TTTParams(B, H, T, d, 16, _lib.TTT_BF16, 0, 1e-6, 0)
+    with torch.cuda.device(dev):
+        rc = _lib.lib().ttt_input_projection(
+            ctypes.byref(p), D, _ptr(x), _ptr(w_in), _ptr(b_eta), float(eta_base), _ptr(q),
+            _ptr(k), _ptr(v), _ptr(eta), _stream(x, stream))
+    _lib.check("ttt_input_projection", rc)
+    return q, k, v, eta

@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     L = _lib.lib()
     for name in _declared_functions():
         assert hasattr(L, name), name
-    assert _lib.abi_version() == 10
+    assert _lib.abi_version() == 11
     for code in range(8):
         assert _lib.status_string(code)
     assert "unknown" in _lib.status_string(99)
@@ -356,3 +356,31 @@ def test_mlp_compact_step_rejects_bad_arguments():
     assert _mlp_compact(p, hist=_addr(5)) == _lib.TTT_ERR_ALIAS             # hist == w1 base
     assert _mlp_compact(p, z=_addr(1)) == _lib.TTT_ERR_ALIAS                # z == q
     assert _mlp_compact(p, b2b=_addr(4)) == _lib.TTT_ERR_ALIAS              # b2 base == eta
+
+
+def _input(p, d_model=128, eta_base=0.01, **ptrs):
+    names = ["x", "w", "b", "q", "k", "v", "eta"]
+    args = [ptrs.get(n, _addr(i + 1)) for i, n in enumerate(names)]
+    return _lib.lib().ttt_input_projection(ctypes.byref(p) if p is not None else None,
+                                           d_model, args[0], args[1], args[2],
+                                           ctypes.c_float(eta_base), *args[3:], None)
+
+
+def test_input_projection_rejects_bad_arguments():
+    p = _params()
+    assert _input(None) == _lib.TTT_ERR_NULL
+    for name in ["x", "w", "b", "q", "k", "v", "eta"]:
+        assert _input(p, **{name: None}) == _lib.TTT_ERR_NULL, name
+    assert _input(_params(io_dtype=_lib.TTT_F32)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _input(p, d_model=100) == _lib.TTT_ERR_UNSUPPORTED      # not a multiple of 64
+    assert _input(p, d_model=0) == _lib.TTT_ERR_SHAPE
+    assert _input(_params(d=32)) == _lib.TTT_ERR_UNSUPPORTED
+    assert _input(_params(B=1 << 12, T=1 << 19)) == _lib.TTT_ERR_SHAPE   # B*T > 2^30
+    assert _input(p, eta_base=0.0) == _lib.TTT_ERR_ARG
+    assert _input(p, eta_base=float("nan")) == _lib.TTT_ERR_ARG
+    assert _input(p, x=ctypes.c_void_p(BASE + GAP + 8)) == _lib.TTT_ERR_ARG   # misaligned
+    assert _input(p, w=ctypes.c_void_p(BASE + 2 * GAP + 2)) == _lib.TTT_ERR_ARG
+    assert _input(p, k=ctypes.c_void_p(BASE + 5 * GAP + 4)) == _lib.TTT_ERR_ARG
+    assert _input(p, q=_addr(1)) == _lib.TTT_ERR_ALIAS        # q == x
+    assert _input(p, eta=_addr(2)) == _lib.TTT_ERR_ALIAS      # eta == w_in
+    assert _input(p, v=_addr(5)) == _lib.TTT_ERR_ALIAS        # v == k
