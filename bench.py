@@ -16,7 +16,11 @@ roofline of the scan kernel (algorithmic bytes or flops per launch over the
 launch time measured with HIP events on the launch stream) and the fp64 CPU
 oracle timed on the host cores.
 
-Other modes (turn rocprofv3 output into the short summaries kept under
+Other timed modes: --backward (the scan's backward pass, --train with the
+forward that saves the bases), --decode [--compact] (the streaming step),
+--input (the input side: q, k, v projections and the learning-rate gate).
+
+Summary modes (turn rocprofv3 output into the short summaries kept under
 profiles/):
   --summarize-trace DIR                 a `rocprofv3 --kernel-trace --stats`
       run of this benchmark: per-kernel average durations;
@@ -55,16 +59,20 @@ KERNEL_SOURCES = {
                            "ttt_device.hpp", "ttt_args.hpp"],
     "mlp_backward": ["ttt_mlp_backward.hip", "ttt_mlp_backward.hpp", "ttt_args.hpp",
                      "ttt_device.hpp"],
+    "input": ["ttt_input.hip", "ttt_input.hpp", "ttt_args.hpp", "ttt_device.hpp"],
 }
 KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k",
                "backward": "ttt_linear_bwd_k", "decode_compact": "ttt_linear_decode_compact_k",
                "mlp_decode": "ttt_mlp_decode_k",
                "mlp_decode_compact": "ttt_mlp_decode_compact_k",
-               "mlp_backward": "ttt_mlp_bwd_k"}
+               "mlp_backward": "ttt_mlp_bwd_k", "input": "ttt_input_k"}
 BACKWARD_METRIC = "TTT-Linear backward tokens/s at 1.3B shape T=8k; % fp32 MFMA roofline"
 TRAIN_METRIC = ("TTT-Linear training step (forward saving the bases + backward) tokens/s at "
                 "1.3B shape T=8k; % fp32 MFMA roofline of the backward")
 MLP_BACKWARD_METRIC = "TTT-MLP backward tokens/s at 125M shape T=2k; % fp32 MFMA roofline"
+INPUT_METRIC = ("TTT input side (q, k, v projections and the eta gate) tokens/s; "
+                "% bf16 MFMA roofline")
+DEFAULT_INPUT_WORKLOAD = "input_1p3b_b4_t8k"
 # MI355X dense fp32 matrix (MFMA) rate: the roof of fp32-precision
 # contractions; both backward kernels run their products on it.
 FP32_MFMA_PEAK_TFS = 157.3
@@ -802,6 +810,121 @@ def run_mlp_backward(args, w) -> dict:
     return res
 
 
+def input_workload(args):
+    from linear_rnn_ttt_amd.inputs import INPUT_WORKLOADS
+
+    name = args.workload if args.workload in INPUT_WORKLOADS else DEFAULT_INPUT_WORKLOAD
+    return INPUT_WORKLOADS[name]
+
+
+def input_alg(w) -> dict:
+    """Algorithmic work of one input-side launch: flops 2 M D N (M = B T
+    tokens, N = 3 H d + H output columns); bytes: x and the stacked weights
+    read once (bf16), b_eta, q, k, v written (bf16) and eta (fp32)."""
+    M, N = w.B * w.T, w.n_out
+    flops = 2 * M * w.D * N
+    bytes_ = M * w.D * 2 + N * w.D * 2 + w.H * 4 + 3 * M * w.H * w.d * 2 + M * w.H * 4
+    return {"flops": flops, "bytes": bytes_, "flops_per_token": 2 * w.D * N}
+
+
+def run_input(args) -> dict:
+    import numpy as np
+    import torch
+
+    from linear_rnn_ttt_amd import ttt_input_projection
+    from linear_rnn_ttt_amd.inputs import make_input_side
+
+    w = input_workload(args)
+    inp = make_input_side(w)
+    x = torch.from_numpy(inp["x"]).cuda().to(torch.bfloat16)
+    wi = torch.from_numpy(inp["w_in"]).cuda().to(torch.bfloat16)
+    be = torch.from_numpy(inp["b_eta"]).cuda()
+    eb = float(inp["eta_base"])
+    out = ttt_input_projection(x, wi, be, heads=w.H, eta_base=eb, head_dim=w.d)
+    stream = torch.cuda.current_stream()
+
+    def step(s_=None, e_=None):
+        if s_ is not None:
+            s_.record(stream)
+        ttt_input_projection(x, wi, be, heads=w.H, eta_base=eb, head_dim=w.d, out=out)
+        if e_ is not None:
+            e_.record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    if args.copy_calibration:
+        copy_calibration()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s_, e_ in ev:
+        step(s_, e_)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    avg_launch_s = sum(s_.elapsed_time(e_) for s_, e_ in ev) / len(ev) / 1e3
+    ms_per_step = wall / args.steps * 1e3
+    alg = input_alg(w)
+    tflops = alg["flops"] / avg_launch_s / 1e12
+    res = {
+        "metric": INPUT_METRIC,
+        "value": round(w.tokens / (ms_per_step / 1e3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",   # bf16 matrix-unit products, fp32 accumulation
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "d_model": w.D, "H": w.H,
+                   "d": w.d, "n_out": w.n_out, "parallelism": "none (1 GPU)",
+                   "launch": "ttt_input_projection: one 512-thread workgroup per 256 x 128 "
+                             "output tile, bf16 16x16x32 matrix-unit products"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
+                     "peak": BF16_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_MFMA_PEAK_TFS, 5),
+                     "traffic": read_traffic("input", w.name),
+                     "kernel": KERNEL_NAME["input"],
+                     "avg_launch_ms": round(avg_launch_s * 1e3, 4),
+                     "algorithmic_flops_per_launch": alg["flops"],
+                     "algorithmic_bytes_per_launch": alg["bytes"],
+                     "hbm_gbs_algorithmic": round(alg["bytes"] / avg_launch_s / 1e9, 1)},
+        "outputs_finite": bool(all(torch.isfinite(t.float()).all().item() for t in out)),
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline_input(w, inp, args.cpu_budget)
+    return res
+
+
+def cpu_baseline_input(w, inp, budget_s: float):
+    """The fp64 input-side oracle on the first n tokens of batch entry 0, n
+    doubled from 64 until a run takes a quarter of the budget; tokens/s."""
+    from oracle.input_side import input_side
+
+    n, dt = 32, 0.0
+    while dt < budget_s / 4 and n < w.T:
+        n *= 2
+        t0 = time.perf_counter()
+        input_side(inp["x"][:1, :n], inp["w_in"], inp["b_eta"], w.H, w.d, inp["eta_base"])
+        dt = time.perf_counter() - t0
+    return {"value": round(n / dt, 1), "unit": "tokens/s", "cores": _blas_threads(),
+            "kind": "oracle",
+            "sample": "batch entry 0, first %d tokens, %.2f s wall, fp64 numpy" % (n, dt)}
+
+
+def _blas_threads() -> int:
+    """Threads the fp64 matrix products may use (the BLAS pool; numpy does
+    not report it, so the OpenMP / BLAS environment or the core count)."""
+    for var in ("OPENBLAS_NUM_THREADS", "OMP_NUM_THREADS", "MKL_NUM_THREADS"):
+        if os.environ.get(var, "").isdigit():
+            return int(os.environ[var])
+    return os.cpu_count() or 1
+
+
 def cpu_baseline_mlp_backward(w, inp, dz, budget_s: float):
     """The fp64 TTT-MLP backward oracle on one unit (batch 0, head 0) for the
     first T_s tokens, T_s doubled from 64 until a run takes a quarter of the
@@ -896,9 +1019,9 @@ def summarize_pipes(d, args, cmd, workgroups: int):
         "- kernel_source_sha256: `%s`" % kernel_hash(kind),
         "- counters (mean per dispatch): " + ", ".join(
             "%s %.4g" % (k, v) for k, v in vals.items()),
-        "- workgroups per launch: %d (one per CU)" % workgroups,
-        "- busy cycles per CU: %.4g (SQ_BUSY_CU_CYCLES / workgroups); GRBM_GUI_ACTIVE / 8 "
-        "XCDs: %.4g" % (per_cu, vals["GRBM_GUI_ACTIVE"] / 8), "",
+        "- workgroups per launch: %d" % workgroups,
+        "- busy CU cycles per workgroup: %.4g (SQ_BUSY_CU_CYCLES / workgroups); "
+        "GRBM_GUI_ACTIVE / 8 XCDs: %.4g" % (per_cu, vals["GRBM_GUI_ACTIVE"] / 8), "",
         "| pipe, per busy CU | fraction of cycles |", "|---|---|",
         "| VALU issuing (SQ_ACTIVE_INST_VALU) | %.1f %% |" % (
             100 * vals["SQ_ACTIVE_INST_VALU"] / busy),
@@ -926,6 +1049,10 @@ def _profiled(args):
                     decode_compact_bytes(w), decode_flops(w))
         return ("mlp_decode" if w.kind == "mlp" else "decode", decode_tag(w), decode_bytes(w),
                 decode_flops(w))
+    if args.input:
+        w = input_workload(args)
+        alg = input_alg(w)
+        return "input", w.name, alg["bytes"], alg["flops"]
     if args.backward:
         w = WORKLOADS[args.workload]
         if w.kind == "mlp":
@@ -1021,6 +1148,9 @@ def main(argv=None):
                     help="with --decode: the compact pending state (base + mini-batch rows)")
     ap.add_argument("--train", action="store_true",
                     help="with --backward: time forward (saving the bases) + backward")
+    ap.add_argument("--input", action="store_true",
+                    help="time the input side (ttt_input_projection) on --workload "
+                         "input_1p3b_b4_t8k (default) or input_125m_b8_t2k")
     ap.add_argument("--batch", type=int, default=0,
                     help="streams for --decode (default: the workload's batch)")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"))
@@ -1050,7 +1180,8 @@ def main(argv=None):
         print("bench.py: --steps must be >= 1 and --warmup >= 0", file=sys.stderr)
         return 2
     out = (run_decode(args) if args.decode else
-           run_backward(args) if args.backward else run(args))
+           run_backward(args) if args.backward else
+           run_input(args) if args.input else run(args))
     print(json.dumps(out), flush=True)
     return 0
 
