@@ -490,6 +490,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       S.qw = h;
       S.s1 = h;
       S.s1t = h;
+      u32x2 qb[4], kb[4];   // bf16 data: the rows as bf16 (exact) for the Grams
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt) {
         const Frag wb = col_frag(X.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
@@ -497,8 +498,22 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         const Frag qf = row_frag(X.q, c, 16 * kt + 4 * g);
         h = mma(kf, MB16 ? wb : col_frag(X.wb, 16 * kt + 4 * g, col), h);
         S.qw = mma(qf, wb, S.qw);
-        S.s1 = mma(qf, kf, S.s1);     // s1[i]  = q_{4g+i} . k_c
-        S.s1t = mma(kf, qf, S.s1t);   // s1t[i] = k_{4g+i} . q_c
+        if constexpr (BF16) {
+          qb[kt] = u32x2{pack_bf16(qf[0], qf[1]), pack_bf16(qf[2], qf[3])};
+          kb[kt] = u32x2{pack_bf16(kf[0], kf[1]), pack_bf16(kf[2], kf[3])};
+        } else {
+          S.s1 = mma(qf, kf, S.s1);     // s1[i]  = q_{4g+i} . k_c
+          S.s1t = mma(kf, qf, S.s1t);   // s1t[i] = k_{4g+i} . q_c
+        }
+      }
+      if constexpr (BF16) {
+        // the same Grams from the exact bf16 rows: two 16x16x32 products each
+        // (bf16 x bf16 products are exact in fp32) instead of 32 fp32 ones
+#pragma unroll
+        for (int kp = 0; kp < 4; kp += 2) {
+          S.s1 = mfma32(cat(qb[kp], qb[kp + 1]), cat(kb[kp], kb[kp + 1]), S.s1);
+          S.s1t = mfma32(cat(kb[kp], kb[kp + 1]), cat(qb[kp], qb[kp + 1]), S.s1t);
+        }
       }
       put_tile(X.t[0], g, c, 16 * cb, h);
     } else {

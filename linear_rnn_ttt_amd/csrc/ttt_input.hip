@@ -36,14 +36,16 @@
 #include "ttt_device.hpp"
 #include "ttt_input.hpp"
 
+#define TTT_LDS __attribute__((address_space(3)))
+
 namespace tttk {
 namespace {
 
 constexpr int BM = 256, BN = 128, BK = 64, NT = 512, LDK = BK, HD = 64, XCDS = 8;
 
 struct InLds {
-  uint16_t a[2][BM][LDK];
-  uint16_t b[2][BN][LDK];
+  uint16_t a[3][BM][LDK];
+  uint16_t b[3][BN][LDK];
 };
 
 __device__ __forceinline__ float sigmoid(float y) { return 1.0f / (1.0f + expf(-y)); }
@@ -61,38 +63,38 @@ __global__ __launch_bounds__(NT) void ttt_input_k(InputArgs a) {
   const int g = lane >> 4, c = lane & 15;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // this thread's 16-byte pieces of a step: x rows lr + 64 j (j < 4) and
-  // W_in rows lr + 64 j (j < 2), k offset lk within the step
-  const int lr = tid >> 3, lk = (tid & 7) * 8;
+  // Copies go straight from memory into LDS (global_load_lds: no registers).
+  // One wave instruction moves 1 KB: 8 rows of 128 bytes, lane l landing at
+  // byte 16 l -- row l / 8, chunk l % 8 of the block -- so each lane fetches
+  // the source chunk that belongs in that (swizzled) slot.  Per step the x
+  // tile is 32 such blocks and the W_in tile 16; wave w copies x blocks
+  // w + 8 j (j < 4) and W_in blocks w + 8 j (j < 2).
+  const int cr = lane >> 3, cq = lane & 7;
   const uint16_t* xg = static_cast<const uint16_t*>(a.x);
   const uint16_t* wg = static_cast<const uint16_t*>(a.w);
   const uint16_t* pa[4];
   const uint16_t* pb[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    pa[j] = xg + static_cast<size_t>(min(m0 + lr + 64 * j, M - 1)) * D + lk;
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * (wave + 8 * j) + cr;   // row of the x tile
+    pa[j] = xg + static_cast<size_t>(min(m0 + r, M - 1)) * D + 8 * (cq ^ (r & 7));
+  }
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-    pb[j] = wg + static_cast<size_t>(min(n0 + lr + 64 * j, N - 1)) * D + lk;
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * (wave + 8 * j) + cr;   // row of the W_in tile
+    pb[j] = wg + static_cast<size_t>(min(n0 + r, N - 1)) * D + 8 * (cq ^ (r & 7));
+  }
   const int steps = D / BK;
-  // two register sets of staged pieces: a step's tiles are loaded two steps
-  // before they are written to LDS, so a load has two steps of products to
-  // arrive in (one step is shorter than a memory round trip)
-  struct Stage {
-    u32x4 a[4], b[2];
-  };
-  auto gload = [&](Stage& r, int step) {
+  auto issue = [&](int buf, int step) {
     const int k0 = min(step, steps - 1) * BK;   // past the end: the last step again
 #pragma unroll
-    for (int j = 0; j < 4; ++j) r.a[j] = *reinterpret_cast<const u32x4*>(pa[j] + k0);
+    for (int j = 0; j < 4; ++j)
+      __builtin_amdgcn_global_load_lds(pa[j] + k0, (TTT_LDS void*)&L.a[buf][8 * (wave + 8 * j)][0],
+                                       16, 0, 0);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) r.b[j] = *reinterpret_cast<const u32x4*>(pb[j] + k0);
-  };
-  auto lstore = [&](int buf, const Stage& r) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) *reinterpret_cast<u32x4*>(&L.a[buf][lr + 64 * j][lk ^ ((lr & 7) << 3)]) = r.a[j];
-#pragma unroll
-    for (int j = 0; j < 2; ++j) *reinterpret_cast<u32x4*>(&L.b[buf][lr + 64 * j][lk ^ ((lr & 7) << 3)]) = r.b[j];
+    for (int j = 0; j < 2; ++j)
+      __builtin_amdgcn_global_load_lds(pb[j] + k0, (TTT_LDS void*)&L.b[buf][8 * (wave + 8 * j)][0],
+                                       16, 0, 0);
   };
 
   f32x4 acc[4][4];
@@ -106,10 +108,12 @@ __global__ __launch_bounds__(NT) void ttt_input_k(InputArgs a) {
       u32x4 af[4], bf[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        af[i] = *reinterpret_cast<const u32x4*>(&L.a[buf][64 * wm + 16 * i + c][(32 * kk + 8 * g) ^ ((c & 7) << 3)]);
+        af[i] = *reinterpret_cast<const u32x4*>(
+            &L.a[buf][64 * wm + 16 * i + c][(32 * kk + 8 * g) ^ ((c & 7) << 3)]);
 #pragma unroll
       for (int j = 0; j < 4; ++j)
-        bf[j] = *reinterpret_cast<const u32x4*>(&L.b[buf][64 * wn + 16 * j + c][(32 * kk + 8 * g) ^ ((c & 7) << 3)]);
+        bf[j] = *reinterpret_cast<const u32x4*>(
+            &L.b[buf][64 * wn + 16 * j + c][(32 * kk + 8 * g) ^ ((c & 7) << 3)]);
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -117,25 +121,27 @@ __global__ __launch_bounds__(NT) void ttt_input_k(InputArgs a) {
     }
   };
 
-  // step s: multiply LDS buffer s % 2; write step s + 1 (loaded at step
-  // s - 1) to the other buffer; load step s + 3 into the freed set.  Two
-  // steps per iteration so the register sets are named statically.
-  Stage r0, r1;
-  gload(r0, 0);
-  gload(r1, 1);
-  lstore(0, r0);
-  gload(r0, 2);
-  lds_barrier();
-  for (int s = 0; s < steps; s += 2) {
-    compute(0);
-    lstore(1, r1);
-    gload(r1, s + 3);
-    lds_barrier();
-    if (s + 1 < steps) compute(1);
-    lstore(0, r0);
-    gload(r0, s + 4);
-    lds_barrier();
+  // Three LDS buffers: at step s the products read buffer s % 3 while the
+  // copies of step s + 1 (issued a step ago) land and those of step s + 2 are
+  // issued into the third.  Before the step's barrier each wave waits for its
+  // own copies of step s + 1 only (six instructions issued after them may
+  // still be in flight): the barrier's usual LDS fence would wait for all.
+  issue(0, 0);
+  issue(1, 1);
+  asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+  lds_barrier_copies_in_flight();
+  int cur = 0;
+  for (int s = 0; s < steps; ++s) {
+    compute(cur);
+    issue(cur == 0 ? 2 : cur - 1, s + 2);   // buffer (s + 2) % 3
+    asm volatile("s_waitcnt vmcnt(6)" ::: "memory");
+    lds_barrier_copies_in_flight();
+    cur = cur == 2 ? 0 : cur + 1;
   }
+  // the last copies (repeats of the last step) must land before the LDS is
+  // reused below
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  lds_barrier_copies_in_flight();
 
   // epilogue: accumulator (i, j) holds Y[m0 + 64 wm + 16 i + 4 g + r][n0 + 64 wn + 16 j + c].
   // A wave's 64 columns are one head of q, k or v (3 H 64 is a multiple of
