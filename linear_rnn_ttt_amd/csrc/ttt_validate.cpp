@@ -7,6 +7,7 @@
 
 #include <cmath>
 #include <cstdint>
+#include <initializer_list>
 
 namespace tttv {
 namespace {

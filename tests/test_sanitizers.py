@@ -179,6 +179,49 @@ int main() {
                                  A(9), A(10), A(11), F(12), F(13), F(14), F(15), A(20), bw, &a),
            TTT_OK);
     if (a.bases_saved != 1) ++fails;
+    ttt_params mb32 = P(2, 3, 100, 64, 32, TTT_BF16, 0);
+    EXPECT(tttv::linear_backward(&mb32, A(1), A(2), A(3), F(4), F(5), F(6), F(7), A(8), nullptr,
+                                 A(9), A(10), A(11), F(12), F(13), F(14), F(15), A(20), bw, &a),
+           TTT_OK);
+    if (a.tiles_per_mb != 2) ++fails;
+    ttt_params mb24 = P(2, 3, 100, 64, 24, TTT_BF16, 0);
+    EXPECT(tttv::linear_backward(&mb24, A(1), A(2), A(3), F(4), F(5), F(6), F(7), A(8), nullptr,
+                                 A(9), A(10), A(11), F(12), F(13), F(14), F(15), A(20), bw, &a),
+           TTT_ERR_UNSUPPORTED);
+    ttt_params saved32 = P(2, 3, 100, 64, 32, TTT_BF16, TTT_BASES_SAVED);
+    EXPECT(tttv::linear_backward(&saved32, A(1), A(2), A(3), F(4), F(5), F(6), F(7), A(8),
+                                 nullptr, A(9), A(10), A(11), F(12), F(13), F(14), F(15), A(20),
+                                 bw, &a), TTT_ERR_UNSUPPORTED);
+  }
+  {  // MLP backward
+    tttk::MlpBackwardArgs m;
+    const uint64_t need = tttv::mlp_backward_workspace_bytes(&p);
+    EXPECT(tttv::mlp_backward(&p, 256, A(1), A(2), A(3), F(4), F(5), F(6), F(7), F(8), F(9),
+                              F(10), A(11), nullptr, nullptr, nullptr, nullptr, A(12), A(13),
+                              A(14), F(15), F(16), F(17), F(18), F(19), F(21), F(22), A(20),
+                              need, &m), TTT_OK);
+    EXPECT(tttv::mlp_backward(&p, 256, A(1), A(2), A(3), F(4), F(5), F(6), F(7), F(8), F(9),
+                              F(10), A(11), nullptr, nullptr, nullptr, nullptr, A(12), A(13),
+                              A(14), F(15), F(16), F(17), F(18), F(19), F(21), F(22), A(20),
+                              need - 1, &m), TTT_ERR_SHAPE);
+    EXPECT(tttv::mlp_backward(&p, 256, A(1), A(2), A(3), F(4), F(5), F(6), F(7), F(8), F(9),
+                              F(10), A(11), nullptr, nullptr, nullptr, nullptr, A(12), A(12),
+                              A(14), F(15), F(16), F(17), F(18), F(19), F(21), F(22), A(20),
+                              need, &m), TTT_ERR_ALIAS);
+  }
+  {  // input side
+    tttk::InputArgs in;
+    EXPECT(tttv::input_projection(&p, 128, A(1), A(2), F(3), 0.01f, A(4), A(5), A(6), F(7), &in),
+           TTT_OK);
+    if (in.D != 128 || in.H != 3) ++fails;
+    EXPECT(tttv::input_projection(&p, 100, A(1), A(2), F(3), 0.01f, A(4), A(5), A(6), F(7), &in),
+           TTT_ERR_UNSUPPORTED);
+    EXPECT(tttv::input_projection(&p, 128, A(1), A(2), F(3), 0.0f, A(4), A(5), A(6), F(7), &in),
+           TTT_ERR_ARG);
+    EXPECT(tttv::input_projection(&p, 128, A(1), A(2), F(3), 0.01f, A(1), A(5), A(6), F(7), &in),
+           TTT_ERR_ALIAS);
+    EXPECT(tttv::input_projection(&p, 128, A(1), A(2), F(3), 0.01f, A(4), nullptr, A(6), F(7),
+                                  &in), TTT_ERR_NULL);
   }
   {  // MLP forward
     tttk::MlpArgs a;
