@@ -6,8 +6,11 @@ no shared state; each call has its own workspace)."""
 import pytest
 import torch
 
-from linear_rnn_ttt_amd import ttt_linear_forward, ttt_mlp_forward
-from linear_rnn_ttt_amd.inputs import WORKLOADS, make_inputs
+import numpy as np
+
+from linear_rnn_ttt_amd import (ttt_input_projection, ttt_linear_backward, ttt_linear_forward,
+                                ttt_mlp_backward, ttt_mlp_forward)
+from linear_rnn_ttt_amd.inputs import INPUT_WORKLOADS, WORKLOADS, make_input_side, make_inputs
 
 from _parity import to_dev
 
@@ -31,6 +34,54 @@ def _mlp_args(B=1, H=2, T=100):
     return [to_dev(inp[x], "bf16") for x in "qkv"] + [to_dev(inp[x]) for x in
                                                       ("eta", "w1", "b1", "w2", "b2",
                                                        "gamma", "beta")]
+
+
+def _flat(out):
+    """The tensors of an op's result (nested tuples flattened, None dropped)."""
+    if isinstance(out, torch.Tensor):
+        return [out]
+    return [t for x in out if x is not None for t in _flat(x)]
+
+
+@pytest.mark.parametrize("kind", ["linear backward", "mlp backward", "input side"])
+def test_graph_capture_and_replay_of_backward_and_input(kind):
+    """The backward passes and the input side captured in a graph: four
+    replays, with eager work between them, each bit-identical to the eager
+    call (their workspaces are allocated in the graph's pool)."""
+    if kind == "linear backward":
+        args = _lin_args(T=90)
+        dz = to_dev(np.random.default_rng(0).standard_normal((2, 3, 90, 64)).astype(np.float32),
+                    "bf16")
+        run = lambda: ttt_linear_backward(*args, dz)
+    elif kind == "mlp backward":
+        args = _mlp_args(T=40)
+        dz = to_dev(np.random.default_rng(1).standard_normal((1, 2, 40, 64)).astype(np.float32),
+                    "bf16")
+        run = lambda: ttt_mlp_backward(*args, dz)
+    else:
+        inp = make_input_side(INPUT_WORKLOADS["input_125m_b8_t2k"], B=2, T=130, D=192, H=3)
+        x, w_in, b_eta = (to_dev(inp["x"], "bf16"), to_dev(inp["w_in"], "bf16"),
+                          to_dev(inp["b_eta"]))
+        run = lambda: ttt_input_projection(x, w_in, b_eta, heads=3,
+                                           eta_base=float(inp["eta_base"]))
+    ref = [t.clone() for t in _flat(run())]
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        out = _flat(run())
+    for rep in range(4):
+        for t in out:
+            t.zero_()                              # eager work between the replays
+        g.replay()
+        torch.cuda.synchronize()
+        for got, want in zip(out, ref):
+            assert torch.equal(got, want), (kind, rep)
 
 
 @pytest.mark.parametrize("kind", ["linear", "linear split", "mlp"])
