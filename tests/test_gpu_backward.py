@@ -346,3 +346,16 @@ def test_backward_from_saved_bases_full_size_one_head():
           flush=True)
     for n, v in e.items():
         assert v <= TOL["bf16"], (n, v)
+
+
+def test_backward_more_units_than_compute_units():
+    """B*H = 320 units (more workgroups than the GPU holds at once), bf16,
+    with a final-state cotangent, against the oracle."""
+    B, H, T = 10, 32, 20
+    inp = make_inputs(BF, B=B, H=H, T=T)
+    dz, dwT = cotangents(inp, "bf16", seed=320)
+    got, want = run_both(inp, "bf16", dz, dwT)
+    e = errors(got, want, B, H)
+    print("B10 H32 T20: %s" % " ".join("%s %.1e" % kv for kv in e.items()), flush=True)
+    for n, v in e.items():
+        assert v <= TOL["bf16"], (n, v)

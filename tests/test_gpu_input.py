@@ -109,3 +109,14 @@ def test_input_side_feeds_the_scan():
     e = z_err(from_dev(z), zr)
     print("projection + scan: z %.1e" % e, flush=True)
     assert e <= TOL["bf16"]
+
+
+def test_input_side_more_tiles_than_compute_units():
+    """40 heads (7,720 output columns) over 1,200 tokens: 305 output tiles,
+    more than the GPU holds at once and not a multiple of the 8 XCDs (the
+    remapped launch has idle workgroups), against the oracle."""
+    B, T, D, H = 4, 300, 64, 40
+    inp = make_input_side(SMALL, B=B, T=T, D=D, H=H)
+    got = run(inp, H)
+    want = input_side(inp["x"], inp["w_in"], inp["b_eta"], H, 64, inp["eta_base"])
+    check(got, want, "B4 T300 D64 H40")

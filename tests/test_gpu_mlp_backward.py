@@ -158,3 +158,18 @@ def test_mlp_backward_deterministic_and_workspace_reuse():
     b = gpu(inp, "bf16", dz, fin)
     for n in NAMES:
         assert np.array_equal(a[n], b[n]), n
+
+
+def test_mlp_backward_more_units_than_compute_units():
+    """B*H = 320 units (more workgroups than the GPU holds at once), bf16,
+    with final-state cotangents, against the oracle."""
+    B, H, T = 5, 64, 17
+    inp = make_inputs(MLP, B=B, H=H, T=T)
+    dz, fin = cotangents(inp, "bf16", seed=321)
+    got = gpu(inp, "bf16", dz, fin)
+    want = mlp_backward(*(inp[x] for x in ("q", "k", "v", "eta") + STATE + ("gamma", "beta")),
+                        dz, fin)
+    e = errors(got, want, B, H)
+    print("B5 H64 T17: %s" % " ".join("%s %.1e" % kv for kv in e.items()), flush=True)
+    for n, v in e.items():
+        assert v <= TOL["bf16"], (n, v)
