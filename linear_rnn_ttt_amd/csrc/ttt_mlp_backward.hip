@@ -105,6 +105,48 @@ __device__ __forceinline__ void gemm(int wave, int w0, int nw, FA a, FB b, EPI e
   }
 }
 
+// The same product with the contraction split over S waves per output tile,
+// for products of few tiles (TILES * S <= 8 waves): wave w takes tile
+// w % TILES and the 16-k chunks w / TILES, w / TILES + S, ...; the partial
+// tiles meet in `part` (LDS, (S - 1) * TILES tiles) and the first wave of
+// each tile adds them up and runs epi.  Every wave of the workgroup must
+// call it (it holds a barrier).  Consecutive calls alternate between two
+// `part` buffers, so a buffer is written again only after a later barrier
+// that follows its reads.
+template <int R, int C, int K, int S, class FA, class FB, class EPI>
+__device__ __forceinline__ void gemm_ks(int wave, f32x4* part, FA a, FB b, EPI epi) {
+  static_assert(R % 16 == 0 && C % 16 == 0 && K % 16 == 0, "tile multiples");
+  constexpr int TN = C / 16, TILES = (R / 16) * TN, CH = K / 16;
+  static_assert(TILES * S <= NWV && S >= 1, "one wave per tile and part");
+  int g = (threadIdx.x & 63) >> 4, c = threadIdx.x & 15;
+  asm volatile("" : "+v"(g), "+v"(c));
+  const int lane = threadIdx.x & 63;
+  const int t = wave % TILES, p = wave / TILES;
+  const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  if (p < S) {
+#pragma unroll 1
+    for (int ch = p; ch < CH; ch += S) {
+      const int k0 = 16 * ch;
+      float av[4], bv[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        av[j] = a(m0 + c, k0 + 4 * j + g);
+        bv[j] = b(k0 + 4 * j + g, n0 + c);
+      }
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
+    }
+    if (p > 0) part[((p - 1) * TILES + t) * 64 + lane] = acc;
+  }
+  __syncthreads();
+  if (p == 0) {
+#pragma unroll
+    for (int q = 1; q < S; ++q) acc += part[((q - 1) * TILES + t) * 64 + lane];
+    epi(m0, n0, acc);
+  }
+}
+
 // Sum over the 32 lanes of a half-wave.
 __device__ __forceinline__ float sum32(float x) {
 #pragma unroll
@@ -142,6 +184,7 @@ struct Lds {
   float eta[16];
   float rho[16], ma[16], mx[16];   // K-side LN: 1/sigma, mean(a), mean(a x)
   float dln[16][2][D];             // dgamma, dbeta partials per token slot
+  f32x4 part[2][7][64];            // partial tiles of the split-contraction products
 };
 
 template <bool BF16, bool LN, bool RES>
@@ -214,7 +257,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                      }
                    });
     __syncthreads();
-    gemm<NB, D, M>(wave, 0, NWV, [&](int m, int k) { return X(1)[m * M + k]; },
+    gemm_ks<NB, D, M, 2>(wave, L.part[0][0], [&](int m, int k) { return X(1)[m * M + k]; },
                    [&](int k, int j) { return W2[k * D + j]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int j = n0 + (lane & 15);
@@ -339,7 +382,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
       L.m[idx][i][s] = s <= i ? v * L.eta[s] : 0.f;
     };
     // M1 = tril(Q K^T + 1) eta
-    gemm<NB, NB, D>(wave, 0, 1, [&](int i, int f) { return Q[i * D + f]; },
+    gemm_ks<NB, NB, D, 4>(wave, L.part[1][0], [&](int i, int f) { return Q[i * D + f]; },
                     [&](int f, int s) { return K[s * D + f]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
@@ -364,7 +407,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     __syncthreads();
     const float* AQ = X(5);
     // M2 = tril(AQ A^T + 1) eta
-    gemm<NB, NB, M>(wave, 0, 1, [&](int i, int k) { return AQ[i * M + k]; },
+    gemm_ks<NB, NB, M, 8>(wave, L.part[0][0], [&](int i, int k) { return AQ[i * M + k]; },
                     [&](int k, int s) { return A[s * M + k]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
@@ -373,8 +416,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                     });
     __syncthreads();
     // OQ = AQ W2 + b2 - M2 G_o -> Y7
-    gemm<NB, D, M + NB>(
-        wave, 0, NWV,
+    gemm_ks<NB, D, M + NB, 2>(
+        wave, L.part[1][0],
         [&](int i, int k) { return k < M ? AQ[i * M + k] : -L.m[1][i][k - M]; },
         [&](int k, int j) { return k < M ? W2[k * D + j] : Go[(k - M) * D + j]; },
         [&](int m0, int n0, f32x4 acc) {
@@ -418,7 +461,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     __syncthreads();
     const float* DOq = Y(7);
     // Mdo = tril(DOq G_o^T) eta
-    gemm<NB, NB, D>(wave, 0, 1, [&](int i, int j) { return DOq[i * D + j]; },
+    gemm_ks<NB, NB, D, 4>(wave, L.part[0][0], [&](int i, int j) { return DOq[i * D + j]; },
                     [&](int j, int s) { return Go[s * D + j]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
@@ -444,31 +487,31 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     //   Mdp = tril(dPQ G_p^T) eta, Tk = triu(K Q^T + 1), Ta = triu(A AQ^T + 1),
     //   Tgp = triu(G_p dPQ^T), Tgo = triu(G_o DOq^T)   ([s][i] for i >= s)
     auto triu_put = [&](int idx, int s, int i, float v) { L.m[idx][s][i] = i >= s ? v : 0.f; };
-    gemm<NB, NB, M>(wave, 0, 1, [&](int i, int k) { return dPQ[i * M + k]; },
+    gemm_ks<NB, NB, M, 8>(wave, L.part[1][0], [&](int i, int k) { return dPQ[i * M + k]; },
                     [&](int k, int s) { return Gp[s * M + k]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) tril_eta(3, 4 * g + i, lane & 15, acc[i]);
                     });
-    gemm<NB, NB, D>(wave, 1, 1, [&](int s, int f) { return K[s * D + f]; },
+    gemm_ks<NB, NB, D, 4>(wave, L.part[0][0], [&](int s, int f) { return K[s * D + f]; },
                     [&](int f, int i) { return Q[i * D + f]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) triu_put(4, 4 * g + i, lane & 15, acc[i] + 1.f);
                     });
-    gemm<NB, NB, M>(wave, 2, 1, [&](int s, int k) { return A[s * M + k]; },
+    gemm_ks<NB, NB, M, 8>(wave, L.part[1][0], [&](int s, int k) { return A[s * M + k]; },
                     [&](int k, int i) { return AQ[i * M + k]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) triu_put(5, 4 * g + i, lane & 15, acc[i] + 1.f);
                     });
-    gemm<NB, NB, M>(wave, 3, 1, [&](int s, int k) { return Gp[s * M + k]; },
+    gemm_ks<NB, NB, M, 8>(wave, L.part[0][0], [&](int s, int k) { return Gp[s * M + k]; },
                     [&](int k, int i) { return dPQ[i * M + k]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) triu_put(6, 4 * g + i, lane & 15, acc[i]);
                     });
-    gemm<NB, NB, D>(wave, 4, 1, [&](int s, int j) { return Go[s * D + j]; },
+    gemm_ks<NB, NB, D, 4>(wave, L.part[1][0], [&](int s, int j) { return Go[s * D + j]; },
                     [&](int j, int i) { return DOq[i * D + j]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
@@ -482,8 +525,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     // dQ = res dz + dPQ W1^T - Mdp K (stored); KA = K A1 + a1 + Tk dPQ -> X6;
     // AA = A A2 + a2 + Ta DOq -> Y8; GA1 = G_p A1^T + Tgp Q -> Y9;
     // GA2 = G_o A2^T + Tgo AQ -> X7
-    gemm<NB, D, M + NB>(
-        wave, 0, NWV,
+    gemm_ks<NB, D, M + NB, 2>(
+        wave, L.part[0][0],
         [&](int i, int k) { return k < M ? dPQ[i * M + k] : -L.m[3][i][k - M]; },
         [&](int k, int f) { return k < M ? W1[f * M + k] : K[(k - M) * D + f]; },
         [&](int m0, int n0, f32x4 acc) {
@@ -504,8 +547,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) X(6)[(m0 + 4 * g + i) * M + nn] = acc[i] + a1[nn];
         });
-    gemm<NB, D, M + NB>(
-        wave, 0, NWV,
+    gemm_ks<NB, D, M + NB, 2>(
+        wave, L.part[1][0],
         [&](int s, int k) { return k < M ? A[s * M + k] : L.m[5][s][k - M]; },
         [&](int k, int j) { return k < M ? A2[k * D + j] : DOq[(k - M) * D + j]; },
         [&](int m0, int n0, f32x4 acc) {
@@ -513,8 +556,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
 #pragma unroll
           for (int i = 0; i < 4; ++i) Y(8)[(m0 + 4 * g + i) * D + j] = acc[i] + a2[j];
         });
-    gemm<NB, D, M + NB>(
-        wave, 0, NWV,
+    gemm_ks<NB, D, M + NB, 2>(
+        wave, L.part[0][0],
         [&](int s, int k) { return k < M ? Gp[s * M + k] : L.m[6][s][k - M]; },
         [&](int k, int f) { return k < M ? A1[f * M + k] : Q[(k - M) * D + f]; },
         [&](int m0, int n0, f32x4 acc) {
@@ -554,7 +597,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     __syncthreads();
     const float* dU = X(6);
     // dG_o = -eta AA + dU W2 -> Y8
-    gemm<NB, D, M>(wave, 0, NWV, [&](int s, int k) { return dU[s * M + k]; },
+    gemm_ks<NB, D, M, 2>(wave, L.part[1][0], [&](int s, int k) { return dU[s * M + k]; },
                    [&](int k, int j) { return W2[k * D + j]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int j = n0 + (lane & 15);
@@ -629,7 +672,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     __syncthreads();
     const float* dP = X(7);
     // dK = dP W1^T - eta GA1 - res dt (stored)
-    gemm<NB, D, M>(wave, 0, NWV, [&](int s, int k) { return dP[s * M + k]; },
+    gemm_ks<NB, D, M, 2>(wave, L.part[0][0], [&](int s, int k) { return dP[s * M + k]; },
                    [&](int k, int f) { return W1[f * M + k]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int f = n0 + (lane & 15);
