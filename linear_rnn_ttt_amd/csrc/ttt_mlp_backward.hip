@@ -62,6 +62,7 @@ constexpr int NWV = NT / 64;
 constexpr int SZ = D * M + M + M * D + D;  // floats of one state (W1, b1, W2, b2)
 constexpr int OB1 = D * M, OW2 = D * M + M, OB2 = D * M + M + M * D;
 constexpr int NX = 8, NY = 12;             // per-tile intermediates: 16x256 and 16x64
+constexpr int YD = D + 4;  // LDS row stride of the 16x64 intermediates (4 banks apart)
 static_assert(SZ == MLP_BWD_STATE_FLOATS && NX * NB * M + NY * NB * D + 2 * D == MLP_BWD_TILE_FLOATS,
               "workspace layout and host size disagree");
 
@@ -95,8 +96,8 @@ __device__ __forceinline__ void gemm(int wave, int w0, int nw, FA a, FB b, EPI e
       float av[4], bv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        av[j] = a(m0 + c, k0 + 4 * j + g);
-        bv[j] = b(k0 + 4 * j + g, n0 + c);
+        av[j] = a(m0 + c, k0 + 4 * g + j);
+        bv[j] = b(k0 + 4 * g + j, n0 + c);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
@@ -131,8 +132,8 @@ __device__ __forceinline__ void gemm_ks(int wave, f32x4* part, FA a, FB b, EPI e
       float av[4], bv[4];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        av[j] = a(m0 + c, k0 + 4 * j + g);
-        bv[j] = b(k0 + 4 * j + g, n0 + c);
+        av[j] = a(m0 + c, k0 + 4 * g + j);
+        bv[j] = b(k0 + 4 * g + j, n0 + c);
       }
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
@@ -185,6 +186,7 @@ struct Lds {
   float rho[16], ma[16], mx[16];   // K-side LN: 1/sigma, mean(a), mean(a x)
   float dln[16][2][D];             // dgamma, dbeta partials per token slot
   f32x4 part[2][7][64];            // partial tiles of the split-contraction products
+  float y[NY][NB][YD];             // per-tile 16 x 64 intermediates, rows padded
 };
 
 template <bool BF16, bool LN, bool RES>
@@ -198,10 +200,9 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
   float* bases = ws;
   float* adj = ws + static_cast<size_t>(n) * SZ;
   float* Xb = adj + SZ;
-  float* Yb = Xb + NX * NB * M;
   float* dln_out = ws + a.unit_floats - 2 * D;   // the unit's dgamma, dbeta
   auto X = [&](int i) { return Xb + i * NB * M; };
-  auto Y = [&](int i) { return Yb + i * NB * D; };
+  auto Y = [&](int i) { return &L.y[i][0][0]; };
   const float* gam = a.gamma + static_cast<size_t>(head) * D;
   const float* bet = a.beta + static_cast<size_t>(head) * D;
   const size_t row0 = static_cast<size_t>(unit) * T;   // first token row of the unit
@@ -229,10 +230,10 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
       const int s = i / D, f = i % D, tok = c * NB + s;
       const bool ok = tok < T;
       const size_t e = (row0 + tok) * D + f;
-      Y(0)[i] = ok ? ld_io<BF16>(a.k, e) : 0.f;
-      Y(1)[i] = ok ? ld_io<BF16>(a.q, e) : 0.f;
-      Y(2)[i] = ok ? ld_io<BF16>(a.v, e) : 0.f;
-      if (with_dz) Y(3)[i] = ok ? ld_io<BF16>(a.dz, e) : 0.f;
+      Y(0)[s * YD + f] = ok ? ld_io<BF16>(a.k, e) : 0.f;
+      Y(1)[s * YD + f] = ok ? ld_io<BF16>(a.q, e) : 0.f;
+      Y(2)[s * YD + f] = ok ? ld_io<BF16>(a.v, e) : 0.f;
+      if (with_dz) Y(3)[s * YD + f] = ok ? ld_io<BF16>(a.dz, e) : 0.f;
     }
     if (tid < NB) L.eta[tid] = c * NB + tid < T ? a.eta[row0 + c * NB + tid] : 0.f;
   };
@@ -245,7 +246,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     const float* b1 = S + OB1;
     const float* W2 = S + OW2;
     const float* b2 = S + OB2;
-    gemm<NB, M, D>(wave, 0, NWV, [&](int m, int k) { return Y(0)[m * D + k]; },
+    gemm<NB, M, D>(wave, 0, NWV, [&](int m, int k) { return Y(0)[m * YD + k]; },
                    [&](int k, int nn) { return W1[k * M + nn]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int nn = n0 + (lane & 15);
@@ -262,7 +263,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                    [&](int m0, int n0, f32x4 acc) {
                      const int j = n0 + (lane & 15);
 #pragma unroll
-                     for (int i = 0; i < 4; ++i) Y(4)[(m0 + 4 * g + i) * D + j] = acc[i] + b2[j];
+                     for (int i = 0; i < 4; ++i) Y(4)[(m0 + 4 * g + i) * YD + j] = acc[i] + b2[j];
                    });
     __syncthreads();
     // LN of O and the loss gradient G_o: wave w has tokens 2w, 2w+1; lane
@@ -272,9 +273,9 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
       float o[2], t[2], x[2], av[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        o[u] = Y(4)[s * D + f + u];
-        const float kk = RES ? Y(0)[s * D + f + u] : 0.f;
-        t[u] = Y(2)[s * D + f + u] - (LN ? bet[f + u] : 0.f) - kk;
+        o[u] = Y(4)[s * YD + f + u];
+        const float kk = RES ? Y(0)[s * YD + f + u] : 0.f;
+        t[u] = Y(2)[s * YD + f + u] - (LN ? bet[f + u] : 0.f) - kk;
       }
       if (LN) {
         const float mu = sum32(o[0] + o[1]) * (1.f / D);
@@ -289,8 +290,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
         const float mx = sum32(av[0] * x[0] + av[1] * x[1]) * (1.f / D);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          Y(5)[s * D + f + u] = x[u];
-          Y(6)[s * D + f + u] = rho * (av[u] - ma - x[u] * mx);
+          Y(5)[s * YD + f + u] = x[u];
+          Y(6)[s * YD + f + u] = rho * (av[u] - ma - x[u] * mx);
         }
         if ((lane & 31) == 0) {
           L.rho[s] = rho;
@@ -299,14 +300,14 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) Y(6)[s * D + f + u] = 2.f * (o[u] - t[u]);
+        for (int u = 0; u < 2; ++u) Y(6)[s * YD + f + u] = 2.f * (o[u] - t[u]);
       }
 #pragma unroll
-      for (int u = 0; u < 2; ++u) Y(2)[s * D + f + u] = t[u];
+      for (int u = 0; u < 2; ++u) Y(2)[s * YD + f + u] = t[u];
     }
     __syncthreads();
     // U = G_o W2^T, G_p = U GELU'(P)
-    gemm<NB, M, D>(wave, 0, NWV, [&](int m, int k) { return Y(6)[m * D + k]; },
+    gemm<NB, M, D>(wave, 0, NWV, [&](int m, int k) { return Y(6)[m * YD + k]; },
                    [&](int k, int nn) { return W2[nn * D + k]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int nn = n0 + (lane & 15);
@@ -328,7 +329,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     float* Sn = bases + static_cast<size_t>(c + 1) * SZ;
     kside(S);
     // W1' = W1 - K^T (eta G_p), W2' = W2 - A^T (eta G_o)
-    gemm<D, M, NB>(wave, 0, NWV, [&](int f, int s) { return Y(0)[s * D + f]; },
+    gemm<D, M, NB>(wave, 0, NWV, [&](int f, int s) { return Y(0)[s * YD + f]; },
                    [&](int s, int nn) { return L.eta[s] * X(3)[s * M + nn]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int nn = n0 + (lane & 15);
@@ -339,7 +340,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                      }
                    });
     gemm<M, D, NB>(wave, 0, NWV, [&](int nn, int s) { return X(1)[s * M + nn]; },
-                   [&](int s, int j) { return L.eta[s] * Y(6)[s * D + j]; },
+                   [&](int s, int j) { return L.eta[s] * Y(6)[s * YD + j]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int j = n0 + (lane & 15);
 #pragma unroll
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
         Sn[OB1 + nn] = S[OB1 + nn] - sum;
       } else {
         const int j = nn - M;
-        for (int s = 0; s < NB; ++s) sum += L.eta[s] * Y(6)[s * D + j];
+        for (int s = 0; s < NB; ++s) sum += L.eta[s] * Y(6)[s * YD + j];
         Sn[OB2 + j] = S[OB2 + j] - sum;
       }
     }
@@ -382,8 +383,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
       L.m[idx][i][s] = s <= i ? v * L.eta[s] : 0.f;
     };
     // M1 = tril(Q K^T + 1) eta
-    gemm_ks<NB, NB, D, 4>(wave, L.part[1][0], [&](int i, int f) { return Q[i * D + f]; },
-                    [&](int f, int s) { return K[s * D + f]; },
+    gemm_ks<NB, NB, D, 4>(wave, L.part[1][0], [&](int i, int f) { return Q[i * YD + f]; },
+                    [&](int f, int s) { return K[s * YD + f]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i)
@@ -393,7 +394,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     // PQ = Q W1 + b1 - M1 G_p -> X4, AQ = GELU(PQ) -> X5
     gemm<NB, M, D + NB>(
         wave, 0, NWV,
-        [&](int i, int k) { return k < D ? Q[i * D + k] : -L.m[0][i][k - D]; },
+        [&](int i, int k) { return k < D ? Q[i * YD + k] : -L.m[0][i][k - D]; },
         [&](int k, int nn) { return k < D ? W1[k * M + nn] : Gp[(k - D) * M + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
@@ -419,11 +420,11 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     gemm_ks<NB, D, M + NB, 2>(
         wave, L.part[1][0],
         [&](int i, int k) { return k < M ? AQ[i * M + k] : -L.m[1][i][k - M]; },
-        [&](int k, int j) { return k < M ? W2[k * D + j] : Go[(k - M) * D + j]; },
+        [&](int k, int j) { return k < M ? W2[k * D + j] : Go[(k - M) * YD + j]; },
         [&](int m0, int n0, f32x4 acc) {
           const int j = n0 + (lane & 15);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Y(7)[(m0 + 4 * g + i) * D + j] = acc[i] + b2[j];
+          for (int i = 0; i < 4; ++i) Y(7)[(m0 + 4 * g + i) * YD + j] = acc[i] + b2[j];
         });
     __syncthreads();
     // output LN backward: DOq -> Y7; dgamma, dbeta
@@ -432,8 +433,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
       float o[2], dz[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
-        o[u] = Y(7)[s * D + f + u];
-        dz[u] = Y(3)[s * D + f + u];
+        o[u] = Y(7)[s * YD + f + u];
+        dz[u] = Y(3)[s * YD + f + u];
       }
       if (LN) {
         const float mu = sum32(o[0] + o[1]) * (1.f / D);
@@ -449,20 +450,20 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
         const float m2 = sum32(gd[0] * x[0] + gd[1] * x[1]) * (1.f / D);
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-          Y(7)[s * D + f + u] = rho * (gd[u] - m1 - x[u] * m2);
+          Y(7)[s * YD + f + u] = rho * (gd[u] - m1 - x[u] * m2);
           dg_acc[u] += dz[u] * x[u];
           db_acc[u] += dz[u];
         }
       } else {
 #pragma unroll
-        for (int u = 0; u < 2; ++u) Y(7)[s * D + f + u] = dz[u];
+        for (int u = 0; u < 2; ++u) Y(7)[s * YD + f + u] = dz[u];
       }
     }
     __syncthreads();
     const float* DOq = Y(7);
     // Mdo = tril(DOq G_o^T) eta
-    gemm_ks<NB, NB, D, 4>(wave, L.part[0][0], [&](int i, int j) { return DOq[i * D + j]; },
-                    [&](int j, int s) { return Go[s * D + j]; },
+    gemm_ks<NB, NB, D, 4>(wave, L.part[0][0], [&](int i, int j) { return DOq[i * YD + j]; },
+                    [&](int j, int s) { return Go[s * YD + j]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) tril_eta(2, 4 * g + i, lane & 15, acc[i]);
@@ -471,7 +472,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     // dPQ = (DOq W2^T - Mdo A) GELU'(PQ) -> X4
     gemm<NB, M, D + NB>(
         wave, 0, NWV,
-        [&](int i, int k) { return k < D ? DOq[i * D + k] : -L.m[2][i][k - D]; },
+        [&](int i, int k) { return k < D ? DOq[i * YD + k] : -L.m[2][i][k - D]; },
         [&](int k, int nn) { return k < D ? W2[nn * D + k] : A[(k - D) * M + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
@@ -493,8 +494,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) tril_eta(3, 4 * g + i, lane & 15, acc[i]);
                     });
-    gemm_ks<NB, NB, D, 4>(wave, L.part[0][0], [&](int s, int f) { return K[s * D + f]; },
-                    [&](int f, int i) { return Q[i * D + f]; },
+    gemm_ks<NB, NB, D, 4>(wave, L.part[0][0], [&](int s, int f) { return K[s * YD + f]; },
+                    [&](int f, int i) { return Q[i * YD + f]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) triu_put(4, 4 * g + i, lane & 15, acc[i] + 1.f);
@@ -511,8 +512,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) triu_put(6, 4 * g + i, lane & 15, acc[i]);
                     });
-    gemm_ks<NB, NB, D, 4>(wave, L.part[1][0], [&](int s, int j) { return Go[s * D + j]; },
-                    [&](int j, int i) { return DOq[i * D + j]; },
+    gemm_ks<NB, NB, D, 4>(wave, L.part[1][0], [&](int s, int j) { return Go[s * YD + j]; },
+                    [&](int j, int i) { return DOq[i * YD + j]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) triu_put(7, 4 * g + i, lane & 15, acc[i]);
@@ -528,19 +529,19 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     gemm_ks<NB, D, M + NB, 2>(
         wave, L.part[0][0],
         [&](int i, int k) { return k < M ? dPQ[i * M + k] : -L.m[3][i][k - M]; },
-        [&](int k, int f) { return k < M ? W1[f * M + k] : K[(k - M) * D + f]; },
+        [&](int k, int f) { return k < M ? W1[f * M + k] : K[(k - M) * YD + f]; },
         [&](int m0, int n0, f32x4 acc) {
           const int f = n0 + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int s = m0 + 4 * g + i, tok = c * NB + s;
-            const float v = acc[i] + (RES ? Y(3)[s * D + f] : 0.f);
+            const float v = acc[i] + (RES ? Y(3)[s * YD + f] : 0.f);
             if (tok < T) st_io<BF16>(a.dq, (row0 + tok) * D + f, v);
           }
         });
     gemm<NB, M, D + NB>(
         wave, 0, NWV,
-        [&](int s, int k) { return k < D ? K[s * D + k] : L.m[4][s][k - D]; },
+        [&](int s, int k) { return k < D ? K[s * YD + k] : L.m[4][s][k - D]; },
         [&](int k, int nn) { return k < D ? A1[k * M + nn] : dPQ[(k - D) * M + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
@@ -550,24 +551,24 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     gemm_ks<NB, D, M + NB, 2>(
         wave, L.part[1][0],
         [&](int s, int k) { return k < M ? A[s * M + k] : L.m[5][s][k - M]; },
-        [&](int k, int j) { return k < M ? A2[k * D + j] : DOq[(k - M) * D + j]; },
+        [&](int k, int j) { return k < M ? A2[k * D + j] : DOq[(k - M) * YD + j]; },
         [&](int m0, int n0, f32x4 acc) {
           const int j = n0 + (lane & 15);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Y(8)[(m0 + 4 * g + i) * D + j] = acc[i] + a2[j];
+          for (int i = 0; i < 4; ++i) Y(8)[(m0 + 4 * g + i) * YD + j] = acc[i] + a2[j];
         });
     gemm_ks<NB, D, M + NB, 2>(
         wave, L.part[0][0],
         [&](int s, int k) { return k < M ? Gp[s * M + k] : L.m[6][s][k - M]; },
-        [&](int k, int f) { return k < M ? A1[f * M + k] : Q[(k - M) * D + f]; },
+        [&](int k, int f) { return k < M ? A1[f * M + k] : Q[(k - M) * YD + f]; },
         [&](int m0, int n0, f32x4 acc) {
           const int f = n0 + (lane & 15);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) Y(9)[(m0 + 4 * g + i) * D + f] = acc[i];
+          for (int i = 0; i < 4; ++i) Y(9)[(m0 + 4 * g + i) * YD + f] = acc[i];
         });
     gemm<NB, M, D + NB>(
         wave, 0, NWV,
-        [&](int s, int k) { return k < D ? Go[s * D + k] : L.m[7][s][k - D]; },
+        [&](int s, int k) { return k < D ? Go[s * YD + k] : L.m[7][s][k - D]; },
         [&](int k, int nn) { return k < D ? A2[nn * D + k] : AQ[(k - D) * M + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
@@ -581,7 +582,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
       const int s = 2 * wave + (lane >> 5), l32 = lane & 31;
       float acc = 0.f;
       for (int nn = l32; nn < M; nn += 32) acc += X(6)[s * M + nn] * Gp[s * M + nn];
-      for (int j = l32; j < D; j += 32) acc += Y(8)[s * D + j] * Go[s * D + j];
+      for (int j = l32; j < D; j += 32) acc += Y(8)[s * YD + j] * Go[s * YD + j];
       acc = sum32(acc);
       const int tok = c * NB + s;
       if (l32 == 0 && tok < T) a.deta[row0 + tok] = -acc;
@@ -604,7 +605,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
 #pragma unroll
                      for (int i = 0; i < 4; ++i) {
                        const int s = m0 + 4 * g + i;
-                       Y(8)[s * D + j] = acc[i] - L.eta[s] * Y(8)[s * D + j];
+                       Y(8)[s * YD + j] = acc[i] - L.eta[s] * Y(8)[s * YD + j];
                      }
                    });
     __syncthreads();
@@ -614,14 +615,14 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
       const int tok = c * NB + s;
       float u[2], dO[2], dt[2];
 #pragma unroll
-      for (int v = 0; v < 2; ++v) u[v] = Y(8)[s * D + f + v];
+      for (int v = 0; v < 2; ++v) u[v] = Y(8)[s * YD + f + v];
       if (LN) {
         const float rho = L.rho[s], ma = L.ma[s], mx = L.mx[s];
         float x[2], t[2], av[2];
 #pragma unroll
         for (int v = 0; v < 2; ++v) {
-          x[v] = Y(5)[s * D + f + v];
-          t[v] = Y(2)[s * D + f + v];
+          x[v] = Y(5)[s * YD + f + v];
+          t[v] = Y(2)[s * YD + f + v];
           av[v] = 2.f * gam[f + v] * (gam[f + v] * x[v] - t[v]);
         }
         const float drho = sum32(u[0] * (av[0] - ma - x[0] * mx) + u[1] * (av[1] - ma - x[1] * mx));
@@ -651,15 +652,15 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
       }
 #pragma unroll
       for (int v = 0; v < 2; ++v) {
-        Y(10)[s * D + f + v] = dO[v];
-        Y(11)[s * D + f + v] = dt[v];
+        Y(10)[s * YD + f + v] = dO[v];
+        Y(11)[s * YD + f + v] = dt[v];
         if (tok < T) st_io<BF16>(a.dv, (row0 + tok) * D + f + v, dt[v]);
       }
     }
     __syncthreads();
     const float* dOk = Y(10);
     // dP = (-eta GA2 + dO W2^T) GELU'(P) + X2 -> X7
-    gemm<NB, M, D>(wave, 0, NWV, [&](int s, int k) { return dOk[s * D + k]; },
+    gemm<NB, M, D>(wave, 0, NWV, [&](int s, int k) { return dOk[s * YD + k]; },
                    [&](int k, int nn) { return W2[nn * D + k]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int nn = n0 + (lane & 15);
@@ -679,8 +680,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
 #pragma unroll
                      for (int i = 0; i < 4; ++i) {
                        const int s = m0 + 4 * g + i, tok = c * NB + s;
-                       const float v = acc[i] - L.eta[s] * Y(9)[s * D + f] -
-                                       (RES ? Y(11)[s * D + f] : 0.f);
+                       const float v = acc[i] - L.eta[s] * Y(9)[s * YD + f] -
+                                       (RES ? Y(11)[s * YD + f] : 0.f);
                        if (tok < T) st_io<BF16>(a.dk, (row0 + tok) * D + f, v);
                      }
                    });
@@ -689,7 +690,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     float* A2w = adj + OW2;
     gemm<D, M, 2 * NB>(
         wave, 0, NWV,
-        [&](int f, int k) { return k < NB ? Q[k * D + f] : K[(k - NB) * D + f]; },
+        [&](int f, int k) { return k < NB ? Q[k * YD + f] : K[(k - NB) * YD + f]; },
         [&](int k, int nn) { return k < NB ? dPQ[k * M + nn] : dP[(k - NB) * M + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
@@ -702,7 +703,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
           return k < NB ? AQ[k * M + nn] : (k < 2 * NB ? A[(k - NB) * M + nn] : dU[(k - 2 * NB) * M + nn]);
         },
         [&](int k, int j) {
-          return k < NB ? DOq[k * D + j] : (k < 2 * NB ? dOk[(k - NB) * D + j] : Go[(k - 2 * NB) * D + j]);
+          return k < NB ? DOq[k * YD + j] : (k < 2 * NB ? dOk[(k - NB) * YD + j] : Go[(k - 2 * NB) * YD + j]);
         },
         [&](int m0, int n0, f32x4 acc) {
           const int j = n0 + (lane & 15);
@@ -712,11 +713,20 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     for (int nn = tid; nn < M + D; nn += NT) {
       float sum = 0.f;
       if (nn < M) {
-        for (int s = 0; s < NB; ++s) sum += dPQ[s * M + nn] + dP[s * M + nn];
-        adj[OB1 + nn] += sum;
+        // all 32 loads in flight before the sum (one round trip)
+        float u[NB], w[NB];
+#pragma unroll
+        for (int s = 0; s < NB; ++s) {
+          u[s] = dPQ[s * M + nn];
+          w[s] = dP[s * M + nn];
+        }
+        const float prev = adj[OB1 + nn];
+#pragma unroll
+        for (int s = 0; s < NB; ++s) sum += u[s] + w[s];
+        adj[OB1 + nn] = prev + sum;
       } else {
         const int j = nn - M;
-        for (int s = 0; s < NB; ++s) sum += DOq[s * D + j] + dOk[s * D + j];
+        for (int s = 0; s < NB; ++s) sum += DOq[s * YD + j] + dOk[s * YD + j];
         adj[OB2 + j] += sum;
       }
     }
