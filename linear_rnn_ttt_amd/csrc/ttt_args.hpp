@@ -195,9 +195,10 @@ struct MlpBackwardArgs {
 };
 
 // Floats of one TTT-MLP state (W1 64x256, b1 256, W2 256x64, b2 64) and of
-// the backward's per-tile intermediates of one unit.
+// the backward's per-tile intermediates of one unit kept in the workspace
+// (three 16x256 ones, rows padded to 260 floats; the rest live in LDS).
 constexpr uint64_t MLP_BWD_STATE_FLOATS = 64 * 256 + 256 + 256 * 64 + 64;
-constexpr uint64_t MLP_BWD_TILE_FLOATS = 8 * 16 * 256 + 12 * 16 * 64 + 2 * 64;
+constexpr uint64_t MLP_BWD_TILE_FLOATS = 3 * 16 * 260 + 2 * 64;
 
 // The input side (ttt_input_projection): Y = x W_in^T, then per column the
 // q/k/v store or the learning-rate gate.

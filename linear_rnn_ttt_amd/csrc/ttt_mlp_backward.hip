@@ -61,9 +61,15 @@ constexpr int NT = 512;  // threads per workgroup
 constexpr int NWV = NT / 64;
 constexpr int SZ = D * M + M + M * D + D;  // floats of one state (W1, b1, W2, b2)
 constexpr int OB1 = D * M, OW2 = D * M + M, OB2 = D * M + M + M * D;
-constexpr int NX = 8, NY = 12;             // per-tile intermediates: 16x256 and 16x64
-constexpr int YD = D + 4;  // LDS row stride of the 16x64 intermediates (4 banks apart)
-static_assert(SZ == MLP_BWD_STATE_FLOATS && NX * NB * M + NY * NB * D + 2 * D == MLP_BWD_TILE_FLOATS,
+constexpr int NY = 12;     // per-tile 16x64 intermediates (LDS)
+constexpr int YD = D + 4;  // their row stride (rows 4 banks apart)
+constexpr int XM = M + 4;  // row stride of the 16x256 intermediates
+// the eight 16x256 intermediates X0..X7: five that the products read often
+// in LDS, the three only used elementwise (P, U, KA / dU) in the workspace
+constexpr int NXL = 5, NXG = 3;
+constexpr int XSLOT[8] = {0, 0, 1, 1, 2, 3, 2, 4};   // slot in LDS or in the workspace
+constexpr bool XLDS[8] = {false, true, false, true, true, true, false, true};
+static_assert(SZ == MLP_BWD_STATE_FLOATS && NXG * NB * XM + 2 * D == MLP_BWD_TILE_FLOATS,
               "workspace layout and host size disagree");
 
 
@@ -184,9 +190,12 @@ struct Lds {
   float m[8][16][17];   // masked 16x16 coefficient tiles
   float eta[16];
   float rho[16], ma[16], mx[16];   // K-side LN: 1/sigma, mean(a), mean(a x)
-  float dln[16][2][D];             // dgamma, dbeta partials per token slot
   f32x4 part[2][7][64];            // partial tiles of the split-contraction products
-  float y[NY][NB][YD];             // per-tile 16 x 64 intermediates, rows padded
+  union {
+    float y[NY][NB][YD];           // per-tile 16 x 64 intermediates, rows padded
+    float dln[16][2][D];           // after the walk: dgamma, dbeta partials per token slot
+  };
+  float x[NXL][NB][XM];            // the LDS-resident 16 x 256 intermediates
 };
 
 template <bool BF16, bool LN, bool RES>
@@ -201,7 +210,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
   float* adj = ws + static_cast<size_t>(n) * SZ;
   float* Xb = adj + SZ;
   float* dln_out = ws + a.unit_floats - 2 * D;   // the unit's dgamma, dbeta
-  auto X = [&](int i) { return Xb + i * NB * M; };
+  auto X = [&](int i) { return XLDS[i] ? &L.x[XSLOT[i]][0][0] : Xb + XSLOT[i] * NB * XM; };
   auto Y = [&](int i) { return &L.y[i][0][0]; };
   const float* gam = a.gamma + static_cast<size_t>(head) * D;
   const float* bet = a.beta + static_cast<size_t>(head) * D;
@@ -253,12 +262,12 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
 #pragma unroll
                      for (int i = 0; i < 4; ++i) {
                        const float p = acc[i] + b1[nn];
-                       X(0)[(m0 + 4 * g + i) * M + nn] = p;
-                       X(1)[(m0 + 4 * g + i) * M + nn] = gelu(p);
+                       X(0)[(m0 + 4 * g + i) * XM + nn] = p;
+                       X(1)[(m0 + 4 * g + i) * XM + nn] = gelu(p);
                      }
                    });
     __syncthreads();
-    gemm_ks<NB, D, M, 2>(wave, L.part[0][0], [&](int m, int k) { return X(1)[m * M + k]; },
+    gemm_ks<NB, D, M, 2>(wave, L.part[0][0], [&](int m, int k) { return X(1)[m * XM + k]; },
                    [&](int k, int j) { return W2[k * D + j]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int j = n0 + (lane & 15);
@@ -313,7 +322,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                      const int nn = n0 + (lane & 15);
 #pragma unroll
                      for (int i = 0; i < 4; ++i) {
-                       const int e = (m0 + 4 * g + i) * M + nn;
+                       const int e = (m0 + 4 * g + i) * XM + nn;
                        X(2)[e] = acc[i];
                        X(3)[e] = acc[i] * gelu1(X(0)[e]);
                      }
@@ -330,7 +339,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     kside(S);
     // W1' = W1 - K^T (eta G_p), W2' = W2 - A^T (eta G_o)
     gemm<D, M, NB>(wave, 0, NWV, [&](int f, int s) { return Y(0)[s * YD + f]; },
-                   [&](int s, int nn) { return L.eta[s] * X(3)[s * M + nn]; },
+                   [&](int s, int nn) { return L.eta[s] * X(3)[s * XM + nn]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int nn = n0 + (lane & 15);
 #pragma unroll
@@ -339,7 +348,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                        Sn[e] = S[e] - acc[i];
                      }
                    });
-    gemm<M, D, NB>(wave, 0, NWV, [&](int nn, int s) { return X(1)[s * M + nn]; },
+    gemm<M, D, NB>(wave, 0, NWV, [&](int nn, int s) { return X(1)[s * XM + nn]; },
                    [&](int s, int j) { return L.eta[s] * Y(6)[s * YD + j]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int j = n0 + (lane & 15);
@@ -352,7 +361,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     for (int nn = tid; nn < M + D; nn += NT) {
       float sum = 0.f;
       if (nn < M) {
-        for (int s = 0; s < NB; ++s) sum += L.eta[s] * X(3)[s * M + nn];
+        for (int s = 0; s < NB; ++s) sum += L.eta[s] * X(3)[s * XM + nn];
         Sn[OB1 + nn] = S[OB1 + nn] - sum;
       } else {
         const int j = nn - M;
@@ -395,21 +404,21 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     gemm<NB, M, D + NB>(
         wave, 0, NWV,
         [&](int i, int k) { return k < D ? Q[i * YD + k] : -L.m[0][i][k - D]; },
-        [&](int k, int nn) { return k < D ? W1[k * M + nn] : Gp[(k - D) * M + nn]; },
+        [&](int k, int nn) { return k < D ? W1[k * M + nn] : Gp[(k - D) * XM + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const float p = acc[i] + b1[nn];
-            X(4)[(m0 + 4 * g + i) * M + nn] = p;
-            X(5)[(m0 + 4 * g + i) * M + nn] = gelu(p);
+            X(4)[(m0 + 4 * g + i) * XM + nn] = p;
+            X(5)[(m0 + 4 * g + i) * XM + nn] = gelu(p);
           }
         });
     __syncthreads();
     const float* AQ = X(5);
     // M2 = tril(AQ A^T + 1) eta
-    gemm_ks<NB, NB, M, 8>(wave, L.part[0][0], [&](int i, int k) { return AQ[i * M + k]; },
-                    [&](int k, int s) { return A[s * M + k]; },
+    gemm_ks<NB, NB, M, 8>(wave, L.part[0][0], [&](int i, int k) { return AQ[i * XM + k]; },
+                    [&](int k, int s) { return A[s * XM + k]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i)
@@ -419,7 +428,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     // OQ = AQ W2 + b2 - M2 G_o -> Y7
     gemm_ks<NB, D, M + NB, 2>(
         wave, L.part[1][0],
-        [&](int i, int k) { return k < M ? AQ[i * M + k] : -L.m[1][i][k - M]; },
+        [&](int i, int k) { return k < M ? AQ[i * XM + k] : -L.m[1][i][k - M]; },
         [&](int k, int j) { return k < M ? W2[k * D + j] : Go[(k - M) * YD + j]; },
         [&](int m0, int n0, f32x4 acc) {
           const int j = n0 + (lane & 15);
@@ -473,12 +482,12 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     gemm<NB, M, D + NB>(
         wave, 0, NWV,
         [&](int i, int k) { return k < D ? DOq[i * YD + k] : -L.m[2][i][k - D]; },
-        [&](int k, int nn) { return k < D ? W2[nn * D + k] : A[(k - D) * M + nn]; },
+        [&](int k, int nn) { return k < D ? W2[nn * D + k] : A[(k - D) * XM + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const int e = (m0 + 4 * g + i) * M + nn;
+            const int e = (m0 + 4 * g + i) * XM + nn;
             X(4)[e] = acc[i] * gelu1(X(4)[e]);
           }
         });
@@ -488,8 +497,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     //   Mdp = tril(dPQ G_p^T) eta, Tk = triu(K Q^T + 1), Ta = triu(A AQ^T + 1),
     //   Tgp = triu(G_p dPQ^T), Tgo = triu(G_o DOq^T)   ([s][i] for i >= s)
     auto triu_put = [&](int idx, int s, int i, float v) { L.m[idx][s][i] = i >= s ? v : 0.f; };
-    gemm_ks<NB, NB, M, 8>(wave, L.part[1][0], [&](int i, int k) { return dPQ[i * M + k]; },
-                    [&](int k, int s) { return Gp[s * M + k]; },
+    gemm_ks<NB, NB, M, 8>(wave, L.part[1][0], [&](int i, int k) { return dPQ[i * XM + k]; },
+                    [&](int k, int s) { return Gp[s * XM + k]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) tril_eta(3, 4 * g + i, lane & 15, acc[i]);
@@ -500,14 +509,14 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) triu_put(4, 4 * g + i, lane & 15, acc[i] + 1.f);
                     });
-    gemm_ks<NB, NB, M, 8>(wave, L.part[1][0], [&](int s, int k) { return A[s * M + k]; },
-                    [&](int k, int i) { return AQ[i * M + k]; },
+    gemm_ks<NB, NB, M, 8>(wave, L.part[1][0], [&](int s, int k) { return A[s * XM + k]; },
+                    [&](int k, int i) { return AQ[i * XM + k]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) triu_put(5, 4 * g + i, lane & 15, acc[i] + 1.f);
                     });
-    gemm_ks<NB, NB, M, 8>(wave, L.part[0][0], [&](int s, int k) { return Gp[s * M + k]; },
-                    [&](int k, int i) { return dPQ[i * M + k]; },
+    gemm_ks<NB, NB, M, 8>(wave, L.part[0][0], [&](int s, int k) { return Gp[s * XM + k]; },
+                    [&](int k, int i) { return dPQ[i * XM + k]; },
                     [&](int m0, int n0, f32x4 acc) {
 #pragma unroll
                       for (int i = 0; i < 4; ++i) triu_put(6, 4 * g + i, lane & 15, acc[i]);
@@ -528,7 +537,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     // GA2 = G_o A2^T + Tgo AQ -> X7
     gemm_ks<NB, D, M + NB, 2>(
         wave, L.part[0][0],
-        [&](int i, int k) { return k < M ? dPQ[i * M + k] : -L.m[3][i][k - M]; },
+        [&](int i, int k) { return k < M ? dPQ[i * XM + k] : -L.m[3][i][k - M]; },
         [&](int k, int f) { return k < M ? W1[f * M + k] : K[(k - M) * YD + f]; },
         [&](int m0, int n0, f32x4 acc) {
           const int f = n0 + (lane & 15);
@@ -542,15 +551,15 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     gemm<NB, M, D + NB>(
         wave, 0, NWV,
         [&](int s, int k) { return k < D ? K[s * YD + k] : L.m[4][s][k - D]; },
-        [&](int k, int nn) { return k < D ? A1[k * M + nn] : dPQ[(k - D) * M + nn]; },
+        [&](int k, int nn) { return k < D ? A1[k * M + nn] : dPQ[(k - D) * XM + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) X(6)[(m0 + 4 * g + i) * M + nn] = acc[i] + a1[nn];
+          for (int i = 0; i < 4; ++i) X(6)[(m0 + 4 * g + i) * XM + nn] = acc[i] + a1[nn];
         });
     gemm_ks<NB, D, M + NB, 2>(
         wave, L.part[1][0],
-        [&](int s, int k) { return k < M ? A[s * M + k] : L.m[5][s][k - M]; },
+        [&](int s, int k) { return k < M ? A[s * XM + k] : L.m[5][s][k - M]; },
         [&](int k, int j) { return k < M ? A2[k * D + j] : DOq[(k - M) * YD + j]; },
         [&](int m0, int n0, f32x4 acc) {
           const int j = n0 + (lane & 15);
@@ -559,7 +568,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
         });
     gemm_ks<NB, D, M + NB, 2>(
         wave, L.part[0][0],
-        [&](int s, int k) { return k < M ? Gp[s * M + k] : L.m[6][s][k - M]; },
+        [&](int s, int k) { return k < M ? Gp[s * XM + k] : L.m[6][s][k - M]; },
         [&](int k, int f) { return k < M ? A1[f * M + k] : Q[(k - M) * YD + f]; },
         [&](int m0, int n0, f32x4 acc) {
           const int f = n0 + (lane & 15);
@@ -569,11 +578,11 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     gemm<NB, M, D + NB>(
         wave, 0, NWV,
         [&](int s, int k) { return k < D ? Go[s * YD + k] : L.m[7][s][k - D]; },
-        [&](int k, int nn) { return k < D ? A2[nn * D + k] : AQ[(k - D) * M + nn]; },
+        [&](int k, int nn) { return k < D ? A2[nn * D + k] : AQ[(k - D) * XM + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) X(7)[(m0 + 4 * g + i) * M + nn] = acc[i];
+          for (int i = 0; i < 4; ++i) X(7)[(m0 + 4 * g + i) * XM + nn] = acc[i];
         });
     __syncthreads();
     // deta = -rowsum(KA G_p) - rowsum(AA G_o); dU = -eta KA GELU'(P) -> X6;
@@ -581,15 +590,15 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     {
       const int s = 2 * wave + (lane >> 5), l32 = lane & 31;
       float acc = 0.f;
-      for (int nn = l32; nn < M; nn += 32) acc += X(6)[s * M + nn] * Gp[s * M + nn];
+      for (int nn = l32; nn < M; nn += 32) acc += X(6)[s * XM + nn] * Gp[s * XM + nn];
       for (int j = l32; j < D; j += 32) acc += Y(8)[s * YD + j] * Go[s * YD + j];
       acc = sum32(acc);
       const int tok = c * NB + s;
       if (l32 == 0 && tok < T) a.deta[row0 + tok] = -acc;
     }
     __syncthreads();
-    for (int e = tid; e < NB * M; e += NT) {
-      const int s = e / M;
+    for (int i = tid; i < NB * M; i += NT) {
+      const int s = i / M, e = s * XM + i % M;
       const float p = P[e];
       const float dgp = -L.eta[s] * X(6)[e];
       X(2)[e] = dgp * X(2)[e] * gelu2(p);
@@ -598,7 +607,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     __syncthreads();
     const float* dU = X(6);
     // dG_o = -eta AA + dU W2 -> Y8
-    gemm_ks<NB, D, M, 2>(wave, L.part[1][0], [&](int s, int k) { return dU[s * M + k]; },
+    gemm_ks<NB, D, M, 2>(wave, L.part[1][0], [&](int s, int k) { return dU[s * XM + k]; },
                    [&](int k, int j) { return W2[k * D + j]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int j = n0 + (lane & 15);
@@ -666,14 +675,14 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                      const int nn = n0 + (lane & 15);
 #pragma unroll
                      for (int i = 0; i < 4; ++i) {
-                       const int s = m0 + 4 * g + i, e = s * M + nn;
+                       const int s = m0 + 4 * g + i, e = s * XM + nn;
                        X(7)[e] = (acc[i] - L.eta[s] * X(7)[e]) * gelu1(P[e]) + X(2)[e];
                      }
                    });
     __syncthreads();
     const float* dP = X(7);
     // dK = dP W1^T - eta GA1 - res dt (stored)
-    gemm_ks<NB, D, M, 2>(wave, L.part[0][0], [&](int s, int k) { return dP[s * M + k]; },
+    gemm_ks<NB, D, M, 2>(wave, L.part[0][0], [&](int s, int k) { return dP[s * XM + k]; },
                    [&](int k, int f) { return W1[f * M + k]; },
                    [&](int m0, int n0, f32x4 acc) {
                      const int f = n0 + (lane & 15);
@@ -691,7 +700,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     gemm<D, M, 2 * NB>(
         wave, 0, NWV,
         [&](int f, int k) { return k < NB ? Q[k * YD + f] : K[(k - NB) * YD + f]; },
-        [&](int k, int nn) { return k < NB ? dPQ[k * M + nn] : dP[(k - NB) * M + nn]; },
+        [&](int k, int nn) { return k < NB ? dPQ[k * XM + nn] : dP[(k - NB) * XM + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
 #pragma unroll
@@ -700,7 +709,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     gemm<M, D, 3 * NB>(
         wave, 0, NWV,
         [&](int nn, int k) {
-          return k < NB ? AQ[k * M + nn] : (k < 2 * NB ? A[(k - NB) * M + nn] : dU[(k - 2 * NB) * M + nn]);
+          return k < NB ? AQ[k * XM + nn] : (k < 2 * NB ? A[(k - NB) * XM + nn] : dU[(k - 2 * NB) * XM + nn]);
         },
         [&](int k, int j) {
           return k < NB ? DOq[k * YD + j] : (k < 2 * NB ? dOk[(k - NB) * YD + j] : Go[(k - 2 * NB) * YD + j]);
@@ -717,8 +726,8 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
         float u[NB], w[NB];
 #pragma unroll
         for (int s = 0; s < NB; ++s) {
-          u[s] = dPQ[s * M + nn];
-          w[s] = dP[s * M + nn];
+          u[s] = dPQ[s * XM + nn];
+          w[s] = dP[s * XM + nn];
         }
         const float prev = adj[OB1 + nn];
 #pragma unroll
