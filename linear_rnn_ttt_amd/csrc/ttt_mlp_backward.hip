@@ -77,73 +77,151 @@ __device__ __forceinline__ f32x4 mfma4(float a, float b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
-// C[m][n] = sum_k a(m, k) b(k, n) for an R x C output (multiples of 16) over
-// K (multiple of 16): 16x16 tiles dealt to waves w0, w0 + nw, ... of the
-// workgroup; epi(m0, n0, acc) gets tile (m0, n0) with acc[i] at lane (g,c)
-// = C[m0 + 4g + i][n0 + c].  Operand fetches: a(m0 + c, k + g) and
-// b(k + g, n0 + c) for each group of 4 k, issued 16 k at a time ahead of
-// their four products.
-template <int R, int C, int K, class FA, class FB, class EPI>
-__device__ __forceinline__ void gemm(int wave, int w0, int nw, FA a, FB b, EPI epi) {
-  static_assert(R % 16 == 0 && C % 16 == 0 && K % 16 == 0, "tile multiples");
-  // lane indices behind an empty asm: the operand addresses derived from
-  // them are formed here, at each product, instead of being hoisted out of
-  // the mini-batch loop and held live in registers for every product site
-  int g = (threadIdx.x & 63) >> 4, c = threadIdx.x & 15;
+// Products C[m][n] = sum_k a(m, k) b(k, n) on 16x16 output tiles.  The
+// contraction is given as one or more stretches (Seg<K>: K values of k, a
+// multiple of 16, with their own a and b; k counts from 0 in each), so that
+// operands stacked from different arrays need no select per element.  In a
+// 16-k chunk lane (g, c) feeds a(m0 + c, k0 + 4g + j) and b(k0 + 4g + j,
+// n0 + c) to product j (j < 4): its four k are consecutive, so a row-major
+// operand is one 16-byte read.  The next chunk's operands are fetched before
+// the current chunk's four products.
+template <int K_, class FA, class FB>
+struct Seg {
+  static constexpr int K = K_;
+  FA a;
+  FB b;
+};
+template <int K, class FA, class FB>
+__device__ __forceinline__ Seg<K, FA, FB> seg(FA a, FB b) {
+  static_assert(K % 16 == 0 && K > 0, "stretches of whole 16-k chunks");
+  return Seg<K, FA, FB>{a, b};
+}
+
+template <class SG>
+__device__ __forceinline__ void fetch(const SG& sg, int m0, int n0, int g, int c, int k0, float* av,
+                                      float* bv) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    av[j] = sg.a(m0 + c, k0 + 4 * g + j);
+    bv[j] = sg.b(k0 + 4 * g + j, n0 + c);
+  }
+}
+
+// chunks first, first + step, ... of one stretch accumulated onto acc
+template <class SG>
+__device__ __forceinline__ void run_seg(const SG& sg, int m0, int n0, int g, int c, int first,
+                                        int step, f32x4& acc) {
+  constexpr int CH = SG::K / 16;
+  if (first >= CH) return;
+  float av[4], bv[4];
+  fetch(sg, m0, n0, g, c, 16 * first, av, bv);
+  int ch = first;
+#pragma unroll 1
+  for (; ch + step < CH; ch += step) {
+    float an[4], bn[4];
+    fetch(sg, m0, n0, g, c, 16 * (ch + step), an, bn);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      av[j] = an[j];
+      bv[j] = bn[j];
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
+}
+
+// lane indices behind an empty asm: the operand addresses derived from them
+// are formed at each product instead of being hoisted out of the mini-batch
+// loop and held live in registers for every product site
+__device__ __forceinline__ void lane_gc(int& g, int& c) {
+  g = (threadIdx.x & 63) >> 4;
+  c = threadIdx.x & 15;
   asm volatile("" : "+v"(g), "+v"(c));
+}
+
+// R x C output (multiples of 16): tiles dealt to waves w0, w0 + nw, ... of
+// the workgroup, tile (m0, n0) ending in epi(m0, n0, acc, pre), acc[i] at
+// lane (g, c) being C[m0 + 4g + i][n0 + c] and pre = pre(m0, n0) a value the
+// epilogue needs from memory (the old state or adjoint tile), fetched one
+// tile ahead.
+template <int R, int C, class PRE, class EPI, class... SG>
+__device__ __forceinline__ void gemm_p(int wave, int w0, int nw, PRE pre, EPI epi,
+                                       const SG&... sg) {
+  static_assert(R % 16 == 0 && C % 16 == 0, "tile multiples");
+  int g, c;
+  lane_gc(g, c);
   constexpr int TN = C / 16, TILES = (R / 16) * TN;
   if (wave < w0 || wave >= w0 + nw) return;
+  int t = wave - w0;
+  f32x4 nxt = pre((t / TN) * 16, (t % TN) * 16);
 #pragma unroll 1
-  for (int t = wave - w0; t < TILES; t += nw) {
+  for (; t < TILES; t += nw) {
     const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+    const f32x4 cur = nxt;
+    const int tn = t + nw < TILES ? t + nw : t;
+    nxt = pre((tn / TN) * 16, (tn % TN) * 16);
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 1
-    for (int k0 = 0; k0 < K; k0 += 16) {
-      float av[4], bv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        av[j] = a(m0 + c, k0 + 4 * g + j);
-        bv[j] = b(k0 + 4 * g + j, n0 + c);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
-    }
-    epi(m0, n0, acc);
+    (run_seg(sg, m0, n0, g, c, 0, 1, acc), ...);
+    epi(m0, n0, acc, cur);
   }
+}
+
+struct Zero {
+  __device__ f32x4 operator()(int, int) const { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+};
+
+template <int R, int C, class EPI, class... SG>
+__device__ __forceinline__ void gemm_s(int wave, int w0, int nw, EPI epi, const SG&... sg) {
+  gemm_p<R, C>(
+      wave, w0, nw, Zero{}, [&](int m0, int n0, f32x4 acc, f32x4) { epi(m0, n0, acc); }, sg...);
+}
+
+template <int R, int C, int K, class FA, class FB, class EPI>
+__device__ __forceinline__ void gemm(int wave, int w0, int nw, FA a, FB b, EPI epi) {
+  gemm_s<R, C>(wave, w0, nw, epi, seg<K>(a, b));
 }
 
 // The same product with the contraction split over S waves per output tile,
 // for products of few tiles (TILES * S <= 8 waves): wave w takes tile
-// w % TILES and the 16-k chunks w / TILES, w / TILES + S, ...; the partial
-// tiles meet in `part` (LDS, (S - 1) * TILES tiles) and the first wave of
-// each tile adds them up and runs epi.  Every wave of the workgroup must
-// call it (it holds a barrier).  Consecutive calls alternate between two
-// `part` buffers, so a buffer is written again only after a later barrier
-// that follows its reads.
-template <int R, int C, int K, int S, class FA, class FB, class EPI>
-__device__ __forceinline__ void gemm_ks(int wave, f32x4* part, FA a, FB b, EPI epi) {
-  static_assert(R % 16 == 0 && C % 16 == 0 && K % 16 == 0, "tile multiples");
-  constexpr int TN = C / 16, TILES = (R / 16) * TN, CH = K / 16;
+// w % TILES and the 16-k chunks (counted over all stretches) w / TILES,
+// w / TILES + S, ...; the partial tiles meet in `part` (LDS, (S - 1) * TILES
+// tiles) and the first wave of each tile adds them up and runs epi.  Every
+// wave of the workgroup must call it (it holds a barrier).  Consecutive
+// calls alternate between two `part` buffers, so a buffer is written again
+// only after a later barrier that follows its reads.
+template <int CB, int S, class SG>
+__device__ __forceinline__ void run_seg_ks(const SG& sg, int m0, int n0, int g, int c, int p,
+                                           f32x4& acc) {
+  // first local chunk whose global index CB + l is p mod S
+  const int first = ((p - CB) % S + S) % S;
+  run_seg(sg, m0, n0, g, c, first, S, acc);
+}
+template <int R, int C, int S, class EPI, class SG0>
+__device__ __forceinline__ void ks_body(int p, int m0, int n0, int g, int c, f32x4& acc,
+                                        const SG0& s0) {
+  run_seg_ks<0, S>(s0, m0, n0, g, c, p, acc);
+}
+template <int R, int C, int S, class EPI, class SG0, class SG1>
+__device__ __forceinline__ void ks_body(int p, int m0, int n0, int g, int c, f32x4& acc,
+                                        const SG0& s0, const SG1& s1) {
+  run_seg_ks<0, S>(s0, m0, n0, g, c, p, acc);
+  run_seg_ks<SG0::K / 16, S>(s1, m0, n0, g, c, p, acc);
+}
+template <int R, int C, int S, class EPI, class... SG>
+__device__ __forceinline__ void gemm_kss(int wave, f32x4* part, EPI epi, const SG&... sg) {
+  static_assert(R % 16 == 0 && C % 16 == 0, "tile multiples");
+  constexpr int TN = C / 16, TILES = (R / 16) * TN;
   static_assert(TILES * S <= NWV && S >= 1, "one wave per tile and part");
-  int g = (threadIdx.x & 63) >> 4, c = threadIdx.x & 15;
-  asm volatile("" : "+v"(g), "+v"(c));
+  int g, c;
+  lane_gc(g, c);
   const int lane = threadIdx.x & 63;
   const int t = wave % TILES, p = wave / TILES;
   const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
   if (p < S) {
-#pragma unroll 1
-    for (int ch = p; ch < CH; ch += S) {
-      const int k0 = 16 * ch;
-      float av[4], bv[4];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        av[j] = a(m0 + c, k0 + 4 * g + j);
-        bv[j] = b(k0 + 4 * g + j, n0 + c);
-      }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
-    }
+    ks_body<R, C, S, EPI>(p, m0, n0, g, c, acc, sg...);
     if (p > 0) part[((p - 1) * TILES + t) * 64 + lane] = acc;
   }
   __syncthreads();
@@ -152,6 +230,23 @@ __device__ __forceinline__ void gemm_ks(int wave, f32x4* part, FA a, FB b, EPI e
     for (int q = 1; q < S; ++q) acc += part[((q - 1) * TILES + t) * 64 + lane];
     epi(m0, n0, acc);
   }
+}
+template <int R, int C, int K, int S, class FA, class FB, class EPI>
+__device__ __forceinline__ void gemm_ks(int wave, f32x4* part, FA a, FB b, EPI epi) {
+  gemm_kss<R, C, S>(wave, part, epi, seg<K>(a, b));
+}
+
+// two stretches: a1, a2, b1, b2, epi
+template <int R, int C, int K1, int K2, class FA1, class FA2, class FB1, class FB2, class EPI>
+__device__ __forceinline__ void gemm2(int wave, int w0, int nw, FA1 a1, FA2 a2, FB1 b1, FB2 b2,
+                                      EPI epi) {
+  gemm_s<R, C>(wave, w0, nw, epi, seg<K1>(a1, b1), seg<K2>(a2, b2));
+}
+template <int R, int C, int K1, int K2, int S, class FA1, class FA2, class FB1, class FB2,
+          class EPI>
+__device__ __forceinline__ void gemm_ks2(int wave, f32x4* part, FA1 a1, FA2 a2, FB1 b1, FB2 b2,
+                                         EPI epi) {
+  gemm_kss<R, C, S>(wave, part, epi, seg<K1>(a1, b1), seg<K2>(a2, b2));
 }
 
 // Sum over the 32 lanes of a half-wave.
@@ -205,7 +300,10 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, g = lane >> 4;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int T = a.T, n = (T + 15) / 16;
-  float* ws = a.ws + static_cast<size_t>(unit) * a.unit_floats;
+  // 16-byte aligned: the workspace starts on 256 bytes and unit_floats is a
+  // multiple of 4, so row-major state reads can be 16-byte loads
+  float* ws = static_cast<float*>(
+      __builtin_assume_aligned(a.ws + static_cast<size_t>(unit) * a.unit_floats, 16));
   float* bases = ws;
   float* adj = ws + static_cast<size_t>(n) * SZ;
   float* Xb = adj + SZ;
@@ -338,26 +436,36 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     float* Sn = bases + static_cast<size_t>(c + 1) * SZ;
     kside(S);
     // W1' = W1 - K^T (eta G_p), W2' = W2 - A^T (eta G_o)
-    gemm<D, M, NB>(wave, 0, NWV, [&](int f, int s) { return Y(0)[s * YD + f]; },
-                   [&](int s, int nn) { return L.eta[s] * X(3)[s * XM + nn]; },
-                   [&](int m0, int n0, f32x4 acc) {
-                     const int nn = n0 + (lane & 15);
+    // (the old tile of S is fetched one tile ahead)
+    gemm_p<D, M>(
+        wave, 0, NWV,
+        [&](int m0, int n0) {
+          f32x4 v;
 #pragma unroll
-                     for (int i = 0; i < 4; ++i) {
-                       const int e = (m0 + 4 * g + i) * M + nn;
-                       Sn[e] = S[e] - acc[i];
-                     }
-                   });
-    gemm<M, D, NB>(wave, 0, NWV, [&](int nn, int s) { return X(1)[s * XM + nn]; },
-                   [&](int s, int j) { return L.eta[s] * Y(6)[s * YD + j]; },
-                   [&](int m0, int n0, f32x4 acc) {
-                     const int j = n0 + (lane & 15);
+          for (int i = 0; i < 4; ++i) v[i] = S[(m0 + 4 * g + i) * M + n0 + (lane & 15)];
+          return v;
+        },
+        [&](int m0, int n0, f32x4 acc, f32x4 old) {
 #pragma unroll
-                     for (int i = 0; i < 4; ++i) {
-                       const int e = OW2 + (m0 + 4 * g + i) * D + j;
-                       Sn[e] = S[e] - acc[i];
-                     }
-                   });
+          for (int i = 0; i < 4; ++i) Sn[(m0 + 4 * g + i) * M + n0 + (lane & 15)] = old[i] - acc[i];
+        },
+        seg<NB>([&](int f, int s) { return Y(0)[s * YD + f]; },
+                [&](int s, int nn) { return L.eta[s] * X(3)[s * XM + nn]; }));
+    gemm_p<M, D>(
+        wave, 0, NWV,
+        [&](int m0, int n0) {
+          f32x4 v;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = S[OW2 + (m0 + 4 * g + i) * D + n0 + (lane & 15)];
+          return v;
+        },
+        [&](int m0, int n0, f32x4 acc, f32x4 old) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            Sn[OW2 + (m0 + 4 * g + i) * D + n0 + (lane & 15)] = old[i] - acc[i];
+        },
+        seg<NB>([&](int nn, int s) { return X(1)[s * XM + nn]; },
+                [&](int s, int j) { return L.eta[s] * Y(6)[s * YD + j]; }));
     for (int nn = tid; nn < M + D; nn += NT) {
       float sum = 0.f;
       if (nn < M) {
@@ -401,10 +509,12 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                     });
     __syncthreads();
     // PQ = Q W1 + b1 - M1 G_p -> X4, AQ = GELU(PQ) -> X5
-    gemm<NB, M, D + NB>(
+    gemm2<NB, M, D, NB>(
         wave, 0, NWV,
-        [&](int i, int k) { return k < D ? Q[i * YD + k] : -L.m[0][i][k - D]; },
-        [&](int k, int nn) { return k < D ? W1[k * M + nn] : Gp[(k - D) * XM + nn]; },
+        [&](int i, int k) { return Q[i * YD + k]; },
+        [&](int i, int k) { return -L.m[0][i][k]; },
+        [&](int k, int nn) { return W1[k * M + nn]; },
+        [&](int k, int nn) { return Gp[k * XM + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
 #pragma unroll
@@ -426,10 +536,12 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                     });
     __syncthreads();
     // OQ = AQ W2 + b2 - M2 G_o -> Y7
-    gemm_ks<NB, D, M + NB, 2>(
+    gemm_ks2<NB, D, M, NB, 2>(
         wave, L.part[1][0],
-        [&](int i, int k) { return k < M ? AQ[i * XM + k] : -L.m[1][i][k - M]; },
-        [&](int k, int j) { return k < M ? W2[k * D + j] : Go[(k - M) * YD + j]; },
+        [&](int i, int k) { return AQ[i * XM + k]; },
+        [&](int i, int k) { return -L.m[1][i][k]; },
+        [&](int k, int j) { return W2[k * D + j]; },
+        [&](int k, int j) { return Go[k * YD + j]; },
         [&](int m0, int n0, f32x4 acc) {
           const int j = n0 + (lane & 15);
 #pragma unroll
@@ -479,10 +591,12 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                     });
     __syncthreads();
     // dPQ = (DOq W2^T - Mdo A) GELU'(PQ) -> X4
-    gemm<NB, M, D + NB>(
+    gemm2<NB, M, D, NB>(
         wave, 0, NWV,
-        [&](int i, int k) { return k < D ? DOq[i * YD + k] : -L.m[2][i][k - D]; },
-        [&](int k, int nn) { return k < D ? W2[nn * D + k] : A[(k - D) * XM + nn]; },
+        [&](int i, int k) { return DOq[i * YD + k]; },
+        [&](int i, int k) { return -L.m[2][i][k]; },
+        [&](int k, int nn) { return W2[nn * D + k]; },
+        [&](int k, int nn) { return A[k * XM + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
 #pragma unroll
@@ -535,10 +649,12 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     // dQ = res dz + dPQ W1^T - Mdp K (stored); KA = K A1 + a1 + Tk dPQ -> X6;
     // AA = A A2 + a2 + Ta DOq -> Y8; GA1 = G_p A1^T + Tgp Q -> Y9;
     // GA2 = G_o A2^T + Tgo AQ -> X7
-    gemm_ks<NB, D, M + NB, 2>(
+    gemm_ks2<NB, D, M, NB, 2>(
         wave, L.part[0][0],
-        [&](int i, int k) { return k < M ? dPQ[i * XM + k] : -L.m[3][i][k - M]; },
-        [&](int k, int f) { return k < M ? W1[f * M + k] : K[(k - M) * YD + f]; },
+        [&](int i, int k) { return dPQ[i * XM + k]; },
+        [&](int i, int k) { return -L.m[3][i][k]; },
+        [&](int k, int f) { return W1[f * M + k]; },
+        [&](int k, int f) { return K[k * YD + f]; },
         [&](int m0, int n0, f32x4 acc) {
           const int f = n0 + (lane & 15);
 #pragma unroll
@@ -548,37 +664,45 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
             if (tok < T) st_io<BF16>(a.dq, (row0 + tok) * D + f, v);
           }
         });
-    gemm<NB, M, D + NB>(
+    gemm2<NB, M, D, NB>(
         wave, 0, NWV,
-        [&](int s, int k) { return k < D ? K[s * YD + k] : L.m[4][s][k - D]; },
-        [&](int k, int nn) { return k < D ? A1[k * M + nn] : dPQ[(k - D) * XM + nn]; },
+        [&](int s, int k) { return K[s * YD + k]; },
+        [&](int s, int k) { return L.m[4][s][k]; },
+        [&](int k, int nn) { return A1[k * M + nn]; },
+        [&](int k, int nn) { return dPQ[k * XM + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i) X(6)[(m0 + 4 * g + i) * XM + nn] = acc[i] + a1[nn];
         });
-    gemm_ks<NB, D, M + NB, 2>(
+    gemm_ks2<NB, D, M, NB, 2>(
         wave, L.part[1][0],
-        [&](int s, int k) { return k < M ? A[s * XM + k] : L.m[5][s][k - M]; },
-        [&](int k, int j) { return k < M ? A2[k * D + j] : DOq[(k - M) * YD + j]; },
+        [&](int s, int k) { return A[s * XM + k]; },
+        [&](int s, int k) { return L.m[5][s][k]; },
+        [&](int k, int j) { return A2[k * D + j]; },
+        [&](int k, int j) { return DOq[k * YD + j]; },
         [&](int m0, int n0, f32x4 acc) {
           const int j = n0 + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i) Y(8)[(m0 + 4 * g + i) * YD + j] = acc[i] + a2[j];
         });
-    gemm_ks<NB, D, M + NB, 2>(
+    gemm_ks2<NB, D, M, NB, 2>(
         wave, L.part[0][0],
-        [&](int s, int k) { return k < M ? Gp[s * XM + k] : L.m[6][s][k - M]; },
-        [&](int k, int f) { return k < M ? A1[f * M + k] : Q[(k - M) * YD + f]; },
+        [&](int s, int k) { return Gp[s * XM + k]; },
+        [&](int s, int k) { return L.m[6][s][k]; },
+        [&](int k, int f) { return A1[f * M + k]; },
+        [&](int k, int f) { return Q[k * YD + f]; },
         [&](int m0, int n0, f32x4 acc) {
           const int f = n0 + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i) Y(9)[(m0 + 4 * g + i) * YD + f] = acc[i];
         });
-    gemm<NB, M, D + NB>(
+    gemm2<NB, M, D, NB>(
         wave, 0, NWV,
-        [&](int s, int k) { return k < D ? Go[s * YD + k] : L.m[7][s][k - D]; },
-        [&](int k, int nn) { return k < D ? A2[nn * D + k] : AQ[(k - D) * XM + nn]; },
+        [&](int s, int k) { return Go[s * YD + k]; },
+        [&](int s, int k) { return L.m[7][s][k]; },
+        [&](int k, int nn) { return A2[nn * D + k]; },
+        [&](int k, int nn) { return AQ[k * XM + nn]; },
         [&](int m0, int n0, f32x4 acc) {
           const int nn = n0 + (lane & 15);
 #pragma unroll
@@ -697,28 +821,40 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     // A1 += Q^T dPQ + K^T dP;  A2 += AQ^T DOq + A^T dO + dU^T G_o
     float* A1w = adj;
     float* A2w = adj + OW2;
-    gemm<D, M, 2 * NB>(
+    gemm_p<D, M>(
         wave, 0, NWV,
-        [&](int f, int k) { return k < NB ? Q[k * YD + f] : K[(k - NB) * YD + f]; },
-        [&](int k, int nn) { return k < NB ? dPQ[k * XM + nn] : dP[(k - NB) * XM + nn]; },
-        [&](int m0, int n0, f32x4 acc) {
-          const int nn = n0 + (lane & 15);
+        [&](int m0, int n0) {
+          f32x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) A1w[(m0 + 4 * g + i) * M + nn] += acc[i];
-        });
-    gemm<M, D, 3 * NB>(
+          for (int i = 0; i < 4; ++i) v[i] = A1w[(m0 + 4 * g + i) * M + n0 + (lane & 15)];
+          return v;
+        },
+        [&](int m0, int n0, f32x4 acc, f32x4 old) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) A1w[(m0 + 4 * g + i) * M + n0 + (lane & 15)] = old[i] + acc[i];
+        },
+        seg<NB>([&](int f, int k) { return Q[k * YD + f]; },
+                [&](int k, int nn) { return dPQ[k * XM + nn]; }),
+        seg<NB>([&](int f, int k) { return K[k * YD + f]; },
+                [&](int k, int nn) { return dP[k * XM + nn]; }));
+    gemm_p<M, D>(
         wave, 0, NWV,
-        [&](int nn, int k) {
-          return k < NB ? AQ[k * XM + nn] : (k < 2 * NB ? A[(k - NB) * XM + nn] : dU[(k - 2 * NB) * XM + nn]);
-        },
-        [&](int k, int j) {
-          return k < NB ? DOq[k * YD + j] : (k < 2 * NB ? dOk[(k - NB) * YD + j] : Go[(k - 2 * NB) * YD + j]);
-        },
-        [&](int m0, int n0, f32x4 acc) {
-          const int j = n0 + (lane & 15);
+        [&](int m0, int n0) {
+          f32x4 v;
 #pragma unroll
-          for (int i = 0; i < 4; ++i) A2w[(m0 + 4 * g + i) * D + j] += acc[i];
-        });
+          for (int i = 0; i < 4; ++i) v[i] = A2w[(m0 + 4 * g + i) * D + n0 + (lane & 15)];
+          return v;
+        },
+        [&](int m0, int n0, f32x4 acc, f32x4 old) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) A2w[(m0 + 4 * g + i) * D + n0 + (lane & 15)] = old[i] + acc[i];
+        },
+        seg<NB>([&](int nn, int k) { return AQ[k * XM + nn]; },
+                [&](int k, int j) { return DOq[k * YD + j]; }),
+        seg<NB>([&](int nn, int k) { return A[k * XM + nn]; },
+                [&](int k, int j) { return dOk[k * YD + j]; }),
+        seg<NB>([&](int nn, int k) { return dU[k * XM + nn]; },
+                [&](int k, int j) { return Go[k * YD + j]; }));
     for (int nn = tid; nn < M + D; nn += NT) {
       float sum = 0.f;
       if (nn < M) {
