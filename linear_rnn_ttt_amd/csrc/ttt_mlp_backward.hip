@@ -107,29 +107,66 @@ __device__ __forceinline__ void fetch(const SG& sg, int m0, int n0, int g, int c
   }
 }
 
-// chunks first, first + step, ... of one stretch accumulated onto acc
+template <int G, class SG>
+__device__ __forceinline__ void fetch_g(const SG& sg, int m0, int n0, int g, int c, int k0, int kd,
+                                        float (&av)[G][4], float (&bv)[G][4]) {
+#pragma unroll
+  for (int q = 0; q < G; ++q) fetch(sg, m0, n0, g, c, k0 + q * kd, av[q], bv[q]);
+  // keep the group's loads ahead of the products that follow: left alone,
+  // the scheduler sinks each load next to its product, one round trip each
+  __builtin_amdgcn_sched_barrier(0);
+}
+template <int G>
+__device__ __forceinline__ void mma_g(const float (&av)[G][4], const float (&bv)[G][4], f32x4& acc) {
+#pragma unroll
+  for (int q = 0; q < G; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma4(av[q][j], bv[q][j], acc);
+}
+
+// chunks first, first + step, ... of one stretch accumulated onto acc, in
+// groups of G chunks whose operands are fetched together (one memory round
+// trip per group).  Two register sets take turns, every fetch in the loop
+// is unconditional and the loop head sees the same fetches in flight on
+// every entry, so each group's products wait only for that group's operands
+// (a conditional fetch, or copying one set into the other, makes the
+// compiler wait for all).
 template <class SG>
 __device__ __forceinline__ void run_seg(const SG& sg, int m0, int n0, int g, int c, int first,
                                         int step, f32x4& acc) {
   constexpr int CH = SG::K / 16;
+  constexpr int G = CH < 4 ? CH : 4;
   if (first >= CH) return;
-  float av[4], bv[4];
-  fetch(sg, m0, n0, g, c, 16 * first, av, bv);
-  int ch = first;
+  const int nch = (CH - first + step - 1) / step;   // chunks of this wave
+  const int ngr = nch / G, rem = nch - ngr * G;
+  const int kd = 16 * step;                         // k between a wave's chunks
+  int k0 = 16 * first;
+  if (ngr > 0) {
+    float a0[G][4], b0[G][4], a1[G][4], b1[G][4];
+    fetch_g<G>(sg, m0, n0, g, c, k0, kd, a0, b0);
+    int i = 0;
 #pragma unroll 1
-  for (; ch + step < CH; ch += step) {
-    float an[4], bn[4];
-    fetch(sg, m0, n0, g, c, 16 * (ch + step), an, bn);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      av[j] = an[j];
-      bv[j] = bn[j];
+    for (; i + 2 < ngr; i += 2) {
+      fetch_g<G>(sg, m0, n0, g, c, k0 + (i + 1) * G * kd, kd, a1, b1);
+      mma_g<G>(a0, b0, acc);
+      fetch_g<G>(sg, m0, n0, g, c, k0 + (i + 2) * G * kd, kd, a0, b0);
+      mma_g<G>(a1, b1, acc);
     }
+    if (ngr - i == 2) {
+      fetch_g<G>(sg, m0, n0, g, c, k0 + (i + 1) * G * kd, kd, a1, b1);
+      mma_g<G>(a0, b0, acc);
+      mma_g<G>(a1, b1, acc);
+    } else {
+      mma_g<G>(a0, b0, acc);
+    }
+    k0 += ngr * G * kd;
   }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) acc = mfma4(av[j], bv[j], acc);
+#pragma unroll 1
+  for (int r = 0; r < rem; ++r) {
+    float av[1][4], bv[1][4];
+    fetch_g<1>(sg, m0, n0, g, c, k0 + r * kd, kd, av, bv);
+    mma_g<1>(av, bv, acc);
+  }
 }
 
 // lane indices behind an empty asm: the operand addresses derived from them
@@ -141,11 +178,55 @@ __device__ __forceinline__ void lane_gc(int& g, int& c) {
   asm volatile("" : "+v"(g), "+v"(c));
 }
 
+// The same for the row-wise passes: an index derived from the thread id is
+// taken through an empty asm where a pass starts, so the LDS addresses of
+// that pass are formed there (the per-row offsets folding into the
+// instructions) instead of being hoisted, one register each, out of the
+// mini-batch loop.
+__device__ __forceinline__ int opaque(int x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+
+// Operand registers of one tile's whole contraction (every stretch at most
+// 64 deep, i.e. one group): fetched together, one round trip per tile.
+template <class... SG>
+struct Bufs;
+template <>
+struct Bufs<> {};
+template <class S0, class... R>
+struct Bufs<S0, R...> {
+  static constexpr int CH = S0::K / 16;
+  float a[CH][4], b[CH][4];
+  Bufs<R...> rest;
+};
+__device__ __forceinline__ void fetch_all(Bufs<>&, int, int, int, int) {}
+template <class S0, class... R>
+__device__ __forceinline__ void fetch_all(Bufs<S0, R...>& bf, int m0, int n0, int g, int c,
+                                          const S0& s0, const R&... r) {
+#pragma unroll
+  for (int q = 0; q < Bufs<S0, R...>::CH; ++q) fetch(s0, m0, n0, g, c, 16 * q, bf.a[q], bf.b[q]);
+  fetch_all(bf.rest, m0, n0, g, c, r...);
+}
+__device__ __forceinline__ void mma_all(const Bufs<>&, f32x4&) {}
+template <class S0, class... R>
+__device__ __forceinline__ void mma_all(const Bufs<S0, R...>& bf, f32x4& acc) {
+#pragma unroll
+  for (int q = 0; q < Bufs<S0, R...>::CH; ++q)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc = mfma4(bf.a[q][j], bf.b[q][j], acc);
+  mma_all(bf.rest, acc);
+}
+
 // R x C output (multiples of 16): tiles dealt to waves w0, w0 + nw, ... of
 // the workgroup, tile (m0, n0) ending in epi(m0, n0, acc, pre), acc[i] at
 // lane (g, c) being C[m0 + 4g + i][n0 + c] and pre = pre(m0, n0) a value the
-// epilogue needs from memory (the old state or adjoint tile), fetched one
-// tile ahead.
+// epilogue needs from memory (the old state or adjoint tile, or workspace
+// intermediates), fetched one tile ahead.  When every stretch is at most 64
+// deep, a tile's operands are fetched in one go, and with few operand
+// registers (at most 24) the next tile's operands and pre are fetched while
+// the current tile's products run (two register sets, tiles in pairs; the
+// last fetch repeats the last tile).
 template <int R, int C, class PRE, class EPI, class... SG>
 __device__ __forceinline__ void gemm_p(int wave, int w0, int nw, PRE pre, EPI epi,
                                        const SG&... sg) {
@@ -153,18 +234,59 @@ __device__ __forceinline__ void gemm_p(int wave, int w0, int nw, PRE pre, EPI ep
   int g, c;
   lane_gc(g, c);
   constexpr int TN = C / 16, TILES = (R / 16) * TN;
+  constexpr bool SMALL = ((SG::K <= 64) && ...);
+  constexpr int REGS = ((SG::K / 2) + ...);   // operand floats per lane and tile
   if (wave < w0 || wave >= w0 + nw) return;
-  int t = wave - w0;
-  f32x4 nxt = pre((t / TN) * 16, (t % TN) * 16);
+  const int t0 = wave - w0;
+  if constexpr (SMALL && REGS <= 24) {
+    const int nt = (TILES - t0 + nw - 1) / nw;   // tiles of this wave
+    auto tm = [&](int i) { return ((t0 + min(i, nt - 1) * nw) / TN) * 16; };
+    auto tn = [&](int i) { return ((t0 + min(i, nt - 1) * nw) % TN) * 16; };
+    Bufs<SG...> A, B;
+    auto pa = pre(tm(0), tn(0));
+    fetch_all(A, tm(0), tn(0), g, c, sg...);
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll 1
-  for (; t < TILES; t += nw) {
-    const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
-    const f32x4 cur = nxt;
-    const int tn = t + nw < TILES ? t + nw : t;
-    nxt = pre((tn / TN) * 16, (tn % TN) * 16);
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    (run_seg(sg, m0, n0, g, c, 0, 1, acc), ...);
-    epi(m0, n0, acc, cur);
+    for (int i = 0; i < nt; i += 2) {
+      auto pb = pre(tm(i + 1), tn(i + 1));
+      fetch_all(B, tm(i + 1), tn(i + 1), g, c, sg...);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      mma_all(A, acc);
+      epi(tm(i), tn(i), acc, pa);
+      if (i + 1 >= nt) break;
+      pa = pre(tm(i + 2), tn(i + 2));
+      fetch_all(A, tm(i + 2), tn(i + 2), g, c, sg...);
+      __builtin_amdgcn_sched_barrier(0);
+      acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      mma_all(B, acc);
+      epi(tm(i + 1), tn(i + 1), acc, pb);
+    }
+  } else if constexpr (SMALL) {
+#pragma unroll 1
+    for (int t = t0; t < TILES; t += nw) {
+      const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+      const auto pv = pre(m0, n0);
+      Bufs<SG...> A;
+      fetch_all(A, m0, n0, g, c, sg...);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      mma_all(A, acc);
+      epi(m0, n0, acc, pv);
+    }
+  } else {
+    int t = t0;
+    auto nxt = pre((t / TN) * 16, (t % TN) * 16);
+#pragma unroll 1
+    for (; t < TILES; t += nw) {
+      const int m0 = (t / TN) * 16, n0 = (t % TN) * 16;
+      const auto cur = nxt;
+      const int tq = t + nw < TILES ? t + nw : t;
+      nxt = pre((tq / TN) * 16, (tq % TN) * 16);
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      (run_seg(sg, m0, n0, g, c, 0, 1, acc), ...);
+      epi(m0, n0, acc, cur);
+    }
   }
 }
 
@@ -175,7 +297,8 @@ struct Zero {
 template <int R, int C, class EPI, class... SG>
 __device__ __forceinline__ void gemm_s(int wave, int w0, int nw, EPI epi, const SG&... sg) {
   gemm_p<R, C>(
-      wave, w0, nw, Zero{}, [&](int m0, int n0, f32x4 acc, f32x4) { epi(m0, n0, acc); }, sg...);
+      wave, w0, nw, Zero{}, [&](int m0, int n0, f32x4 acc, const f32x4&) { epi(m0, n0, acc); },
+      sg...);
 }
 
 template <int R, int C, int K, class FA, class FB, class EPI>
@@ -333,7 +456,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
   // inputs of tile c as fp32 rows (zero past T): K -> Y0, Q -> Y1, V -> Y2,
   // dz -> Y3 (with_dz), eta -> LDS (zero past T)
   auto load_tile = [&](int c, bool with_dz) {
-    for (int i = tid; i < NB * D; i += NT) {
+    for (int i = opaque(tid); i < NB * D; i += NT) {
       const int s = i / D, f = i % D, tok = c * NB + s;
       const bool ok = tok < T;
       const size_t e = (row0 + tok) * D + f;
@@ -376,7 +499,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     // LN of O and the loss gradient G_o: wave w has tokens 2w, 2w+1; lane
     // half h, feature pair 2(l % 32), +1
     {
-      const int s = 2 * wave + (lane >> 5), f = 2 * (lane & 31);
+      const int ol = opaque(lane), s = 2 * wave + (ol >> 5), f = 2 * (ol & 31);
       float o[2], t[2], x[2], av[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -414,17 +537,25 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     }
     __syncthreads();
     // U = G_o W2^T, G_p = U GELU'(P)
-    gemm<NB, M, D>(wave, 0, NWV, [&](int m, int k) { return Y(6)[m * YD + k]; },
-                   [&](int k, int nn) { return W2[nn * D + k]; },
-                   [&](int m0, int n0, f32x4 acc) {
-                     const int nn = n0 + (lane & 15);
+    gemm_p<NB, M>(
+        wave, 0, NWV,
+        [&](int m0, int n0) {   // P of the tile, from the workspace
+          f32x4 v;
 #pragma unroll
-                     for (int i = 0; i < 4; ++i) {
-                       const int e = (m0 + 4 * g + i) * XM + nn;
-                       X(2)[e] = acc[i];
-                       X(3)[e] = acc[i] * gelu1(X(0)[e]);
-                     }
-                   });
+          for (int i = 0; i < 4; ++i) v[i] = X(0)[(m0 + 4 * g + i) * XM + n0 + (lane & 15)];
+          return v;
+        },
+        [&](int m0, int n0, f32x4 acc, const f32x4& pv) {
+          const int nn = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int e = (m0 + 4 * g + i) * XM + nn;
+            X(2)[e] = acc[i];
+            X(3)[e] = acc[i] * gelu1(pv[i]);
+          }
+        },
+        seg<D>([&](int m, int k) { return Y(6)[m * YD + k]; },
+               [&](int k, int nn) { return W2[nn * D + k]; }));
     __syncthreads();
   };
 
@@ -466,7 +597,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
         },
         seg<NB>([&](int nn, int s) { return X(1)[s * XM + nn]; },
                 [&](int s, int j) { return L.eta[s] * Y(6)[s * YD + j]; }));
-    for (int nn = tid; nn < M + D; nn += NT) {
+    for (int nn = opaque(tid); nn < M + D; nn += NT) {
       float sum = 0.f;
       if (nn < M) {
         for (int s = 0; s < NB; ++s) sum += L.eta[s] * X(3)[s * XM + nn];
@@ -550,7 +681,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     __syncthreads();
     // output LN backward: DOq -> Y7; dgamma, dbeta
     {
-      const int s = 2 * wave + (lane >> 5), f = 2 * (lane & 31);
+      const int ol = opaque(lane), s = 2 * wave + (ol >> 5), f = 2 * (ol & 31);
       float o[2], dz[2];
 #pragma unroll
       for (int u = 0; u < 2; ++u) {
@@ -712,7 +843,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     // deta = -rowsum(KA G_p) - rowsum(AA G_o); dU = -eta KA GELU'(P) -> X6;
     // -eta KA U GELU''(P) -> X2
     {
-      const int s = 2 * wave + (lane >> 5), l32 = lane & 31;
+      const int ol = opaque(lane), s = 2 * wave + (ol >> 5), l32 = ol & 31;
       float acc = 0.f;
       for (int nn = l32; nn < M; nn += 32) acc += X(6)[s * XM + nn] * Gp[s * XM + nn];
       for (int j = l32; j < D; j += 32) acc += Y(8)[s * YD + j] * Go[s * YD + j];
@@ -721,12 +852,26 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
       if (l32 == 0 && tok < T) a.deta[row0 + tok] = -acc;
     }
     __syncthreads();
-    for (int i = tid; i < NB * M; i += NT) {
-      const int s = i / M, e = s * XM + i % M;
-      const float p = P[e];
-      const float dgp = -L.eta[s] * X(6)[e];
-      X(2)[e] = dgp * X(2)[e] * gelu2(p);
-      X(6)[e] = dgp * gelu1(p);
+    {
+      // all 24 workspace loads in flight before the arithmetic
+      static_assert(NB * M == 8 * NT, "eight elements per thread");
+      const int i0 = opaque(tid);
+      float pv[8], kv[8], uv[8];
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = i0 + r * NT, e = (i / M) * XM + i % M;
+        pv[r] = P[e];
+        kv[r] = X(6)[e];
+        uv[r] = X(2)[e];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int r = 0; r < 8; ++r) {
+        const int i = i0 + r * NT, s = i / M, e = s * XM + i % M;
+        const float dgp = -L.eta[s] * kv[r];
+        X(2)[e] = dgp * uv[r] * gelu2(pv[r]);
+        X(6)[e] = dgp * gelu1(pv[r]);
+      }
     }
     __syncthreads();
     const float* dU = X(6);
@@ -744,7 +889,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     __syncthreads();
     // LN-gradient backward: dO -> Y10, dt -> Y11 (dv stored), dgamma, dbeta
     {
-      const int s = 2 * wave + (lane >> 5), f = 2 * (lane & 31);
+      const int ol = opaque(lane), s = 2 * wave + (ol >> 5), f = 2 * (ol & 31);
       const int tok = c * NB + s;
       float u[2], dO[2], dt[2];
 #pragma unroll
@@ -793,16 +938,29 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
     __syncthreads();
     const float* dOk = Y(10);
     // dP = (-eta GA2 + dO W2^T) GELU'(P) + X2 -> X7
-    gemm<NB, M, D>(wave, 0, NWV, [&](int s, int k) { return dOk[s * YD + k]; },
-                   [&](int k, int nn) { return W2[nn * D + k]; },
-                   [&](int m0, int n0, f32x4 acc) {
-                     const int nn = n0 + (lane & 15);
+    struct PX2 { f32x4 p, x2; };
+    gemm_p<NB, M>(
+        wave, 0, NWV,
+        [&](int m0, int n0) {   // P and X2 of the tile, from the workspace
+          PX2 v;
 #pragma unroll
-                     for (int i = 0; i < 4; ++i) {
-                       const int s = m0 + 4 * g + i, e = s * XM + nn;
-                       X(7)[e] = (acc[i] - L.eta[s] * X(7)[e]) * gelu1(P[e]) + X(2)[e];
-                     }
-                   });
+          for (int i = 0; i < 4; ++i) {
+            const int e = (m0 + 4 * g + i) * XM + n0 + (lane & 15);
+            v.p[i] = P[e];
+            v.x2[i] = X(2)[e];
+          }
+          return v;
+        },
+        [&](int m0, int n0, f32x4 acc, const PX2& v) {
+          const int nn = n0 + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int s = m0 + 4 * g + i, e = s * XM + nn;
+            X(7)[e] = (acc[i] - L.eta[s] * X(7)[e]) * gelu1(v.p[i]) + v.x2[i];
+          }
+        },
+        seg<D>([&](int s, int k) { return dOk[s * YD + k]; },
+               [&](int k, int nn) { return W2[nn * D + k]; }));
     __syncthreads();
     const float* dP = X(7);
     // dK = dP W1^T - eta GA1 - res dt (stored)
@@ -855,7 +1013,7 @@ __global__ __launch_bounds__(NT) void ttt_mlp_bwd_k(MlpBackwardArgs a) {
                 [&](int k, int j) { return dOk[k * YD + j]; }),
         seg<NB>([&](int nn, int k) { return dU[k * XM + nn]; },
                 [&](int k, int j) { return Go[k * YD + j]; }));
-    for (int nn = tid; nn < M + D; nn += NT) {
+    for (int nn = opaque(tid); nn < M + D; nn += NT) {
       float sum = 0.f;
       if (nn < M) {
         // all 32 loads in flight before the sum (one round trip)
