@@ -597,16 +597,475 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
   }
 }
 
+// ===========================================================================
+// bf16 data: ttt_mlp_fwd_b16<LN, RES>.  The same state layout per wave
+// (W1, W2, W2^T in accumulator registers), reorganised around the matrix
+// unit's 32-deep product (on gfx950 a 16x16x32 bf16 product issues at the
+// rate of a 16x16x16 one, so it halves the matrix time of every product
+// whose contraction is 32 deep or more) and around two barriers per tile:
+//   phase A  P_k = K W1 + b1 with tokens as rows, GELU and GELU' (one
+//            exponential and one reciprocal), A_k transposed once on the matrix unit, the O_k
+//            partial over the wave's hidden units; Q W1 + b1 for the output;
+//   barrier 1
+//   phase B  waves 0-3: LayerNorm backward of O_k, each wave on 4 whole
+//            tokens (16 lanes per token, 4 features per lane: the
+//            feature sums are DPP row sums, no exchange), -eta G_o
+//            published as rows and as columns; waves 4-7: LayerNorm of the
+//            previous tile's O_q and its z;
+//   barrier 2
+//   phase D  U_p = (U_o W2^T) * GELU'(P_k) with tokens as rows (the layout
+//            every consumer of U_p takes; W2 with features as rows comes from
+//            a transpose of its bf16 tiles on the matrix unit, which costs what
+//            updating a second, transposed copy of W2 would, and frees 32
+//            registers); the output from the state at the tile's start,
+//            P_q = Q W1 + b1 + tril(Q K^T + 1) U_p and
+//            O_q = A_q W2 + b2 + tril(A_q A_k^T + 1) U_o (the same bf16 W2
+//            tiles); then the updates of W1, b1, W2, b2.  (Taking the output
+//            from the updated state minus the strictly upper terms instead
+//            would share W2's conversion with the next tile, but early in a
+//            sequence, where a tile's update is large next to the state, the
+//            subtraction cancels: z errors of 4e-2 on the first tokens of a
+//            tile.)
+// Every accumulate chain keeps one product shape: the bias tiles are
+// updated by 32-deep products with zero upper slots, because they seed the
+// 32-deep chains of P and O.
+constexpr int GSTEPS = 192;           // table entries per unit of x
+constexpr float GR = 6.0f;            // table range [-GR, GR)
+constexpr int GN = 2 * 6 * GSTEPS;    // entries
+
+struct MlpLdsB {
+  Stage<true, 4> st;
+  f32x4 pk[NW][16][16];   // O_k^T partials: [wave][token][chunk ^ token], chunk m = features 4m..4m+3
+  f32x4 pq[NW][16][16];   // O_q^T partials of the previous tile, same layout
+  // -eta G_o rows: [token][4p + g] = features 32p+4g+(0..3), 32p+16+4g+(0..3);
+  // rows padded to 9 chunks, so that the 16 tokens a read spans start in
+  // different banks
+  u32x4 uor[16][9];
+  // -eta G_o columns: [feature tile f][lane (g,c)] = tokens 4g+(0..3) of
+  // feature 16f+c; tiles padded by 2 entries (the 2-byte writes of one lane
+  // to the four tiles fall in different banks)
+  u32x2 uoc[4][66];
+  u32x2 mq[2][64];        // tril(K Q^T + 1) [tile parity][lane (g,c)]: k_{4g+i} . q_c + 1, 4g+i <= c
+  u32x2 ktb[2][4][64];    // K^T [tile parity][feature tile r][lane (g,c)]: K[4g+i][16r+c]
+  f32x4 b2[2][16];        // b2 at the start of tile t in [t & 1] (features 4m..4m+3)
+  f32x2 gphi[GN];         // (Phi, next Phi - Phi) at x_i = -GR + i / GSTEPS
+};
+
+// The four fp32 values of a lane as one 4-element bf16 operand.
+__device__ __forceinline__ u32x2 pk4(f32x4 v) {
+  return u32x2{pack_bf16(v[0], v[1]), pack_bf16(v[2], v[3])};
+}
+
+// GELU and GELU' of the hidden pre-activations of the gradient point, which
+// sit on the scan's serial path: evaluated per value (phi_exp: one
+// reciprocal and one exponential), not read from LDS, whose latency and
+// data-dependent bank conflicts cost more there (5 % of the scan).
+__device__ __forceinline__ void gelu_both(float x, float& y, float& dy) {
+  const PhiExp pe = phi_exp(x);
+  const float phi = x >= 0.f ? 1.0f - pe.h : pe.h;
+  y = x * phi;
+  dy = fmaf(x * pe.ex, 0.39894228040143268f, phi);
+}
+// GELU alone (the output side, off the serial path): x Phi(x) with Phi
+// interpolated linearly in the table (step 1/192: within 8.2e-7).  Outside
+// [-GR, GR) the end entries are used: Phi is 0 or 1 there to within 1e-9,
+// so x Phi stays exact to that level for any x.
+__device__ __forceinline__ float gelu_only(const f32x2* tphi, float x) {
+  const float u = __builtin_amdgcn_fmed3f(fmaf(x, (float)GSTEPS, GR * GSTEPS), 0.f,
+                                          (float)GN - 0.002f);
+  const f32x2 e = tphi[(int)u];
+  return x * fmaf(__builtin_amdgcn_fractf(u), e[1], e[0]);
+}
+
+// x from another lane of the same 16-lane row (DPP control CTRL).
+template <int CTRL>
+__device__ __forceinline__ float rdpp(float x) {
+  return bitsf(static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(fbits(x)), CTRL, 0xf, 0xf, false)));
+}
+// Sums over each 16-lane row, in every lane of the row (lanes l^1, l^2,
+// then the mirrored lane of the half row and of the row).
+template <int N>
+__device__ __forceinline__ void row_sums(float (&x)[N]) {
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += rdpp<0xB1>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += rdpp<0x4E>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += rdpp<0x141>(x[j]);
+#pragma unroll
+  for (int j = 0; j < N; ++j) x[j] += rdpp<0x140>(x[j]);
+}
+
+template <bool LN, bool RES>
+__global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd_b16(MlpArgs a) {
+  __shared__ MlpLdsB L;
+  constexpr int TBM = 4;
+
+  const int tid = threadIdx.x;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & 63;
+  const int g = lane >> 4;
+  const int c = lane & 15;
+  const int unit = blockIdx.x;
+  const int head = unit % a.H;
+  const int T = a.T;
+  const size_t row0 = (size_t)unit * T;
+  const int HB = HW * w;          // the wave's hidden units
+  const bool kside = w < 4;       // phase B: LN backward of O_k (else LN of O_q and z)
+  const int ft = w & 3;           // feature tile of the wave's b2 copy
+  // phase B layout: token 4 ft + jb of the tile, features 4 mb .. 4 mb + 3
+  const int jb = lane >> 4, mb = lane & 15;
+  const int tokb = 4 * ft + jb;
+  const size_t s0 = a.state0_per_batch ? (size_t)unit : (size_t)head;
+
+  // ---- state --------------------------------------------------------------
+  // W1c[r][n] lane (g,c) = W1[16r + 4g + i][HB + 16n + c]
+  // W2c[n][f] lane (g,c) = W2[HB + 16n + 4g + i][16f + c]
+  // b1r[n]    lane (g,c) = b1[HB + 16n + c]        (any i: token rows)
+  // b1h[n]    lane (g,c) = b1[HB + 16n + 4g + i]   (any c: hidden rows)
+  // b2q       lane (g,c) = b2[16ft + 4g + i]       (any c; waves 0-3, which
+  //                                                publish it to LDS for the
+  //                                                LayerNorm inputs)
+  // (W2 with features as rows, for U_o W2^T, is formed from W2c each tile
+  // by a transpose on the matrix unit.)
+  f32x4 W1c[4][2], W2c[2][4], b1r[2], b1h[2], b2q;
+  {
+    const float* w1 = a.w1 + s0 * D * MH;
+    const float* w2 = a.w2 + s0 * MH * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          W1c[r][n][i] = w1[(16 * r + 4 * g + i) * MH + HB + 16 * n + c];
+          W2c[n][r][i] = w2[(HB + 16 * n + 4 * g + i) * D + 16 * r + c];
+        }
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        b1r[n][i] = a.b1[s0 * MH + HB + 16 * n + c];
+        b1h[n][i] = a.b1[s0 * MH + HB + 16 * n + 4 * g + i];
+      }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) b2q[i] = a.b2[s0 * D + 16 * ft + 4 * g + i];
+    if (kside && c == 0) L.b2[0][4 * ft + g] = b2q;
+  }
+  // LN parameters of the lane's phase-B features
+  f32x4 gam = {1.f, 1.f, 1.f, 1.f}, bet = {0.f, 0.f, 0.f, 0.f};
+  if (LN) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      gam[i] = a.gamma[(size_t)head * D + 4 * mb + i];
+      bet[i] = a.beta[(size_t)head * D + 4 * mb + i];
+    }
+  }
+  const u32x2 ident = ident_op(g, c);
+  const u32x2 ones = ones_op();
+  const u32x2 z2 = {0u, 0u};
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+
+  // Phi table
+  for (int i = tid; i < GN; i += NT) {
+    const float p0 = 0.5f * erfcf((GR - (float)i / (float)GSTEPS) * 0.70710678118654752f);
+    const float p1 = 0.5f * erfcf((GR - (float)(i + 1) / (float)GSTEPS) * 0.70710678118654752f);
+    L.gphi[i] = f32x2{p0, p1 - p0};
+  }
+
+  const int n_tiles = (T + 15) / 16;
+  stage_issue<true, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, 0, T, 0, w & 3, w >> 2, 2);
+  wait_vmem();
+  lds_barrier();
+
+  f32x4 qres = zero;   // q rows of the tile whose z phase B stores
+
+  // LN of the previous tile's O_q and its z (waves 4-7)
+  auto output_store = [&](int tp) {
+    f32x4 o = L.b2[tp & 1][mb];
+#pragma unroll
+    for (int ww = 0; ww < NW; ++ww) o += L.pq[ww][tokb][mb ^ tokb];
+    f32x4 zf;
+    if (LN) {
+      float s[1] = {(o[0] + o[1]) + (o[2] + o[3])};
+      row_sums(s);
+      const float mu = s[0] * (1.0f / D);
+      f32x4 e;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) e[i] = o[i] - mu;
+      float v[1] = {(e[0] * e[0] + e[1] * e[1]) + (e[2] * e[2] + e[3] * e[3])};
+      row_sums(v);
+      const float rs = __frsqrt_rn(v[0] * (1.0f / D) + a.eps);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zf[i] = (RES ? qres[i] : 0.f) + fmaf(gam[i] * rs, e[i], bet[i]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zf[i] = (RES ? qres[i] : 0.f) + o[i];
+    }
+    const int tok = 16 * tp + tokb;
+    if (tok < T)
+      *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.z) + (row0 + tok) * D + 4 * mb) = pk4(zf);
+  };
+
+  for (int tile = 0; tile < n_tiles; ++tile) {
+    const int blk = tile / TBM, tb = tile % TBM, buf = blk & 1;
+    const bool next_block = (blk + 1) * TBM < n_tiles;
+    const uint16_t* Lq = L.st.qkv[buf][0];
+    const uint16_t* Lk = L.st.qkv[buf][1];
+    const uint16_t* Lv = L.st.qkv[buf][2];
+    const int t0 = tb * 16;
+
+    // ================= phase A ==============================================
+    const Rows kb = load_rows<true>(Lk, t0, c, g);
+    // W1 as 16x16x32 operands: B of K W1 ([feature slot][hidden c]) and A of
+    // (Q W1)^T ([hidden c][feature slot]) are the same registers
+    u32x4 w1b[2][2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int p = 0; p < 2; ++p) w1b[n][p] = cat(pk4(W1c[2 * p][n]), pk4(W1c[2 * p + 1][n]));
+    // P_k with tokens as rows: lane (g,c) = P_k[4g+i][HB + 16n + c]
+    f32x4 Ak[2], Dk[2];
+    u32x2 akr[2], akh[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      f32x4 acc = mfma32(kb.p[0].hi, w1b[n][0], b1r[n]);
+      acc = mfma32(kb.p[1].hi, w1b[n][1], acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float y, dy;
+        gelu_both(acc[i], y, dy);
+        Ak[n][i] = y;
+        Dk[n][i] = dy;
+      }
+      akr[n] = pk4(Ak[n]);
+      // hidden rows: lane (g,c) = A_k[c][HB + 16n + 4g + i]
+      akh[n] = pk4(mfma16(akr[n], ident, zero));
+    }
+    // W2 at the tile's start as bf16 tiles (until its update in phase D):
+    // pairs of them are the A operands of W2^T ([feature c][hidden slot])
+    u32x2 w2h[2][4];
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) w2h[n][f] = pk4(W2c[n][f]);
+    {
+      const u32x4 akb = cat(akh[0], akh[1]);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        L.pk[w][c][(4 * f + g) ^ c] = mfma32(cat(w2h[0][f], w2h[1][f]), akb, zero);
+      }
+    }
+    // Q W1 + b1 (hidden rows) for this tile's output
+    const Rows qb = load_rows<true>(Lq, t0, c, g);
+    f32x4 Pq[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      f32x4 acc = mfma32(w1b[n][0], qb.p[0].hi, b1h[n]);
+      Pq[n] = mfma32(w1b[n][1], qb.p[1].hi, acc);
+    }
+    // tiles every wave needs, one wave each
+    if (w == 0) {
+      f32x4 M = gram<false>(kb, qb);   // lane (g,c): k_{4g+i} . q_c
+#pragma unroll
+      for (int i = 0; i < 4; ++i) M[i] = (4 * g + i <= c) ? M[i] + 1.f : 0.f;
+      L.mq[tile & 1][lane] = pk4(M);
+    } else if (w == 1) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const Op4 kr = row_tile(kb, r);
+        L.ktb[tile & 1][r][lane] = transpose_op<false>(Split4{kr.hi, kr.lo}, ident).hi;
+      }
+    }
+    lds_barrier_copies_in_flight();   // (1)
+    if (tb == 0 && next_block) {
+      // every wave has passed barrier 1, after which nothing reads the other
+      // buffer (the previous block)
+      stage_issue<true, TBM>(L.st, a.q, a.k, a.v, a.eta, row0, blk + 1, T, buf ^ 1, w & 3,
+                             w >> 2, 2);
+    }
+
+    // ================= phase B ==============================================
+    if (kside) {
+      f32x4 o = L.b2[tile & 1][mb];
+#pragma unroll
+      for (int ww = 0; ww < NW; ++ww) o += L.pk[ww][tokb][mb ^ tokb];
+      const f32x4 kr = val4(Lk + lds_off<true>(t0 + tokb, 4 * mb));
+      const f32x4 vr = val4(Lv + lds_off<true>(t0 + tokb, 4 * mb));
+      const float eta = 16 * tile + tokb < T ? L.st.eta[buf][t0 + tokb] : 0.f;
+      f32x4 uo;
+      if (LN) {
+        float s[1] = {(o[0] + o[1]) + (o[2] + o[3])};
+        row_sums(s);
+        const float mu = s[0] * (1.0f / D);
+        f32x4 e;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) e[i] = o[i] - mu;
+        float v[1] = {(e[0] * e[0] + e[1] * e[1]) + (e[2] * e[2] + e[3] * e[3])};
+        row_sums(v);
+        const float rs = __frsqrt_rn(v[0] * (1.0f / D) + a.eps);
+        f32x4 xh, gy;
+        float m[2] = {0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          xh[i] = e[i] * rs;
+          const float tg = 2.f * gam[i];
+          // gamma dl/dy = 2 gamma (k + gamma xhat + beta - v)
+          gy[i] = tg * (((RES ? kr[i] : 0.f) + bet[i] - vr[i]) + gam[i] * xh[i]);
+          m[0] += gy[i];
+          m[1] = fmaf(gy[i], xh[i], m[1]);
+        }
+        row_sums(m);
+        const float ma = m[0] * (1.0f / D), mx = m[1] * (1.0f / D);
+        const float c1 = -eta * rs;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) uo[i] = c1 * fmaf(-xh[i], mx, gy[i] - ma);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) uo[i] = -2.f * eta * (o[i] + (RES ? kr[i] : 0.f) - vr[i]);
+      }
+      // rows: features 4 mb .. 4 mb + 3 = 16 f + 4 gg + (0..3)
+      const u32x2 ub = pk4(uo);
+      const int f = mb >> 2, gg = mb & 3;
+      *reinterpret_cast<u32x2*>(reinterpret_cast<uint32_t*>(&L.uor[tokb][4 * (f >> 1) + gg]) +
+                                2 * (f & 1)) = ub;
+      // columns: lane 16 (tokb / 4) + 4 gg + i of tile f, slot tokb % 4
+      uint16_t* col = reinterpret_cast<uint16_t*>(&L.uoc[f][16 * (tokb >> 2) + 4 * gg]) + (tokb & 3);
+      col[0] = (uint16_t)(ub.x & 0xffffu);
+      col[4] = (uint16_t)(ub.x >> 16);
+      col[8] = (uint16_t)(ub.y & 0xffffu);
+      col[12] = (uint16_t)(ub.y >> 16);
+    } else {
+      if (tile > 0) output_store(tile - 1);
+      qres = val4(Lq + lds_off<true>(t0 + tokb, 4 * mb));
+    }
+    lds_barrier_copies_in_flight();   // (2)
+
+    // ================= phase D ==============================================
+    const u32x4 uo0 = L.uor[c][g], uo1 = L.uor[c][4 + g];
+    u32x2 uoc[4];
+#pragma unroll
+    for (int f = 0; f < 4; ++f) uoc[f] = L.uoc[f][lane];
+    // W2's bf16 tiles: the A operands of the output's A_q W2 and,
+    // transposed on the matrix unit, the B operands [feature slot][hidden c]
+    // of U_o W2^T
+    u32x2 upr[2];
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      u32x2 wt[4];
+#pragma unroll
+      for (int f = 0; f < 4; ++f) wt[f] = pk4(mfma16(w2h[n][f], ident, zero));
+      f32x4 u = mfma32(uo0, cat(wt[0], wt[1]), zero);
+      u = mfma32(uo1, cat(wt[2], wt[3]), u);
+      upr[n] = pk4(u * Dk[n]);   // U_p = (U_o W2^T) * GELU'(P_k), token rows
+    }
+    // output: P_q, A_q, this wave's share of O_q (state at the tile's start)
+    {
+      const u32x2 mqv = L.mq[tile & 1][lane];
+      f32x4 aq[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const f32x4 p = mfma32(cat(upr[n], z2), cat(mqv, z2), Pq[n]);   // + tril(Q K^T + 1) U_p
+#pragma unroll
+        for (int i = 0; i < 4; ++i) aq[n][i] = gelu_only(L.gphi, p[i]);
+      }
+      const u32x4 aqb = cat(pk4(aq[0]), pk4(aq[1]));
+      // this wave's share of tril(A_q A_k^T + 1): lane (g,c) at s' = 4g+i, s = c
+      f32x4 ma = mfma32(cat(akh[0], akh[1]), aqb, zero);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ma[i] = (4 * g + i <= c) ? ma[i] + (w == 0 ? 1.f : 0.f) : 0.f;
+      const u32x2 mas = pk4(ma);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        f32x4 o = mfma32(cat(w2h[0][f], w2h[1][f]), aqb, zero);
+        o = mfma32(cat(uoc[f], z2), cat(mas, z2), o);   // + tril(A_q A_k^T + 1) U_o
+        L.pq[w][c][(4 * f + g) ^ c] = o;   // summed after barrier 1 of the next tile
+      }
+    }
+    // updates
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const u32x2 kt = L.ktb[tile & 1][r][lane];
+#pragma unroll
+      for (int n = 0; n < 2; ++n) W1c[r][n] = mfma16(kt, upr[n], W1c[r][n]);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      b1r[n] = mfma32(cat(ones, z2), cat(upr[n], z2), b1r[n]);
+      b1h[n] = mfma32(cat(upr[n], z2), cat(ones, z2), b1h[n]);
+    }
+#pragma unroll
+    for (int n = 0; n < 2; ++n)
+#pragma unroll
+      for (int f = 0; f < 4; ++f) W2c[n][f] = mfma16(akr[n], uoc[f], W2c[n][f]);
+    if (kside) {
+      // (uoc[ft] re-read: a register array indexed by the wave's ft would
+      // be a chain of selects)
+      b2q = mfma32(cat(L.uoc[ft][lane], z2), cat(ones, z2), b2q);
+      if (c == 0) L.b2[(tile + 1) & 1][4 * ft + g] = b2q;   // read after barrier 1 of the next tile
+    }
+
+    // the next block must be visible to every wave before its first tile
+    if (tb == TBM - 1 && next_block) {
+      wait_vmem();
+      lds_barrier();
+    }
+  }
+
+  // ---- z of the last tile ----------------------------------------------------
+  lds_barrier();
+  if (!kside) output_store(n_tiles - 1);
+
+  // ---- final state ------------------------------------------------------------
+  if (a.w1_out) {
+    int g = lane >> 4, c = lane & 15;
+    asm volatile("" : "+v"(g), "+v"(c));
+    float* w1 = a.w1_out + (size_t)unit * D * MH;
+    float* w2 = a.w2_out + (size_t)unit * MH * D;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          w1[(16 * r + 4 * g + i) * MH + HB + 16 * n + c] = W1c[r][n][i];
+          w2[(HB + 16 * n + 4 * g + i) * D + 16 * r + c] = W2c[n][r][i];
+        }
+    if (c == 0) {
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.b1_out[(size_t)unit * MH + HB + 16 * n + 4 * g + i] = b1h[n][i];
+      if (kside) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) a.b2_out[(size_t)unit * D + 16 * ft + 4 * g + i] = b2q[i];
+      }
+    }
+  }
+}
+
 template <bool BF16, bool LN, bool RES>
 hipError_t launch3(const MlpArgs& a, hipStream_t s) {
   hipLaunchKernelGGL((ttt_mlp_fwd<BF16, LN, RES>), dim3(a.B * a.H), dim3(NT), 0, s, a);
   return hipGetLastError();
 }
 
+template <bool LN, bool RES>
+hipError_t launch_b16(const MlpArgs& a, hipStream_t s) {
+  hipLaunchKernelGGL((ttt_mlp_fwd_b16<LN, RES>), dim3(a.B * a.H), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
 template <bool BF16>
 hipError_t launch1(const MlpArgs& a, bool ln, bool res, hipStream_t s) {
-  if (ln) return res ? launch3<BF16, true, true>(a, s) : launch3<BF16, true, false>(a, s);
-  return res ? launch3<BF16, false, true>(a, s) : launch3<BF16, false, false>(a, s);
+  if constexpr (BF16) {
+    if (ln) return res ? launch_b16<true, true>(a, s) : launch_b16<true, false>(a, s);
+    return res ? launch_b16<false, true>(a, s) : launch_b16<false, false>(a, s);
+  } else {
+    if (ln) return res ? launch3<false, true, true>(a, s) : launch3<false, true, false>(a, s);
+    return res ? launch3<false, false, true>(a, s) : launch3<false, false, false>(a, s);
+  }
 }
 
 }  // namespace
