@@ -18,6 +18,11 @@
 //     W2 -= A_k^T (eta G_o), b2 -= 1^T (eta G_o)
 // (the "+ 1" terms are the bias updates seen by later tokens of the tile).
 //
+// Two kernels.  ttt_mlp_fwd_b16 (further down) serves bf16 data; the
+// kernel described here, ttt_mlp_fwd, serves fp32 data (the BF16 template
+// argument is kept so that both operand forms stay in one place, but only
+// its fp32 instances are launched).
+//
 // Mapping onto one CU: one 512-thread workgroup (8 waves, two per SIMD) per
 // (batch, head) unit.
 //   * Wave w owns hidden units 32w..32w+31: W1[:, 32w:32w+32], b1[32w:32w+32]
