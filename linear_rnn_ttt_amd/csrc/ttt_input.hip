@@ -29,10 +29,13 @@
 // on store.
 //
 // Tile order: consecutive workgroup ids land on the 8 XCDs in turn, so the
-// id is remapped to give each XCD a contiguous run of tiles; within a run
-// the N tiles of one x row block come one after another, so that block
-// (256 rows, 1 MB at D = 2048) is read from HBM once per XCD and then from
-// its L2.
+// id is remapped to give each XCD a contiguous run of tiles.  Within a run
+// the tiles go by groups of 4 x row blocks (256 rows, 1 MB each at
+// D = 2048), column by column inside a group: the 32 tiles an XCD works on
+// at once then share 4 x blocks and 8 W_in tiles (8 MB) rather than one x
+// block and 32 W_in tiles (17 MB), so W_in is streamed 4x less often
+// (measured at B4 T8192, D = 2048: 0.90 -> 0.87 ms; groups of 2 or 8
+// rows: 0.88 ms).
 #include "ttt_device.hpp"
 #include "ttt_input.hpp"
 
@@ -41,7 +44,7 @@
 namespace tttk {
 namespace {
 
-constexpr int BM = 256, BN = 128, BK = 64, NT = 512, LDK = BK, HD = 64, XCDS = 8;
+constexpr int BM = 256, BN = 128, BK = 64, NT = 512, LDK = BK, HD = 64, XCDS = 8, GM = 4;
 
 struct InLds {
   uint16_t a[3][BM][LDK];
@@ -57,7 +60,10 @@ __global__ __launch_bounds__(NT) void ttt_input_k(InputArgs a) {
   const int per = (nt + XCDS - 1) / XCDS;
   const int tile = (blockIdx.x % XCDS) * per + blockIdx.x / XCDS;
   if (tile >= nt) return;
-  const int m0 = (tile / ntn) * BM, n0 = (tile % ntn) * BN;
+  // groups of GM row blocks, their tiles column by column
+  const int grp = tile / (GM * ntn), within = tile % (GM * ntn);
+  const int gsize = min(GM, ntm - grp * GM);
+  const int m0 = (grp * GM + within % gsize) * BM, n0 = (within / gsize) * BN;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
