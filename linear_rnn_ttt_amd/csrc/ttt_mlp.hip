@@ -603,14 +603,16 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
 }
 
 // ===========================================================================
-// bf16 data: ttt_mlp_fwd_b16<LN, RES>.  The same state layout per wave
-// (W1, W2, W2^T in accumulator registers), reorganised around the matrix
-// unit's 32-deep product (on gfx950 a 16x16x32 bf16 product issues at the
-// rate of a 16x16x16 one, so it halves the matrix time of every product
-// whose contraction is 32 deep or more) and around two barriers per tile:
+// bf16 data: ttt_mlp_fwd_b16<LN, RES>.  Wave w again owns hidden units
+// 32w..32w+31 (W1 and W2 in accumulator registers, no transposed copy of
+// W2), with the work reorganised around the matrix unit's 32-deep product
+// (on gfx950 a 16x16x32 bf16 product issues at the rate of a 16x16x16 one,
+// so it halves the matrix time of every product whose contraction is 32
+// deep or more) and around two barriers per tile:
 //   phase A  P_k = K W1 + b1 with tokens as rows, GELU and GELU' (one
-//            exponential and one reciprocal), A_k transposed once on the matrix unit, the O_k
-//            partial over the wave's hidden units; Q W1 + b1 for the output;
+//            exponential and one reciprocal), A_k transposed once on the
+//            matrix unit, the O_k partial over the wave's hidden units;
+//            Q W1 + b1 for the output;
 //   barrier 1
 //   phase B  waves 0-3: LayerNorm backward of O_k, each wave on 4 whole
 //            tokens (16 lanes per token, 4 features per lane: the
@@ -629,8 +631,8 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
 //            from the updated state minus the strictly upper terms instead
 //            would share W2's conversion with the next tile, but early in a
 //            sequence, where a tile's update is large next to the state, the
-//            subtraction cancels: z errors of 4e-2 on the first tokens of a
-//            tile.)
+//            subtraction cancels: z errors of 3.8e-2 on the first tokens of
+//            a tile.)
 // Every accumulate chain keeps one product shape: the bias tiles are
 // updated by 32-deep products with zero upper slots, because they seed the
 // 32-deep chains of P and O.

@@ -85,6 +85,22 @@ def test_special_cases(case, io):
             np.testing.assert_array_equal(a[0], inp[s])
 
 
+@pytest.mark.parametrize("io", ["f32", "bf16"])
+def test_large_hidden_preactivations(io):
+    """W1 and b1 scaled so that the hidden pre-activations spread over about
+    +-20: GELU and GELU' are then taken far into both tails (GELU(x) -> x and
+    0, GELU'(x) -> 1 and 0), beyond the range of the bf16 kernel's Phi table
+    (+-6) and into the saturated part of its per-value formula."""
+    inp = make_inputs(MLP if io == "bf16" else MLP32, B=1, H=2, T=64)
+    rng = np.random.default_rng(11)
+    inp["w1"] = (inp["w1"] * 400.0).astype(np.float32)
+    inp["b1"] = rng.standard_normal(inp["b1"].shape).astype(np.float32) * 4.0
+    # the spread the test relies on (k rows have norm about 1)
+    p = np.einsum("btd,hdm->bhtm", inp["k"][:, 0], inp["w1"][:1])
+    assert np.abs(p).max() > 12.0
+    _check("mlp large pre-activations %s" % io, inp, io)
+
+
 def test_more_units_than_compute_units():
     """B*H = 320 units, more workgroups than the GPU holds at once."""
     _check("mlp B10 H32 T40 bf16", make_inputs(MLP, B=10, H=32, T=40), "bf16")
