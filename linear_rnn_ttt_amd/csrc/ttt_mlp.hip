@@ -624,10 +624,11 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd(MlpArgs a) {
 //            every consumer of U_p takes; W2 with features as rows comes from
 //            a transpose of its bf16 tiles on the matrix unit, which costs what
 //            updating a second, transposed copy of W2 would, and frees 32
-//            registers); the output from the state at the tile's start,
-//            P_q = Q W1 + b1 + tril(Q K^T + 1) U_p and
-//            O_q = A_q W2 + b2 + tril(A_q A_k^T + 1) U_o (the same bf16 W2
-//            tiles); then the updates of W1, b1, W2, b2.  (Taking the output
+//            registers); the output pre-activation from the state at the
+//            tile's start, P_q = Q W1 + b1 + tril(Q K^T + 1) U_p; the
+//            updates of W1, b1, W2; then the rest of the output,
+//            O_q = A_q W2 + b2 + tril(A_q A_k^T + 1) U_o (the bf16 W2 tiles
+//            of the tile's start), and the update of b2.  (Taking the output
 //            from the updated state minus the strictly upper terms instead
 //            would share W2's conversion with the next tile, but early in a
 //            sequence, where a tile's update is large next to the state, the
@@ -967,30 +968,16 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd_b16(MlpArgs a) {
       u = mfma32(uo1, cat(wt[2], wt[3]), u);
       upr[n] = pk4(u * Dk[n]);   // U_p = (U_o W2^T) * GELU'(P_k), token rows
     }
-    // output: P_q, A_q, this wave's share of O_q (state at the tile's start)
-    {
-      const u32x2 mqv = L.mq[tile & 1][lane];
-      f32x4 aq[2];
+    // output pre-activation P_q = Q W1 + b1 + tril(Q K^T + 1) U_p (state at
+    // the tile's start)
+    const u32x2 mqv = L.mq[tile & 1][lane];
+    f32x4 pq[2];
 #pragma unroll
-      for (int n = 0; n < 2; ++n) {
-        const f32x4 p = mfma32(cat(upr[n], z2), cat(mqv, z2), Pq[n]);   // + tril(Q K^T + 1) U_p
-#pragma unroll
-        for (int i = 0; i < 4; ++i) aq[n][i] = gelu_only(L.gphi, p[i]);
-      }
-      const u32x4 aqb = cat(pk4(aq[0]), pk4(aq[1]));
-      // this wave's share of tril(A_q A_k^T + 1): lane (g,c) at s' = 4g+i, s = c
-      f32x4 ma = mfma32(cat(akh[0], akh[1]), aqb, zero);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) ma[i] = (4 * g + i <= c) ? ma[i] + (w == 0 ? 1.f : 0.f) : 0.f;
-      const u32x2 mas = pk4(ma);
-#pragma unroll
-      for (int f = 0; f < 4; ++f) {
-        f32x4 o = mfma32(cat(w2h[0][f], w2h[1][f]), aqb, zero);
-        o = mfma32(cat(uoc[f], z2), cat(mas, z2), o);   // + tril(A_q A_k^T + 1) U_o
-        L.pq[w][c][(4 * f + g) ^ c] = o;   // summed after barrier 1 of the next tile
-      }
-    }
-    // updates
+    for (int n = 0; n < 2; ++n) pq[n] = mfma32(cat(upr[n], z2), cat(mqv, z2), Pq[n]);
+    // updates: from here on the output reads only the bf16 tiles of phase A,
+    // so the update products do not depend on it; issued ahead of the
+    // output's GELU and dependent products, they give the scheduler matrix
+    // work to overlap with that chain (3.5 % faster than after the output)
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const u32x2 kt = L.ktb[tile & 1][r][lane];
@@ -1006,6 +993,26 @@ __global__ __launch_bounds__(NT, 1) void ttt_mlp_fwd_b16(MlpArgs a) {
     for (int n = 0; n < 2; ++n)
 #pragma unroll
       for (int f = 0; f < 4; ++f) W2c[n][f] = mfma16(akr[n], uoc[f], W2c[n][f]);
+    // output: A_q and this wave's share of O_q
+    {
+      f32x4 aq[2];
+#pragma unroll
+      for (int n = 0; n < 2; ++n)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) aq[n][i] = gelu_only(L.gphi, pq[n][i]);
+      const u32x4 aqb = cat(pk4(aq[0]), pk4(aq[1]));
+      // this wave's share of tril(A_q A_k^T + 1): lane (g,c) at s' = 4g+i, s = c
+      f32x4 ma = mfma32(cat(akh[0], akh[1]), aqb, zero);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ma[i] = (4 * g + i <= c) ? ma[i] + (w == 0 ? 1.f : 0.f) : 0.f;
+      const u32x2 mas = pk4(ma);
+#pragma unroll
+      for (int f = 0; f < 4; ++f) {
+        f32x4 o = mfma32(cat(w2h[0][f], w2h[1][f]), aqb, zero);
+        o = mfma32(cat(uoc[f], z2), cat(mas, z2), o);   // + tril(A_q A_k^T + 1) U_o
+        L.pq[w][c][(4 * f + g) ^ c] = o;   // summed after barrier 1 of the next tile
+      }
+    }
     if (kside) {
       // (uoc[ft] re-read: a register array indexed by the wave's ft would
       // be a chain of selects)
