@@ -498,7 +498,10 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
       if (p > n + 2) break;
       // ---- every LDS read of the period first, so that their latencies
       //      overlap: the exchanged sums of tile p and the inputs of tile
-      //      p+1 prepared in the last period
+      //      p+1 prepared in the last period.  They are issued in the order
+      //      of first use (the groups held in place by scheduling barriers),
+      //      so the LN coefficients wait only for the sums: LDS reads return
+      //      in order, and the compiler waits for a count, not for all.
       f32x4 xs[4], su4;
       if (LN) {
 #pragma unroll
@@ -506,11 +509,13 @@ __device__ __forceinline__ void chain_part(LinLds<BF16>& L, const LinearArgs& a,
         su4 = L.xu[p & 1][c];
       }
       const float eta = tile_eta(L.st, blk, tb, c);
+      __builtin_amdgcn_sched_barrier(0);
       const f32x4 bk = L.bkb[(p - 1) & 1][w][lane];  // K_{p+1} W_{p-2}
-      const ScoreOps s1 = read_score(L.grp[(p - 1) & 1][0], lane);  // K_p K_{p+1}^T
       const ScoreOps s2 = read_score(L.grp[(p - 1) & 1][1], lane);  // K_{p-1} K_{p+1}^T
-      const f32x2 tk = L.tkb[(p - 1) & 1][c];
+      __builtin_amdgcn_sched_barrier(0);
       const KV kvn = kv_of(blk, tb + 1);
+      const ScoreOps s1 = read_score(L.grp[(p - 1) & 1][0], lane);  // K_p K_{p+1}^T
+      const f32x2 tk = L.tkb[(p - 1) & 1][c];
       __builtin_amdgcn_sched_barrier(0);
       // ---- independent of tile p's gradient: u of tile p+1, the
       //      correction of K_{p+1} W_{p-2} by tile p-1
@@ -705,11 +710,12 @@ __device__ __forceinline__ void update_part(LinLds<BF16>& L, const LinearArgs& a
     for (int tb = 0; tb < TB; ++tb) {
       const int p = blk * TB + tb;
       if (p > n + 2) break;
-      // Start the period's work 256 cycles late (bf16 data): the chain
+      // Start the period's work 192 cycles late (bf16 data): the chain
       // waves' serial work then meets fewer of these matrix products on its
-      // SIMD.  (B4 H32 T8192: about 1.5 % faster; 512 cycles or more make
-      // this wave's work the longer path.)
-      if constexpr (BF16) __builtin_amdgcn_s_sleep(4);
+      // SIMD.  (B4 H32 T8192: about 2 % faster than no delay, 0.5 % faster
+      // than 256 cycles; 320 cycles or more make this wave's work the longer
+      // path.)
+      if constexpr (BF16) __builtin_amdgcn_s_sleep(3);
       // every LDS read of the period first
       const auto* Kp = tile_rows(L.st, 1, blk, tb);
       const u32x4 g1 = L.gtb[(p - 1) & 1][w][lane];  // (-eta G_{p-1})^T as [hi, mid]
