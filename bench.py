@@ -687,9 +687,18 @@ def run_backward(args) -> dict:
                    "parallelism": "none (1 GPU)",
                    "launch": ("ttt_linear_forward_save (one 768-thread workgroup per unit) + "
                               if train else "") +
-                             "ttt_linear_backward: one 512-thread workgroup per (batch, head) "
-                             "unit, fp32 matrix-unit products, mini-batch bases in a "
-                             "workspace" + (" stored by the forward" if train else "")},
+                             ("ttt_linear_backward: " +
+                              ("" if train else "replay of the bases (one 512-thread workgroup "
+                               "per unit), ") +
+                              "front half of every 16-token tile (one 512-thread workgroup "
+                              "per unit and tile), reverse walk (one 512-thread workgroup "
+                              "per unit); fp32 matrix-unit products, bases and front "
+                              "records in a workspace" +
+                              (", bases stored by the forward" if train else "")
+                              if w.mini_batch == 16 else
+                              "ttt_linear_backward: one 512-thread workgroup per (batch, "
+                              "head) unit, fp32 matrix-unit products, bases in a "
+                              "workspace")},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 3),
                      "peak": FP32_MFMA_PEAK_TFS, "unit": "TFLOP/s",
                      "frac": round(tflops / FP32_MFMA_PEAK_TFS, 5),
@@ -1077,9 +1086,25 @@ def summarize_trace(d, args, cmd):
     for name, calls, tot, avg, pct in rows:
         short = name if len(name) < 70 else name[:67] + "..."
         lines.append("| `%s` | %d | %.1f | %.2f | %.1f |" % (short, calls, tot, avg, pct))
+    per_name = con.execute("select name, count(*), avg(duration) from kernels where name like ? "
+                           "group by name order by name", ("%" + KERNEL_NAME[kind] + "%",)
+                           ).fetchall()
     k = con.execute("select count(*), avg(duration), min(duration), max(duration) from kernels "
                     "where name like ?", ("%" + KERNEL_NAME[kind] + "%",)).fetchone()
-    if k and k[0]:
+    if len(per_name) > 1:
+        # one launch of each instance per call (the backward's replay, front
+        # and reverse-walk roles): the call's time is the sum of their averages
+        lines += ["", "Instances of %s (one launch of each per call):" % KERNEL_NAME[kind], ""]
+        lines += ["- `%s`: %d launches, average %.2f us" % (n if len(n) < 90 else n[:87] + "...",
+                                                             cnt, avg / 1e3)
+                  for n, cnt, avg in per_name]
+        avg_us = sum(avg for _, _, avg in per_name) / 1e3
+        lines += ["", "Average %.2f us per call (sum over the instances); %d algorithmic bytes "
+                  "per call -> %.1f GB/s (%.2f%% of 8 TB/s); %.3e algorithmic flops -> "
+                  "%.2f TFLOP/s." % (avg_us, alg_bytes, alg_bytes / avg_us / 1e3,
+                                     100 * alg_bytes / avg_us / 1e3 / HBM_PEAK_GBS, alg_flops,
+                                     alg_flops / avg_us / 1e6)]
+    elif k and k[0]:
         avg_us = k[1] / 1e3
         lines += ["", "Kernel %s: %d launches, average %.2f us (min %.2f, max %.2f)." % (
             KERNEL_NAME[kind], k[0], avg_us, k[2] / 1e3, k[3] / 1e3)]

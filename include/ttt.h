@@ -249,9 +249,11 @@ ttt_status ttt_linear_forward_save(const ttt_params* p,
 /*
  * Bytes of device workspace that ttt_linear_backward needs for these
  * parameters: 16 KB per unit and 16-token tile (the state at every tile's
- * start), plus 16 KB + 512 bytes per unit, rounded up to 256 bytes
- * (0 if p fails the common checks).  About 1 GB for B = 4, H = 32,
- * T = 8192.
+ * start), plus 16 KB + 512 bytes per unit, rounded up to 256 bytes; with
+ * mini_batch = 16 another 15,104 bytes per unit and tile (the records
+ * that the front half of each tile, computed for all tiles at once, leaves
+ * for the reverse walk) (0 if p fails the common checks).  About 2 GB for
+ * B = 4, H = 32, T = 8192 with 16-token mini-batches.
  */
 uint64_t ttt_linear_backward_workspace_bytes(const ttt_params* p);
 

@@ -107,6 +107,12 @@ struct MlpDecodeArgs {
   float eps;
 };
 
+// Floats per (unit, 16-token tile) record of the backward's front half:
+// x, G, DO [16][64] each, rho, mean(a), mean(a x) [16] each, the two masked
+// Gram fragments [64 lanes][4] each, and the tile's dgamma, dbeta partials
+// [2][64]; padded to a multiple of 256 bytes.
+constexpr int kBwdRecFloats = 3776;
+
 struct BackwardArgs {
   const void* q;            // [B,H,T,64] bf16 or fp32
   const void* k;
@@ -131,6 +137,9 @@ struct BackwardArgs {
   float* ws_base;
   float* ws_dw0;
   float* ws_dln;
+  // 16-token mini-batches: the per-tile records of the adjoint-free front
+  // half [units][tiles][kBwdRecFloats] (nullptr otherwise)
+  float* ws_front;
   int32_t B, H, T;
   int32_t tiles_per_mb;     // mini-batch / 16
   float eps;

@@ -38,6 +38,11 @@
 // replays the forward recurrence and stores the state at every 16-token
 // tile's start in the workspace (16 KB per tile: the device has room for
 // all of them, so nothing is recomputed); phase 2 walks the tiles in reverse.
+// With 16-token mini-batches the two phases are three launches: the replay,
+// then the part of every tile that needs no adjoint (everything up to the
+// output LN's backward, and dq), one workgroup per unit and tile over the
+// whole device, which leaves a record per tile in the workspace, then the
+// reverse walk, which only does what depends on the adjoint.
 // Every product runs on the fp32 matrix unit (16x16x4 products: exact fp32
 // products, fp32 accumulation): the recurrences of the states and of the
 // adjoint amplify rounding on ill-conditioned units, where products of bf16
@@ -82,6 +87,36 @@ struct __attribute__((aligned(16))) BwdLds {
   TileBuf b[2];
   float dln[2][NW][DD];
 };
+
+// Roles of the kernel.  kWhole: the whole pass (replay, then the reverse
+// walk with every tile's front half computed on the way).  For 16-token
+// mini-batches the pass runs as three launches instead: kReplay (phase 1
+// alone), kFront (the front half of one tile per workgroup: the loads, K W,
+// Q W, the Grams, both LNs, dq = [dZ] + DO W^T - M2 K, none of which needs
+// the adjoint; every tile of every unit at once) and kBack (the reverse walk
+// over the records kFront leaves: K A, G A^T, the LN-gradient backward, the
+// A update and dk).
+constexpr int kWhole = 0, kReplay = 1, kFront = 2, kBack = 3;
+
+// One tile in LDS: two front workgroups fit on a CU.
+struct __attribute__((aligned(16))) FrontLds {
+  TileBuf b[1];
+  float dln[2][NW][DD];
+};
+template <int ROLE>
+struct LdsOf {
+  using type = BwdLds;
+};
+template <>
+struct LdsOf<kFront> {
+  using type = FrontLds;
+};
+
+// Offsets (floats) in a front record (kBwdRecFloats per unit and tile).
+constexpr int REC_X = 0, REC_G = 1024, REC_DO = 2048, REC_RHO = 3072, REC_MA = 3088,
+              REC_MX = 3104, REC_U1 = 3120, REC_U2 = 3376, REC_DLN = 3632;
+static_assert(REC_DLN + 2 * DD <= kBwdRecFloats && kBwdRecFloats % 64 == 0,
+              "front record layout");
 
 template <bool BF16>
 __device__ __forceinline__ float ld_io(const void* p, size_t i) {
@@ -165,6 +200,14 @@ struct Fetch {
   float4 wb[2];      // share of the mini-batch's base (phase 2, several tiles)
   float eta;         // eta of token tid % 16
   float v[4], dz[4];  // this wave's token rows, feature f
+  // kBack: the tile's front record -- G and DO shares (elements 2 tid,
+  // 2 tid + 1), x and the LN row terms of this wave's rows, the masked Gram
+  // fragment (U1 for the primal waves, U2 for the dual ones) and the front
+  // half's dgamma, dbeta partial at feature f
+  float2 gr, dor;
+  float x[4], rho[4], ma[4], mx[4];
+  f32x4 u;
+  float dln0, dln1;
 };
 
 // ---- matrix-unit fragments (lane l: g = l / 16, c = l % 16) ---------------
@@ -247,6 +290,7 @@ struct TileRegs {
   Frag Wt[4];        // dual waves
   Inner R;
   float ga[RO], dt[RO];
+  f32x4 u;           // kBack: U1 (primal) or U2 (dual) from the front record
 };
 
 template <bool LN, bool RES>
@@ -290,10 +334,15 @@ __device__ __forceinline__ void inner_grad(const float (&h)[RO], const float (&v
   }
 }
 
-template <bool BF16, bool LN, bool RES, bool MB16>
+template <bool BF16, bool LN, bool RES, bool MB16, int ROLE>
 __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
-  __shared__ BwdLds L;
-  const int unit = blockIdx.x;
+  static_assert(ROLE == kWhole || MB16, "the split roles are for 16-token mini-batches");
+  __shared__ typename LdsOf<ROLE>::type L;
+  const int T = a.T;
+  const int tiles = (T + TB - 1) / TB;
+  // kFront: one workgroup per (unit, tile), tile fastest
+  const int unit = ROLE == kFront ? static_cast<int>(blockIdx.x) / tiles
+                                  : static_cast<int>(blockIdx.x);
   const int head = unit % a.H;
   const int tid = threadIdx.x;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -304,8 +353,6 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   const int f = tid & 63;                                   // feature of the token-row algebra
   const int g = f >> 4, c = f & 15;                         // matrix-unit lane coordinates
   const int col = 16 * cb + c;                              // this lane's product column
-  const int T = a.T;
-  const int tiles = (T + TB - 1) / TB;
   const int nmb = MB16 ? 1 : a.tiles_per_mb;   // 16-token tiles per mini-batch
   const size_t row_unit = static_cast<size_t>(unit) * T;   // first token row of the unit
   float* bases = a.ws_base + static_cast<size_t>(unit) * tiles * DD * DD;
@@ -321,6 +368,8 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   // ---- phase 1: the bases of every mini-batch ------------------------------
   // Wacc[rt][i] = W[16 rt + 4g + i][col] (updated by the primal waves only;
   // the base stores of the dual waves go to a zero-range resource)
+  Fetch F;
+  if constexpr (ROLE == kWhole || ROLE == kReplay) {
   f32x4 Wacc[4], Wb[4];   // the state and (several tiles per mini-batch) its base
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt)
@@ -339,7 +388,6 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     for (int j = 0; j < RO; ++j)
       F.v[j] = ld_io<BF16>(a.v, (row_unit + t0 + min(RO * w + j, nv - 1)) * DD + f);
   };
-  Fetch F;
   if (!a.bases_saved) fetch1(0, F);
   for (int ct = 0; ct < tiles && !a.bases_saved; ++ct) {
     const int t0 = ct * TB;
@@ -397,6 +445,8 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     lds_barrier();
   }
   __syncthreads();   // every base stored before any wave reads one back
+  }
+  if constexpr (ROLE == kReplay) return;
 
   // ---- phase 2: the mini-batches in reverse, two in flight ------------------
   // Only part of a mini-batch's work needs A, the adjoint carried between
@@ -421,7 +471,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   f32x4 Am[4], Bm[4];
 #pragma unroll
   for (int rt = 0; rt < 4; ++rt) Bm[rt] = f4(0.f, 0.f, 0.f, 0.f);
-  {
+  if constexpr (ROLE != kFront) {
     const float* A0 = a.dw_final ? a.dw_final + static_cast<size_t>(unit) * DD * DD : a.w0;
     const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(A0), (short)0, a.dw_final ? DD * DD * 4 : 0, 0x00020000);
@@ -457,7 +507,25 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     for (int j = 0; j < RO; ++j) {
       const size_t row = row_unit + t0 + min(RO * w + j, nv - 1);
       F.v[j] = ld_io<BF16>(a.v, row * DD + f);
-      F.dz[j] = ld_io<BF16>(a.dz, row * DD + f);
+      if constexpr (ROLE != kBack) F.dz[j] = ld_io<BF16>(a.dz, row * DD + f);
+    }
+    if constexpr (ROLE == kBack) {
+      const float* rec = a.ws_front + (static_cast<size_t>(unit) * tiles + ct) * kBwdRecFloats;
+      F.gr = reinterpret_cast<const float2*>(rec + REC_G)[tid];
+      F.dor = reinterpret_cast<const float2*>(rec + REC_DO)[tid];
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        const int i = RO * w + j;
+        if constexpr (LN) {
+          F.x[j] = rec[REC_X + i * DD + f];
+          F.rho[j] = rec[REC_RHO + i];
+          F.ma[j] = rec[REC_MA + i];
+          F.mx[j] = rec[REC_MX + i];
+        }
+      }
+      F.u = reinterpret_cast<const f32x4*>(rec + (primal ? REC_U1 : REC_U2))[f];
+      F.dln0 = rec[REC_DLN + f];
+      F.dln1 = rec[REC_DLN + DD + f];
     }
   };
   float dgam = 0.f, dbet = 0.f;
@@ -480,7 +548,27 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       S.vr[j] = S.ok[j] ? F.v[j] : 0.f;
       S.dzr[j] = S.ok[j] ? F.dz[j] : 0.f;
     }
-    fetch2(max(ct - 1, 0), F);   // unconditional: the last one re-reads a tile
+    if constexpr (ROLE == kBack) {
+      // the front record: G and DO to LDS (zero rows past T as written),
+      // the LN row terms and the Gram fragment to registers, and the front
+      // half's LN-parameter partial into wave 0's sums
+      *reinterpret_cast<float2*>(&X.g[(2 * tid) >> 6][(2 * tid) & 63]) = F.gr;
+      *reinterpret_cast<float2*>(&X.dO[(2 * tid) >> 6][(2 * tid) & 63]) = F.dor;
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        S.R.x[j] = F.x[j];
+        S.R.rho[j] = F.rho[j];
+        S.R.ma[j] = F.ma[j];
+        S.R.mx[j] = F.mx[j];
+      }
+      S.u = F.u;
+      if (w == 0) {
+        dgam += F.dln0;
+        dbet += F.dln1;
+      }
+    }
+    // unconditional (the last one re-reads a tile); kFront has one tile
+    if constexpr (ROLE != kFront) fetch2(max(ct - 1, 0), F);
   };
   // S1: primal: K W (to the row algebra), Q W, the two Q/K Grams; dual: its
   // W^T column block (B operand) for DO W^T and DH W^T
@@ -594,17 +682,30 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   // S5: primal: KA = K A + U1 DO; dual: dQ' = DO W^T - M2 K and
   // GA = G A^T + U2 Q with the DO/G Grams.  M2, U1, U2 in A layout (row c,
   // column s = 4g + i).
+  // U1 in A layout from the primal waves' Q/K Gram
+  auto u1_of = [&](const TileRegs& S) {
+    f32x4 u1;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) u1[i] = 4 * g + i >= c ? S.s1[i] : 0.f;   // q_s . k_c, s >= c
+    return u1;
+  };
   auto S5 = [&](TileBuf& X, TileRegs& S) {
     if (primal) {
       f32x4 pka = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         pka = mma(row_frag(X.k, c, 16 * kt + 4 * g), frag(Am[kt]), pka);
-      float u1[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) u1[i] = 4 * g + i >= c ? S.s1[i] : 0.f;   // q_s . k_c, s >= c
-      pka = mma(frag(f4(u1[0], u1[1], u1[2], u1[3])), col_frag(X.dO, 4 * g, col), pka);
+      const f32x4 u1 = ROLE == kBack ? S.u : u1_of(S);
+      pka = mma(frag(u1), col_frag(X.dO, 4 * g, col), pka);
       put_tile(X.t[1], g, c, 16 * cb, pka);
+    } else if constexpr (ROLE == kBack) {
+      // G A^T + U2 Q, U2 from the record (dq was the front half's)
+      f32x4 pga = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt)
+        pga = mma(row_frag(X.g, c, 16 * kt + 4 * g), frag(Am[kt]), pga);
+      pga = mma(frag(S.u), col_frag(X.q, 4 * g, col), pga);
+      put_tile(X.t[2], g, c, 16 * cb, pga);
     } else {
       f32x4 pdq = f4(0.f, 0.f, 0.f, 0.f), pga = pdq, s2 = pdq, s2t = pdq;
 #pragma unroll
@@ -631,17 +732,61 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       put_tile(X.t[2], g, c, 16 * cb, pga);
     }
   };
+  // kFront: the adjoint-free part of S5 -- dual: dQ' = DO W^T - M2 K into
+  // t[0] and U2 (from the DO/G Grams) into the record; primal wave 0: U1
+  auto S5f = [&](TileBuf& X, TileRegs& S, float* rec) {
+    if (primal) {
+      if (w == 0) reinterpret_cast<f32x4*>(rec + REC_U1)[f] = u1_of(S);
+    } else {
+      f32x4 pdq = f4(0.f, 0.f, 0.f, 0.f), s2 = pdq, s2t = pdq;
+#pragma unroll
+      for (int kt = 0; kt < 4; ++kt) {
+        const Frag df = row_frag(X.dO, c, 16 * kt + 4 * g);
+        const Frag gf = row_frag(X.g, c, 16 * kt + 4 * g);
+        pdq = mma(df, S.Wt[kt], pdq);
+        s2 = mma(df, gf, s2);     // s2[i]  = do_{4g+i} . g_c
+        s2t = mma(gf, df, s2t);   // s2t[i] = g_{4g+i} . do_c
+      }
+      f32x4 m2, u2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 4 * g + i;
+        m2[i] = s <= c ? -X.eta[s] * s2t[i] : 0.f;   // -eta_s (do_c . g_s), s <= c
+        u2[i] = s >= c ? s2[i] : 0.f;                // do_s . g_c, s >= c
+      }
+      pdq = mma(frag(m2), col_frag(X.k, 4 * g, col), pdq);
+      put_tile(X.t[0], g, c, 16 * cb, pdq);
+      if (w == 4) reinterpret_cast<f32x4*>(rec + REC_U2)[f] = u2;
+    }
+  };
   // S6: dq, deta and the LN-gradient backward on this wave's rows: DH, dv
   auto S6 = [&](TileBuf& X, TileRegs& S) {
     const int t0 = S.t0;
     float ka[RO], dh[RO];
+    if constexpr (ROLE == kBack) {
+      // what S1 and S2 would have left: eta and k rows, g, and t, a from the
+      // record's x (the same operations, so the same values)
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        const int i = RO * w + j;
+        S.er[j] = X.eta[i];
+        S.kr[j] = X.k[i][f];
+        S.R.g[j] = X.g[i][f];
+        if constexpr (LN) {
+          S.R.t[j] = S.vr[j] - bet - (RES ? S.kr[j] : 0.f);
+          S.R.a[j] = 2.f * gam * (gam * S.R.x[j] - S.R.t[j]);
+        }
+      }
+    }
 #pragma unroll
     for (int j = 0; j < RO; ++j) {
       const int i = RO * w + j;
-      const float dq = X.t[0][i][f] + (RES ? S.dzr[j] : 0.f);
       ka[j] = X.t[1][i][f];
       S.ga[j] = X.t[2][i][f];
-      store_row<BF16>(o_dq, t0 + i, f, dq);
+      if constexpr (ROLE != kBack) {
+        const float dq = X.t[0][i][f] + (RES ? S.dzr[j] : 0.f);
+        store_row<BF16>(o_dq, t0 + i, f, dq);
+      }
     }
     // deta_i = -KA_i . g_i and the backward of g_i for u = -eta_i KA_i
     float u[RO], de[RO];
@@ -726,7 +871,9 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
 #pragma unroll
       for (int kt = 0; kt < 4; ++kt)
         pdk = mma(row_frag(X.dh, c, 16 * kt + 4 * g),
-                   MB16 ? S.Wt[kt] : row_frag(X.wb, col, 16 * kt + 4 * g), pdk);
+                  ROLE == kBack ? row_frag(X.w, col, 16 * kt + 4 * g)
+                                : (MB16 ? S.Wt[kt] : row_frag(X.wb, col, 16 * kt + 4 * g)),
+                  pdk);
       put_tile(X.t[0], g, c, 16 * cb, pdk);
       const Frag qb = col_frag(X.q, 4 * g, col), kb = col_frag(X.k, 4 * g, col);
 #pragma unroll
@@ -756,43 +903,75 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
   };
 
-  TileRegs Sb, Sf;
-  fetch2(tiles - 1, F);
-  {
-    // prologue: the front half of the last mini-batch
-    TileBuf& X = L.b[(tiles - 1) & 1];
-    S0(tiles - 1, X, Sb);
+  if constexpr (ROLE == kFront) {
+    // one tile: its front half and its record
+    const int ct = static_cast<int>(blockIdx.x) % tiles;
+    float* rec = a.ws_front + (static_cast<size_t>(unit) * tiles + ct) * kBwdRecFloats;
+    TileBuf& X = L.b[0];
+    TileRegs S;
+    fetch2(ct, F);
+    S0(ct, X, S);
     lds_barrier();
-    S1(X, Sb);
+    S1(X, S);
     lds_barrier();
-    S2(X, Sb);
+    S2(X, S);
     lds_barrier();
-    S3(X, Sb);
+    S3(X, S);
     lds_barrier();
-    S4(X, Sb);
+    S4(X, S);
     lds_barrier();
-  }
-  for (int ct = tiles - 1; ct >= 1; --ct) {
-    TileBuf& Xb = L.b[ct & 1];         // the back half of mini-batch ct
-    TileBuf& Xf = L.b[(ct - 1) & 1];   // the front half of mini-batch ct - 1
-    S5(Xb, Sb);
-    S0(ct - 1, Xf, Sf);
-    lds_barrier();  // I1
-    S6(Xb, Sb);
-    S1(Xf, Sf);
-    lds_barrier();  // I2
-    S7(Xb, Sb);
-    S2(Xf, Sf);
-    lds_barrier();  // I3
-    S8(Xb, Sb);
-    S3(Xf, Sf);
-    lds_barrier();  // I4
-    S4(Xf, Sf);
-    lds_barrier();  // I5
-    Sb = Sf;
-  }
-  {
-    // epilogue: the back half of the first mini-batch
+    S5f(X, S, rec);
+    lds_barrier();
+#pragma unroll
+    for (int j = 0; j < RO; ++j) {
+      const int i = RO * w + j;
+      store_row<BF16>(o_dq, S.t0 + i, f, X.t[0][i][f] + (RES ? S.dzr[j] : 0.f));
+      rec[REC_G + i * DD + f] = S.R.g[j];
+      rec[REC_DO + i * DD + f] = X.dO[i][f];
+      if constexpr (LN) {
+        rec[REC_X + i * DD + f] = S.R.x[j];
+        if (f == 0) {
+          rec[REC_RHO + i] = S.R.rho[j];
+          rec[REC_MA + i] = S.R.ma[j];
+          rec[REC_MX + i] = S.R.mx[j];
+        }
+      }
+    }
+    // the tile's dgamma, dbeta (output LN), summed over the waves in order
+    L.dln[0][w][f] = dgam;
+    L.dln[1][w][f] = dbet;
+    lds_barrier();
+    if (w == 0) {
+      float sg = 0.f, sb = 0.f;
+#pragma unroll
+      for (int v = 0; v < NW; ++v) {
+        sg += L.dln[0][v][f];
+        sb += L.dln[1][v][f];
+      }
+      rec[REC_DLN + f] = sg;
+      rec[REC_DLN + DD + f] = sb;
+    }
+    return;
+  } else if constexpr (ROLE == kBack) {
+    // the reverse walk over the records: S5-S8 per tile, the next tile's
+    // loads in S5's interval
+    TileRegs Sb, Sf;
+    fetch2(tiles - 1, F);
+    S0(tiles - 1, L.b[(tiles - 1) & 1], Sb);
+    lds_barrier();
+    for (int ct = tiles - 1; ct >= 1; --ct) {
+      TileBuf& Xb = L.b[ct & 1];
+      S5(Xb, Sb);
+      S0(ct - 1, L.b[(ct - 1) & 1], Sf);
+      lds_barrier();
+      S6(Xb, Sb);
+      lds_barrier();
+      S7(Xb, Sb);
+      lds_barrier();
+      S8(Xb, Sb);
+      lds_barrier();
+      Sb = Sf;
+    }
     TileBuf& X = L.b[0];
     S5(X, Sb);
     lds_barrier();
@@ -801,6 +980,53 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     S7(X, Sb);
     lds_barrier();
     S8(X, Sb);
+  } else {
+    TileRegs Sb, Sf;
+    fetch2(tiles - 1, F);
+    {
+      // prologue: the front half of the last mini-batch
+      TileBuf& X = L.b[(tiles - 1) & 1];
+      S0(tiles - 1, X, Sb);
+      lds_barrier();
+      S1(X, Sb);
+      lds_barrier();
+      S2(X, Sb);
+      lds_barrier();
+      S3(X, Sb);
+      lds_barrier();
+      S4(X, Sb);
+      lds_barrier();
+    }
+    for (int ct = tiles - 1; ct >= 1; --ct) {
+      TileBuf& Xb = L.b[ct & 1];         // the back half of mini-batch ct
+      TileBuf& Xf = L.b[(ct - 1) & 1];   // the front half of mini-batch ct - 1
+      S5(Xb, Sb);
+      S0(ct - 1, Xf, Sf);
+      lds_barrier();  // I1
+      S6(Xb, Sb);
+      S1(Xf, Sf);
+      lds_barrier();  // I2
+      S7(Xb, Sb);
+      S2(Xf, Sf);
+      lds_barrier();  // I3
+      S8(Xb, Sb);
+      S3(Xf, Sf);
+      lds_barrier();  // I4
+      S4(Xf, Sf);
+      lds_barrier();  // I5
+      Sb = Sf;
+    }
+    {
+      // epilogue: the back half of the first mini-batch
+      TileBuf& X = L.b[0];
+      S5(X, Sb);
+      lds_barrier();
+      S6(X, Sb);
+      lds_barrier();
+      S7(X, Sb);
+      lds_barrier();
+      S8(X, Sb);
+    }
   }
 
   // ---- dW0 of this unit and its LN-parameter partial sums --------------------
@@ -852,20 +1078,28 @@ __global__ __launch_bounds__(256) void ttt_linear_bwd_sum_k(BackwardArgs a) {
   }
 }
 
-template <bool BF16, bool LN, bool MB16>
-hipError_t launch_b3(const BackwardArgs& a, bool res, hipStream_t s) {
-  const dim3 grid(a.B * a.H), block(NW * 64);
+template <bool BF16, bool LN, bool MB16, int ROLE>
+hipError_t launch_role(const BackwardArgs& a, bool res, dim3 grid, hipStream_t s) {
+  const dim3 block(NW * 64);
   if (res)
-    hipLaunchKernelGGL((ttt_linear_bwd_k<BF16, LN, true, MB16>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_bwd_k<BF16, LN, true, MB16, ROLE>), grid, block, 0, s, a);
   else
-    hipLaunchKernelGGL((ttt_linear_bwd_k<BF16, LN, false, MB16>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((ttt_linear_bwd_k<BF16, LN, false, MB16, ROLE>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
+// 16-token mini-batches: replay (unless the forward saved the bases), the
+// front half of every tile, the reverse walk; longer ones: the whole pass.
 template <bool BF16, bool LN>
 hipError_t launch_b2(const BackwardArgs& a, bool res, hipStream_t s) {
-  return a.tiles_per_mb == 1 ? launch_b3<BF16, LN, true>(a, res, s)
-                             : launch_b3<BF16, LN, false>(a, res, s);
+  const int units = a.B * a.H;
+  if (a.tiles_per_mb != 1) return launch_role<BF16, LN, false, kWhole>(a, res, dim3(units), s);
+  const int tiles = (a.T + TB - 1) / TB;
+  hipError_t e = hipSuccess;
+  if (!a.bases_saved) e = launch_role<BF16, LN, true, kReplay>(a, res, dim3(units), s);
+  if (e == hipSuccess) e = launch_role<BF16, LN, true, kFront>(a, res, dim3(units * tiles), s);
+  if (e == hipSuccess) e = launch_role<BF16, LN, true, kBack>(a, res, dim3(units), s);
+  return e;
 }
 
 }  // namespace

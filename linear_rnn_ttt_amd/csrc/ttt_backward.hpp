@@ -10,8 +10,11 @@
 
 namespace tttk {
 
-// Two kernels on `stream`: the scan (one workgroup per unit) and the sums
-// over the batch.  Returns the hipError_t of the launches.
+// Kernels on `stream`: the scan -- one launch (one workgroup per unit) for
+// mini-batches of several tiles; for 16-token ones the replay of the bases
+// (unless the forward saved them), the front half of every tile (one
+// workgroup per unit and tile) and the reverse walk (one per unit) -- then
+// the sums over the batch.  Returns the hipError_t of the launches.
 hipError_t launch_linear_backward(const BackwardArgs& a, bool bf16, bool ln, bool residual,
                                   hipStream_t stream);
 

@@ -75,7 +75,11 @@ BackwardLayout backward_layout(const ttt_params* p) {
   BackwardLayout ly;
   ly.dw0_offset = units * tiles * dd4;
   ly.dln_offset = ly.dw0_offset + units * dd4;
-  ly.total = (ly.dln_offset + units * 2 * kHeadDim * 4 + 255) / 256 * 256;
+  ly.front_offset = (ly.dln_offset + units * 2 * kHeadDim * 4 + 255) / 256 * 256;
+  // 16-token mini-batches: one record of the front half per unit and tile
+  const uint64_t front =
+      p->mini_batch == 16 ? units * tiles * static_cast<uint64_t>(tttk::kBwdRecFloats) * 4 : 0;
+  ly.total = ly.front_offset + front;
   return ly;
 }
 
@@ -477,6 +481,7 @@ ttt_status linear_backward(const ttt_params* p, const void* q, const void* k, co
   a->ws_base = reinterpret_cast<float*>(base);
   a->ws_dw0 = reinterpret_cast<float*>(base + ly.dw0_offset);
   a->ws_dln = reinterpret_cast<float*>(base + ly.dln_offset);
+  a->ws_front = p->mini_batch == 16 ? reinterpret_cast<float*>(base + ly.front_offset) : nullptr;
   a->B = p->B;
   a->H = p->H;
   a->T = p->T;

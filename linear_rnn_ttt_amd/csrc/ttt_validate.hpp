@@ -28,7 +28,7 @@ SplitLayout split_layout(const ttt_params* p);
 // (16 KB per 16-token tile and unit), the per-unit dW0 (16 KB per unit) and
 // the per-unit LN parameter gradients (512 B per unit).
 struct BackwardLayout {
-  uint64_t dw0_offset, dln_offset, total;
+  uint64_t dw0_offset, dln_offset, front_offset, total;
 };
 BackwardLayout backward_layout(const ttt_params* p);
 

@@ -226,12 +226,15 @@ def _backward(p, ws=None, ws_bytes=None, **ptrs):
 
 
 def test_backward_workspace_size():
-    # 16 KB per 16-token tile and unit (the bases), 16 KB + 512 B per unit, 256-byte rounding
+    # 16 KB per 16-token tile and unit (the bases), 16 KB + 512 B per unit, 256-byte
+    # rounding; 16-token mini-batches add a 15,104-byte front record per tile and unit
     p = _params(B=2, H=3, T=100)
     units, tiles = 6, 7
-    want = units * tiles * 16384 + units * 16384 + units * 512
+    want = (units * tiles * 16384 + units * 16384 + units * 512 + 255) // 256 * 256
     assert _lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p)) == \
-        (want + 255) // 256 * 256
+        want + units * tiles * 15104
+    p32 = _params(B=2, H=3, T=100, mini_batch=32)
+    assert _lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(p32)) == want
     assert _lib.lib().ttt_linear_backward_workspace_bytes(ctypes.byref(_params(d=16))) == 0
     assert _lib.lib().ttt_linear_backward_workspace_bytes(None) == 0
 
