@@ -98,9 +98,19 @@ struct __attribute__((aligned(16))) BwdLds {
 // A update and dk).
 constexpr int kWhole = 0, kReplay = 1, kFront = 2, kBack = 3;
 
-// One tile in LDS: two front workgroups fit on a CU.
+// One tile of the front half in LDS (no base of several tiles, no DH, two
+// product tiles): three front workgroups fit on a CU.
+struct __attribute__((aligned(16))) FrontBuf {
+  float k[TB][LS];
+  float q[TB][LS];
+  float g[TB][LS];
+  float dO[TB][LS];
+  float w[DD][LS];
+  float t[2][TB][LS];
+  float eta[TB];
+};
 struct __attribute__((aligned(16))) FrontLds {
-  TileBuf b[1];
+  FrontBuf b[1];
   float dln[2][NW][DD];
 };
 template <int ROLE>
@@ -531,14 +541,14 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   float dgam = 0.f, dbet = 0.f;
 
   // S0: the prefetched tile ct into buffer X, its rows into S; fetch ct - 1
-  auto S0 = [&](int ct, TileBuf& X, TileRegs& S) {
+  auto S0 = [&](int ct, auto& X, TileRegs& S) {
     S.t0 = ct * TB;
     S.nv = min(TB, T - S.t0);
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       const int e = tid + NW * 64 * m;
       *reinterpret_cast<float4*>(&X.w[e >> 4][4 * (e & 15)]) = F.w[m];
-      if (!MB16) *reinterpret_cast<float4*>(&X.wb[e >> 4][4 * (e & 15)]) = F.wb[m];
+      if constexpr (!MB16) *reinterpret_cast<float4*>(&X.wb[e >> 4][4 * (e & 15)]) = F.wb[m];
     }
     put_fetched<BF16>(tid < 256 ? X.k : X.q, tq, F.k, S.nv);
     if (tid < TB) X.eta[tid] = tid < S.nv ? F.eta : 0.f;
@@ -572,7 +582,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   };
   // S1: primal: K W (to the row algebra), Q W, the two Q/K Grams; dual: its
   // W^T column block (B operand) for DO W^T and DH W^T
-  auto S1 = [&](TileBuf& X, TileRegs& S) {
+  auto S1 = [&](auto& X, TileRegs& S) {
     if (primal) {
       f32x4 h = f4(0.f, 0.f, 0.f, 0.f);
       S.qw = h;
@@ -584,7 +594,10 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         const Frag wb = col_frag(X.w, 16 * kt + 4 * g, col);   // W[16kt + 4g + i][col]
         const Frag kf = row_frag(X.k, c, 16 * kt + 4 * g);
         const Frag qf = row_frag(X.q, c, 16 * kt + 4 * g);
-        h = mma(kf, MB16 ? wb : col_frag(X.wb, 16 * kt + 4 * g, col), h);
+        if constexpr (MB16)
+          h = mma(kf, wb, h);
+        else
+          h = mma(kf, col_frag(X.wb, 16 * kt + 4 * g, col), h);
         S.qw = mma(qf, wb, S.qw);
         if constexpr (BF16) {
           qb[kt] = u32x2{pack_bf16(qf[0], qf[1]), pack_bf16(qf[2], qf[3])};
@@ -615,7 +628,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
   };
   // S2: the inner LN gradient G on this wave's rows
-  auto S2 = [&](TileBuf& X, TileRegs& S) {
+  auto S2 = [&](auto& X, TileRegs& S) {
     float h[RO];
 #pragma unroll
     for (int j = 0; j < RO; ++j) h[j] = X.t[0][RO * w + j][f];
@@ -628,7 +641,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   };
   // S3: o = Q W - M1 G with M1[c][s] = eta_s (q_c . k_s) for s <= c, whose
   // A-layout entries (row c, column s = 4g + i) are s1t
-  auto S3 = [&](TileBuf& X, TileRegs& S) {
+  auto S3 = [&](auto& X, TileRegs& S) {
     if (primal) {
       float m[4];
 #pragma unroll
@@ -642,7 +655,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
   };
   // S4: the output LN backward on this wave's rows
-  auto S4 = [&](TileBuf& X, TileRegs& S) {
+  auto S4 = [&](auto& X, TileRegs& S) {
     float dO[RO];
     if constexpr (LN) {
       float o[RO], s[RO], xc[RO];
@@ -734,7 +747,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
   };
   // kFront: the adjoint-free part of S5 -- dual: dQ' = DO W^T - M2 K into
   // t[0] and U2 (from the DO/G Grams) into the record; primal wave 0: U1
-  auto S5f = [&](TileBuf& X, TileRegs& S, float* rec) {
+  auto S5f = [&](auto& X, TileRegs& S, float* rec) {
     if (primal) {
       if (w == 0) reinterpret_cast<f32x4*>(rec + REC_U1)[f] = u1_of(S);
     } else {
@@ -907,7 +920,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     // one tile: its front half and its record
     const int ct = static_cast<int>(blockIdx.x) % tiles;
     float* rec = a.ws_front + (static_cast<size_t>(unit) * tiles + ct) * kBwdRecFloats;
-    TileBuf& X = L.b[0];
+    auto& X = L.b[0];
     TileRegs S;
     fetch2(ct, F);
     S0(ct, X, S);
@@ -953,24 +966,66 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
     return;
   } else if constexpr (ROLE == kBack) {
-    // the reverse walk over the records: S5-S8 per tile, the next tile's
-    // loads in S5's interval
+    // the reverse walk over the records: per tile three barrier intervals,
+    // [dk of the tile after it, S5, the loads of the tile before it], [S6],
+    // [S7] -- dk reads only the tile's t[0], which neither S5 (t[1], t[2]
+    // of the current tile) nor the loads (inputs and record of the tile
+    // before, in the same buffer) touch
+    struct Tail {
+      int t0;
+      float er[RO], ga[RO], dt[RO];
+    };
+    auto tail_of = [&](const TileRegs& S) {
+      Tail t;
+      t.t0 = S.t0;
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        t.er[j] = S.er[j];
+        t.ga[j] = S.ga[j];
+        t.dt[j] = S.dt[j];
+      }
+      return t;
+    };
+    auto S8t = [&](TileBuf& X, const Tail& t) {
+#pragma unroll
+      for (int j = 0; j < RO; ++j) {
+        const int i = RO * w + j;
+        const float dk = X.t[0][i][f] - t.er[j] * t.ga[j] - (RES ? t.dt[j] : 0.f);
+        store_row<BF16>(o_dk, t.t0 + i, f, dk);
+      }
+    };
     TileRegs Sb, Sf;
+    Tail tl;
     fetch2(tiles - 1, F);
     S0(tiles - 1, L.b[(tiles - 1) & 1], Sb);
     lds_barrier();
-    for (int ct = tiles - 1; ct >= 1; --ct) {
-      TileBuf& Xb = L.b[ct & 1];
-      S5(Xb, Sb);
-      S0(ct - 1, L.b[(ct - 1) & 1], Sf);
-      lds_barrier();
-      S6(Xb, Sb);
-      lds_barrier();
-      S7(Xb, Sb);
-      lds_barrier();
-      S8(Xb, Sb);
-      lds_barrier();
-      Sb = Sf;
+    if (tiles > 1) {
+      {
+        TileBuf& Xb = L.b[(tiles - 1) & 1];
+        S5(Xb, Sb);
+        S0(tiles - 2, L.b[tiles & 1], Sf);
+        lds_barrier();
+        S6(Xb, Sb);
+        lds_barrier();
+        S7(Xb, Sb);
+        lds_barrier();
+        tl = tail_of(Sb);
+        Sb = Sf;
+      }
+      for (int ct = tiles - 2; ct >= 1; --ct) {
+        TileBuf& Xb = L.b[ct & 1];
+        S8t(L.b[(ct + 1) & 1], tl);
+        S5(Xb, Sb);
+        S0(ct - 1, L.b[(ct - 1) & 1], Sf);
+        lds_barrier();
+        S6(Xb, Sb);
+        lds_barrier();
+        S7(Xb, Sb);
+        lds_barrier();
+        tl = tail_of(Sb);
+        Sb = Sf;
+      }
+      S8t(L.b[1], tl);   // tile 1
     }
     TileBuf& X = L.b[0];
     S5(X, Sb);
