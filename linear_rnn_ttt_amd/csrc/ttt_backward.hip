@@ -113,6 +113,26 @@ struct __attribute__((aligned(16))) FrontLds {
   FrontBuf b[1];
   float dln[2][NW][DD];
 };
+// The reverse walk's tiles (no base of several tiles): with bf16 data the
+// adjoint update takes DO and DH as three bf16 parts each, stored
+// transposed -- [part][feature][token pair], rows of 40 bytes -- so that a
+// matrix-unit fragment (4 tokens of one feature) is one 8-byte read.
+struct __attribute__((aligned(16))) BackBuf {
+  float k[TB][LS];
+  float q[TB][LS];
+  float g[TB][LS];
+  float dO[TB][LS];
+  float dh[TB][LS];
+  float w[DD][LS];
+  float t[3][TB][LS];
+  float eta[TB];
+  uint32_t dot[3][DD][10];
+  uint32_t dht[3][DD][10];
+};
+struct __attribute__((aligned(16))) BackLds {
+  BackBuf b[2];
+  float dln[2][NW][DD];
+};
 template <int ROLE>
 struct LdsOf {
   using type = BwdLds;
@@ -121,6 +141,25 @@ template <>
 struct LdsOf<kFront> {
   using type = FrontLds;
 };
+template <>
+struct LdsOf<kBack> {
+  using type = BackLds;
+};
+
+// Two values as three bf16 parts each (hi, mid, lo: about 24 significant
+// bits), packed in pairs: part p of (x0, x1) in u[p].
+__device__ __forceinline__ void split2x3(float x0, float x1, uint32_t (&u)[3]) {
+  u[0] = pack_bf16(x0, x1);
+  float r0 = x0 - bf16_lo_to_f32(u[0]), r1 = x1 - bf16_hi_to_f32(u[0]);
+  u[1] = pack_bf16(r0, r1);
+  r0 -= bf16_lo_to_f32(u[1]);
+  r1 -= bf16_hi_to_f32(u[1]);
+  u[2] = pack_bf16(r0, r1);
+}
+// A fragment of exact bf16 values held as fp32: the four values packed.
+__device__ __forceinline__ u32x2 pack_frag(f32x4 x) {
+  return u32x2{pack_bf16(x[0], x[1]), pack_bf16(x[2], x[3])};
+}
 
 // Offsets (floats) in a front record (kBwdRecFloats per unit and tile).
 constexpr int REC_X = 0, REC_G = 1024, REC_DO = 2048, REC_RHO = 3072, REC_MA = 3088,
@@ -702,7 +741,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     for (int i = 0; i < 4; ++i) u1[i] = 4 * g + i >= c ? S.s1[i] : 0.f;   // q_s . k_c, s >= c
     return u1;
   };
-  auto S5 = [&](TileBuf& X, TileRegs& S) {
+  auto S5 = [&](auto& X, TileRegs& S) {
     if (primal) {
       f32x4 pka = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -773,7 +812,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
   };
   // S6: dq, deta and the LN-gradient backward on this wave's rows: DH, dv
-  auto S6 = [&](TileBuf& X, TileRegs& S) {
+  auto S6 = [&](auto& X, TileRegs& S) {
     const int t0 = S.t0;
     float ka[RO], dh[RO];
     if constexpr (ROLE == kBack) {
@@ -862,13 +901,67 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       store_row<BF16>(o_dv, t0 + i, f, S.dt[j]);
       X.dh[i][f] = dh[j];
     }
+    if constexpr (ROLE == kBack && BF16) {
+      // DO and DH of this wave's two token rows in three bf16 parts,
+      // transposed, for the adjoint update
+      static_assert(RO == 2, "one token pair per wave");
+      uint32_t po[3], ph[3];
+      split2x3(X.dO[RO * w][f], X.dO[RO * w + 1][f], po);
+      split2x3(dh[0], dh[1], ph);
+#pragma unroll
+      for (int p = 0; p < 3; ++p) {
+        X.dot[p][f][w] = po[p];
+        X.dht[p][f][w] = ph[p];
+      }
+    }
   };
   // S7: primal: A += Q^T DO + K^T DH; dual: DH W^T, and A^T += DO^T Q +
   // DH^T K.  The A operand of row tile rt of X^T is X[4g + i][16 rt + c].
   // With several tiles per mini-batch the output term Q^T DO goes to the
   // adjoint of the state at the tile's start and the gradient term K^T DH
   // to that of the mini-batch's base (Bm); the two meet at its first tile.
-  auto S7 = [&](TileBuf& X, TileRegs& S) {
+  auto S7 = [&](auto& X, TileRegs& S) {
+    if constexpr (ROLE == kBack && BF16) {
+      // q and k are exact in bf16: Q^T DO and K^T DH as bf16 products with DO
+      // and DH in three parts -- hi and mid paired in one 32-deep product,
+      // the two lo parts in another; exact products, fp32 accumulation.
+      // The chain keeps one product shape: a 16-deep product accumulating
+      // right behind a 32-deep one gave wrong values here.
+      auto parts = [&](const uint32_t (&t)[3][DD][10], int feat, u32x2 (&o)[3]) {
+#pragma unroll
+        for (int p = 0; p < 3; ++p) o[p] = *reinterpret_cast<const u32x2*>(&t[p][feat][2 * g]);
+      };
+      if (primal) {
+        u32x2 dop[3], dhp[3];   // B operands: DO, DH [4g + i][col]
+        parts(X.dot, col, dop);
+        parts(X.dht, col, dhp);
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          const u32x2 qa = pack_frag(col_frag(X.q, 4 * g, 16 * rt + c));   // Q^T[16 rt + c][4g + i]
+          const u32x2 ka = pack_frag(col_frag(X.k, 4 * g, 16 * rt + c));
+          Am[rt] = mfma32(cat(qa, qa), cat(dop[0], dop[1]), Am[rt]);
+          Am[rt] = mfma32(cat(qa, ka), cat(dop[2], dhp[2]), Am[rt]);
+          Am[rt] = mfma32(cat(ka, ka), cat(dhp[0], dhp[1]), Am[rt]);
+        }
+      } else {
+        f32x4 pdk = f4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+        for (int kt = 0; kt < 4; ++kt)
+          pdk = mma(row_frag(X.dh, c, 16 * kt + 4 * g), row_frag(X.w, col, 16 * kt + 4 * g), pdk);
+        put_tile(X.t[0], g, c, 16 * cb, pdk);
+        const u32x2 qb = pack_frag(col_frag(X.q, 4 * g, col));   // B operands: Q, K [4g + i][col]
+        const u32x2 kb = pack_frag(col_frag(X.k, 4 * g, col));
+#pragma unroll
+        for (int rt = 0; rt < 4; ++rt) {
+          u32x2 dop[3], dhp[3];   // A operands: DO^T, DH^T [16 rt + c][4g + i]
+          parts(X.dot, 16 * rt + c, dop);
+          parts(X.dht, 16 * rt + c, dhp);
+          Am[rt] = mfma32(cat(dop[0], dop[1]), cat(qb, qb), Am[rt]);
+          Am[rt] = mfma32(cat(dop[2], dhp[2]), cat(qb, kb), Am[rt]);
+          Am[rt] = mfma32(cat(dhp[0], dhp[1]), cat(kb, kb), Am[rt]);
+        }
+      }
+    } else {
     if (primal) {
       const Frag dob = col_frag(X.dO, 4 * g, col), dhb = col_frag(X.dh, 4 * g, col);
 #pragma unroll
@@ -882,11 +975,14 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     } else {
       f32x4 pdk = f4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-      for (int kt = 0; kt < 4; ++kt)
-        pdk = mma(row_frag(X.dh, c, 16 * kt + 4 * g),
-                  ROLE == kBack ? row_frag(X.w, col, 16 * kt + 4 * g)
-                                : (MB16 ? S.Wt[kt] : row_frag(X.wb, col, 16 * kt + 4 * g)),
-                  pdk);
+      for (int kt = 0; kt < 4; ++kt) {
+        if constexpr (ROLE == kBack)
+          pdk = mma(row_frag(X.dh, c, 16 * kt + 4 * g), row_frag(X.w, col, 16 * kt + 4 * g), pdk);
+        else if constexpr (MB16)
+          pdk = mma(row_frag(X.dh, c, 16 * kt + 4 * g), S.Wt[kt], pdk);
+        else
+          pdk = mma(row_frag(X.dh, c, 16 * kt + 4 * g), row_frag(X.wb, col, 16 * kt + 4 * g), pdk);
+      }
       put_tile(X.t[0], g, c, 16 * cb, pdk);
       const Frag qb = col_frag(X.q, 4 * g, col), kb = col_frag(X.k, 4 * g, col);
 #pragma unroll
@@ -898,6 +994,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
           Bm[rt] = mma(col_frag(X.dh, 4 * g, 16 * rt + c), kb, Bm[rt]);
       }
     }
+    }
     if (!MB16 && (S.t0 / TB) % nmb == 0) {
 #pragma unroll
       for (int rt = 0; rt < 4; ++rt) {
@@ -907,7 +1004,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     }
   };
   // S8: dk on this wave's rows
-  auto S8 = [&](TileBuf& X, TileRegs& S) {
+  auto S8 = [&](auto& X, TileRegs& S) {
 #pragma unroll
     for (int j = 0; j < RO; ++j) {
       const int i = RO * w + j;
@@ -986,7 +1083,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       }
       return t;
     };
-    auto S8t = [&](TileBuf& X, const Tail& t) {
+    auto S8t = [&](auto& X, const Tail& t) {
 #pragma unroll
       for (int j = 0; j < RO; ++j) {
         const int i = RO * w + j;
@@ -1001,7 +1098,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
     lds_barrier();
     if (tiles > 1) {
       {
-        TileBuf& Xb = L.b[(tiles - 1) & 1];
+        auto& Xb = L.b[(tiles - 1) & 1];
         S5(Xb, Sb);
         S0(tiles - 2, L.b[tiles & 1], Sf);
         lds_barrier();
@@ -1013,7 +1110,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
         Sb = Sf;
       }
       for (int ct = tiles - 2; ct >= 1; --ct) {
-        TileBuf& Xb = L.b[ct & 1];
+        auto& Xb = L.b[ct & 1];
         S8t(L.b[(ct + 1) & 1], tl);
         S5(Xb, Sb);
         S0(ct - 1, L.b[(ct - 1) & 1], Sf);
@@ -1027,7 +1124,7 @@ __global__ __launch_bounds__(NW * 64) void ttt_linear_bwd_k(BackwardArgs a) {
       }
       S8t(L.b[1], tl);   // tile 1
     }
-    TileBuf& X = L.b[0];
+    auto& X = L.b[0];
     S5(X, Sb);
     lds_barrier();
     S6(X, Sb);
