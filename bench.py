@@ -1005,6 +1005,17 @@ PIPE_COUNTERS = ["SQ_ACTIVE_INST_VALU", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_ACTIVE_I
                  "SQ_INSTS_MFMA", "GRBM_GUI_ACTIVE"]
 
 
+def _per_call(rows):
+    """Mean per call of a per-dispatch counter over [(kernel name, value)]:
+    the mean over the dispatches of each kernel instance, summed over the
+    instances (a call launches each instance once: the TTT-Linear backward's
+    replay, front and reverse-walk roles; every other kernel has one)."""
+    by = {}
+    for n, v in rows:
+        by.setdefault(n, []).append(v)
+    return sum(sum(v) / len(v) for v in by.values())
+
+
 def summarize_pipes(d, args, cmd, workgroups: int):
     """Pipe utilisation of the profiled kernel from one `rocprofv3 --pmc`
     pass of PIPE_COUNTERS.  The busy fractions are per busy CU: the active
@@ -1017,9 +1028,9 @@ def summarize_pipes(d, args, cmd, workgroups: int):
     kname = KERNEL_NAME[kind]
     vals = {}
     for ctr in PIPE_COUNTERS:
-        rows = [v for n, _, v in _counter_per_dispatch(
+        rows = [(n, v) for n, _, v in _counter_per_dispatch(
             d, ctr, "max" if ctr.startswith("GRBM") else "sum") if kname in n]
-        vals[ctr] = sum(rows) / len(rows)
+        vals[ctr] = _per_call(rows)
     busy = vals["SQ_BUSY_CU_CYCLES"]
     per_cu = busy / workgroups
     lines = [
@@ -1121,15 +1132,15 @@ def summarize_pmc(fetch_dir, write_dir, args, cmd_fetch, cmd_write):
     kname = KERNEL_NAME[kind]
     fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
-    kf = [v for n, _, v in fetch if kname in n]
-    kw = [v for n, _, v in write if kname in n]
+    kf = [(n, v) for n, _, v in fetch if kname in n]
+    kw = [(n, v) for n, _, v in write if kname in n]
     # the 1 GiB device-to-device copy: the largest copyBuffer dispatch
     cf = max(v for n, _, v in fetch if "copyBuffer" in n)
     cw = max(v for n, _, v in write if "copyBuffer" in n)
     f_fetch = (COPY_BYTES / 1024.0) / cf
     f_write = (COPY_BYTES / 1024.0) / cw
-    fetch_kib = sum(kf) / len(kf)
-    write_kib = sum(kw) / len(kw)
+    fetch_kib = _per_call(kf)
+    write_kib = _per_call(kw)
     traffic = fetch_kib * 1024 * f_fetch + write_kib * 1024 * f_write
     lines = [
         "# HBM traffic of `%s` on %s (rocprofv3 --pmc)" % (kname, name),
