@@ -55,15 +55,16 @@ def test_input_side_matches_the_oracle(B, T, D, H):
 
 
 def test_input_side_gate_extremes_and_determinism():
-    """Large gate biases saturate eta at eta_base and 0; two calls agree bit
+    """Large gate biases saturate eta at eta_base and 0; ten calls agree bit
     for bit."""
     H = 4
     inp = make_input_side(SMALL, B=1, T=70, D=128, H=H)
     inp["b_eta"] = np.array([30.0, -30.0, 0.0, 2.0], np.float32)
     a = run(inp, H)
-    b = run(inp, H)
-    for x, y in zip(a, b):
-        assert np.array_equal(x, y)
+    for _ in range(9):
+        b = run(inp, H)
+        for x, y in zip(a, b):
+            assert np.array_equal(x, y)
     want = input_side(inp["x"], inp["w_in"], inp["b_eta"], H, 64, inp["eta_base"])
     check(a, want, "gate extremes")
     assert np.allclose(a[3][:, 0], inp["eta_base"], rtol=1e-6)

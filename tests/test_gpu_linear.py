@@ -136,12 +136,16 @@ def test_resume_and_in_place():
     assert state_err(from_dev(w2), from_dev(wf)) <= 1e-5
 
 
-def test_deterministic():
+@pytest.mark.parametrize("split", [False, True])
+def test_deterministic(split):
+    """Ten runs of the same launch give the same bits (the two-workgroup
+    launch too, whose output side follows a cross-CU hand-off)."""
     w = WORKLOADS["linear_125m_b8h12_t2k"]
-    inp = make_inputs(w, T=512)
-    a = _gpu(inp, "bf16")
-    b = _gpu(inp, "bf16")
-    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    inp = make_inputs(w, B=2, T=512)
+    a = _gpu(inp, "bf16", split=split)
+    for _ in range(9):
+        b = _gpu(inp, "bf16", split=split)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 @pytest.mark.parametrize("name,strict", [("linear_125m_b8h12_t2k", True),

@@ -139,12 +139,14 @@ def test_resume_and_in_place():
 
 
 def test_deterministic():
+    """Ten runs give the same bits."""
     inp = make_inputs(MLP, B=2, H=4, T=256)
     a = _gpu(inp, "bf16")
-    b = _gpu(inp, "bf16")
-    assert np.array_equal(a[0], b[0])
-    for x, y in zip(a[1], b[1]):
-        assert np.array_equal(x, y)
+    for _ in range(9):
+        b = _gpu(inp, "bf16")
+        assert np.array_equal(a[0], b[0])
+        for x, y in zip(a[1], b[1]):
+            assert np.array_equal(x, y)
 
 
 @pytest.mark.parametrize("name", ["mlp_125m_b8h12_t2k", "mlp_long_b1h32_t32k"])

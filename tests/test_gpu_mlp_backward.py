@@ -155,9 +155,10 @@ def test_mlp_backward_deterministic_and_workspace_reuse():
     inp = make_inputs(MLP, B=2, H=2, T=40)
     dz, fin = cotangents(inp, "bf16", seed=5)
     a = gpu(inp, "bf16", dz, fin)
-    b = gpu(inp, "bf16", dz, fin)
-    for n in NAMES:
-        assert np.array_equal(a[n], b[n]), n
+    for _ in range(9):   # ten runs in all
+        b = gpu(inp, "bf16", dz, fin)
+        for n in NAMES:
+            assert np.array_equal(a[n], b[n]), n
 
 
 def test_mlp_backward_more_units_than_compute_units():
