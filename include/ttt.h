@@ -287,12 +287,17 @@ uint64_t ttt_linear_backward_workspace_bytes(const ttt_params* p);
  * and inputs; the backward then skips replaying the forward
  * recurrence.  The library cannot check this: stale bases give wrong
  * gradients.
- * gfx950: two kernels on hip_stream.  One 512-thread workgroup per unit
- * first replays the forward recurrence and stores the state at every
- * 16-token tile's start in the workspace, then walks the tiles in reverse
- * (fp32 arithmetic);
- * a second kernel sums dw0 (shared w0), dln_gamma and dln_beta over the
- * batch in a fixed order.  Results are deterministic.
+ * gfx950: kernels on hip_stream.  The forward recurrence is replayed (one
+ * 512-thread workgroup per unit, unless TTT_BASES_SAVED) and the state at
+ * every 16-token tile's start stored in the workspace; the tiles are then
+ * walked in reverse.  With mini_batch = 16 the part of every tile that needs
+ * no adjoint runs first for all tiles at once (one workgroup per unit and
+ * tile, records in the workspace) and the reverse walk (one workgroup per
+ * unit) only carries the adjoint; longer mini-batches replay and walk in
+ * one launch.  Products at fp32 precision (fp32 matrix-unit products, or
+ * exact bf16 products of bf16 inputs with three-part bf16 operands); a last
+ * kernel sums dw0 (shared w0), dln_gamma and dln_beta over the batch in a
+ * fixed order.  Results are deterministic.
  */
 ttt_status ttt_linear_backward(const ttt_params* p,
                                const void* q, const void* k, const void* v,
