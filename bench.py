@@ -51,7 +51,8 @@ KERNEL_SOURCES = {
                "ttt_args.hpp"],
     "mlp": ["ttt_mlp.hip", "ttt_tile.hpp", "ttt_device.hpp", "ttt_kernels.hpp", "ttt_args.hpp"],
     "decode": ["ttt_decode.hip", "ttt_device.hpp", "ttt_kernels.hpp", "ttt_args.hpp"],
-    "backward": ["ttt_backward.hip", "ttt_backward.hpp", "ttt_device.hpp", "ttt_args.hpp"],
+    "backward": ["ttt_backward.hip", "ttt_backward.hpp", "ttt_device.hpp", "ttt_args.hpp",
+                 "ttt_linear.hip", "ttt_tile.hpp", "ttt_kernels.hpp"],
     "decode_compact": ["ttt_decode_compact.hip", "ttt_stream.hpp", "ttt_device.hpp",
                        "ttt_args.hpp"],
     "mlp_decode": ["ttt_mlp_decode.hip", "ttt_stream.hpp", "ttt_device.hpp", "ttt_args.hpp"],
@@ -61,6 +62,10 @@ KERNEL_SOURCES = {
                      "ttt_device.hpp"],
     "input": ["ttt_input.hip", "ttt_input.hpp", "ttt_args.hpp", "ttt_device.hpp"],
 }
+# Other kernels a call launches whose time and traffic belong to it (the
+# TTT-Linear backward takes its 16-token mini-batch bases from the forward
+# kernel).
+CALL_EXTRA = {"backward": ["ttt_linear_fwd"]}
 KERNEL_NAME = {"linear": "ttt_linear_fwd", "mlp": "ttt_mlp_fwd", "decode": "ttt_linear_decode_k",
                "backward": "ttt_linear_bwd_k", "decode_compact": "ttt_linear_decode_compact_k",
                "mlp_decode": "ttt_mlp_decode_k",
@@ -688,8 +693,8 @@ def run_backward(args) -> dict:
                    "launch": ("ttt_linear_forward_save (one 768-thread workgroup per unit) + "
                               if train else "") +
                              ("ttt_linear_backward: " +
-                              ("" if train else "replay of the bases (one 512-thread workgroup "
-                               "per unit), ") +
+                              ("" if train else "the bases from the forward kernel (one "
+                               "768-thread workgroup per unit), ") +
                               "front half of every 16-token tile (one 512-thread workgroup "
                               "per unit and tile), reverse walk (one 512-thread workgroup "
                               "per unit); fp32 matrix-unit products, bases and front "
@@ -1028,8 +1033,9 @@ def summarize_pipes(d, args, cmd, workgroups: int):
     kname = KERNEL_NAME[kind]
     vals = {}
     for ctr in PIPE_COUNTERS:
+        names = [kname] + CALL_EXTRA.get(kind, [])
         rows = [(n, v) for n, _, v in _counter_per_dispatch(
-            d, ctr, "max" if ctr.startswith("GRBM") else "sum") if kname in n]
+            d, ctr, "max" if ctr.startswith("GRBM") else "sum") if any(k in n for k in names)]
         vals[ctr] = _per_call(rows)
     busy = vals["SQ_BUSY_CU_CYCLES"]
     per_cu = busy / workgroups
@@ -1097,15 +1103,18 @@ def summarize_trace(d, args, cmd):
     for name, calls, tot, avg, pct in rows:
         short = name if len(name) < 70 else name[:67] + "..."
         lines.append("| `%s` | %d | %.1f | %.2f | %.1f |" % (short, calls, tot, avg, pct))
-    per_name = con.execute("select name, count(*), avg(duration) from kernels where name like ? "
-                           "group by name order by name", ("%" + KERNEL_NAME[kind] + "%",)
-                           ).fetchall()
+    per_name = []
+    for kn in [KERNEL_NAME[kind]] + CALL_EXTRA.get(kind, []):
+        per_name += con.execute("select name, count(*), avg(duration) from kernels where name "
+                                "like ? group by name order by name", ("%" + kn + "%",)
+                                ).fetchall()
     k = con.execute("select count(*), avg(duration), min(duration), max(duration) from kernels "
                     "where name like ?", ("%" + KERNEL_NAME[kind] + "%",)).fetchone()
     if len(per_name) > 1:
         # one launch of each instance per call (the backward's replay, front
         # and reverse-walk roles): the call's time is the sum of their averages
-        lines += ["", "Instances of %s (one launch of each per call):" % KERNEL_NAME[kind], ""]
+        lines += ["", "Kernels of one call (one launch of each): %s" % ", ".join(
+            [KERNEL_NAME[kind]] + CALL_EXTRA.get(kind, [])), ""]
         lines += ["- `%s`: %d launches, average %.2f us" % (n if len(n) < 90 else n[:87] + "...",
                                                              cnt, avg / 1e3)
                   for n, cnt, avg in per_name]
@@ -1132,8 +1141,9 @@ def summarize_pmc(fetch_dir, write_dir, args, cmd_fetch, cmd_write):
     kname = KERNEL_NAME[kind]
     fetch = _counter_per_dispatch(fetch_dir, "FETCH_SIZE")
     write = _counter_per_dispatch(write_dir, "WRITE_SIZE")
-    kf = [(n, v) for n, _, v in fetch if kname in n]
-    kw = [(n, v) for n, _, v in write if kname in n]
+    names = [kname] + CALL_EXTRA.get(kind, [])
+    kf = [(n, v) for n, _, v in fetch if any(k in n for k in names)]
+    kw = [(n, v) for n, _, v in write if any(k in n for k in names)]
     # the 1 GiB device-to-device copy: the largest copyBuffer dispatch
     cf = max(v for n, _, v in fetch if "copyBuffer" in n)
     cw = max(v for n, _, v in write if "copyBuffer" in n)

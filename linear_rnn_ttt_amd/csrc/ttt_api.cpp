@@ -194,6 +194,17 @@ ttt_status ttt_linear_backward(const ttt_params* p, const void* q, const void* k
                                               dw_final, dq, dk, dv, deta, dw0, dln_gamma,
                                               dln_beta, workspace, workspace_bytes, &a);
   if (st != TTT_OK) return st;
+  if (p->mini_batch == 16 && !(p->flags & TTT_BASES_SAVED)) {
+    // the bases from the forward kernel, which holds each one anyway (faster
+    // than the backward's own replay); the walk then reads them as saved
+    tttk::LinearArgs la;
+    const ttt_status sf = tttv::linear_forward_bases(p, q, k, v, eta, w0, ln_gamma, ln_beta,
+                                                     workspace, &la);
+    if (sf != TTT_OK) return sf;
+    const ttt_status sl = linear_launch(p, la, hip_stream);
+    if (sl != TTT_OK) return sl;
+    a.bases_saved = 1;
+  }
   return status_of(tttk::launch_linear_backward(a, bf16_of(p), ln_of(p), res_of(p),
                                                 static_cast<hipStream_t>(hip_stream)));
 }

@@ -1240,8 +1240,10 @@ hipError_t launch_role(const BackwardArgs& a, bool res, dim3 grid, hipStream_t s
   return hipGetLastError();
 }
 
-// 16-token mini-batches: replay (unless the forward saved the bases), the
-// front half of every tile, the reverse walk; longer ones: the whole pass.
+// 16-token mini-batches: the front half of every tile and the reverse walk
+// (the host API has the forward kernel store the bases first; kReplay runs
+// only for a caller of this launcher that did neither); longer mini-batches:
+// the whole pass.
 template <bool BF16, bool LN>
 hipError_t launch_b2(const BackwardArgs& a, bool res, hipStream_t s) {
   const int units = a.B * a.H;

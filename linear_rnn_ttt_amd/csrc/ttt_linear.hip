@@ -345,10 +345,12 @@ __device__ __forceinline__ uint32_t bf16_bits(float x) { return pack_bf16(x, 0.f
 template <bool BF16>
 struct ZOut {
   __amdgpu_buffer_rsrc_t r;
+  // z == nullptr (the backward's run for the bases alone): a zero range, so
+  // the hardware drops every store
   __device__ __forceinline__ ZOut(void* z, size_t row0, int T) {
     constexpr int RB = D * (BF16 ? 2 : 4);
-    r = __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(z) + row0 * RB, (short)0, T * RB,
-                                          0x00020000);
+    r = __builtin_amdgcn_make_buffer_rsrc(static_cast<char*>(z) + row0 * RB, (short)0,
+                                          z ? T * RB : 0, 0x00020000);
   }
   __device__ __forceinline__ void store(int tok, int fo, f32x4 v) const {
     if (BF16) {

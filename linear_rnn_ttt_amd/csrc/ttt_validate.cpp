@@ -173,6 +173,22 @@ ttt_status linear_split_noalloc(const ttt_params* p, const void* q, const void* 
   return TTT_OK;
 }
 
+ttt_status linear_forward_bases(const ttt_params* p, const void* q, const void* k,
+                                const void* v, const float* eta, const float* w0,
+                                const float* ln_gamma, const float* ln_beta, void* workspace,
+                                tttk::LinearArgs* a) {
+  // the workspace stands in for z in the forward's checks (it is checked not
+  // to overlap the inputs) and is then replaced by no z at all
+  const ttt_status st = linear_forward(p, q, k, v, eta, w0, ln_gamma, ln_beta, workspace,
+                                       nullptr, nullptr, 0, a);
+  if (st != TTT_OK) return st;
+  if (p->mini_batch != 16) return TTT_ERR_UNSUPPORTED;
+  a->z = nullptr;
+  a->w_out = nullptr;
+  a->bases = static_cast<float*>(workspace);
+  return TTT_OK;
+}
+
 ttt_status linear_forward_save(const ttt_params* p, const void* q, const void* k,
                                const void* v, const float* eta, const float* w0,
                                const float* ln_gamma, const float* ln_beta, void* z,

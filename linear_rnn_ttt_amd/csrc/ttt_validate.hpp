@@ -59,6 +59,14 @@ ttt_status linear_split_noalloc(const ttt_params* p, const void* q, const void* 
 // The workspace fields of a split launch at `workspace` (split_layout).
 void set_split_workspace(const ttt_params* p, void* workspace, tttk::LinearArgs* a);
 
+// ttt_linear_backward with 16-token mini-batches and no saved bases: the
+// forward in its base-saving form with no z and no final state, storing the
+// bases into the backward's (already validated) workspace.
+ttt_status linear_forward_bases(const ttt_params* p, const void* q, const void* k,
+                                const void* v, const float* eta, const float* w0,
+                                const float* ln_gamma, const float* ln_beta, void* workspace,
+                                tttk::LinearArgs* a);
+
 // ttt_linear_forward_save.
 ttt_status linear_forward_save(const ttt_params* p, const void* q, const void* k,
                                const void* v, const float* eta, const float* w0,

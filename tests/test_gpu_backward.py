@@ -321,6 +321,31 @@ def test_backward_from_saved_bases_matches_the_oracle(case):
         assert v <= TOL[io], (n, v)
 
 
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_backward_without_saved_bases_is_the_training_path(io):
+    """With 16-token mini-batches the backward takes its bases from the
+    forward kernel itself, so a call without saved bases gives the same bits
+    as ttt_linear_forward(save_for_backward=...) followed by the backward
+    from those bases (ragged T, per-batch W0 too)."""
+    wl = BF if io == "bf16" else F32
+    for T, per_batch in ((70, False), (33, True)):
+        inp = make_inputs(wl, B=2, H=3, T=T)
+        if per_batch:
+            inp["w0"] = np.stack([inp["w0"], 0.5 * inp["w0"]])
+        dz, dwT = cotangents(inp, io, seed=T + 11)
+        dev = {x: to_dev(inp[x], io if x in "qkv" else None) for x in inp}
+        args = (dev["q"], dev["k"], dev["v"], dev["eta"], dev["w0"], dev["gamma"], dev["beta"])
+        kw = dict(state0_per_batch=per_batch)
+        a = ttt_linear_backward(*args, to_dev(dz, io), to_dev(dwT), **kw)
+        ws = torch.full((1 << 22,), 255, dtype=torch.uint8, device="cuda")
+        ttt_linear_forward(*args, save_for_backward=ws, **kw)
+        b = ttt_linear_backward(*args, to_dev(dz, io), to_dev(dwT), workspace=ws,
+                                bases_saved=True, **kw)
+        torch.cuda.synchronize()
+        for n, x, y in zip(NAMES, a, b):
+            assert torch.equal(x, y), (T, n)
+
+
 def test_backward_from_saved_bases_full_size_one_head():
     """Forward with saved bases, then the backward without the replay, at
     the 1.3B-layer workload; head 5 (all four batch entries) vs the oracle."""
